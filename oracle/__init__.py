@@ -1,0 +1,222 @@
+"""ctypes wrapper of the CPU oracle (``ebl_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the CPU
+baseline leg of ``bench.py`` may use this module; the library and its Python
+binding never import it.  The oracle is single-threaded plain C that follows
+arXiv 2407.04272 (quantization encoder of section III-D, vector
+homogenization of section III-B, Algorithm 1's error-bound policy) and this
+project's stream layout, documented in ``ebl_oracle.h``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libebl_oracle.so")
+SOURCES = [os.path.join(HERE, "ebl_oracle.c")]
+
+EB_ABS, EB_REL = 0, 1
+SCHED_NONE, SCHED_INV_SQRT, SCHED_STEP = 0, 1, 2
+OK, ERR_INVALID, ERR_CAPACITY, ERR_CORRUPT, ERR_OOM = 0, 1, 2, 3, 5
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (IEEE fp32, no contraction, no fast-math)."""
+    if not force and os.path.exists(LIB_PATH):
+        return LIB_PATH
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-ffp-contract=off",
+           "-fno-fast-math", "-fPIC", "-shared", "-o", LIB_PATH, *SOURCES, "-lm"]
+    subprocess.run(cmd, check=True, cwd=HERE)
+    return LIB_PATH
+
+
+class _Cfg(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_uint32), ("B", ctypes.c_uint32), ("D", ctypes.c_uint32),
+        ("P", ctypes.c_uint32), ("eb_mode", ctypes.c_uint32),
+        ("eb", ctypes.POINTER(ctypes.c_float)),
+        ("table_mult", ctypes.POINTER(ctypes.c_float)),
+        ("sched_kind", ctypes.c_int32), ("sched_steps", ctypes.c_int32),
+        ("sched_t0", ctypes.c_double), ("sched_k", ctypes.c_double),
+        ("sched_phase", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        L = ctypes.CDLL(LIB_PATH)
+        f32p = ctypes.POINTER(ctypes.c_float)
+        cfgp = ctypes.POINTER(_Cfg)
+        L.ebo_schedule.restype = ctypes.c_double
+        L.ebo_schedule.argtypes = [cfgp, ctypes.c_int64]
+        L.ebo_table_factor.restype = ctypes.c_float
+        L.ebo_table_factor.argtypes = [cfgp, ctypes.c_uint32, ctypes.c_int64]
+        L.ebo_range.restype = None
+        L.ebo_range.argtypes = [f32p, ctypes.c_size_t, f32p, f32p]
+        L.ebo_eb_valid.restype = ctypes.c_int
+        L.ebo_eb_valid.argtypes = [ctypes.c_float]
+        L.ebo_quantize.restype = ctypes.c_int
+        L.ebo_quantize.argtypes = [ctypes.c_float, ctypes.c_float, ctypes.POINTER(ctypes.c_int32)]
+        L.ebo_dequantize.restype = ctypes.c_float
+        L.ebo_dequantize.argtypes = [ctypes.c_int32, ctypes.c_float]
+        L.ebo_zigzag.restype = ctypes.c_uint32
+        L.ebo_zigzag.argtypes = [ctypes.c_int32]
+        L.ebo_unzigzag.restype = ctypes.c_int32
+        L.ebo_unzigzag.argtypes = [ctypes.c_uint32]
+        L.ebo_homo_index.restype = ctypes.c_double
+        L.ebo_homo_index.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
+        L.ebo_table_eb.restype = ctypes.c_float
+        L.ebo_table_eb.argtypes = [cfgp, ctypes.c_uint32, ctypes.c_int64, f32p]
+        L.ebo_max_compressed_bytes.restype = ctypes.c_size_t
+        L.ebo_max_compressed_bytes.argtypes = [cfgp]
+        L.ebo_compress.restype = ctypes.c_int
+        L.ebo_compress.argtypes = [cfgp, ctypes.c_int64, f32p, ctypes.c_void_p, ctypes.c_size_t,
+                                   ctypes.POINTER(ctypes.c_size_t), ctypes.c_void_p,
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.ebo_decompress.restype = ctypes.c_int
+        L.ebo_decompress.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint32,
+                                     ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, f32p]
+        _lib = L
+    return _lib
+
+
+def _f32ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+
+
+@dataclass
+class Config:
+    """Shape and error-bound policy of one compression problem."""
+    T: int
+    B: int
+    D: int
+    P: int = 1
+    eb_mode: int = EB_ABS
+    eb: tuple = (1e-4,)
+    table_mult: tuple | None = None
+    sched_kind: int = SCHED_NONE
+    sched_t0: float = 1000.0
+    sched_k: float = 2.0
+    sched_phase: int = 1
+    sched_steps: int = 1
+
+    def _c(self):
+        eb = np.ascontiguousarray(np.asarray(self.eb, dtype=np.float32).reshape(-1))
+        if eb.size == 1 and self.T > 1:
+            eb = np.full(self.T, eb[0], dtype=np.float32)
+        mult = None
+        if self.table_mult is not None:
+            mult = np.ascontiguousarray(np.asarray(self.table_mult, dtype=np.float32))
+        c = _Cfg(self.T, self.B, self.D, self.P, self.eb_mode, _f32ptr(eb),
+                 _f32ptr(mult) if mult is not None else ctypes.POINTER(ctypes.c_float)(),
+                 self.sched_kind, self.sched_steps, self.sched_t0, self.sched_k,
+                 self.sched_phase)
+        return c, (eb, mult)  # keep arrays alive with the struct
+
+
+def schedule(cfg: Config, it: int) -> float:
+    c, keep = cfg._c()
+    return lib().ebo_schedule(ctypes.byref(c), it)
+
+
+def table_factor(cfg: Config, t: int, it: int) -> float:
+    c, keep = cfg._c()
+    return lib().ebo_table_factor(ctypes.byref(c), t, it)
+
+
+def table_eb(cfg: Config, t: int, it: int, x: np.ndarray) -> float:
+    c, keep = cfg._c()
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    return lib().ebo_table_eb(ctypes.byref(c), t, it, _f32ptr(x))
+
+
+def value_range(x: np.ndarray):
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+    lo, hi = ctypes.c_float(), ctypes.c_float()
+    lib().ebo_range(_f32ptr(x), x.size, ctypes.byref(lo), ctypes.byref(hi))
+    return lo.value, hi.value
+
+
+def eb_valid(eb: float) -> bool:
+    return bool(lib().ebo_eb_valid(eb))
+
+
+def quantize(x: float, eb: float):
+    q = ctypes.c_int32()
+    o = lib().ebo_quantize(x, eb, ctypes.byref(q))
+    return q.value, bool(o)
+
+
+def dequantize(q: int, eb: float) -> float:
+    return lib().ebo_dequantize(q, eb)
+
+
+def zigzag(q: int) -> int:
+    return lib().ebo_zigzag(q)
+
+
+def unzigzag(z: int) -> int:
+    return lib().ebo_unzigzag(z)
+
+
+def homo_index(n_original: int, n_compressed: int) -> float:
+    return lib().ebo_homo_index(n_original, n_compressed)
+
+
+def max_compressed_bytes(cfg: Config) -> int:
+    c, keep = cfg._c()
+    return lib().ebo_max_compressed_bytes(ctypes.byref(c))
+
+
+@dataclass
+class Compressed:
+    stream: np.ndarray          # uint8 bytes of the stream
+    codes: np.ndarray | None    # int32 [T,B,D]
+    outlier: np.ndarray | None  # uint8 [T,B,D]
+    first: np.ndarray | None    # uint32 [T,B]
+    eb: np.ndarray | None       # float32 [P*T]
+
+
+def compress(cfg: Config, it: int, x: np.ndarray, debug: bool = True) -> Compressed:
+    c, keep = cfg._c()
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(cfg.T, cfg.B, cfg.D)
+    cap = max_compressed_bytes(cfg)
+    if cap == 0:
+        raise ValueError("invalid configuration")
+    out = np.zeros(cap, dtype=np.uint8)
+    n = ctypes.c_size_t()
+    codes = np.zeros((cfg.T, cfg.B, cfg.D), np.int32) if debug else None
+    outl = np.zeros((cfg.T, cfg.B, cfg.D), np.uint8) if debug else None
+    first = np.zeros((cfg.T, cfg.B), np.uint32) if debug else None
+    ebs = np.zeros(cfg.P * cfg.T, np.float32) if debug else None
+
+    def p(a):
+        return a.ctypes.data if a is not None else None
+
+    rc = lib().ebo_compress(ctypes.byref(c), it, _f32ptr(x), out.ctypes.data, cap,
+                            ctypes.byref(n), p(codes), p(outl), p(first), p(ebs))
+    if rc != OK:
+        raise RuntimeError(f"oracle compress failed with status {rc}")
+    return Compressed(out[: n.value].copy(), codes, outl, first, ebs)
+
+
+def decompress(cfg: Config, stream: np.ndarray, status: bool = False):
+    s = np.ascontiguousarray(stream, dtype=np.uint8)
+    y = np.zeros((cfg.T, cfg.B, cfg.D), np.float32)
+    rc = lib().ebo_decompress(s.ctypes.data, s.size, cfg.T, cfg.B, cfg.D, cfg.P, _f32ptr(y))
+    if status:
+        return rc, y
+    if rc != OK:
+        raise RuntimeError(f"oracle decompress failed with status {rc}")
+    return y

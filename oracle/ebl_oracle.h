@@ -1,0 +1,143 @@
+/*
+ * ebl_oracle.h -- plain, slow, single-threaded CPU oracle for the
+ * error-bounded lossy compressor of DLRM embedding traffic.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this code: only the tests, the smoke check and the benchmark's CPU
+ * baseline leg use it.  It shares no source with the HIP library.
+ *
+ * Method (arXiv 2407.04272, "Accelerating Communication in Deep Learning
+ * Recommendation Model Training with Dual-Level Adaptive Lossy Compression"):
+ *   - section III-D: a quantization encoder turns floats into integer bins,
+ *     followed by a lossless encoder; no prediction step (III-B, observation 1,
+ *     and Fig. 4 show the Lorenzo predictor breaking identical vectors);
+ *   - section III-B observation 2 / III-D "Vector-based LZ Encoding": identical
+ *     (quantized) embedding vectors are encoded once and referenced;
+ *   - section III-C / Algorithm 1: per-table error bound times an
+ *     iteration-wise decay factor;
+ *   - section III-A stages 1-4 and III-E "Buffer Optimization" (Fig. 7): all
+ *     tables of all destination chunks go into ONE contiguous stream whose
+ *     per-chunk sizes are the metadata of the variable-size all-to-all.
+ *
+ * The byte layout below is this project's own (the pages fix no format).
+ * All integers are little-endian; every padding byte and unused bit is zero.
+ *
+ * STREAM
+ *   header, 64 bytes:
+ *     0  u32 magic 0x434C4245 (bytes "EBLC")   4  u16 version = 1
+ *     6  u16 coder = 1 (bit-plane packing)      8  u32 T (tables)
+ *     12 u32 B (rows per table)                 16 u32 D (dim)
+ *     20 u32 P (destination chunks)             24 u32 tile_rows = 64
+ *     28 u32 eb_mode (0 absolute, 1 range-relative)
+ *     32 i64 iter                               40 u64 uncompressed bytes 4*T*B*D
+ *     48 u64 total stream bytes                 56 u64 reserved = 0
+ *   chunk byte counts: P x u64, zero-padded to a multiple of 16 bytes
+ *   chunk 0, chunk 1, ..., chunk P-1
+ *
+ * CHUNK p (rows [floor(p*B/P), floor((p+1)*B/P)) of every table)
+ *   segment offset table: T x u64, offset of segment (p,t) from the chunk
+ *   start, zero-padded to 16; then segments (p,0) .. (p,T-1).
+ *
+ * SEGMENT (p,t)  (16-byte aligned; its size is a multiple of 16)
+ *   header, 32 bytes:
+ *     0 u32 rows   4 u32 ntiles = ceil(rows/64)   8 f32 eb (0 when invalid)
+ *     12 u32 flags (bit 0: eb valid)   16 u32 U (first occurrences)
+ *     20 u32 n_out (outliers stored in coded tiles)   24 u64 segment bytes
+ *   tile directory: ntiles x u32 offset of each tile record from the segment
+ *   start, zero-padded to 16; then the tile records in order.
+ *
+ * TILE RECORD (tile k = segment rows [64k, min(64k+64, rows)), n rows)
+ *   header, 16 bytes:
+ *     0 u64 first-occurrence bitmap (bit i: row 64k+i is the first row of the
+ *           segment with its key; 0 for every tile of an invalid-eb segment)
+ *     8 u32 n_out   12 u16 U_t = popcount(bitmap)   14 u8 mode   15 u8 0
+ *   mode 0 RAW: n*D raw fp32 values, row-major; zero pad to 16.
+ *   mode 1 BITPACK, with E = the codes of the tile's first-occurrence rows in
+ *   row order, flattened (U_t*D elements), in blocks of 64 (tail padded with
+ *   code 0), nblk = ceil(U_t*D/64):
+ *     at 16:                  widths, nblk x u8
+ *     at align4:              refs, (n-U_t) x (u16 if rows <= 65536 else u32),
+ *                             the segment row of each repeated row's first
+ *                             occurrence, in row order
+ *     at align4:              outlier positions, n_out x u32, ascending index
+ *                             into E
+ *     right after:            outlier values, n_out x u32 raw fp32 bits
+ *     at align8:              bit planes: block b contributes w_b u64 words,
+ *                             word j bit i = bit j of zigzag(E[64b+i])
+ *     zero pad to 16.
+ *   A tile is BITPACK iff its segment's eb is valid and the BITPACK record is
+ *   strictly smaller than the RAW record; otherwise RAW.
+ */
+#ifndef EBL_ORACLE_H
+#define EBL_ORACLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EBO_MAGIC 0x434C4245u
+#define EBO_VERSION 1u
+#define EBO_CODER_BITPACK 1u
+#define EBO_TILE_ROWS 64u
+#define EBO_QMAX 2047
+
+enum { EBO_OK = 0, EBO_ERR_INVALID = 1, EBO_ERR_CAPACITY = 2, EBO_ERR_CORRUPT = 3,
+       EBO_ERR_OOM = 5 };
+enum { EBO_EB_ABS = 0, EBO_EB_REL = 1 };
+enum { EBO_SCHED_NONE = 0, EBO_SCHED_INV_SQRT = 1, EBO_SCHED_STEP = 2 };
+
+typedef struct {
+  uint32_t T, B, D, P;
+  uint32_t eb_mode;          /* EBO_EB_ABS or EBO_EB_REL                  */
+  const float* eb;           /* [T] absolute eb, or range factor (REL)     */
+  const float* table_mult;   /* [T] table-class multiplier, NULL means 1   */
+  int32_t sched_kind;        /* EBO_SCHED_*                                */
+  int32_t sched_steps;       /* STEP: number of stairs                     */
+  double sched_t0;           /* INV_SQRT: (1 + i/t0)^-1/2                  */
+  double sched_k;            /* STEP: starting multiple of the base eb     */
+  int64_t sched_phase;       /* STEP: length of the decay phase            */
+} ebo_cfg;
+
+/* Iteration-wise factor (Algorithm 1 OnlineDecay, read non-cumulatively). */
+double ebo_schedule(const ebo_cfg* c, int64_t iter);
+/* f_t = (float)((double)eb[t] * (double)mult[t] * schedule(iter)). */
+float ebo_table_factor(const ebo_cfg* c, uint32_t t, int64_t iter);
+/* min/max over the non-NaN values (+INF/-INF when there are none). */
+void ebo_range(const float* x, size_t n, float* lo, float* hi);
+int ebo_eb_valid(float eb);
+/* Linear quantization of one value; returns 1 for an outlier (q set to 0). */
+int ebo_quantize(float x, float eb, int32_t* q);
+float ebo_dequantize(int32_t q, float eb);
+uint32_t ebo_zigzag(int32_t q);
+int32_t ebo_unzigzag(uint32_t z);
+
+/* Eq. (1) Homogenization Index: (N_original - N_compressed) / N_original. */
+double ebo_homo_index(uint64_t n_original, uint64_t n_compressed);
+
+/* Per-table error bound used for every segment of table t (fp32). */
+float ebo_table_eb(const ebo_cfg* c, uint32_t t, int64_t iter, const float* x);
+
+/* Size of the stream when every tile is RAW: the compressed-size bound. */
+size_t ebo_max_compressed_bytes(const ebo_cfg* c);
+
+/*
+ * Compress x[T][B][D] (row-major fp32) into out.  Optional outputs (NULL to
+ * skip): codes[T*B*D] (0 for outliers), outlier[T*B*D] (0/1),
+ * first[T*B] (segment row of each row's first occurrence; row itself for
+ * invalid-eb segments), eb_seg[P*T] (segment eb as stored).
+ */
+int ebo_compress(const ebo_cfg* c, int64_t iter, const float* x, uint8_t* out, size_t cap,
+                 size_t* out_bytes, int32_t* codes, uint8_t* outlier, uint32_t* first,
+                 float* eb_seg);
+
+/* Decompress a stream whose header matches (T,B,D,P); y gets T*B*D floats. */
+int ebo_decompress(const uint8_t* s, size_t nbytes, uint32_t T, uint32_t B, uint32_t D,
+                   uint32_t P, float* y);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,411 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: exact
+rational arithmetic, closed forms, brute force on tiny inputs, an
+independent stream reader written from the layout spec, or numbers printed
+on the pages (arXiv 2407.04272).
+"""
+from fractions import Fraction
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+import streamfmt as SF
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def f32(v):
+    return float(np.float32(v))
+
+
+# --------------------------------------------------------------------------
+# quantization encoder (section III-D): q = round(x / 2eb), |x - x^| <= eb
+# --------------------------------------------------------------------------
+def test_ties_round_half_to_even():
+    # eb = 0.5 -> bin width 1: exact ties go to the even bin
+    for x, q in [(0.5, 0), (1.5, 2), (2.5, 2), (3.5, 4), (-0.5, 0), (-1.5, -2), (-2.5, -2)]:
+        got, out = O.quantize(x, 0.5)
+        assert (got, out) == (q, False), x
+
+
+def test_quantizer_matches_exact_rounding_away_from_ties():
+    rng = np.random.default_rng(1)
+    for _ in range(4000):
+        eb = f32(10.0 ** rng.uniform(-8, 1))
+        x = f32(rng.uniform(-2040, 2040) * 2 * eb)
+        ratio = Fraction(x) / (2 * Fraction(eb))
+        frac = ratio - math.floor(ratio)
+        if abs(frac - Fraction(1, 2)) < Fraction(1, 1000):
+            continue  # near a tie: covered by the bound test below
+        want = round(ratio)
+        got, out = O.quantize(x, eb)
+        assert not out and got == want, (x, eb)
+
+
+def test_bound_holds_exactly_for_every_value():
+    rng = np.random.default_rng(2)
+    n_out = 0
+    for _ in range(6000):
+        eb = f32(10.0 ** rng.uniform(-10, 2))
+        x = f32(rng.choice([1.0, -1.0]) * 10.0 ** rng.uniform(-12, 4))
+        q, out = O.quantize(x, eb)
+        if out:
+            n_out += 1
+            assert q == 0
+            continue
+        assert abs(q) <= 2047
+        xh = O.dequantize(q, eb)
+        assert abs(Fraction(x) - Fraction(xh)) <= Fraction(eb), (x, eb, q)
+    assert n_out > 0
+
+
+def test_float_quotient_on_a_tie_that_is_not_a_tie():
+    # Search values whose rounded quotient fl(x/s) is exactly k + 1/2 while the
+    # true quotient is not: round-half-even may pick the far bin.  The value is
+    # an outlier exactly when its fp32 reconstruction fl(q*s) misses eb, judged
+    # here in exact rational arithmetic.
+    rng = np.random.default_rng(3)
+    found_far = 0
+    for _ in range(200000):
+        eb = f32(rng.uniform(0.5, 1.0))
+        s = np.float32(eb) + np.float32(eb)
+        k = int(rng.integers(1, 2000))
+        x = np.float32((k + 0.5) * float(s))
+        x = np.nextafter(x, np.float32(np.inf) if rng.random() < 0.5 else np.float32(-np.inf))
+        t = np.float32(x) / s
+        if float(t) != k + 0.5:
+            continue
+        exact = Fraction(float(x)) / Fraction(float(s))
+        if exact == Fraction(2 * k + 1, 2):
+            continue
+        q, out = O.quantize(float(x), eb)
+        near = math.floor(exact + Fraction(1, 2))          # the correct bin
+        rne = k if k % 2 == 0 else k + 1                   # what RNE of k + 1/2 picks
+        xh = np.float32(rne) * s                           # reconstruction is fl(q * s)
+        misses = abs(Fraction(float(x)) - Fraction(float(xh))) > Fraction(eb)
+        assert out == misses, (float(x), eb, k)
+        if not out:
+            assert q == rne        # kept: its fp32 reconstruction still meets eb
+            assert abs(q - near) <= 1
+        else:
+            found_far += 1
+            assert q == 0          # stored verbatim instead
+    assert found_far > 0
+
+
+def test_out_of_range_nan_inf_are_outliers():
+    for x in [math.nan, math.inf, -math.inf, 1e30, -1e30]:
+        q, out = O.quantize(x, 1e-3)
+        assert out and q == 0
+    # 2047 bins is the largest code
+    assert O.quantize(2047.0, 0.5) == (2047, False)
+    assert O.quantize(2048.0, 0.5) == (0, True)
+
+
+def test_integer_values_with_dyadic_eb_round_trip_exactly():
+    for k in range(0, 6):
+        eb = 2.0 ** (-1 - k)            # bin width 2^-k
+        xs = np.arange(-(2047 >> k), (2047 >> k) + 1, dtype=np.float32)
+        for x in xs[:: max(1, xs.size // 200)]:
+            q, out = O.quantize(float(x), eb)
+            assert not out and O.dequantize(q, eb) == float(x)
+
+
+def test_zigzag_is_a_bijection_on_the_code_range():
+    zs = [O.zigzag(q) for q in range(-2047, 2048)]
+    assert sorted(zs) == list(range(0, 4095))
+    assert all(O.unzigzag(O.zigzag(q)) == q for q in range(-2047, 2048))
+    assert max(zs).bit_length() == 12
+
+
+# --------------------------------------------------------------------------
+# error-bound policy (section III-C, Algorithm 1)
+# --------------------------------------------------------------------------
+def test_inverse_sqrt_schedule_closed_forms():
+    cfg = O.Config(T=1, B=1, D=1, sched_kind=O.SCHED_INV_SQRT, sched_t0=1000.0)
+    assert O.schedule(cfg, 0) == 1.0
+    assert O.schedule(cfg, 3000) == 0.5      # 4^-1/2
+    assert O.schedule(cfg, 15000) == 0.25    # 16^-1/2
+    vals = [O.schedule(cfg, i) for i in range(10)]
+    assert all(a > b for a, b in zip(vals, vals[1:]))
+    assert O.schedule(cfg, -5) == 1.0        # negative iterations clamp to 0
+
+
+def test_staircase_schedule_closed_forms():
+    # Decay_2x (Fig. 10 caption): from twice the base eb down to the base eb
+    cfg = O.Config(T=1, B=1, D=1, sched_kind=O.SCHED_STEP, sched_k=2.0, sched_phase=100,
+                   sched_steps=4)
+    want = {0: 2.0, 24: 2.0, 25: 1.75, 49: 1.75, 50: 1.5, 75: 1.25, 99: 1.25, 100: 1.0,
+            10 ** 6: 1.0}
+    for i, v in want.items():
+        assert O.schedule(cfg, i) == v, i
+    none = O.Config(T=1, B=1, D=1)
+    assert O.schedule(none, 12345) == 1.0
+
+
+def test_table_factor_is_one_rounding_of_the_product():
+    cfg = O.Config(T=2, B=1, D=1, eb=(0.005, 0.01), table_mult=(1.0, 3.0),
+                   sched_kind=O.SCHED_INV_SQRT, sched_t0=1000.0)
+    assert O.table_factor(cfg, 0, 0) == f32(0.005)
+    assert O.table_factor(cfg, 0, 3000) == f32(float(np.float32(0.005)) * 0.5)
+    # exact product 3 * f32(0.01) rounded once to fp32
+    exact = Fraction(float(np.float32(0.01))) * 3
+    assert Fraction(O.table_factor(cfg, 1, 0)) == Fraction(float(np.float32(float(exact))))
+
+
+def test_range_ignores_nan_and_relative_eb():
+    x = np.array([np.nan, -0.25, 3.0, np.nan, 1.0], np.float32)
+    assert O.value_range(x) == (-0.25, 3.0)
+    assert O.value_range(np.array([np.nan, np.nan], np.float32)) == (math.inf, -math.inf)
+    cfg = O.Config(T=1, B=5, D=1, eb_mode=O.EB_REL, eb=(0.01,))
+    assert O.table_eb(cfg, 0, 0, x) == f32(float(np.float32(0.01)) * 3.25)
+
+
+def test_eb_validity():
+    assert O.eb_valid(1e-30) and O.eb_valid(1.0)
+    for v in [0.0, -1.0, math.nan, math.inf, 3e38]:   # 3e38: 2 eb overflows
+        assert not O.eb_valid(v)
+
+
+# --------------------------------------------------------------------------
+# Homogenization Index, Eq. (1), against Tables III and IV
+# --------------------------------------------------------------------------
+def test_homo_index_against_printed_tables():
+    rows = []
+    with open(os.path.join(HERE, "golden", "homo_index_tables.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            src, tab, eb, n_o, n_q, batch, printed = line.split()
+            rows.append((int(n_o), int(n_q), float(printed)))
+    assert len(rows) == 16
+    for n_o, n_q, printed in rows:
+        eta = O.homo_index(n_o, n_q)
+        assert 0.0 <= eta <= 1.0
+        assert round(1.0 - eta, 6) == pytest.approx(printed, abs=1e-6)
+    assert O.homo_index(110, 68) == pytest.approx(42 / 110, abs=1e-15)
+
+
+# --------------------------------------------------------------------------
+# vector deduplication (section III-B obs. 2): brute force on tiny inputs
+# --------------------------------------------------------------------------
+def brute_first(x, eb):
+    rows = []
+    for r in range(x.shape[0]):
+        key = []
+        for v in x[r]:
+            q, out = O.quantize(float(v), eb)
+            key.append(("o", np.float32(v).view(np.uint32).item()) if out else ("q", q))
+        rows.append(tuple(key))
+    first = []
+    for r in range(len(rows)):
+        for r2 in range(r + 1):
+            if rows[r2] == rows[r]:
+                first.append(r2)
+                break
+    return np.array(first)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_dedup_matches_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    B, D = int(rng.integers(1, 140)), int(rng.integers(1, 9))
+    eb = 0.05
+    base = rng.normal(0, 0.2, (max(1, B // 3), D)).astype(np.float32)
+    x = base[rng.integers(0, base.shape[0], B)]
+    x = x + rng.uniform(-0.02, 0.02, x.shape).astype(np.float32) * (rng.random((B, 1)) < 0.5)
+    x = x.astype(np.float32)
+    if B > 4:
+        x[2, 0] = np.nan
+        x[3] = x[2]
+        x[4, -1] = 1e9
+    cfg = O.Config(T=1, B=B, D=D, eb=(eb,))
+    c = O.compress(cfg, 0, x[None])
+    want = brute_first(x, eb)
+    np.testing.assert_array_equal(c.first[0], want)
+    # quantization only merges rows: distinct quantized rows <= distinct raw rows
+    u_quant = len(set(want.tolist()))
+    u_raw = np.unique(x.view(np.uint32), axis=0).shape[0]
+    assert u_quant <= u_raw
+
+
+# --------------------------------------------------------------------------
+# stream: independent reader, zero padding, bit planes, bound, determinism
+# --------------------------------------------------------------------------
+def check_stream(cfg, x, it=0):
+    c = O.compress(cfg, it, x)
+    st = SF.parse(c.stream)
+    assert not c.stream[~st.covered].any(), "non-zero padding"
+    codes, outl, first, y = SF.decode(st, c.stream)
+    yo = O.decompress(cfg, c.stream)
+    np.testing.assert_array_equal(y.view(np.uint32), yo.view(np.uint32))
+    # widths = bit length of each block's largest zigzag code
+    for seg in st.segments:
+        for tl in seg.tiles:
+            if tl.mode != 1:
+                continue
+            zz = np.zeros(len(tl.widths) * 64, np.int64)
+            zz[:tl.zz.size] = tl.zz
+            mx = zz.reshape(-1, 64).max(axis=1)
+            np.testing.assert_array_equal(tl.widths, [int(m).bit_length() for m in mx])
+    # the oracle's own debug outputs agree with what the stream says
+    for seg in st.segments:
+        r0 = seg.p * cfg.B // cfg.P
+        r1 = (seg.p + 1) * cfg.B // cfg.P
+        if not seg.valid:
+            continue
+        mask = first[seg.t, r0:r1] >= 0
+        np.testing.assert_array_equal(first[seg.t, r0:r1][mask], c.first[seg.t, r0:r1][mask])
+        np.testing.assert_array_equal(codes[seg.t, r0:r1], c.codes[seg.t, r0:r1])
+        np.testing.assert_array_equal(outl[seg.t, r0:r1], c.outlier[seg.t, r0:r1].astype(bool))
+    # error bound on every element (outliers exact, NaN payloads preserved)
+    for seg in st.segments:
+        r0 = seg.p * cfg.B // cfg.P
+        r1 = (seg.p + 1) * cfg.B // cfg.P
+        xs, ys = x[seg.t, r0:r1], yo[seg.t, r0:r1]
+        if seg.valid:
+            err = np.abs(xs.astype(np.float64) - ys.astype(np.float64))
+            fin = np.isfinite(xs)
+            assert (err[fin] <= np.float64(seg.eb)).all()
+            np.testing.assert_array_equal(xs[~fin].view(np.uint32), ys[~fin].view(np.uint32))
+        else:
+            np.testing.assert_array_equal(xs.view(np.uint32), ys.view(np.uint32))
+    assert c.stream.size <= O.max_compressed_bytes(cfg)
+    assert O.compress(cfg, it, x).stream.tobytes() == c.stream.tobytes()
+    return c, st
+
+
+@pytest.mark.parametrize("T,B,D,P", [(1, 1, 1, 1), (1, 63, 3, 1), (2, 64, 16, 1),
+                                      (3, 65, 64, 2), (2, 130, 128, 3), (1, 200, 5, 4),
+                                      (2, 3, 8, 5), (1, 0, 4, 1), (1, 129, 256, 1)])
+def test_stream_shapes_and_invariants(T, B, D, P):
+    rng = np.random.default_rng(T * 1000 + B * 10 + D + P)
+    base = rng.normal(0, 0.1, (T, max(1, B // 2 + 1), D)).astype(np.float32)
+    idx = rng.integers(0, base.shape[1], (T, B))
+    x = np.take_along_axis(base, idx[:, :, None], axis=1).astype(np.float32)
+    cfg = O.Config(T=T, B=B, D=D, P=P, eb_mode=O.EB_REL, eb=(0.01,))
+    check_stream(cfg, x)
+
+
+def test_special_values_and_raw_fallbacks():
+    rng = np.random.default_rng(7)
+    T, B, D = 4, 70, 8
+    x = rng.normal(0, 1, (T, B, D)).astype(np.float32)
+    x[0, 3, 2] = np.nan
+    x[0, 4, 1] = np.inf
+    x[0, 5, 0] = -np.inf
+    x[0, 6, 3] = -0.0
+    x[0, 7] = np.float32(np.uint32(0x7FC00123).view(np.float32))  # NaN payload
+    x[1] = np.nan            # all-NaN table: invalid eb -> RAW segment
+    x[2] = 0.25              # constant table: zero range -> RAW segment
+    x[3] = rng.normal(0, 1e6, (B, D)).astype(np.float32)
+    cfg = O.Config(T=T, B=B, D=D, eb_mode=O.EB_REL, eb=(0.01,))
+    c, st = check_stream(cfg, x)
+    assert not st.segments[1].valid and not st.segments[2].valid
+    assert all(tl.mode == 0 for tl in st.segments[1].tiles)
+
+
+def test_all_outliers_fall_back_to_raw_tiles():
+    # eb -> 0: every nonzero value is an outlier; the tile is stored RAW and
+    # the round trip is exact (the pages' "exact round-trip at eb -> 0")
+    rng = np.random.default_rng(8)
+    x = rng.integers(-1000, 1000, (2, 100, 16)).astype(np.float32)
+    cfg = O.Config(T=2, B=100, D=16, eb=(1e-30,))
+    c, st = check_stream(cfg, x)
+    y = O.decompress(cfg, c.stream)
+    np.testing.assert_array_equal(y, x)
+    assert all(tl.mode == 0 for s in st.segments for tl in s.tiles)
+    assert c.stream.size == O.max_compressed_bytes(cfg)
+
+
+def test_references_into_raw_tiles_decode_by_requantization():
+    # tile 0 incompressible (huge spread -> RAW), later rows repeat tile-0 rows
+    rng = np.random.default_rng(9)
+    B, D = 200, 32
+    x = np.zeros((1, B, D), np.float32)
+    x[0, :64] = rng.normal(0, 1, (64, D)) * np.float32(10.0) ** rng.integers(-3, 4, (64, D))
+    x[0, 64:] = rng.normal(0, 0.01, (B - 64, D))
+    x[0, 100] = x[0, 3]
+    x[0, 150] = x[0, 10]
+    cfg = O.Config(T=1, B=B, D=D, eb=(1e-3,))
+    c, st = check_stream(cfg, x)
+    assert st.segments[0].tiles[0].mode == 0
+    assert c.first[0, 100] == 3 and c.first[0, 150] == 10
+
+
+def test_compression_ratio_is_total_bytes_based():
+    # Table V "avg." is the harmonic mean of per-table ratios, i.e. the ratio
+    # of total bytes for equal-sized tables; the stream reports total bytes.
+    rng = np.random.default_rng(10)
+    x = rng.normal(0, 0.01, (3, 256, 32)).astype(np.float32)
+    x[1] = x[1, :1]   # all rows identical
+    cfg = O.Config(T=3, B=256, D=32, eb=(1e-3,))
+    c, st = check_stream(cfg, x)
+    seg_bytes = [s.nbytes for s in st.segments]
+    per_cr = [4 * 256 * 32 / b for b in seg_bytes]
+    overhead = c.stream.size - sum(seg_bytes)
+    assert 3 * 4 * 256 * 32 / (sum(seg_bytes)) == pytest.approx(3 / sum(1 / v for v in per_cr))
+    assert overhead == 64 + 16 + 32
+
+
+# --------------------------------------------------------------------------
+# corrupt and truncated streams never crash the decoder
+# --------------------------------------------------------------------------
+def test_corrupt_streams_are_rejected_or_decoded_safely():
+    rng = np.random.default_rng(11)
+    x = rng.normal(0, 0.1, (2, 150, 24)).astype(np.float32)
+    x[:, 80:] = x[:, :70]
+    cfg = O.Config(T=2, B=150, D=24, eb=(1e-2,))
+    good = O.compress(cfg, 0, x).stream
+    assert O.decompress(cfg, good, status=True)[0] == O.OK
+    assert O.decompress(cfg, good[:-16], status=True)[0] == O.ERR_CORRUPT
+    bad = good.copy()
+    bad[0] ^= 1
+    assert O.decompress(cfg, bad, status=True)[0] == O.ERR_CORRUPT
+    n_err = 0
+    for i in range(400):
+        bad = good.copy()
+        for _ in range(int(rng.integers(1, 4))):
+            bad[int(rng.integers(0, bad.size))] ^= np.uint8(1 << int(rng.integers(0, 8)))
+        rc, _ = O.decompress(cfg, bad, status=True)
+        assert rc in (O.OK, O.ERR_CORRUPT)
+        n_err += rc != O.OK
+        cut = int(rng.integers(0, good.size))
+        assert O.decompress(cfg, good[:cut], status=True)[0] == O.ERR_CORRUPT
+    assert n_err > 0
+    # wrong shape
+    cfg2 = O.Config(T=2, B=151, D=24, eb=(1e-2,))
+    assert O.decompress(cfg2, good, status=True)[0] == O.ERR_CORRUPT
+
+
+def test_invalid_configuration_is_an_error():
+    x = np.zeros((1, 4, 4), np.float32)
+    with pytest.raises(RuntimeError):
+        O.compress(O.Config(T=1, B=4, D=4, eb=(0.0,)), 0, x)
+    with pytest.raises(RuntimeError):
+        O.compress(O.Config(T=1, B=4, D=4, eb=(math.nan,)), 0, x)
+    with pytest.raises(RuntimeError):
+        O.compress(O.Config(T=1, B=4, D=4, eb=(1e-3,), table_mult=(-1.0,)), 0, x)
+
+
+# --------------------------------------------------------------------------
+# the synthetic workloads (two tables each, or fewer rows) through the oracle
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
+def test_workload_subsets_meet_the_bound(name):
+    import synth
+    w = synth.workload(name, iteration=1, tables=None if name == "c1" else [0, 3])
+    x = w.x.numpy()
+    T, B, D = x.shape
+    if name != "c1":
+        x = np.ascontiguousarray(x[:, :1024])
+        B = 1024
+    cfg = O.Config(T=T, B=B, D=D, eb_mode=w.eb_mode, eb=tuple(w.eb), sched_kind=w.sched_kind,
+                   sched_t0=w.sched_t0)
+    c, st = check_stream(cfg, x, it=w.iteration)
+    cr = x.nbytes / c.stream.size
+    assert cr > 1.5, cr
