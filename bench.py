@@ -1,0 +1,206 @@
+#!/usr/bin/env python3
+"""Benchmark of the error-bounded lossy compressor on one MI355X.
+
+One step = compress + decompress of one synthetic batch (every stage of the
+path: range reduction, quantization, duplicate-row detection, bit-plane
+packing, stream assembly, and the inverse).  The default workload is 26 tables
+x 8192 rows x 128 dims fp32, multi-hot pooled lookups, eb = 0.005 * range *
+(1 + t/1000)^-1/2; ten batches (t = 0..9) are resident in HBM and steps cycle
+through them, so the 1 GiB working set exceeds the 256 MiB Infinity Cache.
+
+Prints ONE JSON line.  `value` is round-trip throughput in GB/s of
+uncompressed input; the roofline object reports the dominant kernel's
+algorithmic bytes per launch over its HIP-event-measured duration.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+WORKLOADS = {
+    "c1": "1x2048x16 fp32 one-hot Zipf(1.05) lookups, abs eb 1e-4",
+    "c2": "26x4096x64 fp32 one-hot Zipf lookups, eb 0.01*range",
+    "c3": "26x8192x128 fp32 multi-hot pooled lookups, eb 0.005*range*(1+t/1000)^-1/2",
+    "c4": "26x8192x128 fp32 gradients N(0,1e-3)+5% Laplace rows, sum-duplicated, abs eb 1e-5",
+    "c5": "64x16384x256 fp32 one-hot Zipf(1.2) lookups, eb 0.01*range",
+}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "error_bounded_lossy_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(x_cpu, w, min_seconds: float):
+    """The oracle (single-threaded C) on a bounded sample of the same batch:
+    round trips of table subsets until `min_seconds` of CPU work is done."""
+    import numpy as np
+    import oracle as O
+    T, B, D = x_cpu.shape
+    done_bytes, spent, tables = 0, 0.0, 0
+    t = 0
+    while spent < min_seconds and tables < 4 * T:
+        sel = [t % T, (t + 1) % T]
+        xs = np.ascontiguousarray(x_cpu[sel])
+        cfg = O.Config(T=2, B=B, D=D, eb_mode=w.eb_mode, eb=tuple(w.eb[:2]),
+                       sched_kind=w.sched_kind, sched_t0=w.sched_t0)
+        t0 = time.perf_counter()
+        c = O.compress(cfg, w.iteration, xs, debug=False)
+        O.decompress(cfg, c.stream)
+        spent += time.perf_counter() - t0
+        done_bytes += xs.nbytes
+        tables += 2
+        t += 2
+    return {"value": round(done_bytes / spent / 1e9, 5), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{tables} table round trips ({tables}x{B}x{D} fp32, "
+                      f"{done_bytes / 2**20:.0f} MiB) of batch t={w.iteration}, {spent:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
+    ap.add_argument("--batches", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share; --gpus {args.gpus} is not supported "
+              f"(the all-to-all across GPUs is out of scope of this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import error_bounded_lossy_amd as ec
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {args.batches} batches of {args.workload}", file=sys.stderr,
+          flush=True)
+    batches = [synth.workload(args.workload, iteration=i, device=dev) for i in range(args.batches)]
+    w0 = batches[0]
+    T, B, D = w0.shape
+    N = T * B * D
+    sched = {"kind": w0.sched_kind, "t0": w0.sched_t0} if w0.sched_kind else None
+    plan = ec.Plan(T, B, D, 1, w0.eb_mode, w0.eb, schedule=sched, device=dev)
+    out = plan.empty_stream()
+    y = torch.empty(T, B, D, dtype=torch.float32, device=dev)
+
+    # compression ratio of every batch (untimed)
+    crs, sizes = [], []
+    for w in batches:
+        plan.compress(w.x, out, w.iteration)
+        cr, nb, _ = plan.ratio()
+        crs.append(cr)
+        sizes.append(nb)
+    mean_bytes = sum(sizes) / len(sizes)
+
+    def step(i):
+        w = batches[i % len(batches)]
+        plan.compress(w.x, out, w.iteration)
+        plan.decompress(out, y)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    plan.profile_enable(True, max_launches=3 * args.steps + 8)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    _, _, st = plan.ratio(raise_on_error=False)
+    if st != 0:
+        print(f"[bench] device status {st}", file=sys.stderr)
+        sys.exit(1)
+    ms = e0.elapsed_time(e1)
+    t_prep, n_prep = plan.profile_read(ec.KERNEL_PREP)
+    t_enc, n_enc = plan.profile_read(ec.KERNEL_ENCODE)
+    t_dec, n_dec = plan.profile_read(ec.KERNEL_DECODE)
+    plan.profile_enable(False)
+
+    rel = w0.eb_mode == ec.EB_REL_RANGE
+    S = mean_bytes
+    tc = (t_prep + t_enc) / args.steps * 1e-3
+    td = t_dec / args.steps * 1e-3
+    step_s = ms / args.steps * 1e-3
+    bytes_c = 4 * N * (2 if rel else 1) + S
+    bytes_d = S + 4 * N
+    kernels = {
+        "prep": (t_prep / max(n_prep, 1), 4 * N if rel else 0),
+        "encode": (t_enc / max(n_enc, 1), 4 * N + S),
+        "decode": (t_dec / max(n_dec, 1), S + 4 * N),
+    }
+    dom = max(kernels, key=lambda k: kernels[k][0])
+    dom_ms, dom_bytes = kernels[dom]
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    traffic = load_traffic(dom, args.workload)
+    res = {
+        "metric": "compress+decompress GB/s (uncompressed) per MI355X; ratio at eb; % HBM roof",
+        "value": round(4 * N / step_s / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {WORKLOADS[args.workload]}", "tables": T,
+                   "batch": B, "dim": D, "chunks": 1, "batches_cycled": len(batches)},
+        "compress_GBps": round(4 * N / tc / 1e9, 2),
+        "decompress_GBps": round(4 * N / td / 1e9, 2),
+        "compression_ratio": round(sum(crs) / len(crs), 4),
+        "compression_ratio_per_batch": [round(c, 4) for c in crs],
+        "hbm_roof_frac_roundtrip": round((bytes_c + bytes_d) / step_s / 1e9 / HBM_PEAK_GBS, 4),
+        "kernel_ms": {k: round(v[0], 5) for k, v in kernels.items()},
+        "wall_s": round(wall, 4),
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": int(dom_bytes)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on a CPU sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w0.x.cpu().numpy(), w0, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,235 @@
+"""Python binding of libec.so, the gfx950 error-bounded lossy compressor for
+DLRM embedding traffic (arXiv 2407.04272).
+
+This module only marshals arguments for the C ABI declared in include/ec.h:
+torch supplies device memory and streams, and every step of compression and
+decompression runs in the library's HIP kernels.  There is no fallback: if
+libec.so cannot be loaded, importing the binding's functions raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+LIB_PATH = os.path.join(HERE, "libec.so")
+HEADER = os.path.join(ROOT, "include", "ec.h")
+
+EC_OK, EC_ERR_INVALID, EC_ERR_CAPACITY, EC_ERR_CORRUPT = 0, 1, 2, 3
+EC_ERR_DEVICE, EC_ERR_OOM, EC_ERR_UNSUPPORTED = 4, 5, 6
+EB_ABS, EB_REL_RANGE = 0, 1
+SCHED_NONE, SCHED_INV_SQRT, SCHED_STEP = 0, 1, 2
+CODER_BITPACK = 1
+KERNEL_PREP, KERNEL_ENCODE, KERNEL_DECODE = 0, 1, 2
+ABI_VERSION = 1
+
+
+class ECError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+        self.status = status
+
+
+class _Schedule(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("steps", ctypes.c_int32), ("t0", ctypes.c_double),
+                ("k", ctypes.c_double), ("phase", ctypes.c_int64)]
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [
+        ("abi_version", ctypes.c_uint32), ("num_tables", ctypes.c_uint32),
+        ("rows", ctypes.c_uint32), ("dim", ctypes.c_uint32), ("num_chunks", ctypes.c_uint32),
+        ("eb_mode", ctypes.c_int32), ("eb", ctypes.POINTER(ctypes.c_float)),
+        ("table_mult", ctypes.POINTER(ctypes.c_float)), ("sched", _Schedule),
+        ("coder", ctypes.c_int32), ("debug_hash_bits", ctypes.c_uint32),
+        ("d_workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """Load libec.so (raises if it is missing: there is no CPU fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing; build it with error_bounded_lossy_amd/build.py")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, sz, st = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    dp = ctypes.POINTER(_Desc)
+    L.ec_max_dim.restype = ctypes.c_uint32
+    L.ec_max_dim.argtypes = []
+    L.ec_workspace_bytes.restype = sz
+    L.ec_workspace_bytes.argtypes = [dp]
+    L.ec_plan.restype = st
+    L.ec_plan.argtypes = [dp, ctypes.POINTER(vp)]
+    L.ec_plan_destroy.restype = st
+    L.ec_plan_destroy.argtypes = [vp]
+    L.ec_max_compressed_bytes.restype = sz
+    L.ec_max_compressed_bytes.argtypes = [vp]
+    L.ec_compress.restype = st
+    L.ec_compress.argtypes = [vp, ctypes.c_int64, vp, vp, sz, vp]
+    L.ec_decompress.restype = st
+    L.ec_decompress.argtypes = [vp, vp, sz, vp, vp]
+    L.ec_ratio.restype = st
+    L.ec_ratio.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_uint64),
+                           ctypes.POINTER(ctypes.c_double)]
+    L.ec_status_string.restype = ctypes.c_char_p
+    L.ec_status_string.argtypes = [st]
+    L.ec_debug_attach.restype = st
+    L.ec_debug_attach.argtypes = [vp, vp, vp, vp, vp]
+    L.ec_profile_enable.restype = st
+    L.ec_profile_enable.argtypes = [vp, st, ctypes.c_uint32]
+    L.ec_profile_read.restype = st
+    L.ec_profile_read.argtypes = [vp, st, ctypes.POINTER(ctypes.c_double),
+                                  ctypes.POINTER(ctypes.c_uint64)]
+    _lib = L
+    return L
+
+
+def declared_functions() -> list[str]:
+    """Names of the functions include/ec.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ec_[a-z_]+)\s*\(", text)))
+
+
+def status_string(status: int) -> str:
+    try:
+        return lib().ec_status_string(status).decode()
+    except ImportError:
+        return "status"
+
+
+def _check(status: int, what: str):
+    if status != EC_OK:
+        raise ECError(status, what)
+
+
+def _stream_handle(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _desc(T, B, D, P, eb_mode, eb, table_mult, schedule, debug_hash_bits, keep):
+    ebs = [float(v) for v in (eb if hasattr(eb, "__len__") else [eb])]
+    if len(ebs) == 1 and T > 1:
+        ebs = ebs * T
+    arr = (ctypes.c_float * len(ebs))(*ebs)
+    keep.append(arr)
+    mult = ctypes.POINTER(ctypes.c_float)()
+    if table_mult is not None:
+        m = (ctypes.c_float * len(table_mult))(*[float(v) for v in table_mult])
+        keep.append(m)
+        mult = ctypes.cast(m, ctypes.POINTER(ctypes.c_float))
+    sch = schedule or {}
+    s = _Schedule(int(sch.get("kind", SCHED_NONE)), int(sch.get("steps", 1)),
+                  float(sch.get("t0", 1000.0)), float(sch.get("k", 2.0)),
+                  int(sch.get("phase", 1)))
+    return _Desc(ABI_VERSION, T, B, D, P, int(eb_mode), ctypes.cast(arr, ctypes.POINTER(ctypes.c_float)),
+                 mult, s, CODER_BITPACK, int(debug_hash_bits), None, 0)
+
+
+def workspace_bytes(T, B, D, P=1, eb_mode=EB_ABS, eb=1e-4, table_mult=None, schedule=None,
+                    debug_hash_bits=0) -> int:
+    keep = []
+    d = _desc(T, B, D, P, eb_mode, eb, table_mult, schedule, debug_hash_bits, keep)
+    return int(lib().ec_workspace_bytes(ctypes.byref(d)))
+
+
+class Plan:
+    """A compression plan: shape, error-bound policy and a torch-allocated workspace.
+
+    schedule: None, {"kind": SCHED_INV_SQRT, "t0": 1000.0} or
+              {"kind": SCHED_STEP, "k": 2.0, "phase": 100, "steps": 4}.
+    """
+
+    def __init__(self, T: int, B: int, D: int, P: int = 1, eb_mode: int = EB_ABS, eb=1e-4,
+                 table_mult=None, schedule=None, debug_hash_bits: int = 0, device=None):
+        import torch
+        self.T, self.B, self.D, self.P = T, B, D, P
+        self._keep = []
+        self._desc = _desc(T, B, D, P, eb_mode, eb, table_mult, schedule, debug_hash_bits,
+                           self._keep)
+        L = lib()
+        nbytes = int(L.ec_workspace_bytes(ctypes.byref(self._desc)))
+        if nbytes == 0:
+            raise ECError(EC_ERR_INVALID, "ec_workspace_bytes")
+        self.device = torch.device(device or "cuda")
+        self.workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
+        base = self.workspace.data_ptr()
+        aligned = (base + 255) // 256 * 256
+        self._desc.d_workspace = aligned
+        self._desc.workspace_bytes = nbytes
+        h = ctypes.c_void_p()
+        _check(L.ec_plan(ctypes.byref(self._desc), ctypes.byref(h)), "ec_plan")
+        self._h = h
+        self.max_compressed_bytes = int(L.ec_max_compressed_bytes(h))
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().ec_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def empty_stream(self):
+        import torch
+        return torch.empty(self.max_compressed_bytes, dtype=torch.uint8, device=self.device)
+
+    def compress(self, x, out, iteration: int = 0, stream=None):
+        """Enqueue compression of fp32 x [T,B,D] into the uint8 tensor `out`."""
+        import torch
+        assert x.dtype == torch.float32 and x.is_contiguous() and x.numel() == self.T * self.B * self.D
+        assert out.dtype == torch.uint8 and out.is_contiguous()
+        _check(lib().ec_compress(self._h, int(iteration), x.data_ptr(), out.data_ptr(),
+                                 out.numel(), _stream_handle(stream)), "ec_compress")
+
+    def decompress(self, stream_bytes, y, stream=None):
+        """Enqueue decompression of the uint8 stream into fp32 y [T,B,D]."""
+        import torch
+        assert y.dtype == torch.float32 and y.is_contiguous() and y.numel() == self.T * self.B * self.D
+        assert stream_bytes.dtype == torch.uint8 and stream_bytes.is_contiguous()
+        _check(lib().ec_decompress(self._h, stream_bytes.data_ptr(), stream_bytes.numel(),
+                                   y.data_ptr(), _stream_handle(stream)), "ec_decompress")
+
+    def ratio(self, per_segment: bool = False, raise_on_error: bool = True):
+        """Wait for the plan's work; return (total CR, stream bytes[, per-segment CR], status)."""
+        cr = ctypes.c_double()
+        nb = ctypes.c_uint64()
+        per = (ctypes.c_double * (self.P * self.T))() if per_segment else None
+        st = lib().ec_ratio(self._h, ctypes.byref(cr), ctypes.byref(nb),
+                            ctypes.cast(per, ctypes.POINTER(ctypes.c_double)) if per else None)
+        if raise_on_error:
+            _check(st, "ec_ratio")
+        out = (cr.value, int(nb.value))
+        if per_segment:
+            out = out + (list(per),)
+        return out + (st,)
+
+    def debug_attach(self, codes=None, outlier=None, first=None, eb=None):
+        p = lambda t: t.data_ptr() if t is not None else None
+        _check(lib().ec_debug_attach(self._h, p(codes), p(outlier), p(first), p(eb)),
+               "ec_debug_attach")
+        self._dbg = (codes, outlier, first, eb)
+
+    def profile_enable(self, enable: bool = True, max_launches: int = 4096):
+        _check(lib().ec_profile_enable(self._h, int(enable), int(max_launches)), "ec_profile_enable")
+
+    def profile_read(self, kernel: int):
+        ms = ctypes.c_double()
+        n = ctypes.c_uint64()
+        _check(lib().ec_profile_read(self._h, int(kernel), ctypes.byref(ms), ctypes.byref(n)),
+               "ec_profile_read")
+        return ms.value, int(n.value)

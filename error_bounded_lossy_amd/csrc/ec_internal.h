@@ -1,0 +1,108 @@
+// ec_internal.h -- argument blocks shared by the host runtime and the gfx950
+// kernels.  Not part of the public ABI (include/ec.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ec {
+
+constexpr uint32_t kTileRows = 64;    // rows per tile record (one bitmap word)
+constexpr uint32_t kThreads = 256;    // threads per workgroup (4 wave64)
+constexpr uint32_t kMagic = 0x434C4245u;
+constexpr uint32_t kVersion = 1;
+constexpr uint32_t kCoderBitpack = 1;
+
+// Error codes the device stores into the host-visible status word.
+constexpr uint32_t kDevErrCorrupt = 3;
+constexpr uint32_t kDevErrTimeout = 4;
+
+// Host-visible report block (pinned, device-mapped host memory).
+struct Report {
+  uint64_t total_bytes;
+  uint32_t status;
+  uint32_t pad;
+  uint64_t seg_bytes[1];  // [nseg], allocated past the struct
+};
+
+struct Shape {
+  uint32_t T, B, D, P;
+  uint32_t nseg;         // P * T
+  uint32_t ntiles;       // scheduled tiles: sum over segments of max(ceil(rows/64), 1)
+  uint64_t base_bytes;   // stream header + chunk byte counts
+};
+
+// Workspace pointers.  "Constant" arrays are written once at plan time; the
+// dynamic region [dyn, dyn + dyn_words) is zeroed by the prep kernel of every
+// compress call.
+struct Work {
+  const float* eb_base;          // [T]
+  const float* mult;             // [T]
+  const uint32_t* seg_tile_base; // [nseg + 1] first scheduled tile of each segment
+  const uint64_t* hash_off;      // [nseg] first slot of each segment's hash table
+  const uint32_t* hash_log2;     // [nseg] log2 of each segment's slot count
+  float* range_part;             // [T][nbr][2] per-workgroup (min, max)
+  uint32_t nbr;                  // range workgroups per table
+  // dynamic
+  uint64_t* dyn;
+  uint64_t dyn_words;
+  uint32_t* ctrl;                // [0] tile ticket, [1] finished segments
+  uint64_t* seg_start;           // [nseg] absolute offset + 1 (0: not yet known)
+  uint64_t* seg_end;             // [nseg] absolute end offset + 1
+  uint64_t* chunk_start;         // [P] absolute offset + 1
+  uint32_t* seg_U;               // [nseg]
+  uint32_t* seg_nout;            // [nseg]
+  uint32_t* seg_done;            // [nseg] finished tiles
+  uint64_t* tile_status;         // [ntiles] look-back words
+  uint32_t* tile_inserted;       // [ntiles] rows inserted into the hash table
+  uint64_t* tile_rec;            // [ntiles] absolute record offset
+  uint64_t* hash;                // slots: (hash32 << 32) | (row + 1), 0 = empty
+};
+
+struct PrepArgs {
+  const float* x;
+  Shape sh;
+  Work w;
+  int rel;
+};
+
+struct EncArgs {
+  const float* x;
+  uint8_t* out;
+  uint64_t out_cap;
+  Shape sh;
+  Work w;
+  uint32_t eb_mode;
+  int64_t iter;
+  double sched;                  // iteration-wise factor, computed on the host
+  uint64_t hash_keep;            // mask applied to row hashes (tests weaken it)
+  Report* report;                // device pointer of the pinned report block
+  int32_t* dbg_codes;
+  uint8_t* dbg_outlier;
+  uint32_t* dbg_first;
+  float* dbg_eb;
+};
+
+struct DecArgs {
+  const uint8_t* in;
+  uint64_t cap;
+  float* y;
+  Shape sh;
+  const uint32_t* seg_tile_base;
+  Report* report;
+};
+
+// LDS bytes of the encode kernel for dimension D.
+inline size_t encode_lds_bytes(uint32_t D) {
+  size_t codes = ((size_t)2 * kTileRows * D + 15) / 16 * 16;
+  size_t fixed = kTileRows * (8 + 4 + 4 + 1) + 16;
+  size_t per_blk = (size_t)(D + 4) * (4 + 4 + 1) + 64;
+  return codes + fixed + per_blk;
+}
+
+hipError_t launch_prep(const PrepArgs& a, uint32_t grid, hipStream_t s);
+hipError_t launch_encode(const EncArgs& a, hipStream_t s);
+hipError_t launch_decode(const DecArgs& a, hipStream_t s);
+hipError_t set_encode_lds_limit(size_t bytes);
+
+}  // namespace ec

@@ -1,0 +1,482 @@
+// ec_runtime.cpp -- host side of the C ABI in include/ec.h: descriptor
+// validation, workspace layout, the error-bound policy's iteration factor
+// (arXiv 2407.04272, section III-C and Algorithm 1), kernel launches on the
+// caller's stream, the pinned report block, and opt-in launch profiling.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/ec.h"
+#include "ec_internal.h"
+
+namespace {
+
+uint64_t aup(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+struct Layout {
+  // byte offsets inside the workspace
+  uint64_t eb_base, mult, seg_tile_base, hash_off, hash_log2, range_part;
+  uint64_t dyn, ctrl, seg_start, seg_end, chunk_start, seg_U, seg_nout, seg_done;
+  uint64_t tile_status, tile_inserted, tile_rec, hash;
+  uint64_t dyn_bytes, total;
+  uint32_t nbr;
+  std::vector<uint32_t> seg_tile_base_v;
+  std::vector<uint64_t> hash_off_v;
+  std::vector<uint32_t> hash_log2_v;
+  ec::Shape sh;
+  uint64_t max_bytes;
+};
+
+uint32_t rows_of_chunk(uint32_t B, uint32_t P, uint32_t p) {
+  uint64_t a = (uint64_t)p * B / P, b = (uint64_t)(p + 1) * B / P;
+  return (uint32_t)(b - a);
+}
+
+int g_max_dim = -1;
+size_t g_lds_limit = 0;
+
+uint32_t device_max_dim() {
+  if (g_max_dim >= 0) return (uint32_t)g_max_dim;
+  int dev = 0;
+  size_t limit = 65536;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess &&
+        v > 0)
+      limit = (size_t)v;
+  }
+  g_lds_limit = limit;
+  uint32_t d = 1;
+  while (d < 4096 && ec::encode_lds_bytes(d + 1) + 512 <= limit) d++;
+  g_max_dim = (int)d;
+  return d;
+}
+
+bool finite_pos(float v) { return std::isfinite(v) && v > 0.0f; }
+
+// Validates the descriptor (host pointers only) and computes the layout.
+ec_status make_layout(const ec_plan_desc* d, Layout* L) {
+  if (!d || d->abi_version != EC_ABI_VERSION) return EC_ERR_INVALID;
+  const uint32_t T = d->num_tables, B = d->rows, D = d->dim, P = d->num_chunks;
+  if (T < 1 || D < 1 || P < 1 || !d->eb) return EC_ERR_INVALID;
+  if (d->eb_mode != EC_EB_ABS && d->eb_mode != EC_EB_REL_RANGE) return EC_ERR_INVALID;
+  if (d->coder != EC_CODER_BITPACK) return EC_ERR_UNSUPPORTED;
+  if (d->debug_hash_bits > 64) return EC_ERR_INVALID;
+  const ec_schedule& s = d->sched;
+  if (s.kind == EC_SCHED_INV_SQRT) {
+    if (!(s.t0 > 0.0) || !std::isfinite(s.t0)) return EC_ERR_INVALID;
+  } else if (s.kind == EC_SCHED_STEP) {
+    if (s.phase < 1 || s.steps < 1 || !(s.k >= 1.0) || !std::isfinite(s.k)) return EC_ERR_INVALID;
+  } else if (s.kind != EC_SCHED_NONE) {
+    return EC_ERR_INVALID;
+  }
+  for (uint32_t t = 0; t < T; t++) {
+    float e = d->eb[t];
+    if (d->eb_mode == EC_EB_ABS) {
+      if (!finite_pos(e) || !std::isfinite(e + e)) return EC_ERR_INVALID;
+    } else if (!finite_pos(e)) {
+      return EC_ERR_INVALID;
+    }
+    if (d->table_mult && !finite_pos(d->table_mult[t])) return EC_ERR_INVALID;
+  }
+  if (D > device_max_dim()) return EC_ERR_UNSUPPORTED;
+  if ((uint64_t)T * B * D >= (1ull << 40)) return EC_ERR_UNSUPPORTED;
+
+  const uint64_t nseg = (uint64_t)P * T;
+  L->seg_tile_base_v.assign(nseg + 1, 0);
+  L->hash_off_v.assign(nseg, 0);
+  L->hash_log2_v.assign(nseg, 0);
+  uint64_t tiles = 0, slots = 0, maxb = 64 + aup(8ull * P, 16);
+  for (uint32_t p = 0; p < P; p++) {
+    const uint32_t rows = rows_of_chunk(B, P, p);
+    const uint32_t nt = (rows + 63) / 64;
+    // per-segment stream size must fit the u32 tile directory
+    uint64_t seg_max = 32 + aup(4ull * nt, 16) + 16ull * nt + 4ull * rows * D + 16ull * nt;
+    if (seg_max >= (1ull << 31)) return EC_ERR_UNSUPPORTED;
+    uint32_t lg = 6;
+    while ((1ull << lg) < 2ull * rows) lg++;
+    uint64_t seg_bytes = 32 + aup(4ull * nt, 16);
+    for (uint32_t k = 0; k < nt; k++) {
+      uint32_t n = rows - 64 * k < 64 ? rows - 64 * k : 64;
+      seg_bytes += 16 + aup(4ull * n * D, 16);
+    }
+    maxb += aup(8ull * T, 16) + (uint64_t)T * seg_bytes;
+    for (uint32_t t = 0; t < T; t++) {
+      uint64_t sidx = (uint64_t)p * T + t;
+      L->seg_tile_base_v[sidx] = (uint32_t)tiles;
+      L->hash_off_v[sidx] = slots;
+      L->hash_log2_v[sidx] = lg;
+      tiles += nt ? nt : 1;
+      slots += 1ull << lg;
+    }
+  }
+  if (tiles >= (1ull << 31)) return EC_ERR_UNSUPPORTED;
+  L->seg_tile_base_v[nseg] = (uint32_t)tiles;
+  L->sh = {T, B, D, P, (uint32_t)nseg, (uint32_t)tiles, 64 + aup(8ull * P, 16)};
+  L->max_bytes = maxb;
+
+  const uint64_t nel = (uint64_t)B * D;
+  uint64_t nbr = (nel + 32767) / 32768;
+  L->nbr = (uint32_t)(nbr < 1 ? 1 : (nbr > 256 ? 256 : nbr));
+
+  uint64_t o = 0;
+  auto take = [&](uint64_t bytes) {
+    uint64_t at = aup(o, 256);
+    o = at + bytes;
+    return at;
+  };
+  L->eb_base = take(4ull * T);
+  L->mult = take(4ull * T);
+  L->seg_tile_base = take(4ull * (nseg + 1));
+  L->hash_off = take(8ull * nseg);
+  L->hash_log2 = take(4ull * nseg);
+  L->range_part = take(8ull * T * L->nbr);
+  o = aup(o, 256);
+  L->dyn = o;
+  L->ctrl = take(16);
+  L->seg_start = take(8ull * nseg);
+  L->seg_end = take(8ull * nseg);
+  L->chunk_start = take(8ull * P);
+  L->seg_U = take(4ull * nseg);
+  L->seg_nout = take(4ull * nseg);
+  L->seg_done = take(4ull * nseg);
+  L->tile_status = take(8ull * tiles);
+  L->tile_inserted = take(4ull * tiles);
+  L->tile_rec = take(8ull * tiles);
+  L->hash = take(8ull * slots);
+  o = aup(o, 256);
+  L->dyn_bytes = o - L->dyn;
+  L->total = o;
+  return EC_OK;
+}
+
+double schedule_factor(const ec_schedule& s, int64_t iter) {
+  int64_t i = iter < 0 ? 0 : iter;
+  if (s.kind == EC_SCHED_INV_SQRT) return std::pow(1.0 + (double)i / s.t0, -0.5);
+  if (s.kind == EC_SCHED_STEP) {
+    int64_t m = i < s.phase ? i : s.phase;
+    int64_t stair = (int64_t)s.steps * m / s.phase;
+    double drop = ((s.k - 1.0) * (double)stair) / (double)s.steps;
+    return s.k - drop;
+  }
+  return 1.0;
+}
+
+struct ProfRec {
+  int kernel;
+  hipEvent_t a, b;
+};
+
+}  // namespace
+
+struct ec_plan_s {
+  Layout L;
+  ec_plan_desc desc;
+  std::vector<float> eb, mult;
+  uint8_t* ws = nullptr;
+  ec::Work work{};
+  ec::Report* report_host = nullptr;
+  ec::Report* report_dev = nullptr;
+  hipEvent_t done = nullptr;
+  bool have_done = false;
+  int32_t* dbg_codes = nullptr;
+  uint8_t* dbg_outlier = nullptr;
+  uint32_t* dbg_first = nullptr;
+  float* dbg_eb = nullptr;
+  bool prof_on = false;
+  std::vector<hipEvent_t> prof_pool;
+  std::vector<ProfRec> prof_recs;
+  size_t prof_next = 0;
+  uint64_t prof_dropped = 0;
+};
+
+namespace {
+
+bool capturing(hipStream_t s) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &st) != hipSuccess) return false;
+  return st != hipStreamCaptureStatusNone;
+}
+
+template <typename F>
+ec_status profiled(ec_plan_s* pl, int kernel, hipStream_t s, F&& launch) {
+  hipEvent_t a = nullptr, b = nullptr;
+  if (pl->prof_on && pl->prof_next + 2 <= pl->prof_pool.size()) {
+    a = pl->prof_pool[pl->prof_next++];
+    b = pl->prof_pool[pl->prof_next++];
+    if (hipEventRecord(a, s) != hipSuccess) return EC_ERR_DEVICE;
+  } else if (pl->prof_on) {
+    pl->prof_dropped++;
+  }
+  if (launch() != hipSuccess) return EC_ERR_DEVICE;
+  if (a) {
+    if (hipEventRecord(b, s) != hipSuccess) return EC_ERR_DEVICE;
+    pl->prof_recs.push_back({kernel, a, b});
+  }
+  return EC_OK;
+}
+
+void record_done(ec_plan_s* pl, hipStream_t s) {
+  if (capturing(s)) return;
+  if (hipEventRecord(pl->done, s) == hipSuccess) pl->have_done = true;
+}
+
+}  // namespace
+
+extern "C" {
+
+uint32_t ec_max_dim(void) { return device_max_dim(); }
+
+size_t ec_workspace_bytes(const ec_plan_desc* desc) {
+  Layout L;
+  if (make_layout(desc, &L) != EC_OK) return 0;
+  return (size_t)L.total;
+}
+
+ec_status ec_plan(const ec_plan_desc* desc, ec_plan_t* out) {
+  if (!out) return EC_ERR_INVALID;
+  *out = nullptr;
+  ec_plan_s* pl = new (std::nothrow) ec_plan_s();
+  if (!pl) return EC_ERR_OOM;
+  ec_status st = make_layout(desc, &pl->L);
+  if (st != EC_OK) {
+    delete pl;
+    return st;
+  }
+  const Layout& L = pl->L;
+  if (!desc->d_workspace || desc->workspace_bytes < L.total ||
+      ((uintptr_t)desc->d_workspace & 255u)) {
+    delete pl;
+    return desc->d_workspace && desc->workspace_bytes < L.total ? EC_ERR_CAPACITY
+                                                                 : EC_ERR_INVALID;
+  }
+  pl->desc = *desc;
+  const uint32_t T = L.sh.T;
+  pl->eb.assign(desc->eb, desc->eb + T);
+  pl->mult.assign(T, 1.0f);
+  if (desc->table_mult) pl->mult.assign(desc->table_mult, desc->table_mult + T);
+  pl->desc.eb = pl->eb.data();
+  pl->desc.table_mult = nullptr;
+  pl->ws = static_cast<uint8_t*>(desc->d_workspace);
+
+  size_t lds = ec::encode_lds_bytes(L.sh.D);
+  if (lds > 65536 && ec::set_encode_lds_limit(lds) != hipSuccess) {
+    delete pl;
+    return EC_ERR_UNSUPPORTED;
+  }
+  size_t rep_bytes = sizeof(ec::Report) + 8ull * L.sh.nseg;
+  void* hp = nullptr;
+  if (hipHostMalloc(&hp, rep_bytes, hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess) {
+    delete pl;
+    return EC_ERR_DEVICE;
+  }
+  std::memset(hp, 0, rep_bytes);
+  pl->report_host = static_cast<ec::Report*>(hp);
+  void* dp = nullptr;
+  if (hipHostGetDevicePointer(&dp, hp, 0) != hipSuccess ||
+      hipEventCreateWithFlags(&pl->done, hipEventDisableTiming) != hipSuccess) {
+    (void)hipHostFree(hp);
+    delete pl;
+    return EC_ERR_DEVICE;
+  }
+  pl->report_dev = static_cast<ec::Report*>(dp);
+
+  // constants into the workspace (blocking copies, plan time only)
+  uint8_t* ws = pl->ws;
+  bool ok = hipMemcpy(ws + L.eb_base, pl->eb.data(), 4ull * T, hipMemcpyHostToDevice) == hipSuccess;
+  ok = ok && hipMemcpy(ws + L.mult, pl->mult.data(), 4ull * T, hipMemcpyHostToDevice) == hipSuccess;
+  ok = ok && hipMemcpy(ws + L.seg_tile_base, L.seg_tile_base_v.data(),
+                       4ull * L.seg_tile_base_v.size(), hipMemcpyHostToDevice) == hipSuccess;
+  ok = ok && hipMemcpy(ws + L.hash_off, L.hash_off_v.data(), 8ull * L.hash_off_v.size(),
+                       hipMemcpyHostToDevice) == hipSuccess;
+  ok = ok && hipMemcpy(ws + L.hash_log2, L.hash_log2_v.data(), 4ull * L.hash_log2_v.size(),
+                       hipMemcpyHostToDevice) == hipSuccess;
+  if (!ok) {
+    (void)hipEventDestroy(pl->done);
+    (void)hipHostFree(hp);
+    delete pl;
+    return EC_ERR_DEVICE;
+  }
+  ec::Work& w = pl->work;
+  w.eb_base = reinterpret_cast<const float*>(ws + L.eb_base);
+  w.mult = reinterpret_cast<const float*>(ws + L.mult);
+  w.seg_tile_base = reinterpret_cast<const uint32_t*>(ws + L.seg_tile_base);
+  w.hash_off = reinterpret_cast<const uint64_t*>(ws + L.hash_off);
+  w.hash_log2 = reinterpret_cast<const uint32_t*>(ws + L.hash_log2);
+  w.range_part = reinterpret_cast<float*>(ws + L.range_part);
+  w.nbr = L.nbr;
+  w.dyn = reinterpret_cast<uint64_t*>(ws + L.dyn);
+  w.dyn_words = L.dyn_bytes / 8;
+  w.ctrl = reinterpret_cast<uint32_t*>(ws + L.ctrl);
+  w.seg_start = reinterpret_cast<uint64_t*>(ws + L.seg_start);
+  w.seg_end = reinterpret_cast<uint64_t*>(ws + L.seg_end);
+  w.chunk_start = reinterpret_cast<uint64_t*>(ws + L.chunk_start);
+  w.seg_U = reinterpret_cast<uint32_t*>(ws + L.seg_U);
+  w.seg_nout = reinterpret_cast<uint32_t*>(ws + L.seg_nout);
+  w.seg_done = reinterpret_cast<uint32_t*>(ws + L.seg_done);
+  w.tile_status = reinterpret_cast<uint64_t*>(ws + L.tile_status);
+  w.tile_inserted = reinterpret_cast<uint32_t*>(ws + L.tile_inserted);
+  w.tile_rec = reinterpret_cast<uint64_t*>(ws + L.tile_rec);
+  w.hash = reinterpret_cast<uint64_t*>(ws + L.hash);
+  *out = pl;
+  return EC_OK;
+}
+
+ec_status ec_plan_destroy(ec_plan_t pl) {
+  if (!pl) return EC_ERR_INVALID;
+  if (pl->have_done) (void)hipEventSynchronize(pl->done);
+  for (hipEvent_t e : pl->prof_pool) (void)hipEventDestroy(e);
+  if (pl->done) (void)hipEventDestroy(pl->done);
+  if (pl->report_host) (void)hipHostFree(pl->report_host);
+  delete pl;
+  return EC_OK;
+}
+
+size_t ec_max_compressed_bytes(ec_plan_t pl) { return pl ? (size_t)pl->L.max_bytes : 0; }
+
+ec_status ec_compress(ec_plan_t pl, int64_t iter, const float* d_in, void* d_out, size_t out_cap,
+                      void* stream) {
+  if (!pl || !d_out) return EC_ERR_INVALID;
+  const ec::Shape& sh = pl->L.sh;
+  if (!d_in && (uint64_t)sh.B * sh.D > 0) return EC_ERR_INVALID;
+  if (((uintptr_t)d_in & 15u) || ((uintptr_t)d_out & 15u)) return EC_ERR_INVALID;
+  if (out_cap < pl->L.max_bytes) return EC_ERR_CAPACITY;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  ec::PrepArgs pa{d_in, sh, pl->work, pl->desc.eb_mode == EC_EB_REL_RANGE ? 1 : 0};
+  uint32_t grid;
+  if (pa.rel && sh.B > 0) {
+    grid = sh.T * pl->L.nbr;
+  } else {
+    pa.rel = 0;
+    uint64_t g = (pl->work.dyn_words + 1023) / 1024;
+    grid = (uint32_t)(g < 1 ? 1 : (g > 2048 ? 2048 : g));
+  }
+  ec_status st = profiled(pl, EC_KERNEL_PREP, s, [&] { return ec::launch_prep(pa, grid, s); });
+  if (st != EC_OK) return st;
+
+  ec::EncArgs ea{};
+  ea.x = d_in;
+  ea.out = static_cast<uint8_t*>(d_out);
+  ea.out_cap = out_cap;
+  ea.sh = sh;
+  ea.w = pl->work;
+  ea.eb_mode = (uint32_t)pl->desc.eb_mode;
+  ea.iter = iter;
+  ea.sched = schedule_factor(pl->desc.sched, iter);
+  uint32_t hb = pl->desc.debug_hash_bits;
+  ea.hash_keep = (hb == 0 || hb >= 64) ? ~0ull : ((1ull << hb) - 1ull);
+  ea.report = pl->report_dev;
+  ea.dbg_codes = pl->dbg_codes;
+  ea.dbg_outlier = pl->dbg_outlier;
+  ea.dbg_first = pl->dbg_first;
+  ea.dbg_eb = pl->dbg_eb;
+  st = profiled(pl, EC_KERNEL_ENCODE, s, [&] { return ec::launch_encode(ea, s); });
+  if (st != EC_OK) return st;
+  record_done(pl, s);
+  return EC_OK;
+}
+
+ec_status ec_decompress(ec_plan_t pl, const void* d_stream, size_t stream_cap, float* d_out,
+                        void* stream) {
+  if (!pl || !d_stream) return EC_ERR_INVALID;
+  const ec::Shape& sh = pl->L.sh;
+  if (!d_out && (uint64_t)sh.B * sh.D > 0) return EC_ERR_INVALID;
+  if (((uintptr_t)d_stream & 15u) || ((uintptr_t)d_out & 15u)) return EC_ERR_INVALID;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  ec::DecArgs da{};
+  da.in = static_cast<const uint8_t*>(d_stream);
+  da.cap = stream_cap;
+  da.y = d_out;
+  da.sh = sh;
+  da.seg_tile_base = pl->work.seg_tile_base;
+  da.report = pl->report_dev;
+  ec_status st = profiled(pl, EC_KERNEL_DECODE, s, [&] { return ec::launch_decode(da, s); });
+  if (st != EC_OK) return st;
+  record_done(pl, s);
+  return EC_OK;
+}
+
+ec_status ec_ratio(ec_plan_t pl, double* total_cr, uint64_t* compressed_bytes,
+                   double* per_segment_cr) {
+  if (!pl) return EC_ERR_INVALID;
+  if (pl->have_done && hipEventSynchronize(pl->done) != hipSuccess) return EC_ERR_DEVICE;
+  const ec::Shape& sh = pl->L.sh;
+  volatile ec::Report* r = pl->report_host;
+  uint64_t total = r->total_bytes;
+  uint32_t status = r->status;
+  r->status = 0;
+  if (compressed_bytes) *compressed_bytes = total;
+  if (total_cr) *total_cr = total ? (4.0 * sh.T * (double)sh.B * sh.D) / (double)total : 0.0;
+  if (per_segment_cr) {
+    for (uint32_t i = 0; i < sh.nseg; i++) {
+      uint32_t p = i / sh.T;
+      uint64_t b = r->seg_bytes[i];
+      per_segment_cr[i] = b ? 4.0 * rows_of_chunk(sh.B, sh.P, p) * (double)sh.D / (double)b : 0.0;
+    }
+  }
+  if (status == ec::kDevErrCorrupt) return EC_ERR_CORRUPT;
+  if (status != 0) return EC_ERR_DEVICE;
+  return EC_OK;
+}
+
+const char* ec_status_string(ec_status s) {
+  switch (s) {
+    case EC_OK: return "ok";
+    case EC_ERR_INVALID: return "invalid argument";
+    case EC_ERR_CAPACITY: return "capacity too small";
+    case EC_ERR_CORRUPT: return "corrupt stream";
+    case EC_ERR_DEVICE: return "device error";
+    case EC_ERR_OOM: return "out of host memory";
+    case EC_ERR_UNSUPPORTED: return "unsupported shape";
+  }
+  return "unknown status";
+}
+
+ec_status ec_debug_attach(ec_plan_t pl, int32_t* d_codes, uint8_t* d_outlier, uint32_t* d_first,
+                          float* d_eb) {
+  if (!pl) return EC_ERR_INVALID;
+  pl->dbg_codes = d_codes;
+  pl->dbg_outlier = d_outlier;
+  pl->dbg_first = d_first;
+  pl->dbg_eb = d_eb;
+  return EC_OK;
+}
+
+ec_status ec_profile_enable(ec_plan_t pl, int enable, uint32_t max_launches) {
+  if (!pl) return EC_ERR_INVALID;
+  if (pl->have_done) (void)hipEventSynchronize(pl->done);
+  pl->prof_recs.clear();
+  pl->prof_next = 0;
+  pl->prof_dropped = 0;
+  pl->prof_on = enable != 0;
+  size_t want = enable ? 2ull * max_launches : 0;
+  while (pl->prof_pool.size() < want) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return EC_ERR_DEVICE;
+    pl->prof_pool.push_back(e);
+  }
+  return EC_OK;
+}
+
+ec_status ec_profile_read(ec_plan_t pl, int kernel, double* total_ms, uint64_t* launches) {
+  if (!pl || !total_ms || !launches) return EC_ERR_INVALID;
+  double sum = 0.0;
+  uint64_t cnt = 0;
+  for (const ProfRec& r : pl->prof_recs) {
+    if (r.kernel != kernel) continue;
+    if (hipEventSynchronize(r.b) != hipSuccess) return EC_ERR_DEVICE;
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return EC_ERR_DEVICE;
+    sum += ms;
+    cnt++;
+  }
+  *total_ms = sum;
+  *launches = cnt;
+  return EC_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,170 @@
+/*
+ * ec.h -- C ABI of the MI355X (gfx950) error-bounded lossy compressor for
+ * DLRM embedding traffic.
+ *
+ * The method is the one of arXiv 2407.04272, "Accelerating Communication in
+ * Deep Learning Recommendation Model Training with Dual-Level Adaptive Lossy
+ * Compression":
+ *   - section I and III-D: an error-bounded lossy compressor applied to the
+ *     embedding lookups (forward) and their gradients (backward) just before
+ *     and after the all-to-all; every reconstructed element x^ satisfies
+ *     |x - x^| <= eb for the error bound eb of its table;
+ *   - section III-D: a quantization encoder (q = round(x / 2eb)) followed by
+ *     a lossless encoder; repeated (homogenized) embedding vectors are
+ *     stored once (the vector-based LZ idea) and the codes of the remaining
+ *     vectors are bit-plane packed per 64-element block;
+ *   - section III-C / Algorithm 1: the eb of table t at iteration i is the
+ *     configured table eb (optionally scaled by the table's value range and by
+ *     a per-table class multiplier) times an iteration-wise decay factor;
+ *   - section III-A stages 1-4 and III-E "Buffer Optimization" (Fig. 7): all
+ *     tables of all destination chunks are written by one pass into ONE
+ *     contiguous stream; chunk p's bytes are one slice whose size is in the
+ *     stream header (the metadata of the variable-size all-to-all).
+ *
+ * Conventions
+ *   - Input x is fp32 [T][B][D], row-major, in device memory.  Chunk p holds
+ *     rows [floor(p*B/P), floor((p+1)*B/P)) of every table; a (chunk, table)
+ *     pair is a "segment", the unit that repeated rows are detected in.
+ *   - Device pointers (d_*) must be 16-byte aligned and stay valid until the
+ *     work enqueued on `stream` has finished.  `stream` is a hipStream_t
+ *     passed as void*; NULL means the default stream.
+ *   - The caller owns every device buffer (input, stream buffer, output,
+ *     workspace).  The plan owns only host memory (a copy of the descriptor
+ *     and a small pinned host block the device reports sizes into).
+ *   - ec_compress / ec_decompress enqueue kernels and return; they never
+ *     allocate, free or synchronize.  One plan serves one stream at a time;
+ *     separate plans are independent.
+ *   - Every entry point returns ec_status; nothing is printed and no C++
+ *     exception crosses the ABI.  Argument errors are detected on the host
+ *     before anything is enqueued.  Conditions found on the device (corrupt
+ *     stream, internal time-out) are sticky and returned by ec_ratio.
+ */
+#ifndef EC_H
+#define EC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EC_ABI_VERSION 1u
+
+typedef struct ec_plan_s* ec_plan_t;
+
+typedef enum {
+  EC_OK = 0,
+  EC_ERR_INVALID = 1,     /* bad argument or descriptor                      */
+  EC_ERR_CAPACITY = 2,    /* output or workspace smaller than required       */
+  EC_ERR_CORRUPT = 3,     /* stream failed validation on the device          */
+  EC_ERR_DEVICE = 4,      /* HIP error or device-side time-out               */
+  EC_ERR_OOM = 5,         /* host allocation failed                          */
+  EC_ERR_UNSUPPORTED = 6  /* shape beyond this build's limits (e.g. D > max) */
+} ec_status;
+
+typedef enum {
+  EC_EB_ABS = 0,       /* eb[t] is the absolute error bound                  */
+  EC_EB_REL_RANGE = 1  /* eb_t = eb[t] * (max - min) of this call's table t  */
+} ec_eb_mode;
+
+typedef enum {
+  EC_SCHED_NONE = 0,     /* factor 1                                         */
+  EC_SCHED_INV_SQRT = 1, /* (1 + i/t0)^(-1/2)                                */
+  EC_SCHED_STEP = 2      /* k - (k-1) * floor(steps*min(i,phase)/phase)/steps:
+                            staircase from k down to 1 (the pages' default
+                            step-wise decay, section III-C)                 */
+} ec_sched_kind;
+
+typedef enum { EC_CODER_BITPACK = 1 } ec_coder;
+
+/* Kernel ids for the profiling counters. */
+typedef enum { EC_KERNEL_PREP = 0, EC_KERNEL_ENCODE = 1, EC_KERNEL_DECODE = 2 } ec_kernel;
+
+typedef struct {
+  int32_t kind;   /* ec_sched_kind                  */
+  int32_t steps;  /* STEP: number of stairs (>= 1)  */
+  double t0;      /* INV_SQRT: > 0                  */
+  double k;       /* STEP: starting multiple (>= 1) */
+  int64_t phase;  /* STEP: decay-phase length (>= 1) */
+} ec_schedule;
+
+typedef struct {
+  uint32_t abi_version;     /* EC_ABI_VERSION                                  */
+  uint32_t num_tables;      /* T >= 1                                          */
+  uint32_t rows;            /* B >= 0 rows per table                           */
+  uint32_t dim;             /* 1 <= D <= ec_max_dim()                          */
+  uint32_t num_chunks;      /* P >= 1 destination chunks                       */
+  int32_t eb_mode;          /* ec_eb_mode                                      */
+  const float* eb;          /* host [T]; ABS: finite > 0 with 2*eb finite;
+                               REL: finite > 0.  Copied by ec_plan.            */
+  const float* table_mult;  /* host [T] finite > 0 class multipliers (the
+                               large/medium/small table classes of Algorithm 1)
+                               or NULL for 1.  Copied by ec_plan.             */
+  ec_schedule sched;        /* iteration-wise decay                            */
+  int32_t coder;            /* EC_CODER_BITPACK                                */
+  uint32_t debug_hash_bits; /* 0: normal.  1..32: keep only that many bits of
+                               the internal row hash (forces hash collisions;
+                               output bytes are unchanged).  Tests only.       */
+  void* d_workspace;        /* device, >= ec_workspace_bytes(desc) bytes, 256-B
+                               aligned; owned by the caller, used by the plan
+                               until ec_plan_destroy                           */
+  size_t workspace_bytes;
+} ec_plan_desc;
+
+/* Largest supported D on the current device (limited by LDS per workgroup). */
+uint32_t ec_max_dim(void);
+
+/* Workspace bytes the plan needs (0 if the descriptor is invalid). */
+size_t ec_workspace_bytes(const ec_plan_desc* desc);
+
+/* Validate the descriptor and build a plan.  Host work plus one blocking copy
+ * of the per-table constants into the workspace.  *out is NULL on failure. */
+ec_status ec_plan(const ec_plan_desc* desc, ec_plan_t* out);
+
+/* Release the plan's host resources (the workspace stays the caller's). */
+ec_status ec_plan_destroy(ec_plan_t plan);
+
+/* Upper bound of a compressed stream (every tile stored raw); 0 for NULL. */
+size_t ec_max_compressed_bytes(ec_plan_t plan);
+
+/* Compress d_in (fp32 [T][B][D]) at iteration `iter` into d_out (capacity
+ * out_cap >= ec_max_compressed_bytes).  The stream's size becomes known on the
+ * host through ec_ratio; on the device it is the u64 at byte 48 of d_out. */
+ec_status ec_compress(ec_plan_t plan, int64_t iter, const float* d_in, void* d_out,
+                      size_t out_cap, void* stream);
+
+/* Decompress a stream of this plan's shape (d_stream holds stream_cap readable
+ * bytes) into d_out (fp32 [T][B][D]).  Every field is validated on the device
+ * before use; a corrupt stream makes ec_ratio return EC_ERR_CORRUPT and leaves
+ * the affected rows zero. */
+ec_status ec_decompress(ec_plan_t plan, const void* d_stream, size_t stream_cap, float* d_out,
+                        void* stream);
+
+/* Wait for this plan's last enqueued call, then report the last compression:
+ * total_cr = 4*T*B*D / stream bytes (headers included), the stream bytes, and
+ * per_segment_cr[p*T + t] = 4*rows(p)*D / segment bytes (may be NULL).  Returns
+ * and clears the sticky device status. */
+ec_status ec_ratio(ec_plan_t plan, double* total_cr, uint64_t* compressed_bytes,
+                   double* per_segment_cr);
+
+const char* ec_status_string(ec_status s);
+
+/* Tests only: make subsequent ec_compress calls also write the quantization
+ * codes (int32 [T*B*D], 0 for outliers), outlier flags (u8 [T*B*D]), the
+ * first-occurrence segment row of every row (u32 [T*B]) and the eb of every
+ * segment (f32 [P*T], 0 when invalid).  NULL disables an output. */
+ec_status ec_debug_attach(ec_plan_t plan, int32_t* d_codes, uint8_t* d_outlier,
+                          uint32_t* d_first, float* d_eb);
+
+/* Profiling: when enabled, every kernel launch of the plan is bracketed by HIP
+ * events on the launch stream (at most `max_launches` launches are kept).
+ * ec_profile_read waits for them and returns the summed duration and count
+ * for one ec_kernel id; ec_profile_enable(plan, 0, 0) clears and disables. */
+ec_status ec_profile_enable(ec_plan_t plan, int enable, uint32_t max_launches);
+ec_status ec_profile_read(ec_plan_t plan, int kernel, double* total_ms, uint64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EC_H */

@@ -240,3 +240,24 @@ def decode(st: Stream, buf: np.ndarray):
                 outl[seg.t, r0 + r] = oo
                 y[seg.t, r0 + r] = vv
     return codes, outl, first, y
+
+
+def parse_segments(buf: np.ndarray):
+    """Segment headers only (no tile walk): list of Segment without tiles."""
+    buf = np.asarray(buf, dtype=np.uint8)
+    assert _u(buf, 0, 4) == 0x434C4245
+    T, B, D, P = (_u(buf, o, 4) for o in (8, 12, 16, 20))
+    chunk_bytes = [_u(buf, 64 + 8 * p, 8) for p in range(P)]
+    at = 64 + _a(8 * P, 16)
+    segs = []
+    for p in range(P):
+        c0 = at
+        for t in range(T):
+            s0 = c0 + _u(buf, c0 + 8 * t, 8)
+            segs.append(Segment(p, t, s0, _u(buf, s0, 4), _u(buf, s0 + 4, 4),
+                                float(np.frombuffer(bytes(buf[s0 + 8:s0 + 12]), np.float32)[0]),
+                                bool(_u(buf, s0 + 12, 4) & 1), _u(buf, s0 + 16, 4),
+                                _u(buf, s0 + 20, 4), _u(buf, s0 + 24, 8)))
+        at += chunk_bytes[p]
+    assert at == _u(buf, 48, 8)
+    return segs

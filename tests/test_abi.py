@@ -1,0 +1,75 @@
+"""Host-side checks of the C-ABI library (no GPU compute): it loads, exports
+every function include/ec.h declares, and rejects bad descriptors on the host."""
+import ctypes
+import math
+
+import pytest
+
+import error_bounded_lossy_amd as ec
+
+
+def test_library_exports_every_declared_symbol():
+    L = ec.lib()
+    names = ec.declared_functions()
+    assert {"ec_plan", "ec_compress", "ec_decompress", "ec_ratio"} <= set(names)
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_status_strings():
+    assert ec.status_string(ec.EC_OK) == "ok"
+    assert ec.status_string(ec.EC_ERR_CORRUPT) == "corrupt stream"
+    assert ec.status_string(99) == "unknown status"
+
+
+def test_workspace_sizing_and_descriptor_validation():
+    ok = ec.workspace_bytes(26, 8192, 128, 1, ec.EB_REL_RANGE, 0.005,
+                            schedule={"kind": ec.SCHED_INV_SQRT, "t0": 1000.0})
+    assert ok > 0 and ok % 256 == 0
+    # hash tables alone: 26 segments x 16384 slots x 8 bytes
+    assert ok > 26 * 16384 * 8
+    bad = [
+        dict(T=0, B=10, D=4),
+        dict(T=1, B=10, D=0),
+        dict(T=1, B=10, D=4, P=0),
+        dict(T=1, B=10, D=4, eb=0.0),
+        dict(T=1, B=10, D=4, eb=math.nan),
+        dict(T=1, B=10, D=4, eb=math.inf),
+        dict(T=1, B=10, D=4, eb=3e38),                     # 2*eb overflows
+        dict(T=1, B=10, D=4, eb_mode=1, eb=-0.1),
+        dict(T=1, B=10, D=4, eb_mode=7),
+        dict(T=1, B=10, D=4, table_mult=[0.0]),
+        dict(T=1, B=10, D=4, schedule={"kind": ec.SCHED_INV_SQRT, "t0": 0.0}),
+        dict(T=1, B=10, D=4, schedule={"kind": ec.SCHED_STEP, "phase": 0}),
+        dict(T=1, B=10, D=4, schedule={"kind": 9}),
+    ]
+    for kw in bad:
+        kw = dict(kw)
+        T, B, D = kw.pop("T"), kw.pop("B"), kw.pop("D")
+        assert ec.workspace_bytes(T, B, D, **kw) == 0, kw
+    # D beyond what one workgroup's LDS can stage is unsupported
+    assert ec.workspace_bytes(1, 10, 1 << 16) == 0
+
+
+def test_plan_rejects_bad_arguments_before_touching_the_device():
+    L = ec.lib()
+    keep = []
+    d = ec._desc(1, 10, 4, 1, ec.EB_ABS, 0.0, None, None, 0, keep)
+    h = ctypes.c_void_p()
+    assert L.ec_plan(ctypes.byref(d), ctypes.byref(h)) == ec.EC_ERR_INVALID
+    assert not h.value
+    assert L.ec_plan(None, ctypes.byref(h)) == ec.EC_ERR_INVALID
+    assert L.ec_compress(None, 0, None, None, 0, None) == ec.EC_ERR_INVALID
+    assert L.ec_decompress(None, None, 0, None, None) == ec.EC_ERR_INVALID
+    assert L.ec_ratio(None, None, None, None) == ec.EC_ERR_INVALID
+    assert L.ec_max_compressed_bytes(None) == 0
+    # a valid descriptor without a workspace is rejected on the host
+    d = ec._desc(1, 10, 4, 1, ec.EB_ABS, 1e-3, None, None, 0, keep)
+    assert L.ec_plan(ctypes.byref(d), ctypes.byref(h)) == ec.EC_ERR_INVALID
+
+
+def test_binding_has_no_fallback(monkeypatch, tmp_path):
+    monkeypatch.setattr(ec, "_lib", None)
+    monkeypatch.setattr(ec, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        ec.lib()

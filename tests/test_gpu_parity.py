@@ -1,0 +1,223 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Streams must match byte for byte (which fixes codes, first-occurrence maps and
+every packed bit), the debug outputs (codes, outlier flags, first occurrences,
+segment eb) must match exactly, and the decompressed tensor must be bitwise
+identical to the oracle's reconstruction (hence within eb of the input)."""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import error_bounded_lossy_amd as ec  # noqa: E402
+import oracle as O  # noqa: E402
+import streamfmt as SF  # noqa: E402
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def make_cfg(T, B, D, P=1, eb_mode=0, eb=(1e-3,), mult=None, sched=None):
+    sched = sched or {}
+    return O.Config(T=T, B=B, D=D, P=P, eb_mode=eb_mode, eb=tuple(eb), table_mult=mult,
+                    sched_kind=sched.get("kind", 0), sched_t0=sched.get("t0", 1000.0),
+                    sched_k=sched.get("k", 2.0), sched_phase=sched.get("phase", 1),
+                    sched_steps=sched.get("steps", 1))
+
+
+def run_gpu(cfg, x_np, it=0, hash_bits=0, debug=True, sched=None):
+    T, B, D, P = cfg.T, cfg.B, cfg.D, cfg.P
+    plan = ec.Plan(T, B, D, P, cfg.eb_mode, list(cfg.eb) if len(cfg.eb) > 1 else cfg.eb[0],
+                   table_mult=cfg.table_mult, schedule=sched, debug_hash_bits=hash_bits)
+    x = torch.from_numpy(np.ascontiguousarray(x_np, np.float32)).cuda()
+    out = plan.empty_stream()
+    dbg = None
+    if debug:
+        dbg = (torch.full((T * B * D,), -7, dtype=torch.int32, device="cuda"),
+               torch.full((T * B * D,), 9, dtype=torch.uint8, device="cuda"),
+               torch.full((T * B,), 0xFFFF, dtype=torch.int32, device="cuda"),
+               torch.full((P * T,), -1.0, dtype=torch.float32, device="cuda"))
+        plan.debug_attach(*dbg)
+    plan.compress(x, out, it)
+    cr, nbytes, per, st = plan.ratio(per_segment=True)
+    stream = out[:nbytes].cpu().numpy()
+    y = torch.full_like(x, float("nan"))
+    plan.decompress(out[:nbytes], y)
+    plan.ratio()
+    res = dict(stream=stream, y=y.cpu().numpy(), cr=cr, per=per, plan=plan, out=out, x=x)
+    if debug:
+        res.update(codes=dbg[0].cpu().numpy().reshape(T, B, D),
+                   outlier=dbg[1].cpu().numpy().reshape(T, B, D),
+                   first=dbg[2].cpu().numpy().view(np.uint32).reshape(T, B),
+                   eb=dbg[3].cpu().numpy())
+    return res
+
+
+def assert_parity(cfg, x, it=0, hash_bits=0, sched=None, label=""):
+    say(f"[parity] {label} T={cfg.T} B={cfg.B} D={cfg.D} P={cfg.P} mode={cfg.eb_mode} "
+        f"it={it} hash_bits={hash_bits}")
+    ref = O.compress(cfg, it, x)
+    yo = O.decompress(cfg, ref.stream)
+    g = run_gpu(cfg, x, it, hash_bits, sched=sched)
+    np.testing.assert_array_equal(g["eb"], ref.eb)
+    np.testing.assert_array_equal(g["codes"], ref.codes)
+    np.testing.assert_array_equal(g["outlier"], ref.outlier)
+    np.testing.assert_array_equal(g["first"], ref.first)
+    assert g["stream"].size == ref.stream.size
+    if not np.array_equal(g["stream"], ref.stream):
+        bad = np.nonzero(g["stream"] != ref.stream)[0]
+        raise AssertionError(f"stream differs at {bad.size} bytes, first {bad[:8]}")
+    np.testing.assert_array_equal(g["y"].view(np.uint32), yo.view(np.uint32))
+    assert g["cr"] == pytest.approx(x.nbytes / ref.stream.size if x.size else 0.0, rel=1e-12) \
+        or x.size == 0
+    return g, ref
+
+
+def dup_rows(rng, T, B, D, scale=0.1, frac_unique=0.4):
+    base = rng.normal(0, scale, (T, max(1, int(B * frac_unique) + 1), D)).astype(np.float32)
+    idx = rng.integers(0, base.shape[1], (T, B))
+    return np.take_along_axis(base, idx[:, :, None], axis=1).astype(np.float32)
+
+
+SHAPES = [(1, 1, 1, 1), (1, 63, 3, 1), (2, 64, 16, 1), (3, 65, 64, 2), (2, 130, 128, 3),
+          (1, 200, 5, 4), (2, 3, 8, 5), (1, 129, 256, 1), (4, 257, 32, 1), (2, 1000, 100, 1),
+          (1, 4096, 128, 1)]
+
+
+@pytest.mark.parametrize("T,B,D,P", SHAPES)
+def test_shapes_rel(T, B, D, P):
+    rng = np.random.default_rng(T * 7919 + B * 31 + D * 3 + P)
+    x = dup_rows(rng, T, B, D)
+    assert_parity(make_cfg(T, B, D, P, eb_mode=1, eb=(0.01,)), x, label="rel")
+
+
+@pytest.mark.parametrize("T,B,D,P", SHAPES[:8])
+def test_shapes_abs_schedule(T, B, D, P):
+    rng = np.random.default_rng(100 + T * 7919 + B * 31 + D * 3 + P)
+    x = dup_rows(rng, T, B, D, scale=0.05)
+    sched = {"kind": ec.SCHED_STEP, "k": 2.0, "phase": 10, "steps": 4}
+    cfg = make_cfg(T, B, D, P, eb_mode=0, eb=[1e-3 * (1 + t) for t in range(T)],
+                   mult=[1.0 + 0.5 * t for t in range(T)], sched=sched)
+    assert_parity(cfg, x, it=5, sched=sched, label="abs+step")
+
+
+def test_empty_batch():
+    cfg = make_cfg(2, 0, 8, 1, eb_mode=1, eb=(0.01,))
+    assert_parity(cfg, np.zeros((2, 0, 8), np.float32), label="B=0")
+
+
+def test_more_chunks_than_rows():
+    rng = np.random.default_rng(5)
+    x = dup_rows(rng, 2, 3, 8)
+    assert_parity(make_cfg(2, 3, 8, 7, eb_mode=0, eb=(1e-2,)), x, label="P>B")
+
+
+def test_special_values_and_raw_segments():
+    rng = np.random.default_rng(7)
+    T, B, D = 4, 70, 8
+    x = rng.normal(0, 1, (T, B, D)).astype(np.float32)
+    x[0, 3, 2] = np.nan
+    x[0, 4, 1] = np.inf
+    x[0, 5, 0] = -np.inf
+    x[0, 6, 3] = -0.0
+    x[0, 7] = np.float32(np.uint32(0x7FC00123).view(np.float32))
+    x[0, 40] = x[0, 7]
+    x[1] = np.nan
+    x[2] = 0.25
+    x[3] = rng.normal(0, 1e6, (B, D)).astype(np.float32)
+    assert_parity(make_cfg(T, B, D, eb_mode=1, eb=(0.01,)), x, label="special")
+
+
+def test_raw_tiles_and_references_into_them():
+    rng = np.random.default_rng(9)
+    B, D = 200, 32
+    x = np.zeros((1, B, D), np.float32)
+    x[0, :64] = rng.normal(0, 1, (64, D)) * np.float32(10.0) ** rng.integers(-3, 4, (64, D))
+    x[0, 64:] = rng.normal(0, 0.01, (B - 64, D))
+    x[0, 100] = x[0, 3]
+    x[0, 150] = x[0, 10]
+    g, ref = assert_parity(make_cfg(1, B, D, eb=(1e-3,)), x, label="raw-refs")
+    assert SF.parse(ref.stream).segments[0].tiles[0].mode == 0
+
+
+def test_eb_to_zero_is_exact():
+    rng = np.random.default_rng(8)
+    x = rng.integers(-1000, 1000, (2, 100, 16)).astype(np.float32)
+    g, _ = assert_parity(make_cfg(2, 100, 16, eb=(1e-30,)), x, label="eb->0")
+    np.testing.assert_array_equal(g["y"], x)
+
+
+@pytest.mark.parametrize("bits", [1, 4, 12])
+def test_weak_hash_gives_identical_bytes(bits):
+    rng = np.random.default_rng(11 + bits)
+    x = dup_rows(rng, 2, 700, 24, frac_unique=0.3)
+    assert_parity(make_cfg(2, 700, 24, eb_mode=1, eb=(0.02,)), x, hash_bits=bits,
+                  label=f"weak-hash-{bits}")
+
+
+def test_determinism_across_runs():
+    rng = np.random.default_rng(12)
+    x = dup_rows(rng, 3, 3000, 64, frac_unique=0.2)
+    cfg = make_cfg(3, 3000, 64, eb_mode=1, eb=(0.01,))
+    first = run_gpu(cfg, x, debug=False)["stream"]
+    for _ in range(3):
+        assert np.array_equal(run_gpu(cfg, x, debug=False)["stream"], first)
+
+
+def test_per_segment_ratio_and_chunk_sizes():
+    rng = np.random.default_rng(13)
+    x = dup_rows(rng, 3, 500, 32)
+    cfg = make_cfg(3, 500, 32, P=4, eb_mode=1, eb=(0.01,))
+    g, ref = assert_parity(cfg, x, label="ratio")
+    st = SF.parse(ref.stream)
+    for seg in st.segments:
+        rows = (seg.p + 1) * 500 // 4 - seg.p * 500 // 4
+        assert g["per"][seg.p * 3 + seg.t] == pytest.approx(4 * rows * 32 / seg.nbytes)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_workloads_full_size_sampled_tables(name):
+    """Full-size batch on the GPU (the launch the benchmark times); the oracle
+    recomputes two sampled tables, whose segment bytes and reconstruction must
+    match the GPU stream exactly."""
+    import synth
+    say(f"[workload] {name} full size")
+    w = synth.workload(name, iteration=3, device="cuda")
+    T, B, D = w.shape
+    sched = {"kind": w.sched_kind, "t0": w.sched_t0} if w.sched_kind else None
+    plan = ec.Plan(T, B, D, 1, w.eb_mode, w.eb, schedule=sched)
+    out = plan.empty_stream()
+    plan.compress(w.x, out, w.iteration)
+    cr, nbytes, per, _ = plan.ratio(per_segment=True)
+    y = torch.empty_like(w.x)
+    plan.decompress(out[:nbytes], y)
+    plan.ratio()
+    gst = out[:nbytes].cpu().numpy()
+    gsegs = SF.parse_segments(gst)
+    picks = [0, T - 1] if T > 1 else [0]
+    xs = w.x[picks].cpu().numpy()
+    cfg = make_cfg(len(picks), B, D, 1, eb_mode=w.eb_mode, eb=tuple(w.eb[:len(picks)]),
+                   sched={"kind": w.sched_kind, "t0": w.sched_t0})
+    ref = O.compress(cfg, w.iteration, xs)
+    rsegs = SF.parse_segments(ref.stream)
+    for j, t in enumerate(picks):
+        gs, rs = gsegs[t], rsegs[j]
+        assert gs.nbytes == rs.nbytes
+        assert np.array_equal(gst[gs.offset:gs.offset + gs.nbytes],
+                              ref.stream[rs.offset:rs.offset + rs.nbytes])
+    yo = O.decompress(cfg, ref.stream)
+    yg = y[picks].cpu().numpy()
+    np.testing.assert_array_equal(yg.view(np.uint32), yo.view(np.uint32))
+    # the bound on every element of the whole batch
+    xg = w.x
+    ebs = torch.tensor([s.eb for s in gsegs], device="cuda").view(T, 1, 1)
+    fin = torch.isfinite(xg)
+    err = (xg.double() - y.double()).abs()
+    assert bool((err[fin] <= ebs.expand_as(xg).double()[fin]).all())
+    say(f"[workload] {name} CR={cr:.3f}")
