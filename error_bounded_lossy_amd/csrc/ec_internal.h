@@ -30,6 +30,7 @@ struct Shape {
   uint32_t nseg;         // P * T
   uint32_t ntiles;       // scheduled tiles: sum over segments of max(ceil(rows/64), 1)
   uint64_t base_bytes;   // stream header + chunk byte counts
+  uint32_t tiles_per_seg;  // scheduled tiles of every segment when all are equal, else 0
 };
 
 // Workspace pointers.  "Constant" arrays are written once at plan time; the
@@ -46,16 +47,15 @@ struct Work {
   // dynamic
   uint64_t* dyn;
   uint64_t dyn_words;
-  uint32_t* ctrl;                // [0] tile ticket, [1] finished segments
   uint64_t* seg_start;           // [nseg] absolute offset + 1 (0: not yet known)
   uint64_t* seg_end;             // [nseg] absolute end offset + 1
   uint64_t* chunk_start;         // [P] absolute offset + 1
-  uint32_t* seg_U;               // [nseg]
-  uint32_t* seg_nout;            // [nseg]
-  uint32_t* seg_done;            // [nseg] finished tiles
+  uint32_t* seg_fin;             // [nseg] segment header written
   uint64_t* tile_status;         // [ntiles] look-back words
   uint32_t* tile_inserted;       // [ntiles] rows inserted into the hash table
-  uint64_t* tile_rec;            // [ntiles] absolute record offset
+  uint64_t* tile_rec;            // [ntiles] absolute record offset + 1 (record written)
+  uint32_t* tile_U;              // [ntiles] first occurrences in the tile
+  uint32_t* tile_nout;           // [ntiles] outliers stored by the tile
   uint64_t* hash;                // slots: (hash32 << 32) | (row + 1), 0 = empty
 };
 
@@ -98,6 +98,13 @@ inline size_t encode_lds_bytes(uint32_t D) {
   size_t fixed = kTileRows * (8 + 4 + 4 + 1) + 16;
   size_t per_blk = (size_t)(D + 4) * (4 + 4 + 1) + 64;
   return codes + fixed + per_blk;
+}
+
+// LDS bytes of the decode kernel for dimension D: staged bit planes (at most
+// 12 per 64-element block), block offsets, widths and up to 256 outliers.
+inline size_t decode_lds_bytes(uint32_t D) {
+  size_t planes = 8ull * (12ull * D < 6144 ? 12ull * D : 6144);
+  return planes + 4ull * (D + 8) + ((D + 8 + 15) / 16) * 16 + 8ull * 256;
 }
 
 hipError_t launch_prep(const PrepArgs& a, uint32_t grid, hipStream_t s);

@@ -84,20 +84,29 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
   return v;
 }
 
-__device__ __forceinline__ uint64_t ld_acq64(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t ld_acq32(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t ld_rlx64(const uint64_t* p) {
+// Cross-workgroup communication uses only agent-scope RELAXED atomics (their
+// values are coherent across the XCDs) plus workgroup-scope fences, which only
+// wait for this wave's own memory operations.  Agent-scope acquire/release
+// would write back or invalidate a whole XCD L2 on every call.
+__device__ __forceinline__ void fence_wg() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup"); }
+__device__ __forceinline__ uint64_t ld64(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void st_rel64(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ uint32_t ld32(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void st_rel32(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void st64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st32(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// read-modify-write read: returns the value at the coherence point
+__device__ __forceinline__ uint64_t rmw_read64(uint64_t* p) {
+  return __hip_atomic_fetch_or(p, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t rmw_read32(uint32_t* p) {
+  return __hip_atomic_fetch_or(p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ void report_error(Report* r, uint32_t code) {
@@ -213,19 +222,351 @@ __global__ void __launch_bounds__(kThreads) ec_prep_kernel(PrepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// encode
+// encode: pieces shared by the generic and the D = 64*C kernels
 // ---------------------------------------------------------------------------
 struct EncShared {
   uint32_t ticket, seg, tile, n, rows, ntiles;
   float eb;
   int valid;
   uint64_t bitmap;
-  uint32_t U, nblk, sumw, nout, mode, fin_seg, fin_all;
-  uint64_t rec_size, rec_abs, item, excl;
+  uint32_t U, nblk, sumw, nout, mode, fin_seg, fin_all, fits;
+  uint64_t rec_size, rec_abs, item;
   uint32_t off_refs, off_opos, off_oval, off_pl;
   uint32_t part[kThreads / 64];
 };
 
+// Thread 0: locate this workgroup's tile.  Tiles are numbered in stream
+// order and tile i runs on workgroup i; every wait in the encoder is on a
+// tile with a smaller number.  Workgroups are dispatched in increasing order
+// (per XCD), so the lowest unfinished tile is always resident and waits on
+// nothing unfinished: the waits cannot deadlock.  They are also bounded.
+__device__ __forceinline__ void take_tile(const EncArgs& a, EncShared& sh) {
+  const uint32_t ticket = blockIdx.x;
+  uint32_t s, k;
+  if (a.sh.tiles_per_seg) {  // every segment has the same number of tiles
+    s = ticket / a.sh.tiles_per_seg;
+    k = ticket - s * a.sh.tiles_per_seg;
+  } else {
+    s = find_segment(a.w.seg_tile_base, a.sh.nseg, ticket);
+    k = ticket - a.w.seg_tile_base[s];
+  }
+  const uint32_t pch = s / a.sh.T;
+  const uint32_t r0 = chunk_row0(a.sh, pch), rows = chunk_row0(a.sh, pch + 1) - r0;
+  const uint32_t nt = (rows + kTileRows - 1) / kTileRows;
+  sh.ticket = ticket;
+  sh.seg = s;
+  sh.tile = k;
+  sh.rows = rows;
+  sh.ntiles = nt;
+  sh.n = nt ? min(kTileRows, rows - k * kTileRows) : 0;
+}
+
+// Error bound of table t (Algorithm 1's factor times the table's value range
+// in range-relative mode).  Called by one whole wave; lanes reduce the range
+// partials in parallel.  Result and validity are returned to every lane.
+__device__ __forceinline__ float table_eb(const EncArgs& a, uint32_t t, bool& valid) {
+  const uint32_t lane = threadIdx.x & 63;
+  double f = (double)a.w.eb_base[t] * (double)a.w.mult[t];
+  f = f * a.sched;
+  float eb = (float)f;
+  if (a.eb_mode == 1) {
+    float lo = INFINITY, hi = -INFINITY;
+    if (a.sh.B > 0) {
+      const float* rp = a.w.range_part + 2 * (uint64_t)t * a.w.nbr;
+      for (uint32_t j = lane; j < a.w.nbr; j += 64) {
+        float l = rp[2 * j], h = rp[2 * j + 1];
+        lo = l < lo ? l : lo;
+        hi = h > hi ? h : hi;
+      }
+      for (int o = 32; o > 0; o >>= 1) {
+        float l2 = __shfl_xor(lo, o), h2 = __shfl_xor(hi, o);
+        lo = l2 < lo ? l2 : lo;
+        hi = h2 > hi ? h2 : hi;
+      }
+    }
+    float range = hi - lo;
+    eb = eb * range;
+  }
+  float e2 = eb + eb;
+  valid = isfinite(eb) && eb > 0.0f && isfinite(e2);
+  return eb;
+}
+
+// Record sizes for the tile (thread 0): RAW vs BITPACK choice and the
+// look-back item (record plus, for a segment's first tile, the segment and
+// chunk prefixes that precede it in the stream).
+__device__ __forceinline__ void size_record(const EncArgs& a, EncShared& sh, bool valid,
+                                            uint32_t n, uint32_t U, uint32_t nblk,
+                                            uint32_t sumw, uint32_t nout) {
+  const uint32_t D = a.sh.D, T = a.sh.T;
+  const uint32_t k = sh.tile, t = sh.seg % T, rows = sh.rows, ntiles = sh.ntiles;
+  uint32_t rb = rows <= 65536 ? 2 : 4;
+  uint32_t off_refs = (uint32_t)align_up(16 + nblk, 4);
+  uint32_t off_opos = (uint32_t)align_up(off_refs + rb * (n - U), 4);
+  uint32_t off_oval = off_opos + 4 * nout;
+  uint32_t off_pl = (uint32_t)align_up(off_oval + 4 * nout, 8);
+  uint64_t bp = align_up(off_pl + 8ull * sumw, 16);
+  uint64_t raw = 16 + align_up(4ull * n * D, 16);
+  uint32_t mode = (valid && bp < raw) ? 1u : 0u;
+  uint64_t rec = n ? (mode ? bp : raw) : 0;
+  uint64_t seg_prefix = 32 + align_up(4ull * ntiles, 16);
+  uint64_t chunk_prefix = align_up(8ull * T, 16);
+  sh.mode = mode;
+  sh.rec_size = rec;
+  sh.item = rec + (k == 0 ? seg_prefix + (t == 0 ? chunk_prefix : 0) : 0);
+  sh.off_refs = off_refs;
+  sh.off_opos = off_opos;
+  sh.off_oval = off_oval;
+  sh.off_pl = off_pl;
+  sh.sumw = sumw;
+  sh.nout = nout;
+  sh.nblk = nblk;
+  sh.U = U;
+}
+
+// Wave 0: decoupled look-back over tiles in ticket (= stream) order; publishes
+// the segment / chunk starts and the record offset.  Sets sh.rec_abs, sh.fits.
+__device__ __forceinline__ void place_record(const EncArgs& a, EncShared& sh) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint64_t kAgg = 1ull << 62, kIncl = 2ull << 62, kVal = (1ull << 62) - 1;
+  const uint32_t ticket = sh.ticket, s = sh.seg, k = sh.tile, ntiles = sh.ntiles;
+  const uint32_t T = a.sh.T, pch = s / T, t = s % T;
+  const uint64_t item = sh.item;
+  uint64_t excl = 0;
+  if (ticket == 0) {
+    if (lane == 0) st64(&a.w.tile_status[0], kIncl | item);
+  } else {
+    if (lane == 0) st64(&a.w.tile_status[ticket], kAgg | item);
+    int64_t top = (int64_t)ticket - 1;
+    while (true) {
+      int64_t idx = top - (int64_t)lane;
+      uint64_t v = kIncl;  // before tile 0: inclusive prefix 0
+      if (idx >= 0) {
+        uint32_t spins = 0;
+        while (((v = ld64(&a.w.tile_status[idx])) >> 62) == 0) {
+          __builtin_amdgcn_s_sleep(1);
+          if (++spins > kSpinLimit) {
+            report_error(a.report, kDevErrTimeout);
+            v = kIncl;
+            break;
+          }
+        }
+      }
+      uint64_t incl_mask = __ballot((v >> 62) == 2);
+      if (incl_mask) {
+        int L = __ffsll((long long)incl_mask) - 1;
+        uint64_t mine = (int)lane <= L ? (v & kVal) : 0;
+        excl += wave_sum_u64(mine);
+        break;
+      }
+      excl += wave_sum_u64(v & kVal);
+      top -= 64;
+    }
+    if (lane == 0) st64(&a.w.tile_status[ticket], kIncl | (excl + item));
+  }
+  if (lane == 0) {
+    uint64_t pos = a.sh.base_bytes + excl;
+    if (k == 0 && t == 0) {
+      st64(&a.w.chunk_start[pch], pos + 1);
+      pos += align_up(8ull * T, 16);
+    }
+    if (k == 0) {
+      st64(&a.w.seg_start[s], pos + 1);
+      pos += 32 + align_up(4ull * ntiles, 16);
+    }
+    if (k + 1 >= ntiles) st64(&a.w.seg_end[s], pos + sh.rec_size + 1);
+    sh.rec_abs = pos;
+    sh.fits = pos + sh.rec_size <= a.out_cap;
+    if (!sh.fits) report_error(a.report, kDevErrTimeout);
+  }
+}
+
+// Bounded spin until a relaxed 64-bit word becomes non-zero.
+__device__ __forceinline__ uint64_t spin_nonzero64(const EncArgs& a, const uint64_t* p) {
+  uint64_t v;
+  uint32_t spins = 0;
+  while ((v = ld64(p)) == 0) {
+    __builtin_amdgcn_s_sleep(2);
+    if (++spins > kSpinLimit) {
+      report_error(a.report, kDevErrTimeout);
+      return 0;
+    }
+  }
+  return v;
+}
+
+// Whole workgroup, after the record is written.  Every tile publishes its
+// record offset and counts (no shared counters, so no atomic contention);
+// the last tile of a segment gathers them and writes the segment header and
+// tile directory; the last tile of the stream writes the stream header and
+// chunk table once every segment is finished.
+__device__ void complete_tile(const EncArgs& a, EncShared& sh, bool valid, float eb) {
+  const uint32_t tid = threadIdx.x;
+  const uint32_t ticket = sh.ticket, s = sh.seg, k = sh.tile, ntiles = sh.ntiles, rows = sh.rows;
+  const uint32_t T = a.sh.T, pch = s / T, t = s % T;
+  __syncthreads();
+  if (tid == 0) {
+    st32(&a.w.tile_U[ticket], sh.U);
+    st32(&a.w.tile_nout[ticket], sh.mode ? sh.nout : 0u);
+    fence_wg();
+    st64(&a.w.tile_rec[ticket], sh.rec_abs + 1);
+  }
+  if (k + 1 < (ntiles ? ntiles : 1)) return;  // not the segment's last tile
+
+  const uint32_t tb = ticket - k;
+  uint32_t u = 0, o = 0;
+  for (uint32_t j = tid; j < ntiles; j += kThreads) {
+    spin_nonzero64(a, &a.w.tile_rec[tb + j]);
+    u += ld32(&a.w.tile_U[tb + j]);
+    o += ld32(&a.w.tile_nout[tb + j]);
+  }
+  u = wave_sum_u32(u);
+  o = wave_sum_u32(o);
+  const uint32_t lane = tid & 63, wv = tid >> 6;
+  if (lane == 0) {
+    sh.part[wv] = u;
+  }
+  __syncthreads();
+  uint32_t U = 0;
+  for (uint32_t j = 0; j < kThreads / 64; j++) U += sh.part[j];
+  __syncthreads();
+  if (lane == 0) sh.part[wv] = o;
+  __syncthreads();
+  uint32_t NO = 0;
+  for (uint32_t j = 0; j < kThreads / 64; j++) NO += sh.part[j];
+  // tile 0 published seg_start before its record offset, which the loop above
+  // has seen (the barriers order this read after that observation)
+  const uint64_t seg_start = ld64(&a.w.seg_start[s]) - 1;
+  const uint64_t seg_end = ld64(&a.w.seg_end[s]) - 1;
+  bool ok = seg_end <= a.out_cap && seg_start + 32 + 4ull * ntiles <= seg_end;
+  uint64_t chunk_start = 0;
+  if (t == 0) {
+    chunk_start = seg_start - align_up(8ull * T, 16);
+  } else {
+    const uint64_t v = spin_nonzero64(a, &a.w.chunk_start[pch]);
+    chunk_start = v ? v - 1 : 0;
+  }
+  ok = ok && chunk_start + align_up(8ull * T, 16) <= seg_start;
+  if (ok) {
+    uint8_t* sg = a.out + seg_start;
+    for (uint32_t j = tid; j < ntiles; j += kThreads)
+      reinterpret_cast<uint32_t*>(sg + 32)[j] = (uint32_t)(ld64(&a.w.tile_rec[tb + j]) - 1 - seg_start);
+    uint32_t dend = 32 + 4 * ntiles, dpad = (uint32_t)align_up(dend, 16) - dend;
+    if (tid < dpad) sg[dend + tid] = 0;
+    if (tid == 0) {
+      const uint64_t bytes = seg_end - seg_start;
+      uint32_t* h = reinterpret_cast<uint32_t*>(sg);
+      h[0] = rows;
+      h[1] = ntiles;
+      h[2] = f2u(valid ? eb : 0.0f);
+      h[3] = valid ? 1u : 0u;
+      h[4] = U;
+      h[5] = NO;
+      reinterpret_cast<uint64_t*>(sg)[3] = bytes;
+      reinterpret_cast<uint64_t*>(a.out + chunk_start)[t] = seg_start - chunk_start;
+      if (a.report) a.report->seg_bytes[s] = bytes;
+    }
+  } else if (tid == 0) {
+    report_error(a.report, kDevErrTimeout);
+  }
+  if (tid == 0) {
+    fence_wg();
+    st32(&a.w.seg_fin[s], 1u);
+  }
+  if (ticket + 1 != a.sh.ntiles) return;  // not the stream's last tile
+
+  // the stream's last tile: wait for every segment, then header + chunk table
+  for (uint32_t q = tid; q < a.sh.nseg; q += kThreads) {
+    uint32_t spins = 0;
+    while (ld32(&a.w.seg_fin[q]) == 0) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins > kSpinLimit) {
+        report_error(a.report, kDevErrTimeout);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t P = a.sh.P, D = a.sh.D;
+  for (uint32_t q = tid; q < P; q += kThreads) {
+    uint64_t cs = ld64(&a.w.chunk_start[q]) - 1;
+    uint64_t ce = ld64(&a.w.seg_end[(uint64_t)q * T + T - 1]) - 1;
+    if (cs + align_up(8ull * T, 16) > ce || ce > a.out_cap) {
+      report_error(a.report, kDevErrTimeout);
+      continue;
+    }
+    reinterpret_cast<uint64_t*>(a.out + 64)[q] = ce - cs;
+    if (T & 1u) reinterpret_cast<uint64_t*>(a.out + cs)[T] = 0;  // pad of segment table
+  }
+  if ((P & 1u) && tid == 0) reinterpret_cast<uint64_t*>(a.out + 64)[P] = 0;
+  if (tid == 0) {
+    const uint64_t total = ld64(&a.w.seg_end[a.sh.nseg - 1]) - 1;
+    uint32_t* h = reinterpret_cast<uint32_t*>(a.out);
+    h[0] = kMagic;
+    h[1] = kVersion | (kCoderBitpack << 16);
+    h[2] = T;
+    h[3] = a.sh.B;
+    h[4] = D;
+    h[5] = P;
+    h[6] = kTileRows;
+    h[7] = a.eb_mode;
+    uint64_t* h64 = reinterpret_cast<uint64_t*>(a.out);
+    h64[4] = (uint64_t)a.iter;
+    h64[5] = 4ull * T * a.sh.B * D;
+    h64[6] = total;
+    h64[7] = 0;
+    if (a.report) a.report->total_bytes = total;
+  }
+}
+
+// Wait until every earlier tile of segment s has inserted its rows.
+__device__ __forceinline__ void wait_inserted(const EncArgs& a, uint32_t s, uint32_t k) {
+  const uint32_t tb = a.w.seg_tile_base[s];
+  for (uint32_t j = threadIdx.x; j < k; j += kThreads) {
+    uint32_t spins = 0;
+    while (ld32(&a.w.tile_inserted[tb + j]) == 0) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins > kSpinLimit) {
+        report_error(a.report, kDevErrTimeout);
+        break;
+      }
+    }
+  }
+}
+
+// RAW record body: the tile's rows verbatim (zero pad to 16).
+__device__ __forceinline__ void write_raw_rows(uint8_t* rec, const float* xt, uint32_t ne,
+                                               uint32_t D) {
+  const uint32_t tid = threadIdx.x;
+  float* dst = reinterpret_cast<float*>(rec + 16);
+  if ((D & 3) == 0) {
+    const float4* x4 = reinterpret_cast<const float4*>(xt);
+    float4* d4 = reinterpret_cast<float4*>(dst);
+    for (uint32_t i = tid; i < ne / 4; i += kThreads) d4[i] = x4[i];
+  } else {
+    for (uint32_t i = tid; i < ne; i += kThreads) dst[i] = xt[i];
+    uint32_t pad = (uint32_t)(align_up(4ull * ne, 16) - 4ull * ne) / 4;
+    if (tid < pad) dst[ne + tid] = 0.0f;
+  }
+}
+
+// Zero pad bytes between a BITPACK record's sections and after its planes.
+__device__ __forceinline__ void write_record_pads(uint8_t* rec, const EncShared& sh, uint32_t n,
+                                                  uint32_t rows) {
+  const uint32_t tid = threadIdx.x;
+  const uint32_t rb = rows <= 65536 ? 2 : 4;
+  for (uint32_t b = sh.nblk + tid; b < sh.off_refs - 16; b += kThreads) rec[16 + b] = 0;
+  uint32_t rend = sh.off_refs + rb * (n - sh.U);
+  if (tid < sh.off_opos - rend) rec[rend + tid] = 0;
+  uint32_t oend = sh.off_oval + 4 * sh.nout;
+  if (tid < sh.off_pl - oend) rec[oend + tid] = 0;
+  uint64_t pend = sh.off_pl + 8ull * sh.sumw;
+  if (tid < sh.rec_size - pend) rec[pend + tid] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// generic encoder (any D): codes staged in LDS
+// ---------------------------------------------------------------------------
 // Compare segment row `cand` (re-quantized from the input) with tile row `i`
 // (codes in LDS); the whole wave participates, the result is uniform.
 __device__ bool rows_equal(const int16_t* s_codes, const float* xs, const float* xt,
@@ -250,7 +591,6 @@ __global__ void __launch_bounds__(kThreads) ec_encode_kernel(EncArgs a) {
   const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const uint32_t D = a.sh.D, T = a.sh.T;
 
-  // LDS carve-up (matches encode_lds_bytes)
   int16_t* s_codes = reinterpret_cast<int16_t*>(smem);
   uint8_t* p = smem + ((size_t)2 * kTileRows * D + 15) / 16 * 16;
   uint64_t* s_hash = reinterpret_cast<uint64_t*>(p);
@@ -267,50 +607,21 @@ __global__ void __launch_bounds__(kThreads) ec_encode_kernel(EncArgs a) {
   p += D + 4;
   uint8_t* s_urow = p;                                 // [64] tile row of each uid
 
-  // ---- which tile ----
-  if (tid == 0) {
-    uint32_t ticket = atomicAdd(&a.w.ctrl[0], 1u);
-    uint32_t s = find_segment(a.w.seg_tile_base, a.sh.nseg, ticket);
-    uint32_t pch = s / T;
-    uint32_t r0 = chunk_row0(a.sh, pch), rows = chunk_row0(a.sh, pch + 1) - r0;
-    uint32_t nt = (rows + kTileRows - 1) / kTileRows;
-    uint32_t k = ticket - a.w.seg_tile_base[s];
-    sh.ticket = ticket;
-    sh.seg = s;
-    sh.tile = k;
-    sh.rows = rows;
-    sh.ntiles = nt;
-    sh.n = nt ? min(kTileRows, rows - k * kTileRows) : 0;
-  }
+  if (tid == 0) take_tile(a, sh);
   __syncthreads();
   const uint32_t ticket = sh.ticket, s = sh.seg, k = sh.tile, n = sh.n, rows = sh.rows;
-  const uint32_t ntiles = sh.ntiles;
   const uint32_t pch = s / T, t = s % T;
   const uint32_t row0 = chunk_row0(a.sh, pch);
   const float* xs = a.x + ((uint64_t)t * a.sh.B + row0) * D;  // segment rows
   const float* xt = xs + (uint64_t)k * kTileRows * D;        // tile rows
-
-  // ---- error bound of this table (Algorithm 1 factor, optional range) ----
-  if (tid == 0) {
-    double f = (double)a.w.eb_base[t] * (double)a.w.mult[t];
-    f = f * a.sched;
-    float eb = (float)f;
-    if (a.eb_mode == 1) {
-      float lo = INFINITY, hi = -INFINITY;
-      const float* rp = a.w.range_part + 2 * (uint64_t)t * a.w.nbr;
-      for (uint32_t j = 0; a.sh.B > 0 && j < a.w.nbr; j++) {
-        float l = rp[2 * j], h = rp[2 * j + 1];
-        lo = l < lo ? l : lo;
-        hi = h > hi ? h : hi;
-      }
-      float range = hi - lo;
-      eb = eb * range;
+  if (wv == 0) {
+    bool v;
+    float e = table_eb(a, t, v);
+    if (lane == 0) {
+      sh.eb = e;
+      sh.valid = v;
+      if (a.dbg_eb && k == 0) a.dbg_eb[s] = v ? e : 0.0f;
     }
-    float e2 = eb + eb;
-    int valid = isfinite(eb) && eb > 0.0f && isfinite(e2);
-    sh.eb = eb;
-    sh.valid = valid;
-    if (a.dbg_eb && k == 0) a.dbg_eb[s] = valid ? eb : 0.0f;
   }
   __syncthreads();
   const float eb = sh.eb;
@@ -318,7 +629,6 @@ __global__ void __launch_bounds__(kThreads) ec_encode_kernel(EncArgs a) {
   const bool valid = sh.valid != 0;
   const uint32_t ne = n * D;
 
-  // ---- quantize the tile into LDS (128-bit loads when rows are 16-B sized) ----
   if (valid) {
     if ((D & 3) == 0) {
       const float4* x4 = reinterpret_cast<const float4*>(xt);
@@ -374,24 +684,16 @@ __global__ void __launch_bounds__(kThreads) ec_encode_kernel(EncArgs a) {
         bool need = false;
         uint32_t cand = 0;
         if (active) {
-          uint64_t v = ld_rlx64(&htab[slot]);
-          if (v == 0) {
-            uint64_t old = atomicCAS((unsigned long long*)&htab[slot], 0ull,
-                                     (unsigned long long)mine);
-            if (old == 0) {
-              s_slot[i] = slot;
-              active = false;
-            } else {
-              v = old;
-            }
-          }
-          if (active) {
-            if ((uint32_t)(v >> 32) == h32 && (uint32_t)v - 1u < rows) {
-              need = true;
-              cand = (uint32_t)v - 1u;
-            } else {
-              slot = (slot + 1) & cap_mask;
-            }
+          uint64_t old = atomicCAS((unsigned long long*)&htab[slot], 0ull,
+                                   (unsigned long long)mine);
+          if (old == 0) {
+            s_slot[i] = slot;
+            active = false;
+          } else if ((uint32_t)(old >> 32) == h32 && (uint32_t)old - 1u < rows) {
+            need = true;
+            cand = (uint32_t)old - 1u;
+          } else {
+            slot = (slot + 1) & cap_mask;
           }
         }
         uint64_t m = __ballot(need);
@@ -421,22 +723,11 @@ __global__ void __launch_bounds__(kThreads) ec_encode_kernel(EncArgs a) {
     }
     __syncthreads();
     if (tid == 0) {
-      __threadfence();
-      st_rel32(&a.w.tile_inserted[ticket], 1u);
+      fence_wg();
+      st32(&a.w.tile_inserted[ticket], 1u);
     }
-    // ---- wait until every earlier tile of the segment has inserted its rows ----
-    const uint32_t tb = a.w.seg_tile_base[s];
-    for (uint32_t j = tid; j < k; j += kThreads) {
-      uint32_t spins = 0;
-      while (ld_acq32(&a.w.tile_inserted[tb + j]) == 0) {
-        __builtin_amdgcn_s_sleep(2);
-        if (++spins > kSpinLimit) {
-          report_error(a.report, kDevErrTimeout);
-          break;
-        }
-      }
-    }
-    __threadfence();
+    wait_inserted(a, s, k);
+    fence_wg();
     __syncthreads();
   }
 
@@ -444,7 +735,7 @@ __global__ void __launch_bounds__(kThreads) ec_encode_kernel(EncArgs a) {
   if (wv == 0) {
     bool inrow = lane < n;
     uint32_t first = k * kTileRows + lane;
-    if (valid && inrow) first = (uint32_t)ld_rlx64(&htab[s_slot[lane]]) - 1u;
+    if (valid && inrow) first = (uint32_t)rmw_read64(&htab[s_slot[lane]]) - 1u;
     bool uniq = valid && inrow && first == k * kTileRows + lane;
     uint64_t bm = __ballot(uniq);
     if (inrow) s_first[lane] = first;
@@ -490,91 +781,13 @@ __global__ void __launch_bounds__(kThreads) ec_encode_kernel(EncArgs a) {
     sumw = block_exclusive_scan(s_boff, nblk, sh.part);
     nout = block_exclusive_scan(s_obase, nblk, sh.part);
   }
-
-  // ---- record layout, RAW fallback, look-back placement ----
-  if (tid == 0) {
-    uint32_t rb = rows <= 65536 ? 2 : 4;
-    uint32_t off_refs = (uint32_t)align_up(16 + nblk, 4);
-    uint32_t off_opos = (uint32_t)align_up(off_refs + rb * (n - U), 4);
-    uint32_t off_oval = off_opos + 4 * nout;
-    uint32_t off_pl = (uint32_t)align_up(off_oval + 4 * nout, 8);
-    uint64_t bp = align_up(off_pl + 8ull * sumw, 16);
-    uint64_t raw = 16 + align_up(4ull * n * D, 16);
-    uint32_t mode = (valid && bp < raw) ? 1u : 0u;
-    uint64_t rec = n ? (mode ? bp : raw) : 0;
-    uint64_t seg_prefix = 32 + align_up(4ull * ntiles, 16);
-    uint64_t chunk_prefix = align_up(8ull * T, 16);
-    uint64_t item = rec + (k == 0 ? seg_prefix + (t == 0 ? chunk_prefix : 0) : 0);
-    sh.mode = mode;
-    sh.rec_size = rec;
-    sh.item = item;
-    sh.off_refs = off_refs;
-    sh.off_opos = off_opos;
-    sh.off_oval = off_oval;
-    sh.off_pl = off_pl;
-    sh.sumw = sumw;
-    sh.nout = nout;
-    sh.nblk = nblk;
-  }
+  if (tid == 0) size_record(a, sh, valid, n, U, nblk, sumw, nout);
   __syncthreads();
-
-  // decoupled look-back over tiles in stream order (wave 0)
-  if (wv == 0) {
-    const uint64_t kAgg = 1ull << 62, kIncl = 2ull << 62, kVal = (1ull << 62) - 1;
-    const uint64_t item = sh.item;
-    uint64_t excl = 0;
-    if (ticket == 0) {
-      if (lane == 0) st_rel64(&a.w.tile_status[0], kIncl | item);
-    } else {
-      if (lane == 0) st_rel64(&a.w.tile_status[ticket], kAgg | item);
-      int64_t top = (int64_t)ticket - 1;
-      while (true) {
-        int64_t idx = top - (int64_t)lane;
-        uint64_t v = kIncl;  // before tile 0: inclusive prefix 0
-        if (idx >= 0) {
-          uint32_t spins = 0;
-          while (((v = ld_acq64(&a.w.tile_status[idx])) >> 62) == 0) {
-            __builtin_amdgcn_s_sleep(1);
-            if (++spins > kSpinLimit) {
-              report_error(a.report, kDevErrTimeout);
-              v = kIncl;
-              break;
-            }
-          }
-        }
-        uint64_t incl_mask = __ballot((v >> 62) == 2);
-        if (incl_mask) {
-          int L = __ffsll((long long)incl_mask) - 1;
-          uint64_t mine = (int)lane <= L ? (v & kVal) : 0;
-          excl += wave_sum_u64(mine);
-          break;
-        }
-        excl += wave_sum_u64(v & kVal);
-        top -= 64;
-      }
-      if (lane == 0) st_rel64(&a.w.tile_status[ticket], kIncl | (excl + item));
-    }
-    if (lane == 0) {
-      uint64_t pos = a.sh.base_bytes + excl;
-      if (k == 0 && t == 0) {
-        st_rel64(&a.w.chunk_start[pch], pos + 1);
-        pos += align_up(8ull * T, 16);
-      }
-      if (k == 0) {
-        st_rel64(&a.w.seg_start[s], pos + 1);
-        pos += 32 + align_up(4ull * ntiles, 16);
-      }
-      a.w.tile_rec[ticket] = pos;
-      if (k + 1 >= ntiles) a.w.seg_end[s] = pos + sh.rec_size + 1;
-      sh.rec_abs = pos;
-      sh.fin_all = pos + sh.rec_size <= a.out_cap;  // reused as "record fits"
-      if (!sh.fin_all) report_error(a.report, kDevErrTimeout);
-    }
-  }
+  if (wv == 0) place_record(a, sh);
   __syncthreads();
 
   // ---- write the tile record ----
-  if (n > 0 && sh.fin_all) {
+  if (n > 0 && sh.fits) {
     uint8_t* rec = a.out + sh.rec_abs;
     const uint32_t mode = sh.mode;
     if (tid == 0) {
@@ -583,38 +796,18 @@ __global__ void __launch_bounds__(kThreads) ec_encode_kernel(EncArgs a) {
       reinterpret_cast<uint64_t*>(rec)[1] = w1;
     }
     if (mode == 0) {
-      // RAW: rows verbatim, zero pad to 16
-      float* dst = reinterpret_cast<float*>(rec + 16);
-      if ((D & 3) == 0) {
-        const float4* x4 = reinterpret_cast<const float4*>(xt);
-        float4* d4 = reinterpret_cast<float4*>(dst);
-        for (uint32_t i = tid; i < ne / 4; i += kThreads) d4[i] = x4[i];
-      } else {
-        for (uint32_t i = tid; i < ne; i += kThreads) dst[i] = xt[i];
-        uint32_t pad = (uint32_t)(align_up(4ull * ne, 16) - 4ull * ne) / 4;
-        if (tid < pad) dst[ne + tid] = 0.0f;
-      }
+      write_raw_rows(rec, xt, ne, D);
     } else {
       const uint32_t rb = rows <= 65536 ? 2 : 4;
       const uint32_t off_refs = sh.off_refs, off_opos = sh.off_opos, off_oval = sh.off_oval;
       const uint32_t off_pl = sh.off_pl;
-      // widths + zero pad up to the refs
-      for (uint32_t b = tid; b < off_refs - 16; b += kThreads) rec[16 + b] = b < nblk ? s_width[b] : 0;
-      // refs (first occurrence of every repeated row, row order) + pad
+      for (uint32_t b = tid; b < nblk; b += kThreads) rec[16 + b] = s_width[b];
       if (tid < n && !((bitmap >> tid) & 1ull)) {
         uint32_t j = tid - (uint32_t)__popcll(bitmap & ((1ull << tid) - 1ull));
         if (rb == 2) reinterpret_cast<uint16_t*>(rec + off_refs)[j] = (uint16_t)s_first[tid];
         else reinterpret_cast<uint32_t*>(rec + off_refs)[j] = s_first[tid];
       }
-      {
-        uint32_t rend = off_refs + rb * (n - U);
-        if (tid < off_opos - rend) rec[rend + tid] = 0;
-        uint32_t oend = off_oval + 4 * nout;
-        if (tid < off_pl - oend) rec[oend + tid] = 0;
-        uint64_t pend = off_pl + 8ull * sumw;
-        if (tid < sh.rec_size - pend) rec[pend + tid] = 0;
-      }
-      // outliers and bit planes, one wave per 64-element block
+      write_record_pads(rec, sh, n, rows);
       uint64_t* planes = reinterpret_cast<uint64_t*>(rec + off_pl);
       uint32_t* opos = reinterpret_cast<uint32_t*>(rec + off_opos);
       uint32_t* oval = reinterpret_cast<uint32_t*>(rec + off_oval);
@@ -646,121 +839,376 @@ __global__ void __launch_bounds__(kThreads) ec_encode_kernel(EncArgs a) {
       }
     }
   }
+  complete_tile(a, sh, valid, eb);
+}
 
-  // ---- segment and stream completion ----
-  __syncthreads();
-  if (tid == 0) {
-    __threadfence();
-    atomicAdd(&a.w.seg_U[s], U);
-    atomicAdd(&a.w.seg_nout[s], sh.mode ? nout : 0u);
-    __threadfence();
-    uint32_t done = atomicAdd(&a.w.seg_done[s], 1u);
-    sh.fin_seg = (done + 1 >= (ntiles ? ntiles : 1)) ? 1u : 0u;
-  }
-  __syncthreads();
-  if (!sh.fin_seg) return;
-  __threadfence();
-  const uint64_t seg_start = ld_acq64(&a.w.seg_start[s]) - 1;
-  const uint64_t seg_end = ld_acq64(&a.w.seg_end[s]) - 1;
-  if (seg_end > a.out_cap || seg_start + 32 + 4ull * ntiles > seg_end) {
-    if (tid == 0) report_error(a.report, kDevErrTimeout);
-    return;
-  }
-  uint64_t chunk_start = 0;
-  if (t == 0) {
-    chunk_start = seg_start - align_up(8ull * T, 16);
+// ---------------------------------------------------------------------------
+// encoder for D = 64*C: one wave per (row, 64-element chunk), lane = element,
+// so every wavefront ballot is directly one bit plane of one block.  Widths,
+// planes, outlier masks and row hashes come out of the quantization pass in
+// registers; LDS keeps only the planes (for repeated-row checks and the final
+// copy), never the codes.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t fmix32(uint32_t h) {
+  h ^= h >> 16;
+  h *= 0x85ebca6bu;
+  h ^= h >> 13;
+  h *= 0xc2b2ae35u;
+  h ^= h >> 16;
+  return h;
+}
+
+// Exact quantization with a multiply by r = fl(1/s) (correctly rounded): the
+// product is within 2^-11 of fl(x/s) for |x/s| < 2048, so whenever it lies at
+// least 2^-10 away from every rounding boundary (k + 1/2) and well inside the
+// code range, rint of it equals rint(fl(x/s)).  Otherwise the IEEE division
+// decides, exactly as quantize() does.
+__device__ __forceinline__ bool quantize_fast(float x, float eb, float s, float r, int& q) {
+  float tp = x * r;
+  float qp = rintf(tp);
+  float f = tp - qp;
+  float qf;
+  if (fabsf(f) < 0.4990234375f && fabsf(tp) < 2046.5f) {
+    qf = qp;
   } else {
-    uint64_t v;
-    uint32_t spins = 0;
-    while ((v = ld_acq64(&a.w.chunk_start[pch])) == 0) {
-      __builtin_amdgcn_s_sleep(2);
-      if (++spins > kSpinLimit) {
-        report_error(a.report, kDevErrTimeout);
-        v = 1;
-        break;
+    float t = x / s;
+    if (!(fabsf(t) <= 2047.0f)) {
+      q = 0;
+      return true;
+    }
+    qf = rintf(t);
+  }
+  float xh = qf * s;
+  float err = x - xh;
+  if (!(fabsf(err) <= eb)) {
+    q = 0;
+    return true;
+  }
+  q = (int)qf;
+  return false;
+}
+
+template <int C>
+struct FastLds {
+  uint64_t planes[kTileRows][C][12];
+  uint64_t omask[kTileRows][C];
+  uint8_t w[kTileRows][C];
+};
+
+template <int C>
+__global__ void __launch_bounds__(kThreads) ec_encode_fast(EncArgs a) {
+  constexpr uint32_t D = 64u * C;
+  constexpr uint32_t kRowsPerWave = kTileRows / (kThreads / 64);      // 16
+  constexpr uint32_t kBatch = (8 / C) < 1 ? 1 : (8 / C);  // rows per load batch
+  extern __shared__ __align__(16) uint8_t smem[];
+  FastLds<C>& L = *reinterpret_cast<FastLds<C>*>(smem);
+  __shared__ EncShared sh;
+  __shared__ uint64_t s_hash[kTileRows];
+  __shared__ uint32_t s_slot[kTileRows], s_first[kTileRows], s_rowbase[kTileRows];
+  __shared__ uint32_t s_obase[kTileRows];
+  __shared__ uint8_t s_urow[kTileRows];
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const uint32_t T = a.sh.T;
+
+  if (tid == 0) take_tile(a, sh);
+  __syncthreads();
+  const uint32_t ticket = sh.ticket, s = sh.seg, k = sh.tile, n = sh.n, rows = sh.rows;
+  const uint32_t pch = s / T, t = s % T;
+  const uint32_t row0 = chunk_row0(a.sh, pch);
+  const float* xs = a.x + ((uint64_t)t * a.sh.B + row0) * D;
+  const float* xt = xs + (uint64_t)k * kTileRows * D;
+  if (wv == 0) {
+    bool v;
+    float e = table_eb(a, t, v);
+    if (lane == 0) {
+      sh.eb = e;
+      sh.valid = v;
+      if (a.dbg_eb && k == 0) a.dbg_eb[s] = v ? e : 0.0f;
+    }
+  }
+  __syncthreads();
+  const float eb = sh.eb;
+  const float s2 = eb + eb;
+  const float r2 = 1.0f / s2;
+  const bool valid = sh.valid != 0;
+  const uint64_t g0 = ((uint64_t)t * a.sh.B + row0 + (uint64_t)k * kTileRows) * D;
+
+  // ---- quantize, planes, widths, outlier masks, row hashes ----
+  // Rows are processed in small fully unrolled batches (loads first).
+  if (valid) {
+    const uint32_t rbeg = wv * kRowsPerWave;
+#pragma unroll 1
+    for (uint32_t rb = 0; rb < kRowsPerWave; rb += kBatch) {
+      float v[kBatch][C];
+#pragma unroll
+      for (uint32_t rr = 0; rr < kBatch; rr++)
+#pragma unroll
+        for (uint32_t j = 0; j < C; j++) {
+          const uint32_t i = rbeg + rb + rr;
+          v[rr][j] = i < n ? xt[(uint64_t)i * D + 64 * j + lane] : 0.0f;
+        }
+#pragma unroll
+      for (uint32_t rr = 0; rr < kBatch; rr++) {
+        const uint32_t i = rbeg + rb + rr;
+        if (i >= n) continue;
+        uint32_t hlo = 0, hhi = 0;
+#pragma unroll
+        for (uint32_t j = 0; j < C; j++) {
+          const float x = v[rr][j];
+          const uint32_t d = 64 * j + lane;
+          // q = rint(x / 2eb) via the correctly rounded reciprocal; the IEEE
+          // division decides near rounding boundaries (see quantize_fast)
+          const float tp = x * r2;
+          float qf = rintf(tp);
+          const float f = tp - qf;
+          const bool unsure = !(fabsf(f) < 0.4990234375f && fabsf(tp) < 2046.5f);
+          bool oor = false;
+          if (__any(unsure)) {
+            if (unsure) {
+              const float tq = x / s2;
+              oor = !(fabsf(tq) <= 2047.0f);
+              qf = rintf(tq);
+            }
+          }
+          const float xh = qf * s2;
+          const float err = x - xh;
+          const bool out = oor || !(fabsf(err) <= eb);
+          const int q = out ? 0 : (int)qf;
+          const uint32_t zz = zigzag(q);
+          uint32_t h = ((out ? f2u(x) : (uint32_t)q) ^ (d * 0x9e3779b9u) ^ (out ? 0x7f4a7c15u : 0u));
+          h *= 0x85ebca6bu;
+          h ^= h >> 16;
+          hlo += h;
+          hhi += h * (2u * d + 1u);
+          // width = bit length of the chunk's largest zigzag code (binary
+          // search with ballots), then one ballot per bit plane
+          uint32_t lo = 0, hi = 12;
+          while (lo < hi) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if (__any((zz >> mid) != 0u)) lo = mid + 1;
+            else hi = mid;
+          }
+          const uint32_t w = lo;
+          uint64_t mine = 0;  // lane b keeps plane b
+          for (uint32_t b = 0; b < w; b++) {
+            const uint64_t pk = __ballot((zz >> b) & 1u);
+            mine = lane == b ? pk : mine;
+          }
+          if (lane < w) L.planes[i][j][lane] = mine;
+          const uint64_t om = __ballot(out);
+          if (lane == 0) {
+            L.omask[i][j] = om;
+            L.w[i][j] = (uint8_t)w;
+          }
+        }
+        const uint64_t H = ((uint64_t)wave_sum_u32(hhi) << 32) | wave_sum_u32(hlo);
+        if (lane == 0) s_hash[i] = H;
       }
     }
-    chunk_start = v - 1;
-  }
-  if (chunk_start + align_up(8ull * T, 16) > seg_start) {
-    if (tid == 0) report_error(a.report, kDevErrTimeout);
-    return;
-  }
-  uint8_t* sg = a.out + seg_start;
-  const uint32_t tb = a.w.seg_tile_base[s];
-  for (uint32_t j = tid; j < ntiles; j += kThreads)
-    reinterpret_cast<uint32_t*>(sg + 32)[j] = (uint32_t)(a.w.tile_rec[tb + j] - seg_start);
-  {
-    uint32_t dend = 32 + 4 * ntiles, dpad = (uint32_t)align_up(dend, 16) - dend;
-    if (tid < dpad) sg[dend + tid] = 0;
-  }
-  if (tid == 0) {
-    const uint64_t bytes = seg_end - seg_start;
-    uint32_t* h = reinterpret_cast<uint32_t*>(sg);
-    h[0] = rows;
-    h[1] = ntiles;
-    h[2] = f2u(valid ? eb : 0.0f);
-    h[3] = valid ? 1u : 0u;
-    h[4] = __hip_atomic_load(&a.w.seg_U[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    h[5] = __hip_atomic_load(&a.w.seg_nout[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    reinterpret_cast<uint64_t*>(sg)[3] = bytes;
-    reinterpret_cast<uint64_t*>(a.out + chunk_start)[t] = seg_start - chunk_start;
-    if (a.report) a.report->seg_bytes[s] = bytes;
-    __threadfence();
-    uint32_t g = atomicAdd(&a.w.ctrl[1], 1u);
-    sh.fin_all = (g + 1 == a.sh.nseg) ? 1u : 0u;
+    if (a.dbg_codes || a.dbg_outlier) {  // tests only: codes rebuilt from the planes
+      __syncthreads();
+      for (uint32_t e = tid; e < n * D; e += kThreads) {
+        const uint32_t i = e / D, d = e % D, j = d / 64, l = d % 64;
+        const uint32_t w = L.w[i][j];
+        uint32_t zz = 0;
+        for (uint32_t b = 0; b < w; b++) zz |= (uint32_t)((L.planes[i][j][b] >> l) & 1ull) << b;
+        const bool out = (L.omask[i][j] >> l) & 1ull;
+        if (a.dbg_codes) a.dbg_codes[g0 + e] = out ? 0 : unzigzag(zz);
+        if (a.dbg_outlier) a.dbg_outlier[g0 + e] = out ? 1 : 0;
+      }
+    }
+  } else if (a.dbg_codes || a.dbg_outlier) {
+    for (uint32_t e = tid; e < n * D; e += kThreads) {
+      if (a.dbg_codes) a.dbg_codes[g0 + e] = 0;
+      if (a.dbg_outlier) a.dbg_outlier[g0 + e] = 0;
+    }
   }
   __syncthreads();
-  if (!sh.fin_all) return;
-  __threadfence();
-  // the last segment to finish writes the stream header and chunk table
-  const uint32_t P = a.sh.P;
-  for (uint32_t q = tid; q < P; q += kThreads) {
-    uint64_t cs = ld_acq64(&a.w.chunk_start[q]) - 1;
-    uint64_t ce = ld_acq64(&a.w.seg_end[(uint64_t)q * T + T - 1]) - 1;
-    if (cs + align_up(8ull * T, 16) > ce || ce > a.out_cap) {
-      report_error(a.report, kDevErrTimeout);
-      continue;
+
+  uint64_t* htab = a.w.hash + (valid ? a.w.hash_off[s] : 0);
+  const uint32_t cap_mask = (1u << a.w.hash_log2[s]) - 1u;
+  if (valid && n > 0) {
+    // ---- insert: each wave owns 16 rows (lanes 0..15); compares use the wave ----
+    const uint32_t i = wv * 16 + lane;
+    bool active = lane < 16 && i < n;
+    uint64_t H = active ? (s_hash[i] & a.hash_keep) : 0;
+    uint32_t h32 = (uint32_t)(H >> 32);
+    uint32_t slot = (uint32_t)H & cap_mask;
+    uint64_t mine = ((uint64_t)h32 << 32) | (uint64_t)(k * kTileRows + i + 1);
+    uint32_t guard = 0;
+    while (__ballot(active) != 0) {
+      bool need = false;
+      uint32_t cand = 0;
+      if (active) {
+        uint64_t old = atomicCAS((unsigned long long*)&htab[slot], 0ull, (unsigned long long)mine);
+        if (old == 0) {
+          s_slot[i] = slot;
+          active = false;
+        } else if ((uint32_t)(old >> 32) == h32 && (uint32_t)old - 1u < rows) {
+          need = true;
+          cand = (uint32_t)old - 1u;
+        } else {
+          slot = (slot + 1) & cap_mask;
+        }
+      }
+      uint64_t m = __ballot(need);
+      while (m) {
+        const int Ln = __ffsll((long long)m) - 1;
+        m &= m - 1;
+        const uint32_t iL = __shfl(i, Ln), cL = __shfl(cand, Ln);
+        // row iL (planes in LDS) against candidate row cL re-quantized
+        bool eq = true;
+#pragma unroll
+        for (uint32_t j = 0; j < C; j++) {
+          const uint32_t d = 64 * j + lane;
+          const float xo = xs[(uint64_t)cL * D + d];
+          int qo;
+          const bool oo = quantize_fast(xo, eb, s2, r2, qo);
+          const uint32_t zo = zigzag(qo);
+          const uint32_t w = L.w[iL][j];
+          uint32_t zm = 0;
+          for (uint32_t b = 0; b < w; b++) zm |= (uint32_t)((L.planes[iL][j][b] >> lane) & 1ull) << b;
+          const bool om = (L.omask[iL][j] >> lane) & 1ull;
+          bool e = (oo == om) && (zo == zm);
+          if (e && om) e = f2u(xo) == f2u(xt[(uint64_t)iL * D + d]);
+          eq = eq && e;
+        }
+        eq = __all(eq);
+        if ((int)lane == Ln) {
+          if (eq) {
+            atomicMin((unsigned long long*)&htab[slot], (unsigned long long)mine);
+            s_slot[i] = slot;
+            active = false;
+          } else {
+            slot = (slot + 1) & cap_mask;
+          }
+        }
+      }
+      if (++guard > cap_mask + 2) {  // cannot happen: the table is at most half full
+        if (active) {
+          report_error(a.report, kDevErrTimeout);
+          s_slot[i] = slot;
+          active = false;
+        }
+      }
     }
-    reinterpret_cast<uint64_t*>(a.out + 64)[q] = ce - cs;
-    if (T & 1u) reinterpret_cast<uint64_t*>(a.out + cs)[T] = 0;  // pad of segment table
+    __syncthreads();
+    if (tid == 0) {
+      fence_wg();
+      st32(&a.w.tile_inserted[ticket], 1u);
+    }
+    wait_inserted(a, s, k);
+    fence_wg();
+    __syncthreads();
   }
-  if ((P & 1u) && tid == 0) reinterpret_cast<uint64_t*>(a.out + 64)[P] = 0;
-  if (tid == 0) {
-    const uint64_t total = ld_acq64(&a.w.seg_end[a.sh.nseg - 1]) - 1;
-    uint32_t* h = reinterpret_cast<uint32_t*>(a.out);
-    h[0] = kMagic;
-    h[1] = kVersion | (kCoderBitpack << 16);
-    h[2] = T;
-    h[3] = a.sh.B;
-    h[4] = D;
-    h[5] = P;
-    h[6] = kTileRows;
-    h[7] = a.eb_mode;
-    uint64_t* h64 = reinterpret_cast<uint64_t*>(a.out);
-    h64[4] = (uint64_t)a.iter;
-    h64[5] = 4ull * T * a.sh.B * D;
-    h64[6] = total;
-    h64[7] = 0;
-    if (a.report) a.report->total_bytes = total;
+
+  // ---- first occurrences, per-row plane and outlier bases (wave 0) ----
+  if (wv == 0) {
+    const bool inrow = lane < n;
+    uint32_t first = k * kTileRows + lane;
+    if (valid && inrow) first = (uint32_t)rmw_read64(&htab[s_slot[lane]]) - 1u;
+    const bool uniq = valid && inrow && first == k * kTileRows + lane;
+    const uint64_t bm = __ballot(uniq);
+    uint32_t rw = 0, ro = 0;
+    if (uniq) {
+#pragma unroll
+      for (uint32_t j = 0; j < C; j++) {
+        rw += L.w[lane][j];
+        ro += (uint32_t)__popcll(L.omask[lane][j]);
+      }
+    }
+    uint32_t iw = rw, io = ro;  // inclusive scans over lanes
+    for (int o = 1; o < 64; o <<= 1) {
+      uint32_t a1 = __shfl_up(iw, o), a2 = __shfl_up(io, o);
+      if (lane >= (uint32_t)o) {
+        iw += a1;
+        io += a2;
+      }
+    }
+    s_rowbase[lane] = iw - rw;
+    s_obase[lane] = io - ro;
+    if (inrow) s_first[lane] = first;
+    if (uniq) s_urow[__popcll(bm & __lanemask_lt())] = (uint8_t)lane;
+    if (a.dbg_first && inrow)
+      a.dbg_first[(uint64_t)t * a.sh.B + row0 + k * kTileRows + lane] = first;
+    const uint32_t sumw = __shfl(iw, 63), nout = __shfl(io, 63);
+    if (lane == 0) {
+      sh.bitmap = bm;
+      const uint32_t U = (uint32_t)__popcll(bm);
+      size_record(a, sh, valid, n, U, U * C, sumw, nout);
+    }
   }
+  __syncthreads();
+  if (wv == 0) place_record(a, sh);
+  __syncthreads();
+
+  // ---- write the tile record ----
+  if (n > 0 && sh.fits) {
+    uint8_t* rec = a.out + sh.rec_abs;
+    const uint32_t mode = sh.mode, U = sh.U, nout = sh.nout, nblk = sh.nblk;
+    const uint64_t bitmap = sh.bitmap;
+    if (tid == 0) {
+      uint64_t w1 = (uint64_t)(mode ? nout : 0u) | ((uint64_t)U << 32) | ((uint64_t)mode << 48);
+      reinterpret_cast<uint64_t*>(rec)[0] = bitmap;
+      reinterpret_cast<uint64_t*>(rec)[1] = w1;
+    }
+    if (mode == 0) {
+      write_raw_rows(rec, xt, n * D, D);
+    } else {
+      const uint32_t rb = rows <= 65536 ? 2 : 4;
+      for (uint32_t b = tid; b < nblk; b += kThreads) rec[16 + b] = L.w[s_urow[b / C]][b % C];
+      if (tid < n && !((bitmap >> tid) & 1ull)) {
+        uint32_t j = tid - (uint32_t)__popcll(bitmap & ((1ull << tid) - 1ull));
+        if (rb == 2) reinterpret_cast<uint16_t*>(rec + sh.off_refs)[j] = (uint16_t)s_first[tid];
+        else reinterpret_cast<uint32_t*>(rec + sh.off_refs)[j] = s_first[tid];
+      }
+      write_record_pads(rec, sh, n, rows);
+      uint64_t* planes = reinterpret_cast<uint64_t*>(rec + sh.off_pl);
+      uint32_t* opos = reinterpret_cast<uint32_t*>(rec + sh.off_opos);
+      uint32_t* oval = reinterpret_cast<uint32_t*>(rec + sh.off_oval);
+      for (uint32_t u = wv; u < U; u += kThreads / 64) {
+        const uint32_t i = s_urow[u];
+        uint32_t pb = s_rowbase[i], ob = s_obase[i];
+#pragma unroll
+        for (uint32_t j = 0; j < C; j++) {
+          const uint32_t w = L.w[i][j];
+          if (lane < w) planes[pb + lane] = L.planes[i][j][lane];
+          pb += w;
+          const uint64_t om = L.omask[i][j];
+          if (om) {
+            if ((om >> lane) & 1ull) {
+              const uint32_t o = ob + (uint32_t)__popcll(om & __lanemask_lt());
+              opos[o] = u * D + 64 * j + lane;
+              oval[o] = f2u(xt[(uint64_t)i * D + 64 * j + lane]);
+            }
+            ob += (uint32_t)__popcll(om);
+          }
+        }
+      }
+    }
+  }
+  complete_tile(a, sh, valid, eb);
 }
 
 // ---------------------------------------------------------------------------
 // decode
 // ---------------------------------------------------------------------------
+constexpr uint32_t kOutCap = 256;  // outliers staged in LDS per tile
+
 struct DecTile {
   const uint8_t* rec;   // record start
   uint64_t avail;       // bytes from the record start to the segment end
   uint64_t bitmap;
   uint32_t n, U, nout, mode, ok;
+  uint32_t nblk, off_refs, off_opos, off_oval, off_pl;
 };
 
 struct DecShared {
-  uint32_t ok, seg, tile, n, rows, ntiles, valid;
+  uint32_t ok, seg, tile, n, rows, ntiles, valid, bad;
   float eb;
   uint64_t seg_off, seg_bytes;
   DecTile tl;
+  uint32_t part[kThreads / 64];
 };
 
 __device__ __forceinline__ uint64_t rd64(const uint8_t* p) {
@@ -770,8 +1218,8 @@ __device__ __forceinline__ uint32_t rd32(const uint8_t* p) {
   return *reinterpret_cast<const uint32_t*>(p);
 }
 
-// Locate and check tile record k of a segment.  Every thread may call this;
-// all reads are bounds-checked against the segment.
+// Locate and check tile record k of a segment; every read is bounds-checked
+// against the segment.
 __device__ DecTile locate_tile(const uint8_t* seg, uint64_t seg_bytes, uint32_t ntiles,
                                uint32_t rows, uint32_t k, uint32_t D, bool valid) {
   DecTile r{};
@@ -801,8 +1249,14 @@ __device__ DecTile locate_tile(const uint8_t* seg, uint64_t seg_bytes, uint32_t 
     uint32_t rb = rows <= 65536 ? 2 : 4;
     uint64_t off_refs = align_up(16 + nblk, 4);
     uint64_t off_opos = align_up(off_refs + (uint64_t)rb * (r.n - r.U), 4);
-    uint64_t off_pl = align_up(off_opos + 8ull * r.nout, 8);
+    uint64_t off_oval = off_opos + 4ull * r.nout;
+    uint64_t off_pl = align_up(off_oval + 4ull * r.nout, 8);
     if (off_pl > r.avail) return r;
+    r.nblk = (uint32_t)nblk;
+    r.off_refs = (uint32_t)off_refs;
+    r.off_opos = (uint32_t)off_opos;
+    r.off_oval = (uint32_t)off_oval;
+    r.off_pl = (uint32_t)off_pl;
   } else {
     return r;
   }
@@ -810,86 +1264,77 @@ __device__ DecTile locate_tile(const uint8_t* seg, uint64_t seg_bytes, uint32_t 
   return r;
 }
 
-// Reconstruct the key values of first-occurrence row `i` of tile `tl` into
-// y[0..D) (whole wave).  Returns false on a malformed record.
-__device__ bool decode_key_row(const DecTile& tl, uint32_t i, uint32_t rows, uint32_t D,
-                               float eb, float s2, float* y, bool requant_raw) {
+// Decode the D values of E[e0 .. e0 + D) into y (whole wave, lane = element
+// within a 64-wide chunk).  Block b's planes start at word boff(b):
+//   boff given (LDS prefix):  boff[b];
+//   boff == nullptr:          run0 + sum of widths[b0 .. b), with run0 the
+//                             offset of block b0 = e0 / 64.
+// Returns false if a width or a plane index is out of range.
+template <typename WP, typename PP, typename OP>
+__device__ __forceinline__ bool decode_span(float* y, uint32_t D, uint32_t e0, uint32_t nblk,
+                                            WP widths, const uint32_t* boff, uint32_t run0,
+                                            PP planes, uint64_t plane_words, OP opos, OP oval,
+                                            uint32_t nout, float s2) {
   const uint32_t lane = threadIdx.x & 63;
-  if (tl.mode == 0) {
-    const float* src = reinterpret_cast<const float*>(tl.rec + 16) + (uint64_t)i * D;
-    for (uint32_t d = lane; d < D; d += 64) {
-      float v = src[d];
-      if (requant_raw) {
-        int q;
-        v = quantize(v, eb, s2, q) ? v : (float)q * s2;
-      }
-      y[d] = v;
-    }
-    return true;
-  }
-  const uint32_t u = (uint32_t)__popcll(tl.bitmap & ((1ull << i) - 1ull));
-  const uint32_t nE = tl.U * D, nblk = (nE + 63) / 64;
-  const uint32_t rb = rows <= 65536 ? 2 : 4;
-  const uint32_t off_refs = (uint32_t)align_up(16 + nblk, 4);
-  const uint32_t off_opos = (uint32_t)align_up(off_refs + rb * (tl.n - tl.U), 4);
-  const uint32_t off_oval = off_opos + 4 * tl.nout;
-  const uint32_t off_pl = (uint32_t)align_up(off_oval + 4 * tl.nout, 8);
-  const uint8_t* widths = tl.rec + 16;
-  const uint32_t e0 = u * D, b0 = e0 >> 6;
-  uint32_t part = 0, bad = 0;
-  for (uint32_t j = lane; j < b0; j += 64) {
-    uint32_t w = widths[j];
-    bad |= w > 12;
-    part += w;
-  }
-  uint32_t run = wave_sum_u32(part);
-  if (__any(bad)) return false;
-  // outliers of this row: first index with position >= e0 (binary search)
-  const uint32_t* opos = reinterpret_cast<const uint32_t*>(tl.rec + off_opos);
-  const uint32_t* oval = reinterpret_cast<const uint32_t*>(tl.rec + off_oval);
-  uint32_t olo = 0, ohi = tl.nout;
+  uint32_t olo = 0, ohi = nout;  // first outlier at or after e0
   while (olo < ohi) {
     uint32_t mid = (olo + ohi) >> 1;
     if (opos[mid] < e0) olo = mid + 1;
     else ohi = mid;
   }
-  const uint64_t plane_words = (tl.avail - off_pl) / 8;
-  const uint64_t* planes = reinterpret_cast<const uint64_t*>(tl.rec + off_pl);
-  bool okrow = true;
+  const uint32_t b0 = e0 >> 6;
+  uint32_t run = run0;
+  bool ok = true;
   for (uint32_t m = 0; m * 64 < D; m++) {
     const uint32_t A = b0 + m;
     const uint32_t wA = A < nblk ? widths[A] : 0;
     const uint32_t wB = A + 1 < nblk ? widths[A + 1] : 0;
+    const uint32_t offA = boff ? (A < nblk ? boff[A] : 0) : run;
+    const uint32_t offB = boff ? (A + 1 < nblk ? boff[A + 1] : 0) : run + wA;
     const uint32_t d = m * 64 + lane;
     const uint32_t e = e0 + d;
     const bool inB = (e >> 6) != A;
     const uint32_t w = inB ? wB : wA;
-    const uint32_t off = inB ? run + wA : run;
+    const uint32_t off = inB ? offB : offA;
+    const bool lane_ok = w <= 12 && (uint64_t)off + w <= plane_words;
     uint32_t zz = 0;
-    bool lane_ok = w <= 12 && (uint64_t)off + w <= plane_words;
     if (d < D && lane_ok) {
       const uint32_t bit = e & 63;
       for (uint32_t j = 0; j < w; j++) zz |= (uint32_t)((planes[off + j] >> bit) & 1ull) << j;
     }
-    okrow = okrow && (d >= D || lane_ok);
+    ok = ok && (d >= D || lane_ok);
     float v = (float)unzigzag(zz) * s2;
-    while (olo < tl.nout) {
+    const uint32_t chunk_end = e0 + min(D, m * 64 + 64);
+    while (olo < nout) {
       uint32_t pos = opos[olo];
-      if (pos >= e0 + min(D, m * 64 + 64)) break;
+      if (pos >= chunk_end) break;
       if (pos == e) v = __uint_as_float(oval[olo]);
       olo++;
     }
     if (d < D) y[d] = v;
     run += wA;
   }
-  return __all(okrow);
+  return __all(ok);
 }
 
 __global__ void __launch_bounds__(kThreads) ec_decode_kernel(DecArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
   __shared__ DecShared sh;
+  __shared__ uint32_t s_src[kTileRows];      // local uid, or kExt | row for references
+  __shared__ uint32_t s_xoff[kTileRows];     // external: record offset in the segment
+  __shared__ uint32_t s_xu[kTileRows];       // external: uid (BITPACK) or row (RAW)
+  __shared__ uint32_t s_xbase[kTileRows];    // external: plane word offset of the row's block
+  constexpr uint32_t kExt = 0x80000000u, kBad = 0x40000000u;
   const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const uint32_t D = a.sh.D, T = a.sh.T, B = a.sh.B, P = a.sh.P;
   const uint32_t ticket = blockIdx.x;
+  const uint32_t plane_cap = min(12u * D, 6144u);
+  uint64_t* s_planes = reinterpret_cast<uint64_t*>(smem);
+  uint32_t* s_boff = reinterpret_cast<uint32_t*>(smem + 8ull * plane_cap);
+  uint8_t* s_width = reinterpret_cast<uint8_t*>(s_boff + D + 8);
+  uint32_t* s_opos = reinterpret_cast<uint32_t*>(s_width + ((D + 8 + 15) / 16) * 16);
+  uint32_t* s_oval = s_opos + kOutCap;
+
   if (tid == 0) {
     uint32_t s = find_segment(a.seg_tile_base, a.sh.nseg, ticket);
     uint32_t pch = s / T, t = s % T;
@@ -901,6 +1346,7 @@ __global__ void __launch_bounds__(kThreads) ec_decode_kernel(DecArgs a) {
     sh.rows = rows;
     sh.ntiles = nt;
     sh.n = nt ? min(kTileRows, rows - k * kTileRows) : 0;
+    sh.bad = 0;
     uint32_t ok = 1;
     const uint8_t* in = a.in;
     uint64_t total = 0;
@@ -944,28 +1390,25 @@ __global__ void __launch_bounds__(kThreads) ec_decode_kernel(DecArgs a) {
       ok = tl.ok;
       sh.tl = tl;
     }
-    if (!ok) report_error(a.report, kDevErrCorrupt);
     sh.ok = ok;
   }
   __syncthreads();
   const uint32_t s = sh.seg, k = sh.tile, n = sh.n, rows = sh.rows;
   const uint32_t pch = s / T, t = s % T;
   float* yseg = a.y + ((uint64_t)t * B + chunk_row0(a.sh, pch)) * D;
-  if (n == 0) return;
+  float* yt = yseg + (uint64_t)k * kTileRows * D;
+  if (n == 0) {
+    if (!sh.ok && tid == 0) report_error(a.report, kDevErrCorrupt);
+    return;
+  }
   if (!sh.ok) {
-    float* yt = yseg + (uint64_t)k * kTileRows * D;
     for (uint32_t i = tid; i < n * D; i += kThreads) yt[i] = 0.0f;
+    if (tid == 0) report_error(a.report, kDevErrCorrupt);
     return;
   }
   const DecTile tl = sh.tl;
-  const float eb = sh.eb, s2 = eb + eb;
-  const uint8_t* sg = a.in + sh.seg_off;
-  const uint64_t sbytes = sh.seg_bytes;
-  const uint32_t rb = rows <= 65536 ? 2 : 4;
-
   if (tl.mode == 0) {  // RAW: rows verbatim
     const float* src = reinterpret_cast<const float*>(tl.rec + 16);
-    float* yt = yseg + (uint64_t)k * kTileRows * D;
     if ((D & 3) == 0) {
       const float4* s4 = reinterpret_cast<const float4*>(src);
       float4* y4 = reinterpret_cast<float4*>(yt);
@@ -976,27 +1419,136 @@ __global__ void __launch_bounds__(kThreads) ec_decode_kernel(DecArgs a) {
     return;
   }
 
-  const uint32_t nblk = (tl.U * D + 63) / 64;
-  const uint32_t off_refs = (uint32_t)align_up(16 + nblk, 4);
-  for (uint32_t i = wv; i < n; i += kThreads / 64) {
-    const uint32_t r = k * kTileRows + i;
-    float* y = yseg + (uint64_t)r * D;
-    bool ok;
+  // ---- BITPACK: stage widths (-> word offsets), bit planes, outliers ----
+  const float eb = sh.eb, s2 = eb + eb;
+  const uint8_t* sg = a.in + sh.seg_off;
+  const uint64_t sbytes = sh.seg_bytes;
+  const uint32_t rb = rows <= 65536 ? 2 : 4;
+  const uint32_t nblk = tl.nblk;
+  uint32_t badw = 0;
+  for (uint32_t b = tid; b < nblk; b += kThreads) {
+    uint32_t w = tl.rec[16 + b];
+    badw |= w > 12;
+    s_width[b] = (uint8_t)w;
+    s_boff[b] = w;
+  }
+  if (badw) sh.bad = 1;
+  const uint32_t sumw = nblk ? block_exclusive_scan(s_boff, nblk, sh.part) : 0;
+  const uint64_t plane_words = (tl.avail - tl.off_pl) / 8;
+  const uint64_t* g_planes = reinterpret_cast<const uint64_t*>(tl.rec + tl.off_pl);
+  const uint32_t* g_opos = reinterpret_cast<const uint32_t*>(tl.rec + tl.off_opos);
+  const uint32_t* g_oval = reinterpret_cast<const uint32_t*>(tl.rec + tl.off_oval);
+  const bool planes_fit = sumw <= plane_words;
+  const bool stage_planes = planes_fit && sumw <= plane_cap;
+  const bool stage_out = tl.nout <= kOutCap;
+  if (stage_planes)
+    for (uint32_t i = tid; i < sumw; i += kThreads) s_planes[i] = g_planes[i];
+  if (stage_out)
+    for (uint32_t i = tid; i < tl.nout; i += kThreads) {
+      s_opos[i] = g_opos[i];
+      s_oval[i] = g_oval[i];
+    }
+  // source of every row: a uid of this record, or a reference into an
+  // earlier record (resolved lane-parallel so the metadata loads overlap)
+  if (tid < n) {
+    const uint32_t i = tid, r = k * kTileRows + i;
+    const uint64_t below = tl.bitmap & ((1ull << i) - 1ull);
+    uint32_t src;
     if ((tl.bitmap >> i) & 1ull) {
-      ok = decode_key_row(tl, i, rows, D, eb, s2, y, false);
+      src = (uint32_t)__popcll(below);
     } else {
-      uint32_t j = i - (uint32_t)__popcll(tl.bitmap & ((1ull << i) - 1ull));
-      uint32_t ref = rb == 2 ? reinterpret_cast<const uint16_t*>(tl.rec + off_refs)[j]
-                             : reinterpret_cast<const uint32_t*>(tl.rec + off_refs)[j];
-      ok = ref < r;
-      if (ok) {
+      const uint32_t j = i - (uint32_t)__popcll(below);
+      const uint32_t ref = rb == 2 ? reinterpret_cast<const uint16_t*>(tl.rec + tl.off_refs)[j]
+                                   : reinterpret_cast<const uint32_t*>(tl.rec + tl.off_refs)[j];
+      if (ref >= r) {
+        src = kBad;
+      } else if (ref >= k * kTileRows) {
+        const uint32_t i2 = ref - k * kTileRows;
+        src = ((tl.bitmap >> i2) & 1ull) ? (uint32_t)__popcll(tl.bitmap & ((1ull << i2) - 1ull))
+                                          : kBad;
+      } else {
         const uint32_t k2 = ref / kTileRows, i2 = ref % kTileRows;
-        DecTile t2 = k2 == k ? tl : locate_tile(sg, sbytes, sh.ntiles, rows, k2, D, true);
-        ok = t2.ok && ((t2.bitmap >> i2) & 1ull);
-        if (ok) ok = decode_key_row(t2, i2, rows, D, eb, s2, y, true);
+        DecTile t2 = locate_tile(sg, sbytes, sh.ntiles, rows, k2, D, true);
+        src = kExt | i;
+        if (!t2.ok || !((t2.bitmap >> i2) & 1ull)) {
+          src = kBad;
+        } else if (t2.mode == 0) {
+          s_xoff[i] = (uint32_t)(t2.rec - sg);
+          s_xu[i] = i2;
+        } else {
+          const uint32_t u2 = (uint32_t)__popcll(t2.bitmap & ((1ull << i2) - 1ull));
+          const uint32_t b0 = (u2 * D) >> 6;
+          // plane word offset of block b0: sum of the record's first b0 widths
+          const uint32_t* w4 = reinterpret_cast<const uint32_t*>(t2.rec + 16);
+          uint32_t base = 0;
+          for (uint32_t q = 0; q < b0 / 4; q++) {
+            uint32_t v = w4[q];
+            v = (v & 0x00ff00ffu) + ((v >> 8) & 0x00ff00ffu);
+            base += (v & 0xffffu) + (v >> 16);
+          }
+          for (uint32_t q = b0 & ~3u; q < b0; q++) base += t2.rec[16 + q];
+          s_xoff[i] = (uint32_t)(t2.rec - sg);
+          s_xu[i] = u2;
+          s_xbase[i] = base;
+        }
       }
     }
-    if (!ok) {
+    s_src[i] = src;
+  }
+  __syncthreads();
+
+  // ---- decode, one wave per output row ----
+  for (uint32_t i = wv; i < n; i += kThreads / 64) {
+    const uint32_t src = s_src[i];
+    float* y = yt + (uint64_t)i * D;
+    bool ok = (src & kBad) == 0;
+    if (ok && !(src & kExt)) {
+      const uint32_t e0 = src * D;
+      if (stage_planes && stage_out)
+        ok = decode_span(y, D, e0, nblk, s_width, s_boff, 0, s_planes, (uint64_t)sumw,
+                         (const uint32_t*)s_opos, (const uint32_t*)s_oval, tl.nout, s2);
+      else if (planes_fit)
+        ok = decode_span(y, D, e0, nblk, s_width, s_boff, 0, g_planes, plane_words, g_opos,
+                         g_oval, tl.nout, s2);
+      else
+        ok = false;
+    } else if (ok) {
+      const uint8_t* rec2 = sg + s_xoff[i];
+      const uint32_t u2 = s_xu[i];
+      const uint32_t w3 = rd32(rec2 + 12);
+      if (((w3 >> 16) & 0xffu) == 0) {  // referenced row stored RAW: re-quantize it
+        const float* src2 = reinterpret_cast<const float*>(rec2 + 16) + (uint64_t)u2 * D;
+        for (uint32_t d = lane; d < D; d += 64) {
+          float v = src2[d];
+          int q;
+          y[d] = quantize(v, eb, s2, q) ? v : (float)q * s2;
+        }
+      } else {
+        DecTile t2;
+        t2.rec = rec2;
+        t2.avail = sbytes - (uint64_t)(rec2 - sg);
+        t2.U = w3 & 0xffffu;
+        t2.nout = rd32(rec2 + 8);
+        // a referenced tile precedes the current one, so it is not the
+        // segment's last tile and holds a full 64 rows
+        const uint32_t n2 = kTileRows;
+        const uint32_t nE = t2.U * D, nb2 = (nE + 63) / 64;
+        const uint32_t off_refs = (uint32_t)align_up(16 + nb2, 4);
+        const uint32_t off_opos = (uint32_t)align_up(off_refs + rb * (n2 - t2.U), 4);
+        const uint32_t off_oval = off_opos + 4 * t2.nout;
+        const uint32_t off_pl = (uint32_t)align_up(off_oval + 4 * t2.nout, 8);
+        if (off_pl > t2.avail) {
+          ok = false;
+        } else {
+          ok = decode_span(y, D, u2 * D, nb2, rec2 + 16, (const uint32_t*)nullptr, s_xbase[i],
+                           reinterpret_cast<const uint64_t*>(rec2 + off_pl),
+                           (t2.avail - off_pl) / 8,
+                           reinterpret_cast<const uint32_t*>(rec2 + off_opos),
+                           reinterpret_cast<const uint32_t*>(rec2 + off_oval), t2.nout, s2);
+        }
+      }
+    }
+    if (!ok || sh.bad) {
       for (uint32_t d = lane; d < D; d += 64) y[d] = 0.0f;
       if (lane == 0) report_error(a.report, kDevErrCorrupt);
     }
@@ -1016,13 +1568,26 @@ hipError_t set_encode_lds_limit(size_t bytes) {
 }
 
 hipError_t launch_encode(const EncArgs& a, hipStream_t s) {
-  size_t lds = encode_lds_bytes(a.sh.D);
-  hipLaunchKernelGGL(ec_encode_kernel, dim3(a.sh.ntiles), dim3(kThreads), lds, s, a);
+  const dim3 grid(a.sh.ntiles), block(kThreads);
+  switch (a.sh.D) {
+    case 64:
+      hipLaunchKernelGGL(ec_encode_fast<1>, grid, block, sizeof(FastLds<1>), s, a);
+      break;
+    case 128:
+      hipLaunchKernelGGL(ec_encode_fast<2>, grid, block, sizeof(FastLds<2>), s, a);
+      break;
+    case 256:
+      hipLaunchKernelGGL(ec_encode_fast<4>, grid, block, sizeof(FastLds<4>), s, a);
+      break;
+    default:
+      hipLaunchKernelGGL(ec_encode_kernel, grid, block, encode_lds_bytes(a.sh.D), s, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(ec_decode_kernel, dim3(a.sh.ntiles), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(ec_decode_kernel, dim3(a.sh.ntiles), dim3(kThreads), decode_lds_bytes(a.sh.D),
+                     s, a);
   return hipGetLastError();
 }
 

@@ -19,8 +19,8 @@ uint64_t aup(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 struct Layout {
   // byte offsets inside the workspace
   uint64_t eb_base, mult, seg_tile_base, hash_off, hash_log2, range_part;
-  uint64_t dyn, ctrl, seg_start, seg_end, chunk_start, seg_U, seg_nout, seg_done;
-  uint64_t tile_status, tile_inserted, tile_rec, hash;
+  uint64_t dyn, seg_start, seg_end, chunk_start, seg_fin;
+  uint64_t tile_status, tile_inserted, tile_rec, tile_U, tile_nout, hash;
   uint64_t dyn_bytes, total;
   uint32_t nbr;
   std::vector<uint32_t> seg_tile_base_v;
@@ -115,7 +115,15 @@ ec_status make_layout(const ec_plan_desc* d, Layout* L) {
   }
   if (tiles >= (1ull << 31)) return EC_ERR_UNSUPPORTED;
   L->seg_tile_base_v[nseg] = (uint32_t)tiles;
-  L->sh = {T, B, D, P, (uint32_t)nseg, (uint32_t)tiles, 64 + aup(8ull * P, 16)};
+  uint32_t tps = 0;
+  for (uint32_t p = 0; p < P; p++) {
+    uint32_t rows = rows_of_chunk(B, P, p), nt = (rows + 63) / 64;
+    uint32_t v = nt ? nt : 1;
+    if (p == 0) tps = v;
+    else if (v != tps) tps = 0;
+    if (tps == 0) break;
+  }
+  L->sh = {T, B, D, P, (uint32_t)nseg, (uint32_t)tiles, 64 + aup(8ull * P, 16), tps};
   L->max_bytes = maxb;
 
   const uint64_t nel = (uint64_t)B * D;
@@ -136,16 +144,15 @@ ec_status make_layout(const ec_plan_desc* d, Layout* L) {
   L->range_part = take(8ull * T * L->nbr);
   o = aup(o, 256);
   L->dyn = o;
-  L->ctrl = take(16);
   L->seg_start = take(8ull * nseg);
   L->seg_end = take(8ull * nseg);
   L->chunk_start = take(8ull * P);
-  L->seg_U = take(4ull * nseg);
-  L->seg_nout = take(4ull * nseg);
-  L->seg_done = take(4ull * nseg);
+  L->seg_fin = take(4ull * nseg);
   L->tile_status = take(8ull * tiles);
   L->tile_inserted = take(4ull * tiles);
   L->tile_rec = take(8ull * tiles);
+  L->tile_U = take(4ull * tiles);
+  L->tile_nout = take(4ull * tiles);
   L->hash = take(8ull * slots);
   o = aup(o, 256);
   L->dyn_bytes = o - L->dyn;
@@ -310,16 +317,15 @@ ec_status ec_plan(const ec_plan_desc* desc, ec_plan_t* out) {
   w.nbr = L.nbr;
   w.dyn = reinterpret_cast<uint64_t*>(ws + L.dyn);
   w.dyn_words = L.dyn_bytes / 8;
-  w.ctrl = reinterpret_cast<uint32_t*>(ws + L.ctrl);
   w.seg_start = reinterpret_cast<uint64_t*>(ws + L.seg_start);
   w.seg_end = reinterpret_cast<uint64_t*>(ws + L.seg_end);
   w.chunk_start = reinterpret_cast<uint64_t*>(ws + L.chunk_start);
-  w.seg_U = reinterpret_cast<uint32_t*>(ws + L.seg_U);
-  w.seg_nout = reinterpret_cast<uint32_t*>(ws + L.seg_nout);
-  w.seg_done = reinterpret_cast<uint32_t*>(ws + L.seg_done);
+  w.seg_fin = reinterpret_cast<uint32_t*>(ws + L.seg_fin);
   w.tile_status = reinterpret_cast<uint64_t*>(ws + L.tile_status);
   w.tile_inserted = reinterpret_cast<uint32_t*>(ws + L.tile_inserted);
   w.tile_rec = reinterpret_cast<uint64_t*>(ws + L.tile_rec);
+  w.tile_U = reinterpret_cast<uint32_t*>(ws + L.tile_U);
+  w.tile_nout = reinterpret_cast<uint32_t*>(ws + L.tile_nout);
   w.hash = reinterpret_cast<uint64_t*>(ws + L.hash);
   *out = pl;
   return EC_OK;

@@ -118,9 +118,10 @@ def test_more_chunks_than_rows():
     assert_parity(make_cfg(2, 3, 8, 7, eb_mode=0, eb=(1e-2,)), x, label="P>B")
 
 
-def test_special_values_and_raw_segments():
+@pytest.mark.parametrize("D", [8, 64, 128])
+def test_special_values_and_raw_segments(D):
     rng = np.random.default_rng(7)
-    T, B, D = 4, 70, 8
+    T, B = 4, 70
     x = rng.normal(0, 1, (T, B, D)).astype(np.float32)
     x[0, 3, 2] = np.nan
     x[0, 4, 1] = np.inf
@@ -134,9 +135,10 @@ def test_special_values_and_raw_segments():
     assert_parity(make_cfg(T, B, D, eb_mode=1, eb=(0.01,)), x, label="special")
 
 
-def test_raw_tiles_and_references_into_them():
+@pytest.mark.parametrize("D", [32, 128, 256])
+def test_raw_tiles_and_references_into_them(D):
     rng = np.random.default_rng(9)
-    B, D = 200, 32
+    B = 200
     x = np.zeros((1, B, D), np.float32)
     x[0, :64] = rng.normal(0, 1, (64, D)) * np.float32(10.0) ** rng.integers(-3, 4, (64, D))
     x[0, 64:] = rng.normal(0, 0.01, (B - 64, D))
@@ -146,19 +148,42 @@ def test_raw_tiles_and_references_into_them():
     assert SF.parse(ref.stream).segments[0].tiles[0].mode == 0
 
 
-def test_eb_to_zero_is_exact():
+@pytest.mark.parametrize("D", [16, 64])
+def test_eb_to_zero_is_exact(D):
     rng = np.random.default_rng(8)
-    x = rng.integers(-1000, 1000, (2, 100, 16)).astype(np.float32)
-    g, _ = assert_parity(make_cfg(2, 100, 16, eb=(1e-30,)), x, label="eb->0")
+    x = rng.integers(-1000, 1000, (2, 100, D)).astype(np.float32)
+    g, _ = assert_parity(make_cfg(2, 100, D, eb=(1e-30,)), x, label="eb->0")
     np.testing.assert_array_equal(g["y"], x)
 
 
-@pytest.mark.parametrize("bits", [1, 4, 12])
-def test_weak_hash_gives_identical_bytes(bits):
-    rng = np.random.default_rng(11 + bits)
-    x = dup_rows(rng, 2, 700, 24, frac_unique=0.3)
-    assert_parity(make_cfg(2, 700, 24, eb_mode=1, eb=(0.02,)), x, hash_bits=bits,
+@pytest.mark.parametrize("bits,D", [(1, 24), (4, 24), (12, 24), (1, 64), (4, 128), (12, 256)])
+def test_weak_hash_gives_identical_bytes(bits, D):
+    rng = np.random.default_rng(11 + bits + D)
+    x = dup_rows(rng, 2, 700, D, frac_unique=0.3)
+    # near-duplicates: rows that differ in one element by less than a bin
+    x[:, 500:] = x[:, :200]
+    x[:, 500:, 3] += np.float32(1e-7)
+    assert_parity(make_cfg(2, 700, D, eb_mode=1, eb=(0.02,)), x, hash_bits=bits,
                   label=f"weak-hash-{bits}")
+
+
+def test_rounding_boundaries_and_code_range_edges():
+    """Values on and next to bin edges and at the ends of the code range,
+    where the fast multiply-by-reciprocal quantizer must defer to division."""
+    eb = np.float32(0.001)
+    s = eb + eb
+    ks = np.arange(-2048, 2049, dtype=np.float32)
+    base = np.concatenate([(ks + 0.5) * s, ks * s, (ks + 0.25) * s])
+    vals = np.concatenate([base, np.nextafter(base, np.float32(np.inf)),
+                           np.nextafter(base, np.float32(-np.inf))]).astype(np.float32)
+    D = 128
+    n = (vals.size + D - 1) // D
+    x = np.zeros(n * D, np.float32)
+    x[:vals.size] = vals
+    x = x.reshape(1, n, D)
+    for d in (128, 16):
+        xx = x.reshape(1, -1, d)
+        assert_parity(make_cfg(1, xx.shape[1], d, eb=(float(eb),)), xx, label=f"edges-D{d}")
 
 
 def test_determinism_across_runs():
