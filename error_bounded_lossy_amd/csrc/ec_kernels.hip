@@ -85,10 +85,22 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
 }
 
 // Cross-workgroup communication uses only agent-scope RELAXED atomics (their
-// values are coherent across the XCDs) plus workgroup-scope fences, which only
-// wait for this wave's own memory operations.  Agent-scope acquire/release
-// would write back or invalidate a whole XCD L2 on every call.
+// values are coherent across the XCDs); agent-scope acquire/release would write
+// back or invalidate a whole XCD L2 on every call.  Ordering is explicit:
+//  * publish: every wave whose atomics a flag announces runs wait_vm() (its
+//    stores and read-modify-writes are then performed at the coherence point)
+//    before the barrier after which the flag is stored.  A workgroup fence or
+//    barrier alone does not wait for global memory on this target, so a flag
+//    could otherwise overtake the data it announces.
+//  * consume: loads of the data are issued only after a load of the flag has
+//    returned the published value (a spin loop or a barrier behind it).
 __device__ __forceinline__ void fence_wg() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup"); }
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// atomic minimum whose result is awaited (the wave stalls until it is performed)
+__device__ __forceinline__ void atomic_min_performed(uint64_t* p, uint64_t v) {
+  const uint64_t old = __hip_atomic_fetch_min(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("" ::"v"(old));
+}
 __device__ __forceinline__ uint64_t ld64(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -182,14 +194,24 @@ __global__ void __launch_bounds__(kThreads) ec_prep_kernel(PrepArgs a) {
   float lo = INFINITY, hi = -INFINITY;
   if (beg < end) {
     if ((nel & 3) == 0) {
+      // four independent 128-bit loads in flight per thread
       const float4* x4 = reinterpret_cast<const float4*>(xt);
-      for (uint64_t i = beg / 4 + threadIdx.x; i < end / 4; i += kThreads) {
-        float4 v = x4[i];
-        float e[4] = {v.x, v.y, v.z, v.w};
+      const uint64_t e4 = end / 4;
+      for (uint64_t i = beg / 4 + threadIdx.x; i < e4; i += 4 * kThreads) {
+        float4 v[4];
 #pragma unroll
-        for (int c = 0; c < 4; c++) {
-          if (e[c] < lo) lo = e[c];  // NaN compares false: skipped
-          if (e[c] > hi) hi = e[c];
+        for (int u = 0; u < 4; u++) {
+          const uint64_t ii = i + (uint64_t)u * kThreads;
+          v[u] = ii < e4 ? x4[ii] : make_float4(NAN, NAN, NAN, NAN);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+          const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+          for (int c = 0; c < 4; c++) {
+            if (e[c] < lo) lo = e[c];  // NaN compares false: skipped
+            if (e[c] > hi) hi = e[c];
+          }
         }
       }
     } else {
@@ -406,9 +428,11 @@ __device__ void complete_tile(const EncArgs& a, EncShared& sh, bool valid, float
   const uint32_t T = a.sh.T, pch = s / T, t = s % T;
   __syncthreads();
   if (tid == 0) {
+    // tid 0 also stored this tile's look-back word and, for a segment's first
+    // tile, the segment and chunk starts: all performed before tile_rec
     st32(&a.w.tile_U[ticket], sh.U);
     st32(&a.w.tile_nout[ticket], sh.mode ? sh.nout : 0u);
-    fence_wg();
+    wait_vm();
     st64(&a.w.tile_rec[ticket], sh.rec_abs + 1);
   }
   if (k + 1 < (ntiles ? ntiles : 1)) return;  // not the segment's last tile
@@ -437,7 +461,7 @@ __device__ void complete_tile(const EncArgs& a, EncShared& sh, bool valid, float
   // tile 0 published seg_start before its record offset, which the loop above
   // has seen (the barriers order this read after that observation)
   const uint64_t seg_start = ld64(&a.w.seg_start[s]) - 1;
-  const uint64_t seg_end = ld64(&a.w.seg_end[s]) - 1;
+  const uint64_t seg_end = sh.rec_abs + sh.rec_size;  // this tile ends the segment
   bool ok = seg_end <= a.out_cap && seg_start + 32 + 4ull * ntiles <= seg_end;
   uint64_t chunk_start = 0;
   if (t == 0) {
@@ -470,7 +494,8 @@ __device__ void complete_tile(const EncArgs& a, EncShared& sh, bool valid, float
     report_error(a.report, kDevErrTimeout);
   }
   if (tid == 0) {
-    fence_wg();
+    // seg_end (stored by tid 0 in place_record) is performed before seg_fin
+    wait_vm();
     st32(&a.w.seg_fin[s], 1u);
   }
   if (ticket + 1 != a.sh.ntiles) return;  // not the stream's last tile
@@ -704,7 +729,7 @@ __global__ void __launch_bounds__(kThreads) ec_encode_kernel(EncArgs a) {
           bool eq = rows_equal(s_codes, xs, xt, iL, cL, D, eb, s2);
           if ((int)lane == L) {
             if (eq) {
-              atomicMin((unsigned long long*)&htab[slot], (unsigned long long)mine);
+              atomic_min_performed(&htab[slot], mine);
               s_slot[i] = slot;
               active = false;
             } else {
@@ -721,11 +746,9 @@ __global__ void __launch_bounds__(kThreads) ec_encode_kernel(EncArgs a) {
         }
       }
     }
+    wait_vm();  // this wave's slot writes are performed before the flag
     __syncthreads();
-    if (tid == 0) {
-      fence_wg();
-      st32(&a.w.tile_inserted[ticket], 1u);
-    }
+    if (tid == 0) st32(&a.w.tile_inserted[ticket], 1u);
     wait_inserted(a, s, k);
     fence_wg();
     __syncthreads();
@@ -858,6 +881,60 @@ __device__ __forceinline__ uint32_t fmix32(uint32_t h) {
   return h;
 }
 
+// OR / sum of a 32-bit value over the wave with DPP butterflies (each step
+// combines disjoint lane sets); the result is returned to every lane.
+template <bool kSum>
+__device__ __forceinline__ uint32_t wave_reduce_dpp(uint32_t v) {
+  auto op = [](uint32_t a, uint32_t b) { return kSum ? a + b : (a | b); };
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast15
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// One bit plane of a block: double the pre-shifted codes, take the carry-out
+// lane mask as plane B and park it in lane B of (lo, hi).  B is an immediate
+// (gfx9 reads at most one SGPR per vector instruction).
+template <int B>
+__device__ __forceinline__ void plane_step(uint32_t& zs, uint32_t& lo, uint32_t& hi) {
+  uint64_t pk;
+  asm volatile("v_add_co_u32_e64 %0, %1, %2, %2" : "=v"(zs), "=s"(pk) : "v"(zs));
+  asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(lo) : "s"((uint32_t)pk), "n"(B));
+  asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(hi) : "s"((uint32_t)(pk >> 32)), "n"(B));
+}
+
+// Bit planes w-1 .. 0 of the codes zz (w <= 12): plane b ends up in lane b.
+__device__ __forceinline__ void bit_planes(uint32_t zz, uint32_t w, uint32_t& lo, uint32_t& hi) {
+  uint32_t zs = w ? zz << (32u - w) : 0u;  // top plane at bit 31
+  switch (w) {
+    case 12: plane_step<11>(zs, lo, hi); [[fallthrough]];
+    case 11: plane_step<10>(zs, lo, hi); [[fallthrough]];
+    case 10: plane_step<9>(zs, lo, hi); [[fallthrough]];
+    case 9: plane_step<8>(zs, lo, hi); [[fallthrough]];
+    case 8: plane_step<7>(zs, lo, hi); [[fallthrough]];
+    case 7: plane_step<6>(zs, lo, hi); [[fallthrough]];
+    case 6: plane_step<5>(zs, lo, hi); [[fallthrough]];
+    case 5: plane_step<4>(zs, lo, hi); [[fallthrough]];
+    case 4: plane_step<3>(zs, lo, hi); [[fallthrough]];
+    case 3: plane_step<2>(zs, lo, hi); [[fallthrough]];
+    case 2: plane_step<1>(zs, lo, hi); [[fallthrough]];
+    case 1: plane_step<0>(zs, lo, hi); [[fallthrough]];
+    default: break;
+  }
+}
+
+// v + v + (bit `lane` of the wave-uniform mask m): appends one bit plane to
+// codes being rebuilt most-significant plane first.
+__device__ __forceinline__ uint32_t double_add_plane(uint32_t v, uint64_t m) {
+  uint32_t r;
+  uint64_t c;
+  asm volatile("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(c) : "v"(v), "s"(m));
+  return r;
+}
+
 // Exact quantization with a multiply by r = fl(1/s) (correctly rounded): the
 // product is within 2^-11 of fl(x/s) for |x/s| < 2048, so whenever it lies at
 // least 2^-10 away from every rounding boundary (k + 1/2) and well inside the
@@ -899,7 +976,9 @@ template <int C>
 __global__ void __launch_bounds__(kThreads) ec_encode_fast(EncArgs a) {
   constexpr uint32_t D = 64u * C;
   constexpr uint32_t kRowsPerWave = kTileRows / (kThreads / 64);      // 16
-  constexpr uint32_t kBatch = (8 / C) < 1 ? 1 : (8 / C);  // rows per load batch
+  // all of a wave's rows are loaded up front when they fit in 32 registers
+  constexpr bool kPreload = kRowsPerWave * C <= 32;
+  constexpr uint32_t kBatch = kPreload ? kRowsPerWave : (32 / C);  // rows per batch
   extern __shared__ __align__(16) uint8_t smem[];
   FastLds<C>& L = *reinterpret_cast<FastLds<C>*>(smem);
   __shared__ EncShared sh;
@@ -917,6 +996,19 @@ __global__ void __launch_bounds__(kThreads) ec_encode_fast(EncArgs a) {
   const uint32_t row0 = chunk_row0(a.sh, pch);
   const float* xs = a.x + ((uint64_t)t * a.sh.B + row0) * D;
   const float* xt = xs + (uint64_t)k * kTileRows * D;
+  // the wave's rows: the loads are issued before the error bound is known, so
+  // they and the range-partial reduction share one memory latency
+  const uint32_t rbeg = wv * kRowsPerWave;
+  float xv[kBatch][C];  // kBatch == kRowsPerWave when the whole share is preloaded
+  if (kPreload) {
+#pragma unroll
+    for (uint32_t rr = 0; rr < kBatch; rr++)
+#pragma unroll
+      for (uint32_t j = 0; j < C; j++) {
+        const uint32_t i = rbeg + rr;
+        xv[rr][j] = i < n ? xt[(uint64_t)i * D + 64 * j + lane] : 0.0f;
+      }
+  }
   if (wv == 0) {
     bool v;
     float e = table_eb(a, t, v);
@@ -931,22 +1023,27 @@ __global__ void __launch_bounds__(kThreads) ec_encode_fast(EncArgs a) {
   const float s2 = eb + eb;
   const float r2 = 1.0f / s2;
   const bool valid = sh.valid != 0;
+  uint32_t hk1[C], hk2[C];  // odd 24-bit multipliers per element position
+#pragma unroll
+  for (uint32_t j = 0; j < C; j++) {
+    hk1[j] = (fmix32(64 * j + lane + 0x9e3779b9u) & 0xffffffu) | 1u;
+    hk2[j] = (fmix32(64 * j + lane + 0x7f4a7c15u) & 0xffffffu) | 1u;
+  }
   const uint64_t g0 = ((uint64_t)t * a.sh.B + row0 + (uint64_t)k * kTileRows) * D;
 
   // ---- quantize, planes, widths, outlier masks, row hashes ----
-  // Rows are processed in small fully unrolled batches (loads first).
   if (valid) {
-    const uint32_t rbeg = wv * kRowsPerWave;
 #pragma unroll 1
     for (uint32_t rb = 0; rb < kRowsPerWave; rb += kBatch) {
-      float v[kBatch][C];
+      if (!kPreload) {
 #pragma unroll
-      for (uint32_t rr = 0; rr < kBatch; rr++)
+        for (uint32_t rr = 0; rr < kBatch; rr++)
 #pragma unroll
-        for (uint32_t j = 0; j < C; j++) {
-          const uint32_t i = rbeg + rb + rr;
-          v[rr][j] = i < n ? xt[(uint64_t)i * D + 64 * j + lane] : 0.0f;
-        }
+          for (uint32_t j = 0; j < C; j++) {
+            const uint32_t i = rbeg + rb + rr;
+            xv[rr][j] = i < n ? xt[(uint64_t)i * D + 64 * j + lane] : 0.0f;
+          }
+      }
 #pragma unroll
       for (uint32_t rr = 0; rr < kBatch; rr++) {
         const uint32_t i = rbeg + rb + rr;
@@ -954,54 +1051,55 @@ __global__ void __launch_bounds__(kThreads) ec_encode_fast(EncArgs a) {
         uint32_t hlo = 0, hhi = 0;
 #pragma unroll
         for (uint32_t j = 0; j < C; j++) {
-          const float x = v[rr][j];
-          const uint32_t d = 64 * j + lane;
-          // q = rint(x / 2eb) via the correctly rounded reciprocal; the IEEE
-          // division decides near rounding boundaries (see quantize_fast)
+          const float x = xv[rr][j];
+          // q = rint(x / 2eb) via the correctly rounded reciprocal.  When the
+          // product is at least 2^-10 from every rounding boundary and inside
+          // the code range, rint agrees with rint(fl(x/s)) and |x - fl(q s)| is
+          // strictly below eb, so the value is not an outlier; otherwise the
+          // IEEE division and the reconstruction check decide (rare).
           const float tp = x * r2;
           float qf = rintf(tp);
           const float f = tp - qf;
-          const bool unsure = !(fabsf(f) < 0.4990234375f && fabsf(tp) < 2046.5f);
-          bool oor = false;
+          // one compare: |f| < 2046.5/4104 (= 0.49866, at least 2^-10 from 1/2)
+          // and |tp| < 2046.5; NaN or infinite products are unsure
+          const bool unsure = !(fmaxf(fabsf(f) * 4104.0f, fabsf(tp)) < 2046.5f);
+          uint64_t om = 0;
           if (__any(unsure)) {
+            bool out = false;
             if (unsure) {
               const float tq = x / s2;
-              oor = !(fabsf(tq) <= 2047.0f);
+              const bool oor = !(fabsf(tq) <= 2047.0f);
               qf = rintf(tq);
+              const float xh = qf * s2;
+              const float err = x - xh;
+              out = oor || !(fabsf(err) <= eb);
+              if (out) {  // outlier: code 0, raw bits enter the row hash
+                qf = 0.0f;
+                const uint32_t bits = f2u(x);
+                hlo += (bits ^ 0x7f4a7c15u) * 0x85ebca6bu + hk1[j];
+                hhi += (bits ^ 0x3c6ef372u) * 0xc2b2ae35u + hk2[j];
+              }
             }
+            om = __ballot(out);
           }
-          const float xh = qf * s2;
-          const float err = x - xh;
-          const bool out = oor || !(fabsf(err) <= eb);
-          const int q = out ? 0 : (int)qf;
-          const uint32_t zz = zigzag(q);
-          uint32_t h = ((out ? f2u(x) : (uint32_t)q) ^ (d * 0x9e3779b9u) ^ (out ? 0x7f4a7c15u : 0u));
-          h *= 0x85ebca6bu;
-          h ^= h >> 16;
-          hlo += h;
-          hhi += h * (2u * d + 1u);
-          // width = bit length of the chunk's largest zigzag code (binary
-          // search with ballots), then one ballot per bit plane
-          uint32_t lo = 0, hi = 12;
-          while (lo < hi) {
-            const uint32_t mid = (lo + hi) >> 1;
-            if (__any((zz >> mid) != 0u)) lo = mid + 1;
-            else hi = mid;
-          }
-          const uint32_t w = lo;
-          uint64_t mine = 0;  // lane b keeps plane b
-          for (uint32_t b = 0; b < w; b++) {
-            const uint64_t pk = __ballot((zz >> b) & 1u);
-            mine = lane == b ? pk : mine;
-          }
-          if (lane < w) L.planes[i][j][lane] = mine;
-          const uint64_t om = __ballot(out);
+          const int q = (int)qf;
+          const uint32_t zz = ((uint32_t)q << 1) ^ (uint32_t)(q >> 31);
+          // row hash: position-weighted sums of the codes (two 32-bit halves)
+          hlo += __umul24(zz, hk1[j]);
+          hhi += __umul24(zz, hk2[j]);
+          // width = bit length of the largest code of the block; plane b is
+          // the ballot of bit b and ends up in lane b
+          const uint32_t mx = wave_reduce_dpp<false>(zz);
+          const uint32_t w = mx ? 32u - __clz(mx) : 0u;
+          uint32_t plo = 0, phi = 0;
+          bit_planes(zz, w, plo, phi);
+          if (lane < w) L.planes[i][j][lane] = ((uint64_t)phi << 32) | plo;
           if (lane == 0) {
             L.omask[i][j] = om;
             L.w[i][j] = (uint8_t)w;
           }
         }
-        const uint64_t H = ((uint64_t)wave_sum_u32(hhi) << 32) | wave_sum_u32(hlo);
+        const uint64_t H = ((uint64_t)wave_reduce_dpp<true>(hhi) << 32) | wave_reduce_dpp<true>(hlo);
         if (lane == 0) s_hash[i] = H;
       }
     }
@@ -1076,7 +1174,7 @@ __global__ void __launch_bounds__(kThreads) ec_encode_fast(EncArgs a) {
         eq = __all(eq);
         if ((int)lane == Ln) {
           if (eq) {
-            atomicMin((unsigned long long*)&htab[slot], (unsigned long long)mine);
+            atomic_min_performed(&htab[slot], mine);
             s_slot[i] = slot;
             active = false;
           } else {
@@ -1092,11 +1190,9 @@ __global__ void __launch_bounds__(kThreads) ec_encode_fast(EncArgs a) {
         }
       }
     }
+    wait_vm();  // this wave's slot writes are performed before the flag
     __syncthreads();
-    if (tid == 0) {
-      fence_wg();
-      st32(&a.w.tile_inserted[ticket], 1u);
-    }
+    if (tid == 0) st32(&a.w.tile_inserted[ticket], 1u);
     wait_inserted(a, s, k);
     fence_wg();
     __syncthreads();
@@ -1210,6 +1306,18 @@ struct DecShared {
   DecTile tl;
   uint32_t part[kThreads / 64];
 };
+
+// The stream is read-only while it is decoded: reading its bit planes
+// through the constant address space lets wave-uniform loads be scalar loads.
+typedef const __attribute__((address_space(4))) uint64_t const_u64;
+__device__ __forceinline__ const_u64* as_const_u64(const uint8_t* p) {
+  return (const_u64*)(uintptr_t)p;
+}
+
+__device__ __forceinline__ uint32_t uniform32(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+  return ((uint64_t)uniform32((uint32_t)(v >> 32)) << 32) | uniform32((uint32_t)v);
+}
 
 __device__ __forceinline__ uint64_t rd64(const uint8_t* p) {
   return *reinterpret_cast<const uint64_t*>(p);
@@ -1555,6 +1663,301 @@ __global__ void __launch_bounds__(kThreads) ec_decode_kernel(DecArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// decoder for D = 64*C.  The stream and the output are restrict kernel
+// arguments, so the wave-uniform bit-plane loads become scalar loads and each
+// plane costs one conditional select per element (codes built MSB first).
+// ---------------------------------------------------------------------------
+// Thread 0: check the stream header, chunk table, segment header and tile
+// record of tile `ticket`; fills sh (offsets relative to `in`).
+__device__ void dec_locate(const DecArgs& a, const uint8_t* in, uint32_t ticket, DecShared& sh,
+                           uint64_t& rec_off) {
+  const uint32_t T = a.sh.T, B = a.sh.B, D = a.sh.D, P = a.sh.P;
+  uint32_t s = find_segment(a.seg_tile_base, a.sh.nseg, ticket);
+  uint32_t pch = s / T, t = s % T;
+  uint32_t r0 = chunk_row0(a.sh, pch), rows = chunk_row0(a.sh, pch + 1) - r0;
+  uint32_t nt = (rows + kTileRows - 1) / kTileRows;
+  uint32_t k = ticket - a.seg_tile_base[s];
+  sh.seg = s;
+  sh.tile = k;
+  sh.rows = rows;
+  sh.ntiles = nt;
+  sh.n = nt ? min(kTileRows, rows - k * kTileRows) : 0;
+  sh.bad = 0;
+  uint32_t ok = 1;
+  uint64_t total = 0;
+  if (a.cap < 64) ok = 0;
+  if (ok) {
+    const uint32_t* h = reinterpret_cast<const uint32_t*>(in);
+    total = rd64(in + 48);
+    ok = h[0] == kMagic && h[1] == (kVersion | (kCoderBitpack << 16)) && h[2] == T &&
+         h[3] == B && h[4] == D && h[5] == P && h[6] == kTileRows && h[7] <= 1 &&
+         rd64(in + 40) == 4ull * T * B * D && rd64(in + 56) == 0 && total <= a.cap;
+  }
+  uint64_t base = 64 + align_up(8ull * P, 16);
+  uint64_t chunk = base, cb = 0;
+  if (ok && base > total) ok = 0;
+  for (uint32_t q = 0; ok && q <= pch; q++) {
+    cb = rd64(in + 64 + 8ull * q);
+    if (cb < align_up(8ull * T, 16) || cb > total - chunk) ok = 0;
+    else if (q < pch) chunk += cb;
+  }
+  uint64_t so = 0, sb = 0;
+  if (ok) {
+    so = rd64(in + chunk + 8ull * t);
+    if (so < align_up(8ull * T, 16) || (so & 15u) || so + 32 > cb) ok = 0;
+  }
+  if (ok) {
+    const uint8_t* sg = in + chunk + so;
+    uint32_t flags = rd32(sg + 12);
+    float eb = __uint_as_float(rd32(sg + 8));
+    sb = rd64(sg + 24);
+    int valid = isfinite(eb) && eb > 0.0f && isfinite(eb + eb);
+    if (rd32(sg) != rows || rd32(sg + 4) != nt || flags > 1 || (int)flags != valid ||
+        sb > cb - so || sb < 32 + align_up(4ull * nt, 16))
+      ok = 0;
+    sh.eb = eb;
+    sh.valid = flags;
+  }
+  sh.seg_off = chunk + so;
+  sh.seg_bytes = sb;
+  rec_off = 0;
+  if (ok && nt) {
+    DecTile tl = locate_tile(in + chunk + so, sb, nt, rows, k, D, sh.valid != 0);
+    ok = tl.ok;
+    sh.tl = tl;
+    rec_off = (uint64_t)(tl.rec - in);
+  }
+  sh.ok = ok;
+}
+
+// Decode one 64-element block (lane = element): w <= 12 planes from word
+// `off` of `planes` (valid words: [0, nwords)).  The planes are fetched in
+// one burst of 8 or 12 words when that stays inside the record's segment;
+// bits past w are masked off.
+template <typename PP>
+__device__ __forceinline__ float decode_block(PP planes, uint32_t off, uint32_t w,
+                                              uint64_t nwords, float s2) {
+  uint32_t zz = 0;
+  if (w <= 8 && (uint64_t)off + 8 <= nwords) {
+    uint64_t p[8];
+#pragma unroll
+    for (int q = 0; q < 8; q++) p[q] = planes[off + q];
+#pragma unroll
+    for (int q = 7; q >= 0; q--) zz = double_add_plane(zz, p[q]);
+  } else if ((uint64_t)off + 12 <= nwords) {
+    uint64_t p[12];
+#pragma unroll
+    for (int q = 0; q < 12; q++) p[q] = planes[off + q];
+#pragma unroll
+    for (int q = 11; q >= 0; q--) zz = double_add_plane(zz, p[q]);
+  } else {
+    for (int q = (int)w - 1; q >= 0; q--) zz = double_add_plane(zz, planes[off + (uint32_t)q]);
+  }
+  zz &= (1u << w) - 1u;
+  return (float)unzigzag(zz) * s2;
+}
+
+// Overwrite the outliers of E[e0, e0 + D) (sorted positions) in the row values.
+template <int C, typename OP>
+__device__ __forceinline__ void patch_outliers(float (&v)[C], uint32_t e0, OP opos, OP oval,
+                                               uint32_t nout) {
+  constexpr uint32_t D = 64u * C;
+  const uint32_t lane = threadIdx.x & 63;
+  uint32_t lo = 0, hi = nout;
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi) >> 1;
+    if (opos[mid] < e0) lo = mid + 1;
+    else hi = mid;
+  }
+  for (; lo < nout; lo++) {
+    const uint32_t pos = opos[lo];
+    if (pos >= e0 + D) break;
+    const uint32_t d = pos - e0;
+#pragma unroll
+    for (uint32_t j = 0; j < C; j++)
+      if (d == 64 * j + lane) v[j] = __uint_as_float(oval[lo]);
+  }
+}
+
+template <int C>
+__global__ void __launch_bounds__(kThreads) ec_decode_fast(const uint8_t* __restrict__ in,
+                                                          float* __restrict__ yout, DecArgs a) {
+  constexpr uint32_t D = 64u * C;
+  constexpr uint32_t kExt = 0x80000000u, kBad = 0x40000000u;
+  __shared__ DecShared sh;
+  __shared__ uint64_t s_rec;
+  __shared__ uint32_t s_src[kTileRows], s_xoff[kTileRows], s_xu[kTileRows], s_xbase[kTileRows];
+  __shared__ uint8_t s_width[kTileRows * C];
+  __shared__ uint32_t s_boff[kTileRows * C];
+  __shared__ uint32_t s_opos[kOutCap], s_oval[kOutCap];
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const uint32_t T = a.sh.T, B = a.sh.B;
+  if (tid == 0) {
+    uint64_t ro;
+    dec_locate(a, in, blockIdx.x, sh, ro);
+    s_rec = ro;
+  }
+  __syncthreads();
+  const uint32_t s = sh.seg, k = sh.tile, n = sh.n, rows = sh.rows;
+  const uint32_t pch = s / T, t = s % T;
+  float* yt = yout + ((uint64_t)t * B + chunk_row0(a.sh, pch) + (uint64_t)k * kTileRows) * D;
+  if (n == 0) {
+    if (!sh.ok && tid == 0) report_error(a.report, kDevErrCorrupt);
+    return;
+  }
+  if (!sh.ok) {
+    for (uint32_t i = tid; i < n * D; i += kThreads) yt[i] = 0.0f;
+    if (tid == 0) report_error(a.report, kDevErrCorrupt);
+    return;
+  }
+  // offsets read from LDS are wave-uniform: say so, so that loads through
+  // them are scalar
+  const uint8_t* sg = in + uniform64(sh.seg_off);
+  const uint8_t* rec = in + uniform64(s_rec);
+  const uint32_t mode = uniform32(sh.tl.mode), U = uniform32(sh.tl.U), nout = uniform32(sh.tl.nout);
+  if (mode == 0) {  // RAW: rows verbatim
+    const float4* s4 = reinterpret_cast<const float4*>(rec + 16);
+    float4* y4 = reinterpret_cast<float4*>(yt);
+    for (uint32_t i = tid; i < n * D / 4; i += kThreads) y4[i] = s4[i];
+    return;
+  }
+  const float eb = sh.eb, s2 = eb + eb;
+  const uint64_t sbytes = uniform64(sh.seg_bytes);
+  const uint32_t rb = rows <= 65536 ? 2 : 4;
+  const uint64_t bitmap = uniform64(sh.tl.bitmap);
+  const uint32_t nblk = U * C;
+  const uint32_t off_refs = uniform32(sh.tl.off_refs), off_opos = uniform32(sh.tl.off_opos);
+  const uint32_t off_oval = uniform32(sh.tl.off_oval), off_pl = uniform32(sh.tl.off_pl);
+  const uint64_t plane_words = (uniform64(sh.tl.avail) - off_pl) / 8;
+  const_u64* planes = as_const_u64(rec + off_pl);
+  const uint32_t* g_opos = reinterpret_cast<const uint32_t*>(rec + off_opos);
+  const uint32_t* g_oval = reinterpret_cast<const uint32_t*>(rec + off_oval);
+  uint32_t badw = 0;
+  for (uint32_t b = tid; b < nblk; b += kThreads) {
+    const uint32_t w = rec[16 + b];
+    badw |= w > 12;
+    s_width[b] = (uint8_t)w;
+    s_boff[b] = w;
+  }
+  if (badw) sh.bad = 1;
+  const uint32_t sumw = nblk ? block_exclusive_scan(s_boff, nblk, sh.part) : 0;
+  if (sumw > plane_words && tid == 0) sh.bad = 1;
+  const bool stage_out = nout <= kOutCap;
+  if (stage_out)
+    for (uint32_t i = tid; i < nout; i += kThreads) {
+      s_opos[i] = g_opos[i];
+      s_oval[i] = g_oval[i];
+    }
+  if (tid < n) {  // source of every row (lane-parallel, so metadata loads overlap)
+    const uint32_t i = tid, r = k * kTileRows + i;
+    const uint64_t below = bitmap & ((1ull << i) - 1ull);
+    uint32_t src;
+    if ((bitmap >> i) & 1ull) {
+      src = (uint32_t)__popcll(below);
+    } else {
+      const uint32_t j = i - (uint32_t)__popcll(below);
+      const uint32_t ref = rb == 2 ? reinterpret_cast<const uint16_t*>(rec + off_refs)[j]
+                                   : reinterpret_cast<const uint32_t*>(rec + off_refs)[j];
+      if (ref >= r) {
+        src = kBad;
+      } else if (ref >= k * kTileRows) {
+        const uint32_t i2 = ref - k * kTileRows;
+        src = ((bitmap >> i2) & 1ull) ? (uint32_t)__popcll(bitmap & ((1ull << i2) - 1ull)) : kBad;
+      } else {
+        const uint32_t k2 = ref / kTileRows, i2 = ref % kTileRows;
+        DecTile t2 = locate_tile(sg, sbytes, sh.ntiles, rows, k2, D, true);
+        src = kExt | i;
+        if (!t2.ok || !((t2.bitmap >> i2) & 1ull)) {
+          src = kBad;
+        } else if (t2.mode == 0) {
+          s_xoff[i] = (uint32_t)(t2.rec - sg);
+          s_xu[i] = i2;
+        } else {
+          const uint32_t u2 = (uint32_t)__popcll(t2.bitmap & ((1ull << i2) - 1ull));
+          const uint32_t b0 = u2 * C;
+          const uint32_t* w4 = reinterpret_cast<const uint32_t*>(t2.rec + 16);
+          uint32_t base = 0;
+          for (uint32_t q = 0; q < b0 / 4; q++) {
+            uint32_t v = w4[q];
+            v = (v & 0x00ff00ffu) + ((v >> 8) & 0x00ff00ffu);
+            base += (v & 0xffffu) + (v >> 16);
+          }
+          for (uint32_t q = b0 & ~3u; q < b0; q++) base += t2.rec[16 + q];
+          s_xoff[i] = (uint32_t)(t2.rec - sg);
+          s_xu[i] = u2;
+          s_xbase[i] = base;
+        }
+      }
+    }
+    s_src[i] = src;
+  }
+  __syncthreads();
+
+  const bool tile_bad = sh.bad != 0;
+  for (uint32_t i = wv; i < n; i += kThreads / 64) {
+    const uint32_t src = __builtin_amdgcn_readfirstlane(s_src[i]);
+    float* y = yt + (uint64_t)i * D;
+    bool ok = !tile_bad && (src & kBad) == 0;
+    float v[C];
+    if (ok && !(src & kExt)) {
+      const uint32_t u = src;
+#pragma unroll
+      for (uint32_t j = 0; j < C; j++) {
+        const uint32_t b = u * C + j;
+        const uint32_t w = __builtin_amdgcn_readfirstlane(s_width[b]);
+        const uint32_t off = __builtin_amdgcn_readfirstlane(s_boff[b]);
+        ok = ok && (uint64_t)off + w <= plane_words;
+        v[j] = ok ? decode_block(planes, off, w, plane_words, s2) : 0.0f;
+      }
+      if (nout) {
+        if (stage_out) patch_outliers<C>(v, u * D, (const uint32_t*)s_opos, (const uint32_t*)s_oval, nout);
+        else patch_outliers<C>(v, u * D, g_opos, g_oval, nout);
+      }
+    } else if (ok) {
+      const uint8_t* rec2 = sg + __builtin_amdgcn_readfirstlane(s_xoff[i]);
+      const uint32_t u2 = __builtin_amdgcn_readfirstlane(s_xu[i]);
+      const uint32_t w3 = rd32(rec2 + 12);
+      if (((w3 >> 16) & 0xffu) == 0) {  // referenced row stored RAW: re-quantize it
+        const float* src2 = reinterpret_cast<const float*>(rec2 + 16) + (uint64_t)u2 * D;
+#pragma unroll
+        for (uint32_t j = 0; j < C; j++) {
+          const float xv = src2[64 * j + lane];
+          int q;
+          v[j] = quantize(xv, eb, s2, q) ? xv : (float)q * s2;
+        }
+      } else {
+        // a referenced tile precedes this one, so it holds a full 64 rows
+        const uint32_t U2 = w3 & 0xffffu, nout2 = rd32(rec2 + 8);
+        const uint32_t nb2 = U2 * C;
+        const uint32_t o_refs = (uint32_t)align_up(16 + nb2, 4);
+        const uint32_t o_opos = (uint32_t)align_up(o_refs + rb * (kTileRows - U2), 4);
+        const uint32_t o_oval = o_opos + 4 * nout2;
+        const uint32_t o_pl = (uint32_t)align_up(o_oval + 4 * nout2, 8);
+        const uint64_t avail2 = sbytes - (uint64_t)(rec2 - sg);
+        ok = o_pl <= avail2 && u2 < U2;
+        const uint64_t pw2 = ok ? (avail2 - o_pl) / 8 : 0;
+        const_u64* planes2 = as_const_u64(rec2 + o_pl);
+        uint32_t run = __builtin_amdgcn_readfirstlane(s_xbase[i]);
+#pragma unroll
+        for (uint32_t j = 0; j < C; j++) {
+          const uint32_t w = ok ? rec2[16 + u2 * C + j] : 0u;
+          ok = ok && w <= 12 && (uint64_t)run + w <= pw2;
+          v[j] = ok ? decode_block(planes2, run, w, pw2, s2) : 0.0f;
+          run += w;
+        }
+        if (ok && nout2)
+          patch_outliers<C>(v, u2 * D, reinterpret_cast<const uint32_t*>(rec2 + o_opos),
+                            reinterpret_cast<const uint32_t*>(rec2 + o_oval), nout2);
+      }
+    }
+    ok = __all(ok);
+#pragma unroll
+    for (uint32_t j = 0; j < C; j++) y[64 * j + lane] = ok ? v[j] : 0.0f;
+    if (!ok && lane == 0) report_error(a.report, kDevErrCorrupt);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_prep(const PrepArgs& a, uint32_t grid, hipStream_t s) {
@@ -1586,8 +1989,20 @@ hipError_t launch_encode(const EncArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_decode(const DecArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(ec_decode_kernel, dim3(a.sh.ntiles), dim3(kThreads), decode_lds_bytes(a.sh.D),
-                     s, a);
+  const dim3 grid(a.sh.ntiles), block(kThreads);
+  switch (a.sh.D) {
+    case 64:
+      hipLaunchKernelGGL(ec_decode_fast<1>, grid, block, 0, s, a.in, a.y, a);
+      break;
+    case 128:
+      hipLaunchKernelGGL(ec_decode_fast<2>, grid, block, 0, s, a.in, a.y, a);
+      break;
+    case 256:
+      hipLaunchKernelGGL(ec_decode_fast<4>, grid, block, 0, s, a.in, a.y, a);
+      break;
+    default:
+      hipLaunchKernelGGL(ec_decode_kernel, grid, block, decode_lds_bytes(a.sh.D), s, a);
+  }
   return hipGetLastError();
 }
 

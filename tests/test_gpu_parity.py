@@ -206,6 +206,45 @@ def test_per_segment_ratio_and_chunk_sizes():
         assert g["per"][seg.p * 3 + seg.t] == pytest.approx(4 * rows * 32 / seg.nbytes)
 
 
+def describe_segment_diff(g, r, D):
+    """Where two segment byte strings (same length) first differ: header field,
+    tile directory entry, or tile record and the part of it."""
+    idx = np.flatnonzero(g != r)
+    if idx.size == 0:
+        return "identical"
+    i = int(idx[0])
+    nt = int(r[4:8].view(np.uint32)[0])
+    head = f"{idx.size} bytes differ, first at {i}"
+    if i < 32:
+        return f"{head}: segment header word {i // 4}"
+    if i < 32 + 4 * nt:
+        return f"{head}: tile directory entry {(i - 32) // 4}"
+    dirs = r[32:32 + 4 * nt].view(np.uint32).astype(np.int64)
+    if nt == 0 or i < dirs[0]:
+        return f"{head}: tile directory padding"
+    j = int(np.searchsorted(dirs, i, side="right") - 1)
+    o = i - int(dirs[j])
+    rec = r[dirs[j]:]
+    n_out = int(rec[8:12].view(np.uint32)[0])
+    u_t = int(rec[12:14].view(np.uint16)[0])
+    mode = int(rec[14])
+    if o < 16:
+        part = "record header"
+    elif mode == 0:
+        part = "raw rows"
+    else:
+        rows = int(r[0:4].view(np.uint32)[0])
+        n = min(64, rows - 64 * j)
+        nblk = (u_t * D + 63) // 64
+        rb = 2 if rows <= 65536 else 4
+        o_refs = (16 + nblk + 3) // 4 * 4
+        o_opos = (o_refs + rb * (n - u_t) + 3) // 4 * 4
+        o_pl = (o_opos + 8 * n_out + 7) // 8 * 8
+        part = ("widths" if o < o_refs else "refs" if o < o_opos else
+                "outliers" if o < o_pl else "planes")
+    return f"{head}: tile {j} (U_t={u_t}, n_out={n_out}, mode={mode}) {part} byte {o}"
+
+
 @pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
 def test_workloads_full_size_sampled_tables(name):
     """Full-size batch on the GPU (the launch the benchmark times); the oracle
@@ -233,9 +272,10 @@ def test_workloads_full_size_sampled_tables(name):
     rsegs = SF.parse_segments(ref.stream)
     for j, t in enumerate(picks):
         gs, rs = gsegs[t], rsegs[j]
-        assert gs.nbytes == rs.nbytes
-        assert np.array_equal(gst[gs.offset:gs.offset + gs.nbytes],
-                              ref.stream[rs.offset:rs.offset + rs.nbytes])
+        assert gs.nbytes == rs.nbytes, (t, gs.nbytes, rs.nbytes)
+        gb = gst[gs.offset:gs.offset + gs.nbytes]
+        rb = ref.stream[rs.offset:rs.offset + rs.nbytes]
+        assert np.array_equal(gb, rb), f"table {t}: " + describe_segment_diff(gb, rb, D)
     yo = O.decompress(cfg, ref.stream)
     yg = y[picks].cpu().numpy()
     np.testing.assert_array_equal(yg.view(np.uint32), yo.view(np.uint32))
