@@ -83,6 +83,130 @@ def cpu_baseline(x_cpu, w, min_seconds: float):
                       f"{done_bytes / 2**20:.0f} MiB) of batch t={w.iteration}, {spent:.1f} s"}
 
 
+KERNEL_PREFIX = {"prep": "ec_prep", "encode": ("ec_encode", "ec_quantize"), "assemble": "ec_assemble",
+                 "decode": "ec_decode"}
+
+
+def _short_kernel(name: str) -> str:
+    name = name.replace("ec::(anonymous namespace)::", "")
+    if name.startswith("void "):
+        name = name[5:]
+    return name.split("(")[0]
+
+
+def _read_counter_csvs(d: str):
+    """{kernel: {counter: [per-dispatch values]}} from a rocprofv3 --pmc run."""
+    import csv
+    import glob
+    out = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                k = _short_kernel(row.get("Kernel_Name", "?"))
+                c = row.get("Counter_Name")
+                out.setdefault(k, {}).setdefault(c, []).append(float(row.get("Counter_Value") or 0))
+    return out
+
+
+def summarize_counters(d: str, workload: str, copy_bytes: int, command: str):
+    """HBM traffic per launch of each path kernel from four rocprofv3 --pmc runs
+    (FETCH_SIZE and WRITE_SIZE of the workload, and of a plain copy of known
+    size): each counter is scaled by bytes-moved / counter-reading of the copy.
+    Writes profiles/<kernel>_<workload>_counters.json."""
+    wf = _read_counter_csvs(os.path.join(d, f"pmc_{workload}_fetch"))
+    ww = _read_counter_csvs(os.path.join(d, f"pmc_{workload}_write"))
+    cf = _read_counter_csvs(os.path.join(d, "pmc_copy_fetch"))
+    cw = _read_counter_csvs(os.path.join(d, "pmc_copy_write"))
+
+    def copy_kib(tab, counter):
+        vals = [v for k, cs in tab.items() for v in cs.get(counter, [])]
+        vals = sorted(vals)[len(vals) // 4:]  # drop warm-up outliers, keep the bulk
+        return sum(vals) / len(vals)
+
+    f_kib, w_kib = copy_kib(cf, "FETCH_SIZE"), copy_kib(cw, "WRITE_SIZE")
+    f_scale = copy_bytes / (f_kib * 1024.0)
+    w_scale = copy_bytes / (w_kib * 1024.0)
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    for kern, prefix in KERNEL_PREFIX.items():
+        fk = [v for k, cs in wf.items() if k.startswith(prefix) for v in cs.get("FETCH_SIZE", [])]
+        wk = [v for k, cs in ww.items() if k.startswith(prefix) for v in cs.get("WRITE_SIZE", [])]
+        if not fk or not wk:
+            continue
+        names = sorted({k for k in list(wf) + list(ww) if k.startswith(prefix)})
+        fetch = sum(fk) / len(fk)
+        write = sum(wk) / len(wk)
+        rec = {
+            "kernel": kern, "kernel_names": names, "workload": workload,
+            "source_hash": kernel_source_hash(),
+            "dispatches": {"fetch_run": len(fk), "write_run": len(wk)},
+            "fetch_kib_per_dispatch": round(fetch, 1),
+            "write_kib_per_dispatch": round(write, 1),
+            "copy_calibration": {
+                "kernel": "torch.neg over a float32 buffer (reads and writes copy_bytes each)",
+                "copy_bytes": copy_bytes, "fetch_kib": round(f_kib, 1), "write_kib": round(w_kib, 1),
+                "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5)},
+            "hbm_fetch_bytes_per_launch": int(fetch * 1024 * f_scale),
+            "hbm_write_bytes_per_launch": int(write * 1024 * w_scale),
+            "hbm_bytes_per_launch": int(fetch * 1024 * f_scale + write * 1024 * w_scale),
+            "command": command,
+        }
+        path = os.path.join(ROOT, "profiles", f"{kern}_{workload}_counters.json")
+        with open(path, "w") as fh:
+            json.dump(rec, fh, indent=1)
+            fh.write("\n")
+        print(f"{path}: {rec['hbm_bytes_per_launch'] / 1e6:.2f} MB per launch "
+              f"(fetch {fetch:.0f} KiB x {f_scale:.3f}, write {write:.0f} KiB x {w_scale:.3f})")
+
+
+def summarize_stats(d: str, workload: str, command: str):
+    """Kernel-trace statistics (rocprofv3 --stats) of a bench run, as text:
+    writes profiles/<kernel>_<workload>_kernel_stats.txt for the path kernels."""
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no kernel_stats.csv under {d}")
+    lines = [f"# rocprofv3 kernel statistics, workload {workload}: {WORKLOADS[workload]}",
+             f"# command: {command}",
+             f"# source_hash: {kernel_source_hash()}",
+             f"{'kernel':<44} {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'pct':>6}"]
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    other = [0, 0.0, 0.0]
+    for r in rows:
+        name = _short_kernel(r["Name"])
+        if not name.startswith("ec_"):  # synthetic-input generation and the like
+            other[0] += int(r["Calls"])
+            other[1] += float(r["TotalDurationNs"])
+            other[2] += float(r["Percentage"])
+            continue
+        lines.append(f"{name[:44]:<44} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>9.2f} "
+                     f"{float(r['MinNs']) / 1e3:>9.2f} {float(r['MaxNs']) / 1e3:>9.2f} "
+                     f"{float(r['Percentage']):>6.2f}")
+    lines.append(f"{'(all other kernels: input generation, torch)':<44} {other[0]:>6} "
+                 f"{'':>9} {'':>9} {'':>9} {other[2]:>6.2f}")
+    text = "\n".join(lines) + "\n"
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    path = os.path.join(ROOT, "profiles", f"path_kernels_{workload}_kernel_stats.txt")
+    with open(path, "w") as fh:
+        fh.write(text)
+    print(text, end="")
+
+
+def copy_calibration(nbytes: int, reps: int):
+    """A plain elementwise copy of known size for counter calibration."""
+    import torch
+    n = nbytes // 4
+    src = torch.empty(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(f"[bench] copy calibration: {reps} x {nbytes} bytes", file=sys.stderr)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -92,7 +216,24 @@ def main():
     ap.add_argument("--batches", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain copy of BYTES (counter calibration)")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="write profiles/*_counters.json from rocprofv3 --pmc runs under DIR")
+    ap.add_argument("--summarize-stats", metavar="DIR",
+                    help="write profiles/*_kernel_stats.txt from a rocprofv3 --stats run under DIR")
+    ap.add_argument("--command", default="", help="command line recorded in a summary")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.workload,
+                           args.copy_calibration or (256 << 20), args.command)
+        return
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats, args.workload, args.command)
+        return
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, 8)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share; --gpus {args.gpus} is not supported "
               f"(the all-to-all across GPUs is out of scope of this build)", file=sys.stderr)
@@ -132,7 +273,7 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    plan.profile_enable(True, max_launches=3 * args.steps + 8)
+    plan.profile_enable(True, max_launches=4 * args.steps + 8)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -151,20 +292,26 @@ def main():
     t_prep, n_prep = plan.profile_read(ec.KERNEL_PREP)
     t_enc, n_enc = plan.profile_read(ec.KERNEL_ENCODE)
     t_dec, n_dec = plan.profile_read(ec.KERNEL_DECODE)
+    t_asm, n_asm = plan.profile_read(ec.KERNEL_ASSEMBLE)
     plan.profile_enable(False)
 
     rel = w0.eb_mode == ec.EB_REL_RANGE
     S = mean_bytes
-    tc = (t_prep + t_enc) / args.steps * 1e-3
+    tc = (t_prep + t_enc + t_asm) / args.steps * 1e-3
     td = t_dec / args.steps * 1e-3
     step_s = ms / args.steps * 1e-3
     bytes_c = 4 * N * (2 if rel else 1) + S
     bytes_d = S + 4 * N
+    # algorithmic bytes per launch: the input read by the range pass (REL) and
+    # by the quantize pass, the stream written by assembly (by the one encode
+    # kernel when there is no assembly pass), and both for decode
     kernels = {
         "prep": (t_prep / max(n_prep, 1), 4 * N if rel else 0),
-        "encode": (t_enc / max(n_enc, 1), 4 * N + S),
+        "encode": (t_enc / max(n_enc, 1), 4 * N + (0 if n_asm else S)),
         "decode": (t_dec / max(n_dec, 1), S + 4 * N),
     }
+    if n_asm:
+        kernels["assemble"] = (t_asm / n_asm, S)
     dom = max(kernels, key=lambda k: kernels[k][0])
     dom_ms, dom_bytes = kernels[dom]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9

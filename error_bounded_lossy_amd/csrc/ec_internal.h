@@ -57,6 +57,12 @@ struct Work {
   uint32_t* tile_U;              // [ntiles] first occurrences in the tile
   uint32_t* tile_nout;           // [ntiles] outliers stored by the tile
   uint64_t* hash;                // slots: (hash32 << 32) | (row + 1), 0 = empty
+  // staging between the quantize and assemble passes (D = 64, 128, 256 only;
+  // written by the quantize pass before it is read, never cleared)
+  uint64_t* stage_pl;            // [ntiles][64][D/64][12] bit-plane words
+  uint8_t* stage_w;              // [ntiles][64][D/64] width | 0x80 if outliers
+  uint64_t* stage_om;            // [ntiles][64][D/64] outlier masks (flagged only)
+  uint32_t* stage_slot;          // [ntiles][64] hash slot of each row
 };
 
 struct PrepArgs {
@@ -109,6 +115,9 @@ inline size_t decode_lds_bytes(uint32_t D) {
 
 hipError_t launch_prep(const PrepArgs& a, uint32_t grid, hipStream_t s);
 hipError_t launch_encode(const EncArgs& a, hipStream_t s);
+// true when D runs as quantize + assemble (launch_assemble after launch_encode)
+bool encode_has_assembly(uint32_t D);
+hipError_t launch_assemble(const EncArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecArgs& a, hipStream_t s);
 hipError_t set_encode_lds_limit(size_t bytes);
 

@@ -1,23 +1,29 @@
 // ec_kernels.hip -- gfx950 (CDNA4, wave64) kernels of the error-bounded lossy
 // compressor for DLRM embedding traffic (arXiv 2407.04272).
 //
-//  prep    clears the per-call workspace and, for range-relative error
-//          bounds, reduces every table's (min, max) over non-NaN values
-//          (one coalesced 128-bit-load pass over the input).
-//  encode  one workgroup per 64-row tile, in stream order taken from a ticket
-//          counter: quantize (section III-D), hash the quantized rows into a
-//          per-segment table to find each row's first occurrence (section
-//          III-B "Vector Homogenization", the vector-based LZ of III-D), pack
-//          the first-occurrence rows' codes as bit planes by wavefront ballot,
-//          and place the tile record with a decoupled look-back prefix scan so
-//          that every tile, table and chunk lands in ONE contiguous stream in a
-//          single pass (section III-E "Buffer Optimization", Fig. 7).
-//  decode  one workgroup per tile; each output row is written once.
+//  prep      clears the per-call workspace and, for range-relative error
+//            bounds, reduces every table's (min, max) over non-NaN values
+//            (one coalesced 128-bit-load pass over the input).
+//  quantize  (D = 64, 128, 256) one workgroup per 64-row tile: quantize
+//            (section III-D), pack the codes of every 64-element block as bit
+//            planes, stage planes and widths in the workspace, and insert the
+//            tile's quantized rows into the segment's hash table (section
+//            III-B "Vector Homogenization", the vector-based LZ of III-D).
+//  assemble  one workgroup per tile, after every row is in the table: first
+//            occurrences, record size, a decoupled look-back prefix scan that
+//            places every tile, table and chunk in ONE contiguous stream
+//            (section III-E "Buffer Optimization", Fig. 7), and the copy of the
+//            staged planes of first-occurrence rows.
+//  encode    (other D) both passes in one kernel, tiles waiting on earlier
+//            tiles' hash insertions.
+//  decode    one workgroup per tile; each output row is written once.
 //
 // Quantization uses IEEE fp32 division and round-to-nearest-even; the build
 // disables FP contraction so the reconstruction check is the exact fp32
 // sequence div, rint, mul, sub.
 #include "ec_internal.h"
+
+#include <type_traits>
 
 namespace ec {
 namespace {
@@ -866,11 +872,13 @@ __global__ void __launch_bounds__(kThreads) ec_encode_kernel(EncArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// encoder for D = 64*C: one wave per (row, 64-element chunk), lane = element,
-// so every wavefront ballot is directly one bit plane of one block.  Widths,
-// planes, outlier masks and row hashes come out of the quantization pass in
-// registers; LDS keeps only the planes (for repeated-row checks and the final
-// copy), never the codes.
+// encoder for D = 64*C.  A 64-element block is one row chunk with element i in
+// lane i.  The codes of two blocks are packed as the 16-bit halves of one
+// register, and a 32x32 bit-matrix transpose in each half-wave turns them into
+// bit planes: afterwards lane L holds the 32-bit half (L >> 5) of plane
+// (L & 15) of block ((L >> 4) & 1) of the pair.  A block's width follows from
+// which of its plane words are non-zero.  Plane words stay in registers until
+// the record is written; LDS keeps only widths, outlier masks and row data.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t fmix32(uint32_t h) {
   h ^= h >> 16;
@@ -879,51 +887,6 @@ __device__ __forceinline__ uint32_t fmix32(uint32_t h) {
   h *= 0xc2b2ae35u;
   h ^= h >> 16;
   return h;
-}
-
-// OR / sum of a 32-bit value over the wave with DPP butterflies (each step
-// combines disjoint lane sets); the result is returned to every lane.
-template <bool kSum>
-__device__ __forceinline__ uint32_t wave_reduce_dpp(uint32_t v) {
-  auto op = [](uint32_t a, uint32_t b) { return kSum ? a + b : (a | b); };
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast15
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast31
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-
-// One bit plane of a block: double the pre-shifted codes, take the carry-out
-// lane mask as plane B and park it in lane B of (lo, hi).  B is an immediate
-// (gfx9 reads at most one SGPR per vector instruction).
-template <int B>
-__device__ __forceinline__ void plane_step(uint32_t& zs, uint32_t& lo, uint32_t& hi) {
-  uint64_t pk;
-  asm volatile("v_add_co_u32_e64 %0, %1, %2, %2" : "=v"(zs), "=s"(pk) : "v"(zs));
-  asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(lo) : "s"((uint32_t)pk), "n"(B));
-  asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(hi) : "s"((uint32_t)(pk >> 32)), "n"(B));
-}
-
-// Bit planes w-1 .. 0 of the codes zz (w <= 12): plane b ends up in lane b.
-__device__ __forceinline__ void bit_planes(uint32_t zz, uint32_t w, uint32_t& lo, uint32_t& hi) {
-  uint32_t zs = w ? zz << (32u - w) : 0u;  // top plane at bit 31
-  switch (w) {
-    case 12: plane_step<11>(zs, lo, hi); [[fallthrough]];
-    case 11: plane_step<10>(zs, lo, hi); [[fallthrough]];
-    case 10: plane_step<9>(zs, lo, hi); [[fallthrough]];
-    case 9: plane_step<8>(zs, lo, hi); [[fallthrough]];
-    case 8: plane_step<7>(zs, lo, hi); [[fallthrough]];
-    case 7: plane_step<6>(zs, lo, hi); [[fallthrough]];
-    case 6: plane_step<5>(zs, lo, hi); [[fallthrough]];
-    case 5: plane_step<4>(zs, lo, hi); [[fallthrough]];
-    case 4: plane_step<3>(zs, lo, hi); [[fallthrough]];
-    case 3: plane_step<2>(zs, lo, hi); [[fallthrough]];
-    case 2: plane_step<1>(zs, lo, hi); [[fallthrough]];
-    case 1: plane_step<0>(zs, lo, hi); [[fallthrough]];
-    default: break;
-  }
 }
 
 // v + v + (bit `lane` of the wave-uniform mask m): appends one bit plane to
@@ -965,50 +928,195 @@ __device__ __forceinline__ bool quantize_fast(float x, float eb, float s, float 
   return false;
 }
 
-template <int C>
-struct FastLds {
-  uint64_t planes[kTileRows][C][12];
-  uint64_t omask[kTileRows][C];
-  uint8_t w[kTileRows][C];
+// Per-lane byte selectors, rotate amounts and masks of the transpose stages.
+struct XposeSel {
+  uint32_t p16, p8, r4, m4, r2, m2, r1, m1;
 };
+__device__ __forceinline__ XposeSel xpose_sel(uint32_t L) {
+  XposeSel s;
+  s.p16 = (L & 16) ? 0x03020706u : 0x05040100u;
+  s.p8 = (L & 8) ? 0x03070105u : 0x06020400u;
+  s.r4 = (L & 4) ? 4u : 28u;
+  s.m4 = (L & 4) ? 0xF0F0F0F0u : 0x0F0F0F0Fu;
+  s.r2 = (L & 2) ? 2u : 30u;
+  s.m2 = (L & 2) ? 0xCCCCCCCCu : 0x33333333u;
+  s.r1 = (L & 1) ? 1u : 31u;
+  s.m1 = (L & 1) ? 0xAAAAAAAAu : 0x55555555u;
+  return s;
+}
 
+// 32x32 bit transpose inside each half-wave: bit i of lane 32h + j of the
+// result is bit j of lane 32h + i of v.  Stage s exchanges, between lanes L and
+// L ^ s, the bits whose position differs from the lane in bit s: the lower lane
+// keeps the positions with bit s clear and takes the partner's ones moved up by
+// s, the upper lane the converse.  Stages 16 and 8 move whole half-words and
+// bytes (one byte permute); stages 4, 2, 1 rotate the partner word and merge.
+__device__ __forceinline__ uint32_t xpose32(uint32_t v, const XposeSel& s) {
+  uint32_t y = (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);  // lane ^ 16
+  v = __builtin_amdgcn_perm(y, v, s.p16);
+  y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false);  // row_ror:8
+  v = __builtin_amdgcn_perm(y, v, s.p8);
+  // lane ^ 4: banks 0 and 2 of each row read four lanes up, banks 1 and 3 down
+  y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x12C, 0xF, 0x5, false);
+  y = (uint32_t)__builtin_amdgcn_update_dpp((int)y, (int)v, 0x124, 0xF, 0xA, false);
+  v = (v & s.m4) | (__builtin_amdgcn_alignbit(y, y, s.r4) & ~s.m4);
+  y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);  // quad [2,3,0,1]
+  v = (v & s.m2) | (__builtin_amdgcn_alignbit(y, y, s.r2) & ~s.m2);
+  y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);  // quad [1,0,3,2]
+  v = (v & s.m1) | (__builtin_amdgcn_alignbit(y, y, s.r1) & ~s.m1);
+  return v;
+}
+
+// Zigzag codes of two blocks packed as 16-bit halves (|q| <= 2047).
+typedef short short2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t zigzag_pair(int qa, int qb) {
+  const uint32_t p = __builtin_amdgcn_perm((uint32_t)qb, (uint32_t)qa, 0x05040100u);
+  const short2v v = __builtin_bit_cast(short2v, p);
+  return __builtin_bit_cast(uint32_t, (short2v)((v << (short)1) ^ (v >> (short)15)));
+}
+
+// Sums over the wave of RB per-lane values at once (RB = 4, 8 or 16),
+// halving the number of registers at each step while the lanes of one
+// register come to hold partial sums of different rows.  Afterwards lane L
+// holds the sum of row L / (64 / RB).
+template <int RB>
+__device__ __forceinline__ uint32_t rows_reduce(const uint32_t (&h)[RB], uint32_t lane) {
+  uint32_t a[RB / 2], b[RB / 4];
+#pragma unroll
+  for (int r = 0; r < RB / 2; r++) {  // lanes 0-31: row r, 32-63: row r + RB/2
+    const auto p = __builtin_amdgcn_permlane32_swap(h[r], h[r + RB / 2], false, false);
+    a[r] = p[0] + p[1];
+  }
+#pragma unroll
+  for (int r = 0; r < RB / 4; r++) {  // 16-lane groups: rows r, r+RB/4, r+RB/2, r+3RB/4
+    const auto p = __builtin_amdgcn_permlane16_swap(a[r], a[r + RB / 4], false, false);
+    b[r] = p[0] + p[1];
+  }
+  const bool l8 = lane & 8, l4 = lane & 4;
+  auto ror8 = [](uint32_t u) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x128, 0xF, 0xF, false); };
+  auto hmirror = [](uint32_t u) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x141, 0xF, 0xF, false); };
+  uint32_t v;
+  if constexpr (RB == 4) {
+    v = b[0] + ror8(b[0]);
+    v += hmirror(v);
+  } else if constexpr (RB == 8) {  // 8-lane groups
+    v = (l8 ? b[1] : b[0]) + ror8(l8 ? b[0] : b[1]);
+    v += hmirror(v);
+  } else {  // 8-lane groups, then 4-lane groups (partner from the mirrored half-row)
+    const uint32_t c0 = (l8 ? b[2] : b[0]) + ror8(l8 ? b[0] : b[2]);
+    const uint32_t c1 = (l8 ? b[3] : b[1]) + ror8(l8 ? b[1] : b[3]);
+    v = (l4 ? c1 : c0) + hmirror(l4 ? c0 : c1);
+  }
+  v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+  return v;
+}
+
+// Do rows a and b (D = 64*C floats each) have equal codes and outlier bits?
+// Bitwise-equal rows always do; otherwise both are quantized and compared.
 template <int C>
-__global__ void __launch_bounds__(kThreads) ec_encode_fast(EncArgs a) {
+__device__ __forceinline__ bool rows_same(const float* ra, const float* rb, uint32_t lane,
+                                          float eb, float s2, float r2) {
+  float va[C], vb[C];
+  bool raw = true;
+#pragma unroll
+  for (int j = 0; j < C; j++) {
+    va[j] = ra[64 * j + lane];
+    vb[j] = rb[64 * j + lane];
+    raw = raw && f2u(va[j]) == f2u(vb[j]);
+  }
+  if (__all(raw)) return true;
+  bool eq = true;
+#pragma unroll
+  for (int j = 0; j < C; j++) {
+    int qa, qb;
+    const bool oa = quantize_fast(va[j], eb, s2, r2, qa);
+    const bool ob = quantize_fast(vb[j], eb, s2, r2, qb);
+    eq = eq && oa == ob && (oa ? f2u(va[j]) == f2u(vb[j]) : qa == qb);
+  }
+  return __all(eq);
+}
+
+// Tile row and block of the two blocks of plane register p of a wave whose
+// rows start at rbeg (RB rows per batch): block A for hi = 0, block B for 1.
+template <int C, int RB>
+__device__ __forceinline__ void pair_coords(uint32_t p, uint32_t hi, uint32_t rbeg,
+                                            uint32_t& row, uint32_t& blk) {
+  constexpr uint32_t kPB = RB * C / 2;  // plane registers per batch
+  const uint32_t ib = rbeg + (p / kPB) * RB, lp = p % kPB;
+  if constexpr (C == 1) {
+    row = ib + 2 * lp + hi;
+    blk = 0;
+  } else if constexpr (C == 2) {
+    row = ib + lp;
+    blk = hi;
+  } else {
+    row = ib + lp / 2;
+    blk = 2 * (lp & 1u) + hi;
+  }
+}
+
+// v with lane P (an immediate) replaced by the wave-uniform s
+template <int P>
+__device__ __forceinline__ void put_lane(uint32_t& v, uint32_t s) {
+  asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(s), "n"(P));
+}
+
+// f(integral_constant<I>) for I = B .. E-1, unrolled at compile time
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Stage layout (per tile): plane words [64 rows][C blocks][12 planes] u64
+// (only planes below the block width are written), widths [64][C] u8 with
+// bit 7 set on blocks holding outliers, outlier masks [64][C] u64 (flagged
+// blocks only), hash slot of every row [64] u32.
+constexpr uint32_t kStagePlanes = 12;
+constexpr uint8_t kOutlierFlag = 0x80;
+
+// ---------------------------------------------------------------------------
+// quantize pass for D = 64*C: codes, row hashes, bit planes and widths of one
+// tile, staged in the workspace; the tile's rows go into the segment's hash
+// table.  Nothing here waits on another workgroup.
+// ---------------------------------------------------------------------------
+template <int C>
+__global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
   constexpr uint32_t D = 64u * C;
-  constexpr uint32_t kRowsPerWave = kTileRows / (kThreads / 64);      // 16
-  // all of a wave's rows are loaded up front when they fit in 32 registers
-  constexpr bool kPreload = kRowsPerWave * C <= 32;
-  constexpr uint32_t kBatch = kPreload ? kRowsPerWave : (32 / C);  // rows per batch
-  extern __shared__ __align__(16) uint8_t smem[];
-  FastLds<C>& L = *reinterpret_cast<FastLds<C>*>(smem);
+  constexpr uint32_t kRowsPerWave = kTileRows / (kThreads / 64);  // 16
+  constexpr uint32_t kRB = 16 / C;                                 // rows per batch (16 blocks)
+  constexpr uint32_t kNB = kRowsPerWave / kRB;                     // batches per wave
+  constexpr uint32_t kPB = kRB * C / 2;                            // plane registers per batch
   __shared__ EncShared sh;
-  __shared__ uint64_t s_hash[kTileRows];
-  __shared__ uint32_t s_slot[kTileRows], s_first[kTileRows], s_rowbase[kTileRows];
-  __shared__ uint32_t s_obase[kTileRows];
-  __shared__ uint8_t s_urow[kTileRows];
+  __shared__ uint32_t s_hash[kTileRows];
+  __shared__ uint8_t s_oflag[kTileRows][C];
   const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const uint32_t T = a.sh.T;
 
   if (tid == 0) take_tile(a, sh);
+  for (uint32_t e = tid; e < kTileRows * C; e += kThreads) (&s_oflag[0][0])[e] = 0;
   __syncthreads();
   const uint32_t ticket = sh.ticket, s = sh.seg, k = sh.tile, n = sh.n, rows = sh.rows;
   const uint32_t pch = s / T, t = s % T;
   const uint32_t row0 = chunk_row0(a.sh, pch);
   const float* xs = a.x + ((uint64_t)t * a.sh.B + row0) * D;
   const float* xt = xs + (uint64_t)k * kTileRows * D;
-  // the wave's rows: the loads are issued before the error bound is known, so
-  // they and the range-partial reduction share one memory latency
   const uint32_t rbeg = wv * kRowsPerWave;
-  float xv[kBatch][C];  // kBatch == kRowsPerWave when the whole share is preloaded
-  if (kPreload) {
+  float xv[2][kRB][C];  // double buffer: the next batch loads while one is coded
+  auto load_batch = [&](uint32_t nb, float (&buf)[kRB][C]) {
 #pragma unroll
-    for (uint32_t rr = 0; rr < kBatch; rr++)
+    for (uint32_t rr = 0; rr < kRB; rr++)
 #pragma unroll
       for (uint32_t j = 0; j < C; j++) {
-        const uint32_t i = rbeg + rr;
-        xv[rr][j] = i < n ? xt[(uint64_t)i * D + 64 * j + lane] : 0.0f;
+        const uint32_t i = rbeg + nb * kRB + rr;
+        buf[rr][j] = i < n ? xt[(uint64_t)i * D + 64 * j + lane] : 0.0f;
       }
-  }
+  };
+  // the first batch is in flight while wave 0 reduces the range partials
+  load_batch(0, xv[0]);
   if (wv == 0) {
     bool v;
     float e = table_eb(a, t, v);
@@ -1023,205 +1131,256 @@ __global__ void __launch_bounds__(kThreads) ec_encode_fast(EncArgs a) {
   const float s2 = eb + eb;
   const float r2 = 1.0f / s2;
   const bool valid = sh.valid != 0;
-  uint32_t hk1[C], hk2[C];  // odd 24-bit multipliers per element position
-#pragma unroll
-  for (uint32_t j = 0; j < C; j++) {
-    hk1[j] = (fmix32(64 * j + lane + 0x9e3779b9u) & 0xffffffu) | 1u;
-    hk2[j] = (fmix32(64 * j + lane + 0x7f4a7c15u) & 0xffffffu) | 1u;
-  }
   const uint64_t g0 = ((uint64_t)t * a.sh.B + row0 + (uint64_t)k * kTileRows) * D;
-
-  // ---- quantize, planes, widths, outlier masks, row hashes ----
-  if (valid) {
-#pragma unroll 1
-    for (uint32_t rb = 0; rb < kRowsPerWave; rb += kBatch) {
-      if (!kPreload) {
-#pragma unroll
-        for (uint32_t rr = 0; rr < kBatch; rr++)
-#pragma unroll
-          for (uint32_t j = 0; j < C; j++) {
-            const uint32_t i = rbeg + rb + rr;
-            xv[rr][j] = i < n ? xt[(uint64_t)i * D + 64 * j + lane] : 0.0f;
-          }
+  const bool dbg = a.dbg_codes || a.dbg_outlier;
+  if (!valid || n == 0) {
+    if (dbg)
+      for (uint32_t e = tid; e < n * D; e += kThreads) {
+        if (a.dbg_codes) a.dbg_codes[g0 + e] = 0;
+        if (a.dbg_outlier) a.dbg_outlier[g0 + e] = 0;
       }
+    return;
+  }
+
+  const XposeSel xsel = xpose_sel(lane);
+  uint32_t hk[C];  // odd 24-bit multipliers per element position
 #pragma unroll
-      for (uint32_t rr = 0; rr < kBatch; rr++) {
-        const uint32_t i = rbeg + rb + rr;
-        if (i >= n) continue;
-        uint32_t hlo = 0, hhi = 0;
+  for (uint32_t j = 0; j < C; j++) hk[j] = (fmix32(64 * j + lane + 0x9e3779b9u) & 0xffffffu) | 1u;
+  // staging: lane's 32-bit half of plane (lane & 15) of block A or B of a pair
+  uint32_t* stage32 = reinterpret_cast<uint32_t*>(a.w.stage_pl + (uint64_t)ticket * kTileRows * C * kStagePlanes);
+  const uint32_t lane_word = (lane & 15u) * 2u + (lane >> 5) + ((lane >> 4) & 1u) * 2u * kStagePlanes;
+  const uint32_t lane_keep = 0xFFFFu >> (lane & 15u);  // planes of the lane's block from its own up
+  uint32_t nz_lo = 0;  // lane p: non-zero plane-word mask of plane register p
+
+  static_for<0, (int)kNB>([&](auto nbc) {
+    constexpr uint32_t nb = decltype(nbc)::value;
+    float (&xb)[kRB][C] = xv[nb & 1];
+    if (nb + 1 < kNB) load_batch(nb + 1, xv[(nb + 1) & 1]);
+    const uint32_t ib = rbeg + nb * kRB;
+    int q[kRB][C];
+    uint64_t um = 0;
+    // q = rint(x / 2eb) via the correctly rounded reciprocal.  When the product
+    // is at least 2^-10 from every rounding boundary and inside the code range,
+    // rint agrees with rint(fl(x/s)) and |x - fl(q s)| is strictly below eb, so
+    // the value is not an outlier.  One compare: |f| < 2046.5/4104 (= 0.49866)
+    // and |tp| < 2046.5; NaN or infinite products are unsure.
+#pragma unroll
+    for (uint32_t rr = 0; rr < kRB; rr++)
+#pragma unroll
+      for (uint32_t j = 0; j < C; j++) {
+        const float tp = xb[rr][j] * r2;
+        const float qf = rintf(tp);
+        const float f = tp - qf;
+        um |= __ballot(!(fmaxf(fabsf(f) * 4104.0f, fabsf(tp)) < 2046.5f));
+        q[rr][j] = (int)qf;
+      }
+    uint32_t hs[kRB];
+#pragma unroll
+    for (uint32_t rr = 0; rr < kRB; rr++) hs[rr] = 0;
+    if (um) {  // rare: the IEEE division and the reconstruction check decide
+#pragma unroll
+      for (uint32_t rr = 0; rr < kRB; rr++) {
+        const uint32_t i = ib + rr;
 #pragma unroll
         for (uint32_t j = 0; j < C; j++) {
-          const float x = xv[rr][j];
-          // q = rint(x / 2eb) via the correctly rounded reciprocal.  When the
-          // product is at least 2^-10 from every rounding boundary and inside
-          // the code range, rint agrees with rint(fl(x/s)) and |x - fl(q s)| is
-          // strictly below eb, so the value is not an outlier; otherwise the
-          // IEEE division and the reconstruction check decide (rare).
+          const float x = xb[rr][j];
           const float tp = x * r2;
-          float qf = rintf(tp);
-          const float f = tp - qf;
-          // one compare: |f| < 2046.5/4104 (= 0.49866, at least 2^-10 from 1/2)
-          // and |tp| < 2046.5; NaN or infinite products are unsure
-          const bool unsure = !(fmaxf(fabsf(f) * 4104.0f, fabsf(tp)) < 2046.5f);
-          uint64_t om = 0;
-          if (__any(unsure)) {
-            bool out = false;
-            if (unsure) {
-              const float tq = x / s2;
-              const bool oor = !(fabsf(tq) <= 2047.0f);
-              qf = rintf(tq);
-              const float xh = qf * s2;
-              const float err = x - xh;
-              out = oor || !(fabsf(err) <= eb);
-              if (out) {  // outlier: code 0, raw bits enter the row hash
-                qf = 0.0f;
-                const uint32_t bits = f2u(x);
-                hlo += (bits ^ 0x7f4a7c15u) * 0x85ebca6bu + hk1[j];
-                hhi += (bits ^ 0x3c6ef372u) * 0xc2b2ae35u + hk2[j];
-              }
-            }
-            om = __ballot(out);
+          const float f = tp - rintf(tp);
+          bool out = false;
+          if (i < n && !(fmaxf(fabsf(f) * 4104.0f, fabsf(tp)) < 2046.5f)) {
+            const float tq = x / s2;
+            const bool oor = !(fabsf(tq) <= 2047.0f);
+            const float qf = rintf(tq);
+            const float err = x - qf * s2;
+            out = oor || !(fabsf(err) <= eb);
+            q[rr][j] = out ? 0 : (int)qf;
+            if (out) hs[rr] += (f2u(x) ^ 0x7f4a7c15u) * 0x85ebca6bu + hk[j];  // raw bits
           }
-          const int q = (int)qf;
-          const uint32_t zz = ((uint32_t)q << 1) ^ (uint32_t)(q >> 31);
-          // row hash: position-weighted sums of the codes (two 32-bit halves)
-          hlo += __umul24(zz, hk1[j]);
-          hhi += __umul24(zz, hk2[j]);
-          // width = bit length of the largest code of the block; plane b is
-          // the ballot of bit b and ends up in lane b
-          const uint32_t mx = wave_reduce_dpp<false>(zz);
-          const uint32_t w = mx ? 32u - __clz(mx) : 0u;
-          uint32_t plo = 0, phi = 0;
-          bit_planes(zz, w, plo, phi);
-          if (lane < w) L.planes[i][j][lane] = ((uint64_t)phi << 32) | plo;
-          if (lane == 0) {
-            L.omask[i][j] = om;
-            L.w[i][j] = (uint8_t)w;
+          const uint64_t om = __ballot(out);
+          if (om) {
+            if (lane == 0) {
+              a.w.stage_om[((uint64_t)ticket * kTileRows + i) * C + j] = om;
+              s_oflag[i][j] = kOutlierFlag;
+            }
+            if (a.dbg_outlier && i < n) a.dbg_outlier[g0 + (uint64_t)i * D + 64 * j + lane] = (om >> lane) & 1ull;
           }
         }
-        const uint64_t H = ((uint64_t)wave_reduce_dpp<true>(hhi) << 32) | wave_reduce_dpp<true>(hlo);
-        if (lane == 0) s_hash[i] = H;
       }
     }
-    if (a.dbg_codes || a.dbg_outlier) {  // tests only: codes rebuilt from the planes
-      __syncthreads();
-      for (uint32_t e = tid; e < n * D; e += kThreads) {
-        const uint32_t i = e / D, d = e % D, j = d / 64, l = d % 64;
-        const uint32_t w = L.w[i][j];
-        uint32_t zz = 0;
-        for (uint32_t b = 0; b < w; b++) zz |= (uint32_t)((L.planes[i][j][b] >> l) & 1ull) << b;
-        const bool out = (L.omask[i][j] >> l) & 1ull;
-        if (a.dbg_codes) a.dbg_codes[g0 + e] = out ? 0 : unzigzag(zz);
-        if (a.dbg_outlier) a.dbg_outlier[g0 + e] = out ? 1 : 0;
+    // row hashes: position-weighted sums of the codes
+#pragma unroll
+    for (uint32_t rr = 0; rr < kRB; rr++)
+#pragma unroll
+      for (uint32_t j = 0; j < C; j++) hs[rr] += __umul24((uint32_t)q[rr][j], hk[j]);
+    if (dbg) {  // tests only
+#pragma unroll
+      for (uint32_t rr = 0; rr < kRB; rr++) {
+        const uint32_t i = ib + rr;
+        if (i >= n) continue;
+#pragma unroll
+        for (uint32_t j = 0; j < C; j++) {
+          const uint64_t e = g0 + (uint64_t)i * D + 64 * j + lane;
+          if (a.dbg_codes) a.dbg_codes[e] = q[rr][j];
+          if (a.dbg_outlier && !s_oflag[i][j]) a.dbg_outlier[e] = 0;
+        }
       }
     }
-  } else if (a.dbg_codes || a.dbg_outlier) {
-    for (uint32_t e = tid; e < n * D; e += kThreads) {
-      if (a.dbg_codes) a.dbg_codes[g0 + e] = 0;
-      if (a.dbg_outlier) a.dbg_outlier[g0 + e] = 0;
-    }
+    // bit planes of block pairs, staged up to each block's width
+    static_for<0, (int)kPB>([&](auto lpc) {
+      constexpr uint32_t lp = decltype(lpc)::value;
+      int qa, qb;
+      if constexpr (C == 1) {
+        qa = q[2 * lp][0];
+        qb = q[2 * lp + 1][0];
+      } else if constexpr (C == 2) {
+        qa = q[lp][0];
+        qb = q[lp][1];
+      } else {
+        qa = q[lp / 2][2 * (lp & 1)];
+        qb = q[lp / 2][2 * (lp & 1) + 1];
+      }
+      const uint32_t y = xpose32(zigzag_pair(qa, qb), xsel);
+      const uint64_t nz = __ballot(y != 0);
+      const uint32_t m32 = (uint32_t)nz | (uint32_t)(nz >> 32);  // block A planes 0-15, B 16-31
+      constexpr uint32_t p = nb * kPB + lp;
+      put_lane<p>(nz_lo, m32);
+      uint32_t row, blk;
+      pair_coords<C, kRB>(p, 0, rbeg, row, blk);
+      if ((m32 >> (lane & 31u)) & lane_keep)  // plane below the block's width
+        stage32[(row * C + blk) * 2u * kStagePlanes + lane_word] = y;
+    });
+    const uint32_t hv = rows_reduce<kRB>(hs, lane);
+    const uint32_t h = __shfl(hv, (int)((lane % kRB) * (64 / kRB)));
+    if (lane < kRB) s_hash[ib + lane] = fmix32(h);
+  });
+  // widths of the wave's blocks, lane-parallel: lane p < kNB*kPB holds pair p
+  if (lane < kNB * kPB) {
+    const uint32_t ma = nz_lo & 0xFFFFu, mb = nz_lo >> 16;
+    uint32_t ra, ba, rb2, bb;
+    pair_coords<C, kRB>(lane, 0, rbeg, ra, ba);
+    pair_coords<C, kRB>(lane, 1, rbeg, rb2, bb);
+    uint8_t* sw = a.w.stage_w + (uint64_t)ticket * kTileRows * C;
+    sw[ra * C + ba] = (uint8_t)((ma ? 32 - __clz(ma) : 0) | s_oflag[ra][ba]);
+    sw[rb2 * C + bb] = (uint8_t)((mb ? 32 - __clz(mb) : 0) | s_oflag[rb2][bb]);
   }
-  __syncthreads();
 
-  uint64_t* htab = a.w.hash + (valid ? a.w.hash_off[s] : 0);
+  // ---- insert: each wave owns 16 rows (lanes 0..15); compares use the wave ----
+  uint64_t* htab = a.w.hash + a.w.hash_off[s];
   const uint32_t cap_mask = (1u << a.w.hash_log2[s]) - 1u;
-  if (valid && n > 0) {
-    // ---- insert: each wave owns 16 rows (lanes 0..15); compares use the wave ----
-    const uint32_t i = wv * 16 + lane;
-    bool active = lane < 16 && i < n;
-    uint64_t H = active ? (s_hash[i] & a.hash_keep) : 0;
-    uint32_t h32 = (uint32_t)(H >> 32);
-    uint32_t slot = (uint32_t)H & cap_mask;
-    uint64_t mine = ((uint64_t)h32 << 32) | (uint64_t)(k * kTileRows + i + 1);
-    uint32_t guard = 0;
-    while (__ballot(active) != 0) {
-      bool need = false;
-      uint32_t cand = 0;
-      if (active) {
-        uint64_t old = atomicCAS((unsigned long long*)&htab[slot], 0ull, (unsigned long long)mine);
-        if (old == 0) {
-          s_slot[i] = slot;
+  const uint32_t i = rbeg + lane;
+  bool active = lane < kRowsPerWave && i < n;
+  const uint32_t H = active ? (s_hash[i] & (uint32_t)a.hash_keep) : 0u;
+  uint32_t slot = H & cap_mask;
+  const uint64_t mine = ((uint64_t)H << 32) | (uint64_t)(k * kTileRows + i + 1);
+  uint32_t guard = 0;
+  while (__ballot(active) != 0) {
+    bool need = false;
+    uint32_t cand = 0;
+    if (active) {
+      const uint64_t old = atomicCAS((unsigned long long*)&htab[slot], 0ull, (unsigned long long)mine);
+      if (old == 0) {
+        active = false;
+      } else if ((uint32_t)(old >> 32) == H && (uint32_t)old - 1u < rows) {
+        need = true;
+        cand = (uint32_t)old - 1u;
+      } else {
+        slot = (slot + 1) & cap_mask;
+      }
+    }
+    uint64_t m = __ballot(need);
+    while (m) {
+      const int Ln = __ffsll((long long)m) - 1;
+      m &= m - 1;
+      const uint32_t iL = __shfl(i, Ln), cL = __shfl(cand, Ln);
+      const bool eq = rows_same<C>(xs + (uint64_t)cL * D, xt + (uint64_t)iL * D, lane, eb, s2, r2);
+      if ((int)lane == Ln) {
+        if (eq) {
+          atomic_min_performed(&htab[slot], mine);
           active = false;
-        } else if ((uint32_t)(old >> 32) == h32 && (uint32_t)old - 1u < rows) {
-          need = true;
-          cand = (uint32_t)old - 1u;
         } else {
           slot = (slot + 1) & cap_mask;
         }
       }
-      uint64_t m = __ballot(need);
-      while (m) {
-        const int Ln = __ffsll((long long)m) - 1;
-        m &= m - 1;
-        const uint32_t iL = __shfl(i, Ln), cL = __shfl(cand, Ln);
-        // row iL (planes in LDS) against candidate row cL re-quantized
-        bool eq = true;
-#pragma unroll
-        for (uint32_t j = 0; j < C; j++) {
-          const uint32_t d = 64 * j + lane;
-          const float xo = xs[(uint64_t)cL * D + d];
-          int qo;
-          const bool oo = quantize_fast(xo, eb, s2, r2, qo);
-          const uint32_t zo = zigzag(qo);
-          const uint32_t w = L.w[iL][j];
-          uint32_t zm = 0;
-          for (uint32_t b = 0; b < w; b++) zm |= (uint32_t)((L.planes[iL][j][b] >> lane) & 1ull) << b;
-          const bool om = (L.omask[iL][j] >> lane) & 1ull;
-          bool e = (oo == om) && (zo == zm);
-          if (e && om) e = f2u(xo) == f2u(xt[(uint64_t)iL * D + d]);
-          eq = eq && e;
-        }
-        eq = __all(eq);
-        if ((int)lane == Ln) {
-          if (eq) {
-            atomic_min_performed(&htab[slot], mine);
-            s_slot[i] = slot;
-            active = false;
-          } else {
-            slot = (slot + 1) & cap_mask;
-          }
-        }
-      }
-      if (++guard > cap_mask + 2) {  // cannot happen: the table is at most half full
-        if (active) {
-          report_error(a.report, kDevErrTimeout);
-          s_slot[i] = slot;
-          active = false;
-        }
+    }
+    if (++guard > cap_mask + 2) {  // cannot happen: the table is at most half full
+      if (active) {
+        report_error(a.report, kDevErrTimeout);
+        active = false;
       }
     }
-    wait_vm();  // this wave's slot writes are performed before the flag
-    __syncthreads();
-    if (tid == 0) st32(&a.w.tile_inserted[ticket], 1u);
-    wait_inserted(a, s, k);
-    fence_wg();
-    __syncthreads();
   }
+  if (lane < kRowsPerWave && i < n) a.w.stage_slot[(uint64_t)ticket * kTileRows + i] = slot;
+}
 
-  // ---- first occurrences, per-row plane and outlier bases (wave 0) ----
+// ---------------------------------------------------------------------------
+// assembly pass for D = 64*C: every row of the segment is in the hash table,
+// so a tile reads its first occurrences, sizes its record, takes its place in
+// the stream (look-back) and copies its staged planes there.
+// ---------------------------------------------------------------------------
+template <int C>
+__global__ void __launch_bounds__(kThreads) ec_assemble_fast(EncArgs a) {
+  constexpr uint32_t D = 64u * C;
+  __shared__ EncShared sh;
+  __shared__ uint64_t s_omask[kTileRows][C];
+  __shared__ uint32_t s_cbase[kTileRows][C];  // plane-word offset of each block in the record
+  __shared__ uint32_t s_first[kTileRows], s_obase[kTileRows];
+  __shared__ uint8_t s_w[kTileRows][C];
+  __shared__ uint8_t s_urow[kTileRows];
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const uint32_t T = a.sh.T;
+
+  if (tid == 0) take_tile(a, sh);
+  __syncthreads();
+  const uint32_t ticket = sh.ticket, s = sh.seg, k = sh.tile, n = sh.n, rows = sh.rows;
+  const uint32_t pch = s / T, t = s % T;
+  const uint32_t row0 = chunk_row0(a.sh, pch);
+  const float* xt = a.x + ((uint64_t)t * a.sh.B + row0 + (uint64_t)k * kTileRows) * D;
+
+  // ---- first occurrences, widths, per-block plane and outlier bases (wave 0) ----
   if (wv == 0) {
+    bool valid;
+    const float eb = table_eb(a, t, valid);
     const bool inrow = lane < n;
     uint32_t first = k * kTileRows + lane;
-    if (valid && inrow) first = (uint32_t)rmw_read64(&htab[s_slot[lane]]) - 1u;
+    uint8_t wb[C];
+#pragma unroll
+    for (uint32_t j = 0; j < C; j++) wb[j] = 0;
+    if (valid && inrow) {
+      const uint32_t slot = a.w.stage_slot[(uint64_t)ticket * kTileRows + lane];
+      const uint8_t* sw = a.w.stage_w + ((uint64_t)ticket * kTileRows + lane) * C;
+#pragma unroll
+      for (uint32_t j = 0; j < C; j++) wb[j] = sw[j];
+      first = (uint32_t)ld64(&a.w.hash[a.w.hash_off[s] + slot]) - 1u;
+    }
     const bool uniq = valid && inrow && first == k * kTileRows + lane;
     const uint64_t bm = __ballot(uniq);
     uint32_t rw = 0, ro = 0;
-    if (uniq) {
 #pragma unroll
-      for (uint32_t j = 0; j < C; j++) {
-        rw += L.w[lane][j];
-        ro += (uint32_t)__popcll(L.omask[lane][j]);
+    for (uint32_t j = 0; j < C; j++) {
+      uint64_t om = 0;
+      if (wb[j] & kOutlierFlag) om = a.w.stage_om[((uint64_t)ticket * kTileRows + lane) * C + j];
+      const uint32_t w = wb[j] & 0x7Fu;
+      s_omask[lane][j] = om;
+      s_w[lane][j] = (uint8_t)w;
+      if (uniq) {
+        rw += w;
+        ro += (uint32_t)__popcll(om);
       }
     }
     uint32_t iw = rw, io = ro;  // inclusive scans over lanes
     for (int o = 1; o < 64; o <<= 1) {
-      uint32_t a1 = __shfl_up(iw, o), a2 = __shfl_up(io, o);
+      const uint32_t a1 = __shfl_up(iw, o), a2 = __shfl_up(io, o);
       if (lane >= (uint32_t)o) {
         iw += a1;
         io += a2;
       }
     }
-    s_rowbase[lane] = iw - rw;
+    uint32_t cb = iw - rw;
+#pragma unroll
+    for (uint32_t j = 0; j < C; j++) {
+      s_cbase[lane][j] = cb;
+      cb += s_w[lane][j];
+    }
     s_obase[lane] = io - ro;
     if (inrow) s_first[lane] = first;
     if (uniq) s_urow[__popcll(bm & __lanemask_lt())] = (uint8_t)lane;
@@ -1229,22 +1388,23 @@ __global__ void __launch_bounds__(kThreads) ec_encode_fast(EncArgs a) {
       a.dbg_first[(uint64_t)t * a.sh.B + row0 + k * kTileRows + lane] = first;
     const uint32_t sumw = __shfl(iw, 63), nout = __shfl(io, 63);
     if (lane == 0) {
+      sh.eb = eb;
+      sh.valid = valid;
       sh.bitmap = bm;
       const uint32_t U = (uint32_t)__popcll(bm);
       size_record(a, sh, valid, n, U, U * C, sumw, nout);
     }
+    place_record(a, sh);
   }
-  __syncthreads();
-  if (wv == 0) place_record(a, sh);
   __syncthreads();
 
   // ---- write the tile record ----
   if (n > 0 && sh.fits) {
     uint8_t* rec = a.out + sh.rec_abs;
-    const uint32_t mode = sh.mode, U = sh.U, nout = sh.nout, nblk = sh.nblk;
+    const uint32_t mode = sh.mode, U = sh.U, nblk = sh.nblk;
     const uint64_t bitmap = sh.bitmap;
     if (tid == 0) {
-      uint64_t w1 = (uint64_t)(mode ? nout : 0u) | ((uint64_t)U << 32) | ((uint64_t)mode << 48);
+      const uint64_t w1 = (uint64_t)(mode ? sh.nout : 0u) | ((uint64_t)U << 32) | ((uint64_t)mode << 48);
       reinterpret_cast<uint64_t*>(rec)[0] = bitmap;
       reinterpret_cast<uint64_t*>(rec)[1] = w1;
     }
@@ -1252,38 +1412,45 @@ __global__ void __launch_bounds__(kThreads) ec_encode_fast(EncArgs a) {
       write_raw_rows(rec, xt, n * D, D);
     } else {
       const uint32_t rb = rows <= 65536 ? 2 : 4;
-      for (uint32_t b = tid; b < nblk; b += kThreads) rec[16 + b] = L.w[s_urow[b / C]][b % C];
+      for (uint32_t b = tid; b < nblk; b += kThreads) rec[16 + b] = s_w[s_urow[b / C]][b % C];
       if (tid < n && !((bitmap >> tid) & 1ull)) {
-        uint32_t j = tid - (uint32_t)__popcll(bitmap & ((1ull << tid) - 1ull));
+        const uint32_t j = tid - (uint32_t)__popcll(bitmap & ((1ull << tid) - 1ull));
         if (rb == 2) reinterpret_cast<uint16_t*>(rec + sh.off_refs)[j] = (uint16_t)s_first[tid];
         else reinterpret_cast<uint32_t*>(rec + sh.off_refs)[j] = s_first[tid];
       }
       write_record_pads(rec, sh, n, rows);
+      // staged plane words: 16 lanes per block, lane = plane
       uint64_t* planes = reinterpret_cast<uint64_t*>(rec + sh.off_pl);
-      uint32_t* opos = reinterpret_cast<uint32_t*>(rec + sh.off_opos);
-      uint32_t* oval = reinterpret_cast<uint32_t*>(rec + sh.off_oval);
-      for (uint32_t u = wv; u < U; u += kThreads / 64) {
-        const uint32_t i = s_urow[u];
-        uint32_t pb = s_rowbase[i], ob = s_obase[i];
+      const uint64_t* stage = a.w.stage_pl + (uint64_t)ticket * kTileRows * C * kStagePlanes;
+      const uint32_t b = tid & 15u;
+      for (uint32_t blk = tid >> 4; blk < n * C; blk += kThreads / 16) {
+        const uint32_t row = blk / C, j = blk % C;
+        if (((bitmap >> row) & 1ull) && b < s_w[row][j])
+          planes[s_cbase[row][j] + b] = stage[(uint64_t)blk * kStagePlanes + b];
+      }
+      if (sh.nout) {
+        uint32_t* opos = reinterpret_cast<uint32_t*>(rec + sh.off_opos);
+        uint32_t* oval = reinterpret_cast<uint32_t*>(rec + sh.off_oval);
+        for (uint32_t u = wv; u < U; u += kThreads / 64) {
+          const uint32_t i = s_urow[u];
+          uint32_t ob = s_obase[i];
 #pragma unroll
-        for (uint32_t j = 0; j < C; j++) {
-          const uint32_t w = L.w[i][j];
-          if (lane < w) planes[pb + lane] = L.planes[i][j][lane];
-          pb += w;
-          const uint64_t om = L.omask[i][j];
-          if (om) {
-            if ((om >> lane) & 1ull) {
-              const uint32_t o = ob + (uint32_t)__popcll(om & __lanemask_lt());
-              opos[o] = u * D + 64 * j + lane;
-              oval[o] = f2u(xt[(uint64_t)i * D + 64 * j + lane]);
+          for (uint32_t j = 0; j < C; j++) {
+            const uint64_t om = s_omask[i][j];
+            if (om) {
+              if ((om >> lane) & 1ull) {
+                const uint32_t o = ob + (uint32_t)__popcll(om & __lanemask_lt());
+                opos[o] = u * D + 64 * j + lane;
+                oval[o] = f2u(xt[(uint64_t)i * D + 64 * j + lane]);
+              }
+              ob += (uint32_t)__popcll(om);
             }
-            ob += (uint32_t)__popcll(om);
           }
         }
       }
     }
   }
-  complete_tile(a, sh, valid, eb);
+  complete_tile(a, sh, sh.valid != 0, sh.eb);
 }
 
 // ---------------------------------------------------------------------------
@@ -1974,16 +2141,36 @@ hipError_t launch_encode(const EncArgs& a, hipStream_t s) {
   const dim3 grid(a.sh.ntiles), block(kThreads);
   switch (a.sh.D) {
     case 64:
-      hipLaunchKernelGGL(ec_encode_fast<1>, grid, block, sizeof(FastLds<1>), s, a);
+      hipLaunchKernelGGL(ec_quantize_fast<1>, grid, block, 0, s, a);
       break;
     case 128:
-      hipLaunchKernelGGL(ec_encode_fast<2>, grid, block, sizeof(FastLds<2>), s, a);
+      hipLaunchKernelGGL(ec_quantize_fast<2>, grid, block, 0, s, a);
       break;
     case 256:
-      hipLaunchKernelGGL(ec_encode_fast<4>, grid, block, sizeof(FastLds<4>), s, a);
+      hipLaunchKernelGGL(ec_quantize_fast<4>, grid, block, 0, s, a);
       break;
     default:
       hipLaunchKernelGGL(ec_encode_kernel, grid, block, encode_lds_bytes(a.sh.D), s, a);
+  }
+  return hipGetLastError();
+}
+
+bool encode_has_assembly(uint32_t D) { return D == 64 || D == 128 || D == 256; }
+
+hipError_t launch_assemble(const EncArgs& a, hipStream_t s) {
+  const dim3 grid(a.sh.ntiles), block(kThreads);
+  switch (a.sh.D) {
+    case 64:
+      hipLaunchKernelGGL(ec_assemble_fast<1>, grid, block, 0, s, a);
+      break;
+    case 128:
+      hipLaunchKernelGGL(ec_assemble_fast<2>, grid, block, 0, s, a);
+      break;
+    case 256:
+      hipLaunchKernelGGL(ec_assemble_fast<4>, grid, block, 0, s, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

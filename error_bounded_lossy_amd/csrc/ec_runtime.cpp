@@ -21,6 +21,7 @@ struct Layout {
   uint64_t eb_base, mult, seg_tile_base, hash_off, hash_log2, range_part;
   uint64_t dyn, seg_start, seg_end, chunk_start, seg_fin;
   uint64_t tile_status, tile_inserted, tile_rec, tile_U, tile_nout, hash;
+  uint64_t stage_pl = 0, stage_w = 0, stage_om = 0, stage_slot = 0;
   uint64_t dyn_bytes, total;
   uint32_t nbr;
   std::vector<uint32_t> seg_tile_base_v;
@@ -156,6 +157,14 @@ ec_status make_layout(const ec_plan_desc* d, Layout* L) {
   L->hash = take(8ull * slots);
   o = aup(o, 256);
   L->dyn_bytes = o - L->dyn;
+  if (ec::encode_has_assembly(D)) {
+    const uint64_t blocks = tiles * 64ull * (D / 64);
+    L->stage_pl = take(8ull * 12 * blocks);
+    L->stage_w = take(blocks);
+    L->stage_om = take(8ull * blocks);
+    L->stage_slot = take(4ull * 64 * tiles);
+    o = aup(o, 256);
+  }
   L->total = o;
   return EC_OK;
 }
@@ -327,6 +336,12 @@ ec_status ec_plan(const ec_plan_desc* desc, ec_plan_t* out) {
   w.tile_U = reinterpret_cast<uint32_t*>(ws + L.tile_U);
   w.tile_nout = reinterpret_cast<uint32_t*>(ws + L.tile_nout);
   w.hash = reinterpret_cast<uint64_t*>(ws + L.hash);
+  if (ec::encode_has_assembly(L.sh.D)) {
+    w.stage_pl = reinterpret_cast<uint64_t*>(ws + L.stage_pl);
+    w.stage_w = ws + L.stage_w;
+    w.stage_om = reinterpret_cast<uint64_t*>(ws + L.stage_om);
+    w.stage_slot = reinterpret_cast<uint32_t*>(ws + L.stage_slot);
+  }
   *out = pl;
   return EC_OK;
 }
@@ -382,6 +397,10 @@ ec_status ec_compress(ec_plan_t pl, int64_t iter, const float* d_in, void* d_out
   ea.dbg_eb = pl->dbg_eb;
   st = profiled(pl, EC_KERNEL_ENCODE, s, [&] { return ec::launch_encode(ea, s); });
   if (st != EC_OK) return st;
+  if (ec::encode_has_assembly(sh.D)) {
+    st = profiled(pl, EC_KERNEL_ASSEMBLE, s, [&] { return ec::launch_assemble(ea, s); });
+    if (st != EC_OK) return st;
+  }
   record_done(pl, s);
   return EC_OK;
 }

@@ -78,8 +78,16 @@ typedef enum {
 
 typedef enum { EC_CODER_BITPACK = 1 } ec_coder;
 
-/* Kernel ids for the profiling counters. */
-typedef enum { EC_KERNEL_PREP = 0, EC_KERNEL_ENCODE = 1, EC_KERNEL_DECODE = 2 } ec_kernel;
+/* Kernel ids for the profiling counters.  For D = 64, 128 and 256 compression
+ * runs as two kernels, ENCODE (quantize, bit planes, hash insertion) then
+ * ASSEMBLE (first occurrences, placement, record writing); for other D the
+ * ENCODE kernel does both and ASSEMBLE is never launched. */
+typedef enum {
+  EC_KERNEL_PREP = 0,
+  EC_KERNEL_ENCODE = 1,
+  EC_KERNEL_DECODE = 2,
+  EC_KERNEL_ASSEMBLE = 3
+} ec_kernel;
 
 typedef struct {
   int32_t kind;   /* ec_sched_kind                  */
