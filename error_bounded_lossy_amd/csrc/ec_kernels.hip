@@ -1947,16 +1947,58 @@ __device__ __forceinline__ void patch_outliers(float (&v)[C], uint32_t e0, OP op
   }
 }
 
+// Un-zigzag two codes packed as 16-bit halves; returns them sign-extended.
+typedef unsigned short ushort2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void unzigzag_pair(uint32_t zz2, int& qa, int& qb) {
+  const ushort2v z = __builtin_bit_cast(ushort2v, zz2);
+  const short2v q = (short2v)(z >> (unsigned short)1) ^ -(short2v)(z & (unsigned short)1);
+  qa = q.x;
+  qb = q.y;
+}
+
+// Sum of the n bytes at p (n < 2^16), 16 bytes per load.
+__device__ __forceinline__ uint32_t sum_bytes(const uint8_t* p, uint32_t n) {
+  uint32_t s = 0, q = 0;
+  if (((uintptr_t)p & 15u) == 0) {
+    for (; q + 16 <= n; q += 16) {
+      const uint4 v = *reinterpret_cast<const uint4*>(p + q);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        const uint32_t t = (w[c] & 0x00ff00ffu) + ((w[c] >> 8) & 0x00ff00ffu);
+        s += (t & 0xffffu) + (t >> 16);
+      }
+    }
+  }
+  for (; q < n; q++) s += p[q];
+  return s;
+}
+
+// Decoder for D = 64*C.  Every row first gets, per 64-element block, the width
+// and the segment-relative word offset of its bit planes (in this tile's
+// record, or in the earlier tile its reference points into).  A wave then
+// decodes two blocks at once: lane L loads the 32-bit half (L >> 5) of plane
+// (L & 15) of block ((L >> 4) & 1), and the same 32x32 transpose as in the
+// encoder (its own inverse) leaves both blocks' zigzag codes of element L as
+// the halves of lane L.
 template <int C>
 __global__ void __launch_bounds__(kThreads) ec_decode_fast(const uint8_t* __restrict__ in,
                                                           float* __restrict__ yout, DecArgs a) {
   constexpr uint32_t D = 64u * C;
-  constexpr uint32_t kExt = 0x80000000u, kBad = 0x40000000u;
+  constexpr uint32_t kRowsPerWave = kTileRows / (kThreads / 64);  // 16
+  // row kinds
+  constexpr uint32_t kPlanes = 0, kRawRef = 1, kBadRow = 2;
   __shared__ DecShared sh;
   __shared__ uint64_t s_rec;
-  __shared__ uint32_t s_src[kTileRows], s_xoff[kTileRows], s_xu[kTileRows], s_xbase[kTileRows];
   __shared__ uint8_t s_width[kTileRows * C];
   __shared__ uint32_t s_boff[kTileRows * C];
+  __shared__ uint32_t s_bo[kTileRows][C];  // plane word offset from the segment start
+  __shared__ uint8_t s_bw[kTileRows][C];
+  __shared__ uint32_t s_kind[kTileRows];
+  __shared__ uint32_t s_orec[kTileRows];   // segment offset of the record holding the row
+  __shared__ uint32_t s_ou[kTileRows];     // the row's first-occurrence index in that record
+  __shared__ uint32_t s_onum[kTileRows];   // outliers of that record
+  __shared__ uint32_t s_oofs[kTileRows];   // segment offset of its outlier positions
   __shared__ uint32_t s_opos[kOutCap], s_oval[kOutCap];
   const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const uint32_t T = a.sh.T, B = a.sh.B;
@@ -1978,11 +2020,11 @@ __global__ void __launch_bounds__(kThreads) ec_decode_fast(const uint8_t* __rest
     if (tid == 0) report_error(a.report, kDevErrCorrupt);
     return;
   }
-  // offsets read from LDS are wave-uniform: say so, so that loads through
-  // them are scalar
-  const uint8_t* sg = in + uniform64(sh.seg_off);
-  const uint8_t* rec = in + uniform64(s_rec);
-  const uint32_t mode = uniform32(sh.tl.mode), U = uniform32(sh.tl.U), nout = uniform32(sh.tl.nout);
+  const uint8_t* sg = in + sh.seg_off;
+  const uint64_t rec_off = s_rec;
+  const uint8_t* rec = in + rec_off;
+  const uint32_t rec_in_seg = (uint32_t)(rec_off - sh.seg_off);
+  const uint32_t mode = sh.tl.mode, U = sh.tl.U, nout = sh.tl.nout;
   if (mode == 0) {  // RAW: rows verbatim
     const float4* s4 = reinterpret_cast<const float4*>(rec + 16);
     float4* y4 = reinterpret_cast<float4*>(yt);
@@ -1990,14 +2032,12 @@ __global__ void __launch_bounds__(kThreads) ec_decode_fast(const uint8_t* __rest
     return;
   }
   const float eb = sh.eb, s2 = eb + eb;
-  const uint64_t sbytes = uniform64(sh.seg_bytes);
+  const uint64_t sbytes = sh.seg_bytes;
   const uint32_t rb = rows <= 65536 ? 2 : 4;
-  const uint64_t bitmap = uniform64(sh.tl.bitmap);
+  const uint64_t bitmap = sh.tl.bitmap;
   const uint32_t nblk = U * C;
-  const uint32_t off_refs = uniform32(sh.tl.off_refs), off_opos = uniform32(sh.tl.off_opos);
-  const uint32_t off_oval = uniform32(sh.tl.off_oval), off_pl = uniform32(sh.tl.off_pl);
-  const uint64_t plane_words = (uniform64(sh.tl.avail) - off_pl) / 8;
-  const_u64* planes = as_const_u64(rec + off_pl);
+  const uint32_t off_refs = sh.tl.off_refs, off_opos = sh.tl.off_opos;
+  const uint32_t off_oval = sh.tl.off_oval, off_pl = sh.tl.off_pl;
   const uint32_t* g_opos = reinterpret_cast<const uint32_t*>(rec + off_opos);
   const uint32_t* g_oval = reinterpret_cast<const uint32_t*>(rec + off_oval);
   uint32_t badw = 0;
@@ -2008,120 +2048,195 @@ __global__ void __launch_bounds__(kThreads) ec_decode_fast(const uint8_t* __rest
     s_boff[b] = w;
   }
   if (badw) sh.bad = 1;
-  const uint32_t sumw = nblk ? block_exclusive_scan(s_boff, nblk, sh.part) : 0;
-  if (sumw > plane_words && tid == 0) sh.bad = 1;
   const bool stage_out = nout <= kOutCap;
   if (stage_out)
     for (uint32_t i = tid; i < nout; i += kThreads) {
       s_opos[i] = g_opos[i];
       s_oval[i] = g_oval[i];
     }
-  if (tid < n) {  // source of every row (lane-parallel, so metadata loads overlap)
+  const uint32_t sumw = nblk ? block_exclusive_scan(s_boff, nblk, sh.part) : 0;
+  const uint64_t seg_words = sbytes / 8;
+  const uint32_t pl_word0 = (rec_in_seg + off_pl) / 8;  // off_pl and records are 8-aligned
+  if (tid == 0 && (uint64_t)pl_word0 + sumw > seg_words) sh.bad = 1;
+
+  // ---- where every row's planes are (lane-parallel: metadata loads overlap) ----
+  if (tid < n) {
     const uint32_t i = tid, r = k * kTileRows + i;
     const uint64_t below = bitmap & ((1ull << i) - 1ull);
-    uint32_t src;
+    uint32_t kind = kPlanes, u = 0, orec = rec_in_seg, onum = nout, oofs = rec_in_seg + off_opos;
+    uint32_t bo[C];
+    uint8_t bw[C];
+#pragma unroll
+    for (uint32_t j = 0; j < C; j++) {
+      bo[j] = 0;
+      bw[j] = 0;
+    }
+    bool local = true;
     if ((bitmap >> i) & 1ull) {
-      src = (uint32_t)__popcll(below);
+      u = (uint32_t)__popcll(below);
     } else {
-      const uint32_t j = i - (uint32_t)__popcll(below);
-      const uint32_t ref = rb == 2 ? reinterpret_cast<const uint16_t*>(rec + off_refs)[j]
-                                   : reinterpret_cast<const uint32_t*>(rec + off_refs)[j];
+      const uint32_t jr = i - (uint32_t)__popcll(below);
+      const uint32_t ref = rb == 2 ? reinterpret_cast<const uint16_t*>(rec + off_refs)[jr]
+                                   : reinterpret_cast<const uint32_t*>(rec + off_refs)[jr];
       if (ref >= r) {
-        src = kBad;
+        kind = kBadRow;
       } else if (ref >= k * kTileRows) {
         const uint32_t i2 = ref - k * kTileRows;
-        src = ((bitmap >> i2) & 1ull) ? (uint32_t)__popcll(bitmap & ((1ull << i2) - 1ull)) : kBad;
+        if ((bitmap >> i2) & 1ull) u = (uint32_t)__popcll(bitmap & ((1ull << i2) - 1ull));
+        else kind = kBadRow;
       } else {
+        local = false;
         const uint32_t k2 = ref / kTileRows, i2 = ref % kTileRows;
         DecTile t2 = locate_tile(sg, sbytes, sh.ntiles, rows, k2, D, true);
-        src = kExt | i;
         if (!t2.ok || !((t2.bitmap >> i2) & 1ull)) {
-          src = kBad;
-        } else if (t2.mode == 0) {
-          s_xoff[i] = (uint32_t)(t2.rec - sg);
-          s_xu[i] = i2;
+          kind = kBadRow;
         } else {
-          const uint32_t u2 = (uint32_t)__popcll(t2.bitmap & ((1ull << i2) - 1ull));
-          const uint32_t b0 = u2 * C;
-          const uint32_t* w4 = reinterpret_cast<const uint32_t*>(t2.rec + 16);
-          uint32_t base = 0;
-          for (uint32_t q = 0; q < b0 / 4; q++) {
-            uint32_t v = w4[q];
-            v = (v & 0x00ff00ffu) + ((v >> 8) & 0x00ff00ffu);
-            base += (v & 0xffffu) + (v >> 16);
+          orec = (uint32_t)(t2.rec - sg);
+          onum = t2.nout;
+          oofs = orec + t2.off_opos;
+          if (t2.mode == 0) {
+            kind = kRawRef;
+            u = i2;
+          } else {
+            u = (uint32_t)__popcll(t2.bitmap & ((1ull << i2) - 1ull));
+            uint32_t run = (orec + t2.off_pl) / 8 + sum_bytes(t2.rec + 16, u * C);
+#pragma unroll
+            for (uint32_t j = 0; j < C; j++) {
+              const uint32_t w = t2.rec[16 + u * C + j];
+              bw[j] = (uint8_t)w;
+              bo[j] = run;
+              run += w;
+              if (w > 12 || (uint64_t)run > seg_words) kind = kBadRow;
+            }
+            if (u >= t2.U) kind = kBadRow;
           }
-          for (uint32_t q = b0 & ~3u; q < b0; q++) base += t2.rec[16 + q];
-          s_xoff[i] = (uint32_t)(t2.rec - sg);
-          s_xu[i] = u2;
-          s_xbase[i] = base;
         }
       }
     }
-    s_src[i] = src;
+    s_kind[i] = kind;
+    s_orec[i] = orec;
+    s_ou[i] = u;
+    s_onum[i] = onum;
+    s_oofs[i] = oofs;
+    if (kind == kPlanes) {
+      if (local) {
+#pragma unroll
+        for (uint32_t j = 0; j < C; j++) {
+          s_bw[i][j] = s_width[u * C + j];
+          s_bo[i][j] = pl_word0 + s_boff[u * C + j];
+        }
+      } else {
+#pragma unroll
+        for (uint32_t j = 0; j < C; j++) {
+          s_bw[i][j] = bw[j];
+          s_bo[i][j] = bo[j];
+        }
+      }
+    }
   }
   __syncthreads();
 
   const bool tile_bad = sh.bad != 0;
-  for (uint32_t i = wv; i < n; i += kThreads / 64) {
-    const uint32_t src = __builtin_amdgcn_readfirstlane(s_src[i]);
-    float* y = yt + (uint64_t)i * D;
-    bool ok = !tile_bad && (src & kBad) == 0;
-    float v[C];
-    if (ok && !(src & kExt)) {
-      const uint32_t u = src;
+  const XposeSel xsel = xpose_sel(lane);
+  const uint32_t* sg32 = reinterpret_cast<const uint32_t*>(sg);
+  const uint32_t plane = lane & 15u, half = lane >> 5, hi = (lane >> 4) & 1u;
+  const uint32_t rbeg = wv * kRowsPerWave;
+  constexpr uint32_t kRowsPerStep = C == 1 ? 2 : 1;  // C = 1: blocks of two rows pair up
+  for (uint32_t i0 = rbeg; i0 < rbeg + kRowsPerWave && i0 < n; i0 += kRowsPerStep) {
+    // the lane's row (C = 1: row i0 + hi) and its kind
+    const uint32_t i = C == 1 ? i0 + hi : i0;
+    const bool live = i < n;
+    const uint32_t kind = live ? s_kind[i] : kPlanes;
+    const bool all_planes = __all(kind == kPlanes) && !tile_bad;
+    float v[2 * ((C + 1) / 2)];
+    bool ok = true;
+    if (all_planes) {
 #pragma unroll
-      for (uint32_t j = 0; j < C; j++) {
-        const uint32_t b = u * C + j;
-        const uint32_t w = __builtin_amdgcn_readfirstlane(s_width[b]);
-        const uint32_t off = __builtin_amdgcn_readfirstlane(s_boff[b]);
-        ok = ok && (uint64_t)off + w <= plane_words;
-        v[j] = ok ? decode_block(planes, off, w, plane_words, s2) : 0.0f;
-      }
-      if (nout) {
-        if (stage_out) patch_outliers<C>(v, u * D, (const uint32_t*)s_opos, (const uint32_t*)s_oval, nout);
-        else patch_outliers<C>(v, u * D, g_opos, g_oval, nout);
-      }
-    } else if (ok) {
-      const uint8_t* rec2 = sg + __builtin_amdgcn_readfirstlane(s_xoff[i]);
-      const uint32_t u2 = __builtin_amdgcn_readfirstlane(s_xu[i]);
-      const uint32_t w3 = rd32(rec2 + 12);
-      if (((w3 >> 16) & 0xffu) == 0) {  // referenced row stored RAW: re-quantize it
-        const float* src2 = reinterpret_cast<const float*>(rec2 + 16) + (uint64_t)u2 * D;
-#pragma unroll
-        for (uint32_t j = 0; j < C; j++) {
-          const float xv = src2[64 * j + lane];
-          int q;
-          v[j] = quantize(xv, eb, s2, q) ? xv : (float)q * s2;
+      for (uint32_t m = 0; m < (C + 1) / 2; m++) {
+        const uint32_t j = C == 1 ? 0 : 2 * m + hi;
+        uint32_t word = 0;
+        if (live) {
+          const uint32_t w = s_bw[i][j];
+          if (plane < w) word = sg32[2 * (s_bo[i][j] + plane) + half];
         }
-      } else {
-        // a referenced tile precedes this one, so it holds a full 64 rows
-        const uint32_t U2 = w3 & 0xffffu, nout2 = rd32(rec2 + 8);
-        const uint32_t nb2 = U2 * C;
-        const uint32_t o_refs = (uint32_t)align_up(16 + nb2, 4);
-        const uint32_t o_opos = (uint32_t)align_up(o_refs + rb * (kTileRows - U2), 4);
-        const uint32_t o_oval = o_opos + 4 * nout2;
-        const uint32_t o_pl = (uint32_t)align_up(o_oval + 4 * nout2, 8);
-        const uint64_t avail2 = sbytes - (uint64_t)(rec2 - sg);
-        ok = o_pl <= avail2 && u2 < U2;
-        const uint64_t pw2 = ok ? (avail2 - o_pl) / 8 : 0;
-        const_u64* planes2 = as_const_u64(rec2 + o_pl);
-        uint32_t run = __builtin_amdgcn_readfirstlane(s_xbase[i]);
+        const uint32_t zz2 = xpose32(word, xsel);
+        int qa, qb;
+        unzigzag_pair(zz2, qa, qb);
+        v[2 * m] = (float)qa * s2;
+        v[2 * m + 1] = (float)qb * s2;
+      }
+      // outliers of the first occurrence each output row copies
 #pragma unroll
-        for (uint32_t j = 0; j < C; j++) {
-          const uint32_t w = ok ? rec2[16 + u2 * C + j] : 0u;
-          ok = ok && w <= 12 && (uint64_t)run + w <= pw2;
-          v[j] = ok ? decode_block(planes2, run, w, pw2, s2) : 0.0f;
-          run += w;
+      for (uint32_t rr = 0; rr < kRowsPerStep; rr++) {
+        const uint32_t ir = i0 + rr;
+        if (ir >= n) continue;
+        const uint32_t on = s_onum[ir];
+        if (on == 0) continue;
+        float vr[C];
+#pragma unroll
+        for (uint32_t j = 0; j < C; j++) vr[j] = v[C == 1 ? rr : j];
+        const uint32_t u = s_ou[ir];
+        if (s_orec[ir] == rec_in_seg && stage_out) {
+          patch_outliers<C>(vr, u * D, (const uint32_t*)s_opos, (const uint32_t*)s_oval, on);
+        } else {
+          const uint32_t* op = reinterpret_cast<const uint32_t*>(sg + s_oofs[ir]);
+          patch_outliers<C>(vr, u * D, op, op + on, on);
         }
-        if (ok && nout2)
-          patch_outliers<C>(v, u2 * D, reinterpret_cast<const uint32_t*>(rec2 + o_opos),
-                            reinterpret_cast<const uint32_t*>(rec2 + o_oval), nout2);
+#pragma unroll
+        for (uint32_t j = 0; j < C; j++) v[C == 1 ? rr : j] = vr[j];
+      }
+    } else {
+      // rows that copy a RAW-stored first occurrence, or a corrupt tile
+#pragma unroll
+      for (uint32_t rr = 0; rr < kRowsPerStep; rr++) {
+        const uint32_t ir = i0 + rr;
+        const uint32_t kr = ir < n ? s_kind[ir] : kPlanes;
+        bool okr = !tile_bad && kr != kBadRow;
+        float vr[C];
+        if (okr && kr == kRawRef) {
+          const float* src2 = reinterpret_cast<const float*>(sg + s_orec[ir] + 16) + (uint64_t)s_ou[ir] * D;
+#pragma unroll
+          for (uint32_t j = 0; j < C; j++) {
+            const float xv = src2[64 * j + lane];
+            int q;
+            vr[j] = quantize(xv, eb, s2, q) ? xv : (float)q * s2;
+          }
+        } else if (okr && ir < n) {
+          // a plane row next to a RAW-copy row (C = 1 pairs): decode it alone
+#pragma unroll
+          for (uint32_t j = 0; j < C; j++) {
+            const uint32_t w = s_bw[ir][j], o = s_bo[ir][j];
+            uint32_t zz = 0;
+            for (uint32_t b = 0; b < w; b++) {
+              const uint64_t word = reinterpret_cast<const uint64_t*>(sg)[o + b];
+              zz |= (uint32_t)((word >> lane) & 1ull) << b;
+            }
+            vr[j] = (float)unzigzag(zz) * s2;
+          }
+          const uint32_t on = s_onum[ir];
+          if (on) {
+            const uint32_t* op = reinterpret_cast<const uint32_t*>(sg + s_oofs[ir]);
+            patch_outliers<C>(vr, s_ou[ir] * D, op, op + on, on);
+          }
+        } else {
+#pragma unroll
+          for (uint32_t j = 0; j < C; j++) vr[j] = 0.0f;
+        }
+        okr = __all(okr || ir >= n);
+#pragma unroll
+        for (uint32_t j = 0; j < C; j++) v[C == 1 ? rr : j] = okr ? vr[j] : 0.0f;
+        if (!okr) ok = false;
       }
     }
-    ok = __all(ok);
-#pragma unroll
-    for (uint32_t j = 0; j < C; j++) y[64 * j + lane] = ok ? v[j] : 0.0f;
     if (!ok && lane == 0) report_error(a.report, kDevErrCorrupt);
+    // stores: C = 1 -> rows i0, i0 + 1; else the C blocks of row i0
+#pragma unroll
+    for (uint32_t rr = 0; rr < kRowsPerStep; rr++) {
+      if (i0 + rr >= n) continue;
+      float* y = yt + (uint64_t)(i0 + rr) * D;
+#pragma unroll
+      for (uint32_t j = 0; j < C; j++) y[64 * j + lane] = v[C == 1 ? rr : j];
+    }
   }
 }
 
