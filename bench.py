@@ -273,8 +273,7 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    plan.profile_enable(True, max_launches=4 * args.steps + 8)
-    torch.cuda.synchronize()
+    # timed region: K steps, no profiling events between the launches
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
@@ -284,20 +283,30 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    ms = e0.elapsed_time(e1)
     _, _, st = plan.ratio(raise_on_error=False)
     if st != 0:
         print(f"[bench] device status {st}", file=sys.stderr)
         sys.exit(1)
-    ms = e0.elapsed_time(e1)
+    # per-kernel durations: the same K steps again, each launch bracketed by
+    # HIP events on the stream it runs on
+    plan.profile_enable(True, max_launches=4 * args.steps + 8)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
     t_prep, n_prep = plan.profile_read(ec.KERNEL_PREP)
     t_enc, n_enc = plan.profile_read(ec.KERNEL_ENCODE)
     t_dec, n_dec = plan.profile_read(ec.KERNEL_DECODE)
     t_asm, n_asm = plan.profile_read(ec.KERNEL_ASSEMBLE)
     plan.profile_enable(False)
+    _, _, st = plan.ratio(raise_on_error=False)
+    if st != 0:
+        print(f"[bench] device status {st}", file=sys.stderr)
+        sys.exit(1)
 
     rel = w0.eb_mode == ec.EB_REL_RANGE
     S = mean_bytes
-    tc = (t_prep + t_enc + t_asm) / args.steps * 1e-3
+    tc = (t_prep + t_enc + t_asm) / args.steps * 1e-3  # kernel time only
     td = t_dec / args.steps * 1e-3
     step_s = ms / args.steps * 1e-3
     bytes_c = 4 * N * (2 if rel else 1) + S

@@ -954,17 +954,41 @@ __device__ __forceinline__ XposeSel xpose_sel(uint32_t L) {
 __device__ __forceinline__ uint32_t xpose32(uint32_t v, const XposeSel& s) {
   uint32_t y = (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);  // lane ^ 16
   v = __builtin_amdgcn_perm(y, v, s.p16);
-  y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false);  // row_ror:8
+  y = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);  // row_ror:8
   v = __builtin_amdgcn_perm(y, v, s.p8);
   // lane ^ 4: banks 0 and 2 of each row read four lanes up, banks 1 and 3 down
-  y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x12C, 0xF, 0x5, false);
+  y = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x12C, 0xF, 0x5, false);
   y = (uint32_t)__builtin_amdgcn_update_dpp((int)y, (int)v, 0x124, 0xF, 0xA, false);
   v = (v & s.m4) | (__builtin_amdgcn_alignbit(y, y, s.r4) & ~s.m4);
-  y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);  // quad [2,3,0,1]
+  y = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // quad [2,3,0,1]
   v = (v & s.m2) | (__builtin_amdgcn_alignbit(y, y, s.r2) & ~s.m2);
-  y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);  // quad [1,0,3,2]
+  y = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // quad [1,0,3,2]
   v = (v & s.m1) | (__builtin_amdgcn_alignbit(y, y, s.r1) & ~s.m1);
   return v;
+}
+
+// Buffer resources: loads past `bytes` return 0 and stores past it are
+// dropped, which predicates them without branches.
+constexpr uint32_t kOff = 0x80000000u;  // an offset past every range
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ float buf_ld_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));  // the bits, not a conversion
+}
+__device__ __forceinline__ uint32_t buf_ld_u32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint64_t buf_ld_u64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  return ((uint64_t)v.y << 32) | v.x;
+}
+__device__ __forceinline__ void buf_st_u64(__amdgpu_buffer_rsrc_t r, uint32_t off, uint64_t v) {
+  u32x2 w;
+  w.x = (uint32_t)v;
+  w.y = (uint32_t)(v >> 32);
+  __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, 0);
 }
 
 // Zigzag codes of two blocks packed as 16-bit halves (|q| <= 2047).
@@ -1106,14 +1130,13 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
   const float* xt = xs + (uint64_t)k * kTileRows * D;
   const uint32_t rbeg = wv * kRowsPerWave;
   float xv[2][kRB][C];  // double buffer: the next batch loads while one is coded
+  const __amdgpu_buffer_rsrc_t rx = buf_rsrc(xt, n * D * 4);  // rows past n read as 0
   auto load_batch = [&](uint32_t nb, float (&buf)[kRB][C]) {
 #pragma unroll
     for (uint32_t rr = 0; rr < kRB; rr++)
 #pragma unroll
-      for (uint32_t j = 0; j < C; j++) {
-        const uint32_t i = rbeg + nb * kRB + rr;
-        buf[rr][j] = i < n ? xt[(uint64_t)i * D + 64 * j + lane] : 0.0f;
-      }
+      for (uint32_t j = 0; j < C; j++)
+        buf[rr][j] = buf_ld_f32(rx, ((rbeg + nb * kRB + rr) * D + 64 * j + lane) * 4);
   };
   // the first batch is in flight while wave 0 reduces the range partials
   load_batch(0, xv[0]);
@@ -1146,10 +1169,12 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
   uint32_t hk[C];  // odd 24-bit multipliers per element position
 #pragma unroll
   for (uint32_t j = 0; j < C; j++) hk[j] = (fmix32(64 * j + lane + 0x9e3779b9u) & 0xffffffu) | 1u;
-  // staging: lane's 32-bit half of plane (lane & 15) of block A or B of a pair
-  uint32_t* stage32 = reinterpret_cast<uint32_t*>(a.w.stage_pl + (uint64_t)ticket * kTileRows * C * kStagePlanes);
-  const uint32_t lane_word = (lane & 15u) * 2u + (lane >> 5) + ((lane >> 4) & 1u) * 2u * kStagePlanes;
-  const uint32_t lane_keep = 0xFFFFu >> (lane & 15u);  // planes of the lane's block from its own up
+  // staging: after the half swap, lane L < 32 holds plane (L & 15) of block
+  // A (L < 16) or B as one 64-bit word
+  const __amdgpu_buffer_rsrc_t rst =
+      buf_rsrc(a.w.stage_pl + (uint64_t)ticket * kTileRows * C * kStagePlanes, kTileRows * C * kStagePlanes * 8);
+  const uint32_t lane_word = (lane & 15u) + ((lane >> 4) & 1u) * kStagePlanes;
+  const uint32_t lane_keep = lane < 32 ? 0xFFFFu >> (lane & 15u) : 0u;  // planes from the lane's own up
   uint32_t nz_lo = 0;  // lane p: non-zero plane-word mask of plane register p
 
   static_for<0, (int)kNB>([&](auto nbc) {
@@ -1246,8 +1271,10 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
       put_lane<p>(nz_lo, m32);
       uint32_t row, blk;
       pair_coords<C, kRB>(p, 0, rbeg, row, blk);
-      if ((m32 >> (lane & 31u)) & lane_keep)  // plane below the block's width
-        stage32[(row * C + blk) * 2u * kStagePlanes + lane_word] = y;
+      const auto hw = __builtin_amdgcn_permlane32_swap(y, y, false, false);  // (lo, hi) halves
+      const uint64_t word = ((uint64_t)hw[1] << 32) | hw[0];
+      const bool keep = (m32 >> (lane & 31u)) & lane_keep;  // plane below the block's width
+      buf_st_u64(rst, keep ? ((row * C + blk) * kStagePlanes + lane_word) * 8 : kOff, word);
     });
     const uint32_t hv = rows_reduce<kRB>(hs, lane);
     const uint32_t h = __shfl(hv, (int)((lane % kRB) * (64 / kRB)));
@@ -1419,15 +1446,24 @@ __global__ void __launch_bounds__(kThreads) ec_assemble_fast(EncArgs a) {
         else reinterpret_cast<uint32_t*>(rec + sh.off_refs)[j] = s_first[tid];
       }
       write_record_pads(rec, sh, n, rows);
-      // staged plane words: 16 lanes per block, lane = plane
-      uint64_t* planes = reinterpret_cast<uint64_t*>(rec + sh.off_pl);
-      const uint64_t* stage = a.w.stage_pl + (uint64_t)ticket * kTileRows * C * kStagePlanes;
+      // staged plane words: 16 lanes per block, lane = plane; every load is
+      // issued before the first store
+      const __amdgpu_buffer_rsrc_t rsrc =
+          buf_rsrc(a.w.stage_pl + (uint64_t)ticket * kTileRows * C * kStagePlanes, kTileRows * C * kStagePlanes * 8);
+      const __amdgpu_buffer_rsrc_t rdst = buf_rsrc(rec + sh.off_pl, sh.sumw * 8);
+      constexpr uint32_t kPass = kTileRows * C / (kThreads / 16);
       const uint32_t b = tid & 15u;
-      for (uint32_t blk = tid >> 4; blk < n * C; blk += kThreads / 16) {
-        const uint32_t row = blk / C, j = blk % C;
-        if (((bitmap >> row) & 1ull) && b < s_w[row][j])
-          planes[s_cbase[row][j] + b] = stage[(uint64_t)blk * kStagePlanes + b];
+      uint64_t wv_[kPass];
+      uint32_t dst[kPass];
+#pragma unroll
+      for (uint32_t ps = 0; ps < kPass; ps++) {
+        const uint32_t blk = ps * (kThreads / 16) + (tid >> 4), row = blk / C, j = blk % C;
+        const bool use = blk < n * C && ((bitmap >> row) & 1ull) && b < s_w[row][j];
+        wv_[ps] = buf_ld_u64(rsrc, use ? (blk * kStagePlanes + b) * 8 : kOff);
+        dst[ps] = use ? (s_cbase[row][j] + b) * 8 : kOff;
       }
+#pragma unroll
+      for (uint32_t ps = 0; ps < kPass; ps++) buf_st_u64(rdst, dst[ps], wv_[ps]);
       if (sh.nout) {
         uint32_t* opos = reinterpret_cast<uint32_t*>(rec + sh.off_opos);
         uint32_t* oval = reinterpret_cast<uint32_t*>(rec + sh.off_oval);
@@ -2136,30 +2172,44 @@ __global__ void __launch_bounds__(kThreads) ec_decode_fast(const uint8_t* __rest
   }
   __syncthreads();
 
-  const bool tile_bad = sh.bad != 0;
+  // segments the encoder writes are below 2^31 bytes, so byte offsets into
+  // one fit the 32-bit buffer range
+  const bool tile_bad = sh.bad != 0 || sbytes >= (1ull << 31);
   const XposeSel xsel = xpose_sel(lane);
-  const uint32_t* sg32 = reinterpret_cast<const uint32_t*>(sg);
+  const __amdgpu_buffer_rsrc_t rseg = buf_rsrc(sg, tile_bad ? 0u : (uint32_t)sbytes);
   const uint32_t plane = lane & 15u, half = lane >> 5, hi = (lane >> 4) & 1u;
   const uint32_t rbeg = wv * kRowsPerWave;
   constexpr uint32_t kRowsPerStep = C == 1 ? 2 : 1;  // C = 1: blocks of two rows pair up
-  for (uint32_t i0 = rbeg; i0 < rbeg + kRowsPerWave && i0 < n; i0 += kRowsPerStep) {
+  constexpr uint32_t kSteps = kRowsPerWave / kRowsPerStep;
+  constexpr uint32_t kM = (C + 1) / 2;  // plane registers per step
+  // all plane words of the wave's rows are requested before any is used
+  uint32_t word[kSteps][kM];
+#pragma unroll
+  for (uint32_t st = 0; st < kSteps; st++) {
+    const uint32_t i = rbeg + st * kRowsPerStep + (C == 1 ? hi : 0u);
+    const bool use = i < n && s_kind[i] == kPlanes;
+#pragma unroll
+    for (uint32_t m = 0; m < kM; m++) {
+      const uint32_t j = C == 1 ? 0u : 2 * m + hi;
+      const bool on = use && plane < s_bw[i][j];
+      word[st][m] = buf_ld_u32(rseg, on ? (2 * (s_bo[i][j] + plane) + half) * 4 : kOff);
+    }
+  }
+#pragma unroll
+  for (uint32_t st = 0; st < kSteps; st++) {
+    const uint32_t i0 = rbeg + st * kRowsPerStep;
+    if (i0 >= n) break;
     // the lane's row (C = 1: row i0 + hi) and its kind
-    const uint32_t i = C == 1 ? i0 + hi : i0;
+    const uint32_t i = i0 + (C == 1 ? hi : 0u);
     const bool live = i < n;
     const uint32_t kind = live ? s_kind[i] : kPlanes;
     const bool all_planes = __all(kind == kPlanes) && !tile_bad;
-    float v[2 * ((C + 1) / 2)];
+    float v[2 * kM];
     bool ok = true;
     if (all_planes) {
 #pragma unroll
-      for (uint32_t m = 0; m < (C + 1) / 2; m++) {
-        const uint32_t j = C == 1 ? 0 : 2 * m + hi;
-        uint32_t word = 0;
-        if (live) {
-          const uint32_t w = s_bw[i][j];
-          if (plane < w) word = sg32[2 * (s_bo[i][j] + plane) + half];
-        }
-        const uint32_t zz2 = xpose32(word, xsel);
+      for (uint32_t m = 0; m < kM; m++) {
+        const uint32_t zz2 = xpose32(word[st][m], xsel);
         int qa, qb;
         unzigzag_pair(zz2, qa, qb);
         v[2 * m] = (float)qa * s2;
@@ -2208,8 +2258,8 @@ __global__ void __launch_bounds__(kThreads) ec_decode_fast(const uint8_t* __rest
             const uint32_t w = s_bw[ir][j], o = s_bo[ir][j];
             uint32_t zz = 0;
             for (uint32_t b = 0; b < w; b++) {
-              const uint64_t word = reinterpret_cast<const uint64_t*>(sg)[o + b];
-              zz |= (uint32_t)((word >> lane) & 1ull) << b;
+              const uint64_t wd = reinterpret_cast<const uint64_t*>(sg)[o + b];
+              zz |= (uint32_t)((wd >> lane) & 1ull) << b;
             }
             vr[j] = (float)unzigzag(zz) * s2;
           }
