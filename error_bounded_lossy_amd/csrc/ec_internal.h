@@ -51,7 +51,9 @@ struct Work {
   uint64_t* seg_end;             // [nseg] absolute end offset + 1
   uint64_t* chunk_start;         // [P] absolute offset + 1
   uint32_t* seg_fin;             // [nseg] segment header written
-  uint64_t* tile_status;         // [ntiles] look-back words
+  uint64_t* tile_status;         // [ntiles] the tile's stream item (+ 1 once known, one-pass encoder)
+  uint64_t* block_status;        // [ceil(ntiles/64)] one-pass encoder: (flag << 62) | sum or
+                                 // inclusive prefix; size pass: the block's item sum
   uint32_t* tile_inserted;       // [ntiles] rows inserted into the hash table
   uint64_t* tile_rec;            // [ntiles] absolute record offset + 1 (record written)
   uint32_t* tile_U;              // [ntiles] first occurrences in the tile
@@ -63,6 +65,12 @@ struct Work {
   uint8_t* stage_w;              // [ntiles][64][D/64] width | 0x80 if outliers
   uint64_t* stage_om;            // [ntiles][64][D/64] outlier masks (flagged only)
   uint32_t* stage_slot;          // [ntiles][64] hash slot of each row
+  // per-tile results of the size pass (D = 64, 128, 256 only; written before
+  // they are read)
+  uint32_t* tile_info;           // [ntiles][4] U, n_out, plane words, mode | valid << 8
+  uint64_t* tile_bitmap;         // [ntiles] first-occurrence rows
+  uint32_t* tile_first;          // [ntiles][64] first occurrence of each row
+  uint32_t* seg_eb;              // [nseg] stored error bound bits (0: raw segment)
 };
 
 struct PrepArgs {
@@ -115,7 +123,8 @@ inline size_t decode_lds_bytes(uint32_t D) {
 
 hipError_t launch_prep(const PrepArgs& a, uint32_t grid, hipStream_t s);
 hipError_t launch_encode(const EncArgs& a, hipStream_t s);
-// true when D runs as quantize + assemble (launch_assemble after launch_encode)
+// true when D runs as quantize + assembly (launch_assemble after launch_encode:
+// size, place and write kernels)
 bool encode_has_assembly(uint32_t D);
 hipError_t launch_assemble(const EncArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecArgs& a, hipStream_t s);

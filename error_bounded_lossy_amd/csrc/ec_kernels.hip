@@ -352,46 +352,58 @@ __device__ __forceinline__ void size_record(const EncArgs& a, EncShared& sh, boo
   sh.U = U;
 }
 
-// Wave 0: decoupled look-back over tiles in ticket (= stream) order; publishes
-// the segment / chunk starts and the record offset.  Sets sh.rec_abs, sh.fits.
+// Bounded spin of one lane until a relaxed 64-bit word becomes non-zero.
+__device__ __forceinline__ uint64_t spin_word(const EncArgs& a, const uint64_t* p) {
+  uint64_t v = ld64(p);
+  uint32_t spins = 0;
+  while (v == 0) {
+    __builtin_amdgcn_s_sleep(1);
+    v = ld64(p);
+    if (++spins > kSpinLimit) {
+      report_error(a.report, kDevErrTimeout);
+      return 0;
+    }
+  }
+  return v;
+}
+
+// Wave 0: the tile's place in the stream, a two-level prefix sum over tiles in
+// ticket (= stream) order.  Each tile publishes its item; the tiles of a block
+// of 64 consecutive tickets sum the items before them in their block (one
+// lane each); the block's last tile publishes the block sum and then the
+// block's inclusive prefix, found by a decoupled look-back over the block
+// words of earlier blocks, which every tile also runs.  Every wait is on a
+// smaller ticket.  Publishes the segment / chunk starts and the record
+// offset; sets sh.rec_abs, sh.fits.
 __device__ __forceinline__ void place_record(const EncArgs& a, EncShared& sh) {
   const uint32_t lane = threadIdx.x & 63;
   const uint64_t kAgg = 1ull << 62, kIncl = 2ull << 62, kVal = (1ull << 62) - 1;
   const uint32_t ticket = sh.ticket, s = sh.seg, k = sh.tile, ntiles = sh.ntiles;
   const uint32_t T = a.sh.T, pch = s / T, t = s % T;
   const uint64_t item = sh.item;
-  uint64_t excl = 0;
-  if (ticket == 0) {
-    if (lane == 0) st64(&a.w.tile_status[0], kIncl | item);
-  } else {
-    if (lane == 0) st64(&a.w.tile_status[ticket], kAgg | item);
-    int64_t top = (int64_t)ticket - 1;
-    while (true) {
-      int64_t idx = top - (int64_t)lane;
-      uint64_t v = kIncl;  // before tile 0: inclusive prefix 0
-      if (idx >= 0) {
-        uint32_t spins = 0;
-        while (((v = ld64(&a.w.tile_status[idx])) >> 62) == 0) {
-          __builtin_amdgcn_s_sleep(1);
-          if (++spins > kSpinLimit) {
-            report_error(a.report, kDevErrTimeout);
-            v = kIncl;
-            break;
-          }
-        }
-      }
-      uint64_t incl_mask = __ballot((v >> 62) == 2);
-      if (incl_mask) {
-        int L = __ffsll((long long)incl_mask) - 1;
-        uint64_t mine = (int)lane <= L ? (v & kVal) : 0;
-        excl += wave_sum_u64(mine);
-        break;
-      }
-      excl += wave_sum_u64(v & kVal);
-      top -= 64;
+  const uint32_t blk = ticket >> 6, pos_in = ticket & 63u;
+  if (lane == 0) st64(&a.w.tile_status[ticket], item + 1);
+  uint64_t v = 0;
+  if (lane < pos_in) v = spin_word(a, &a.w.tile_status[(blk << 6) + lane]) - 1;
+  const uint64_t pre_in = wave_sum_u64(v);
+  const bool last_in_blk = pos_in == 63 || ticket + 1 == a.sh.ntiles;
+  if (last_in_blk && lane == 0) st64(&a.w.block_status[blk], kAgg | (pre_in + item));
+  uint64_t excl_b = 0;  // items of all earlier blocks
+  int64_t top = (int64_t)blk - 1;
+  while (top >= 0) {
+    const int64_t idx = top - (int64_t)lane;
+    const uint64_t w = idx >= 0 ? spin_word(a, &a.w.block_status[idx]) : kIncl;  // before block 0: 0
+    const uint64_t incl_mask = __ballot((w >> 62) == 2);
+    if (incl_mask) {
+      const int L = __ffsll((long long)incl_mask) - 1;
+      excl_b += wave_sum_u64((int)lane <= L ? (w & kVal) : 0);
+      break;
     }
-    if (lane == 0) st64(&a.w.tile_status[ticket], kIncl | (excl + item));
+    excl_b += wave_sum_u64(w & kVal);
+    top -= 64;
   }
+  if (last_in_blk && lane == 0) st64(&a.w.block_status[blk], kIncl | (excl_b + pre_in + item));
+  const uint64_t excl = excl_b + pre_in;
   if (lane == 0) {
     uint64_t pos = a.sh.base_bytes + excl;
     if (k == 0 && t == 0) {
@@ -1340,59 +1352,256 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// assembly pass for D = 64*C: every row of the segment is in the hash table,
-// so a tile reads its first occurrences, sizes its record, takes its place in
-// the stream (look-back) and copies its staged planes there.
+// assembly for D = 64*C, after every row is in the hash table, in three
+// launches that never wait on one another's workgroups:
+//   size   one wave per tile: first occurrences, record layout and size, added
+//          into sums over blocks of 64 tiles and over segments
+//   write  one workgroup per tile: its offset from those sums, the record, the
+//          tile's directory entry and, from first tiles, the segment and
+//          stream headers and tables
 // ---------------------------------------------------------------------------
+struct TileCoord {
+  uint32_t s, k, rows, ntiles, n, pch, t;
+};
+__device__ __forceinline__ TileCoord tile_coord(const EncArgs& a, uint32_t ticket) {
+  TileCoord c;
+  if (a.sh.tiles_per_seg) {
+    c.s = ticket / a.sh.tiles_per_seg;
+    c.k = ticket - c.s * a.sh.tiles_per_seg;
+  } else {
+    c.s = find_segment(a.w.seg_tile_base, a.sh.nseg, ticket);
+    c.k = ticket - a.w.seg_tile_base[c.s];
+  }
+  c.pch = c.s / a.sh.T;
+  c.t = c.s % a.sh.T;
+  const uint32_t r0 = chunk_row0(a.sh, c.pch);
+  c.rows = chunk_row0(a.sh, c.pch + 1) - r0;
+  c.ntiles = (c.rows + kTileRows - 1) / kTileRows;
+  c.n = c.ntiles ? min(kTileRows, c.rows - c.k * kTileRows) : 0;
+  return c;
+}
+
+// Record layout of a tile (same rules as size_record).
+struct RecLayout {
+  uint32_t mode, off_refs, off_opos, off_oval, off_pl;
+  uint64_t rec;  // record bytes
+};
+__device__ __forceinline__ RecLayout rec_layout(uint32_t n, uint32_t U, uint32_t nblk, uint32_t sumw,
+                                                uint32_t nout, uint32_t rows, uint32_t D, bool valid) {
+  RecLayout L;
+  const uint32_t rb = rows <= 65536 ? 2 : 4;
+  L.off_refs = (uint32_t)align_up(16 + nblk, 4);
+  L.off_opos = (uint32_t)align_up(L.off_refs + rb * (n - U), 4);
+  L.off_oval = L.off_opos + 4 * nout;
+  L.off_pl = (uint32_t)align_up(L.off_oval + 4 * nout, 8);
+  const uint64_t bp = align_up(L.off_pl + 8ull * sumw, 16);
+  const uint64_t raw = 16 + align_up(4ull * n * D, 16);
+  L.mode = (valid && bp < raw) ? 1u : 0u;
+  L.rec = n ? (L.mode ? bp : raw) : 0;
+  return L;
+}
+
+__device__ __forceinline__ uint64_t seg_prefix_bytes(uint32_t ntiles) { return 32 + align_up(4ull * ntiles, 16); }
+
+// Size pass: one workgroup per block of 64 tiles, four tiles per wave (their
+// loads are issued together); the block's item sum is stored once.
+constexpr uint32_t kSizeThreads = 1024;
+constexpr uint32_t kTilesPerWave = kTileRows / (kSizeThreads / 64);  // 4
 template <int C>
-__global__ void __launch_bounds__(kThreads) ec_assemble_fast(EncArgs a) {
+__global__ void __launch_bounds__(kSizeThreads) ec_size_fast(EncArgs a) {
   constexpr uint32_t D = 64u * C;
-  __shared__ EncShared sh;
+  constexpr uint32_t Q = kTilesPerWave;
+  __shared__ uint64_t s_sum[kSizeThreads / 64];
+  const uint32_t lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const uint32_t t0 = blockIdx.x * kTileRows + wv * Q;
+  TileCoord c[Q];
+  uint32_t slot[Q];
+  uint8_t wb[Q][C];
+#pragma unroll
+  for (uint32_t q = 0; q < Q; q++) {
+    const uint32_t ticket = min(t0 + q, a.sh.ntiles - 1);  // past the end: a copy, unused
+    c[q] = tile_coord(a, ticket);
+    // staged slot and widths (garbage when the segment is stored raw, then unused)
+    const uint64_t rowi = (uint64_t)ticket * kTileRows + lane;
+    slot[q] = a.w.stage_slot[rowi];
+#pragma unroll
+    for (uint32_t j = 0; j < C; j++) wb[q][j] = a.w.stage_w[rowi * C + j];
+  }
+  bool valid[Q];
+  float eb[Q];
+#pragma unroll
+  for (uint32_t q = 0; q < Q; q++) {
+    if (q > 0 && c[q].t == c[q - 1].t) {
+      valid[q] = valid[q - 1];
+      eb[q] = eb[q - 1];
+    } else {
+      eb[q] = table_eb(a, c[q].t, valid[q]);
+    }
+  }
+  uint32_t first[Q];
+#pragma unroll
+  for (uint32_t q = 0; q < Q; q++) {
+    first[q] = c[q].k * kTileRows + lane;
+    if (valid[q] && lane < c[q].n) {
+      const uint32_t cap_mask = (1u << a.w.hash_log2[c[q].s]) - 1u;
+      first[q] = (uint32_t)ld64(&a.w.hash[a.w.hash_off[c[q].s] + (slot[q] & cap_mask)]) - 1u;
+    }
+  }
+  uint64_t items = 0;
+#pragma unroll
+  for (uint32_t q = 0; q < Q; q++) {
+    const uint32_t ticket = t0 + q;
+    if (ticket >= a.sh.ntiles) break;
+    const TileCoord& cq = c[q];
+    const uint64_t rowi = (uint64_t)ticket * kTileRows + lane;
+    const bool inrow = lane < cq.n;
+    const bool uniq = valid[q] && inrow && first[q] == cq.k * kTileRows + lane;
+    const uint64_t bm = __ballot(uniq);
+    uint32_t rw = 0, ro = 0;
+    if (uniq) {
+#pragma unroll
+      for (uint32_t j = 0; j < C; j++) {
+        rw += wb[q][j] & 0x7Fu;
+        if (wb[q][j] & kOutlierFlag) ro += (uint32_t)__popcll(a.w.stage_om[rowi * C + j]);
+      }
+    }
+    const uint32_t sumw = wave_sum_u32(rw), nout = wave_sum_u32(ro);
+    const uint32_t U = (uint32_t)__popcll(bm);
+    const RecLayout L = rec_layout(cq.n, U, U * C, sumw, nout, cq.rows, D, valid[q]);
+    if (inrow) a.w.tile_first[rowi] = first[q];
+    if (a.dbg_first && inrow)
+      a.dbg_first[(uint64_t)cq.t * a.sh.B + chunk_row0(a.sh, cq.pch) + cq.k * kTileRows + lane] = first[q];
+    const uint64_t pre =
+        cq.k == 0 ? seg_prefix_bytes(cq.ntiles) + (cq.t == 0 ? align_up(8ull * a.sh.T, 16) : 0) : 0;
+    const uint64_t item = L.rec + pre;
+    items += item;
+    if (lane == 0) {
+      a.w.tile_status[ticket] = item;
+      uint4 info;
+      info.x = U;
+      info.y = L.mode ? nout : 0u;
+      info.z = sumw;
+      info.w = L.mode | (valid[q] ? 0x100u : 0u);
+      reinterpret_cast<uint4*>(a.w.tile_info)[ticket] = info;
+      a.w.tile_bitmap[ticket] = bm;
+      if (cq.k == 0) a.w.seg_eb[cq.s] = valid[q] ? f2u(eb[q]) : 0u;
+    }
+  }
+  if (lane == 0) s_sum[wv] = items;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint64_t sum = 0;
+    for (uint32_t w = 0; w < kSizeThreads / 64; w++) sum += s_sum[w];
+    a.w.block_status[blockIdx.x] = sum;
+  }
+}
+
+// Stream bytes before tile j (its item included for no earlier tile), whole
+// wave: the sums of the 64-tile blocks before j's block plus the items of the
+// tiles before j in its block, lane-parallel.
+__device__ __forceinline__ uint64_t tiles_before(const EncArgs& a, uint32_t j) {
+  const uint32_t lane = threadIdx.x & 63, blk = j >> 6;
+  uint64_t v = lane < (j & 63u) ? a.w.tile_status[(blk << 6) + lane] : 0;
+  for (uint32_t b = lane; b < blk; b += 64) v += a.w.block_status[b];
+  return wave_sum_u64(v);
+}
+
+// The tile's entry in its segment's tile directory; a segment's first tile
+// also writes the segment header, the directory pad and the segment's entry in
+// its chunk table; the stream's first tile writes the chunk byte counts and the
+// stream header.  Whole workgroup.  ss: segment start, se: segment end, cs:
+// start of the segment's chunk, un: the segment's U and n_out.
+__device__ void write_stream_tables(const EncArgs& a, const TileCoord& c, uint32_t ticket,
+                                    uint64_t rec_abs, uint64_t ss, uint64_t se, uint64_t cs,
+                                    const uint32_t* un, uint64_t total) {
+  const uint32_t tid = threadIdx.x, T = a.sh.T, P = a.sh.P;
+  if (c.ntiles && tid == 0) reinterpret_cast<uint32_t*>(a.out + ss + 32)[c.k] = (uint32_t)(rec_abs - ss);
+  if (c.k == 0) {
+    uint8_t* sg = a.out + ss;
+    const uint32_t dend = 32 + 4 * c.ntiles, dpad = (uint32_t)align_up(dend, 16) - dend;
+    if (tid < dpad) sg[dend + tid] = 0;
+    if (tid == 0) {
+      const uint32_t ebw = a.w.seg_eb[c.s];
+      uint32_t* h = reinterpret_cast<uint32_t*>(sg);
+      h[0] = c.rows;
+      h[1] = c.ntiles;
+      h[2] = ebw;
+      h[3] = ebw ? 1u : 0u;
+      h[4] = un[0];
+      h[5] = un[1];
+      reinterpret_cast<uint64_t*>(sg)[3] = se - ss;
+      reinterpret_cast<uint64_t*>(a.out + cs)[c.t] = ss - cs;
+      if (c.t == T - 1 && (T & 1u)) reinterpret_cast<uint64_t*>(a.out + cs)[T] = 0;  // table pad
+      if (a.report) a.report->seg_bytes[c.s] = se - ss;
+      if (c.t == T - 1) reinterpret_cast<uint64_t*>(a.out + 64)[c.pch] = se - cs;  // chunk bytes
+    }
+  }
+  if (ticket == 0 && tid == 0) {
+    if (P & 1u) reinterpret_cast<uint64_t*>(a.out + 64)[P] = 0;
+    uint32_t* h = reinterpret_cast<uint32_t*>(a.out);
+    h[0] = kMagic;
+    h[1] = kVersion | (kCoderBitpack << 16);
+    h[2] = T;
+    h[3] = a.sh.B;
+    h[4] = a.sh.D;
+    h[5] = P;
+    h[6] = kTileRows;
+    h[7] = a.eb_mode;
+    uint64_t* h64 = reinterpret_cast<uint64_t*>(a.out);
+    h64[4] = (uint64_t)a.iter;
+    h64[5] = 4ull * T * a.sh.B * a.sh.D;
+    h64[6] = total;
+    h64[7] = 0;
+    if (a.report) a.report->total_bytes = total;
+  }
+}
+
+template <int C>
+__global__ void __launch_bounds__(kThreads) ec_write_fast(EncArgs a) {
+  constexpr uint32_t D = 64u * C;
   __shared__ uint64_t s_omask[kTileRows][C];
   __shared__ uint32_t s_cbase[kTileRows][C];  // plane-word offset of each block in the record
   __shared__ uint32_t s_first[kTileRows], s_obase[kTileRows];
   __shared__ uint8_t s_w[kTileRows][C];
   __shared__ uint8_t s_urow[kTileRows];
+  __shared__ uint64_t s_rec_abs, s_seg_start, s_seg_end, s_chunk_start, s_total, s_bitmap;
+  __shared__ uint32_t s_un[2];
+  __shared__ uint4 s_info;
   const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const uint32_t T = a.sh.T;
-
-  if (tid == 0) take_tile(a, sh);
-  __syncthreads();
-  const uint32_t ticket = sh.ticket, s = sh.seg, k = sh.tile, n = sh.n, rows = sh.rows;
-  const uint32_t pch = s / T, t = s % T;
-  const uint32_t row0 = chunk_row0(a.sh, pch);
-  const float* xt = a.x + ((uint64_t)t * a.sh.B + row0 + (uint64_t)k * kTileRows) * D;
-
-  // ---- first occurrences, widths, per-block plane and outlier bases (wave 0) ----
+  const uint32_t ticket = blockIdx.x;
+  const TileCoord c = tile_coord(a, ticket);
+  const uint32_t n = c.n;
+  const float* xt = a.x + ((uint64_t)c.t * a.sh.B + chunk_row0(a.sh, c.pch) + (uint64_t)c.k * kTileRows) * D;
+  // every staged plane word of the tile is requested before the metadata
+  // (words above a block's width are loaded and then dropped)
+  const __amdgpu_buffer_rsrc_t rsrc =
+      buf_rsrc(a.w.stage_pl + (uint64_t)ticket * kTileRows * C * kStagePlanes, n * C * kStagePlanes * 8);
+  constexpr uint32_t kPass = kTileRows * C / (kThreads / 16);
+  const uint32_t b = tid & 15u;
+  uint64_t wv_[kPass];
+#pragma unroll
+  for (uint32_t ps = 0; ps < kPass; ps++) {
+    const uint32_t blk = ps * (kThreads / 16) + (tid >> 4);
+    wv_[ps] = buf_ld_u64(rsrc, b < kStagePlanes ? (blk * kStagePlanes + b) * 8 : kOff);
+  }
   if (wv == 0) {
-    bool valid;
-    const float eb = table_eb(a, t, valid);
-    const bool inrow = lane < n;
-    uint32_t first = k * kTileRows + lane;
+    const uint64_t rowi = (uint64_t)ticket * kTileRows + lane;
+    const uint64_t bitmap = a.w.tile_bitmap[ticket];
+    const uint4 info = reinterpret_cast<const uint4*>(a.w.tile_info)[ticket];
     uint8_t wb[C];
 #pragma unroll
-    for (uint32_t j = 0; j < C; j++) wb[j] = 0;
-    if (valid && inrow) {
-      const uint32_t slot = a.w.stage_slot[(uint64_t)ticket * kTileRows + lane];
-      const uint8_t* sw = a.w.stage_w + ((uint64_t)ticket * kTileRows + lane) * C;
-#pragma unroll
-      for (uint32_t j = 0; j < C; j++) wb[j] = sw[j];
-      first = (uint32_t)ld64(&a.w.hash[a.w.hash_off[s] + slot]) - 1u;
-    }
-    const bool uniq = valid && inrow && first == k * kTileRows + lane;
-    const uint64_t bm = __ballot(uniq);
+    for (uint32_t j = 0; j < C; j++) wb[j] = a.w.stage_w[rowi * C + j];
+    const uint32_t first = a.w.tile_first[rowi];
+    const bool uniq = (bitmap >> lane) & 1ull;
     uint32_t rw = 0, ro = 0;
 #pragma unroll
     for (uint32_t j = 0; j < C; j++) {
-      uint64_t om = 0;
-      if (wb[j] & kOutlierFlag) om = a.w.stage_om[((uint64_t)ticket * kTileRows + lane) * C + j];
-      const uint32_t w = wb[j] & 0x7Fu;
+      const uint32_t w = uniq ? wb[j] & 0x7Fu : 0u;
+      const uint64_t om = (uniq && (wb[j] & kOutlierFlag)) ? a.w.stage_om[rowi * C + j] : 0ull;
       s_omask[lane][j] = om;
       s_w[lane][j] = (uint8_t)w;
-      if (uniq) {
-        rw += w;
-        ro += (uint32_t)__popcll(om);
-      }
+      rw += w;
+      ro += (uint32_t)__popcll(om);
     }
     uint32_t iw = rw, io = ro;  // inclusive scans over lanes
     for (int o = 1; o < 64; o <<= 1) {
@@ -1409,84 +1618,120 @@ __global__ void __launch_bounds__(kThreads) ec_assemble_fast(EncArgs a) {
       cb += s_w[lane][j];
     }
     s_obase[lane] = io - ro;
-    if (inrow) s_first[lane] = first;
-    if (uniq) s_urow[__popcll(bm & __lanemask_lt())] = (uint8_t)lane;
-    if (a.dbg_first && inrow)
-      a.dbg_first[(uint64_t)t * a.sh.B + row0 + k * kTileRows + lane] = first;
-    const uint32_t sumw = __shfl(iw, 63), nout = __shfl(io, 63);
+    s_first[lane] = first;
+    if (uniq) s_urow[__popcll(bitmap & __lanemask_lt())] = (uint8_t)lane;
     if (lane == 0) {
-      sh.eb = eb;
-      sh.valid = valid;
-      sh.bitmap = bm;
-      const uint32_t U = (uint32_t)__popcll(bm);
-      size_record(a, sh, valid, n, U, U * C, sumw, nout);
+      s_bitmap = bitmap;
+      s_info = info;
     }
-    place_record(a, sh);
+  } else if (wv == 1) {  // the tile's and its segment's places in the stream
+    const uint64_t before = tiles_before(a, ticket), seg_before = tiles_before(a, ticket - c.k);
+    if (lane == 0) {
+      const uint64_t chunk_prefix = c.t == 0 ? align_up(8ull * a.sh.T, 16) : 0;
+      const uint64_t ss = a.sh.base_bytes + seg_before + chunk_prefix;
+      s_seg_start = ss;
+      s_rec_abs = c.k == 0 ? ss + seg_prefix_bytes(c.ntiles) : a.sh.base_bytes + before;
+    }
+  } else if (wv == 2 && c.k == 0) {  // the segment's end and its chunk's start
+    const uint32_t sched = c.ntiles ? c.ntiles : 1u;
+    const uint64_t next = tiles_before(a, ticket + sched);
+    const uint64_t cfirst = c.t == 0 ? 0 : tiles_before(a, a.w.seg_tile_base[c.pch * a.sh.T]);
+    if (lane == 0) {
+      s_seg_end = a.sh.base_bytes + next;
+      s_chunk_start = a.sh.base_bytes + cfirst;
+    }
+  } else if (wv == 3 && c.k == 0) {  // the segment's U and n_out; the stream's size
+    const uint32_t sched = c.ntiles ? c.ntiles : 1u;
+    uint32_t u = 0, o = 0;
+    for (uint32_t j = lane; j < sched; j += 64) {
+      u += a.w.tile_info[4 * (ticket + j)];
+      o += a.w.tile_info[4 * (ticket + j) + 1];
+    }
+    u = wave_sum_u32(u);
+    o = wave_sum_u32(o);
+    const uint64_t all = ticket == 0 ? tiles_before(a, a.sh.ntiles) : 0;
+    if (lane == 0) {
+      s_un[0] = u;
+      s_un[1] = o;
+      s_total = a.sh.base_bytes + all;
+    }
   }
   __syncthreads();
-
-  // ---- write the tile record ----
-  if (n > 0 && sh.fits) {
-    uint8_t* rec = a.out + sh.rec_abs;
-    const uint32_t mode = sh.mode, U = sh.U, nblk = sh.nblk;
-    const uint64_t bitmap = sh.bitmap;
-    if (tid == 0) {
-      const uint64_t w1 = (uint64_t)(mode ? sh.nout : 0u) | ((uint64_t)U << 32) | ((uint64_t)mode << 48);
-      reinterpret_cast<uint64_t*>(rec)[0] = bitmap;
-      reinterpret_cast<uint64_t*>(rec)[1] = w1;
+  if (c.k == 0) {
+    const uint64_t cs = c.t == 0 ? s_seg_start - align_up(8ull * a.sh.T, 16) : s_chunk_start;
+    if (s_seg_end > a.out_cap) {  // cannot happen when out_cap >= the maximum stream size
+      if (tid == 0) report_error(a.report, kDevErrTimeout);
+      return;
     }
-    if (mode == 0) {
-      write_raw_rows(rec, xt, n * D, D);
-    } else {
-      const uint32_t rb = rows <= 65536 ? 2 : 4;
-      for (uint32_t b = tid; b < nblk; b += kThreads) rec[16 + b] = s_w[s_urow[b / C]][b % C];
-      if (tid < n && !((bitmap >> tid) & 1ull)) {
-        const uint32_t j = tid - (uint32_t)__popcll(bitmap & ((1ull << tid) - 1ull));
-        if (rb == 2) reinterpret_cast<uint16_t*>(rec + sh.off_refs)[j] = (uint16_t)s_first[tid];
-        else reinterpret_cast<uint32_t*>(rec + sh.off_refs)[j] = s_first[tid];
-      }
-      write_record_pads(rec, sh, n, rows);
-      // staged plane words: 16 lanes per block, lane = plane; every load is
-      // issued before the first store
-      const __amdgpu_buffer_rsrc_t rsrc =
-          buf_rsrc(a.w.stage_pl + (uint64_t)ticket * kTileRows * C * kStagePlanes, kTileRows * C * kStagePlanes * 8);
-      const __amdgpu_buffer_rsrc_t rdst = buf_rsrc(rec + sh.off_pl, sh.sumw * 8);
-      constexpr uint32_t kPass = kTileRows * C / (kThreads / 16);
-      const uint32_t b = tid & 15u;
-      uint64_t wv_[kPass];
-      uint32_t dst[kPass];
+    write_stream_tables(a, c, ticket, s_rec_abs, s_seg_start, s_seg_end, cs, s_un, s_total);
+  } else {
+    write_stream_tables(a, c, ticket, s_rec_abs, s_seg_start, 0, 0, s_un, 0);
+  }
+  if (n == 0) return;
+  const uint4 info = s_info;
+  const uint32_t U = info.x, nout = info.y, sumw = info.z, mode = info.w & 0xFFu;
+  const bool valid = (info.w >> 8) & 1u;
+  const uint64_t bitmap = s_bitmap;
+  const RecLayout L = rec_layout(n, U, U * C, sumw, mode ? nout : 0u, c.rows, D, valid);
+  if (s_rec_abs + L.rec > a.out_cap) {  // cannot happen when out_cap >= the maximum stream size
+    if (tid == 0) report_error(a.report, kDevErrTimeout);
+    return;
+  }
+  uint8_t* rec = a.out + s_rec_abs;
+  if (tid == 0) {
+    const uint64_t w1 = (uint64_t)(mode ? nout : 0u) | ((uint64_t)U << 32) | ((uint64_t)mode << 48);
+    reinterpret_cast<uint64_t*>(rec)[0] = bitmap;
+    reinterpret_cast<uint64_t*>(rec)[1] = w1;
+  }
+  if (mode == 0) {
+    write_raw_rows(rec, xt, n * D, D);
+    return;
+  }
+  const uint32_t nblk = U * C;
+  const uint32_t rb = c.rows <= 65536 ? 2 : 4;
+  for (uint32_t b = tid; b < nblk; b += kThreads) rec[16 + b] = s_w[s_urow[b / C]][b % C];
+  for (uint32_t b = nblk + tid; b < L.off_refs - 16; b += kThreads) rec[16 + b] = 0;
+  if (tid < n && !((bitmap >> tid) & 1ull)) {
+    const uint32_t j = tid - (uint32_t)__popcll(bitmap & ((1ull << tid) - 1ull));
+    if (rb == 2) reinterpret_cast<uint16_t*>(rec + L.off_refs)[j] = (uint16_t)s_first[tid];
+    else reinterpret_cast<uint32_t*>(rec + L.off_refs)[j] = s_first[tid];
+  }
+  {
+    const uint32_t rend = L.off_refs + rb * (n - U);
+    if (tid < L.off_opos - rend) rec[rend + tid] = 0;
+    const uint32_t oend = L.off_oval + 4 * nout;
+    if (tid < L.off_pl - oend) rec[oend + tid] = 0;
+    const uint64_t pend = L.off_pl + 8ull * sumw;
+    if (tid < L.rec - pend) rec[pend + tid] = 0;
+  }
+  // staged plane words (loaded above): 16 lanes per block, lane = plane
+  const __amdgpu_buffer_rsrc_t rdst = buf_rsrc(rec + L.off_pl, sumw * 8);
 #pragma unroll
-      for (uint32_t ps = 0; ps < kPass; ps++) {
-        const uint32_t blk = ps * (kThreads / 16) + (tid >> 4), row = blk / C, j = blk % C;
-        const bool use = blk < n * C && ((bitmap >> row) & 1ull) && b < s_w[row][j];
-        wv_[ps] = buf_ld_u64(rsrc, use ? (blk * kStagePlanes + b) * 8 : kOff);
-        dst[ps] = use ? (s_cbase[row][j] + b) * 8 : kOff;
-      }
+  for (uint32_t ps = 0; ps < kPass; ps++) {
+    const uint32_t blk = ps * (kThreads / 16) + (tid >> 4), row = blk / C, j = blk % C;
+    const bool use = blk < n * C && ((bitmap >> row) & 1ull) && b < s_w[row][j];
+    buf_st_u64(rdst, use ? (s_cbase[row][j] + b) * 8 : kOff, wv_[ps]);
+  }
+  if (nout) {
+    uint32_t* opos = reinterpret_cast<uint32_t*>(rec + L.off_opos);
+    uint32_t* oval = reinterpret_cast<uint32_t*>(rec + L.off_oval);
+    for (uint32_t u = wv; u < U; u += kThreads / 64) {
+      const uint32_t i = s_urow[u];
+      uint32_t ob = s_obase[i];
 #pragma unroll
-      for (uint32_t ps = 0; ps < kPass; ps++) buf_st_u64(rdst, dst[ps], wv_[ps]);
-      if (sh.nout) {
-        uint32_t* opos = reinterpret_cast<uint32_t*>(rec + sh.off_opos);
-        uint32_t* oval = reinterpret_cast<uint32_t*>(rec + sh.off_oval);
-        for (uint32_t u = wv; u < U; u += kThreads / 64) {
-          const uint32_t i = s_urow[u];
-          uint32_t ob = s_obase[i];
-#pragma unroll
-          for (uint32_t j = 0; j < C; j++) {
-            const uint64_t om = s_omask[i][j];
-            if (om) {
-              if ((om >> lane) & 1ull) {
-                const uint32_t o = ob + (uint32_t)__popcll(om & __lanemask_lt());
-                opos[o] = u * D + 64 * j + lane;
-                oval[o] = f2u(xt[(uint64_t)i * D + 64 * j + lane]);
-              }
-              ob += (uint32_t)__popcll(om);
-            }
+      for (uint32_t j = 0; j < C; j++) {
+        const uint64_t om = s_omask[i][j];
+        if (om) {
+          if ((om >> lane) & 1ull) {
+            const uint32_t o = ob + (uint32_t)__popcll(om & __lanemask_lt());
+            opos[o] = u * D + 64 * j + lane;
+            oval[o] = f2u(xt[(uint64_t)i * D + 64 * j + lane]);
           }
+          ob += (uint32_t)__popcll(om);
         }
       }
     }
   }
-  complete_tile(a, sh, sh.valid != 0, sh.eb);
 }
 
 // ---------------------------------------------------------------------------
@@ -2323,16 +2568,20 @@ hipError_t launch_encode(const EncArgs& a, hipStream_t s) {
 bool encode_has_assembly(uint32_t D) { return D == 64 || D == 128 || D == 256; }
 
 hipError_t launch_assemble(const EncArgs& a, hipStream_t s) {
-  const dim3 grid(a.sh.ntiles), block(kThreads);
+  const dim3 tiles(a.sh.ntiles), blocks((a.sh.ntiles + kTileRows - 1) / kTileRows);
+  const dim3 block(kThreads), sblock(kSizeThreads);
   switch (a.sh.D) {
     case 64:
-      hipLaunchKernelGGL(ec_assemble_fast<1>, grid, block, 0, s, a);
+      hipLaunchKernelGGL(ec_size_fast<1>, blocks, sblock, 0, s, a);
+      hipLaunchKernelGGL(ec_write_fast<1>, tiles, block, 0, s, a);
       break;
     case 128:
-      hipLaunchKernelGGL(ec_assemble_fast<2>, grid, block, 0, s, a);
+      hipLaunchKernelGGL(ec_size_fast<2>, blocks, sblock, 0, s, a);
+      hipLaunchKernelGGL(ec_write_fast<2>, tiles, block, 0, s, a);
       break;
     case 256:
-      hipLaunchKernelGGL(ec_assemble_fast<4>, grid, block, 0, s, a);
+      hipLaunchKernelGGL(ec_size_fast<4>, blocks, sblock, 0, s, a);
+      hipLaunchKernelGGL(ec_write_fast<4>, tiles, block, 0, s, a);
       break;
     default:
       return hipErrorInvalidValue;

@@ -20,8 +20,9 @@ struct Layout {
   // byte offsets inside the workspace
   uint64_t eb_base, mult, seg_tile_base, hash_off, hash_log2, range_part;
   uint64_t dyn, seg_start, seg_end, chunk_start, seg_fin;
-  uint64_t tile_status, tile_inserted, tile_rec, tile_U, tile_nout, hash;
+  uint64_t tile_status, block_status, tile_inserted, tile_rec, tile_U, tile_nout, hash;
   uint64_t stage_pl = 0, stage_w = 0, stage_om = 0, stage_slot = 0;
+  uint64_t tile_info = 0, tile_bitmap = 0, tile_first = 0, seg_eb = 0;
   uint64_t dyn_bytes, total;
   uint32_t nbr;
   std::vector<uint32_t> seg_tile_base_v;
@@ -150,6 +151,7 @@ ec_status make_layout(const ec_plan_desc* d, Layout* L) {
   L->chunk_start = take(8ull * P);
   L->seg_fin = take(4ull * nseg);
   L->tile_status = take(8ull * tiles);
+  L->block_status = take(8ull * ((tiles + 63) / 64));
   L->tile_inserted = take(4ull * tiles);
   L->tile_rec = take(8ull * tiles);
   L->tile_U = take(4ull * tiles);
@@ -163,6 +165,10 @@ ec_status make_layout(const ec_plan_desc* d, Layout* L) {
     L->stage_w = take(blocks);
     L->stage_om = take(8ull * blocks);
     L->stage_slot = take(4ull * 64 * tiles);
+    L->tile_info = take(16ull * tiles);
+    L->tile_bitmap = take(8ull * tiles);
+    L->tile_first = take(4ull * 64 * tiles);
+    L->seg_eb = take(4ull * nseg);
     o = aup(o, 256);
   }
   L->total = o;
@@ -331,6 +337,7 @@ ec_status ec_plan(const ec_plan_desc* desc, ec_plan_t* out) {
   w.chunk_start = reinterpret_cast<uint64_t*>(ws + L.chunk_start);
   w.seg_fin = reinterpret_cast<uint32_t*>(ws + L.seg_fin);
   w.tile_status = reinterpret_cast<uint64_t*>(ws + L.tile_status);
+  w.block_status = reinterpret_cast<uint64_t*>(ws + L.block_status);
   w.tile_inserted = reinterpret_cast<uint32_t*>(ws + L.tile_inserted);
   w.tile_rec = reinterpret_cast<uint64_t*>(ws + L.tile_rec);
   w.tile_U = reinterpret_cast<uint32_t*>(ws + L.tile_U);
@@ -341,6 +348,10 @@ ec_status ec_plan(const ec_plan_desc* desc, ec_plan_t* out) {
     w.stage_w = ws + L.stage_w;
     w.stage_om = reinterpret_cast<uint64_t*>(ws + L.stage_om);
     w.stage_slot = reinterpret_cast<uint32_t*>(ws + L.stage_slot);
+    w.tile_info = reinterpret_cast<uint32_t*>(ws + L.tile_info);
+    w.tile_bitmap = reinterpret_cast<uint64_t*>(ws + L.tile_bitmap);
+    w.tile_first = reinterpret_cast<uint32_t*>(ws + L.tile_first);
+    w.seg_eb = reinterpret_cast<uint32_t*>(ws + L.seg_eb);
   }
   *out = pl;
   return EC_OK;
