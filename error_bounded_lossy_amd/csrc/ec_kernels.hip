@@ -1112,6 +1112,9 @@ __device__ __forceinline__ void static_for(F&& f) {
 // bit 7 set on blocks holding outliers, outlier masks [64][C] u64 (flagged
 // blocks only), hash slot of every row [64] u32.
 constexpr uint32_t kStagePlanes = 12;
+#ifndef EC_QUANT_PREFETCH
+#define EC_QUANT_PREFETCH 0
+#endif
 constexpr uint8_t kOutlierFlag = 0x80;
 
 // ---------------------------------------------------------------------------
@@ -1141,7 +1144,10 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
   const float* xs = a.x + ((uint64_t)t * a.sh.B + row0) * D;
   const float* xt = xs + (uint64_t)k * kTileRows * D;
   const uint32_t rbeg = wv * kRowsPerWave;
-  float xv[2][kRB][C];  // double buffer: the next batch loads while one is coded
+  // with kPrefetch the next batch loads while one is coded (two buffers);
+  // without, other resident waves cover the load latency
+  constexpr bool kPrefetch = EC_QUANT_PREFETCH;
+  float xv[kPrefetch ? 2 : 1][kRB][C];
   const __amdgpu_buffer_rsrc_t rx = buf_rsrc(xt, n * D * 4);  // rows past n read as 0
   auto load_batch = [&](uint32_t nb, float (&buf)[kRB][C]) {
 #pragma unroll
@@ -1191,16 +1197,18 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
 
   static_for<0, (int)kNB>([&](auto nbc) {
     constexpr uint32_t nb = decltype(nbc)::value;
-    float (&xb)[kRB][C] = xv[nb & 1];
-    if (nb + 1 < kNB) load_batch(nb + 1, xv[(nb + 1) & 1]);
+    float (&xb)[kRB][C] = xv[kPrefetch ? (nb & 1) : 0];
+    if (kPrefetch && nb + 1 < kNB) load_batch(nb + 1, xv[kPrefetch ? ((nb + 1) & 1) : 0]);
+    if (!kPrefetch && nb > 0) load_batch(nb, xv[0]);
     const uint32_t ib = rbeg + nb * kRB;
     int q[kRB][C];
     uint64_t um = 0;
-    // q = rint(x / 2eb) via the correctly rounded reciprocal.  When the product
-    // is at least 2^-10 from every rounding boundary and inside the code range,
-    // rint agrees with rint(fl(x/s)) and |x - fl(q s)| is strictly below eb, so
-    // the value is not an outlier.  One compare: |f| < 2046.5/4104 (= 0.49866)
-    // and |tp| < 2046.5; NaN or infinite products are unsure.
+    // q = rint(x / 2eb) via the correctly rounded reciprocal r2: the product
+    // tp and fl(x/s) differ by less than 2^-22 |tp|, so when tp is at least
+    // 2^-21 |tp| inside a rounding interval (and well inside the code range)
+    // rint(tp) = rint(fl(x/s)) and |x - fl(q s)| is strictly below eb: the
+    // value is not an outlier.  f = tp - rint(tp) is exact (Sterbenz); NaN or
+    // infinite products are unsure.
 #pragma unroll
     for (uint32_t rr = 0; rr < kRB; rr++)
 #pragma unroll
@@ -1208,7 +1216,7 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
         const float tp = xb[rr][j] * r2;
         const float qf = rintf(tp);
         const float f = tp - qf;
-        um |= __ballot(!(fmaxf(fabsf(f) * 4104.0f, fabsf(tp)) < 2046.5f));
+        um |= __ballot(!(fmaf(fabsf(tp), 0x1p-21f, fabsf(f)) < 0.5f) || !(fabsf(tp) < 2046.5f));
         q[rr][j] = (int)qf;
       }
     uint32_t hs[kRB];
@@ -1220,11 +1228,12 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
         const uint32_t i = ib + rr;
 #pragma unroll
         for (uint32_t j = 0; j < C; j++) {
-          const float x = xb[rr][j];
+          // reloaded, so that the batch registers die with the fast pass
+          const float x = buf_ld_f32(rx, (i * D + 64 * j + lane) * 4);
           const float tp = x * r2;
           const float f = tp - rintf(tp);
           bool out = false;
-          if (i < n && !(fmaxf(fabsf(f) * 4104.0f, fabsf(tp)) < 2046.5f)) {
+          if (i < n && (!(fmaf(fabsf(tp), 0x1p-21f, fabsf(f)) < 0.5f) || !(fabsf(tp) < 2046.5f))) {
             const float tq = x / s2;
             const bool oor = !(fabsf(tq) <= 2047.0f);
             const float qf = rintf(tq);
