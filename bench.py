@@ -83,8 +83,9 @@ def cpu_baseline(x_cpu, w, min_seconds: float):
                       f"{done_bytes / 2**20:.0f} MiB) of batch t={w.iteration}, {spent:.1f} s"}
 
 
-KERNEL_PREFIX = {"prep": "ec_prep", "encode": ("ec_encode", "ec_quantize"), "assemble": "ec_assemble",
-                 "decode": "ec_decode"}
+KERNEL_PREFIX = {"prep": "ec_prep", "encode": ("ec_encode", "ec_quantize"),
+                 "assemble": ("ec_size", "ec_write"), "decode_index": "ec_dec_index",
+                 "decode": ("ec_decode",)}
 
 
 def _short_kernel(name: str) -> str:
@@ -290,7 +291,7 @@ def main():
         sys.exit(1)
     # per-kernel durations: the same K steps again, each launch bracketed by
     # HIP events on the stream it runs on
-    plan.profile_enable(True, max_launches=4 * args.steps + 8)
+    plan.profile_enable(True, max_launches=5 * args.steps + 8)
     for i in range(args.steps):
         step(args.warmup + i)
     torch.cuda.synchronize()
@@ -298,6 +299,7 @@ def main():
     t_enc, n_enc = plan.profile_read(ec.KERNEL_ENCODE)
     t_dec, n_dec = plan.profile_read(ec.KERNEL_DECODE)
     t_asm, n_asm = plan.profile_read(ec.KERNEL_ASSEMBLE)
+    t_dix, n_dix = plan.profile_read(ec.KERNEL_DECODE_INDEX)
     plan.profile_enable(False)
     _, _, st = plan.ratio(raise_on_error=False)
     if st != 0:
@@ -307,7 +309,7 @@ def main():
     rel = w0.eb_mode == ec.EB_REL_RANGE
     S = mean_bytes
     tc = (t_prep + t_enc + t_asm) / args.steps * 1e-3  # kernel time only
-    td = t_dec / args.steps * 1e-3
+    td = (t_dec + t_dix) / args.steps * 1e-3
     step_s = ms / args.steps * 1e-3
     bytes_c = 4 * N * (2 if rel else 1) + S
     bytes_d = S + 4 * N
@@ -321,6 +323,8 @@ def main():
     }
     if n_asm:
         kernels["assemble"] = (t_asm / n_asm, S)
+    if n_dix:  # reads record headers and widths only: no algorithmic bytes
+        kernels["decode_index"] = (t_dix / n_dix, 0)
     dom = max(kernels, key=lambda k: kernels[k][0])
     dom_ms, dom_bytes = kernels[dom]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9

@@ -25,6 +25,10 @@
 
 #include <type_traits>
 
+#ifndef EC_PREP_LOADS
+#define EC_PREP_LOADS 8  // 128-bit loads in flight per thread in the range pass
+#endif
+
 namespace ec {
 namespace {
 
@@ -200,18 +204,19 @@ __global__ void __launch_bounds__(kThreads) ec_prep_kernel(PrepArgs a) {
   float lo = INFINITY, hi = -INFINITY;
   if (beg < end) {
     if ((nel & 3) == 0) {
-      // four independent 128-bit loads in flight per thread
+      // eight independent 128-bit loads in flight per thread; indices past
+      // the range repeat its last element, which leaves min and max unchanged
       const float4* x4 = reinterpret_cast<const float4*>(xt);
       const uint64_t e4 = end / 4;
-      for (uint64_t i = beg / 4 + threadIdx.x; i < e4; i += 4 * kThreads) {
-        float4 v[4];
+      for (uint64_t i = beg / 4 + threadIdx.x; i < e4; i += EC_PREP_LOADS * kThreads) {
+        float4 v[EC_PREP_LOADS];
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
+        for (int u = 0; u < EC_PREP_LOADS; u++) {
           const uint64_t ii = i + (uint64_t)u * kThreads;
-          v[u] = ii < e4 ? x4[ii] : make_float4(NAN, NAN, NAN, NAN);
+          v[u] = x4[ii < e4 ? ii : e4 - 1];
         }
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
+        for (int u = 0; u < EC_PREP_LOADS; u++) {
           const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
           for (int c = 0; c < 4; c++) {
@@ -1460,7 +1465,7 @@ __global__ void __launch_bounds__(kSizeThreads) ec_size_fast(EncArgs a) {
 #pragma unroll
   for (uint32_t q = 0; q < Q; q++) {
     const uint32_t ticket = t0 + q;
-    if (ticket >= a.sh.ntiles) break;
+    if (ticket >= a.sh.ntiles) continue;  // (no early exit: the loop must unroll)
     const TileCoord& cq = c[q];
     const uint64_t rowi = (uint64_t)ticket * kTileRows + lane;
     const bool inrow = lane < cq.n;
@@ -2240,6 +2245,7 @@ __device__ __forceinline__ void patch_outliers(float (&v)[C], uint32_t e0, OP op
 // Un-zigzag two codes packed as 16-bit halves; returns them sign-extended.
 typedef unsigned short ushort2v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void unzigzag_pair(uint32_t zz2, int& qa, int& qb) {
+  asm volatile("" : "+v"(zz2));  // keeps the transpose whole (no split by demanded bits)
   const ushort2v z = __builtin_bit_cast(ushort2v, zz2);
   const short2v q = (short2v)(z >> (unsigned short)1) ^ -(short2v)(z & (unsigned short)1);
   qa = q.x;
@@ -2264,98 +2270,110 @@ __device__ __forceinline__ uint32_t sum_bytes(const uint8_t* p, uint32_t n) {
   return s;
 }
 
-// Decoder for D = 64*C.  Every row first gets, per 64-element block, the width
-// and the segment-relative word offset of its bit planes (in this tile's
-// record, or in the earlier tile its reference points into).  A wave then
-// decodes two blocks at once: lane L loads the 32-bit half (L >> 5) of plane
-// (L & 15) of block ((L >> 4) & 1), and the same 32x32 transpose as in the
-// encoder (its own inverse) leaves both blocks' zigzag codes of element L as
-// the halves of lane L.
+// Decoder for D = 64*C, in two launches:
+//   index   one wave per tile: locate and check the tile record, scan its
+//           widths, and resolve every row to where its bit planes are (this
+//           tile's record, or the earlier tile a reference points into):
+//           per block (segment word offset << 4 | width), per row its kind,
+//           first-occurrence index and outlier list
+//   decode  one workgroup per tile: two rounds of loads (descriptors, then
+//           plane words), the 32x32 transpose per block pair, stores
+// Lane L of a pair loads the 32-bit half (L >> 5) of plane (L & 15) of block
+// ((L >> 4) & 1); the encoder's transpose, its own inverse, leaves both
+// blocks' zigzag codes of element L in lane L.
+constexpr uint32_t kRowPlanes = 0, kRowRawRef = 1, kRowBad = 2, kRowOutliers = 0x100;
+constexpr uint32_t kTileOk = 1, kTileRaw = 2;
+
 template <int C>
-__global__ void __launch_bounds__(kThreads) ec_decode_fast(const uint8_t* __restrict__ in,
-                                                          float* __restrict__ yout, DecArgs a) {
+__global__ void __launch_bounds__(64) ec_dec_index(const uint8_t* __restrict__ in, DecArgs a) {
   constexpr uint32_t D = 64u * C;
-  constexpr uint32_t kRowsPerWave = kTileRows / (kThreads / 64);  // 16
-  // row kinds
-  constexpr uint32_t kPlanes = 0, kRawRef = 1, kBadRow = 2;
   __shared__ DecShared sh;
   __shared__ uint64_t s_rec;
   __shared__ uint8_t s_width[kTileRows * C];
   __shared__ uint32_t s_boff[kTileRows * C];
-  __shared__ uint32_t s_bo[kTileRows][C];  // plane word offset from the segment start
-  __shared__ uint8_t s_bw[kTileRows][C];
-  __shared__ uint32_t s_kind[kTileRows];
-  __shared__ uint32_t s_orec[kTileRows];   // segment offset of the record holding the row
-  __shared__ uint32_t s_ou[kTileRows];     // the row's first-occurrence index in that record
-  __shared__ uint32_t s_onum[kTileRows];   // outliers of that record
-  __shared__ uint32_t s_oofs[kTileRows];   // segment offset of its outlier positions
-  __shared__ uint32_t s_opos[kOutCap], s_oval[kOutCap];
-  const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const uint32_t T = a.sh.T, B = a.sh.B;
-  if (tid == 0) {
+  const uint32_t lane = threadIdx.x, ticket = blockIdx.x;
+  if (lane == 0) {
     uint64_t ro;
-    dec_locate(a, in, blockIdx.x, sh, ro);
+    dec_locate(a, in, ticket, sh, ro);
     s_rec = ro;
   }
   __syncthreads();
-  const uint32_t s = sh.seg, k = sh.tile, n = sh.n, rows = sh.rows;
-  const uint32_t pch = s / T, t = s % T;
-  float* yt = yout + ((uint64_t)t * B + chunk_row0(a.sh, pch) + (uint64_t)k * kTileRows) * D;
+  const uint32_t k = sh.tile, n = sh.n, rows = sh.rows;
+  uint4* dt = reinterpret_cast<uint4*>(a.dec_tile) + 2 * ticket;
+  const uint64_t seg_off = sh.seg_off, rec_off = s_rec, sbytes = sh.seg_bytes;
+  uint32_t flags = 0;
+  auto put_tile = [&]() {
+    if (lane == 0) {
+      dt[0] = make_uint4(flags, f2u(sh.eb), (uint32_t)seg_off, (uint32_t)(seg_off >> 32));
+      dt[1] = make_uint4((uint32_t)rec_off, (uint32_t)(rec_off >> 32), (uint32_t)sbytes, 0u);
+    }
+  };
+  if (!sh.ok || sbytes >= (1ull << 31)) {
+    if (lane == 0) report_error(a.report, kDevErrCorrupt);
+    put_tile();
+    return;
+  }
   if (n == 0) {
-    if (!sh.ok && tid == 0) report_error(a.report, kDevErrCorrupt);
+    flags = kTileOk;
+    put_tile();
     return;
   }
-  if (!sh.ok) {
-    for (uint32_t i = tid; i < n * D; i += kThreads) yt[i] = 0.0f;
-    if (tid == 0) report_error(a.report, kDevErrCorrupt);
-    return;
-  }
-  const uint8_t* sg = in + sh.seg_off;
-  const uint64_t rec_off = s_rec;
+  const uint8_t* sg = in + seg_off;
   const uint8_t* rec = in + rec_off;
-  const uint32_t rec_in_seg = (uint32_t)(rec_off - sh.seg_off);
+  const uint32_t rec_in_seg = (uint32_t)(rec_off - seg_off);
   const uint32_t mode = sh.tl.mode, U = sh.tl.U, nout = sh.tl.nout;
-  if (mode == 0) {  // RAW: rows verbatim
-    const float4* s4 = reinterpret_cast<const float4*>(rec + 16);
-    float4* y4 = reinterpret_cast<float4*>(yt);
-    for (uint32_t i = tid; i < n * D / 4; i += kThreads) y4[i] = s4[i];
+  if (mode == 0) {
+    flags = kTileOk | kTileRaw;
+    put_tile();
     return;
   }
-  const float eb = sh.eb, s2 = eb + eb;
-  const uint64_t sbytes = sh.seg_bytes;
   const uint32_t rb = rows <= 65536 ? 2 : 4;
   const uint64_t bitmap = sh.tl.bitmap;
   const uint32_t nblk = U * C;
-  const uint32_t off_refs = sh.tl.off_refs, off_opos = sh.tl.off_opos;
-  const uint32_t off_oval = sh.tl.off_oval, off_pl = sh.tl.off_pl;
-  const uint32_t* g_opos = reinterpret_cast<const uint32_t*>(rec + off_opos);
-  const uint32_t* g_oval = reinterpret_cast<const uint32_t*>(rec + off_oval);
-  uint32_t badw = 0;
-  for (uint32_t b = tid; b < nblk; b += kThreads) {
-    const uint32_t w = rec[16 + b];
-    badw |= w > 12;
-    s_width[b] = (uint8_t)w;
-    s_boff[b] = w;
+  const uint32_t off_refs = sh.tl.off_refs, off_opos = sh.tl.off_opos, off_pl = sh.tl.off_pl;
+  // widths and their exclusive scan (each lane owns up to four consecutive blocks)
+  uint32_t wl[4], lsum = 0, badw = 0;
+#pragma unroll
+  for (uint32_t q = 0; q < 4; q++) {
+    const uint32_t b = 4 * lane + q;
+    wl[q] = b < nblk ? rec[16 + b] : 0u;
+    badw |= wl[q] > 12;
+    lsum += wl[q];
   }
-  if (badw) sh.bad = 1;
-  const bool stage_out = nout <= kOutCap;
-  if (stage_out)
-    for (uint32_t i = tid; i < nout; i += kThreads) {
-      s_opos[i] = g_opos[i];
-      s_oval[i] = g_oval[i];
+  uint32_t incl = lsum;
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t v = __shfl_up(incl, o);
+    if (lane >= (uint32_t)o) incl += v;
+  }
+  uint32_t run = incl - lsum;
+#pragma unroll
+  for (uint32_t q = 0; q < 4; q++) {
+    const uint32_t b = 4 * lane + q;
+    if (b < nblk) {
+      s_width[b] = (uint8_t)wl[q];
+      s_boff[b] = run;
     }
-  const uint32_t sumw = nblk ? block_exclusive_scan(s_boff, nblk, sh.part) : 0;
+    run += wl[q];
+  }
+  const uint32_t sumw = __shfl(incl, 63);
   const uint64_t seg_words = sbytes / 8;
   const uint32_t pl_word0 = (rec_in_seg + off_pl) / 8;  // off_pl and records are 8-aligned
-  if (tid == 0 && (uint64_t)pl_word0 + sumw > seg_words) sh.bad = 1;
+  const bool bad = __any(badw) || (uint64_t)pl_word0 + sumw > seg_words;
+  __syncthreads();
+  if (bad) {
+    if (lane == 0) report_error(a.report, kDevErrCorrupt);
+    put_tile();
+    return;
+  }
+  flags = kTileOk;
+  put_tile();
 
-  // ---- where every row's planes are (lane-parallel: metadata loads overlap) ----
-  if (tid < n) {
-    const uint32_t i = tid, r = k * kTileRows + i;
+  // ---- where every row's planes are ----
+  if (lane < n) {
+    const uint32_t i = lane, r = k * kTileRows + i;
     const uint64_t below = bitmap & ((1ull << i) - 1ull);
-    uint32_t kind = kPlanes, u = 0, orec = rec_in_seg, onum = nout, oofs = rec_in_seg + off_opos;
-    uint32_t bo[C];
-    uint8_t bw[C];
+    uint32_t kind = kRowPlanes, u = 0, orec = rec_in_seg, onum = nout, oofs = rec_in_seg + off_opos;
+    uint32_t bo[C], bw[C];
 #pragma unroll
     for (uint32_t j = 0; j < C; j++) {
       bo[j] = 0;
@@ -2369,178 +2387,265 @@ __global__ void __launch_bounds__(kThreads) ec_decode_fast(const uint8_t* __rest
       const uint32_t ref = rb == 2 ? reinterpret_cast<const uint16_t*>(rec + off_refs)[jr]
                                    : reinterpret_cast<const uint32_t*>(rec + off_refs)[jr];
       if (ref >= r) {
-        kind = kBadRow;
+        kind = kRowBad;
       } else if (ref >= k * kTileRows) {
         const uint32_t i2 = ref - k * kTileRows;
         if ((bitmap >> i2) & 1ull) u = (uint32_t)__popcll(bitmap & ((1ull << i2) - 1ull));
-        else kind = kBadRow;
+        else kind = kRowBad;
       } else {
         local = false;
         const uint32_t k2 = ref / kTileRows, i2 = ref % kTileRows;
         DecTile t2 = locate_tile(sg, sbytes, sh.ntiles, rows, k2, D, true);
         if (!t2.ok || !((t2.bitmap >> i2) & 1ull)) {
-          kind = kBadRow;
+          kind = kRowBad;
         } else {
           orec = (uint32_t)(t2.rec - sg);
           onum = t2.nout;
           oofs = orec + t2.off_opos;
           if (t2.mode == 0) {
-            kind = kRawRef;
+            kind = kRowRawRef;
             u = i2;
           } else {
             u = (uint32_t)__popcll(t2.bitmap & ((1ull << i2) - 1ull));
-            uint32_t run = (orec + t2.off_pl) / 8 + sum_bytes(t2.rec + 16, u * C);
+            uint32_t at = (orec + t2.off_pl) / 8 + sum_bytes(t2.rec + 16, u * C);
 #pragma unroll
             for (uint32_t j = 0; j < C; j++) {
               const uint32_t w = t2.rec[16 + u * C + j];
-              bw[j] = (uint8_t)w;
-              bo[j] = run;
-              run += w;
-              if (w > 12 || (uint64_t)run > seg_words) kind = kBadRow;
+              bw[j] = w;
+              bo[j] = at;
+              at += w;
+              if (w > 12 || (uint64_t)at > seg_words) kind = kRowBad;
             }
-            if (u >= t2.U) kind = kBadRow;
           }
         }
       }
     }
-    s_kind[i] = kind;
-    s_orec[i] = orec;
-    s_ou[i] = u;
-    s_onum[i] = onum;
-    s_oofs[i] = oofs;
-    if (kind == kPlanes) {
-      if (local) {
+    if (kind == kRowPlanes && local) {
 #pragma unroll
-        for (uint32_t j = 0; j < C; j++) {
-          s_bw[i][j] = s_width[u * C + j];
-          s_bo[i][j] = pl_word0 + s_boff[u * C + j];
-        }
-      } else {
-#pragma unroll
-        for (uint32_t j = 0; j < C; j++) {
-          s_bw[i][j] = bw[j];
-          s_bo[i][j] = bo[j];
-        }
+      for (uint32_t j = 0; j < C; j++) {
+        bw[j] = s_width[u * C + j];
+        bo[j] = pl_word0 + s_boff[u * C + j];
       }
     }
+    const uint64_t ri = (uint64_t)ticket * kTileRows + i;
+    // the outliers of this row's first occurrence: positions [u*D, u*D + D)
+    // of the sorted list of its record (values follow all onum positions)
+    uint32_t ocnt = 0, ofirst = oofs;
+    if (kind == kRowPlanes && onum) {
+      const uint32_t* op = reinterpret_cast<const uint32_t*>(sg + oofs);
+      uint32_t lo = 0, hi2 = onum;
+      while (lo < hi2) {
+        const uint32_t mid = (lo + hi2) >> 1;
+        if (op[mid] < u * D) lo = mid + 1;
+        else hi2 = mid;
+      }
+      uint32_t e = lo;
+      while (e < onum && op[e] < u * D + D) e++;
+      ocnt = e - lo;
+      ofirst = oofs + 4 * lo;
+    }
+    // x: the kind (| kRowOutliers when the row has outliers); y: first-occurrence
+    // index; z: the row's outliers | its record's outliers << 16; w: offset of
+    // the row's first outlier position (RAW copy rows: of the record)
+    reinterpret_cast<uint4*>(a.dec_row)[ri] = make_uint4(
+        kind | (ocnt ? kRowOutliers : 0u), u, ocnt | (onum << 16), kind == kRowRawRef ? orec : ofirst);
+#pragma unroll
+    for (uint32_t j = 0; j < C; j++) a.dec_blk[ri * C + j] = (bo[j] << 4) | bw[j];
   }
-  __syncthreads();
+}
 
-  // segments the encoder writes are below 2^31 bytes, so byte offsets into
-  // one fit the 32-bit buffer range
-  const bool tile_bad = sh.bad != 0 || sbytes >= (1ull << 31);
-  const XposeSel xsel = xpose_sel(lane);
-  const __amdgpu_buffer_rsrc_t rseg = buf_rsrc(sg, tile_bad ? 0u : (uint32_t)sbytes);
+// Rows of one decode step (row i0, and i0 + 1 when C = 1) that need more than
+// the transposed planes: outliers to patch, a first occurrence stored RAW
+// (re-quantized), or a corrupt reference (zeros, reported).  v holds the
+// transposed values when all_planes.  Rare, so kept out of line.
+template <int C>
+__device__ __forceinline__ void decode_rows_special(
+    const DecArgs& a, const uint8_t* sg, float* yt, uint32_t i0, uint32_t n, bool all_planes,
+    float v0, float v1, float v2, float v3, float eb, float s2, const uint4* drow,
+    const uint32_t* dblk) {
+  const float v[4] = {v0, v1, v2, v3};
+  constexpr uint32_t D = 64u * C;
+  constexpr uint32_t kRowsPerStep = C == 1 ? 2 : 1;
+  const uint32_t lane = threadIdx.x & 63;
+  bool ok = true;
+  for (uint32_t rr = 0; rr < kRowsPerStep; rr++) {
+    const uint32_t ir = i0 + rr;
+    if (ir >= n) continue;
+    uint4 ri = drow[ir];  // kind, first-occurrence index, outliers, offset
+    ri.x &= 0xFFu;
+    float vr[C];
+#pragma unroll
+    for (uint32_t j = 0; j < C; j++) vr[j] = all_planes ? v[C == 1 ? rr : j] : 0.0f;
+    bool okr = ri.x != kRowBad;
+    if (ri.x == kRowPlanes && !all_planes) {
+      // a plane row next to a RAW-copy row (C = 1 pairs): decode it alone
+#pragma unroll
+      for (uint32_t j = 0; j < C; j++) {
+        const uint32_t dsc = dblk[ir * C + j], w = dsc & 15u, o = dsc >> 4;
+        uint32_t zz = 0;
+        for (uint32_t b = 0; b < w; b++) {
+          const uint64_t wd = reinterpret_cast<const uint64_t*>(sg)[o + b];
+          zz |= (uint32_t)((wd >> lane) & 1ull) << b;
+        }
+        vr[j] = (float)unzigzag(zz) * s2;
+      }
+    }
+    if (ri.x == kRowPlanes && (ri.z & 0xFFFFu)) {  // the row's outliers
+      const uint32_t* op = reinterpret_cast<const uint32_t*>(sg + ri.w);
+      patch_outliers<C>(vr, ri.y * D, op, op + (ri.z >> 16), ri.z & 0xFFFFu);
+    } else if (ri.x == kRowRawRef) {  // first occurrence stored RAW: re-quantize it
+      const float* src2 = reinterpret_cast<const float*>(sg + ri.w + 16) + (uint64_t)ri.y * D;
+#pragma unroll
+      for (uint32_t j = 0; j < C; j++) {
+        const float xv = src2[64 * j + lane];
+        int q;
+        vr[j] = quantize(xv, eb, s2, q) ? xv : (float)q * s2;
+      }
+    }
+    if (!okr) {
+#pragma unroll
+      for (uint32_t j = 0; j < C; j++) vr[j] = 0.0f;
+      ok = false;
+    }
+    float* y = yt + (uint64_t)ir * D;
+#pragma unroll
+    for (uint32_t j = 0; j < C; j++) y[64 * j + lane] = vr[j];
+  }
+  if (!__all(ok) && lane == 0) report_error(a.report, kDevErrCorrupt);
+}
+
+template <int C>
+__global__ void __launch_bounds__(kThreads) ec_decode_fast(const uint8_t* __restrict__ in,
+                                                          float* __restrict__ yout, DecArgs a) {
+  constexpr uint32_t D = 64u * C;
+  constexpr uint32_t kRowsPerWave = kTileRows / (kThreads / 64);  // 16
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const uint32_t ticket = blockIdx.x;
+  const uint32_t T = a.sh.T, B = a.sh.B;
+  // tile coordinates (from the plan, not the stream)
+  const uint32_t s = find_segment(a.seg_tile_base, a.sh.nseg, ticket);
+  const uint32_t pch = s / T, t = s % T, k = ticket - a.seg_tile_base[s];
+  const uint32_t rows = chunk_row0(a.sh, pch + 1) - chunk_row0(a.sh, pch);
+  const uint32_t n = rows ? min(kTileRows, rows - k * kTileRows) : 0u;
+  if (n == 0) return;
+  float* yt = yout + ((uint64_t)t * B + chunk_row0(a.sh, pch) + (uint64_t)k * kTileRows) * D;
+  const uint4* dt = reinterpret_cast<const uint4*>(a.dec_tile) + 2 * ticket;
   const uint32_t plane = lane & 15u, half = lane >> 5, hi = (lane >> 4) & 1u;
   const uint32_t rbeg = wv * kRowsPerWave;
   constexpr uint32_t kRowsPerStep = C == 1 ? 2 : 1;  // C = 1: blocks of two rows pair up
   constexpr uint32_t kSteps = kRowsPerWave / kRowsPerStep;
   constexpr uint32_t kM = (C + 1) / 2;  // plane registers per step
-  // all plane words of the wave's rows are requested before any is used
-  uint32_t word[kSteps][kM];
+  const uint4* drow = reinterpret_cast<const uint4*>(a.dec_row) + (uint64_t)ticket * kTileRows;
+  const uint32_t* dblk = a.dec_blk + (uint64_t)ticket * kTileRows * C;
+  // round 1: the tile descriptor and those of the lane's rows and blocks
+  // together (kind[]: the row kind, with kRowOutliers when there are outliers
+  // to patch; garbage for a raw or failed tile, and then unused)
+  uint32_t kind[kSteps], desc[kSteps][kM];
 #pragma unroll
   for (uint32_t st = 0; st < kSteps; st++) {
-    const uint32_t i = rbeg + st * kRowsPerStep + (C == 1 ? hi : 0u);
-    const bool use = i < n && s_kind[i] == kPlanes;
+    const uint32_t i = min(rbeg + st * kRowsPerStep + (C == 1 ? hi : 0u), n - 1);  // past n: a copy
+    kind[st] = drow[i].x;
+#pragma unroll
+    for (uint32_t m = 0; m < kM; m++) desc[st][m] = dblk[i * C + (C == 1 ? 0u : 2 * m + hi)];
+  }
+  const uint4 d0 = dt[0], d1 = dt[1];
+  const uint32_t flags = d0.x;
+  if (!(flags & kTileOk)) {  // the index pass reported it
+    for (uint32_t i = tid; i < n * D; i += kThreads) yt[i] = 0.0f;
+    return;
+  }
+  const uint8_t* sg = in + (((uint64_t)d0.w << 32) | d0.z);
+  if (flags & kTileRaw) {  // RAW: rows verbatim
+    const uint8_t* rec = in + (((uint64_t)d1.y << 32) | d1.x);
+    const float4* s4 = reinterpret_cast<const float4*>(rec + 16);
+    float4* y4 = reinterpret_cast<float4*>(yt);
+    for (uint32_t i = tid; i < n * D / 4; i += kThreads) y4[i] = s4[i];
+    return;
+  }
+  const float eb = __uint_as_float(d0.y), s2 = eb + eb;
+  const __amdgpu_buffer_rsrc_t rseg = buf_rsrc(sg, d1.z);
+  const __amdgpu_buffer_rsrc_t ry = buf_rsrc(yt, n * D * 4);
+  const XposeSel xsel = xpose_sel(lane);
+  // round 2: every plane word of the wave's rows
+  uint32_t word[kSteps][kM];
+#pragma unroll
+  for (uint32_t st = 0; st < kSteps; st++)
 #pragma unroll
     for (uint32_t m = 0; m < kM; m++) {
-      const uint32_t j = C == 1 ? 0u : 2 * m + hi;
-      const bool on = use && plane < s_bw[i][j];
-      word[st][m] = buf_ld_u32(rseg, on ? (2 * (s_bo[i][j] + plane) + half) * 4 : kOff);
+      const uint32_t w = desc[st][m] & 15u, o = desc[st][m] >> 4;
+      const bool on = (kind[st] & 0xFFu) == kRowPlanes && plane < w;
+      word[st][m] = buf_ld_u32(rseg, on ? (2 * (o + plane) + half) * 4 : kOff);
     }
-  }
+  uint32_t special = 0;  // steps with RAW copies or corrupt rows: done last
+  uint32_t patch = 0;    // steps with outliers: their raw values are stored last
 #pragma unroll
   for (uint32_t st = 0; st < kSteps; st++) {
     const uint32_t i0 = rbeg + st * kRowsPerStep;
-    if (i0 >= n) break;
-    // the lane's row (C = 1: row i0 + hi) and its kind
-    const uint32_t i = i0 + (C == 1 ? hi : 0u);
-    const bool live = i < n;
-    const uint32_t kind = live ? s_kind[i] : kPlanes;
-    const bool all_planes = __all(kind == kPlanes) && !tile_bad;
-    float v[2 * kM];
-    bool ok = true;
+    if (i0 < n) {  // (no early exit: the loop must unroll to keep word[] in registers)
+      if (__all((kind[st] & 0xFFu) == kRowPlanes)) {
+        if (__any(kind[st] & kRowOutliers)) patch |= 1u << st;
+        float v[2 * kM];
+#pragma unroll
+        for (uint32_t m = 0; m < kM; m++) {
+          const uint32_t zz2 = xpose32(word[st][m], xsel);
+          int qa, qb;
+          unzigzag_pair(zz2, qa, qb);
+          v[2 * m] = (float)qa * s2;
+          v[2 * m + 1] = (float)qb * s2;
+        }
+#pragma unroll
+        for (uint32_t rr = 0; rr < kRowsPerStep; rr++)
+#pragma unroll
+          for (uint32_t j = 0; j < C; j++)  // rows past n fall outside ry's range
+            __builtin_amdgcn_raw_buffer_store_b32(f2u(v[C == 1 ? rr : j]), ry, 4 * lane,
+                                                  ((i0 + rr) * D + 64 * j) * 4, 0);
+      } else {
+        special |= 1u << st;
+      }
+    }
+  }
+  // outliers: the raw values over the stored codes (same wave, after its
+  // stores are performed)
+  if (patch) {
+    wait_vm();
+    for (uint32_t st = 0; st < kSteps; st++) {
+      if (!((patch >> st) & 1u)) continue;
+      for (uint32_t rr = 0; rr < kRowsPerStep; rr++) {
+        const uint32_t ir = rbeg + st * kRowsPerStep + rr;
+        if (ir >= n) continue;
+        const uint4 ri = drow[ir];
+        const uint32_t cnt = ri.z & 0xFFFFu;
+        if (!(ri.x & kRowOutliers) || cnt == 0) continue;
+        const uint32_t* op = reinterpret_cast<const uint32_t*>(sg + ri.w);
+        const uint32_t* ov = op + (ri.z >> 16);
+        for (uint32_t q = lane; q < cnt; q += 64) {
+          const uint32_t d = op[q] - ri.y * D;  // element within the row
+          if (d < D) yt[(uint64_t)ir * D + d] = __uint_as_float(ov[q]);
+        }
+      }
+    }
+  }
+  // the rare steps, once the plane registers are free: reload and decode again
+  for (uint32_t st = 0; st < kSteps; st++) {
+    if (!((special >> st) & 1u)) continue;
+    const uint32_t i0 = rbeg + st * kRowsPerStep;
+    const uint32_t i = min(i0 + (C == 1 ? hi : 0u), n - 1);
+    const uint32_t kd = drow[i].x & 0xFFu;
+    const bool all_planes = __all(kd == kRowPlanes);
+    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     if (all_planes) {
 #pragma unroll
       for (uint32_t m = 0; m < kM; m++) {
-        const uint32_t zz2 = xpose32(word[st][m], xsel);
+        const uint32_t dsc = dblk[i * C + (C == 1 ? 0u : 2 * m + hi)];
+        const uint32_t w = dsc & 15u, o = dsc >> 4;
+        const uint32_t wd = buf_ld_u32(rseg, plane < w ? (2 * (o + plane) + half) * 4 : kOff);
         int qa, qb;
-        unzigzag_pair(zz2, qa, qb);
-        v[2 * m] = (float)qa * s2;
-        v[2 * m + 1] = (float)qb * s2;
-      }
-      // outliers of the first occurrence each output row copies
-#pragma unroll
-      for (uint32_t rr = 0; rr < kRowsPerStep; rr++) {
-        const uint32_t ir = i0 + rr;
-        if (ir >= n) continue;
-        const uint32_t on = s_onum[ir];
-        if (on == 0) continue;
-        float vr[C];
-#pragma unroll
-        for (uint32_t j = 0; j < C; j++) vr[j] = v[C == 1 ? rr : j];
-        const uint32_t u = s_ou[ir];
-        if (s_orec[ir] == rec_in_seg && stage_out) {
-          patch_outliers<C>(vr, u * D, (const uint32_t*)s_opos, (const uint32_t*)s_oval, on);
-        } else {
-          const uint32_t* op = reinterpret_cast<const uint32_t*>(sg + s_oofs[ir]);
-          patch_outliers<C>(vr, u * D, op, op + on, on);
-        }
-#pragma unroll
-        for (uint32_t j = 0; j < C; j++) v[C == 1 ? rr : j] = vr[j];
-      }
-    } else {
-      // rows that copy a RAW-stored first occurrence, or a corrupt tile
-#pragma unroll
-      for (uint32_t rr = 0; rr < kRowsPerStep; rr++) {
-        const uint32_t ir = i0 + rr;
-        const uint32_t kr = ir < n ? s_kind[ir] : kPlanes;
-        bool okr = !tile_bad && kr != kBadRow;
-        float vr[C];
-        if (okr && kr == kRawRef) {
-          const float* src2 = reinterpret_cast<const float*>(sg + s_orec[ir] + 16) + (uint64_t)s_ou[ir] * D;
-#pragma unroll
-          for (uint32_t j = 0; j < C; j++) {
-            const float xv = src2[64 * j + lane];
-            int q;
-            vr[j] = quantize(xv, eb, s2, q) ? xv : (float)q * s2;
-          }
-        } else if (okr && ir < n) {
-          // a plane row next to a RAW-copy row (C = 1 pairs): decode it alone
-#pragma unroll
-          for (uint32_t j = 0; j < C; j++) {
-            const uint32_t w = s_bw[ir][j], o = s_bo[ir][j];
-            uint32_t zz = 0;
-            for (uint32_t b = 0; b < w; b++) {
-              const uint64_t wd = reinterpret_cast<const uint64_t*>(sg)[o + b];
-              zz |= (uint32_t)((wd >> lane) & 1ull) << b;
-            }
-            vr[j] = (float)unzigzag(zz) * s2;
-          }
-          const uint32_t on = s_onum[ir];
-          if (on) {
-            const uint32_t* op = reinterpret_cast<const uint32_t*>(sg + s_oofs[ir]);
-            patch_outliers<C>(vr, s_ou[ir] * D, op, op + on, on);
-          }
-        } else {
-#pragma unroll
-          for (uint32_t j = 0; j < C; j++) vr[j] = 0.0f;
-        }
-        okr = __all(okr || ir >= n);
-#pragma unroll
-        for (uint32_t j = 0; j < C; j++) v[C == 1 ? rr : j] = okr ? vr[j] : 0.0f;
-        if (!okr) ok = false;
+        unzigzag_pair(xpose32(wd, xsel), qa, qb);
+        v[(2 * m) & 3] = (float)qa * s2;
+        v[(2 * m + 1) & 3] = (float)qb * s2;
       }
     }
-    if (!ok && lane == 0) report_error(a.report, kDevErrCorrupt);
-    // stores: C = 1 -> rows i0, i0 + 1; else the C blocks of row i0
-#pragma unroll
-    for (uint32_t rr = 0; rr < kRowsPerStep; rr++) {
-      if (i0 + rr >= n) continue;
-      float* y = yt + (uint64_t)(i0 + rr) * D;
-#pragma unroll
-      for (uint32_t j = 0; j < C; j++) y[64 * j + lane] = v[C == 1 ? rr : j];
-    }
+    decode_rows_special<C>(a, sg, yt, i0, n, all_planes, v[0], v[1], v[2], v[3], eb, s2, drow, dblk);
   }
 }
 
@@ -2591,6 +2696,26 @@ hipError_t launch_assemble(const EncArgs& a, hipStream_t s) {
     case 256:
       hipLaunchKernelGGL(ec_size_fast<4>, blocks, sblock, 0, s, a);
       hipLaunchKernelGGL(ec_write_fast<4>, tiles, block, 0, s, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+bool decode_has_index(uint32_t D) { return D == 64 || D == 128 || D == 256; }
+
+hipError_t launch_decode_index(const DecArgs& a, hipStream_t s) {
+  const dim3 grid(a.sh.ntiles), block(64);
+  switch (a.sh.D) {
+    case 64:
+      hipLaunchKernelGGL(ec_dec_index<1>, grid, block, 0, s, a.in, a);
+      break;
+    case 128:
+      hipLaunchKernelGGL(ec_dec_index<2>, grid, block, 0, s, a.in, a);
+      break;
+    case 256:
+      hipLaunchKernelGGL(ec_dec_index<4>, grid, block, 0, s, a.in, a);
       break;
     default:
       return hipErrorInvalidValue;
