@@ -110,10 +110,11 @@ def _read_counter_csvs(d: str):
 
 
 def summarize_counters(d: str, workload: str, copy_bytes: int, command: str):
-    """HBM traffic per launch of each path kernel from four rocprofv3 --pmc runs
-    (FETCH_SIZE and WRITE_SIZE of the workload, and of a plain copy of known
-    size): each counter is scaled by bytes-moved / counter-reading of the copy.
-    Writes profiles/<kernel>_<workload>_counters.json."""
+    """HBM traffic per launch of each pass of the path from four rocprofv3 --pmc
+    runs (FETCH_SIZE and WRITE_SIZE of the workload, and of a plain copy of
+    known size): each counter is scaled by bytes-moved / counter-reading of the
+    copy; a pass of several kernels sums their per-dispatch averages.  Writes
+    profiles/<pass>_<workload>_counters.json."""
     wf = _read_counter_csvs(os.path.join(d, f"pmc_{workload}_fetch"))
     ww = _read_counter_csvs(os.path.join(d, f"pmc_{workload}_write"))
     cf = _read_counter_csvs(os.path.join(d, "pmc_copy_fetch"))
@@ -124,24 +125,30 @@ def summarize_counters(d: str, workload: str, copy_bytes: int, command: str):
         vals = sorted(vals)[len(vals) // 4:]  # drop warm-up outliers, keep the bulk
         return sum(vals) / len(vals)
 
+    def mean(xs):
+        return sum(xs) / len(xs)
+
     f_kib, w_kib = copy_kib(cf, "FETCH_SIZE"), copy_kib(cw, "WRITE_SIZE")
     f_scale = copy_bytes / (f_kib * 1024.0)
     w_scale = copy_bytes / (w_kib * 1024.0)
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     for kern, prefix in KERNEL_PREFIX.items():
-        fk = [v for k, cs in wf.items() if k.startswith(prefix) for v in cs.get("FETCH_SIZE", [])]
-        wk = [v for k, cs in ww.items() if k.startswith(prefix) for v in cs.get("WRITE_SIZE", [])]
-        if not fk or not wk:
-            continue
         names = sorted({k for k in list(wf) + list(ww) if k.startswith(prefix)})
-        fetch = sum(fk) / len(fk)
-        write = sum(wk) / len(wk)
+        per = {}
+        for nm in names:
+            fk, wk = wf.get(nm, {}).get("FETCH_SIZE", []), ww.get(nm, {}).get("WRITE_SIZE", [])
+            if fk and wk:
+                per[nm] = {"dispatches": [len(fk), len(wk)], "fetch_kib": round(mean(fk), 1),
+                           "write_kib": round(mean(wk), 1)}
+        if not per:
+            continue
+        fetch = sum(v["fetch_kib"] for v in per.values())
+        write = sum(v["write_kib"] for v in per.values())
         rec = {
-            "kernel": kern, "kernel_names": names, "workload": workload,
+            "pass": kern, "kernels": per, "workload": workload,
             "source_hash": kernel_source_hash(),
-            "dispatches": {"fetch_run": len(fk), "write_run": len(wk)},
-            "fetch_kib_per_dispatch": round(fetch, 1),
-            "write_kib_per_dispatch": round(write, 1),
+            "fetch_kib_per_launch": round(fetch, 1),
+            "write_kib_per_launch": round(write, 1),
             "copy_calibration": {
                 "kernel": "torch.neg over a float32 buffer (reads and writes copy_bytes each)",
                 "copy_bytes": copy_bytes, "fetch_kib": round(f_kib, 1), "write_kib": round(w_kib, 1),
