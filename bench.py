@@ -318,16 +318,21 @@ def main():
     tc = (t_prep + t_enc + t_asm) / args.steps * 1e-3  # kernel time only
     td = (t_dec + t_dix) / args.steps * 1e-3
     step_s = ms / args.steps * 1e-3
-    bytes_c = 4 * N * (2 if rel else 1) + S
+    # the round trip's minimum HBM traffic: read x, write the stream, read it,
+    # write y (a second read of x for the range is not counted)
+    bytes_c = 4 * N + S
     bytes_d = S + 4 * N
-    # algorithmic bytes per launch: the input read by the range pass (REL) and
-    # by the quantize pass, the stream written by assembly (by the one encode
-    # kernel when there is no assembly pass), and both for decode
+    # algorithmic bytes per launch: the input read by the range pass (REL, when
+    # it is a kernel of its own) and by the quantize pass (which also computes
+    # the range when there is no range pass: its second read of a tile is not
+    # counted), the stream written by assembly (by the one encode kernel when
+    # there is no assembly pass), and both for decode
     kernels = {
-        "prep": (t_prep / max(n_prep, 1), 4 * N if rel else 0),
         "encode": (t_enc / max(n_enc, 1), 4 * N + (0 if n_asm else S)),
         "decode": (t_dec / max(n_dec, 1), S + 4 * N),
     }
+    if n_prep:
+        kernels["prep"] = (t_prep / n_prep, 4 * N if rel else 0)
     if n_asm:
         kernels["assemble"] = (t_asm / n_asm, S)
     if n_dix:  # reads record headers and widths only: no algorithmic bytes

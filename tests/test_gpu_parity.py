@@ -286,3 +286,32 @@ def test_workloads_full_size_sampled_tables(name):
     err = (xg.double() - y.double()).abs()
     assert bool((err[fin] <= ebs.expand_as(xg).double()[fin]).all())
     say(f"[workload] {name} CR={cr:.3f}")
+
+
+@pytest.mark.parametrize("T,B,D,mode", [(3, 1000, 128, 1), (2, 8192, 64, 1), (5, 4096, 64, 1),
+                                        (3, 16448, 64, 1), (9, 2100, 256, 1), (2, 1000, 128, 0)])
+def test_plan_reused_across_calls(T, B, D, mode):
+    """One plan, consecutive calls on the same stream whose value ranges and
+    duplicate structure change: every call must match the oracle (nothing of
+    an earlier call's range partials or hash tables may leak into a later one).
+    Shapes from 48 to 771 tiles, one to 257 tiles per table."""
+    say(f"[reuse] T={T} B={B} D={D} mode={mode}")
+    rng = np.random.default_rng(B + D + T)
+    cfg = make_cfg(T, B, D, eb_mode=mode, eb=(0.01,))
+    plan = ec.Plan(T, B, D, 1, mode, 0.01)
+    out = plan.empty_stream()
+    for call, (scale, fu) in enumerate([(1.0, 0.4), (100.0, 0.05), (0.01, 0.9), (3.0, 0.4)]):
+        x = dup_rows(rng, T, B, D, scale=scale, frac_unique=fu)
+        if call == 2:
+            x[0, 5, 3] = np.nan  # NaN is excluded from the range
+        plan.compress(torch.from_numpy(x).cuda(), out, call)
+        _, nbytes, _, _ = plan.ratio(per_segment=True)
+        ref = O.compress(cfg, call, x, debug=False)
+        got = out[:nbytes].cpu().numpy()
+        assert got.size == ref.stream.size, (call, got.size, ref.stream.size)
+        assert np.array_equal(got, ref.stream), f"call {call}"
+        y = torch.empty(T, B, D, device="cuda")
+        plan.decompress(out[:nbytes], y)
+        plan.ratio()
+        yo = O.decompress(cfg, ref.stream)
+        np.testing.assert_array_equal(y.cpu().numpy().view(np.uint32), yo.view(np.uint32))
