@@ -52,8 +52,8 @@ struct Work {
   uint64_t* chunk_start;         // [P] absolute offset + 1
   uint32_t* seg_fin;             // [nseg] segment header written
   uint64_t* tile_status;         // [ntiles] the tile's stream item (+ 1 once known, one-pass encoder)
-  uint64_t* block_status;        // [ceil(ntiles/64)] one-pass encoder: (flag << 62) | sum or
-                                 // inclusive prefix; size pass: the block's item sum
+  uint64_t* block_status;        // [ntiles] one-pass encoder, per 64 tiles: (flag << 62) | sum or
+                                 // inclusive prefix; size pass, per size workgroup: its item sum
   uint32_t* tile_inserted;       // [ntiles] rows inserted into the hash table
   uint64_t* tile_rec;            // [ntiles] absolute record offset + 1 (record written)
   uint32_t* tile_U;              // [ntiles] first occurrences in the tile
@@ -70,7 +70,7 @@ struct Work {
   uint32_t* tile_info;           // [ntiles][4] U, n_out, plane words, mode | valid << 8
   uint64_t* tile_bitmap;         // [ntiles] first-occurrence rows
   uint32_t* tile_first;          // [ntiles][64] first occurrence of each row
-  uint32_t* seg_eb;              // [nseg] stored error bound bits (0: raw segment)
+  uint32_t* seg_eb;              // [nseg] stored error bound bits (0: raw segment), from quantize
 };
 
 struct PrepArgs {

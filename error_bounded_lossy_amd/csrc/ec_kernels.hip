@@ -1170,6 +1170,7 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
       sh.eb = e;
       sh.valid = v;
       if (a.dbg_eb && k == 0) a.dbg_eb[s] = v ? e : 0.0f;
+      if (k == 0) a.w.seg_eb[s] = v ? f2u(e) : 0u;  // 0: raw segment
     }
   }
   __syncthreads();
@@ -1419,15 +1420,19 @@ __device__ __forceinline__ uint64_t seg_prefix_bytes(uint32_t ntiles) { return 3
 
 // Size pass: one workgroup per block of 64 tiles, four tiles per wave (their
 // loads are issued together); the block's item sum is stored once.
-constexpr uint32_t kSizeThreads = 1024;
-constexpr uint32_t kTilesPerWave = kTileRows / (kSizeThreads / 64);  // 4
+#ifndef EC_SIZE_Q
+#define EC_SIZE_Q 2
+#endif
+constexpr uint32_t kSizeThreads = 256;
+constexpr uint32_t kTilesPerWave = EC_SIZE_Q;
+constexpr uint32_t kBlockTiles = kTilesPerWave * (kSizeThreads / 64);  // tiles per size workgroup
 template <int C>
 __global__ void __launch_bounds__(kSizeThreads) ec_size_fast(EncArgs a) {
   constexpr uint32_t D = 64u * C;
   constexpr uint32_t Q = kTilesPerWave;
   __shared__ uint64_t s_sum[kSizeThreads / 64];
   const uint32_t lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const uint32_t t0 = blockIdx.x * kTileRows + wv * Q;
+  const uint32_t t0 = blockIdx.x * kBlockTiles + wv * Q;
   TileCoord c[Q];
   uint32_t slot[Q];
   uint8_t wb[Q][C];
@@ -1441,17 +1446,10 @@ __global__ void __launch_bounds__(kSizeThreads) ec_size_fast(EncArgs a) {
 #pragma unroll
     for (uint32_t j = 0; j < C; j++) wb[q][j] = a.w.stage_w[rowi * C + j];
   }
+  // the segment's error bound, stored by its first quantize tile (0: raw)
   bool valid[Q];
-  float eb[Q];
 #pragma unroll
-  for (uint32_t q = 0; q < Q; q++) {
-    if (q > 0 && c[q].t == c[q - 1].t) {
-      valid[q] = valid[q - 1];
-      eb[q] = eb[q - 1];
-    } else {
-      eb[q] = table_eb(a, c[q].t, valid[q]);
-    }
-  }
+  for (uint32_t q = 0; q < Q; q++) valid[q] = a.w.seg_eb[c[q].s] != 0u;
   uint32_t first[Q];
 #pragma unroll
   for (uint32_t q = 0; q < Q; q++) {
@@ -1498,7 +1496,6 @@ __global__ void __launch_bounds__(kSizeThreads) ec_size_fast(EncArgs a) {
       info.w = L.mode | (valid[q] ? 0x100u : 0u);
       reinterpret_cast<uint4*>(a.w.tile_info)[ticket] = info;
       a.w.tile_bitmap[ticket] = bm;
-      if (cq.k == 0) a.w.seg_eb[cq.s] = valid[q] ? f2u(eb[q]) : 0u;
     }
   }
   if (lane == 0) s_sum[wv] = items;
@@ -1511,11 +1508,12 @@ __global__ void __launch_bounds__(kSizeThreads) ec_size_fast(EncArgs a) {
 }
 
 // Stream bytes before tile j (its item included for no earlier tile), whole
-// wave: the sums of the 64-tile blocks before j's block plus the items of the
-// tiles before j in its block, lane-parallel.
+// wave: the sums of the size workgroups' blocks before j's block plus the
+// items of the tiles before j in its block, lane-parallel.
 __device__ __forceinline__ uint64_t tiles_before(const EncArgs& a, uint32_t j) {
-  const uint32_t lane = threadIdx.x & 63, blk = j >> 6;
-  uint64_t v = lane < (j & 63u) ? a.w.tile_status[(blk << 6) + lane] : 0;
+  static_assert(kBlockTiles <= 64, "one lane per tile of a block");
+  const uint32_t lane = threadIdx.x & 63, blk = j / kBlockTiles, in = j - blk * kBlockTiles;
+  uint64_t v = lane < in ? a.w.tile_status[blk * kBlockTiles + lane] : 0;
   for (uint32_t b = lane; b < blk; b += 64) v += a.w.block_status[b];
   return wave_sum_u64(v);
 }
@@ -2682,7 +2680,7 @@ hipError_t launch_encode(const EncArgs& a, hipStream_t s) {
 bool encode_has_assembly(uint32_t D) { return D == 64 || D == 128 || D == 256; }
 
 hipError_t launch_assemble(const EncArgs& a, hipStream_t s) {
-  const dim3 tiles(a.sh.ntiles), blocks((a.sh.ntiles + kTileRows - 1) / kTileRows);
+  const dim3 tiles(a.sh.ntiles), blocks((a.sh.ntiles + kBlockTiles - 1) / kBlockTiles);
   const dim3 block(kThreads), sblock(kSizeThreads);
   switch (a.sh.D) {
     case 64:

@@ -155,7 +155,7 @@ ec_status make_layout(const ec_plan_desc* d, Layout* L) {
   L->chunk_start = take(8ull * P);
   L->seg_fin = take(4ull * nseg);
   L->tile_status = take(8ull * tiles);
-  L->block_status = take(8ull * ((tiles + 63) / 64));
+  L->block_status = take(8ull * tiles);  // one per block of at least one tile
   L->tile_inserted = take(4ull * tiles);
   L->tile_rec = take(8ull * tiles);
   L->tile_U = take(4ull * tiles);
