@@ -988,6 +988,8 @@ __device__ __forceinline__ uint32_t xpose32(uint32_t v, const XposeSel& s) {
 // dropped, which predicates them without branches.
 constexpr uint32_t kOff = 0x80000000u;  // an offset past every range
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+// cache-policy operand of buffer stores: non-temporal (streaming) access
+constexpr int kCacheStream = 2;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
@@ -2507,7 +2509,7 @@ __device__ __forceinline__ void decode_rows_special(
     }
     float* y = yt + (uint64_t)ir * D;
 #pragma unroll
-    for (uint32_t j = 0; j < C; j++) y[64 * j + lane] = vr[j];
+    for (uint32_t j = 0; j < C; j++) __builtin_nontemporal_store(vr[j], &y[64 * j + lane]);
   }
   if (!__all(ok) && lane == 0) report_error(a.report, kDevErrCorrupt);
 }
@@ -2591,12 +2593,15 @@ __global__ void __launch_bounds__(kThreads) ec_decode_fast(const uint8_t* __rest
           v[2 * m] = (float)qa * s2;
           v[2 * m + 1] = (float)qb * s2;
         }
+        // rows past n fall outside ry's range; streaming stores (the output is
+        // not read again here, and dirty lines left in the caches would be
+        // written back while the next pass reads its input)
 #pragma unroll
         for (uint32_t rr = 0; rr < kRowsPerStep; rr++)
 #pragma unroll
-          for (uint32_t j = 0; j < C; j++)  // rows past n fall outside ry's range
+          for (uint32_t j = 0; j < C; j++)
             __builtin_amdgcn_raw_buffer_store_b32(f2u(v[C == 1 ? rr : j]), ry, 4 * lane,
-                                                  ((i0 + rr) * D + 64 * j) * 4, 0);
+                                                  ((i0 + rr) * D + 64 * j) * 4, kCacheStream);
       } else {
         special |= 1u << st;
       }
