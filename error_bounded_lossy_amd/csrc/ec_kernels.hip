@@ -147,6 +147,19 @@ __device__ __forceinline__ uint32_t find_segment(const uint32_t* base, uint32_t 
   return lo;
 }
 
+// Segment s and tile k of scheduled tile `ticket`: by division when every
+// segment has the same number of tiles, else by search.
+__device__ __forceinline__ void ticket_coords(const Shape& sh, const uint32_t* seg_tile_base,
+                                              uint32_t ticket, uint32_t& s, uint32_t& k) {
+  if (sh.tiles_per_seg) {
+    s = ticket / sh.tiles_per_seg;
+    k = ticket - s * sh.tiles_per_seg;
+  } else {
+    s = find_segment(seg_tile_base, sh.nseg, ticket);
+    k = ticket - seg_tile_base[s];
+  }
+}
+
 __device__ __forceinline__ uint32_t chunk_row0(const Shape& sh, uint32_t p) {
   return (uint32_t)((uint64_t)p * sh.B / sh.P);
 }
@@ -1570,8 +1583,11 @@ __device__ void write_stream_tables(const EncArgs& a, const TileCoord& c, uint32
   }
 }
 
+// D <= 128: eight waves per SIMD, at most 64 VGPRs (the kernel waits on memory,
+// not ALUs; D = 256 would spill)
 template <int C>
-__global__ void __launch_bounds__(kThreads) ec_write_fast(EncArgs a) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C < 4 ? 8 : 1)))
+ec_write_fast(EncArgs a) {
   constexpr uint32_t D = 64u * C;
   __shared__ uint64_t s_omask[kTileRows][C];
   __shared__ uint32_t s_cbase[kTileRows][C];  // plane-word offset of each block in the record
@@ -2135,11 +2151,11 @@ __global__ void __launch_bounds__(kThreads) ec_decode_kernel(DecArgs a) {
 __device__ void dec_locate(const DecArgs& a, const uint8_t* in, uint32_t ticket, DecShared& sh,
                            uint64_t& rec_off) {
   const uint32_t T = a.sh.T, B = a.sh.B, D = a.sh.D, P = a.sh.P;
-  uint32_t s = find_segment(a.seg_tile_base, a.sh.nseg, ticket);
+  uint32_t s, k;
+  ticket_coords(a.sh, a.seg_tile_base, ticket, s, k);
   uint32_t pch = s / T, t = s % T;
   uint32_t r0 = chunk_row0(a.sh, pch), rows = chunk_row0(a.sh, pch + 1) - r0;
   uint32_t nt = (rows + kTileRows - 1) / kTileRows;
-  uint32_t k = ticket - a.seg_tile_base[s];
   sh.seg = s;
   sh.tile = k;
   sh.rows = rows;
@@ -2523,8 +2539,9 @@ __global__ void __launch_bounds__(kThreads) ec_decode_fast(const uint8_t* __rest
   const uint32_t ticket = blockIdx.x;
   const uint32_t T = a.sh.T, B = a.sh.B;
   // tile coordinates (from the plan, not the stream)
-  const uint32_t s = find_segment(a.seg_tile_base, a.sh.nseg, ticket);
-  const uint32_t pch = s / T, t = s % T, k = ticket - a.seg_tile_base[s];
+  uint32_t s, k;
+  ticket_coords(a.sh, a.seg_tile_base, ticket, s, k);
+  const uint32_t pch = s / T, t = s % T;
   const uint32_t rows = chunk_row0(a.sh, pch + 1) - chunk_row0(a.sh, pch);
   const uint32_t n = rows ? min(kTileRows, rows - k * kTileRows) : 0u;
   if (n == 0) return;
