@@ -105,6 +105,10 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
 //  * consume: loads of the data are issued only after a load of the flag has
 //    returned the published value (a spin loop or a barrier behind it).
 __device__ __forceinline__ void fence_wg() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup"); }
+// The wave's index in its workgroup, in a scalar register (the compiler does
+// not see that threadIdx.x >> 6 is uniform: wave-indexed offsets would become
+// per-lane values, and buffer offsets taken from them loops over lanes).
+__device__ __forceinline__ uint32_t wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // atomic minimum whose result is awaited (the wave stalls until it is performed)
 __device__ __forceinline__ void atomic_min_performed(uint64_t* p, uint64_t v) {
@@ -1152,7 +1156,7 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
   __shared__ EncShared sh;
   __shared__ uint32_t s_hash[kTileRows];
   __shared__ uint8_t s_oflag[kTileRows][C];
-  const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const uint32_t T = a.sh.T;
 
   if (tid == 0) take_tile(a, sh);
@@ -1446,7 +1450,7 @@ __global__ void __launch_bounds__(kSizeThreads) ec_size_fast(EncArgs a) {
   constexpr uint32_t D = 64u * C;
   constexpr uint32_t Q = kTilesPerWave;
   __shared__ uint64_t s_sum[kSizeThreads / 64];
-  const uint32_t lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const uint32_t lane = threadIdx.x & 63, wv = wave_id();
   const uint32_t t0 = blockIdx.x * kBlockTiles + wv * Q;
   TileCoord c[Q];
   uint32_t slot[Q];
@@ -1597,7 +1601,7 @@ ec_write_fast(EncArgs a) {
   __shared__ uint64_t s_rec_abs, s_seg_start, s_seg_end, s_chunk_start, s_total, s_bitmap;
   __shared__ uint32_t s_un[2];
   __shared__ uint4 s_info;
-  const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const uint32_t ticket = blockIdx.x;
   const TileCoord c = tile_coord(a, ticket);
   const uint32_t n = c.n;
@@ -2612,13 +2616,15 @@ __global__ void __launch_bounds__(kThreads) ec_decode_fast(const uint8_t* __rest
         }
         // rows past n fall outside ry's range; streaming stores (the output is
         // not read again here, and dirty lines left in the caches would be
-        // written back while the next pass reads its input)
+        // written back while the next pass reads its input); the row offset
+        // is wave-uniform and goes in the scalar offset
 #pragma unroll
         for (uint32_t rr = 0; rr < kRowsPerStep; rr++)
 #pragma unroll
           for (uint32_t j = 0; j < C; j++)
-            __builtin_amdgcn_raw_buffer_store_b32(f2u(v[C == 1 ? rr : j]), ry, 4 * lane,
-                                                  ((i0 + rr) * D + 64 * j) * 4, kCacheStream);
+            __builtin_amdgcn_raw_buffer_store_b32(
+                f2u(v[C == 1 ? rr : j]), ry, 4 * lane,
+                __builtin_amdgcn_readfirstlane(((i0 + rr) * D + 64 * j) * 4), kCacheStream);
       } else {
         special |= 1u << st;
       }
