@@ -84,8 +84,7 @@ def cpu_baseline(x_cpu, w, min_seconds: float):
 
 
 KERNEL_PREFIX = {"prep": "ec_prep", "encode": ("ec_encode", "ec_quantize"),
-                 "assemble": ("ec_size", "ec_write"), "decode_index": "ec_dec_index",
-                 "decode": ("ec_decode",)}
+                 "assemble": ("ec_size", "ec_write"), "decode": ("ec_decode",)}
 
 
 def _short_kernel(name: str) -> str:
@@ -306,7 +305,6 @@ def main():
     t_enc, n_enc = plan.profile_read(ec.KERNEL_ENCODE)
     t_dec, n_dec = plan.profile_read(ec.KERNEL_DECODE)
     t_asm, n_asm = plan.profile_read(ec.KERNEL_ASSEMBLE)
-    t_dix, n_dix = plan.profile_read(ec.KERNEL_DECODE_INDEX)
     plan.profile_enable(False)
     _, _, st = plan.ratio(raise_on_error=False)
     if st != 0:
@@ -316,7 +314,7 @@ def main():
     rel = w0.eb_mode == ec.EB_REL_RANGE
     S = mean_bytes
     tc = (t_prep + t_enc + t_asm) / args.steps * 1e-3  # kernel time only
-    td = (t_dec + t_dix) / args.steps * 1e-3
+    td = t_dec / args.steps * 1e-3
     step_s = ms / args.steps * 1e-3
     # the round trip's minimum HBM traffic: read x, write the stream, read it,
     # write y (a second read of x for the range is not counted)
@@ -335,8 +333,6 @@ def main():
         kernels["prep"] = (t_prep / n_prep, 4 * N if rel else 0)
     if n_asm:
         kernels["assemble"] = (t_asm / n_asm, S)
-    if n_dix:  # reads record headers and widths only: no algorithmic bytes
-        kernels["decode_index"] = (t_dix / n_dix, 0)
     dom = max(kernels, key=lambda k: kernels[k][0])
     dom_ms, dom_bytes = kernels[dom]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9

@@ -22,7 +22,7 @@ EC_ERR_DEVICE, EC_ERR_OOM, EC_ERR_UNSUPPORTED = 4, 5, 6
 EB_ABS, EB_REL_RANGE = 0, 1
 SCHED_NONE, SCHED_INV_SQRT, SCHED_STEP = 0, 1, 2
 CODER_BITPACK = 1
-KERNEL_PREP, KERNEL_ENCODE, KERNEL_DECODE, KERNEL_ASSEMBLE, KERNEL_DECODE_INDEX = 0, 1, 2, 3, 4
+KERNEL_PREP, KERNEL_ENCODE, KERNEL_DECODE, KERNEL_ASSEMBLE = 0, 1, 2, 3
 ABI_VERSION = 1
 
 

@@ -104,10 +104,6 @@ struct DecArgs {
   Shape sh;
   const uint32_t* seg_tile_base;
   Report* report;
-  // decode index (D = 64, 128, 256), written by the index pass
-  uint32_t* dec_tile;  // [ntiles][8] flags, eb bits, segment offset, record offset, segment bytes
-  uint32_t* dec_row;   // [ntiles][64][4] kind, first-occurrence index, outliers, offset
-  uint32_t* dec_blk;   // [ntiles][64][D/64] plane word offset in the segment << 4 | width
 };
 
 // LDS bytes of the encode kernel for dimension D.
@@ -132,9 +128,6 @@ hipError_t launch_encode(const EncArgs& a, hipStream_t s);
 bool encode_has_assembly(uint32_t D);
 hipError_t launch_assemble(const EncArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecArgs& a, hipStream_t s);
-// true when D decodes as index + decode (launch_decode_index before launch_decode)
-bool decode_has_index(uint32_t D);
-hipError_t launch_decode_index(const DecArgs& a, hipStream_t s);
 hipError_t set_encode_lds_limit(size_t bytes);
 
 }  // namespace ec

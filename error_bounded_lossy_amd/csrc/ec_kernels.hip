@@ -2304,23 +2304,40 @@ __device__ __forceinline__ uint32_t sum_bytes(const uint8_t* p, uint32_t n) {
 constexpr uint32_t kRowPlanes = 0, kRowRawRef = 1, kRowBad = 2, kRowOutliers = 0x100;
 constexpr uint32_t kTileOk = 1, kTileRaw = 2;
 
+// LDS of the decoder's index step (one tile)
 template <int C>
-__global__ void __launch_bounds__(64) ec_dec_index(const uint8_t* __restrict__ in, DecArgs a) {
+struct DecIndexLds {
+  DecShared sh;
+  uint64_t rec;
+  uint4 td[2];                     // flags, eb, segment offset; record offset, segment bytes
+  uint4 drow[kTileRows];           // kind | outliers flag, first-occurrence index, counts, offset
+  uint32_t dblk[kTileRows * C];    // plane-word offset << 4 | width
+  uint32_t boff[kTileRows * C];    // the record's block plane offsets
+  uint8_t width[kTileRows * C];    // the record's block widths
+};
+// LDS accesses of one wave complete in order; this waits for them and keeps
+// the compiler from moving accesses across.
+__device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Wave 0 of a decode workgroup: locate and check tile `ticket` and describe
+// where every row's values are (the tile descriptor td[2], row descriptors
+// drow[64] and block descriptors dblk[64*C], all in LDS).  LDS written by
+// one lane and read by others of the same wave is ordered by lds_sync.
+template <int C>
+__device__ __forceinline__ void index_tile(const uint8_t* __restrict__ in, const DecArgs& a, uint32_t ticket,
+                                           DecIndexLds<C>& x) {
   constexpr uint32_t D = 64u * C;
-  __shared__ DecShared sh;
-  __shared__ uint64_t s_rec;
-  __shared__ uint8_t s_width[kTileRows * C];
-  __shared__ uint32_t s_boff[kTileRows * C];
-  const uint32_t lane = threadIdx.x, ticket = blockIdx.x;
+  DecShared& sh = x.sh;
+  const uint32_t lane = threadIdx.x & 63;
   if (lane == 0) {
     uint64_t ro;
     dec_locate(a, in, ticket, sh, ro);
-    s_rec = ro;
+    x.rec = ro;
   }
-  __syncthreads();
+  lds_sync();
   const uint32_t k = sh.tile, n = sh.n, rows = sh.rows;
-  uint4* dt = reinterpret_cast<uint4*>(a.dec_tile) + 2 * ticket;
-  const uint64_t seg_off = sh.seg_off, rec_off = s_rec, sbytes = sh.seg_bytes;
+  uint4* dt = x.td;
+  const uint64_t seg_off = sh.seg_off, rec_off = x.rec, sbytes = sh.seg_bytes;
   uint32_t flags = 0;
   auto put_tile = [&]() {
     if (lane == 0) {
@@ -2370,8 +2387,8 @@ __global__ void __launch_bounds__(64) ec_dec_index(const uint8_t* __restrict__ i
   for (uint32_t q = 0; q < 4; q++) {
     const uint32_t b = 4 * lane + q;
     if (b < nblk) {
-      s_width[b] = (uint8_t)wl[q];
-      s_boff[b] = run;
+      x.width[b] = (uint8_t)wl[q];
+      x.boff[b] = run;
     }
     run += wl[q];
   }
@@ -2379,7 +2396,7 @@ __global__ void __launch_bounds__(64) ec_dec_index(const uint8_t* __restrict__ i
   const uint64_t seg_words = sbytes / 8;
   const uint32_t pl_word0 = (rec_in_seg + off_pl) / 8;  // off_pl and records are 8-aligned
   const bool bad = __any(badw) || (uint64_t)pl_word0 + sumw > seg_words;
-  __syncthreads();
+  lds_sync();
   if (bad) {
     if (lane == 0) report_error(a.report, kDevErrCorrupt);
     put_tile();
@@ -2443,11 +2460,10 @@ __global__ void __launch_bounds__(64) ec_dec_index(const uint8_t* __restrict__ i
     if (kind == kRowPlanes && local) {
 #pragma unroll
       for (uint32_t j = 0; j < C; j++) {
-        bw[j] = s_width[u * C + j];
-        bo[j] = pl_word0 + s_boff[u * C + j];
+        bw[j] = x.width[u * C + j];
+        bo[j] = pl_word0 + x.boff[u * C + j];
       }
     }
-    const uint64_t ri = (uint64_t)ticket * kTileRows + i;
     // the outliers of this row's first occurrence: positions [u*D, u*D + D)
     // of the sorted list of its record (values follow all onum positions)
     uint32_t ocnt = 0, ofirst = oofs;
@@ -2467,10 +2483,10 @@ __global__ void __launch_bounds__(64) ec_dec_index(const uint8_t* __restrict__ i
     // x: the kind (| kRowOutliers when the row has outliers); y: first-occurrence
     // index; z: the row's outliers | its record's outliers << 16; w: offset of
     // the row's first outlier position (RAW copy rows: of the record)
-    reinterpret_cast<uint4*>(a.dec_row)[ri] = make_uint4(
+    x.drow[i] = make_uint4(
         kind | (ocnt ? kRowOutliers : 0u), u, ocnt | (onum << 16), kind == kRowRawRef ? orec : ofirst);
 #pragma unroll
-    for (uint32_t j = 0; j < C; j++) a.dec_blk[ri * C + j] = (bo[j] << 4) | bw[j];
+    for (uint32_t j = 0; j < C; j++) x.dblk[i * C + j] = (bo[j] << 4) | bw[j];
   }
 }
 
@@ -2548,19 +2564,23 @@ __global__ void __launch_bounds__(kThreads) ec_decode_fast(const uint8_t* __rest
   const uint32_t pch = s / T, t = s % T;
   const uint32_t rows = chunk_row0(a.sh, pch + 1) - chunk_row0(a.sh, pch);
   const uint32_t n = rows ? min(kTileRows, rows - k * kTileRows) : 0u;
+  // the index step: wave 0 checks the tile and describes its rows in LDS
+  __shared__ DecIndexLds<C> xi;
+  if (wv == 0) index_tile<C>(in, a, ticket, xi);
+  __syncthreads();
   if (n == 0) return;
   float* yt = yout + ((uint64_t)t * B + chunk_row0(a.sh, pch) + (uint64_t)k * kTileRows) * D;
-  const uint4* dt = reinterpret_cast<const uint4*>(a.dec_tile) + 2 * ticket;
+  const uint4* dt = xi.td;
   const uint32_t plane = lane & 15u, half = lane >> 5, hi = (lane >> 4) & 1u;
   const uint32_t rbeg = wv * kRowsPerWave;
   constexpr uint32_t kRowsPerStep = C == 1 ? 2 : 1;  // C = 1: blocks of two rows pair up
   constexpr uint32_t kSteps = kRowsPerWave / kRowsPerStep;
   constexpr uint32_t kM = (C + 1) / 2;  // plane registers per step
-  const uint4* drow = reinterpret_cast<const uint4*>(a.dec_row) + (uint64_t)ticket * kTileRows;
-  const uint32_t* dblk = a.dec_blk + (uint64_t)ticket * kTileRows * C;
-  // round 1: the tile descriptor and those of the lane's rows and blocks
-  // together (kind[]: the row kind, with kRowOutliers when there are outliers
-  // to patch; garbage for a raw or failed tile, and then unused)
+  const uint4* drow = xi.drow;
+  const uint32_t* dblk = xi.dblk;
+  // the tile descriptor and those of the lane's rows and blocks (kind[]: the
+  // row kind, with kRowOutliers when there are outliers to patch; garbage
+  // for a raw or failed tile, and then unused)
   uint32_t kind[kSteps], desc[kSteps][kM];
 #pragma unroll
   for (uint32_t st = 0; st < kSteps; st++) {
@@ -2722,26 +2742,6 @@ hipError_t launch_assemble(const EncArgs& a, hipStream_t s) {
     case 256:
       hipLaunchKernelGGL(ec_size_fast<4>, blocks, sblock, 0, s, a);
       hipLaunchKernelGGL(ec_write_fast<4>, tiles, block, 0, s, a);
-      break;
-    default:
-      return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-bool decode_has_index(uint32_t D) { return D == 64 || D == 128 || D == 256; }
-
-hipError_t launch_decode_index(const DecArgs& a, hipStream_t s) {
-  const dim3 grid(a.sh.ntiles), block(64);
-  switch (a.sh.D) {
-    case 64:
-      hipLaunchKernelGGL(ec_dec_index<1>, grid, block, 0, s, a.in, a);
-      break;
-    case 128:
-      hipLaunchKernelGGL(ec_dec_index<2>, grid, block, 0, s, a.in, a);
-      break;
-    case 256:
-      hipLaunchKernelGGL(ec_dec_index<4>, grid, block, 0, s, a.in, a);
       break;
     default:
       return hipErrorInvalidValue;

@@ -23,7 +23,6 @@ struct Layout {
   uint64_t tile_status, block_status, tile_inserted, tile_rec, tile_U, tile_nout, hash;
   uint64_t stage_pl = 0, stage_w = 0, stage_om = 0, stage_slot = 0;
   uint64_t tile_info = 0, tile_bitmap = 0, tile_first = 0, seg_eb = 0;
-  uint64_t dec_tile = 0, dec_row = 0, dec_blk = 0;
   uint64_t dyn_bytes, total;
   uint32_t nbr;
   std::vector<uint32_t> seg_tile_base_v;
@@ -173,9 +172,6 @@ ec_status make_layout(const ec_plan_desc* d, Layout* L) {
     L->tile_bitmap = take(8ull * tiles);
     L->tile_first = take(4ull * 64 * tiles);
     L->seg_eb = take(4ull * nseg);
-    L->dec_tile = take(32ull * tiles);
-    L->dec_row = take(16ull * 64 * tiles);
-    L->dec_blk = take(4ull * blocks);
     o = aup(o, 256);
   }
   L->total = o;
@@ -437,15 +433,7 @@ ec_status ec_decompress(ec_plan_t pl, const void* d_stream, size_t stream_cap, f
   da.sh = sh;
   da.seg_tile_base = pl->work.seg_tile_base;
   da.report = pl->report_dev;
-  ec_status st;
-  if (ec::decode_has_index(sh.D)) {
-    da.dec_tile = reinterpret_cast<uint32_t*>(pl->ws + pl->L.dec_tile);
-    da.dec_row = reinterpret_cast<uint32_t*>(pl->ws + pl->L.dec_row);
-    da.dec_blk = reinterpret_cast<uint32_t*>(pl->ws + pl->L.dec_blk);
-    st = profiled(pl, EC_KERNEL_DECODE_INDEX, s, [&] { return ec::launch_decode_index(da, s); });
-    if (st != EC_OK) return st;
-  }
-  st = profiled(pl, EC_KERNEL_DECODE, s, [&] { return ec::launch_decode(da, s); });
+  const ec_status st = profiled(pl, EC_KERNEL_DECODE, s, [&] { return ec::launch_decode(da, s); });
   if (st != EC_OK) return st;
   record_done(pl, s);
   return EC_OK;

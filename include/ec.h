@@ -78,18 +78,18 @@ typedef enum {
 
 typedef enum { EC_CODER_BITPACK = 1 } ec_coder;
 
-/* Kernel ids for the profiling counters.  For D = 64, 128 and 256,
+/* Kernel ids for the profiling counters.  PREP is the value-range pass (and
+ * the clearing of the per-call workspace).  For D = 64, 128 and 256,
  * compression runs ENCODE (quantize, bit planes, hash insertion) then ASSEMBLE
  * (first occurrences and record sizes, then placement and record writing: two
- * kernels timed together), and decompression runs DECODE_INDEX (record
- * location, checks, plane offsets of every row) then DECODE.  For other D,
- * ENCODE and DECODE are single kernels and the other ids stay unused. */
+ * kernels timed together); DECODE checks and locates each record and decodes
+ * it in one kernel.  For other D, ENCODE and DECODE are single kernels and
+ * ASSEMBLE stays unused. */
 typedef enum {
   EC_KERNEL_PREP = 0,
   EC_KERNEL_ENCODE = 1,
   EC_KERNEL_DECODE = 2,
-  EC_KERNEL_ASSEMBLE = 3,
-  EC_KERNEL_DECODE_INDEX = 4
+  EC_KERNEL_ASSEMBLE = 3
 } ec_kernel;
 
 typedef struct {
