@@ -1241,7 +1241,9 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
         const float tp = xb[rr][j] * r2;
         const float qf = rintf(tp);
         const float f = tp - qf;
-        um |= __ballot(!(fmaf(fabsf(tp), 0x1p-21f, fabsf(f)) < 0.5f) || !(fabsf(tp) < 2046.5f));
+        // two ballots of plain compares: the OR of the masks stays scalar
+        um |= __ballot(!(fmaf(fabsf(tp), 0x1p-21f, fabsf(f)) < 0.5f));
+        um |= __ballot(!(fabsf(tp) < 2046.5f));
         q[rr][j] = (int)qf;
       }
     uint32_t hs[kRB];
