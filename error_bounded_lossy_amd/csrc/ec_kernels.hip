@@ -1097,25 +1097,6 @@ __device__ __forceinline__ bool rows_same(const float* ra, const float* rb, uint
   return __all(eq);
 }
 
-// Tile row and block of the two blocks of plane register p of a wave whose
-// rows start at rbeg (RB rows per batch): block A for hi = 0, block B for 1.
-template <int C, int RB>
-__device__ __forceinline__ void pair_coords(uint32_t p, uint32_t hi, uint32_t rbeg,
-                                            uint32_t& row, uint32_t& blk) {
-  constexpr uint32_t kPB = RB * C / 2;  // plane registers per batch
-  const uint32_t ib = rbeg + (p / kPB) * RB, lp = p % kPB;
-  if constexpr (C == 1) {
-    row = ib + 2 * lp + hi;
-    blk = 0;
-  } else if constexpr (C == 2) {
-    row = ib + lp;
-    blk = hi;
-  } else {
-    row = ib + lp / 2;
-    blk = 2 * (lp & 1u) + hi;
-  }
-}
-
 // v with lane P (an immediate) replaced by the wave-uniform s
 template <int P>
 __device__ __forceinline__ void put_lane(uint32_t& v, uint32_t s) {
@@ -1152,10 +1133,9 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
   constexpr uint32_t kRowsPerWave = kTileRows / (kThreads / 64);  // 16
   constexpr uint32_t kRB = 16 / C;                                 // rows per batch (16 blocks)
   constexpr uint32_t kNB = kRowsPerWave / kRB;                     // batches per wave
-  constexpr uint32_t kPB = kRB * C / 2;                            // plane registers per batch
   __shared__ EncShared sh;
   __shared__ uint32_t s_hash[kTileRows];
-  __shared__ uint8_t s_oflag[kTileRows][C];
+  __shared__ __align__(4) uint8_t s_oflag[kTileRows][C];
   const uint32_t tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const uint32_t T = a.sh.T;
 
@@ -1216,9 +1196,12 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
   // A (L < 16) or B as one 64-bit word
   const __amdgpu_buffer_rsrc_t rst =
       buf_rsrc(a.w.stage_pl + (uint64_t)ticket * kTileRows * C * kStagePlanes, kTileRows * C * kStagePlanes * 8);
-  const uint32_t lane_word = (lane & 15u) + ((lane >> 4) & 1u) * kStagePlanes;
-  const uint32_t lane_keep = lane < 32 ? 0xFFFFu >> (lane & 15u) : 0u;  // planes from the lane's own up
-  uint32_t nz_lo = 0;  // lane p: non-zero plane-word mask of plane register p
+  // after the half swap of a group's transposes, lane L holds the plane word
+  // of block (L >> 3) & 3 of the group, plane (L & 7) + 8 (L >> 5)
+  const uint32_t lane_blk = (lane >> 3) & 3u, lane_plane = (lane & 7u) + 8u * (lane >> 5);
+  const uint32_t lane_word = lane_blk * kStagePlanes + lane_plane;
+  const uint32_t lane_m8 = lane < 32 ? 0xFFu >> (lane & 7u) : 0u;  // planes from the lane's own up
+  uint32_t gm_lo = 0, gm_hi = 0;  // lane g: non-zero plane masks of block group g of the wave
 
   static_for<0, (int)kNB>([&](auto nbc) {
     constexpr uint32_t nb = decltype(nbc)::value;
@@ -1298,45 +1281,56 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
         }
       }
     }
-    // bit planes of block pairs, staged up to each block's width
-    static_for<0, (int)kPB>([&](auto lpc) {
-      constexpr uint32_t lp = decltype(lpc)::value;
-      int qa, qb;
-      if constexpr (C == 1) {
-        qa = q[2 * lp][0];
-        qb = q[2 * lp + 1][0];
-      } else if constexpr (C == 2) {
-        qa = q[lp][0];
-        qb = q[lp][1];
+    // bit planes, four blocks at a time (blocks 4g .. 4g+3 of the batch, in
+    // (row, block) order): the low bytes of a lane's four zigzag codes go
+    // through one 32x32 bit transpose per half-wave, so that lane L holds
+    // half L >> 5 of plane L & 7 of block (L >> 3) & 3; the high bits
+    // (planes 8-11) take a second transpose only when a block needs them
+    static_for<0, 4>([&](auto gc) {
+      constexpr uint32_t g = decltype(gc)::value;
+      constexpr uint32_t b0 = 4 * g;
+      const uint32_t p01 = zigzag_pair(q[b0 / C][b0 % C], q[(b0 + 1) / C][(b0 + 1) % C]);
+      const uint32_t p23 = zigzag_pair(q[(b0 + 2) / C][(b0 + 2) % C], q[(b0 + 3) / C][(b0 + 3) % C]);
+      const uint32_t lo = __builtin_amdgcn_perm(p23, p01, 0x06040200u);  // low bytes of codes 0..3
+      const uint32_t hi = __builtin_amdgcn_perm(p23, p01, 0x07050301u);  // high bytes (< 16)
+      const uint32_t ylo = xpose32(lo, xsel);
+      const uint64_t nlo = __ballot(ylo != 0);
+      const uint32_t mlo = (uint32_t)nlo | (uint32_t)(nlo >> 32);  // bit 8k + p: plane p of block k
+      uint32_t yhi = 0, mhi = 0;
+      uint32_t above;  // non-zero planes of the lane's block from the lane's plane up
+      if (__ballot(hi != 0)) {
+        yhi = xpose32(hi, xsel);
+        const uint64_t nhi = __ballot(yhi != 0);
+        mhi = (uint32_t)nhi | (uint32_t)(nhi >> 32);  // bit 8k + p: plane 8 + p of block k
+        above = (__builtin_amdgcn_ubfe(mlo, 8 * lane_blk, 8) | (__builtin_amdgcn_ubfe(mhi, 8 * lane_blk, 4) << 8)) >>
+                lane_plane;
       } else {
-        qa = q[lp / 2][2 * (lp & 1)];
-        qb = q[lp / 2][2 * (lp & 1) + 1];
+        above = (mlo >> (lane & 31u)) & lane_m8;
       }
-      const uint32_t y = xpose32(zigzag_pair(qa, qb), xsel);
-      const uint64_t nz = __ballot(y != 0);
-      const uint32_t m32 = (uint32_t)nz | (uint32_t)(nz >> 32);  // block A planes 0-15, B 16-31
-      constexpr uint32_t p = nb * kPB + lp;
-      put_lane<p>(nz_lo, m32);
-      uint32_t row, blk;
-      pair_coords<C, kRB>(p, 0, rbeg, row, blk);
-      const auto hw = __builtin_amdgcn_permlane32_swap(y, y, false, false);  // (lo, hi) halves
+      put_lane<nb * 4 + g>(gm_lo, __builtin_amdgcn_readfirstlane(mlo));
+      put_lane<nb * 4 + g>(gm_hi, __builtin_amdgcn_readfirstlane(mhi));
+      // lanes 0-31: planes 0-7 of the four blocks, lanes 32-63: planes 8-15;
+      // a plane is staged when it is below its block's width
+      const auto hw = __builtin_amdgcn_permlane32_swap(ylo, yhi, false, false);
       const uint64_t word = ((uint64_t)hw[1] << 32) | hw[0];
-      const bool keep = (m32 >> (lane & 31u)) & lane_keep;  // plane below the block's width
-      buf_st_u64(rst, keep ? ((row * C + blk) * kStagePlanes + lane_word) * 8 : kOff, word);
+      buf_st_u64(rst, above ? ((ib * C + b0) * kStagePlanes + lane_word) * 8 : kOff, word);
     });
     const uint32_t hv = rows_reduce<kRB>(hs, lane);
     const uint32_t h = __shfl(hv, (int)((lane % kRB) * (64 / kRB)));
     if (lane < kRB) s_hash[ib + lane] = fmix32(h);
   });
-  // widths of the wave's blocks, lane-parallel: lane p < kNB*kPB holds pair p
-  if (lane < kNB * kPB) {
-    const uint32_t ma = nz_lo & 0xFFFFu, mb = nz_lo >> 16;
-    uint32_t ra, ba, rb2, bb;
-    pair_coords<C, kRB>(lane, 0, rbeg, ra, ba);
-    pair_coords<C, kRB>(lane, 1, rbeg, rb2, bb);
-    uint8_t* sw = a.w.stage_w + (uint64_t)ticket * kTileRows * C;
-    sw[ra * C + ba] = (uint8_t)((ma ? 32 - __clz(ma) : 0) | s_oflag[ra][ba]);
-    sw[rb2 * C + bb] = (uint8_t)((mb ? 32 - __clz(mb) : 0) | s_oflag[rb2][bb]);
+  // widths of the wave's blocks with their outlier flags, lane-parallel:
+  // lane g < 4 kNB holds block group g (blocks 4g .. 4g+3 of the wave)
+  if (lane < 4 * kNB) {
+    uint32_t wp = 0;  // the group's widths, a byte each
+#pragma unroll
+    for (uint32_t k = 0; k < 4; k++) {
+      const uint32_t bl = (gm_lo >> (8 * k)) & 0xFFu, bh = (gm_hi >> (8 * k)) & 0xFu;
+      wp |= (bh ? 40u - __clz(bh) : (bl ? 32u - __clz(bl) : 0u)) << (8 * k);
+    }
+    const uint32_t bw = rbeg * C + 4 * lane;  // first block of the group in the tile
+    const uint32_t of = *reinterpret_cast<const uint32_t*>(&s_oflag[0][0] + bw);
+    *reinterpret_cast<uint32_t*>(a.w.stage_w + (uint64_t)ticket * kTileRows * C + bw) = wp | of;
   }
 
   // ---- insert: each wave owns 16 rows (lanes 0..15); compares use the wave ----
