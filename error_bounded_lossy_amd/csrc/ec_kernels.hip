@@ -1072,31 +1072,6 @@ __device__ __forceinline__ uint32_t rows_reduce(const uint32_t (&h)[RB], uint32_
   return v;
 }
 
-// Do rows a and b (D = 64*C floats each) have equal codes and outlier bits?
-// Bitwise-equal rows always do; otherwise both are quantized and compared.
-template <int C>
-__device__ __forceinline__ bool rows_same(const float* ra, const float* rb, uint32_t lane,
-                                          float eb, float s2, float r2) {
-  float va[C], vb[C];
-  bool raw = true;
-#pragma unroll
-  for (int j = 0; j < C; j++) {
-    va[j] = ra[64 * j + lane];
-    vb[j] = rb[64 * j + lane];
-    raw = raw && f2u(va[j]) == f2u(vb[j]);
-  }
-  if (__all(raw)) return true;
-  bool eq = true;
-#pragma unroll
-  for (int j = 0; j < C; j++) {
-    int qa, qb;
-    const bool oa = quantize_fast(va[j], eb, s2, r2, qa);
-    const bool ob = quantize_fast(vb[j], eb, s2, r2, qb);
-    eq = eq && oa == ob && (oa ? f2u(va[j]) == f2u(vb[j]) : qa == qb);
-  }
-  return __all(eq);
-}
-
 // v with lane P (an immediate) replaced by the wave-uniform s
 template <int P>
 __device__ __forceinline__ void put_lane(uint32_t& v, uint32_t s) {
@@ -1356,18 +1331,51 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
         slot = (slot + 1) & cap_mask;
       }
     }
+    // tag hits, kCmp at a time with all their row loads in flight together:
+    // equal rows keep the smaller row in the slot (the slot is read by the
+    // next launch only, so the minimum need not be awaited)
+    constexpr int kCmp = C >= 4 ? 2 : 8 / C;
     uint64_t m = __ballot(need);
     while (m) {
-      const int Ln = __ffsll((long long)m) - 1;
-      m &= m - 1;
-      const uint32_t iL = __shfl(i, Ln), cL = __shfl(cand, Ln);
-      const bool eq = rows_same<C>(xs + (uint64_t)cL * D, xt + (uint64_t)iL * D, lane, eb, s2, r2);
-      if ((int)lane == Ln) {
-        if (eq) {
-          atomic_min_performed(&htab[slot], mine);
-          active = false;
-        } else {
-          slot = (slot + 1) & cap_mask;
+      int Lk[kCmp];
+      float va[kCmp][C], vb[kCmp][C];
+#pragma unroll
+      for (int kk = 0; kk < kCmp; kk++) {
+        Lk[kk] = m ? __ffsll((long long)m) - 1 : -1;
+        m &= m - 1;
+        const int Ls = Lk[kk] < 0 ? Lk[0] : Lk[kk];  // no candidate: a copy of the first
+        const uint32_t iL = __shfl(i, Ls), cL = __shfl(cand, Ls);
+#pragma unroll
+        for (int j = 0; j < C; j++) {
+          va[kk][j] = xs[(uint64_t)cL * D + 64 * j + lane];
+          vb[kk][j] = xt[(uint64_t)iL * D + 64 * j + lane];
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < kCmp; kk++) {
+        if (Lk[kk] < 0) continue;
+        bool raw = true;
+#pragma unroll
+        for (int j = 0; j < C; j++) raw = raw && f2u(va[kk][j]) == f2u(vb[kk][j]);
+        bool eq = __all(raw);
+        if (!eq) {  // different bits: the same codes and outliers make the rows equal
+          bool e = true;
+#pragma unroll
+          for (int j = 0; j < C; j++) {
+            int qa, qb;
+            const bool oa = quantize_fast(va[kk][j], eb, s2, r2, qa);
+            const bool ob = quantize_fast(vb[kk][j], eb, s2, r2, qb);
+            e = e && oa == ob && (oa ? f2u(va[kk][j]) == f2u(vb[kk][j]) : qa == qb);
+          }
+          eq = __all(e);
+        }
+        if ((int)lane == Lk[kk]) {
+          if (eq) {
+            __hip_atomic_fetch_min(&htab[slot], mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            active = false;
+          } else {
+            slot = (slot + 1) & cap_mask;
+          }
         }
       }
     }
