@@ -1317,6 +1317,7 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
   uint32_t slot = H & cap_mask;
   const uint64_t mine = ((uint64_t)H << 32) | (uint64_t)(k * kTileRows + i + 1);
   uint32_t guard = 0;
+  uint32_t seen = 0;  // the row (+ 1) of the slot value a tag hit was found in
   while (__ballot(active) != 0) {
     bool need = false;
     uint32_t cand = 0;
@@ -1327,6 +1328,7 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
       } else if ((uint32_t)(old >> 32) == H && (uint32_t)old - 1u < rows) {
         need = true;
         cand = (uint32_t)old - 1u;
+        seen = (uint32_t)old;
       } else {
         slot = (slot + 1) & cap_mask;
       }
@@ -1371,7 +1373,10 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
         }
         if ((int)lane == Lk[kk]) {
           if (eq) {
-            __hip_atomic_fetch_min(&htab[slot], mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            // the smaller row is the first occurrence; the slot only ever
+            // decreases from the value seen, so a larger row needs no update
+            if ((uint32_t)mine < seen)
+              __hip_atomic_fetch_min(&htab[slot], mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             active = false;
           } else {
             slot = (slot + 1) & cap_mask;
