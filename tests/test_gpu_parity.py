@@ -315,3 +315,19 @@ def test_plan_reused_across_calls(T, B, D, mode):
         plan.ratio()
         yo = O.decompress(cfg, ref.stream)
         np.testing.assert_array_equal(y.cpu().numpy().view(np.uint32), yo.view(np.uint32))
+
+
+@pytest.mark.parametrize("D,bits", [(64, 0), (128, 0), (256, 0), (128, 2)])
+def test_hot_rows_many_duplicates(D, bits):
+    """A few rows repeated thousands of times across many tiles (one-hot
+    lookups of a hot index), with near-duplicates that differ by less than a
+    bin and, with few hash bits, tag collisions between different rows: every
+    duplicate must point at the smallest equal row of its segment."""
+    rng = np.random.default_rng(D + bits)
+    T, B = 2, 4096
+    base = rng.normal(0, 0.1, (T, 6, D)).astype(np.float32)
+    idx = rng.choice(6, size=(T, B), p=[0.55, 0.2, 0.1, 0.08, 0.05, 0.02])
+    x = np.take_along_axis(base, idx[:, :, None], axis=1).astype(np.float32)
+    x[:, 1000:1100, 5] += np.float32(1e-7)  # same codes, other bits
+    x[:, 3000] = rng.normal(0, 0.1, (T, D))  # a unique row late in the segment
+    assert_parity(make_cfg(T, B, D, eb_mode=1, eb=(0.02,)), x, hash_bits=bits, label=f"hot-{D}-{bits}")
