@@ -2503,27 +2503,24 @@ __device__ __forceinline__ void index_tile(const uint8_t* __restrict__ in, const
 // the transposed planes: outliers to patch, a first occurrence stored RAW
 // (re-quantized), or a corrupt reference (zeros, reported).  v holds the
 // transposed values when all_planes.  Rare, so kept out of line.
-template <int C>
-__device__ __forceinline__ void decode_rows_special(
-    const DecArgs& a, const uint8_t* sg, float* yt, uint32_t i0, uint32_t n, bool all_planes,
-    float v0, float v1, float v2, float v3, float eb, float s2, const uint4* drow,
-    const uint32_t* dblk) {
-  const float v[4] = {v0, v1, v2, v3};
+template <int C, int ROWS>
+__device__ __forceinline__ void decode_rows_special(const DecArgs& a, const uint8_t* sg, float* yt,
+                                                    uint32_t i0, uint32_t n, float eb, float s2,
+                                                    const uint4* drow, const uint32_t* dblk) {
   constexpr uint32_t D = 64u * C;
-  constexpr uint32_t kRowsPerStep = C == 1 ? 2 : 1;
   const uint32_t lane = threadIdx.x & 63;
   bool ok = true;
-  for (uint32_t rr = 0; rr < kRowsPerStep; rr++) {
+  for (uint32_t rr = 0; rr < (uint32_t)ROWS; rr++) {
     const uint32_t ir = i0 + rr;
     if (ir >= n) continue;
     uint4 ri = drow[ir];  // kind, first-occurrence index, outliers, offset
     ri.x &= 0xFFu;
     float vr[C];
 #pragma unroll
-    for (uint32_t j = 0; j < C; j++) vr[j] = all_planes ? v[C == 1 ? rr : j] : 0.0f;
+    for (uint32_t j = 0; j < C; j++) vr[j] = 0.0f;
     bool okr = ri.x != kRowBad;
-    if (ri.x == kRowPlanes && !all_planes) {
-      // a plane row next to a RAW-copy row (C = 1 pairs): decode it alone
+    if (ri.x == kRowPlanes) {
+      // a plane row in a group with a RAW-copy or corrupt row: decode it alone
 #pragma unroll
       for (uint32_t j = 0; j < C; j++) {
         const uint32_t dsc = dblk[ir * C + j], w = dsc & 15u, o = dsc >> 4;
@@ -2580,27 +2577,29 @@ __global__ void __launch_bounds__(kThreads) ec_decode_fast(const uint8_t* __rest
   if (n == 0) return;
   float* yt = yout + ((uint64_t)t * B + chunk_row0(a.sh, pch) + (uint64_t)k * kTileRows) * D;
   const uint4* dt = xi.td;
-  const uint32_t plane = lane & 15u, half = lane >> 5, hi = (lane >> 4) & 1u;
   const uint32_t rbeg = wv * kRowsPerWave;
-  constexpr uint32_t kRowsPerStep = C == 1 ? 2 : 1;  // C = 1: blocks of two rows pair up
-  constexpr uint32_t kSteps = kRowsPerWave / kRowsPerStep;
-  constexpr uint32_t kM = (C + 1) / 2;  // plane registers per step
+  // four blocks per transpose: group g of the wave holds its blocks
+  // 4g .. 4g+3 in (row, block) order; lane L loads half L >> 5 of plane L & 7
+  // (and of plane 8 + (L & 7)) of block (L >> 3) & 3 of the group
+  constexpr uint32_t kGroupRows = 4 / C;
+  constexpr uint32_t kGroups = kRowsPerWave * C / 4;
+  const uint32_t gplane = lane & 7u, half = lane >> 5, gblk = (lane >> 3) & 3u;
   const uint4* drow = xi.drow;
   const uint32_t* dblk = xi.dblk;
-  // the tile descriptor and those of the lane's rows and blocks (kind[]: the
+  // the descriptors of the lane's row and block in every group (kind[]: the
   // row kind, with kRowOutliers when there are outliers to patch; garbage
   // for a raw or failed tile, and then unused)
-  uint32_t kind[kSteps], desc[kSteps][kM];
+  uint32_t kind[kGroups], desc[kGroups];
 #pragma unroll
-  for (uint32_t st = 0; st < kSteps; st++) {
-    const uint32_t i = min(rbeg + st * kRowsPerStep + (C == 1 ? hi : 0u), n - 1);  // past n: a copy
-    kind[st] = drow[i].x;
-#pragma unroll
-    for (uint32_t m = 0; m < kM; m++) desc[st][m] = dblk[i * C + (C == 1 ? 0u : 2 * m + hi)];
+  for (uint32_t g = 0; g < kGroups; g++) {
+    const uint32_t bi = 4 * g + gblk;
+    const uint32_t i = min(rbeg + bi / C, n - 1);  // past n: a copy
+    kind[g] = drow[i].x;
+    desc[g] = dblk[i * C + bi % C];
   }
   const uint4 d0 = dt[0], d1 = dt[1];
   const uint32_t flags = d0.x;
-  if (!(flags & kTileOk)) {  // the index pass reported it
+  if (!(flags & kTileOk)) {  // the index step reported it
     for (uint32_t i = tid; i < n * D; i += kThreads) yt[i] = 0.0f;
     return;
   }
@@ -2616,46 +2615,42 @@ __global__ void __launch_bounds__(kThreads) ec_decode_fast(const uint8_t* __rest
   const __amdgpu_buffer_rsrc_t rseg = buf_rsrc(sg, d1.z);
   const __amdgpu_buffer_rsrc_t ry = buf_rsrc(yt, n * D * 4);
   const XposeSel xsel = xpose_sel(lane);
-  // round 2: every plane word of the wave's rows
-  uint32_t word[kSteps][kM];
+  // every plane word of the wave's rows (planes 8-11 exist only in blocks
+  // wider than 8)
+  uint32_t wlo[kGroups], whi[kGroups];
 #pragma unroll
-  for (uint32_t st = 0; st < kSteps; st++)
+  for (uint32_t g = 0; g < kGroups; g++) {
+    const uint32_t w = desc[g] & 15u, o = desc[g] >> 4;
+    const bool on = (kind[g] & 0xFFu) == kRowPlanes;
+    wlo[g] = buf_ld_u32(rseg, on && gplane < w ? (2 * (o + gplane) + half) * 4 : kOff);
+    whi[g] = buf_ld_u32(rseg, on && gplane + 8 < w ? (2 * (o + 8 + gplane) + half) * 4 : kOff);
+  }
+  uint32_t special = 0;  // groups with RAW copies or corrupt rows: done last
+  uint32_t patch = 0;    // groups with outliers: their raw values are stored last
 #pragma unroll
-    for (uint32_t m = 0; m < kM; m++) {
-      const uint32_t w = desc[st][m] & 15u, o = desc[st][m] >> 4;
-      const bool on = (kind[st] & 0xFFu) == kRowPlanes && plane < w;
-      word[st][m] = buf_ld_u32(rseg, on ? (2 * (o + plane) + half) * 4 : kOff);
-    }
-  uint32_t special = 0;  // steps with RAW copies or corrupt rows: done last
-  uint32_t patch = 0;    // steps with outliers: their raw values are stored last
-#pragma unroll
-  for (uint32_t st = 0; st < kSteps; st++) {
-    const uint32_t i0 = rbeg + st * kRowsPerStep;
-    if (i0 < n) {  // (no early exit: the loop must unroll to keep word[] in registers)
-      if (__all((kind[st] & 0xFFu) == kRowPlanes)) {
-        if (__any(kind[st] & kRowOutliers)) patch |= 1u << st;
-        float v[2 * kM];
-#pragma unroll
-        for (uint32_t m = 0; m < kM; m++) {
-          const uint32_t zz2 = xpose32(word[st][m], xsel);
-          int qa, qb;
-          unzigzag_pair(zz2, qa, qb);
-          v[2 * m] = (float)qa * s2;
-          v[2 * m + 1] = (float)qb * s2;
-        }
+  for (uint32_t g = 0; g < kGroups; g++) {
+    const uint32_t i0 = rbeg + g * kGroupRows;
+    if (i0 < n) {  // (no early exit: the loop must unroll to keep the words in registers)
+      if (__all((kind[g] & 0xFFu) == kRowPlanes)) {
+        if (__any(kind[g] & kRowOutliers)) patch |= 1u << g;
+        // lane L: element L of the four blocks, low bytes of the codes, and
+        // the high bits when a block is wider than 8
+        const uint32_t ylo = xpose32(wlo[g], xsel);
+        const uint32_t yhi = __ballot(whi[g] != 0) ? xpose32(whi[g], xsel) : 0u;
+        int q[4];
+        unzigzag_pair(__builtin_amdgcn_perm(yhi, ylo, 0x05010400u), q[0], q[1]);
+        unzigzag_pair(__builtin_amdgcn_perm(yhi, ylo, 0x07030602u), q[2], q[3]);
         // rows past n fall outside ry's range; streaming stores (the output is
         // not read again here, and dirty lines left in the caches would be
         // written back while the next pass reads its input); the row offset
         // is wave-uniform and goes in the scalar offset
 #pragma unroll
-        for (uint32_t rr = 0; rr < kRowsPerStep; rr++)
-#pragma unroll
-          for (uint32_t j = 0; j < C; j++)
-            __builtin_amdgcn_raw_buffer_store_b32(
-                f2u(v[C == 1 ? rr : j]), ry, 4 * lane,
-                __builtin_amdgcn_readfirstlane(((i0 + rr) * D + 64 * j) * 4), kCacheStream);
+        for (uint32_t kk = 0; kk < 4; kk++)
+          __builtin_amdgcn_raw_buffer_store_b32(
+              f2u((float)q[kk] * s2), ry, 4 * lane,
+              __builtin_amdgcn_readfirstlane(((i0 + kk / C) * D + 64 * (kk % C)) * 4), kCacheStream);
       } else {
-        special |= 1u << st;
+        special |= 1u << g;
       }
     }
   }
@@ -2663,10 +2658,10 @@ __global__ void __launch_bounds__(kThreads) ec_decode_fast(const uint8_t* __rest
   // stores are performed)
   if (patch) {
     wait_vm();
-    for (uint32_t st = 0; st < kSteps; st++) {
-      if (!((patch >> st) & 1u)) continue;
-      for (uint32_t rr = 0; rr < kRowsPerStep; rr++) {
-        const uint32_t ir = rbeg + st * kRowsPerStep + rr;
+    for (uint32_t g = 0; g < kGroups; g++) {
+      if (!((patch >> g) & 1u)) continue;
+      for (uint32_t rr = 0; rr < kGroupRows; rr++) {
+        const uint32_t ir = rbeg + g * kGroupRows + rr;
         if (ir >= n) continue;
         const uint4 ri = drow[ir];
         const uint32_t cnt = ri.z & 0xFFFFu;
@@ -2680,27 +2675,10 @@ __global__ void __launch_bounds__(kThreads) ec_decode_fast(const uint8_t* __rest
       }
     }
   }
-  // the rare steps, once the plane registers are free: reload and decode again
-  for (uint32_t st = 0; st < kSteps; st++) {
-    if (!((special >> st) & 1u)) continue;
-    const uint32_t i0 = rbeg + st * kRowsPerStep;
-    const uint32_t i = min(i0 + (C == 1 ? hi : 0u), n - 1);
-    const uint32_t kd = drow[i].x & 0xFFu;
-    const bool all_planes = __all(kd == kRowPlanes);
-    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (all_planes) {
-#pragma unroll
-      for (uint32_t m = 0; m < kM; m++) {
-        const uint32_t dsc = dblk[i * C + (C == 1 ? 0u : 2 * m + hi)];
-        const uint32_t w = dsc & 15u, o = dsc >> 4;
-        const uint32_t wd = buf_ld_u32(rseg, plane < w ? (2 * (o + plane) + half) * 4 : kOff);
-        int qa, qb;
-        unzigzag_pair(xpose32(wd, xsel), qa, qb);
-        v[(2 * m) & 3] = (float)qa * s2;
-        v[(2 * m + 1) & 3] = (float)qb * s2;
-      }
-    }
-    decode_rows_special<C>(a, sg, yt, i0, n, all_planes, v[0], v[1], v[2], v[3], eb, s2, drow, dblk);
+  // the rare groups, row by row
+  for (uint32_t g = 0; g < kGroups; g++) {
+    if (!((special >> g) & 1u)) continue;
+    decode_rows_special<C, kGroupRows>(a, sg, yt, rbeg + g * kGroupRows, n, eb, s2, drow, dblk);
   }
 }
 
