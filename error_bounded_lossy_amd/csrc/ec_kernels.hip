@@ -9,14 +9,15 @@
 //            planes, stage planes and widths in the workspace, and insert the
 //            tile's quantized rows into the segment's hash table (section
 //            III-B "Vector Homogenization", the vector-based LZ of III-D).
-//  assemble  one workgroup per tile, after every row is in the table: first
-//            occurrences, record size, a decoupled look-back prefix scan that
-//            places every tile, table and chunk in ONE contiguous stream
-//            (section III-E "Buffer Optimization", Fig. 7), and the copy of the
-//            staged planes of first-occurrence rows.
-//  encode    (other D) both passes in one kernel, tiles waiting on earlier
-//            tiles' hash insertions.
-//  decode    one workgroup per tile; each output row is written once.
+//  assemble  two launches after every row is in the table: size (first
+//            occurrences, record sizes, sums over blocks of tiles) and write
+//            (each tile's place in ONE contiguous stream from those sums,
+//            section III-E "Buffer Optimization", Fig. 7; the record and the
+//            staged planes of first-occurrence rows).
+//  encode    (other D) both passes in one kernel, tiles placed by a decoupled
+//            look-back over earlier tiles.
+//  decode    one workgroup per tile (D = 64, 128, 256: wave 0 checks and
+//            indexes the record first); each output row is written once.
 //
 // Quantization uses IEEE fp32 division and round-to-nearest-even; the build
 // disables FP contraction so the reconstruction check is the exact fp32
@@ -1397,8 +1398,8 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
 // ---------------------------------------------------------------------------
 // assembly for D = 64*C, after every row is in the hash table, in three
 // launches that never wait on one another's workgroups:
-//   size   one wave per tile: first occurrences, record layout and size, added
-//          into sums over blocks of 64 tiles and over segments
+//   size   two tiles per wave: first occurrences, record layout and size,
+//          added into a sum per workgroup (8 tiles)
 //   write  one workgroup per tile: its offset from those sums, the record, the
 //          tile's directory entry and, from first tiles, the segment and
 //          stream headers and tables
@@ -1446,8 +1447,8 @@ __device__ __forceinline__ RecLayout rec_layout(uint32_t n, uint32_t U, uint32_t
 
 __device__ __forceinline__ uint64_t seg_prefix_bytes(uint32_t ntiles) { return 32 + align_up(4ull * ntiles, 16); }
 
-// Size pass: one workgroup per block of 64 tiles, four tiles per wave (their
-// loads are issued together); the block's item sum is stored once.
+// Size pass: one workgroup per block of kBlockTiles tiles, EC_SIZE_Q tiles per
+// wave (their loads are issued together); the block's item sum is stored once.
 #ifndef EC_SIZE_Q
 #define EC_SIZE_Q 2
 #endif
