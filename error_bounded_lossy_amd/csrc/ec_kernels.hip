@@ -1209,13 +1209,19 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
 #pragma unroll
     for (uint32_t rr = 0; rr < kRB; rr++) hs[rr] = 0;
     if (um) {  // rare: the IEEE division and the reconstruction check decide
+      // the batch reloaded (its registers died with the fast pass), every
+      // load issued before the first is used
+      float xr[kRB][C];
+#pragma unroll
+      for (uint32_t rr = 0; rr < kRB; rr++)
+#pragma unroll
+        for (uint32_t j = 0; j < C; j++) xr[rr][j] = buf_ld_f32(rx, ((ib + rr) * D + 64 * j + lane) * 4);
 #pragma unroll
       for (uint32_t rr = 0; rr < kRB; rr++) {
         const uint32_t i = ib + rr;
 #pragma unroll
         for (uint32_t j = 0; j < C; j++) {
-          // reloaded, so that the batch registers die with the fast pass
-          const float x = buf_ld_f32(rx, (i * D + 64 * j + lane) * 4);
+          const float x = xr[rr][j];
           const float tp = x * r2;
           const float f = tp - rintf(tp);
           bool out = false;
