@@ -1549,7 +1549,18 @@ __device__ __forceinline__ uint64_t tiles_before(const EncArgs& a, uint32_t j) {
   static_assert(kBlockTiles <= 64, "one lane per tile of a block");
   const uint32_t lane = threadIdx.x & 63, blk = j / kBlockTiles, in = j - blk * kBlockTiles;
   uint64_t v = lane < in ? a.w.tile_status[blk * kBlockTiles + lane] : 0;
-  for (uint32_t b = lane; b < blk; b += 64) v += a.w.block_status[b];
+  // the block sums before j's block: eight loads per lane issued together
+  // (one round trip up to 512 blocks, not one per 64)
+  for (uint32_t b0 = 0; b0 < blk; b0 += 8 * 64) {
+    uint64_t u[8];
+#pragma unroll
+    for (uint32_t q = 0; q < 8; q++) {
+      const uint32_t b = b0 + 64 * q + lane;
+      u[q] = b < blk ? a.w.block_status[b] : 0ull;
+    }
+#pragma unroll
+    for (uint32_t q = 0; q < 8; q++) v += u[q];
+  }
   return wave_sum_u64(v);
 }
 
