@@ -323,11 +323,20 @@ __device__ __forceinline__ float table_eb(const EncArgs& a, uint32_t t, bool& va
   if (a.eb_mode == 1) {
     float lo = INFINITY, hi = -INFINITY;
     if (a.sh.B > 0) {
-      const float* rp = a.w.range_part + 2 * (uint64_t)t * a.w.nbr;
-      for (uint32_t j = lane; j < a.w.nbr; j += 64) {
-        float l = rp[2 * j], h = rp[2 * j + 1];
-        lo = l < lo ? l : lo;
-        hi = h > hi ? h : hi;
+      const float2* rp = reinterpret_cast<const float2*>(a.w.range_part) + (uint64_t)t * a.w.nbr;
+      // eight partials per lane loaded together (one round trip up to 512)
+      for (uint32_t j0 = 0; j0 < a.w.nbr; j0 += 8 * 64) {
+        float2 v[8];
+#pragma unroll
+        for (uint32_t q = 0; q < 8; q++) {
+          const uint32_t j = j0 + 64 * q + lane;
+          v[q] = j < a.w.nbr ? rp[j] : make_float2(INFINITY, -INFINITY);
+        }
+#pragma unroll
+        for (uint32_t q = 0; q < 8; q++) {
+          lo = v[q].x < lo ? v[q].x : lo;
+          hi = v[q].y > hi ? v[q].y : hi;
+        }
       }
       for (int o = 32; o > 0; o >>= 1) {
         float l2 = __shfl_xor(lo, o), h2 = __shfl_xor(hi, o);
