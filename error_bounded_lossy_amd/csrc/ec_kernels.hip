@@ -787,7 +787,7 @@ __global__ void __launch_bounds__(kThreads) ec_encode_kernel(EncArgs a) {
             }
           }
         }
-        if (++guard > cap_mask + 2) {  // cannot happen: the table is at most half full
+        if (++guard > cap_mask + 2) {  // cannot happen: the table is at most a quarter full
           if (active) {
             report_error(a.report, kDevErrTimeout);
             s_slot[i] = slot;
@@ -1400,7 +1400,7 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
         }
       }
     }
-    if (++guard > cap_mask + 2) {  // cannot happen: the table is at most half full
+    if (++guard > cap_mask + 2) {  // cannot happen: the table is at most a quarter full
       if (active) {
         report_error(a.report, kDevErrTimeout);
         active = false;

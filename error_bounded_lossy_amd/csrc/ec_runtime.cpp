@@ -98,8 +98,11 @@ ec_status make_layout(const ec_plan_desc* d, Layout* L) {
     // per-segment stream size must fit the u32 tile directory
     uint64_t seg_max = 32 + aup(4ull * nt, 16) + 16ull * nt + 4ull * rows * D + 16ull * nt;
     if (seg_max >= (1ull << 31)) return EC_ERR_UNSUPPORTED;
+    // hash slots: a power of two >= 4 rows, so the table is at most a quarter
+    // full and a wave's 16 insertions rarely probe far (at half full the
+    // longest of their linear-probing chains set the pace of the quantize pass)
     uint32_t lg = 6;
-    while ((1ull << lg) < 2ull * rows) lg++;
+    while ((1ull << lg) < 4ull * rows) lg++;
     uint64_t seg_bytes = 32 + aup(4ull * nt, 16);
     for (uint32_t k = 0; k < nt; k++) {
       uint32_t n = rows - 64 * k < 64 ? rows - 64 * k : 64;
