@@ -35,7 +35,10 @@ struct Shape {
 
 // Workspace pointers.  "Constant" arrays are written once at plan time; the
 // dynamic region [dyn, dyn + dyn_words) is zeroed by the prep kernel of every
-// compress call.
+// compress call for D other than 64, 128, 256, and of a plan's first call for
+// those (the write pass then leaves the hash tables zero: it clears the slot
+// of every first occurrence, the only slots in use; the rest of the region
+// is written before it is read).
 struct Work {
   const float* eb_base;          // [T]
   const float* mult;             // [T]
@@ -77,7 +80,8 @@ struct PrepArgs {
   const float* x;
   Shape sh;
   Work w;
-  int rel;
+  int rel;    // per-table (min, max) partials
+  int clear;  // zero the dynamic region
 };
 
 struct EncArgs {

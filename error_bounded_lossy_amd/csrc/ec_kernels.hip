@@ -207,7 +207,8 @@ __device__ uint32_t block_exclusive_scan(uint32_t* a, uint32_t n, uint32_t* s_pa
 __global__ void __launch_bounds__(kThreads) ec_prep_kernel(PrepArgs a) {
   const uint64_t gtid = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
   const uint64_t stride = (uint64_t)gridDim.x * kThreads;
-  for (uint64_t i = gtid; i < a.w.dyn_words; i += stride) a.w.dyn[i] = 0;
+  if (a.clear)
+    for (uint64_t i = gtid; i < a.w.dyn_words; i += stride) a.w.dyn[i] = 0;
   if (!a.rel) return;
 
   __shared__ float s_lo[kThreads / 64], s_hi[kThreads / 64];
@@ -1663,6 +1664,13 @@ ec_write_fast(EncArgs a) {
     for (uint32_t j = 0; j < C; j++) wb[j] = a.w.stage_w[rowi * C + j];
     const uint32_t first = a.w.tile_first[rowi];
     const bool uniq = (bitmap >> lane) & 1ull;
+    // the hash slot of a first occurrence goes back to zero (read by the size
+    // pass, which is done): every slot in use belongs to exactly one first
+    // occurrence, so the tables are clear for the next call
+    if (uniq) {
+      const uint32_t cap_mask = (1u << a.w.hash_log2[c.s]) - 1u;
+      a.w.hash[a.w.hash_off[c.s] + (a.w.stage_slot[rowi] & cap_mask)] = 0ull;
+    }
     uint32_t rw = 0, ro = 0;
 #pragma unroll
     for (uint32_t j = 0; j < C; j++) {

@@ -214,6 +214,7 @@ struct ec_plan_s {
   uint8_t* dbg_outlier = nullptr;
   uint32_t* dbg_first = nullptr;
   float* dbg_eb = nullptr;
+  bool hash_clear = false;  // the hash tables are zero (the last call's write pass cleared them)
   bool prof_on = false;
   std::vector<hipEvent_t> prof_pool;
   std::vector<ProfRec> prof_recs;
@@ -384,7 +385,13 @@ ec_status ec_compress(ec_plan_t pl, int64_t iter, const float* d_in, void* d_out
   if (out_cap < pl->L.max_bytes) return EC_ERR_CAPACITY;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
-  ec::PrepArgs pa{d_in, sh, pl->work, pl->desc.eb_mode == EC_EB_REL_RANGE ? 1 : 0};
+  // D = 64, 128, 256: the dynamic region is zeroed on the plan's first call
+  // only (the write pass leaves the hash tables clear); a call that fails to
+  // launch all its kernels makes the next one clear again
+  const bool assembled = ec::encode_has_assembly(sh.D);
+  const bool clear = !assembled || !pl->hash_clear;
+  pl->hash_clear = false;
+  ec::PrepArgs pa{d_in, sh, pl->work, pl->desc.eb_mode == EC_EB_REL_RANGE ? 1 : 0, clear ? 1 : 0};
   uint32_t grid;
   if (pa.rel && sh.B > 0) {
     grid = sh.T * pl->L.nbr;
@@ -393,7 +400,8 @@ ec_status ec_compress(ec_plan_t pl, int64_t iter, const float* d_in, void* d_out
     uint64_t g = (pl->work.dyn_words + 1023) / 1024;
     grid = (uint32_t)(g < 1 ? 1 : (g > 2048 ? 2048 : g));
   }
-  ec_status st = profiled(pl, EC_KERNEL_PREP, s, [&] { return ec::launch_prep(pa, grid, s); });
+  ec_status st = EC_OK;
+  if (pa.rel || pa.clear) st = profiled(pl, EC_KERNEL_PREP, s, [&] { return ec::launch_prep(pa, grid, s); });
   if (st != EC_OK) return st;
 
   ec::EncArgs ea{};
@@ -414,9 +422,10 @@ ec_status ec_compress(ec_plan_t pl, int64_t iter, const float* d_in, void* d_out
   ea.dbg_eb = pl->dbg_eb;
   st = profiled(pl, EC_KERNEL_ENCODE, s, [&] { return ec::launch_encode(ea, s); });
   if (st != EC_OK) return st;
-  if (ec::encode_has_assembly(sh.D)) {
+  if (assembled) {
     st = profiled(pl, EC_KERNEL_ASSEMBLE, s, [&] { return ec::launch_assemble(ea, s); });
     if (st != EC_OK) return st;
+    pl->hash_clear = true;
   }
   record_done(pl, s);
   return EC_OK;

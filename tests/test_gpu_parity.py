@@ -317,6 +317,40 @@ def test_plan_reused_across_calls(T, B, D, mode):
         np.testing.assert_array_equal(y.cpu().numpy().view(np.uint32), yo.view(np.uint32))
 
 
+@pytest.mark.parametrize("D,mode,bits", [(64, 0, 4), (128, 1, 3), (256, 0, 0)])
+def test_hash_tables_clean_between_calls(D, mode, bits):
+    """The hash tables are cleared on a plan's first call only; afterwards the
+    write pass clears the slots it used.  Calls alternate duplicate-heavy and
+    duplicate-free batches, with weakened row hashes (long probe chains, many
+    tag collisions), a segment stored raw and a tile stored raw: every call
+    must still match the oracle byte for byte."""
+    T, B = 3, 700
+    say(f"[clean] D={D} mode={mode} bits={bits}")
+    rng = np.random.default_rng(D + mode + bits)
+    cfg = make_cfg(T, B, D, eb_mode=mode, eb=(0.01,))
+    plan = ec.Plan(T, B, D, 1, mode, 0.01, debug_hash_bits=bits)
+    out = plan.empty_stream()
+    for call in range(5):
+        if call % 2 == 0:
+            x = dup_rows(rng, T, B, D, scale=0.05, frac_unique=0.1)
+        else:
+            x = rng.normal(0, 0.05, (T, B, D)).astype(np.float32)
+        if call == 2:
+            x[1] = np.nan  # an invalid error bound (range mode) or outliers only
+        if call == 3:
+            x[2, 64:128] = rng.normal(0, 1e4, (64, D)).astype(np.float32)  # a raw tile
+        plan.compress(torch.from_numpy(x).cuda(), out, call)
+        _, nbytes, _, _ = plan.ratio(per_segment=True)
+        ref = O.compress(cfg, call, x, debug=False)
+        got = out[:nbytes].cpu().numpy()
+        assert got.size == ref.stream.size and np.array_equal(got, ref.stream), f"call {call}"
+        y = torch.empty(T, B, D, device="cuda")
+        plan.decompress(out[:nbytes], y)
+        plan.ratio()
+        yo = O.decompress(cfg, ref.stream)
+        np.testing.assert_array_equal(y.cpu().numpy().view(np.uint32), yo.view(np.uint32))
+
+
 @pytest.mark.parametrize("D,bits", [(64, 0), (128, 0), (256, 0), (128, 2)])
 def test_hot_rows_many_duplicates(D, bits):
     """A few rows repeated thousands of times across many tiles (one-hot
