@@ -2316,21 +2316,28 @@ __device__ __forceinline__ void unzigzag_pair(uint32_t zz2, int& qa, int& qb) {
   qb = q.y;
 }
 
-// Sum of the n bytes at p (n < 2^16), 16 bytes per load.
-__device__ __forceinline__ uint32_t sum_bytes(const uint8_t* p, uint32_t n) {
-  uint32_t s = 0, q = 0;
-  if (((uintptr_t)p & 15u) == 0) {
-    for (; q + 16 <= n; q += 16) {
-      const uint4 v = *reinterpret_cast<const uint4*>(p + q);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+// Sum of the m width bytes at byte `off` (16-aligned) of a segment read
+// through its buffer resource (reads past the segment return 0): 16-byte
+// loads issued four at a time, bytes past m masked off, v_sad_u8 sums.
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint32_t sum_widths(__amdgpu_buffer_rsrc_t rseg, uint32_t off, uint32_t m) {
+  uint32_t s = 0;
+  for (uint32_t c0 = 0; 16 * c0 < m; c0 += 4) {
+    u32x4v v[4];
 #pragma unroll
-      for (int c = 0; c < 4; c++) {
-        const uint32_t t = (w[c] & 0x00ff00ffu) + ((w[c] >> 8) & 0x00ff00ffu);
-        s += (t & 0xffffu) + (t >> 16);
-      }
+    for (uint32_t i = 0; i < 4; i++) {
+      const uint32_t at = 16 * (c0 + i);
+      v[i] = __builtin_amdgcn_raw_buffer_load_b128(rseg, at < m ? off + at : kOff, 0, 0);
     }
+#pragma unroll
+    for (uint32_t i = 0; i < 4; i++)
+#pragma unroll
+      for (uint32_t d = 0; d < 4; d++) {
+        const int vb = (int)m - (int)(16 * (c0 + i) + 4 * d);  // bytes of this word below m
+        const uint32_t mask = vb >= 4 ? 0xFFFFFFFFu : (vb <= 0 ? 0u : (1u << (8 * vb)) - 1u);
+        s = __builtin_amdgcn_sad_u8(v[i][d] & mask, 0u, s);
+      }
   }
-  for (; q < n; q++) s += p[q];
   return s;
 }
 
@@ -2488,7 +2495,8 @@ __device__ __forceinline__ void index_tile(const uint8_t* __restrict__ in, const
             u = i2;
           } else {
             u = (uint32_t)__popcll(t2.bitmap & ((1ull << i2) - 1ull));
-            uint32_t at = (orec + t2.off_pl) / 8 + sum_bytes(t2.rec + 16, u * C);
+            uint32_t at = (orec + t2.off_pl) / 8 +
+                          sum_widths(buf_rsrc(sg, (uint32_t)sbytes), orec + 16, u * C);
 #pragma unroll
             for (uint32_t j = 0; j < C; j++) {
               const uint32_t w = t2.rec[16 + u * C + j];
