@@ -2365,6 +2365,8 @@ struct DecIndexLds {
   uint32_t dblk[kTileRows * C];    // plane-word offset << 4 | width
   uint32_t boff[kTileRows * C];    // the record's block plane offsets
   uint8_t width[kTileRows * C];    // the record's block widths
+  uint16_t ofirst[kTileRows];      // the record's outliers of first occurrence u:
+  uint16_t oend[kTileRows];        //   positions [ofirst[u], oend[u]) of its sorted list
 };
 // LDS accesses of one wave complete in order; this waits for them and keeps
 // the compiler from moving accesses across.
@@ -2456,6 +2458,32 @@ __device__ __forceinline__ void index_tile(const uint8_t* __restrict__ in, const
   flags = kTileOk;
   put_tile();
 
+  // ---- the record's outliers by first occurrence (u = position / D) ----
+  // Lane-parallel over the sorted positions: a run of equal u starts where the
+  // previous position has another u and ends where the next one does.  In a
+  // corrupt stream (positions out of order or past U D) runs may come out
+  // wrong, never out of [0, nout): the patch step checks each position.
+  if (nout) {
+    x.ofirst[lane] = 0;
+    x.oend[lane] = 0;
+    lds_sync();
+    const uint32_t* op = reinterpret_cast<const uint32_t*>(rec + off_opos);
+    for (uint32_t g0 = 0; g0 < nout; g0 += 64) {
+      const uint32_t g = g0 + lane;
+      const uint32_t p = g < nout ? op[g] : 0u;
+      const uint32_t pp = g >= 1 && g - 1 < nout ? op[g - 1] : 0u;
+      const uint32_t pn = g + 1 < nout ? op[g + 1] : 0u;
+      if (g < nout) {
+        const uint32_t uo = p / D;
+        if (uo < U) {
+          if (g == 0 || pp / D != uo) x.ofirst[uo] = (uint16_t)g;
+          if (g + 1 == nout || pn / D != uo) x.oend[uo] = (uint16_t)(g + 1);
+        }
+      }
+    }
+    lds_sync();
+  }
+
   // ---- where every row's planes are ----
   if (lane < n) {
     const uint32_t i = lane, r = k * kTileRows + i;
@@ -2519,7 +2547,11 @@ __device__ __forceinline__ void index_tile(const uint8_t* __restrict__ in, const
     // the outliers of this row's first occurrence: positions [u*D, u*D + D)
     // of the sorted list of its record (values follow all onum positions)
     uint32_t ocnt = 0, ofirst = oofs;
-    if (kind == kRowPlanes && onum) {
+    if (kind == kRowPlanes && onum && local) {  // this record: from the runs above
+      const uint32_t f = x.ofirst[u], e = x.oend[u];
+      ocnt = e > f ? e - f : 0u;
+      ofirst = oofs + 4 * f;
+    } else if (kind == kRowPlanes && onum) {  // an earlier tile's record: binary search
       const uint32_t* op = reinterpret_cast<const uint32_t*>(sg + oofs);
       uint32_t lo = 0, hi2 = onum;
       while (lo < hi2) {
