@@ -2460,14 +2460,16 @@ __device__ __forceinline__ void index_tile(const uint8_t* __restrict__ in, const
 
   // ---- the record's outliers by first occurrence (u = position / D) ----
   // Lane-parallel over the sorted positions: a run of equal u starts where the
-  // previous position has another u and ends where the next one does.  In a
-  // corrupt stream (positions out of order or past U D) runs may come out
-  // wrong, never out of [0, nout): the patch step checks each position.
+  // previous position has another u and ends where the next one does.
+  // Positions must increase strictly and stay below U D, else the stream is
+  // reported corrupt (runs then may come out wrong, never out of [0, nout),
+  // and the patch step checks each position).
   if (nout) {
     x.ofirst[lane] = 0;
     x.oend[lane] = 0;
     lds_sync();
     const uint32_t* op = reinterpret_cast<const uint32_t*>(rec + off_opos);
+    bool obad = false;
     for (uint32_t g0 = 0; g0 < nout; g0 += 64) {
       const uint32_t g = g0 + lane;
       const uint32_t p = g < nout ? op[g] : 0u;
@@ -2475,12 +2477,14 @@ __device__ __forceinline__ void index_tile(const uint8_t* __restrict__ in, const
       const uint32_t pn = g + 1 < nout ? op[g + 1] : 0u;
       if (g < nout) {
         const uint32_t uo = p / D;
+        obad |= uo >= U || (g >= 1 && pp >= p);
         if (uo < U) {
           if (g == 0 || pp / D != uo) x.ofirst[uo] = (uint16_t)g;
           if (g + 1 == nout || pn / D != uo) x.oend[uo] = (uint16_t)(g + 1);
         }
       }
     }
+    if (__any(obad) && lane == 0) report_error(a.report, kDevErrCorrupt);
     lds_sync();
   }
 

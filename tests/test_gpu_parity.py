@@ -365,3 +365,82 @@ def test_hot_rows_many_duplicates(D, bits):
     x[:, 1000:1100, 5] += np.float32(1e-7)  # same codes, other bits
     x[:, 3000] = rng.normal(0, 0.1, (T, D))  # a unique row late in the segment
     assert_parity(make_cfg(T, B, D, eb_mode=1, eb=(0.02,)), x, hash_bits=bits, label=f"hot-{D}-{bits}")
+
+
+def test_corrupt_streams_are_rejected_or_decoded_like_the_oracle():
+    """The decoder validates every field it uses.  Targeted corruptions (magic,
+    truncation, wrong shape, a segment offset, a tile directory entry, a block
+    width above 12, a forward reference, an outlier position past its record's
+    rows) must be reported as corrupt, as the oracle's reader reports them;
+    random bit flips and cuts must end in OK or corrupt, and a stream the
+    oracle's reader accepts must decode to the same bits."""
+    rng = np.random.default_rng(23)
+    T, B, D = 2, 300, 128
+    x = dup_rows(rng, T, B, D, scale=0.05, frac_unique=0.3)
+    x[0, 5, 7], x[0, 5, 9], x[1, 200, 3] = 1e6, -1e6, np.nan  # outliers
+    x[1, 64:128] = rng.normal(0, 1e4, (64, D)).astype(np.float32)  # a raw tile
+    x[1, 130] = x[1, 70]  # a reference into it
+    cfg = make_cfg(T, B, D, eb_mode=0, eb=(1e-2,))
+    plan = ec.Plan(T, B, D, 1, 0, 1e-2)
+    good = O.compress(cfg, 0, x).stream
+    st = SF.parse(good)
+    y = torch.empty(T, B, D, device="cuda")
+
+    def gpu_decode(buf, plan=plan, y=y):
+        t = torch.from_numpy(np.ascontiguousarray(buf, np.uint8)).cuda()
+        y.fill_(float("nan"))
+        plan.decompress(t, y)
+        return plan.ratio(raise_on_error=False)[-1], y.cpu().numpy()
+
+    rc, yg = gpu_decode(good)
+    assert rc == ec.EC_OK
+    np.testing.assert_array_equal(yg.view(np.uint32), O.decompress(cfg, good).view(np.uint32))
+
+    seg0 = st.segments[0]
+    packed = [tl for s in st.segments for tl in s.tiles if tl.mode == 1]
+    with_refs = [tl for tl in packed if tl.n - tl.U > 0]
+    with_out = [tl for tl in packed if tl.n_out > 0]
+    assert packed and with_refs and with_out
+    cases = []
+    b = good.copy(); b[0] ^= 1; cases.append(("magic", b))
+    cases.append(("truncated", good[:-16].copy()))
+    b = good.copy(); c0 = 64 + 16; b[c0:c0 + 8] = np.frombuffer(np.uint64(1 << 40).tobytes(), np.uint8)
+    cases.append(("segment offset", b))
+    b = good.copy(); d = seg0.offset + 32 + 4 * (seg0.ntiles - 1)
+    b[d:d + 4] = np.frombuffer(np.uint32(0xFFFFFFF0).tobytes(), np.uint8); cases.append(("tile entry", b))
+    b = good.copy(); b[packed[0].offset + 16] = 13; cases.append(("width 13", b))
+    tl = with_refs[0]; nblk = (tl.U * D + 63) // 64; orf = tl.offset + (16 + nblk + 3) // 4 * 4
+    b = good.copy(); b[orf:orf + 2] = np.frombuffer(np.uint16(0xFFFF).tobytes(), np.uint8)
+    cases.append(("forward reference", b))
+    tl = with_out[0]; nblk = (tl.U * D + 63) // 64
+    oop = tl.offset + ((16 + nblk + 3) // 4 * 4 + 2 * (tl.n - tl.U) + 3) // 4 * 4
+    b = good.copy(); b[oop:oop + 4] = np.frombuffer(np.uint32(tl.U * D + 5).tobytes(), np.uint8)
+    cases.append(("outlier position", b))
+    for label, bad in cases:
+        say(f"[corrupt] {label}")
+        rc_o, _ = O.decompress(cfg, bad, status=True)
+        assert rc_o == O.ERR_CORRUPT, label
+        rc_g, _ = gpu_decode(bad)
+        assert rc_g == ec.EC_ERR_CORRUPT, label
+    say("[corrupt] wrong shape")
+    plan2 = ec.Plan(T, B + 1, D, 1, 0, 1e-2)
+    y2 = torch.empty(T, B + 1, D, device="cuda")
+    assert gpu_decode(good, plan2, y2)[0] == ec.EC_ERR_CORRUPT
+
+    n_ok = n_bad = 0
+    for i in range(60):
+        bad = good.copy()
+        for _ in range(int(rng.integers(1, 4))):
+            bad[int(rng.integers(0, bad.size))] ^= np.uint8(1 << int(rng.integers(0, 8)))
+        if i % 3 == 2:
+            bad = bad[:int(rng.integers(64, bad.size))].copy()
+        rc_o, yo = O.decompress(cfg, bad, status=True)
+        rc_g, yg = gpu_decode(bad)
+        assert rc_g in (ec.EC_OK, ec.EC_ERR_CORRUPT), (i, rc_g)
+        if rc_o == O.OK:
+            assert rc_g == ec.EC_OK, i
+            np.testing.assert_array_equal(yg.view(np.uint32), yo.view(np.uint32))
+        n_ok += rc_g == ec.EC_OK
+        n_bad += rc_g != ec.EC_OK
+    say(f"[corrupt] random: {n_ok} decoded, {n_bad} rejected")
+    assert n_bad > 0
