@@ -1845,11 +1845,14 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t v) {
   return ((uint64_t)uniform32((uint32_t)(v >> 32)) << 32) | uniform32((uint32_t)v);
 }
 
+// Stream words (read-only while decoding): through the constant address
+// space, so a wave-uniform address becomes a scalar load.
+typedef const __attribute__((address_space(4))) uint32_t const_u32;
 __device__ __forceinline__ uint64_t rd64(const uint8_t* p) {
-  return *reinterpret_cast<const uint64_t*>(p);
+  return *(const_u64*)(uintptr_t)p;
 }
 __device__ __forceinline__ uint32_t rd32(const uint8_t* p) {
-  return *reinterpret_cast<const uint32_t*>(p);
+  return *(const_u32*)(uintptr_t)p;
 }
 
 // Locate and check tile record k of a segment; every read is bounds-checked
@@ -2196,8 +2199,9 @@ __global__ void __launch_bounds__(kThreads) ec_decode_kernel(DecArgs a) {
 // ---------------------------------------------------------------------------
 // Thread 0: check the stream header, chunk table, segment header and tile
 // record of tile `ticket`; fills sh (offsets relative to `in`).
-__device__ void dec_locate(const DecArgs& a, const uint8_t* in, uint32_t ticket, DecShared& sh,
+__device__ void dec_locate(const DecArgs& a, const uint8_t* in, uint32_t ticket, DecShared& sh_out,
                            uint64_t& rec_off) {
+  DecShared sh;  // computed by the whole wave (uniform), stored by lane 0
   const uint32_t T = a.sh.T, B = a.sh.B, D = a.sh.D, P = a.sh.P;
   uint32_t s, k;
   ticket_coords(a.sh, a.seg_tile_base, ticket, s, k);
@@ -2255,6 +2259,7 @@ __device__ void dec_locate(const DecArgs& a, const uint8_t* in, uint32_t ticket,
     rec_off = (uint64_t)(tl.rec - in);
   }
   sh.ok = ok;
+  if ((threadIdx.x & 63) == 0) sh_out = sh;
 }
 
 // Decode one 64-element block (lane = element): w <= 12 planes from word
@@ -2382,10 +2387,12 @@ __device__ __forceinline__ void index_tile(const uint8_t* __restrict__ in, const
   constexpr uint32_t D = 64u * C;
   DecShared& sh = x.sh;
   const uint32_t lane = threadIdx.x & 63;
-  if (lane == 0) {
+  {
+    // every lane runs the same checks on the same (wave-uniform) words, so
+    // the reads and the arithmetic can be scalar; lane 0 stores the result
     uint64_t ro;
     dec_locate(a, in, ticket, sh, ro);
-    x.rec = ro;
+    if (lane == 0) x.rec = ro;
   }
   lds_sync();
   const uint32_t k = sh.tile, n = sh.n, rows = sh.rows;
@@ -2640,7 +2647,7 @@ __global__ void __launch_bounds__(kThreads) ec_decode_fast(const uint8_t* __rest
                                                           float* __restrict__ yout, DecArgs a) {
   constexpr uint32_t D = 64u * C;
   constexpr uint32_t kRowsPerWave = kTileRows / (kThreads / 64);  // 16
-  const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const uint32_t ticket = blockIdx.x;
   const uint32_t T = a.sh.T, B = a.sh.B;
   // tile coordinates (from the plan, not the stream)
