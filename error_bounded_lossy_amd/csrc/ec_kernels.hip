@@ -664,7 +664,7 @@ __device__ bool rows_equal(const int16_t* s_codes, const float* xs, const float*
 __global__ void __launch_bounds__(kThreads) ec_encode_kernel(EncArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ EncShared sh;
-  const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const uint32_t D = a.sh.D, T = a.sh.T;
 
   int16_t* s_codes = reinterpret_cast<int16_t*>(smem);
@@ -1962,7 +1962,7 @@ __global__ void __launch_bounds__(kThreads) ec_decode_kernel(DecArgs a) {
   __shared__ uint32_t s_xu[kTileRows];       // external: uid (BITPACK) or row (RAW)
   __shared__ uint32_t s_xbase[kTileRows];    // external: plane word offset of the row's block
   constexpr uint32_t kExt = 0x80000000u, kBad = 0x40000000u;
-  const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const uint32_t D = a.sh.D, T = a.sh.T, B = a.sh.B, P = a.sh.P;
   const uint32_t ticket = blockIdx.x;
   const uint32_t plane_cap = min(12u * D, 6144u);
