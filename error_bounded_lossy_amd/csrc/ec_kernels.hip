@@ -1120,7 +1120,6 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
   constexpr uint32_t kRB = 16 / C;                                 // rows per batch (16 blocks)
   constexpr uint32_t kNB = kRowsPerWave / kRB;                     // batches per wave
   __shared__ EncShared sh;
-  __shared__ uint32_t s_hash[kTileRows];
   __shared__ __align__(4) uint8_t s_oflag[kTileRows][C];
   const uint32_t tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const uint32_t T = a.sh.T;
@@ -1188,6 +1187,13 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
   const uint32_t lane_word = lane_blk * kStagePlanes + lane_plane;
   const uint32_t lane_m8 = lane < 32 ? 0xFFu >> (lane & 7u) : 0u;  // planes from the lane's own up
   uint32_t gm_lo = 0, gm_hi = 0;  // lane g: non-zero plane masks of block group g of the wave
+  // insertion: lane L < 16 owns the wave's row rbeg + L; its first
+  // compare-and-swap is issued as soon as its batch's row hash is known, so
+  // that its round trip overlaps the batch's bit planes
+  uint64_t* htab = a.w.hash + a.w.hash_off[s];
+  const uint32_t cap_mask = (1u << a.w.hash_log2[s]) - 1u;
+  uint32_t H = 0;      // the row's hash (tag and first slot)
+  uint64_t old0 = 0;   // what the first compare-and-swap found in that slot
 
   static_for<0, (int)kNB>([&](auto nbc) {
     constexpr uint32_t nb = decltype(nbc)::value;
@@ -1273,6 +1279,17 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
         }
       }
     }
+    {  // the batch's row hashes to their owner lanes nb kRB .. nb kRB + kRB - 1
+      const uint32_t hv = rows_reduce<kRB>(hs, lane);
+      const uint32_t h = fmix32(__shfl(hv, (int)(((lane - nb * kRB) % kRB) * (64 / kRB))));
+      if (lane >= nb * kRB && lane < nb * kRB + kRB) {
+        H = h & (uint32_t)a.hash_keep;
+        const uint32_t i = rbeg + lane;
+        if (i < n)
+          old0 = atomicCAS((unsigned long long*)&htab[H & cap_mask], 0ull,
+                           (unsigned long long)(((uint64_t)H << 32) | (uint64_t)(k * kTileRows + i + 1)));
+      }
+    }
     // bit planes, four blocks at a time (blocks 4g .. 4g+3 of the batch, in
     // (row, block) order): the low bytes of a lane's four zigzag codes go
     // through one 32x32 bit transpose per half-wave, so that lane L holds
@@ -1307,9 +1324,6 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
       const uint64_t word = ((uint64_t)hw[1] << 32) | hw[0];
       buf_st_u64(rst, above ? ((ib * C + b0) * kStagePlanes + lane_word) * 8 : kOff, word);
     });
-    const uint32_t hv = rows_reduce<kRB>(hs, lane);
-    const uint32_t h = __shfl(hv, (int)((lane % kRB) * (64 / kRB)));
-    if (lane < kRB) s_hash[ib + lane] = fmix32(h);
   });
   // widths of the wave's blocks with their outlier flags, lane-parallel:
   // lane g < 4 kNB holds block group g (blocks 4g .. 4g+3 of the wave)
@@ -1326,11 +1340,9 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
   }
 
   // ---- insert: each wave owns 16 rows (lanes 0..15); compares use the wave ----
-  uint64_t* htab = a.w.hash + a.w.hash_off[s];
-  const uint32_t cap_mask = (1u << a.w.hash_log2[s]) - 1u;
   const uint32_t i = rbeg + lane;
   bool active = lane < kRowsPerWave && i < n;
-  const uint32_t H = active ? (s_hash[i] & (uint32_t)a.hash_keep) : 0u;
+  bool first = true;  // the first attempt's result is old0
   uint32_t slot = H & cap_mask;
   const uint64_t mine = ((uint64_t)H << 32) | (uint64_t)(k * kTileRows + i + 1);
   uint32_t guard = 0;
@@ -1339,7 +1351,9 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
     bool need = false;
     uint32_t cand = 0;
     if (active) {
-      const uint64_t old = atomicCAS((unsigned long long*)&htab[slot], 0ull, (unsigned long long)mine);
+      const uint64_t old =
+          first ? old0 : atomicCAS((unsigned long long*)&htab[slot], 0ull, (unsigned long long)mine);
+      first = false;
       if (old == 0) {
         active = false;
       } else if ((uint32_t)(old >> 32) == H && (uint32_t)old - 1u < rows) {
