@@ -444,3 +444,46 @@ def test_corrupt_streams_are_rejected_or_decoded_like_the_oracle():
         n_bad += rc_g != ec.EC_OK
     say(f"[corrupt] random: {n_ok} decoded, {n_bad} rejected")
     assert n_bad > 0
+
+
+def test_graph_replays_match_eager_calls():
+    """Compression and decompression captured in HIP graphs (one per input)
+    and replayed several times, with eager calls of the same plan in between:
+    every replay's stream and output equal the eager results for its input
+    (nothing in either call allocates, clears with a memset or synchronizes)."""
+    T, B, D = 3, 1000, 128
+    rng = np.random.default_rng(31)
+    xs = [torch.from_numpy(dup_rows(rng, T, B, D, scale=sc, frac_unique=fu)).cuda()
+          for sc, fu in ((1.0, 0.4), (0.01, 0.9))]
+    xs[1][0, 7, 5] = float("nan")
+    plan = ec.Plan(T, B, D, 1, ec.EB_REL_RANGE, 0.01)
+    out = plan.empty_stream()
+    y = torch.empty(T, B, D, device="cuda")
+    refs = []
+    for i, x in enumerate(xs):
+        plan.compress(x, out, i)
+        _, nb, _ = plan.ratio()
+        plan.decompress(out[:nb], y)
+        plan.ratio()
+        refs.append((out[:nb].clone(), y.clone(), nb))
+    say("[graph] capture")
+    side = torch.cuda.Stream()
+    graphs = []
+    for i, x in enumerate(xs):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            plan.compress(x, out, i)
+            plan.decompress(out, y)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for r, i in enumerate([0, 1, 1, 0, 1, 0]):
+        say(f"[graph] replay {r} of graph {i}")
+        graphs[i].replay()
+        torch.cuda.synchronize()
+        ref_s, ref_y, nb = refs[i]
+        assert torch.equal(out[:nb], ref_s), f"replay {r}: stream"
+        assert torch.equal(y.view(torch.int32), ref_y.view(torch.int32)), f"replay {r}: values"
+        if r % 2 == 0:  # eager work of the same plan between replays
+            plan.compress(xs[1 - i], out, 1 - i)
+            plan.ratio()
+    assert plan.ratio(raise_on_error=False)[-1] == ec.EC_OK
