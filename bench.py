@@ -243,7 +243,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share; --gpus {args.gpus} is not supported "
-              f"(the all-to-all across GPUs is out of scope of this build)", file=sys.stderr)
+              f"(the library has no all-to-all across GPUs)", file=sys.stderr)
         sys.exit(2)
 
     import torch

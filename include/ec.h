@@ -60,7 +60,7 @@ typedef enum {
   EC_ERR_CORRUPT = 3,     /* stream failed validation on the device          */
   EC_ERR_DEVICE = 4,      /* HIP error or device-side time-out               */
   EC_ERR_OOM = 5,         /* host allocation failed                          */
-  EC_ERR_UNSUPPORTED = 6  /* shape beyond this build's limits (e.g. D > max) */
+  EC_ERR_UNSUPPORTED = 6  /* shape beyond the library's limits (e.g. D > max) */
 } ec_status;
 
 typedef enum {
