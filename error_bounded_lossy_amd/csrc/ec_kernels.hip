@@ -2718,12 +2718,16 @@ __global__ void __launch_bounds__(kThreads) ec_decode_fast(const uint8_t* __rest
   // every plane word of the wave's rows (planes 8-11 exist only in blocks
   // wider than 8)
   uint32_t wlo[kGroups], whi[kGroups];
+  bool wide = false;  // a block of the wave has planes 8-11
+#pragma unroll
+  for (uint32_t g = 0; g < kGroups; g++) wide = wide || (desc[g] & 15u) > 8;
+  const bool any_wide = __any(wide);
 #pragma unroll
   for (uint32_t g = 0; g < kGroups; g++) {
     const uint32_t w = desc[g] & 15u, o = desc[g] >> 4;
     const bool on = (kind[g] & 0xFFu) == kRowPlanes;
     wlo[g] = buf_ld_u32(rseg, on && gplane < w ? (2 * (o + gplane) + half) * 4 : kOff);
-    whi[g] = buf_ld_u32(rseg, on && gplane + 8 < w ? (2 * (o + 8 + gplane) + half) * 4 : kOff);
+    whi[g] = any_wide ? buf_ld_u32(rseg, on && gplane + 8 < w ? (2 * (o + 8 + gplane) + half) * 4 : kOff) : 0u;
   }
   uint32_t special = 0;  // groups with RAW copies or corrupt rows: done last
   uint32_t patch = 0;    // groups with outliers: their raw values are stored last
