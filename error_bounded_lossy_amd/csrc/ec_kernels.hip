@@ -2084,6 +2084,9 @@ __global__ void __launch_bounds__(kThreads) ec_decode_kernel(DecArgs a) {
     s_boff[b] = w;
   }
   if (badw) sh.bad = 1;
+  // the scan reads each thread's share in its own order (past 256 blocks not
+  // the one the widths were written in): every write must be visible first
+  __syncthreads();
   const uint32_t sumw = nblk ? block_exclusive_scan(s_boff, nblk, sh.part) : 0;
   const uint64_t plane_words = (tl.avail - tl.off_pl) / 8;
   const uint64_t* g_planes = reinterpret_cast<const uint64_t*>(tl.rec + tl.off_pl);

@@ -487,3 +487,25 @@ def test_graph_replays_match_eager_calls():
             plan.compress(xs[1 - i], out, 1 - i)
             plan.ratio()
     assert plan.ratio(raise_on_error=False)[-1] == ec.EC_OK
+
+
+@pytest.mark.parametrize("D", [64, 24])
+def test_segment_beyond_65536_rows(D):
+    """A segment of 70,000 rows: references are stored as 32-bit row indices,
+    and first occurrences lie up to 70,000 rows back (fast path for D = 64,
+    generic path for D = 24)."""
+    rng = np.random.default_rng(D)
+    x = dup_rows(rng, 1, 70000, D, scale=0.05, frac_unique=0.02)
+    assert_parity(make_cfg(1, 70000, D, eb_mode=1, eb=(0.01,)), x, label=f"rows>65536 D={D}")
+
+
+@pytest.mark.parametrize("D", [512, 700, 0])
+def test_large_dims(D):
+    """Large D on the generic kernels, up to the library's limit (0: the limit,
+    set by their LDS): a tile record holds more than 256 blocks, so the
+    decoder's scan of the widths reads other threads' writes."""
+    D = D or int(ec.lib().ec_max_dim())
+    say(f"[large D] D={D}")
+    rng = np.random.default_rng(5)
+    x = dup_rows(rng, 2, 130, D, scale=0.05, frac_unique=0.5)
+    assert_parity(make_cfg(2, 130, D, eb_mode=0, eb=(1e-3,)), x, label=f"large D={D}")
