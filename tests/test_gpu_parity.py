@@ -509,3 +509,19 @@ def test_large_dims(D):
     rng = np.random.default_rng(5)
     x = dup_rows(rng, 2, 130, D, scale=0.05, frac_unique=0.5)
     assert_parity(make_cfg(2, 130, D, eb_mode=0, eb=(1e-3,)), x, label=f"large D={D}")
+
+
+@pytest.mark.parametrize("D", [100, 128])
+def test_many_outliers_per_tile(D):
+    """About 5 % of the elements far outside the code range: a packed tile
+    record holds more outliers than the generic decoder stages in LDS (256),
+    and the fast decoder's outlier runs span several 64-position chunks."""
+    rng = np.random.default_rng(D + 1)
+    T, B = 2, 200
+    x = dup_rows(rng, T, B, D, scale=0.05, frac_unique=0.6)
+    hit = rng.random((T, B, D)) < 0.05
+    x[hit] = rng.choice(np.array([-1e5, 1e5], np.float32), size=int(hit.sum()))
+    cfg = make_cfg(T, B, D, eb_mode=0, eb=(1e-3,))
+    st = SF.parse(O.compress(cfg, 0, x).stream)
+    assert max(tl.n_out for s in st.segments for tl in s.tiles if tl.mode == 1) > 256
+    assert_parity(cfg, x, label=f"outliers D={D}")
