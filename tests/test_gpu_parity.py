@@ -525,3 +525,14 @@ def test_many_outliers_per_tile(D):
     st = SF.parse(O.compress(cfg, 0, x).stream)
     assert max(tl.n_out for s in st.segments for tl in s.tiles if tl.mode == 1) > 256
     assert_parity(cfg, x, label=f"outliers D={D}")
+
+
+@pytest.mark.parametrize("T,B,D,P,mode", [(300, 70, 64, 1, 1), (40, 1, 128, 1, 0), (7, 64, 256, 2, 1),
+                                          (33, 65, 128, 5, 0)])
+def test_many_small_segments(T, B, D, P, mode):
+    """Hundreds of segments of one or two tiles, one-row tables and chunks of
+    a few rows on the D = 64*C kernels: most tiles are a segment's first and
+    write its header and its entry in the chunk table."""
+    rng = np.random.default_rng(T + B + D + P)
+    x = dup_rows(rng, T, B, D, scale=0.05, frac_unique=0.5)
+    assert_parity(make_cfg(T, B, D, P, eb_mode=mode, eb=(0.01,)), x, label="small segments")
