@@ -536,3 +536,34 @@ def test_many_small_segments(T, B, D, P, mode):
     rng = np.random.default_rng(T + B + D + P)
     x = dup_rows(rng, T, B, D, scale=0.05, frac_unique=0.5)
     assert_parity(make_cfg(T, B, D, P, eb_mode=mode, eb=(0.01,)), x, label="small segments")
+
+
+@pytest.mark.parametrize("D,P", [(128, 1), (256, 2), (24, 1)])
+def test_rel_mode_with_classes_and_staircase(D, P):
+    """Range-relative eb with per-table class multipliers (Algorithm 1's
+    large / medium / small tables) and the staircase decay, mid-schedule."""
+    rng = np.random.default_rng(D * 3 + P)
+    T, B = 4, 300
+    x = dup_rows(rng, T, B, D, scale=0.05, frac_unique=0.5)
+    x[1] *= 40.0  # tables with different ranges
+    sched = {"kind": ec.SCHED_STEP, "k": 4.0, "phase": 100, "steps": 3}
+    cfg = make_cfg(T, B, D, P, eb_mode=1, eb=[0.01, 0.02, 0.005, 0.01], mult=[1.0, 1.5, 0.5, 2.0],
+                   sched=sched)
+    assert_parity(cfg, x, it=60, sched=sched, label="rel+classes+step")
+
+
+def test_special_values_wide_rows():
+    """NaN payloads, infinities, signed zeros, an all-NaN table (stored raw)
+    and a constant table at D = 256."""
+    rng = np.random.default_rng(17)
+    T, B, D = 3, 90, 256
+    x = rng.normal(0, 1, (T, B, D)).astype(np.float32)
+    x[0, 3, 200] = np.nan
+    x[0, 4, 7] = np.inf
+    x[0, 5, 255] = -np.inf
+    x[0, 6, 3] = -0.0
+    x[0, 7] = np.float32(np.uint32(0x7FC00123).view(np.float32))
+    x[0, 70] = x[0, 7]
+    x[1] = np.nan
+    x[2] = 0.25
+    assert_parity(make_cfg(T, B, D, eb_mode=1, eb=(0.01,)), x, label="special D=256")
