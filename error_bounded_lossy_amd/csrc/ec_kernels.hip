@@ -2214,8 +2214,9 @@ __global__ void __launch_bounds__(kThreads) ec_decode_kernel(DecArgs a) {
 // arguments, so the wave-uniform bit-plane loads become scalar loads and each
 // plane costs one conditional select per element (codes built MSB first).
 // ---------------------------------------------------------------------------
-// Thread 0: check the stream header, chunk table, segment header and tile
-// record of tile `ticket`; fills sh (offsets relative to `in`).
+// One whole wave (every lane computes the same): check the stream header,
+// chunk table, segment header and tile record of tile `ticket`; lane 0 fills
+// sh_out (offsets relative to `in`).
 __device__ void dec_locate(const DecArgs& a, const uint8_t* in, uint32_t ticket, DecShared& sh_out,
                            uint64_t& rec_off) {
   DecShared sh;  // computed by the whole wave (uniform), stored by lane 0
