@@ -18,7 +18,7 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libebl_oracle.so")
-SOURCES = [os.path.join(HERE, "ebl_oracle.c")]
+SOURCES = [os.path.join(HERE, "ebl_oracle.c"), os.path.join(HERE, "ebl_huffman.c")]
 
 EB_ABS, EB_REL = 0, 1
 SCHED_NONE, SCHED_INV_SQRT, SCHED_STEP = 0, 1, 2
@@ -87,6 +87,22 @@ def lib():
         L.ebo_decompress.restype = ctypes.c_int
         L.ebo_decompress.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint32,
                                      ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, f32p]
+        u8p, u16p, u32p = (ctypes.POINTER(t) for t in (ctypes.c_uint8, ctypes.c_uint16,
+                                                        ctypes.c_uint32))
+        L.ebo_huff_lengths.restype = ctypes.c_int
+        L.ebo_huff_lengths.argtypes = [ctypes.POINTER(ctypes.c_uint64), u8p]
+        L.ebo_huff_codes.restype = None
+        L.ebo_huff_codes.argtypes = [u8p, u32p]
+        L.ebo_huff_encode.restype = ctypes.c_size_t
+        L.ebo_huff_encode.argtypes = [u16p, ctypes.c_size_t, u8p, u32p, u32p, u32p]
+        L.ebo_huff_decode.restype = ctypes.c_int
+        L.ebo_huff_decode.argtypes = [u32p, ctypes.c_size_t, u32p, ctypes.c_size_t, u8p, u16p]
+        L.ebo_huff_book_bytes.restype = ctypes.c_size_t
+        L.ebo_huff_book_bytes.argtypes = [u8p]
+        L.ebo_huff_book_write.restype = ctypes.c_size_t
+        L.ebo_huff_book_write.argtypes = [u8p, u8p]
+        L.ebo_huff_book_read.restype = ctypes.c_int
+        L.ebo_huff_book_read.argtypes = [u8p, ctypes.c_size_t, u8p]
         _lib = L
     return _lib
 
@@ -220,3 +236,76 @@ def decompress(cfg: Config, stream: np.ndarray, status: bool = False):
     if rc != OK:
         raise RuntimeError(f"oracle decompress failed with status {rc}")
     return y
+
+
+# --- canonical Huffman coder (ebl_huffman.c) -------------------------------
+HUFF_NSYM, HUFF_MAXLEN, HUFF_CHUNK = 4095, 12, 256
+
+
+def _p(a: np.ndarray, t):
+    return a.ctypes.data_as(ctypes.POINTER(t))
+
+
+def huff_lengths(freq) -> np.ndarray:
+    """Code lengths (uint8 [4095], 0 = unused) from symbol frequencies."""
+    f = np.zeros(HUFF_NSYM, np.uint64)
+    fr = np.asarray(freq, dtype=np.uint64).reshape(-1)
+    f[: fr.size] = fr
+    ln = np.zeros(HUFF_NSYM, np.uint8)
+    lib().ebo_huff_lengths(_p(f, ctypes.c_uint64), _p(ln, ctypes.c_uint8))
+    return ln
+
+
+def huff_codes(lengths) -> np.ndarray:
+    ln = np.zeros(HUFF_NSYM, np.uint8)
+    l = np.asarray(lengths, dtype=np.uint8).reshape(-1)
+    ln[: l.size] = l
+    code = np.zeros(HUFF_NSYM, np.uint32)
+    lib().ebo_huff_codes(_p(ln, ctypes.c_uint8), _p(code, ctypes.c_uint32))
+    return code
+
+
+def huff_encode(sym, lengths):
+    """Encode uint16 symbols; returns (words uint32, chunk offsets uint32)."""
+    s = np.ascontiguousarray(sym, dtype=np.uint16).reshape(-1)
+    ln = np.ascontiguousarray(lengths, dtype=np.uint8)
+    code = huff_codes(ln)
+    n = s.size
+    nch = (n + HUFF_CHUNK - 1) // HUFF_CHUNK
+    words = np.zeros(HUFF_MAXLEN * n // 32 + nch + 1, np.uint32)
+    off = np.zeros(nch + 1, np.uint32)
+    nw = lib().ebo_huff_encode(_p(s, ctypes.c_uint16), n, _p(ln, ctypes.c_uint8),
+                               _p(code, ctypes.c_uint32), _p(words, ctypes.c_uint32),
+                               _p(off, ctypes.c_uint32))
+    return words[:nw].copy(), off
+
+
+def huff_decode(words, chunk_off, n, lengths, status: bool = False):
+    w = np.ascontiguousarray(words, dtype=np.uint32)
+    o = np.ascontiguousarray(chunk_off, dtype=np.uint32)
+    ln = np.ascontiguousarray(lengths, dtype=np.uint8)
+    assert o.size == (n + HUFF_CHUNK - 1) // HUFF_CHUNK + 1
+    out = np.zeros(n, np.uint16)
+    w1 = w if w.size else np.zeros(1, np.uint32)
+    rc = lib().ebo_huff_decode(_p(w1, ctypes.c_uint32), w.size, _p(o, ctypes.c_uint32), n,
+                               _p(ln, ctypes.c_uint8), _p(out, ctypes.c_uint16))
+    if status:
+        return rc, out
+    if rc != 0:
+        raise RuntimeError("oracle Huffman decode: malformed chunk")
+    return out
+
+
+def huff_book_write(lengths) -> np.ndarray:
+    ln = np.ascontiguousarray(lengths, dtype=np.uint8)
+    out = np.zeros(lib().ebo_huff_book_bytes(_p(ln, ctypes.c_uint8)), np.uint8)
+    lib().ebo_huff_book_write(_p(ln, ctypes.c_uint8), _p(out, ctypes.c_uint8))
+    return out
+
+
+def huff_book_read(book):
+    b = np.ascontiguousarray(book, dtype=np.uint8)
+    b1 = b if b.size else np.zeros(1, np.uint8)
+    ln = np.zeros(HUFF_NSYM, np.uint8)
+    rc = lib().ebo_huff_book_read(_p(b1, ctypes.c_uint8), b.size, _p(ln, ctypes.c_uint8))
+    return rc, ln

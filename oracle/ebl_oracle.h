@@ -137,6 +137,37 @@ int ebo_compress(const ebo_cfg* c, int64_t iter, const float* x, uint8_t* out, s
 int ebo_decompress(const uint8_t* s, size_t nbytes, uint32_t T, uint32_t B, uint32_t D,
                    uint32_t P, float* y);
 
+/*
+ * Canonical Huffman coder of the quantization codes (ebl_huffman.c): the
+ * entropy stage of section III-D, with the construction, length limit, bit
+ * order and codebook layout fixed as described in that file's header.
+ * Symbols are q + 2047 (EBO_HUFF_NSYM of them); codes are at most
+ * EBO_HUFF_MAXLEN bits; every EBO_HUFF_CHUNK symbols start a new 32-bit word.
+ */
+#define EBO_HUFF_NSYM 4095
+#define EBO_HUFF_MAXLEN 12
+#define EBO_HUFF_CHUNK 256
+
+/* Code lengths (0 = unused) from symbol frequencies; returns the number of
+   used symbols.  One used symbol gets length 1. */
+int ebo_huff_lengths(const uint64_t* freq, uint8_t* len);
+/* Canonical code of every symbol (RFC 1951 section 3.2.2), right-aligned. */
+void ebo_huff_codes(const uint8_t* len, uint32_t* code);
+/* Encode n symbols; chunk_off gets ceil(n/256)+1 word offsets (the last is
+   the word count, which is returned).  words must hold 12*n/32 + n/256 + 1. */
+size_t ebo_huff_encode(const uint16_t* sym, size_t n, const uint8_t* len, const uint32_t* code,
+                       uint32_t* words, uint32_t* chunk_off);
+/* Decode n symbols; 0, or -1 if any chunk is malformed (a code that is not in
+   the book, a chunk that does not end in its last word, nonzero padding). */
+int ebo_huff_decode(const uint32_t* words, size_t nwords, const uint32_t* chunk_off, size_t n,
+                    const uint8_t* len, uint16_t* sym);
+/* Codebook: u16 lowest used symbol, u16 highest, 4-bit lengths low nibble
+   first.  No used symbol is stored as lo = 1, hi = 0. */
+size_t ebo_huff_book_bytes(const uint8_t* len);
+size_t ebo_huff_book_write(const uint8_t* len, uint8_t* out);
+/* 0, or -1 for a book that is short, not tight, or not a complete code. */
+int ebo_huff_book_read(const uint8_t* in, size_t nbytes, uint8_t* len);
+
 #ifdef __cplusplus
 }
 #endif
