@@ -15,7 +15,7 @@ import re
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_PATH = os.path.join(HERE, "libec.so")
-HEADER = os.path.join(ROOT, "include", "ec.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("ec.h", "ec_huffman.h")]
 
 EC_OK, EC_ERR_INVALID, EC_ERR_CAPACITY, EC_ERR_CORRUPT = 0, 1, 2, 3
 EC_ERR_DEVICE, EC_ERR_OOM, EC_ERR_UNSUPPORTED = 4, 5, 6
@@ -87,16 +87,30 @@ def lib():
     L.ec_profile_read.restype = st
     L.ec_profile_read.argtypes = [vp, st, ctypes.POINTER(ctypes.c_double),
                                   ctypes.POINTER(ctypes.c_uint64)]
+    u64 = ctypes.c_uint64
+    L.ec_huff_workspace_bytes.restype = sz
+    L.ec_huff_workspace_bytes.argtypes = []
+    L.ec_huff_max_words.restype = u64
+    L.ec_huff_max_words.argtypes = [u64]
+    L.ec_huff_encode.restype = st
+    L.ec_huff_encode.argtypes = [vp, u64, vp, vp, vp, u64, vp, sz, vp]
+    L.ec_huff_decode.restype = st
+    L.ec_huff_decode.argtypes = [vp, u64, vp, vp, u64, u64, vp, vp, sz, vp]
+    L.ec_huff_status.restype = st
+    L.ec_huff_status.argtypes = [vp, vp]
     _lib = L
     return L
 
 
 def declared_functions() -> list[str]:
-    """Names of the functions include/ec.h declares."""
-    with open(HEADER) as f:
-        text = f.read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ec_[a-z_]+)\s*\(", text)))
+    """Names of the functions the headers under include/ declare."""
+    names = set()
+    for h in HEADERS:
+        with open(h) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(ec_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def status_string(status: int) -> str:
@@ -233,3 +247,66 @@ class Plan:
         _check(lib().ec_profile_read(self._h, int(kernel), ctypes.byref(ms), ctypes.byref(n)),
                "ec_profile_read")
         return ms.value, int(n.value)
+
+
+# --- canonical Huffman coder (include/ec_huffman.h) ------------------------
+HUFF_NSYM, HUFF_MAXLEN, HUFF_CHUNK, HUFF_BOOK_MAX = 4095, 12, 256, 2052
+
+
+def huff_max_words(n: int) -> int:
+    return int(lib().ec_huff_max_words(int(n)))
+
+
+def huff_book_bytes(header4) -> int:
+    """Codebook size from its first 4 bytes (u16 lowest, u16 highest symbol)."""
+    b = [int(v) for v in header4[:4]]
+    lo, hi = b[0] | b[1] << 8, b[2] | b[3] << 8
+    return 4 if hi < lo else 4 + (hi - lo + 2) // 2
+
+
+class Huffman:
+    """Workspace holder for ec_huff_encode / ec_huff_decode on one device.
+
+    Symbols travel as int16 tensors (bit patterns of the u16 symbols), words
+    and chunk offsets as int32 tensors (bit patterns of u32)."""
+
+    def __init__(self, device=None):
+        import torch
+        self.device = torch.device(device or "cuda")
+        nbytes = int(lib().ec_huff_workspace_bytes())
+        self.workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
+        base = self.workspace.data_ptr()
+        self._work = (base + 255) // 256 * 256
+        self._work_bytes = nbytes
+
+    def buffers(self, n: int):
+        import torch
+        nch = (n + HUFF_CHUNK - 1) // HUFF_CHUNK
+        book = torch.zeros(HUFF_BOOK_MAX, dtype=torch.uint8, device=self.device)
+        off = torch.zeros(nch + 1, dtype=torch.int32, device=self.device)
+        words = torch.zeros(max(huff_max_words(n), 1), dtype=torch.int32, device=self.device)
+        return book, off, words
+
+    def encode(self, sym, book, chunk_off, words, stream=None):
+        """Enqueue encoding of the int16 tensor `sym` (symbols 0..4094)."""
+        import torch
+        assert sym.dtype == torch.int16 and sym.is_contiguous()
+        n = sym.numel()
+        assert book.numel() >= HUFF_BOOK_MAX and chunk_off.numel() >= (n + 255) // 256 + 1
+        _check(lib().ec_huff_encode(sym.data_ptr() if n else None, n, book.data_ptr(),
+                                    chunk_off.data_ptr(), words.data_ptr(), words.numel(),
+                                    self._work, self._work_bytes, _stream_handle(stream)),
+               "ec_huff_encode")
+
+    def decode(self, book, book_bytes: int, chunk_off, words, n: int, sym, stream=None):
+        """Enqueue decoding of n symbols into the int16 tensor `sym`."""
+        import torch
+        assert sym.dtype == torch.int16 and sym.is_contiguous() and sym.numel() >= n
+        _check(lib().ec_huff_decode(book.data_ptr(), int(book_bytes), chunk_off.data_ptr(),
+                                    words.data_ptr() if words.numel() else None, words.numel(),
+                                    n, sym.data_ptr() if n else None, self._work,
+                                    self._work_bytes, _stream_handle(stream)), "ec_huff_decode")
+
+    def status(self, stream=None) -> int:
+        """Wait for the stream; status of the last call on this workspace."""
+        return int(lib().ec_huff_status(self._work, _stream_handle(stream)))

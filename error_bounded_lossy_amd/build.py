@@ -13,7 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libec.so")
-SOURCES = [os.path.join(CSRC, "ec_kernels.hip"), os.path.join(CSRC, "ec_runtime.cpp")]
+SOURCES = [os.path.join(CSRC, "ec_kernels.hip"), os.path.join(CSRC, "ec_huffman.hip"),
+           os.path.join(CSRC, "ec_runtime.cpp")]
 ARCH = os.environ.get("EC_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

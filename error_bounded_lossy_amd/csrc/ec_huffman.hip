@@ -1,0 +1,715 @@
+// ec_huffman.hip -- canonical Huffman coder of quantization codes on gfx950
+// (the lossless stage after the quantization encoder, arXiv 2407.04272
+// section III-D "Huffman Encoding").  The stream layout and the rules that
+// make the code unique are documented in include/ec_huffman.h.
+//
+// Encode: five launches on one stream.
+//   clear   zero the histogram and the status word
+//   hist    per-workgroup LDS histograms, merged by global atomics
+//   book    one workgroup: sort the used symbols by frequency (bitonic, LDS),
+//           build the tree with two queues (one lane, LDS), depths by pointer
+//           jumping, length limit, lengths by rank, canonical codes by a
+//           packed prefix count, codebook bytes
+//   size    one wave per 256-symbol chunk: word count of the chunk
+//   write   groups of chunks: offsets by a scan, then one wave per chunk packs
+//           its codes (wave prefix of bit counts, LDS OR into a 96-word
+//           buffer) and stores whole words
+// Decode: two launches.
+//   dec_book  one workgroup: validate the codebook, canonical codes, a
+//             4096-entry table from every 12-bit prefix to (symbol, length)
+//   decode    128 chunks per workgroup: their words staged through LDS with
+//             coalesced loads, then one lane per chunk decodes by table
+//             lookups and checks that the chunk ends exactly in its last word.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ec.h"
+#include "ec_huffman.h"
+
+namespace {
+
+constexpr int kNsym = (int)EC_HUFF_NSYM;      // 4095
+constexpr int kMaxLen = (int)EC_HUFF_MAXLEN;  // 12
+constexpr int kChunk = (int)EC_HUFF_CHUNK;    // 256
+constexpr int kTable = 4096;                  // alphabet + one bin for invalid symbols
+constexpr int kChunkWords = kChunk * kMaxLen / 32;  // 96: most words a chunk can take
+constexpr int kMaxGroups = 2048;                    // chunk groups of size / write
+constexpr int kMaxDepth = 64;  // a tree over fewer than 2^31 symbols is shallower
+constexpr int kBookThreads = 1024;
+constexpr int kThreads = 256;
+constexpr int kDecChunks = 128;  // chunks (and lanes) per decode workgroup
+
+enum : uint32_t { kStBadSymbol = 1u, kStCorrupt = 2u, kStDepth = 4u };
+
+// Workspace layout (bytes from the 256-byte aligned base).
+constexpr size_t kOffStatus = 0;                       // u32 [2]: status bits, book valid
+constexpr size_t kOffHist = 256;                       // u32 [4096]
+constexpr size_t kOffEnc = kOffHist + 4 * kTable;      // u32 [4096]: len << 16 | code
+constexpr size_t kOffLut = kOffEnc + 4 * kTable;       // u16 [4096]: sym | len << 12
+constexpr size_t kOffGroups = kOffLut + 2 * kTable;    // u32 [kMaxGroups]
+constexpr size_t kWorkBytes = kOffGroups + 4 * kMaxGroups;
+
+struct Ws {
+  uint32_t* status;
+  uint32_t* hist;
+  uint32_t* enc;
+  uint16_t* lut;
+  uint32_t* groups;
+};
+
+Ws ws_of(void* base) {
+  uint8_t* b = static_cast<uint8_t*>(base);
+  return Ws{reinterpret_cast<uint32_t*>(b + kOffStatus), reinterpret_cast<uint32_t*>(b + kOffHist),
+            reinterpret_cast<uint32_t*>(b + kOffEnc), reinterpret_cast<uint16_t*>(b + kOffLut),
+            reinterpret_cast<uint32_t*>(b + kOffGroups)};
+}
+
+__device__ __forceinline__ void status_or(uint32_t* st, uint32_t bits) {
+  __hip_atomic_fetch_or(st, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & 63u; }
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
+  return x;
+}
+
+// Inclusive prefix sum over the wave.
+__device__ __forceinline__ uint32_t wave_incl(uint32_t x) {
+  const uint32_t ln = lane_id();
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = __shfl_up(x, d, 64);
+    if (ln >= (uint32_t)d) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ uint64_t wave_incl64(uint64_t x) {
+  const uint32_t ln = lane_id();
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint64_t y = __shfl_up(x, d, 64);
+    if (ln >= (uint32_t)d) x += y;
+  }
+  return x;
+}
+
+// Exclusive prefix sum over the workgroup (blockDim.x threads, a multiple of
+// 64, at most 1024); *total gets the sum.  part holds 16 entries.
+__device__ uint32_t block_excl(uint32_t x, uint32_t* part, uint32_t* total) {
+  const uint32_t wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const uint32_t inc = wave_incl(x);
+  __syncthreads();
+  if (lane_id() == 63) part[wv] = inc;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+  for (uint32_t i = 0; i < nw; i++) {
+    const uint32_t v = part[i];
+    before += i < wv ? v : 0;
+    all += v;
+  }
+  *total = all;
+  return before + inc - x;
+}
+
+// Canonical codes (RFC 1951 section 3.2.2): the code of symbol s with length
+// l is first[l] plus the number of symbols below s that have length l.  Each
+// thread owns kTable / blockDim.x consecutive symbols; the per-length counts
+// travel as twelve 16-bit fields packed in three u64 (no field exceeds 4095,
+// so no carry crosses a field).  enc[s] = len << 16 | code, 0 if unused.
+__device__ void canonical_codes(const uint8_t* len, const uint32_t* first, uint32_t* enc,
+                                uint64_t (*part)[3]) {
+  const uint32_t per = kTable / blockDim.x;
+  const uint32_t s0 = threadIdx.x * per;
+  uint64_t c[3] = {0, 0, 0};
+  for (uint32_t k = 0; k < per; k++) {
+    const uint32_t l = len[s0 + k];
+    if (l) c[(l - 1) >> 2] += 1ull << (16 * ((l - 1) & 3));
+  }
+  const uint32_t wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  uint64_t inc[3];
+  for (int k = 0; k < 3; k++) inc[k] = wave_incl64(c[k]);
+  if (lane_id() == 63)
+    for (int k = 0; k < 3; k++) part[wv][k] = inc[k];
+  __syncthreads();
+  uint64_t e[3];
+  for (int k = 0; k < 3; k++) {
+    uint64_t before = 0;
+    for (uint32_t i = 0; i < wv; i++) before += part[i][k];
+    e[k] = before + inc[k] - c[k];
+  }
+  (void)nw;
+  for (uint32_t k = 0; k < per; k++) {
+    const uint32_t s = s0 + k, l = len[s];
+    uint32_t v = 0;
+    if (l) {
+      const int f = (l - 1) >> 2, sh = 16 * ((l - 1) & 3);
+      const uint32_t rank = (uint32_t)(e[f] >> sh) & 0xFFFFu;
+      e[f] += 1ull << sh;
+      v = (l << 16) | (first[l] + rank);
+    }
+    enc[s] = v;
+  }
+}
+
+__global__ void __launch_bounds__(kThreads) huff_clear(Ws w) {
+  const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+  if (i < (uint32_t)kTable) w.hist[i] = 0;
+  if (i < 2) w.status[i] = 0;
+}
+
+__global__ void __launch_bounds__(kThreads) huff_hist(const uint16_t* __restrict__ sym, uint64_t n,
+                                                      Ws w) {
+  __shared__ uint32_t h[kTable];
+  for (int i = threadIdx.x; i < kTable; i += kThreads) h[i] = 0;
+  __syncthreads();
+  auto add = [&](uint32_t s) { atomicAdd(&h[s < (uint32_t)kNsym ? s : (uint32_t)kNsym], 1u); };
+  const uint64_t nv = n >> 3, stride = (uint64_t)gridDim.x * kThreads;
+  const uint4* v = reinterpret_cast<const uint4*>(sym);
+  for (uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x; i < nv; i += stride) {
+    const uint4 q = v[i];
+    const uint32_t x[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      add(x[k] & 0xFFFFu);
+      add(x[k] >> 16);
+    }
+  }
+  for (uint64_t i = (nv << 3) + (uint64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride)
+    add(sym[i]);
+  __syncthreads();
+  for (int i = threadIdx.x; i < kTable; i += kThreads)
+    if (h[i]) atomicAdd(&w.hist[i], h[i]);
+}
+
+__global__ void __launch_bounds__(kBookThreads) huff_book(Ws w, uint8_t* __restrict__ book,
+                                                          uint32_t* __restrict__ chunk_off,
+                                                          uint64_t n) {
+  __shared__ uint64_t key[kTable];
+  __shared__ uint32_t wt[2 * kTable];
+  __shared__ uint32_t pr[2 * kTable];  // parent while building; then ancestor | distance << 16
+  __shared__ uint16_t syms[kTable];
+  __shared__ uint8_t len[kTable];
+  __shared__ uint32_t bits[kMaxDepth];
+  __shared__ uint32_t first[kMaxLen + 1], cum[kMaxLen + 1];
+  __shared__ uint64_t part[16][3];
+  __shared__ int s_m, s_lo, s_hi;
+  const int t = threadIdx.x;
+
+  if (t == 0) {
+    s_m = 0;
+    s_lo = kTable;
+    s_hi = -1;
+  }
+  if (t < kMaxDepth) bits[t] = 0;
+  __syncthreads();
+  // keys: frequency, then the complement of the symbol (so that reading the
+  // sorted keys backwards gives decreasing frequency, then increasing symbol)
+  int cm = 0, lo = kTable, hi = -1;
+  for (int s = t; s < kTable; s += kBookThreads) {
+    const uint32_t f = w.hist[s];
+    uint64_t k = ~0ull;
+    if (s < kNsym && f) {
+      k = ((uint64_t)f << 12) | (uint64_t)(4095 - s);
+      cm++;
+      lo = min(lo, s);
+      hi = max(hi, s);
+    }
+    if (s == kNsym && f) status_or(w.status, kStBadSymbol);
+    key[s] = k;
+    len[s] = 0;
+  }
+  if (cm) {
+    atomicAdd(&s_m, cm);
+    atomicMin(&s_lo, lo);
+    atomicMax(&s_hi, hi);
+  }
+  __syncthreads();
+  const int m = s_m;
+
+  if (m >= 2) {
+    for (int size = 2; size <= kTable; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int p = t; p < kTable / 2; p += kBookThreads) {
+          const int i = (p / stride) * 2 * stride + (p % stride), j = i + stride;
+          const bool asc = (i & size) == 0;
+          const uint64_t a = key[i], b = key[j];
+          if ((a > b) == asc) {
+            key[i] = b;
+            key[j] = a;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int i = t; i < m; i += kBookThreads) {
+      const uint64_t k = key[i];
+      wt[i] = (uint32_t)(k >> 12);
+      syms[i] = (uint16_t)(4095 - (uint32_t)(k & 0xFFFu));
+    }
+    __syncthreads();
+    // two queues: sorted leaves [0, m) and internal nodes [m, nx) in creation
+    // order; of two equal weights the leaf is taken first
+    if (t == 0) {
+      const int nn = 2 * m - 1;
+      int lq = 0, iq = m;
+      for (int nx = m; nx < nn; nx++) {
+        uint32_t sum = 0;
+        for (int k = 0; k < 2; k++) {
+          const bool leaf = lq < m && (iq >= nx || wt[lq] <= wt[iq]);
+          const int p = leaf ? lq++ : iq++;
+          sum += wt[p];
+          pr[p] = (uint32_t)nx;
+        }
+        wt[nx] = sum;
+      }
+    }
+    __syncthreads();
+    const int nn = 2 * m - 1, root = nn - 1;
+    for (int v = t; v < nn; v += kBookThreads) pr[v] = v == root ? (uint32_t)root : (pr[v] | 1u << 16);
+    __syncthreads();
+    // pointer jumping: every pair (ancestor, distance) stays true, and each
+    // round at least doubles the distance until the root is reached
+    for (int r = 0; r < 13; r++) {
+      for (int v = t; v < nn; v += kBookThreads) {
+        const uint32_t x = pr[v], y = pr[x & 0xFFFFu];
+        pr[v] = (y & 0xFFFFu) | (((x >> 16) + (y >> 16)) << 16);
+      }
+      __syncthreads();
+    }
+    for (int v = t; v < m; v += kBookThreads) {
+      const uint32_t d = pr[v] >> 16;
+      if (d < (uint32_t)kMaxDepth) atomicAdd(&bits[d], 1u);
+      else status_or(w.status, kStDepth);
+    }
+  } else if (m == 1 && t == 0) {
+    bits[1] = 1;
+    syms[0] = (uint16_t)s_lo;
+  }
+  __syncthreads();
+  if (t == 0) {
+    // ITU-T T.81 Annex K.3: while a code is longer than the limit, take two
+    // codes of the longest length i: one moves to length i-1 (next to its
+    // prefix), and the other becomes a sibling of a code of the longest
+    // length j < i-1 that exists, which moves to j+1 with it
+    for (int i = kMaxDepth - 1; i > kMaxLen;) {
+      if (bits[i]) {
+        int j = i - 2;
+        while (bits[j] == 0) j--;
+        bits[i] -= 2;
+        bits[i - 1] += 1;
+        bits[j + 1] += 2;
+        bits[j] -= 1;
+      } else {
+        i--;
+      }
+    }
+    cum[0] = 0;
+    first[0] = 0;
+    uint32_t code = 0;
+    for (int l = 1; l <= kMaxLen; l++) {
+      cum[l] = cum[l - 1] + bits[l];
+      if (l > 1) code = (code + bits[l - 1]) << 1;
+      first[l] = code;
+    }
+  }
+  __syncthreads();
+  // rank r (decreasing frequency, then increasing symbol) is the sorted key
+  // m-1-r; ranks take the lengths shortest first
+  for (int r = t; r < m; r += kBookThreads) {
+    int l = 1;
+    while (l < kMaxLen && cum[l] <= (uint32_t)r) l++;
+    len[syms[m - 1 - r]] = (uint8_t)l;
+  }
+  __syncthreads();
+  canonical_codes(len, first, w.enc, part);
+
+  // codebook bytes
+  if (m == 0) {
+    if (t < 4) book[t] = (uint8_t)(t == 0 ? 1 : 0);
+  } else {
+    const int blo = s_lo, bhi = s_hi, nb = bhi - blo + 1;
+    if (t == 0) {
+      book[0] = (uint8_t)blo;
+      book[1] = (uint8_t)(blo >> 8);
+      book[2] = (uint8_t)bhi;
+      book[3] = (uint8_t)(bhi >> 8);
+    }
+    for (int b = t; b < (nb + 1) / 2; b += kBookThreads) {
+      const int s = blo + 2 * b;
+      const uint32_t lo4 = len[s], hi4 = s + 1 <= bhi ? len[s + 1] : 0u;
+      book[4 + b] = (uint8_t)(lo4 | hi4 << 4);
+    }
+  }
+  if (n == 0 && t == 0) chunk_off[0] = 0;
+}
+
+__global__ void __launch_bounds__(kThreads) huff_size(const uint16_t* __restrict__ sym, uint64_t n,
+                                                      Ws w, uint32_t* __restrict__ chunk_off,
+                                                      uint32_t nch, uint32_t per_group) {
+  __shared__ uint8_t lens[kTable];
+  __shared__ uint32_t wsum[kThreads / 64];
+  for (int i = threadIdx.x; i < kTable; i += kThreads) lens[i] = (uint8_t)(w.enc[i] >> 16);
+  __syncthreads();
+  const uint32_t wv = threadIdx.x >> 6, ln = lane_id();
+  const uint32_t c0 = blockIdx.x * per_group, c1 = min(c0 + per_group, nch);
+  uint32_t gsum = 0;
+  for (uint32_t c = c0 + wv; c < c1; c += kThreads / 64) {
+    const uint64_t base = (uint64_t)c * kChunk;
+    const uint64_t cnt = min((uint64_t)kChunk, n - base);
+    uint32_t b = 0;
+    if (cnt == (uint64_t)kChunk) {
+      const uint2 q = reinterpret_cast<const uint2*>(sym + base)[ln];
+      b = lens[min(q.x & 0xFFFFu, 4095u)] + lens[min(q.x >> 16, 4095u)] +
+          lens[min(q.y & 0xFFFFu, 4095u)] + lens[min(q.y >> 16, 4095u)];
+    } else {
+      for (uint32_t k = 0; k < 4; k++) {
+        const uint32_t i = ln * 4 + k;
+        if (i < cnt) b += lens[min((uint32_t)sym[base + i], 4095u)];
+      }
+    }
+    const uint32_t words = (wave_sum(b) + 31) >> 5;
+    if (ln == 0) chunk_off[c + 1] = words;
+    gsum += words;
+  }
+  if (ln == 0) wsum[wv] = gsum;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t s = 0;
+    for (int i = 0; i < kThreads / 64; i++) s += wsum[i];
+    w.groups[blockIdx.x] = s;
+  }
+}
+
+__global__ void __launch_bounds__(kThreads) huff_write(const uint16_t* __restrict__ sym, uint64_t n,
+                                                       Ws w, uint32_t* __restrict__ chunk_off,
+                                                       uint32_t nch, uint32_t per_group,
+                                                       uint32_t* __restrict__ words) {
+  __shared__ uint32_t enc[kTable];
+  __shared__ uint32_t offs[kThreads];
+  __shared__ uint32_t buf[kThreads / 64][kChunkWords];
+  __shared__ uint32_t part[16];
+  const uint32_t t = threadIdx.x, wv = t >> 6, ln = lane_id();
+  for (int i = t; i < kTable; i += kThreads) enc[i] = w.enc[i];
+  for (int i = t; i < kChunkWords * (kThreads / 64); i += kThreads) (&buf[0][0])[i] = 0;
+  // words of all groups before this one
+  uint32_t before = 0;
+  for (uint32_t g = t; g < blockIdx.x; g += kThreads) before += w.groups[g];
+  uint32_t base;
+  block_excl(before, part, &base);
+  const uint32_t c0 = blockIdx.x * per_group, c1 = min(c0 + per_group, nch);
+  if (blockIdx.x == 0 && t == 0) chunk_off[0] = 0;
+  for (uint32_t r0 = c0; r0 < c1; r0 += kThreads) {
+    const uint32_t c = r0 + t;
+    const uint32_t cw = c < c1 ? chunk_off[c + 1] : 0u;
+    uint32_t total;
+    const uint32_t ex = block_excl(cw, part, &total);
+    if (c < c1) chunk_off[c + 1] = base + ex + cw;
+    offs[t] = base + ex;
+    base += total;
+    __syncthreads();
+    for (uint32_t j0 = 0; j0 < (uint32_t)kThreads; j0 += kThreads / 64) {
+      const uint32_t j = j0 + wv, cc = r0 + j;
+      const bool active = cc < c1;
+      uint32_t nbits_wave = 0;
+      if (active) {
+        const uint64_t sbase = (uint64_t)cc * kChunk;
+        const uint64_t cnt = min((uint64_t)kChunk, n - sbase);
+        uint32_t s[4];
+        if (cnt == (uint64_t)kChunk) {
+          const uint2 q = reinterpret_cast<const uint2*>(sym + sbase)[ln];
+          s[0] = q.x & 0xFFFFu;
+          s[1] = q.x >> 16;
+          s[2] = q.y & 0xFFFFu;
+          s[3] = q.y >> 16;
+        } else {
+          for (uint32_t k = 0; k < 4; k++) {
+            const uint32_t i = ln * 4 + k;
+            s[k] = i < cnt ? (uint32_t)sym[sbase + i] : 4095u;  // enc[4095] = 0: no bits
+          }
+        }
+        uint64_t v = 0;
+        uint32_t nb = 0;
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+          const uint32_t e = enc[min(s[k], 4095u)], l = e >> 16;
+          v = (v << l) | (e & 0xFFFFu);
+          nb += l;
+        }
+        const uint32_t inc = wave_incl(nb);
+        nbits_wave = __shfl(inc, 63, 64);
+        const uint32_t pos = inc - nb;
+        if (nb) {
+          const uint64_t top = v << (64 - nb);  // first code bit at bit 63
+          const uint32_t w0 = pos >> 5, off = pos & 31u;
+          const uint32_t a = (uint32_t)(top >> (32 + off));
+          const uint32_t b = (uint32_t)(top >> off);
+          const uint32_t c2 = off ? (uint32_t)(top << (32 - off)) : 0u;
+          if (a) atomicOr(&buf[wv][w0], a);
+          if (b && w0 + 1 < (uint32_t)kChunkWords) atomicOr(&buf[wv][w0 + 1], b);
+          if (c2 && w0 + 2 < (uint32_t)kChunkWords) atomicOr(&buf[wv][w0 + 2], c2);
+        }
+      }
+      __syncthreads();
+      if (active) {
+        const uint32_t nw = (nbits_wave + 31) >> 5, o = offs[j];
+        for (uint32_t i = ln; i < nw; i += 64) {
+          words[o + i] = buf[wv][i];
+          buf[wv][i] = 0;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__global__ void __launch_bounds__(kThreads) huff_dec_book(const uint8_t* __restrict__ book,
+                                                          uint64_t book_bytes,
+                                                          const uint32_t* __restrict__ chunk_off,
+                                                          uint64_t n, Ws w) {
+  __shared__ uint8_t len[kTable];
+  __shared__ uint16_t order[kTable];
+  __shared__ uint32_t cnt[kMaxLen + 1], first[kMaxLen + 1], base[kMaxLen + 1];
+  __shared__ uint64_t part[16][3];
+  __shared__ uint32_t s_kraft, s_m;
+  __shared__ int s_bad;
+  const int t = threadIdx.x;
+  if (t == 0) {
+    s_bad = 0;
+    s_kraft = 0;
+    s_m = 0;
+    w.status[0] = 0;
+  }
+  if (t <= kMaxLen) cnt[t] = 0;
+  for (int i = t; i < kTable; i += kThreads) len[i] = 0;
+  __syncthreads();
+  int bad = 0;
+  uint32_t lo = 1, hi = 0;
+  if (book_bytes < 4) {
+    bad = 1;
+  } else {
+    lo = book[0] | (uint32_t)book[1] << 8;
+    hi = book[2] | (uint32_t)book[3] << 8;
+    if (hi < lo) {
+      bad = !(lo == 1 && hi == 0);
+    } else if (hi >= (uint32_t)kNsym || 4 + (uint64_t)(hi - lo + 2) / 2 > book_bytes) {
+      bad = 1;
+    }
+  }
+  const bool empty = !bad && hi < lo;
+  if (empty && n > 0) bad = 1;
+  if (t == 0 && chunk_off[0] != 0) bad = 1;
+  if (!bad && !empty) {
+    const uint32_t nb = hi - lo + 1;
+    uint32_t kr = 0, mm = 0;
+    for (uint32_t k = t; k < nb; k += kThreads) {
+      const uint32_t l = (book[4 + k / 2] >> (4 * (k & 1))) & 15u;
+      if (l > (uint32_t)kMaxLen) bad = 1;
+      else if (l) {
+        len[lo + k] = (uint8_t)l;
+        kr += 1u << (kMaxLen - l);
+        mm++;
+        atomicAdd(&cnt[l], 1u);
+      }
+    }
+    if (t == 0) {
+      if ((nb & 1) && (book[4 + nb / 2] >> 4)) bad = 1;
+      const uint32_t llo = book[4] & 15u, lhi = (book[4 + (nb - 1) / 2] >> (4 * ((nb - 1) & 1))) & 15u;
+      if (!llo || !lhi) bad = 1;
+    }
+    if (kr) atomicAdd(&s_kraft, kr);
+    if (mm) atomicAdd(&s_m, mm);
+  }
+  if (bad) s_bad = 1;
+  __syncthreads();
+  if (!s_bad && !empty) {
+    const bool complete = s_m == 1 ? cnt[1] == 1 : s_kraft == (1u << kMaxLen);
+    if (!complete) bad = 1;
+  }
+  __syncthreads();
+  if (bad) s_bad = 1;
+  __syncthreads();
+  if (s_bad) {
+    if (t == 0) {
+      status_or(w.status, kStCorrupt);
+      w.status[1] = 0;
+    }
+    return;
+  }
+  if (t == 0) {
+    uint32_t code = 0, idx = 0;
+    for (int l = 1; l <= kMaxLen; l++) {
+      if (l > 1) code = (code + cnt[l - 1]) << 1;
+      first[l] = code;
+      base[l] = idx;
+      idx += cnt[l];
+    }
+    w.status[1] = 1;
+  }
+  __syncthreads();
+  canonical_codes(len, first, w.enc, part);
+  __syncthreads();
+  for (int s = t; s < kNsym; s += kThreads) {
+    const uint32_t e = w.enc[s], l = e >> 16;
+    if (l) order[base[l] + (e & 0xFFFFu) - first[l]] = (uint16_t)s;
+  }
+  __syncthreads();
+  // every 12-bit prefix -> the one code that starts it (0 when none does)
+  for (int i = t; i < kTable; i += kThreads) {
+    uint32_t e = 0;
+    for (int l = 1; l <= kMaxLen; l++) {
+      const uint32_t p = (uint32_t)i >> (kMaxLen - l);
+      if (p - first[l] < cnt[l]) {
+        e = order[base[l] + p - first[l]] | (uint32_t)l << 12;
+        break;
+      }
+    }
+    w.lut[i] = (uint16_t)e;
+  }
+}
+
+__global__ void __launch_bounds__(kDecChunks) huff_decode(const uint32_t* __restrict__ words,
+                                                          uint64_t words_cap,
+                                                          const uint32_t* __restrict__ chunk_off,
+                                                          uint64_t n, uint32_t nch, Ws w,
+                                                          uint16_t* __restrict__ sym) {
+  __shared__ uint16_t lut[kTable];
+  __shared__ uint32_t stage[kDecChunks * kChunkWords];
+  __shared__ uint32_t s_lo, s_hi;
+  const uint32_t t = threadIdx.x;
+  const uint32_t c0 = blockIdx.x * kDecChunks, c = c0 + t;
+  const uint32_t cend = min(c0 + kDecChunks, nch);
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(w.lut);
+    uint4* dst = reinterpret_cast<uint4*>(lut);
+    for (int i = t; i < kTable * 2 / 16; i += kDecChunks) dst[i] = src[i];
+  }
+  bool ok = w.status[1] != 0;
+  uint32_t a = 0, b = 0;
+  if (c < cend) {
+    a = chunk_off[c];
+    b = chunk_off[c + 1];
+    ok = ok && a <= b && b - a <= (uint32_t)kChunkWords && (uint64_t)b <= words_cap;
+    if (c == 0) ok = ok && a == 0;
+  }
+  if (c == c0) s_lo = a;
+  if (c + 1 == cend) s_hi = b;
+  if (!__syncthreads_and(ok)) {
+    if (t == 0) status_or(w.status, kStCorrupt);
+    return;
+  }
+  const uint32_t glo = s_lo, ghi = s_hi;  // consecutive chunks: at most 128 * 96 words
+  for (uint32_t i = t; i < ghi - glo; i += kDecChunks) stage[i] = words[glo + i];
+  __syncthreads();
+  if (c >= cend) return;
+  const uint64_t sbase = (uint64_t)c * kChunk;
+  const uint32_t rem = (uint32_t)min((uint64_t)kChunk, n - sbase);
+  uint32_t p = a - glo;
+  const uint32_t e = b - glo;
+  uint64_t bitbuf = 0;
+  uint32_t have = 0;
+  bool bad = false;
+  uint32_t pk[4] = {0, 0, 0, 0};
+  uint32_t i = 0;
+  for (; i < rem; i++) {
+    if (have <= 32 && p < e) {
+      bitbuf |= (uint64_t)stage[p++] << (32 - have);
+      have += 32;
+    }
+    const uint32_t ent = lut[bitbuf >> 52], l = ent >> 12;
+    if (l == 0 || l > have) {
+      bad = true;
+      break;
+    }
+    bitbuf <<= l;
+    have -= l;
+    const uint32_t s = ent & 0xFFFu;
+    pk[(i >> 1) & 3] |= s << (16 * (i & 1));
+    if ((i & 7) == 7) {
+      *reinterpret_cast<uint4*>(sym + sbase + (i - 7)) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      pk[0] = pk[1] = pk[2] = pk[3] = 0;
+    }
+  }
+  if (!bad) {
+    for (uint32_t k = i & ~7u; k < i; k++) sym[sbase + k] = (uint16_t)(pk[(k >> 1) & 3] >> (16 * (k & 1)));
+    bad = !(p == e && have < 32 && bitbuf == 0);
+  }
+  if (bad) status_or(w.status, kStCorrupt);
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+uint32_t num_chunks(uint64_t n) { return (uint32_t)((n + kChunk - 1) / kChunk); }
+
+}  // namespace
+
+extern "C" {
+
+size_t ec_huff_workspace_bytes(void) { return kWorkBytes; }
+
+uint64_t ec_huff_max_words(uint64_t n) {
+  const uint64_t full = n / kChunk, rem = n % kChunk;
+  return full * kChunkWords + (rem * kMaxLen + 31) / 32;
+}
+
+ec_status ec_huff_encode(const uint16_t* d_sym, uint64_t n, uint8_t* d_book,
+                         uint32_t* d_chunk_off, uint32_t* d_words, uint64_t words_cap,
+                         void* d_work, size_t work_bytes, void* stream) {
+  if (!d_book || !d_chunk_off || !d_work || n > EC_HUFF_MAX_SYMBOLS) return EC_ERR_INVALID;
+  if (n && (!d_sym || !d_words)) return EC_ERR_INVALID;
+  if (!aligned16(d_sym) || !aligned16(d_words) || ((uintptr_t)d_work & 255u)) return EC_ERR_INVALID;
+  if (work_bytes < kWorkBytes || words_cap < ec_huff_max_words(n)) return EC_ERR_CAPACITY;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Ws w = ws_of(d_work);
+  hipLaunchKernelGGL(huff_clear, dim3(kTable / kThreads), dim3(kThreads), 0, s, w);
+  if (n) {
+    const uint64_t vec_blocks = (n / 8 + kThreads * 4 - 1) / (kThreads * 4);
+    const uint32_t hb = (uint32_t)(vec_blocks < 1 ? 1 : (vec_blocks > 1024 ? 1024 : vec_blocks));
+    hipLaunchKernelGGL(huff_hist, dim3(hb), dim3(kThreads), 0, s, d_sym, n, w);
+  }
+  hipLaunchKernelGGL(huff_book, dim3(1), dim3(kBookThreads), 0, s, w, d_book, d_chunk_off, n);
+  if (n) {
+    const uint32_t nch = num_chunks(n);
+    uint32_t groups = (nch + 3) / 4;
+    if (groups > (uint32_t)kMaxGroups) groups = kMaxGroups;
+    const uint32_t per = (nch + groups - 1) / groups;
+    groups = (nch + per - 1) / per;
+    hipLaunchKernelGGL(huff_size, dim3(groups), dim3(kThreads), 0, s, d_sym, n, w, d_chunk_off,
+                       nch, per);
+    hipLaunchKernelGGL(huff_write, dim3(groups), dim3(kThreads), 0, s, d_sym, n, w, d_chunk_off,
+                       nch, per, d_words);
+  }
+  return hipGetLastError() == hipSuccess ? EC_OK : EC_ERR_DEVICE;
+}
+
+ec_status ec_huff_decode(const uint8_t* d_book, uint64_t book_bytes, const uint32_t* d_chunk_off,
+                         const uint32_t* d_words, uint64_t words_cap, uint64_t n,
+                         uint16_t* d_sym, void* d_work, size_t work_bytes, void* stream) {
+  if (!d_book || !d_chunk_off || !d_work || n > EC_HUFF_MAX_SYMBOLS) return EC_ERR_INVALID;
+  if (n && (!d_sym || !d_words)) return EC_ERR_INVALID;
+  if (!aligned16(d_sym) || !aligned16(d_words) || ((uintptr_t)d_work & 255u)) return EC_ERR_INVALID;
+  if (work_bytes < kWorkBytes) return EC_ERR_CAPACITY;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Ws w = ws_of(d_work);
+  hipLaunchKernelGGL(huff_dec_book, dim3(1), dim3(kThreads), 0, s, d_book, book_bytes, d_chunk_off,
+                     n, w);
+  if (n) {
+    const uint32_t nch = num_chunks(n);
+    hipLaunchKernelGGL(huff_decode, dim3((nch + kDecChunks - 1) / kDecChunks), dim3(kDecChunks), 0,
+                       s, d_words, words_cap, d_chunk_off, n, nch, w, d_sym);
+  }
+  return hipGetLastError() == hipSuccess ? EC_OK : EC_ERR_DEVICE;
+}
+
+ec_status ec_huff_status(void* d_work, void* stream) {
+  if (!d_work) return EC_ERR_INVALID;
+  if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return EC_ERR_DEVICE;
+  uint32_t st = 0;
+  if (hipMemcpy(&st, d_work, sizeof(st), hipMemcpyDeviceToHost) != hipSuccess) return EC_ERR_DEVICE;
+  if (st & kStDepth) return EC_ERR_DEVICE;
+  if (st & kStBadSymbol) return EC_ERR_INVALID;
+  if (st & kStCorrupt) return EC_ERR_CORRUPT;
+  return EC_OK;
+}
+
+}  // extern "C"

@@ -73,3 +73,27 @@ def test_binding_has_no_fallback(monkeypatch, tmp_path):
     monkeypatch.setattr(ec, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         ec.lib()
+
+
+def test_huffman_entry_points_check_arguments_on_the_host():
+    L = ec.lib()
+    assert L.ec_huff_workspace_bytes() > 4 * 4096
+    # 12 bits per symbol, each 256-symbol chunk rounded up to whole words
+    assert L.ec_huff_max_words(0) == 0
+    assert L.ec_huff_max_words(1) == 1
+    assert L.ec_huff_max_words(256) == 96
+    assert L.ec_huff_max_words(257) == 97
+    assert L.ec_huff_max_words(256 * 1000 + 3) == 96 * 1000 + 2
+    wb = L.ec_huff_workspace_bytes()
+    fake = 1 << 20  # never dereferenced: every call below fails its host checks
+    enc = L.ec_huff_encode
+    assert enc(fake, 1000, None, fake, fake, 10**6, fake, wb, None) == ec.EC_ERR_INVALID
+    assert enc(fake, 1 << 31, fake, fake, fake, 1 << 40, fake, wb, None) == ec.EC_ERR_INVALID
+    assert enc(fake + 2, 1000, fake, fake, fake, 10**6, fake, wb, None) == ec.EC_ERR_INVALID
+    assert enc(fake, 1000, fake, fake, fake, 10**6, fake + 16, wb, None) == ec.EC_ERR_INVALID
+    assert enc(fake, 1000, fake, fake, fake, 374, fake, wb, None) == ec.EC_ERR_CAPACITY
+    assert enc(fake, 1000, fake, fake, fake, 10**6, fake, wb - 1, None) == ec.EC_ERR_CAPACITY
+    dec = L.ec_huff_decode
+    assert dec(None, 4, fake, fake, 10, 10, fake, fake, wb, None) == ec.EC_ERR_INVALID
+    assert dec(fake, 4, fake, fake, 10, 10, fake, fake, wb - 1, None) == ec.EC_ERR_CAPACITY
+    assert L.ec_huff_status(None, None) == ec.EC_ERR_INVALID
