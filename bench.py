@@ -34,10 +34,17 @@ WORKLOADS = {
 }
 
 
-def kernel_source_hash() -> str:
+HUFFMAN_SOURCES = ("ec_huffman.hip",)
+
+
+def kernel_source_hash(coder: str = "bitpack") -> str:
+    """Hash of the kernel sources a profile was taken on: the compressor's
+    files, or the Huffman coder's file."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "error_bounded_lossy_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
+        if (name in HUFFMAN_SOURCES) != (coder == "huffman"):
+            continue
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
@@ -88,7 +95,7 @@ KERNEL_PREFIX = {"prep": "ec_prep", "encode": ("ec_encode", "ec_quantize"),
 
 
 def _short_kernel(name: str) -> str:
-    name = name.replace("ec::(anonymous namespace)::", "")
+    name = name.replace("ec::(anonymous namespace)::", "").replace("(anonymous namespace)::", "")
     if name.startswith("void "):
         name = name[5:]
     return name.split("(")[0]
@@ -165,9 +172,10 @@ def summarize_counters(d: str, workload: str, copy_bytes: int, command: str):
               f"(fetch {fetch:.0f} KiB x {f_scale:.3f}, write {write:.0f} KiB x {w_scale:.3f})")
 
 
-def summarize_stats(d: str, workload: str, command: str):
+def summarize_stats(d: str, workload: str, command: str, coder: str = "bitpack"):
     """Kernel-trace statistics (rocprofv3 --stats) of a bench run, as text:
-    writes profiles/<kernel>_<workload>_kernel_stats.txt for the path kernels."""
+    writes profiles/path_kernels_<workload>_kernel_stats.txt for the path
+    kernels, or profiles/huffman_kernels_<workload>_kernel_stats.txt."""
     import csv
     import glob
     rows = []
@@ -176,15 +184,17 @@ def summarize_stats(d: str, workload: str, command: str):
             rows += list(csv.DictReader(fh))
     if not rows:
         raise SystemExit(f"no kernel_stats.csv under {d}")
-    lines = [f"# rocprofv3 kernel statistics, workload {workload}: {WORKLOADS[workload]}",
+    what = "codes of " if coder == "huffman" else ""
+    lines = [f"# rocprofv3 kernel statistics, workload {what}{workload}: {WORKLOADS[workload]}",
              f"# command: {command}",
-             f"# source_hash: {kernel_source_hash()}",
+             f"# source_hash: {kernel_source_hash(coder)}",
              f"{'kernel':<44} {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'pct':>6}"]
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
     other = [0, 0.0, 0.0]
     for r in rows:
         name = _short_kernel(r["Name"])
-        if not name.startswith("ec_"):  # synthetic-input generation and the like
+        if not name.startswith(("huff_",) if coder == "huffman" else ("ec_",)):
+            # synthetic-input generation and the like
             other[0] += int(r["Calls"])
             other[1] += float(r["TotalDurationNs"])
             other[2] += float(r["Percentage"])
@@ -196,7 +206,8 @@ def summarize_stats(d: str, workload: str, command: str):
                  f"{'':>9} {'':>9} {'':>9} {other[2]:>6.2f}")
     text = "\n".join(lines) + "\n"
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    path = os.path.join(ROOT, "profiles", f"path_kernels_{workload}_kernel_stats.txt")
+    stem = "huffman_kernels" if coder == "huffman" else "path_kernels"
+    path = os.path.join(ROOT, "profiles", f"{stem}_{workload}_kernel_stats.txt")
     with open(path, "w") as fh:
         fh.write(text)
     print(text, end="")
@@ -212,6 +223,112 @@ def copy_calibration(nbytes: int, reps: int):
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
     print(f"[bench] copy calibration: {reps} x {nbytes} bytes", file=sys.stderr)
+
+
+def workload_codes(w, torch):
+    """Symbols q + 2047 of a workload batch: q = round(x / 2eb) with the
+    batch's per-table eb (range-relative eb scaled by the schedule, or the
+    absolute eb), codes beyond +-2047 and non-finite values counted as q = 0.
+    Input construction for the coder, outside any timed region."""
+    x = w.x
+    T = x.shape[0]
+    flat = x.view(T, -1)
+    fin = torch.isfinite(flat)
+    base = torch.tensor(w.eb, dtype=torch.float64, device=x.device)
+    if w.eb_mode == 1:
+        lo = torch.where(fin, flat, torch.full_like(flat, float("inf"))).amin(1).double()
+        hi = torch.where(fin, flat, torch.full_like(flat, float("-inf"))).amax(1).double()
+        base = base * (hi - lo)
+    if w.sched_kind == 1:
+        base = base * (1.0 + w.iteration / w.sched_t0) ** -0.5
+    eb = base.float().clamp_min(1e-30).double()
+    q = torch.round(flat.double() / (2.0 * eb[:, None]))
+    q = torch.where(fin & (q.abs() <= 2047), q, torch.zeros_like(q))
+    return (q + 2047).to(torch.int16).reshape(-1)
+
+
+def bench_huffman(args):
+    """Canonical Huffman coder alone: one step = encode + decode of one
+    batch's quantization codes (4 bytes of fp32 input per code)."""
+    import torch
+    import synth
+    import error_bounded_lossy_amd as ec
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] codes of {args.batches} batches of {args.workload}", file=sys.stderr,
+          flush=True)
+    syms = [workload_codes(synth.workload(args.workload, iteration=i, device=dev), torch)
+            for i in range(args.batches)]
+    n = syms[0].numel()
+    coder = ec.Huffman(dev)
+    book, off, words = coder.buffers(n)
+    out = torch.empty(n, dtype=torch.int16, device=dev)
+    sizes = []
+    for s in syms:  # compressed size of every batch (untimed)
+        coder.encode(s, book, off, words)
+        if coder.status() != ec.EC_OK:
+            sys.exit("[bench] encode failed")
+        nw = int(off[-1].item()) & 0xFFFFFFFF
+        sizes.append(4 * nw + ec.huff_book_bytes(book[:4].tolist()) + 4 * off.numel())
+
+    def enc(i):
+        coder.encode(syms[i % len(syms)], book, off, words)
+
+    def dec():
+        coder.decode(book, ec.HUFF_BOOK_MAX, off, words, n, out)
+
+    for i in range(args.warmup):
+        enc(i)
+        dec()
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
+    e[0].record()
+    for i in range(args.steps):
+        enc(args.warmup + i)
+        e[2 * i + 1].record()
+        dec()
+        e[2 * i + 2].record()
+    torch.cuda.synchronize()
+    t_enc = sum(e[2 * i].elapsed_time(e[2 * i + 1]) for i in range(args.steps))
+    t_dec = sum(e[2 * i + 1].elapsed_time(e[2 * i + 2]) for i in range(args.steps))
+    if coder.status() != ec.EC_OK:
+        sys.exit("[bench] decode failed")
+    last = syms[(args.warmup + args.steps - 1) % len(syms)]
+    if not torch.equal(out, last):
+        sys.exit("[bench] decoded codes differ from the input")
+    ms = t_enc + t_dec
+    step_s = ms / args.steps * 1e-3
+    S = sum(sizes) / len(sizes)
+    # decode call (codebook table + chunk decode): reads the stream, writes 2 B per code
+    dec_s = t_dec / args.steps * 1e-3
+    dec_bytes = S + 2 * n
+    achieved = dec_bytes / dec_s / 1e9
+    res = {
+        "metric": "canonical Huffman encode+decode GB/s (fp32-equivalent: 4 B per code) per MI355X",
+        "value": round(4 * n / step_s / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u16",
+        "data": "synthetic",
+        "config": {"workload": f"codes of {args.workload}: {WORKLOADS[args.workload]}",
+                   "codes": n, "batches_cycled": len(syms)},
+        "encode_GBps": round(4 * n / (t_enc / args.steps * 1e-3) / 1e9, 2),
+        "decode_GBps": round(4 * n / dec_s / 1e9, 2),
+        "compression_ratio_vs_fp32": round(4 * n / S, 4),
+        "bits_per_code": round(8 * S / n, 4),
+        "roofline": {"bound": "hbm", "kernel": "decode call", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": int(dec_bytes)},
+    }
+    print(json.dumps(res), flush=True)
 
 
 def main():
@@ -230,13 +347,15 @@ def main():
     ap.add_argument("--summarize-stats", metavar="DIR",
                     help="write profiles/*_kernel_stats.txt from a rocprofv3 --stats run under DIR")
     ap.add_argument("--command", default="", help="command line recorded in a summary")
+    ap.add_argument("--coder", default="bitpack", choices=["bitpack", "huffman"],
+                    help="huffman: time the canonical Huffman coder on the workload's codes")
     args = ap.parse_args()
     if args.summarize_counters:
         summarize_counters(args.summarize_counters, args.workload,
                            args.copy_calibration or (256 << 20), args.command)
         return
     if args.summarize_stats:
-        summarize_stats(args.summarize_stats, args.workload, args.command)
+        summarize_stats(args.summarize_stats, args.workload, args.command, args.coder)
         return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, 8)
@@ -245,6 +364,10 @@ def main():
         print(f"bench.py measures one GPU's share; --gpus {args.gpus} is not supported "
               f"(the library has no all-to-all across GPUs)", file=sys.stderr)
         sys.exit(2)
+
+    if args.coder == "huffman":
+        bench_huffman(args)
+        return
 
     import torch
     import synth

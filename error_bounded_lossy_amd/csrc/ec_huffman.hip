@@ -18,8 +18,10 @@
 //   dec_book  one workgroup: validate the codebook, canonical codes, a
 //             4096-entry table from every 12-bit prefix to (symbol, length)
 //   decode    128 chunks per workgroup: their words staged through LDS with
-//             coalesced loads, then one lane per chunk decodes by table
-//             lookups and checks that the chunk ends exactly in its last word.
+//             coalesced loads when they fit in 56 words per chunk on average
+//             (else read from global memory), then one lane per chunk decodes
+//             by table lookups, two words ahead of its bit buffer, and checks
+//             that the chunk ends exactly in its last word.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -38,6 +40,7 @@ constexpr int kMaxDepth = 64;  // a tree over fewer than 2^31 symbols is shallow
 constexpr int kBookThreads = 1024;
 constexpr int kThreads = 256;
 constexpr int kDecChunks = 128;  // chunks (and lanes) per decode workgroup
+constexpr int kStageWords = kDecChunks * 56;  // LDS words staged per decode workgroup
 
 enum : uint32_t { kStBadSymbol = 1u, kStCorrupt = 2u, kStDepth = 4u };
 
@@ -227,7 +230,26 @@ __global__ void __launch_bounds__(kBookThreads) huff_book(Ws w, uint8_t* __restr
   __syncthreads();
   const int m = s_m;
 
-  if (m >= 2) {
+  if (m >= 2 && m <= kBookThreads) {
+    // small alphabet: gather the used keys, then each takes the rank that
+    // the number of smaller keys gives it (keys are distinct)
+    __shared__ uint64_t ck[kBookThreads];
+    __shared__ int s_n;
+    if (t == 0) s_n = 0;
+    __syncthreads();
+    for (int s = t; s < kTable; s += kBookThreads) {
+      const uint64_t k = key[s];
+      if (k != ~0ull) ck[atomicAdd(&s_n, 1)] = k;
+    }
+    __syncthreads();
+    if (t < m) {
+      const uint64_t k = ck[t];
+      int r = 0;
+      for (int i = 0; i < m; i++) r += ck[i] < k;
+      key[r] = k;
+    }
+    __syncthreads();
+  } else if (m > kBookThreads) {
     for (int size = 2; size <= kTable; size <<= 1) {
       for (int stride = size >> 1; stride > 0; stride >>= 1) {
         for (int p = t; p < kTable / 2; p += kBookThreads) {
@@ -242,6 +264,8 @@ __global__ void __launch_bounds__(kBookThreads) huff_book(Ws w, uint8_t* __restr
         __syncthreads();
       }
     }
+  }
+  if (m >= 2) {
     for (int i = t; i < m; i += kBookThreads) {
       const uint64_t k = key[i];
       wt[i] = (uint32_t)(k >> 12);
@@ -253,13 +277,21 @@ __global__ void __launch_bounds__(kBookThreads) huff_book(Ws w, uint8_t* __restr
     if (t == 0) {
       const int nn = 2 * m - 1;
       int lq = 0, iq = m;
+      uint32_t lf = wt[0];  // weight at the front of the leaf queue
       for (int nx = m; nx < nn; nx++) {
         uint32_t sum = 0;
         for (int k = 0; k < 2; k++) {
-          const bool leaf = lq < m && (iq >= nx || wt[lq] <= wt[iq]);
-          const int p = leaf ? lq++ : iq++;
-          sum += wt[p];
-          pr[p] = (uint32_t)nx;
+          const uint32_t inf = iq < nx ? wt[iq] : 0xFFFFFFFFu;  // weights stay below 2^31
+          if (lq < m && lf <= inf) {
+            sum += lf;
+            pr[lq] = (uint32_t)nx;
+            lq++;
+            lf = lq < m ? wt[lq] : 0u;
+          } else {
+            sum += inf;
+            pr[iq] = (uint32_t)nx;
+            iq++;
+          }
         }
         wt[nx] = sum;
       }
@@ -271,11 +303,14 @@ __global__ void __launch_bounds__(kBookThreads) huff_book(Ws w, uint8_t* __restr
     // pointer jumping: every pair (ancestor, distance) stays true, and each
     // round at least doubles the distance until the root is reached
     for (int r = 0; r < 13; r++) {
+      int open = 0;
       for (int v = t; v < nn; v += kBookThreads) {
         const uint32_t x = pr[v], y = pr[x & 0xFFFFu];
-        pr[v] = (y & 0xFFFFu) | (((x >> 16) + (y >> 16)) << 16);
+        const uint32_t z = (y & 0xFFFFu) | (((x >> 16) + (y >> 16)) << 16);
+        pr[v] = z;
+        open |= (z & 0xFFFFu) != (uint32_t)root;
       }
-      __syncthreads();
+      if (!__syncthreads_or(open)) break;
     }
     for (int v = t; v < m; v += kBookThreads) {
       const uint32_t d = pr[v] >> 16;
@@ -463,7 +498,7 @@ __global__ void __launch_bounds__(kThreads) huff_write(const uint16_t* __restric
   }
 }
 
-__global__ void __launch_bounds__(kThreads) huff_dec_book(const uint8_t* __restrict__ book,
+__global__ void __launch_bounds__(kBookThreads) huff_dec_book(const uint8_t* __restrict__ book,
                                                           uint64_t book_bytes,
                                                           const uint32_t* __restrict__ chunk_off,
                                                           uint64_t n, Ws w) {
@@ -481,7 +516,7 @@ __global__ void __launch_bounds__(kThreads) huff_dec_book(const uint8_t* __restr
     w.status[0] = 0;
   }
   if (t <= kMaxLen) cnt[t] = 0;
-  for (int i = t; i < kTable; i += kThreads) len[i] = 0;
+  for (int i = t; i < kTable; i += kBookThreads) len[i] = 0;
   __syncthreads();
   int bad = 0;
   uint32_t lo = 1, hi = 0;
@@ -502,7 +537,7 @@ __global__ void __launch_bounds__(kThreads) huff_dec_book(const uint8_t* __restr
   if (!bad && !empty) {
     const uint32_t nb = hi - lo + 1;
     uint32_t kr = 0, mm = 0;
-    for (uint32_t k = t; k < nb; k += kThreads) {
+    for (uint32_t k = t; k < nb; k += kBookThreads) {
       const uint32_t l = (book[4 + k / 2] >> (4 * (k & 1))) & 15u;
       if (l > (uint32_t)kMaxLen) bad = 1;
       else if (l) {
@@ -549,13 +584,13 @@ __global__ void __launch_bounds__(kThreads) huff_dec_book(const uint8_t* __restr
   __syncthreads();
   canonical_codes(len, first, w.enc, part);
   __syncthreads();
-  for (int s = t; s < kNsym; s += kThreads) {
+  for (int s = t; s < kNsym; s += kBookThreads) {
     const uint32_t e = w.enc[s], l = e >> 16;
     if (l) order[base[l] + (e & 0xFFFFu) - first[l]] = (uint16_t)s;
   }
   __syncthreads();
   // every 12-bit prefix -> the one code that starts it (0 when none does)
-  for (int i = t; i < kTable; i += kThreads) {
+  for (int i = t; i < kTable; i += kBookThreads) {
     uint32_t e = 0;
     for (int l = 1; l <= kMaxLen; l++) {
       const uint32_t p = (uint32_t)i >> (kMaxLen - l);
@@ -568,13 +603,55 @@ __global__ void __launch_bounds__(kThreads) huff_dec_book(const uint8_t* __restr
   }
 }
 
+// Decode one chunk of `rem` symbols from its nwords words at src (LDS or
+// global memory).  The bits are read as if zero words followed the chunk;
+// whether it really ends in its last word is decided from the bits consumed.
+// Returns false if the chunk is malformed.
+__device__ __forceinline__ bool decode_chunk(const uint32_t* src, uint32_t nwords, uint32_t rem,
+                                             const uint16_t* lut, uint16_t* out) {
+  // two words are loaded ahead of the bit buffer, so a refill never waits
+  uint32_t q0 = nwords > 0 ? src[0] : 0u, q1 = nwords > 1 ? src[1] : 0u, p = 2;
+  uint64_t bitbuf = 0;
+  uint32_t have = 0, used = 0;
+  bool bad = false;
+  for (uint32_t g = 0; g < rem; g += 8) {
+    uint32_t pk[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      if (have <= 32) {
+        bitbuf |= (uint64_t)q0 << (32 - have);
+        have += 32;
+        q0 = q1;
+        q1 = p < nwords ? src[p] : 0u;
+        p++;
+      }
+      const uint32_t ent = lut[bitbuf >> 52];
+      const bool act = g + k < rem;
+      const uint32_t l = act ? ent >> 12 : 0u;
+      bad |= act && l == 0;
+      bitbuf <<= l;
+      have -= l;
+      used += l;
+      pk[k >> 1] |= (ent & 0xFFFu) << (16 * (k & 1));
+    }
+    if (g + 8 <= rem) {
+      *reinterpret_cast<uint4*>(out + g) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    } else {
+      for (uint32_t k = 0; k < rem - g; k++) out[g + k] = (uint16_t)(pk[k >> 1] >> (16 * (k & 1)));
+    }
+  }
+  // every consumed bit lies in the chunk, the chunk's last word holds some of
+  // them, and the bits after the last code are zero
+  return !(bad || used > 32 * nwords || used + 32 <= 32 * nwords || bitbuf != 0);
+}
+
 __global__ void __launch_bounds__(kDecChunks) huff_decode(const uint32_t* __restrict__ words,
                                                           uint64_t words_cap,
                                                           const uint32_t* __restrict__ chunk_off,
                                                           uint64_t n, uint32_t nch, Ws w,
                                                           uint16_t* __restrict__ sym) {
   __shared__ uint16_t lut[kTable];
-  __shared__ uint32_t stage[kDecChunks * kChunkWords];
+  __shared__ uint32_t stage[kStageWords];
   __shared__ uint32_t s_lo, s_hi;
   const uint32_t t = threadIdx.x;
   const uint32_t c0 = blockIdx.x * kDecChunks, c = c0 + t;
@@ -598,43 +675,19 @@ __global__ void __launch_bounds__(kDecChunks) huff_decode(const uint32_t* __rest
     if (t == 0) status_or(w.status, kStCorrupt);
     return;
   }
-  const uint32_t glo = s_lo, ghi = s_hi;  // consecutive chunks: at most 128 * 96 words
-  for (uint32_t i = t; i < ghi - glo; i += kDecChunks) stage[i] = words[glo + i];
+  // consecutive valid chunks: the group's words are [glo, ghi), at most
+  // kDecChunks * 96; they go through LDS when they fit (the usual case)
+  const uint32_t glo = s_lo, ghi = s_hi;
+  const bool staged = ghi - glo <= (uint32_t)kStageWords;
+  if (staged)
+    for (uint32_t i = t; i < ghi - glo; i += kDecChunks) stage[i] = words[glo + i];
   __syncthreads();
   if (c >= cend) return;
   const uint64_t sbase = (uint64_t)c * kChunk;
   const uint32_t rem = (uint32_t)min((uint64_t)kChunk, n - sbase);
-  uint32_t p = a - glo;
-  const uint32_t e = b - glo;
-  uint64_t bitbuf = 0;
-  uint32_t have = 0;
-  bool bad = false;
-  uint32_t pk[4] = {0, 0, 0, 0};
-  uint32_t i = 0;
-  for (; i < rem; i++) {
-    if (have <= 32 && p < e) {
-      bitbuf |= (uint64_t)stage[p++] << (32 - have);
-      have += 32;
-    }
-    const uint32_t ent = lut[bitbuf >> 52], l = ent >> 12;
-    if (l == 0 || l > have) {
-      bad = true;
-      break;
-    }
-    bitbuf <<= l;
-    have -= l;
-    const uint32_t s = ent & 0xFFFu;
-    pk[(i >> 1) & 3] |= s << (16 * (i & 1));
-    if ((i & 7) == 7) {
-      *reinterpret_cast<uint4*>(sym + sbase + (i - 7)) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-      pk[0] = pk[1] = pk[2] = pk[3] = 0;
-    }
-  }
-  if (!bad) {
-    for (uint32_t k = i & ~7u; k < i; k++) sym[sbase + k] = (uint16_t)(pk[(k >> 1) & 3] >> (16 * (k & 1)));
-    bad = !(p == e && have < 32 && bitbuf == 0);
-  }
-  if (bad) status_or(w.status, kStCorrupt);
+  const bool good = staged ? decode_chunk(stage + (a - glo), b - a, rem, lut, sym + sbase)
+                           : decode_chunk(words + a, b - a, rem, lut, sym + sbase);
+  if (!good) status_or(w.status, kStCorrupt);
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -691,7 +744,7 @@ ec_status ec_huff_decode(const uint8_t* d_book, uint64_t book_bytes, const uint3
   if (work_bytes < kWorkBytes) return EC_ERR_CAPACITY;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Ws w = ws_of(d_work);
-  hipLaunchKernelGGL(huff_dec_book, dim3(1), dim3(kThreads), 0, s, d_book, book_bytes, d_chunk_off,
+  hipLaunchKernelGGL(huff_dec_book, dim3(1), dim3(kBookThreads), 0, s, d_book, book_bytes, d_chunk_off,
                      n, w);
   if (n) {
     const uint32_t nch = num_chunks(n);
