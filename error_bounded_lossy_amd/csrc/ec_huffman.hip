@@ -277,11 +277,13 @@ __global__ void __launch_bounds__(kBookThreads) huff_book(Ws w, uint8_t* __restr
     if (t == 0) {
       const int nn = 2 * m - 1;
       int lq = 0, iq = m;
-      uint32_t lf = wt[0];  // weight at the front of the leaf queue
+      // weights at the fronts of the two queues (all weights stay below 2^31,
+      // so 2^32-1 marks an empty internal queue); each is read from LDS only
+      // when its queue advances
+      uint32_t lf = wt[0], inf = 0xFFFFFFFFu;
       for (int nx = m; nx < nn; nx++) {
         uint32_t sum = 0;
         for (int k = 0; k < 2; k++) {
-          const uint32_t inf = iq < nx ? wt[iq] : 0xFFFFFFFFu;  // weights stay below 2^31
           if (lq < m && lf <= inf) {
             sum += lf;
             pr[lq] = (uint32_t)nx;
@@ -291,9 +293,11 @@ __global__ void __launch_bounds__(kBookThreads) huff_book(Ws w, uint8_t* __restr
             sum += inf;
             pr[iq] = (uint32_t)nx;
             iq++;
+            inf = iq < nx ? wt[iq] : 0xFFFFFFFFu;
           }
         }
         wt[nx] = sum;
+        if (iq == nx) inf = sum;  // the queue was empty: the new node is its front
       }
     }
     __syncthreads();
@@ -322,30 +326,33 @@ __global__ void __launch_bounds__(kBookThreads) huff_book(Ws w, uint8_t* __restr
     syms[0] = (uint16_t)s_lo;
   }
   __syncthreads();
-  if (t == 0) {
+  if (t < 64) {
+    // wave 0, one length count per lane (lane i holds BITS[i]).
     // ITU-T T.81 Annex K.3: while a code is longer than the limit, take two
     // codes of the longest length i: one moves to length i-1 (next to its
     // prefix), and the other becomes a sibling of a code of the longest
     // length j < i-1 that exists, which moves to j+1 with it
-    for (int i = kMaxDepth - 1; i > kMaxLen;) {
-      if (bits[i]) {
-        int j = i - 2;
-        while (bits[j] == 0) j--;
-        bits[i] -= 2;
-        bits[i - 1] += 1;
-        bits[j + 1] += 2;
-        bits[j] -= 1;
-      } else {
-        i--;
-      }
+    uint32_t cl = bits[t];
+    for (;;) {
+      const uint64_t nz = __ballot(cl != 0);
+      if (nz == 0) break;
+      const int i = 63 - __builtin_clzll(nz);
+      if (i <= kMaxLen) break;
+      const int j = 63 - __builtin_clzll(nz & ((1ull << (i - 1)) - 1));
+      cl += (t == i ? 0u - 2u : 0u) + (t == i - 1 ? 1u : 0u) + (t == j + 1 ? 2u : 0u) +
+            (t == j ? 0u - 1u : 0u);
     }
-    cum[0] = 0;
-    first[0] = 0;
-    uint32_t code = 0;
-    for (int l = 1; l <= kMaxLen; l++) {
-      cum[l] = cum[l - 1] + bits[l];
-      if (l > 1) code = (code + bits[l - 1]) << 1;
-      first[l] = code;
+    // cum[l]: codes of length <= l; first[l] = 2 (first[l-1] + BITS[l-1]),
+    // i.e. the sum over k < l of BITS[k] << (l - k)
+    const uint32_t inc = wave_incl(t >= 1 && t <= kMaxLen ? cl : 0u);
+    uint32_t f = 0;
+    for (int k = 1; k < kMaxLen; k++) {
+      const uint32_t bk = (uint32_t)__shfl((int)cl, k, 64);
+      if (k < t) f += bk << (t - k);
+    }
+    if (t <= kMaxLen) {
+      cum[t] = inc;
+      first[t] = f;
     }
   }
   __syncthreads();
@@ -485,7 +492,11 @@ __global__ void __launch_bounds__(kThreads) huff_write(const uint16_t* __restric
           if (c2 && w0 + 2 < (uint32_t)kChunkWords) atomicOr(&buf[wv][w0 + 2], c2);
         }
       }
-      __syncthreads();
+      // each wave owns its buffer, and a wave's LDS operations complete in
+      // order: a wave-level fence orders the ORs before the reads and the
+      // reads and clears before the next chunk's ORs
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
       if (active) {
         const uint32_t nw = (nbits_wave + 31) >> 5, o = offs[j];
         for (uint32_t i = ln; i < nw; i += 64) {
@@ -493,8 +504,10 @@ __global__ void __launch_bounds__(kThreads) huff_write(const uint16_t* __restric
           buf[wv][i] = 0;
         }
       }
-      __syncthreads();
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
     }
+    __syncthreads();  // offs[] is rewritten by the next round
   }
 }
 
