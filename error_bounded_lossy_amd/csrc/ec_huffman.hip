@@ -169,13 +169,23 @@ __global__ void __launch_bounds__(kThreads) huff_hist(const uint16_t* __restrict
   auto add = [&](uint32_t s) { atomicAdd(&h[s < (uint32_t)kNsym ? s : (uint32_t)kNsym], 1u); };
   const uint64_t nv = n >> 3, stride = (uint64_t)gridDim.x * kThreads;
   const uint4* v = reinterpret_cast<const uint4*>(sym);
-  for (uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x; i < nv; i += stride) {
-    const uint4 q = v[i];
-    const uint32_t x[4] = {q.x, q.y, q.z, q.w};
+  // four 16-byte loads in flight per lane before their 32 LDS updates
+  for (uint64_t i0 = (uint64_t)blockIdx.x * kThreads + threadIdx.x; i0 < nv; i0 += 4 * stride) {
+    uint4 q[4];
 #pragma unroll
-    for (int k = 0; k < 4; k++) {
-      add(x[k] & 0xFFFFu);
-      add(x[k] >> 16);
+    for (int u = 0; u < 4; u++) {
+      const uint64_t i = i0 + u * stride;
+      q[u] = i < nv ? v[i] : make_uint4(0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      if (i0 + u * stride >= nv) break;
+      const uint32_t x[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+#pragma unroll
+      for (int k = 0; k < 4; k++) {
+        add(x[k] & 0xFFFFu);
+        add(x[k] >> 16);
+      }
     }
   }
   for (uint64_t i = (nv << 3) + (uint64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride)
@@ -658,6 +668,49 @@ __device__ __forceinline__ bool decode_chunk(const uint32_t* src, uint32_t nword
   return !(bad || used > 32 * nwords || used + 32 <= 32 * nwords || bitbuf != 0);
 }
 
+// The same for a chunk staged in LDS, without branches in the symbol loop:
+// the word after the bit buffer's next word is loaded together with every
+// table lookup (one LDS wait per symbol), and a refill after the lookup
+// consumes it with selects, so the buffer holds at least 21 bits at every
+// lookup.  Words past the chunk read as zero.  nwords >= 1.
+__device__ __forceinline__ bool decode_chunk_lds(const uint32_t* src, uint32_t nwords,
+                                                 uint32_t rem, const uint16_t* lut,
+                                                 uint16_t* out) {
+  const uint32_t last = nwords - 1;
+  uint64_t bitbuf = (uint64_t)src[0] << 32;
+  uint32_t have = 32, used = 0;
+  uint32_t p = 1;  // index of wq, the next word to insert
+  uint32_t wq = nwords > 1 ? src[1] : 0u;
+  bool bad = false;
+  for (uint32_t g = 0; g < rem; g += 8) {
+    uint32_t pk[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      const uint32_t wn_raw = src[min(p + 1, last)];
+      const uint32_t ent = lut[bitbuf >> 52];
+      const bool act = g + k < rem;
+      const uint32_t l = act ? ent >> 12 : 0u;
+      bad |= act && l == 0;
+      bitbuf <<= l;
+      have -= l;
+      used += l;
+      pk[k >> 1] |= (ent & 0xFFFu) << (16 * (k & 1));
+      const bool rf = have <= 32;
+      const uint32_t wn = p + 1 <= last ? wn_raw : 0u;
+      bitbuf |= rf ? (uint64_t)wq << (32 - have) : 0ull;
+      have += rf ? 32u : 0u;
+      wq = rf ? wn : wq;
+      p += rf ? 1u : 0u;
+    }
+    if (g + 8 <= rem) {
+      *reinterpret_cast<uint4*>(out + g) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    } else {
+      for (uint32_t k = 0; k < rem - g; k++) out[g + k] = (uint16_t)(pk[k >> 1] >> (16 * (k & 1)));
+    }
+  }
+  return !(bad || used > 32 * nwords || used + 32 <= 32 * nwords || bitbuf != 0);
+}
+
 __global__ void __launch_bounds__(kDecChunks) huff_decode(const uint32_t* __restrict__ words,
                                                           uint64_t words_cap,
                                                           const uint32_t* __restrict__ chunk_off,
@@ -698,8 +751,9 @@ __global__ void __launch_bounds__(kDecChunks) huff_decode(const uint32_t* __rest
   if (c >= cend) return;
   const uint64_t sbase = (uint64_t)c * kChunk;
   const uint32_t rem = (uint32_t)min((uint64_t)kChunk, n - sbase);
-  const bool good = staged ? decode_chunk(stage + (a - glo), b - a, rem, lut, sym + sbase)
-                           : decode_chunk(words + a, b - a, rem, lut, sym + sbase);
+  const bool good = b == a ? false
+                    : staged ? decode_chunk_lds(stage + (a - glo), b - a, rem, lut, sym + sbase)
+                             : decode_chunk(words + a, b - a, rem, lut, sym + sbase);
   if (!good) status_or(w.status, kStCorrupt);
 }
 
