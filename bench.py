@@ -51,7 +51,7 @@ def kernel_source_hash(coder: str = "bitpack") -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel: str, workload: str):
+def load_traffic(kernel: str, workload: str, coder: str = "bitpack"):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current kernel sources (else None)."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.json")
@@ -59,7 +59,7 @@ def load_traffic(kernel: str, workload: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_hash") != kernel_source_hash():
+    if rec.get("source_hash") != kernel_source_hash(coder):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -92,6 +92,10 @@ def cpu_baseline(x_cpu, w, min_seconds: float):
 
 KERNEL_PREFIX = {"prep": "ec_prep", "encode": ("ec_encode", "ec_quantize"),
                  "assemble": ("ec_size", "ec_write"), "decode": ("ec_decode",)}
+# the Huffman coder's two calls: encode (five kernels) and decode (two)
+KERNEL_PREFIX_HUFF = {"huffman_encode": ("huff_clear", "huff_hist", "huff_book", "huff_size",
+                                         "huff_write"),
+                      "huffman_decode": ("huff_dec_book", "huff_decode")}
 
 
 def _short_kernel(name: str) -> str:
@@ -115,14 +119,16 @@ def _read_counter_csvs(d: str):
     return out
 
 
-def summarize_counters(d: str, workload: str, copy_bytes: int, command: str):
+def summarize_counters(d: str, workload: str, copy_bytes: int, command: str,
+                       coder: str = "bitpack"):
     """HBM traffic per launch of each pass of the path from four rocprofv3 --pmc
     runs (FETCH_SIZE and WRITE_SIZE of the workload, and of a plain copy of
     known size): each counter is scaled by bytes-moved / counter-reading of the
     copy; a pass of several kernels sums their per-dispatch averages.  Writes
     profiles/<pass>_<workload>_counters.json."""
-    wf = _read_counter_csvs(os.path.join(d, f"pmc_{workload}_fetch"))
-    ww = _read_counter_csvs(os.path.join(d, f"pmc_{workload}_write"))
+    tag = f"huff_{workload}" if coder == "huffman" else workload
+    wf = _read_counter_csvs(os.path.join(d, f"pmc_{tag}_fetch"))
+    ww = _read_counter_csvs(os.path.join(d, f"pmc_{tag}_write"))
     cf = _read_counter_csvs(os.path.join(d, "pmc_copy_fetch"))
     cw = _read_counter_csvs(os.path.join(d, "pmc_copy_write"))
 
@@ -138,7 +144,7 @@ def summarize_counters(d: str, workload: str, copy_bytes: int, command: str):
     f_scale = copy_bytes / (f_kib * 1024.0)
     w_scale = copy_bytes / (w_kib * 1024.0)
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    for kern, prefix in KERNEL_PREFIX.items():
+    for kern, prefix in (KERNEL_PREFIX_HUFF if coder == "huffman" else KERNEL_PREFIX).items():
         names = sorted({k for k in list(wf) + list(ww) if k.startswith(prefix)})
         per = {}
         for nm in names:
@@ -152,7 +158,7 @@ def summarize_counters(d: str, workload: str, copy_bytes: int, command: str):
         write = sum(v["write_kib"] for v in per.values())
         rec = {
             "pass": kern, "kernels": per, "workload": workload,
-            "source_hash": kernel_source_hash(),
+            "source_hash": kernel_source_hash(coder),
             "fetch_kib_per_launch": round(fetch, 1),
             "write_kib_per_launch": round(write, 1),
             "copy_calibration": {
@@ -325,7 +331,8 @@ def bench_huffman(args):
         "bits_per_code": round(8 * S / n, 4),
         "roofline": {"bound": "hbm", "kernel": "decode call", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic("huffman_decode", args.workload, "huffman"),
                      "algorithmic_bytes_per_launch": int(dec_bytes)},
     }
     print(json.dumps(res), flush=True)
@@ -352,7 +359,7 @@ def main():
     args = ap.parse_args()
     if args.summarize_counters:
         summarize_counters(args.summarize_counters, args.workload,
-                           args.copy_calibration or (256 << 20), args.command)
+                           args.copy_calibration or (256 << 20), args.command, args.coder)
         return
     if args.summarize_stats:
         summarize_stats(args.summarize_stats, args.workload, args.command, args.coder)

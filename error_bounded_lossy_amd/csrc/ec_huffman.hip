@@ -682,10 +682,12 @@ __device__ __forceinline__ bool decode_chunk_lds(const uint32_t* src, uint32_t n
   uint32_t p = 1;  // index of wq, the next word to insert
   uint32_t wq = nwords > 1 ? src[1] : 0u;
   bool bad = false;
-  for (uint32_t g = 0; g < rem; g += 8) {
-    uint32_t pk[4] = {0, 0, 0, 0};
+  for (uint32_t g = 0; g < rem; g += 32) {
+    uint32_t pk[16];
 #pragma unroll
-    for (int k = 0; k < 8; k++) {
+    for (int k = 0; k < 16; k++) pk[k] = 0;
+#pragma unroll
+    for (int k = 0; k < 32; k++) {
       const uint32_t wn_raw = src[min(p + 1, last)];
       const uint32_t ent = lut[bitbuf >> 52];
       const bool act = g + k < rem;
@@ -702,8 +704,11 @@ __device__ __forceinline__ bool decode_chunk_lds(const uint32_t* src, uint32_t n
       wq = rf ? wn : wq;
       p += rf ? 1u : 0u;
     }
-    if (g + 8 <= rem) {
-      *reinterpret_cast<uint4*>(out + g) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    if (g + 32 <= rem) {  // 64 bytes of one chunk at a time
+#pragma unroll
+      for (int q = 0; q < 4; q++)
+        *reinterpret_cast<uint4*>(out + g + 8 * q) =
+            make_uint4(pk[4 * q], pk[4 * q + 1], pk[4 * q + 2], pk[4 * q + 3]);
     } else {
       for (uint32_t k = 0; k < rem - g; k++) out[g + k] = (uint16_t)(pk[k >> 1] >> (16 * (k & 1)));
     }
