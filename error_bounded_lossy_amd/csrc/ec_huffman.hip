@@ -287,10 +287,10 @@ __global__ void __launch_bounds__(kBookThreads) huff_book(Ws w, uint8_t* __restr
     if (t == 0) {
       const int nn = 2 * m - 1;
       int lq = 0, iq = m;
-      // weights at the fronts of the two queues (all weights stay below 2^31,
-      // so 2^32-1 marks an empty internal queue); each is read from LDS only
-      // when its queue advances
-      uint32_t lf = wt[0], inf = 0xFFFFFFFFu;
+      // the first two weights of each queue live in registers (all weights
+      // stay below 2^31, so 2^32-1 marks a node not yet created); a queue's
+      // next weight is loaded one pick before it can be needed
+      uint32_t lf = wt[0], lf2 = wt[1], inf = 0xFFFFFFFFu, inf2 = 0xFFFFFFFFu;
       for (int nx = m; nx < nn; nx++) {
         uint32_t sum = 0;
         for (int k = 0; k < 2; k++) {
@@ -298,16 +298,19 @@ __global__ void __launch_bounds__(kBookThreads) huff_book(Ws w, uint8_t* __restr
             sum += lf;
             pr[lq] = (uint32_t)nx;
             lq++;
-            lf = lq < m ? wt[lq] : 0u;
+            lf = lf2;
+            lf2 = lq + 1 < m ? wt[lq + 1] : 0u;
           } else {
             sum += inf;
             pr[iq] = (uint32_t)nx;
             iq++;
-            inf = iq < nx ? wt[iq] : 0xFFFFFFFFu;
+            inf = inf2;
+            inf2 = iq + 1 < nx ? wt[iq + 1] : 0xFFFFFFFFu;
           }
         }
         wt[nx] = sum;
         if (iq == nx) inf = sum;  // the queue was empty: the new node is its front
+        else if (iq + 1 == nx) inf2 = sum;
       }
     }
     __syncthreads();
