@@ -255,7 +255,8 @@ def workload_codes(w, torch):
 
 def bench_huffman(args):
     """Canonical Huffman coder alone: one step = encode + decode of one
-    batch's quantization codes (4 bytes of fp32 input per code)."""
+    batch's quantization codes (4 bytes of fp32 input per code), one codebook
+    per table (the tables are the coder's segments)."""
     import torch
     import synth
     import error_bounded_lossy_amd as ec
@@ -267,7 +268,8 @@ def bench_huffman(args):
     syms = [workload_codes(synth.workload(args.workload, iteration=i, device=dev), torch)
             for i in range(args.batches)]
     n = syms[0].numel()
-    coder = ec.Huffman(dev)
+    T = synth.SHAPES[args.workload][0]
+    coder = ec.Huffman(dev, nseg=T)
     book, off, words = coder.buffers(n)
     out = torch.empty(n, dtype=torch.int16, device=dev)
     sizes = []
@@ -276,7 +278,8 @@ def bench_huffman(args):
         if coder.status() != ec.EC_OK:
             sys.exit("[bench] encode failed")
         nw = int(off[-1].item()) & 0xFFFFFFFF
-        sizes.append(4 * nw + ec.huff_book_bytes(book[:4].tolist()) + 4 * off.numel())
+        bk = book.view(T, ec.HUFF_BOOK_MAX)[:, :4].cpu().tolist()
+        sizes.append(4 * nw + sum(ec.huff_book_bytes(b) for b in bk) + 4 * off.numel())
 
     def enc(i):
         coder.encode(syms[i % len(syms)], book, off, words)
@@ -324,7 +327,7 @@ def bench_huffman(args):
         "dtype": "u16",
         "data": "synthetic",
         "config": {"workload": f"codes of {args.workload}: {WORKLOADS[args.workload]}",
-                   "codes": n, "batches_cycled": len(syms)},
+                   "codes": n, "codebooks": T, "batches_cycled": len(syms)},
         "encode_GBps": round(4 * n / (t_enc / args.steps * 1e-3) / 1e9, 2),
         "decode_GBps": round(4 * n / dec_s / 1e9, 2),
         "compression_ratio_vs_fp32": round(4 * n / S, 4),

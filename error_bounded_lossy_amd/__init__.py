@@ -98,6 +98,12 @@ def lib():
     L.ec_huff_decode.argtypes = [vp, u64, vp, vp, u64, u64, vp, vp, sz, vp]
     L.ec_huff_status.restype = st
     L.ec_huff_status.argtypes = [vp, vp]
+    L.ec_huff_workspace_bytes_segments.restype = sz
+    L.ec_huff_workspace_bytes_segments.argtypes = [ctypes.c_uint32]
+    L.ec_huff_encode_segments.restype = st
+    L.ec_huff_encode_segments.argtypes = [vp, ctypes.c_uint32, u64, vp, vp, vp, u64, vp, sz, vp]
+    L.ec_huff_decode_segments.restype = st
+    L.ec_huff_decode_segments.argtypes = [vp, vp, vp, u64, ctypes.c_uint32, u64, vp, vp, sz, vp]
     _lib = L
     return L
 
@@ -265,26 +271,36 @@ def huff_book_bytes(header4) -> int:
 
 
 class Huffman:
-    """Workspace holder for ec_huff_encode / ec_huff_decode on one device.
+    """Workspace holder for the Huffman coder on one device.
 
-    Symbols travel as int16 tensors (bit patterns of the u16 symbols), words
-    and chunk offsets as int32 tensors (bit patterns of u32)."""
+    nseg = 1 codes one array (ec_huff_encode / ec_huff_decode); nseg > 1 codes
+    nseg equal segments with a codebook each (ec_huff_encode_segments /
+    ec_huff_decode_segments).  Symbols travel as int16 tensors (bit patterns
+    of the u16 symbols), words and chunk offsets as int32 tensors (bit
+    patterns of u32), codebooks as uint8 tensors of nseg * HUFF_BOOK_MAX."""
 
-    def __init__(self, device=None):
+    def __init__(self, device=None, nseg: int = 1):
         import torch
         self.device = torch.device(device or "cuda")
-        nbytes = int(lib().ec_huff_workspace_bytes())
+        self.nseg = int(nseg)
+        nbytes = int(lib().ec_huff_workspace_bytes_segments(self.nseg))
+        if nbytes == 0:
+            raise ECError(EC_ERR_INVALID, "ec_huff_workspace_bytes_segments")
         self.workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
         base = self.workspace.data_ptr()
         self._work = (base + 255) // 256 * 256
         self._work_bytes = nbytes
 
     def buffers(self, n: int):
+        """Codebooks, chunk table and words for n symbols in all (n = nseg * seg_len)."""
         import torch
-        nch = (n + HUFF_CHUNK - 1) // HUFF_CHUNK
-        book = torch.zeros(HUFF_BOOK_MAX, dtype=torch.uint8, device=self.device)
+        assert n % self.nseg == 0
+        L = n // self.nseg
+        nch = self.nseg * ((L + HUFF_CHUNK - 1) // HUFF_CHUNK)
+        book = torch.zeros(self.nseg * HUFF_BOOK_MAX, dtype=torch.uint8, device=self.device)
         off = torch.zeros(nch + 1, dtype=torch.int32, device=self.device)
-        words = torch.zeros(max(huff_max_words(n), 1), dtype=torch.int32, device=self.device)
+        words = torch.zeros(max(self.nseg * huff_max_words(L), 1), dtype=torch.int32,
+                            device=self.device)
         return book, off, words
 
     def encode(self, sym, book, chunk_off, words, stream=None):
@@ -292,20 +308,37 @@ class Huffman:
         import torch
         assert sym.dtype == torch.int16 and sym.is_contiguous()
         n = sym.numel()
-        assert book.numel() >= HUFF_BOOK_MAX and chunk_off.numel() >= (n + 255) // 256 + 1
-        _check(lib().ec_huff_encode(sym.data_ptr() if n else None, n, book.data_ptr(),
-                                    chunk_off.data_ptr(), words.data_ptr(), words.numel(),
-                                    self._work, self._work_bytes, _stream_handle(stream)),
-               "ec_huff_encode")
+        assert n % self.nseg == 0
+        L = n // self.nseg
+        assert book.numel() >= self.nseg * HUFF_BOOK_MAX
+        assert chunk_off.numel() >= self.nseg * ((L + 255) // 256) + 1
+        args = (chunk_off.data_ptr(), words.data_ptr(), words.numel(), self._work,
+                self._work_bytes, _stream_handle(stream))
+        p = sym.data_ptr() if n else None
+        if self.nseg == 1:
+            _check(lib().ec_huff_encode(p, n, book.data_ptr(), *args), "ec_huff_encode")
+        else:
+            _check(lib().ec_huff_encode_segments(p, self.nseg, L, book.data_ptr(), *args),
+                   "ec_huff_encode_segments")
 
     def decode(self, book, book_bytes: int, chunk_off, words, n: int, sym, stream=None):
-        """Enqueue decoding of n symbols into the int16 tensor `sym`."""
+        """Enqueue decoding of n symbols in all into the int16 tensor `sym`
+        (book_bytes is used with nseg = 1; segments read HUFF_BOOK_MAX each)."""
         import torch
         assert sym.dtype == torch.int16 and sym.is_contiguous() and sym.numel() >= n
-        _check(lib().ec_huff_decode(book.data_ptr(), int(book_bytes), chunk_off.data_ptr(),
-                                    words.data_ptr() if words.numel() else None, words.numel(),
-                                    n, sym.data_ptr() if n else None, self._work,
-                                    self._work_bytes, _stream_handle(stream)), "ec_huff_decode")
+        assert n % self.nseg == 0
+        w = words.data_ptr() if words.numel() else None
+        p = sym.data_ptr() if n else None
+        if self.nseg == 1:
+            _check(lib().ec_huff_decode(book.data_ptr(), int(book_bytes), chunk_off.data_ptr(), w,
+                                        words.numel(), n, p, self._work, self._work_bytes,
+                                        _stream_handle(stream)), "ec_huff_decode")
+        else:
+            _check(lib().ec_huff_decode_segments(book.data_ptr(), chunk_off.data_ptr(), w,
+                                                 words.numel(), self.nseg, n // self.nseg, p,
+                                                 self._work, self._work_bytes,
+                                                 _stream_handle(stream)),
+                   "ec_huff_decode_segments")
 
     def status(self, stream=None) -> int:
         """Wait for the stream; status of the last call on this workspace."""

@@ -44,27 +44,40 @@ constexpr int kStageWords = kDecChunks * 56;  // LDS words staged per decode wor
 
 enum : uint32_t { kStBadSymbol = 1u, kStCorrupt = 2u, kStDepth = 4u };
 
-// Workspace layout (bytes from the 256-byte aligned base).
-constexpr size_t kOffStatus = 0;                       // u32 [2]: status bits, book valid
-constexpr size_t kOffHist = 256;                       // u32 [4096]
-constexpr size_t kOffEnc = kOffHist + 4 * kTable;      // u32 [4096]: len << 16 | code
-constexpr size_t kOffLut = kOffEnc + 4 * kTable;       // u16 [4096]: sym | len << 12
-constexpr size_t kOffGroups = kOffLut + 2 * kTable;    // u32 [kMaxGroups]
-constexpr size_t kWorkBytes = kOffGroups + 4 * kMaxGroups;
+// Workspace layout (bytes from the 256-byte aligned base) for nseg segments.
+constexpr int kMaxSegments = (int)EC_HUFF_MAX_SEGMENTS;
+constexpr size_t kBookStride = EC_HUFF_BOOK_MAX;
 
 struct Ws {
-  uint32_t* status;
-  uint32_t* hist;
-  uint32_t* enc;
-  uint16_t* lut;
-  uint32_t* groups;
+  uint32_t* status;  // [0]: status bits of the last call
+  uint32_t* valid;   // [nseg]: codebook of the segment passed validation (decode)
+  uint32_t* hist;    // [nseg][4096]; bin 4095 counts symbols outside the alphabet
+  uint32_t* enc;     // [nseg][4096]: len << 16 | code
+  uint16_t* lut;     // [nseg][4096]: sym | len << 12, 0 = no code
+  uint32_t* groups;  // [kMaxGroups]: words per encode group
 };
 
-Ws ws_of(void* base) {
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+size_t work_bytes(uint32_t nseg) {
+  return 256 + round256(4ull * nseg) + (size_t)nseg * (4 + 4 + 2) * kTable + 4ull * kMaxGroups;
+}
+
+Ws ws_of(void* base, uint32_t nseg) {
   uint8_t* b = static_cast<uint8_t*>(base);
-  return Ws{reinterpret_cast<uint32_t*>(b + kOffStatus), reinterpret_cast<uint32_t*>(b + kOffHist),
-            reinterpret_cast<uint32_t*>(b + kOffEnc), reinterpret_cast<uint16_t*>(b + kOffLut),
-            reinterpret_cast<uint32_t*>(b + kOffGroups)};
+  Ws w;
+  w.status = reinterpret_cast<uint32_t*>(b);
+  b += 256;
+  w.valid = reinterpret_cast<uint32_t*>(b);
+  b += round256(4ull * nseg);
+  w.hist = reinterpret_cast<uint32_t*>(b);
+  b += (size_t)nseg * 4 * kTable;
+  w.enc = reinterpret_cast<uint32_t*>(b);
+  b += (size_t)nseg * 4 * kTable;
+  w.lut = reinterpret_cast<uint16_t*>(b);
+  b += (size_t)nseg * 2 * kTable;
+  w.groups = reinterpret_cast<uint32_t*>(b);
+  return w;
 }
 
 __device__ __forceinline__ void status_or(uint32_t* st, uint32_t bits) {
@@ -155,19 +168,24 @@ __device__ void canonical_codes(const uint8_t* len, const uint32_t* first, uint3
   }
 }
 
-__global__ void __launch_bounds__(kThreads) huff_clear(Ws w) {
+// Zero the status word, and the histograms of nhist segments.
+__global__ void __launch_bounds__(kThreads) huff_clear(Ws w, uint32_t nhist) {
   const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
-  if (i < (uint32_t)kTable) w.hist[i] = 0;
-  if (i < 2) w.status[i] = 0;
+  if (i < nhist * (uint32_t)kTable) w.hist[i] = 0;
+  if (i == 0) w.status[0] = 0;
 }
 
-__global__ void __launch_bounds__(kThreads) huff_hist(const uint16_t* __restrict__ sym, uint64_t n,
+// Histogram of segment blockIdx.y (n symbols from sym + blockIdx.y * n).
+__global__ void __launch_bounds__(kThreads) huff_hist(const uint16_t* __restrict__ sym0, uint64_t n,
                                                       Ws w) {
+  const uint16_t* sym = sym0 + (uint64_t)blockIdx.y * n;
+  uint32_t* hist = w.hist + (size_t)blockIdx.y * kTable;
   __shared__ uint32_t h[kTable];
   for (int i = threadIdx.x; i < kTable; i += kThreads) h[i] = 0;
   __syncthreads();
   auto add = [&](uint32_t s) { atomicAdd(&h[s < (uint32_t)kNsym ? s : (uint32_t)kNsym], 1u); };
-  const uint64_t nv = n >> 3, stride = (uint64_t)gridDim.x * kThreads;
+  // 16-byte loads when every segment starts 16-byte aligned
+  const uint64_t nv = (n & 7) == 0 ? n >> 3 : 0, stride = (uint64_t)gridDim.x * kThreads;
   const uint4* v = reinterpret_cast<const uint4*>(sym);
   // four 16-byte loads in flight per lane before their 32 LDS updates
   for (uint64_t i0 = (uint64_t)blockIdx.x * kThreads + threadIdx.x; i0 < nv; i0 += 4 * stride) {
@@ -192,12 +210,17 @@ __global__ void __launch_bounds__(kThreads) huff_hist(const uint16_t* __restrict
     add(sym[i]);
   __syncthreads();
   for (int i = threadIdx.x; i < kTable; i += kThreads)
-    if (h[i]) atomicAdd(&w.hist[i], h[i]);
+    if (h[i]) atomicAdd(&hist[i], h[i]);
 }
 
-__global__ void __launch_bounds__(kBookThreads) huff_book(Ws w, uint8_t* __restrict__ book,
+// Codebook of segment blockIdx.x (n symbols per segment).
+__global__ void __launch_bounds__(kBookThreads) huff_book(Ws w, uint8_t* __restrict__ books,
                                                           uint32_t* __restrict__ chunk_off,
                                                           uint64_t n) {
+  const uint32_t seg = blockIdx.x;
+  const uint32_t* hist = w.hist + (size_t)seg * kTable;
+  uint32_t* enc = w.enc + (size_t)seg * kTable;
+  uint8_t* book = books + (size_t)seg * kBookStride;
   __shared__ uint64_t key[kTable];
   __shared__ uint32_t wt[2 * kTable];
   __shared__ uint32_t pr[2 * kTable];  // parent while building; then ancestor | distance << 16
@@ -220,7 +243,7 @@ __global__ void __launch_bounds__(kBookThreads) huff_book(Ws w, uint8_t* __restr
   // sorted keys backwards gives decreasing frequency, then increasing symbol)
   int cm = 0, lo = kTable, hi = -1;
   for (int s = t; s < kTable; s += kBookThreads) {
-    const uint32_t f = w.hist[s];
+    const uint32_t f = hist[s];
     uint64_t k = ~0ull;
     if (s < kNsym && f) {
       k = ((uint64_t)f << 12) | (uint64_t)(4095 - s);
@@ -377,7 +400,7 @@ __global__ void __launch_bounds__(kBookThreads) huff_book(Ws w, uint8_t* __restr
     len[syms[m - 1 - r]] = (uint8_t)l;
   }
   __syncthreads();
-  canonical_codes(len, first, w.enc, part);
+  canonical_codes(len, first, enc, part);
 
   // codebook bytes
   if (m == 0) {
@@ -396,15 +419,23 @@ __global__ void __launch_bounds__(kBookThreads) huff_book(Ws w, uint8_t* __restr
       book[4 + b] = (uint8_t)(lo4 | hi4 << 4);
     }
   }
-  if (n == 0 && t == 0) chunk_off[0] = 0;
+  if (n == 0 && seg == 0 && t == 0) chunk_off[0] = 0;
 }
 
-__global__ void __launch_bounds__(kThreads) huff_size(const uint16_t* __restrict__ sym, uint64_t n,
+// Words of every chunk of group blockIdx.x of segment blockIdx.y (n symbols
+// and nch chunks per segment; chunk c of segment s is chunk s*nch + c of the
+// chunk table).
+__global__ void __launch_bounds__(kThreads) huff_size(const uint16_t* __restrict__ sym0, uint64_t n,
                                                       Ws w, uint32_t* __restrict__ chunk_off,
                                                       uint32_t nch, uint32_t per_group) {
   __shared__ uint8_t lens[kTable];
   __shared__ uint32_t wsum[kThreads / 64];
-  for (int i = threadIdx.x; i < kTable; i += kThreads) lens[i] = (uint8_t)(w.enc[i] >> 16);
+  const uint32_t seg = blockIdx.y;
+  const uint16_t* sym = sym0 + (uint64_t)seg * n;
+  chunk_off += (size_t)seg * nch;
+  const bool vec = (n & 3) == 0;  // 8-byte loads when segments start 8-byte aligned
+  for (int i = threadIdx.x; i < kTable; i += kThreads)
+    lens[i] = (uint8_t)(w.enc[(size_t)seg * kTable + i] >> 16);
   __syncthreads();
   const uint32_t wv = threadIdx.x >> 6, ln = lane_id();
   const uint32_t c0 = blockIdx.x * per_group, c1 = min(c0 + per_group, nch);
@@ -413,7 +444,7 @@ __global__ void __launch_bounds__(kThreads) huff_size(const uint16_t* __restrict
     const uint64_t base = (uint64_t)c * kChunk;
     const uint64_t cnt = min((uint64_t)kChunk, n - base);
     uint32_t b = 0;
-    if (cnt == (uint64_t)kChunk) {
+    if (vec && cnt == (uint64_t)kChunk) {
       const uint2 q = reinterpret_cast<const uint2*>(sym + base)[ln];
       b = lens[min(q.x & 0xFFFFu, 4095u)] + lens[min(q.x >> 16, 4095u)] +
           lens[min(q.y & 0xFFFFu, 4095u)] + lens[min(q.y >> 16, 4095u)];
@@ -432,12 +463,15 @@ __global__ void __launch_bounds__(kThreads) huff_size(const uint16_t* __restrict
   if (threadIdx.x == 0) {
     uint32_t s = 0;
     for (int i = 0; i < kThreads / 64; i++) s += wsum[i];
-    w.groups[blockIdx.x] = s;
+    w.groups[seg * gridDim.x + blockIdx.x] = s;
   }
 }
 
-__global__ void __launch_bounds__(kThreads) huff_write(const uint16_t* __restrict__ sym, uint64_t n,
-                                                       Ws w, uint32_t* __restrict__ chunk_off,
+// Chunk offsets and words of group blockIdx.x of segment blockIdx.y; groups
+// are ordered segment by segment, so the words of all segments follow each
+// other in one array.
+__global__ void __launch_bounds__(kThreads) huff_write(const uint16_t* __restrict__ sym0, uint64_t n,
+                                                       Ws w, uint32_t* __restrict__ chunk_off0,
                                                        uint32_t nch, uint32_t per_group,
                                                        uint32_t* __restrict__ words) {
   __shared__ uint32_t enc[kTable];
@@ -445,15 +479,19 @@ __global__ void __launch_bounds__(kThreads) huff_write(const uint16_t* __restric
   __shared__ uint32_t buf[kThreads / 64][kChunkWords];
   __shared__ uint32_t part[16];
   const uint32_t t = threadIdx.x, wv = t >> 6, ln = lane_id();
-  for (int i = t; i < kTable; i += kThreads) enc[i] = w.enc[i];
+  const uint32_t seg = blockIdx.y, gi = seg * gridDim.x + blockIdx.x;
+  const uint16_t* sym = sym0 + (uint64_t)seg * n;
+  uint32_t* chunk_off = chunk_off0 + (size_t)seg * nch;
+  const bool vec = (n & 3) == 0;
+  for (int i = t; i < kTable; i += kThreads) enc[i] = w.enc[(size_t)seg * kTable + i];
   for (int i = t; i < kChunkWords * (kThreads / 64); i += kThreads) (&buf[0][0])[i] = 0;
   // words of all groups before this one
   uint32_t before = 0;
-  for (uint32_t g = t; g < blockIdx.x; g += kThreads) before += w.groups[g];
+  for (uint32_t g = t; g < gi; g += kThreads) before += w.groups[g];
   uint32_t base;
   block_excl(before, part, &base);
   const uint32_t c0 = blockIdx.x * per_group, c1 = min(c0 + per_group, nch);
-  if (blockIdx.x == 0 && t == 0) chunk_off[0] = 0;
+  if (gi == 0 && t == 0) chunk_off0[0] = 0;
   for (uint32_t r0 = c0; r0 < c1; r0 += kThreads) {
     const uint32_t c = r0 + t;
     const uint32_t cw = c < c1 ? chunk_off[c + 1] : 0u;
@@ -471,7 +509,7 @@ __global__ void __launch_bounds__(kThreads) huff_write(const uint16_t* __restric
         const uint64_t sbase = (uint64_t)cc * kChunk;
         const uint64_t cnt = min((uint64_t)kChunk, n - sbase);
         uint32_t s[4];
-        if (cnt == (uint64_t)kChunk) {
+        if (vec && cnt == (uint64_t)kChunk) {
           const uint2 q = reinterpret_cast<const uint2*>(sym + sbase)[ln];
           s[0] = q.x & 0xFFFFu;
           s[1] = q.x >> 16;
@@ -524,10 +562,16 @@ __global__ void __launch_bounds__(kThreads) huff_write(const uint16_t* __restric
   }
 }
 
-__global__ void __launch_bounds__(kBookThreads) huff_dec_book(const uint8_t* __restrict__ book,
+// Validate the codebook of segment blockIdx.x (book_bytes readable bytes at
+// books + blockIdx.x * EC_HUFF_BOOK_MAX) and build its prefix table.
+__global__ void __launch_bounds__(kBookThreads) huff_dec_book(const uint8_t* __restrict__ books,
                                                           uint64_t book_bytes,
                                                           const uint32_t* __restrict__ chunk_off,
                                                           uint64_t n, Ws w) {
+  const uint32_t seg = blockIdx.x;
+  const uint8_t* book = books + (size_t)seg * kBookStride;
+  uint32_t* enc = w.enc + (size_t)seg * kTable;
+  uint16_t* lut = w.lut + (size_t)seg * kTable;
   __shared__ uint8_t len[kTable];
   __shared__ uint16_t order[kTable];
   __shared__ uint32_t cnt[kMaxLen + 1], first[kMaxLen + 1], base[kMaxLen + 1];
@@ -539,7 +583,6 @@ __global__ void __launch_bounds__(kBookThreads) huff_dec_book(const uint8_t* __r
     s_bad = 0;
     s_kraft = 0;
     s_m = 0;
-    w.status[0] = 0;
   }
   if (t <= kMaxLen) cnt[t] = 0;
   for (int i = t; i < kTable; i += kBookThreads) len[i] = 0;
@@ -559,7 +602,7 @@ __global__ void __launch_bounds__(kBookThreads) huff_dec_book(const uint8_t* __r
   }
   const bool empty = !bad && hi < lo;
   if (empty && n > 0) bad = 1;
-  if (t == 0 && chunk_off[0] != 0) bad = 1;
+  if (seg == 0 && t == 0 && chunk_off[0] != 0) bad = 1;
   if (!bad && !empty) {
     const uint32_t nb = hi - lo + 1;
     uint32_t kr = 0, mm = 0;
@@ -593,7 +636,7 @@ __global__ void __launch_bounds__(kBookThreads) huff_dec_book(const uint8_t* __r
   if (s_bad) {
     if (t == 0) {
       status_or(w.status, kStCorrupt);
-      w.status[1] = 0;
+      w.valid[seg] = 0;
     }
     return;
   }
@@ -605,13 +648,13 @@ __global__ void __launch_bounds__(kBookThreads) huff_dec_book(const uint8_t* __r
       base[l] = idx;
       idx += cnt[l];
     }
-    w.status[1] = 1;
+    w.valid[seg] = 1;
   }
   __syncthreads();
-  canonical_codes(len, first, w.enc, part);
+  canonical_codes(len, first, enc, part);
   __syncthreads();
   for (int s = t; s < kNsym; s += kBookThreads) {
-    const uint32_t e = w.enc[s], l = e >> 16;
+    const uint32_t e = enc[s], l = e >> 16;
     if (l) order[base[l] + (e & 0xFFFFu) - first[l]] = (uint16_t)s;
   }
   __syncthreads();
@@ -625,7 +668,7 @@ __global__ void __launch_bounds__(kBookThreads) huff_dec_book(const uint8_t* __r
         break;
       }
     }
-    w.lut[i] = (uint16_t)e;
+    lut[i] = (uint16_t)e;
   }
 }
 
@@ -634,7 +677,7 @@ __global__ void __launch_bounds__(kBookThreads) huff_dec_book(const uint8_t* __r
 // whether it really ends in its last word is decided from the bits consumed.
 // Returns false if the chunk is malformed.
 __device__ __forceinline__ bool decode_chunk(const uint32_t* src, uint32_t nwords, uint32_t rem,
-                                             const uint16_t* lut, uint16_t* out) {
+                                             const uint16_t* lut, uint16_t* out, bool vec) {
   // two words are loaded ahead of the bit buffer, so a refill never waits
   uint32_t q0 = nwords > 0 ? src[0] : 0u, q1 = nwords > 1 ? src[1] : 0u, p = 2;
   uint64_t bitbuf = 0;
@@ -660,10 +703,11 @@ __device__ __forceinline__ bool decode_chunk(const uint32_t* src, uint32_t nword
       used += l;
       pk[k >> 1] |= (ent & 0xFFFu) << (16 * (k & 1));
     }
-    if (g + 8 <= rem) {
+    if (vec && g + 8 <= rem) {
       *reinterpret_cast<uint4*>(out + g) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
     } else {
-      for (uint32_t k = 0; k < rem - g; k++) out[g + k] = (uint16_t)(pk[k >> 1] >> (16 * (k & 1)));
+      for (uint32_t k = 0; k < min(rem - g, 8u); k++)
+        out[g + k] = (uint16_t)(pk[k >> 1] >> (16 * (k & 1)));
     }
   }
   // every consumed bit lies in the chunk, the chunk's last word holds some of
@@ -678,7 +722,7 @@ __device__ __forceinline__ bool decode_chunk(const uint32_t* src, uint32_t nword
 // lookup.  Words past the chunk read as zero.  nwords >= 1.
 __device__ __forceinline__ bool decode_chunk_lds(const uint32_t* src, uint32_t nwords,
                                                  uint32_t rem, const uint16_t* lut,
-                                                 uint16_t* out) {
+                                                 uint16_t* out, bool vec) {
   const uint32_t last = nwords - 1;
   uint64_t bitbuf = (uint64_t)src[0] << 32;
   uint32_t have = 32, used = 0;
@@ -707,41 +751,46 @@ __device__ __forceinline__ bool decode_chunk_lds(const uint32_t* src, uint32_t n
       wq = rf ? wn : wq;
       p += rf ? 1u : 0u;
     }
-    if (g + 32 <= rem) {  // 64 bytes of one chunk at a time
+    if (vec && g + 32 <= rem) {  // 64 bytes of one chunk at a time
 #pragma unroll
       for (int q = 0; q < 4; q++)
         *reinterpret_cast<uint4*>(out + g + 8 * q) =
             make_uint4(pk[4 * q], pk[4 * q + 1], pk[4 * q + 2], pk[4 * q + 3]);
     } else {
-      for (uint32_t k = 0; k < rem - g; k++) out[g + k] = (uint16_t)(pk[k >> 1] >> (16 * (k & 1)));
+      for (uint32_t k = 0; k < min(rem - g, 32u); k++)
+        out[g + k] = (uint16_t)(pk[k >> 1] >> (16 * (k & 1)));
     }
   }
   return !(bad || used > 32 * nwords || used + 32 <= 32 * nwords || bitbuf != 0);
 }
 
+// Chunks [128 blockIdx.x, 128 blockIdx.x + 128) of segment blockIdx.y.
 __global__ void __launch_bounds__(kDecChunks) huff_decode(const uint32_t* __restrict__ words,
                                                           uint64_t words_cap,
-                                                          const uint32_t* __restrict__ chunk_off,
+                                                          const uint32_t* __restrict__ chunk_off0,
                                                           uint64_t n, uint32_t nch, Ws w,
-                                                          uint16_t* __restrict__ sym) {
+                                                          uint16_t* __restrict__ sym0) {
   __shared__ uint16_t lut[kTable];
   __shared__ uint32_t stage[kStageWords];
   __shared__ uint32_t s_lo, s_hi;
-  const uint32_t t = threadIdx.x;
+  const uint32_t t = threadIdx.x, seg = blockIdx.y;
   const uint32_t c0 = blockIdx.x * kDecChunks, c = c0 + t;
   const uint32_t cend = min(c0 + kDecChunks, nch);
+  const uint32_t* chunk_off = chunk_off0 + (size_t)seg * nch;
+  uint16_t* sym = sym0 + (uint64_t)seg * n;
+  const bool vec = (n & 7) == 0;  // 16-byte stores when segments start 16-byte aligned
   {
-    const uint4* src = reinterpret_cast<const uint4*>(w.lut);
+    const uint4* src = reinterpret_cast<const uint4*>(w.lut + (size_t)seg * kTable);
     uint4* dst = reinterpret_cast<uint4*>(lut);
     for (int i = t; i < kTable * 2 / 16; i += kDecChunks) dst[i] = src[i];
   }
-  bool ok = w.status[1] != 0;
+  bool ok = w.valid[seg] != 0;
   uint32_t a = 0, b = 0;
   if (c < cend) {
     a = chunk_off[c];
     b = chunk_off[c + 1];
     ok = ok && a <= b && b - a <= (uint32_t)kChunkWords && (uint64_t)b <= words_cap;
-    if (c == 0) ok = ok && a == 0;
+    if (seg == 0 && c == 0) ok = ok && a == 0;
   }
   if (c == c0) s_lo = a;
   if (c + 1 == cend) s_hi = b;
@@ -760,8 +809,8 @@ __global__ void __launch_bounds__(kDecChunks) huff_decode(const uint32_t* __rest
   const uint64_t sbase = (uint64_t)c * kChunk;
   const uint32_t rem = (uint32_t)min((uint64_t)kChunk, n - sbase);
   const bool good = b == a ? false
-                    : staged ? decode_chunk_lds(stage + (a - glo), b - a, rem, lut, sym + sbase)
-                             : decode_chunk(words + a, b - a, rem, lut, sym + sbase);
+                    : staged ? decode_chunk_lds(stage + (a - glo), b - a, rem, lut, sym + sbase, vec)
+                             : decode_chunk(words + a, b - a, rem, lut, sym + sbase, vec);
   if (!good) status_or(w.status, kStCorrupt);
 }
 
@@ -769,64 +818,111 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 uint32_t num_chunks(uint64_t n) { return (uint32_t)((n + kChunk - 1) / kChunk); }
 
-}  // namespace
-
-extern "C" {
-
-size_t ec_huff_workspace_bytes(void) { return kWorkBytes; }
-
-uint64_t ec_huff_max_words(uint64_t n) {
+uint64_t max_words(uint64_t n) {
   const uint64_t full = n / kChunk, rem = n % kChunk;
   return full * kChunkWords + (rem * kMaxLen + 31) / 32;
 }
 
-ec_status ec_huff_encode(const uint16_t* d_sym, uint64_t n, uint8_t* d_book,
-                         uint32_t* d_chunk_off, uint32_t* d_words, uint64_t words_cap,
-                         void* d_work, size_t work_bytes, void* stream) {
-  if (!d_book || !d_chunk_off || !d_work || n > EC_HUFF_MAX_SYMBOLS) return EC_ERR_INVALID;
+ec_status check_common(const void* d_books, const void* d_chunk_off, const void* d_sym,
+                       const void* d_words, void* d_work, uint32_t nseg, uint64_t n) {
+  if (!d_books || !d_chunk_off || !d_work || nseg == 0 || nseg > (uint32_t)kMaxSegments)
+    return EC_ERR_INVALID;
+  if ((uint64_t)nseg * n > EC_HUFF_MAX_SYMBOLS) return EC_ERR_INVALID;
   if (n && (!d_sym || !d_words)) return EC_ERR_INVALID;
   if (!aligned16(d_sym) || !aligned16(d_words) || ((uintptr_t)d_work & 255u)) return EC_ERR_INVALID;
-  if (work_bytes < kWorkBytes || words_cap < ec_huff_max_words(n)) return EC_ERR_CAPACITY;
+  return EC_OK;
+}
+
+ec_status encode_impl(const uint16_t* d_sym, uint32_t nseg, uint64_t n, uint8_t* d_books,
+                      uint32_t* d_chunk_off, uint32_t* d_words, uint64_t words_cap, void* d_work,
+                      size_t wbytes, void* stream) {
+  const ec_status st = check_common(d_books, d_chunk_off, d_sym, d_words, d_work, nseg, n);
+  if (st != EC_OK) return st;
+  if (wbytes < work_bytes(nseg) || words_cap < nseg * max_words(n)) return EC_ERR_CAPACITY;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const Ws w = ws_of(d_work);
-  hipLaunchKernelGGL(huff_clear, dim3(kTable / kThreads), dim3(kThreads), 0, s, w);
+  const Ws w = ws_of(d_work, nseg);
+  hipLaunchKernelGGL(huff_clear, dim3(nseg * (kTable / kThreads)), dim3(kThreads), 0, s, w, nseg);
   if (n) {
-    const uint64_t vec_blocks = (n / 8 + kThreads * 4 - 1) / (kThreads * 4);
-    const uint32_t hb = (uint32_t)(vec_blocks < 1 ? 1 : (vec_blocks > 1024 ? 1024 : vec_blocks));
-    hipLaunchKernelGGL(huff_hist, dim3(hb), dim3(kThreads), 0, s, d_sym, n, w);
+    const uint64_t want = (n / 8 + kThreads * 4 - 1) / (kThreads * 4);
+    const uint64_t cap = 1024 / nseg > 0 ? 1024 / nseg : 1;
+    const uint32_t hb = (uint32_t)(want < 1 ? 1 : (want > cap ? cap : want));
+    hipLaunchKernelGGL(huff_hist, dim3(hb, nseg), dim3(kThreads), 0, s, d_sym, n, w);
   }
-  hipLaunchKernelGGL(huff_book, dim3(1), dim3(kBookThreads), 0, s, w, d_book, d_chunk_off, n);
+  hipLaunchKernelGGL(huff_book, dim3(nseg), dim3(kBookThreads), 0, s, w, d_books, d_chunk_off, n);
   if (n) {
     const uint32_t nch = num_chunks(n);
     uint32_t groups = (nch + 3) / 4;
-    if (groups > (uint32_t)kMaxGroups) groups = kMaxGroups;
+    const uint32_t gmax = (uint32_t)kMaxGroups / nseg;
+    if (groups > gmax) groups = gmax;
     const uint32_t per = (nch + groups - 1) / groups;
     groups = (nch + per - 1) / per;
-    hipLaunchKernelGGL(huff_size, dim3(groups), dim3(kThreads), 0, s, d_sym, n, w, d_chunk_off,
-                       nch, per);
-    hipLaunchKernelGGL(huff_write, dim3(groups), dim3(kThreads), 0, s, d_sym, n, w, d_chunk_off,
-                       nch, per, d_words);
+    hipLaunchKernelGGL(huff_size, dim3(groups, nseg), dim3(kThreads), 0, s, d_sym, n, w,
+                       d_chunk_off, nch, per);
+    hipLaunchKernelGGL(huff_write, dim3(groups, nseg), dim3(kThreads), 0, s, d_sym, n, w,
+                       d_chunk_off, nch, per, d_words);
   }
   return hipGetLastError() == hipSuccess ? EC_OK : EC_ERR_DEVICE;
+}
+
+ec_status decode_impl(const uint8_t* d_books, uint64_t book_bytes, const uint32_t* d_chunk_off,
+                      const uint32_t* d_words, uint64_t words_cap, uint32_t nseg, uint64_t n,
+                      uint16_t* d_sym, void* d_work, size_t wbytes, void* stream) {
+  const ec_status st = check_common(d_books, d_chunk_off, d_sym, d_words, d_work, nseg, n);
+  if (st != EC_OK) return st;
+  if (wbytes < work_bytes(nseg)) return EC_ERR_CAPACITY;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Ws w = ws_of(d_work, nseg);
+  hipLaunchKernelGGL(huff_clear, dim3(1), dim3(kThreads), 0, s, w, 0u);
+  hipLaunchKernelGGL(huff_dec_book, dim3(nseg), dim3(kBookThreads), 0, s, d_books, book_bytes,
+                     d_chunk_off, n, w);
+  if (n) {
+    const uint32_t nch = num_chunks(n);
+    hipLaunchKernelGGL(huff_decode, dim3((nch + kDecChunks - 1) / kDecChunks, nseg),
+                       dim3(kDecChunks), 0, s, d_words, words_cap, d_chunk_off, n, nch, w, d_sym);
+  }
+  return hipGetLastError() == hipSuccess ? EC_OK : EC_ERR_DEVICE;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ec_huff_workspace_bytes(void) { return work_bytes(1); }
+
+size_t ec_huff_workspace_bytes_segments(uint32_t nseg) {
+  return nseg == 0 || nseg > (uint32_t)kMaxSegments ? 0 : work_bytes(nseg);
+}
+
+uint64_t ec_huff_max_words(uint64_t n) { return max_words(n); }
+
+ec_status ec_huff_encode(const uint16_t* d_sym, uint64_t n, uint8_t* d_book,
+                         uint32_t* d_chunk_off, uint32_t* d_words, uint64_t words_cap,
+                         void* d_work, size_t work_bytes, void* stream) {
+  return encode_impl(d_sym, 1, n, d_book, d_chunk_off, d_words, words_cap, d_work, work_bytes,
+                     stream);
+}
+
+ec_status ec_huff_encode_segments(const uint16_t* d_sym, uint32_t nseg, uint64_t seg_len,
+                                  uint8_t* d_books, uint32_t* d_chunk_off, uint32_t* d_words,
+                                  uint64_t words_cap, void* d_work, size_t work_bytes,
+                                  void* stream) {
+  return encode_impl(d_sym, nseg, seg_len, d_books, d_chunk_off, d_words, words_cap, d_work,
+                     work_bytes, stream);
 }
 
 ec_status ec_huff_decode(const uint8_t* d_book, uint64_t book_bytes, const uint32_t* d_chunk_off,
                          const uint32_t* d_words, uint64_t words_cap, uint64_t n,
                          uint16_t* d_sym, void* d_work, size_t work_bytes, void* stream) {
-  if (!d_book || !d_chunk_off || !d_work || n > EC_HUFF_MAX_SYMBOLS) return EC_ERR_INVALID;
-  if (n && (!d_sym || !d_words)) return EC_ERR_INVALID;
-  if (!aligned16(d_sym) || !aligned16(d_words) || ((uintptr_t)d_work & 255u)) return EC_ERR_INVALID;
-  if (work_bytes < kWorkBytes) return EC_ERR_CAPACITY;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const Ws w = ws_of(d_work);
-  hipLaunchKernelGGL(huff_dec_book, dim3(1), dim3(kBookThreads), 0, s, d_book, book_bytes, d_chunk_off,
-                     n, w);
-  if (n) {
-    const uint32_t nch = num_chunks(n);
-    hipLaunchKernelGGL(huff_decode, dim3((nch + kDecChunks - 1) / kDecChunks), dim3(kDecChunks), 0,
-                       s, d_words, words_cap, d_chunk_off, n, nch, w, d_sym);
-  }
-  return hipGetLastError() == hipSuccess ? EC_OK : EC_ERR_DEVICE;
+  return decode_impl(d_book, book_bytes, d_chunk_off, d_words, words_cap, 1, n, d_sym, d_work,
+                     work_bytes, stream);
+}
+
+ec_status ec_huff_decode_segments(const uint8_t* d_books, const uint32_t* d_chunk_off,
+                                  const uint32_t* d_words, uint64_t words_cap, uint32_t nseg,
+                                  uint64_t seg_len, uint16_t* d_sym, void* d_work,
+                                  size_t work_bytes, void* stream) {
+  return decode_impl(d_books, EC_HUFF_BOOK_MAX, d_chunk_off, d_words, words_cap, nseg, seg_len,
+                     d_sym, d_work, work_bytes, stream);
 }
 
 ec_status ec_huff_status(void* d_work, void* stream) {

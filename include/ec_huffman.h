@@ -51,10 +51,15 @@ extern "C" {
 #define EC_HUFF_MAXLEN 12u
 #define EC_HUFF_CHUNK 256u
 #define EC_HUFF_BOOK_MAX (4u + (EC_HUFF_NSYM + 1u) / 2u) /* 2052 bytes        */
-#define EC_HUFF_MAX_SYMBOLS 0x7FFFFFFFull                /* n < 2^31          */
+#define EC_HUFF_MAX_SYMBOLS 0x7FFFFFFFull                /* n < 2^31 in all   */
+#define EC_HUFF_MAX_SEGMENTS 2048u
 
 /* Workspace bytes one encode or decode call needs (independent of n). */
 size_t ec_huff_workspace_bytes(void);
+
+/* Workspace bytes of a call over nseg segments (0 if nseg is 0 or above
+ * EC_HUFF_MAX_SEGMENTS). */
+size_t ec_huff_workspace_bytes_segments(uint32_t nseg);
 
 /* Words an encoded stream of n symbols can take at most (12 bits per symbol,
  * every chunk rounded up to whole words). */
@@ -82,6 +87,29 @@ ec_status ec_huff_encode(const uint16_t* d_sym, uint64_t n, uint8_t* d_book,
 ec_status ec_huff_decode(const uint8_t* d_book, uint64_t book_bytes, const uint32_t* d_chunk_off,
                          const uint32_t* d_words, uint64_t words_cap, uint64_t n,
                          uint16_t* d_sym, void* d_work, size_t work_bytes, void* stream);
+
+/* Segments: nseg consecutive runs of seg_len symbols each (one per embedding
+ * table, say), every one coded with a codebook of its own, as ec_huff_encode
+ * would code it alone.  Chunks never cross segments: segment s owns chunks
+ * [s*C, (s+1)*C) of the chunk table, C = ceil(seg_len / 256), which has
+ * nseg*C + 1 entries; the words of all segments follow each other in one
+ * array (offsets in the table are from its start).  Codebook s sits at
+ * d_books + s * EC_HUFF_BOOK_MAX.  words_cap >= nseg * ec_huff_max_words(
+ * seg_len); the workspace holds ec_huff_workspace_bytes_segments(nseg) bytes.
+ * Errors as for ec_huff_encode, plus EC_ERR_INVALID for nseg outside
+ * [1, EC_HUFF_MAX_SEGMENTS] or nseg * seg_len > EC_HUFF_MAX_SYMBOLS. */
+ec_status ec_huff_encode_segments(const uint16_t* d_sym, uint32_t nseg, uint64_t seg_len,
+                                  uint8_t* d_books, uint32_t* d_chunk_off, uint32_t* d_words,
+                                  uint64_t words_cap, void* d_work, size_t work_bytes,
+                                  void* stream);
+
+/* Decode what ec_huff_encode_segments wrote (each codebook has
+ * EC_HUFF_BOOK_MAX readable bytes); validation as for ec_huff_decode, per
+ * segment. */
+ec_status ec_huff_decode_segments(const uint8_t* d_books, const uint32_t* d_chunk_off,
+                                  const uint32_t* d_words, uint64_t words_cap, uint32_t nseg,
+                                  uint64_t seg_len, uint16_t* d_sym, void* d_work,
+                                  size_t work_bytes, void* stream);
 
 /* Wait for `stream`, then return the device status of the last encode or
  * decode call that used this workspace: EC_OK, EC_ERR_INVALID (symbol out of

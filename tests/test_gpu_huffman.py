@@ -189,3 +189,96 @@ def test_damaged_streams_are_rejected_like_the_oracle(coder):
         assert st in (ec.EC_OK, ec.EC_ERR_CORRUPT), name
         if ok:
             assert np.array_equal(out, ref), name
+
+
+def oracle_encode_segments(sym: np.ndarray, nseg: int):
+    """The oracle's coder applied to each segment alone; chunk tables and
+    words concatenated with the earlier segments' word counts added."""
+    L = sym.size // nseg
+    books, offs, words, base = [], [], [], 0
+    for s in range(nseg):
+        b, o, w, _ = oracle_encode(sym[s * L:(s + 1) * L])
+        books.append(b)
+        offs.append(o[:-1].astype(np.int64) + base)
+        words.append(w)
+        base += w.size
+    off = np.concatenate(offs + [np.array([base])]).astype(np.uint32)
+    return books, off, np.concatenate(words).astype(np.uint32) if words else np.zeros(0, np.uint32)
+
+
+def check_segments(nseg: int, sym: np.ndarray, what: str):
+    say(f"[huffman segments] {what} nseg={nseg} seg_len={sym.size // nseg}")
+    coder = ec.Huffman("cuda", nseg=nseg)
+    books, ro, rw = oracle_encode_segments(sym, nseg)
+    n = sym.size
+    book, off, words = coder.buffers(n)
+    s = torch.from_numpy(sym.astype(np.uint16).view(np.int16)).cuda()
+    coder.encode(s, book, off, words)
+    assert coder.status() == ec.EC_OK
+    go = off.cpu().numpy().view(np.uint32)
+    gw = words.cpu().numpy().view(np.uint32)[: int(go[-1])]
+    gb = book.cpu().numpy()
+    for k in range(nseg):
+        bk = gb[k * ec.HUFF_BOOK_MAX:(k + 1) * ec.HUFF_BOOK_MAX]
+        assert np.array_equal(bk[: ec.huff_book_bytes(bk)], books[k]), f"codebook {k}"
+    assert np.array_equal(go, ro), "chunk table differs"
+    assert np.array_equal(gw, rw), f"words differ at {np.flatnonzero(gw != rw)[:8]}"
+    out = torch.zeros(max(n, 1), dtype=torch.int16, device="cuda")
+    coder.decode(book, ec.HUFF_BOOK_MAX, off, words, n, out)
+    assert coder.status() == ec.EC_OK
+    assert np.array_equal(out[:n].cpu().numpy().view(np.uint16), sym.astype(np.uint16))
+    return coder, book, off, words
+
+
+@pytest.mark.parametrize("nseg,L", [(2, 1000), (5, 256), (3, 257), (7, 1), (4, 13), (26, 4096),
+                                    (6, 0), (3, 70_003), (40, 300)])
+def test_segments_have_codebooks_of_their_own(nseg, L):
+    """Segments of different widths and offsets (so that codebooks differ),
+    lengths that are and are not multiples of 4, 8 and 256."""
+    rng = np.random.default_rng(nseg * 1000 + L)
+    parts = []
+    for k in range(nseg):
+        scale = [0.3, 4.0, 60.0][k % 3]
+        q = np.clip(np.rint(rng.laplace(5 * k, scale, L)), -2047, 2047).astype(np.int64)
+        parts.append((q + 2047).astype(np.uint16))
+    sym = np.concatenate(parts) if parts else np.zeros(0, np.uint16)
+    check_segments(nseg, sym, "laplace")
+
+
+def test_segments_with_degenerate_members():
+    """One segment with a single symbol, one with the whole alphabet, one with
+    Fibonacci weights that hit the 12-bit limit."""
+    L = 4095 * 3
+    rng = np.random.default_rng(5)
+    a = np.full(L, 100, np.uint16)
+    b = np.tile(np.arange(4095, dtype=np.uint16), 3)
+    rng.shuffle(b)
+    f, x, y = [], 1, 1
+    while sum(f) < L:
+        f.append(x)
+        x, y = y, x + y
+    c = np.repeat(np.arange(2000, 2000 + len(f)), f)[:L].astype(np.uint16)
+    rng.shuffle(c)
+    check_segments(3, np.concatenate([a, b, c]), "degenerate")
+
+
+def test_segments_full_size_per_table_codebooks():
+    """The 26x8192x128 batch's codes with one codebook per table."""
+    import synth
+    import bench
+    w = synth.workload("c3", iteration=3, device="cuda")
+    sym = bench.workload_codes(w, torch).cpu().numpy().view(np.uint16)
+    check_segments(26, sym, "c3 per table")
+
+
+def test_segments_reject_a_damaged_codebook():
+    rng = np.random.default_rng(8)
+    sym = np.concatenate([laplace_codes(rng, 3000, 3.0), laplace_codes(rng, 3000, 30.0)])
+    coder, book, off, words = check_segments(2, sym, "for damage")
+    bad = book.clone()
+    bad[ec.HUFF_BOOK_MAX + 4] ^= 0x10  # a length in segment 1's codebook: no longer complete
+    out = torch.zeros(sym.size, dtype=torch.int16, device="cuda")
+    coder.decode(bad, ec.HUFF_BOOK_MAX, off, words, sym.size, out)
+    assert coder.status() == ec.EC_ERR_CORRUPT
+    coder.decode(book, ec.HUFF_BOOK_MAX, off, words, sym.size, out)
+    assert coder.status() == ec.EC_OK
