@@ -97,3 +97,18 @@ def test_huffman_entry_points_check_arguments_on_the_host():
     assert dec(None, 4, fake, fake, 10, 10, fake, fake, wb, None) == ec.EC_ERR_INVALID
     assert dec(fake, 4, fake, fake, 10, 10, fake, fake, wb - 1, None) == ec.EC_ERR_CAPACITY
     assert L.ec_huff_status(None, None) == ec.EC_ERR_INVALID
+    # segments: a workspace per segment count, limits checked on the host
+    assert L.ec_huff_workspace_bytes_segments(0) == 0
+    assert L.ec_huff_workspace_bytes_segments(2049) == 0
+    assert L.ec_huff_workspace_bytes_segments(1) == wb
+    w26 = L.ec_huff_workspace_bytes_segments(26)
+    assert w26 > wb and w26 - wb >= 25 * 10 * 4096  # histogram, codes, table per segment
+    es = L.ec_huff_encode_segments
+    assert es(fake, 0, 100, fake, fake, fake, 10**6, fake, w26, None) == ec.EC_ERR_INVALID
+    assert es(fake, 2049, 100, fake, fake, fake, 10**8, fake, 1 << 30, None) == ec.EC_ERR_INVALID
+    assert es(fake, 26, 1 << 27, fake, fake, fake, 1 << 40, fake, w26, None) == ec.EC_ERR_INVALID
+    assert es(fake, 26, 1000, fake, fake, fake, 26 * 375 - 1, fake, w26, None) == ec.EC_ERR_CAPACITY
+    assert es(fake, 26, 1000, fake, fake, fake, 10**6, fake, wb, None) == ec.EC_ERR_CAPACITY
+    ds = L.ec_huff_decode_segments
+    assert ds(fake, fake, fake, 10, 0, 10, fake, fake, w26, None) == ec.EC_ERR_INVALID
+    assert ds(fake, fake, fake, 10, 26, 10, fake, fake, wb, None) == ec.EC_ERR_CAPACITY
