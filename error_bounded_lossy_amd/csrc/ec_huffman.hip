@@ -86,19 +86,22 @@ __device__ __forceinline__ void status_or(uint32_t* st, uint32_t bits) {
 
 __device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & 63u; }
 
-__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
-  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
+// Inclusive prefix sum over the wave with DPP moves (no LDS round trips):
+// shifts by 1, 2, 4 and 8 lanes within each row of 16 (lanes with no source
+// add 0), then row 0's total into row 1 and row 2's into row 3 (broadcast of
+// lane 15 of the row before), then lane 31's sum into rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_incl(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
   return x;
 }
 
-// Inclusive prefix sum over the wave.
-__device__ __forceinline__ uint32_t wave_incl(uint32_t x) {
-  const uint32_t ln = lane_id();
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_up(x, d, 64);
-    if (ln >= (uint32_t)d) x += y;
-  }
-  return x;
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl(x), 63);
 }
 
 __device__ __forceinline__ uint64_t wave_incl64(uint64_t x) {
@@ -475,7 +478,7 @@ __global__ void __launch_bounds__(kThreads) huff_write(const uint16_t* __restric
                                                        uint32_t nch, uint32_t per_group,
                                                        uint32_t* __restrict__ words) {
   __shared__ uint32_t enc[kTable];
-  __shared__ uint32_t offs[kThreads];
+  __shared__ uint32_t offs[kThreads], cnts[kThreads];
   __shared__ uint32_t buf[kThreads / 64][kChunkWords];
   __shared__ uint32_t part[16];
   const uint32_t t = threadIdx.x, wv = t >> 6, ln = lane_id();
@@ -499,6 +502,7 @@ __global__ void __launch_bounds__(kThreads) huff_write(const uint16_t* __restric
     const uint32_t ex = block_excl(cw, part, &total);
     if (c < c1) chunk_off[c + 1] = base + ex + cw;
     offs[t] = base + ex;
+    cnts[t] = cw;
     base += total;
     __syncthreads();
     for (uint32_t j0 = 0; j0 < (uint32_t)kThreads; j0 += kThreads / 64) {
@@ -530,7 +534,7 @@ __global__ void __launch_bounds__(kThreads) huff_write(const uint16_t* __restric
           nb += l;
         }
         const uint32_t inc = wave_incl(nb);
-        nbits_wave = __shfl(inc, 63, 64);
+        nbits_wave = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
         const uint32_t pos = inc - nb;
         if (nb) {
           const uint64_t top = v << (64 - nb);  // first code bit at bit 63
@@ -538,7 +542,7 @@ __global__ void __launch_bounds__(kThreads) huff_write(const uint16_t* __restric
           const uint32_t a = (uint32_t)(top >> (32 + off));
           const uint32_t b = (uint32_t)(top >> off);
           const uint32_t c2 = off ? (uint32_t)(top << (32 - off)) : 0u;
-          if (a) atomicOr(&buf[wv][w0], a);
+          if (a && w0 < (uint32_t)kChunkWords) atomicOr(&buf[wv][w0], a);
           if (b && w0 + 1 < (uint32_t)kChunkWords) atomicOr(&buf[wv][w0 + 1], b);
           if (c2 && w0 + 2 < (uint32_t)kChunkWords) atomicOr(&buf[wv][w0 + 2], c2);
         }
@@ -549,7 +553,8 @@ __global__ void __launch_bounds__(kThreads) huff_write(const uint16_t* __restric
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       __builtin_amdgcn_wave_barrier();
       if (active) {
-        const uint32_t nw = (nbits_wave + 31) >> 5, o = offs[j];
+        // never more words than the size pass gave the chunk
+        const uint32_t nw = min((nbits_wave + 31) >> 5, cnts[j]), o = offs[j];
         for (uint32_t i = ln; i < nw; i += 64) {
           words[o + i] = buf[wv][i];
           buf[wv][i] = 0;
