@@ -90,9 +90,22 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   }
   return v;
 }
+// Inclusive prefix sum over a whole wave by DPP moves (no LDS round trips):
+// shifts by 1, 2, 4 and 8 lanes within each row of 16 (lanes with no source
+// add 0), then lane 15 of rows 0 and 2 into rows 1 and 3, then lane 31 into
+// rows 2 and 3.  Every lane of the wave must be active.
+__device__ __forceinline__ uint32_t wave_incl_u32(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+// Sum over a whole wave (every lane active), the same in every lane.
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_u32(v), 63);
 }
 
 // Cross-workgroup communication uses only agent-scope RELAXED atomics (their
@@ -1695,14 +1708,7 @@ ec_write_fast(EncArgs a) {
       rw += w;
       ro += (uint32_t)__popcll(om);
     }
-    uint32_t iw = rw, io = ro;  // inclusive scans over lanes
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t a1 = __shfl_up(iw, o), a2 = __shfl_up(io, o);
-      if (lane >= (uint32_t)o) {
-        iw += a1;
-        io += a2;
-      }
-    }
+    const uint32_t iw = wave_incl_u32(rw), io = wave_incl_u32(ro);  // inclusive scans over lanes
     uint32_t cb = iw - rw;
 #pragma unroll
     for (uint32_t j = 0; j < C; j++) {
@@ -2455,11 +2461,7 @@ __device__ __forceinline__ void index_tile(const uint8_t* __restrict__ in, const
     badw |= wl[q] > 12;
     lsum += wl[q];
   }
-  uint32_t incl = lsum;
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t v = __shfl_up(incl, o);
-    if (lane >= (uint32_t)o) incl += v;
-  }
+  const uint32_t incl = wave_incl_u32(lsum);
   uint32_t run = incl - lsum;
 #pragma unroll
   for (uint32_t q = 0; q < 4; q++) {
@@ -2470,7 +2472,7 @@ __device__ __forceinline__ void index_tile(const uint8_t* __restrict__ in, const
     }
     run += wl[q];
   }
-  const uint32_t sumw = __shfl(incl, 63);
+  const uint32_t sumw = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
   const uint64_t seg_words = sbytes / 8;
   const uint32_t pl_word0 = (rec_in_seg + off_pl) / 8;  // off_pl and records are 8-aligned
   const bool bad = __any(badw) || (uint64_t)pl_word0 + sumw > seg_words;
