@@ -282,3 +282,14 @@ def test_segments_reject_a_damaged_codebook():
     assert coder.status() == ec.EC_ERR_CORRUPT
     coder.decode(book, ec.HUFF_BOOK_MAX, off, words, sym.size, out)
     assert coder.status() == ec.EC_OK
+
+
+def test_groups_of_more_than_256_chunks():
+    """Past 2048 * 256 chunks a group of the size and write passes holds more
+    than 256 chunks, so the write pass scans its offsets in several rounds
+    (134.7 M codes)."""
+    coder = ec.Huffman("cuda")
+    rng = np.random.default_rng(21)
+    n = 256 * 257 * 2048 + 5
+    sym = laplace_codes(rng, n, 3.0)
+    check_parity(coder, sym, "two-pass packing")
