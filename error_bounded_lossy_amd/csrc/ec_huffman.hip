@@ -15,7 +15,8 @@
 //           its codes (wave prefix of bit counts, LDS OR into a 96-word
 //           buffer) and stores whole words
 // Decode: two launches.
-//   dec_book  one workgroup: validate the codebook, canonical codes, a
+//   dec_book  one workgroup per segment: validate the codebook (workgroup 0
+//             also zeroes the status word), canonical codes, a
 //             4096-entry table from every 12-bit prefix to (symbol, length)
 //   decode    128 chunks per workgroup: their words staged through LDS with
 //             coalesced loads when they fit in 56 words per chunk on average
@@ -569,10 +570,13 @@ __global__ void __launch_bounds__(kThreads) huff_write(const uint16_t* __restric
 
 // Validate the codebook of segment blockIdx.x (book_bytes readable bytes at
 // books + blockIdx.x * EC_HUFF_BOOK_MAX) and build its prefix table.
+// report: set the status word for a bad codebook (with no chunks to decode);
+// else workgroup 0 zeroes the status word, and the decode kernel, which runs
+// after this one, reports the segments whose codebook is not valid.
 __global__ void __launch_bounds__(kBookThreads) huff_dec_book(const uint8_t* __restrict__ books,
                                                           uint64_t book_bytes,
                                                           const uint32_t* __restrict__ chunk_off,
-                                                          uint64_t n, Ws w) {
+                                                          uint64_t n, Ws w, int report) {
   const uint32_t seg = blockIdx.x;
   const uint8_t* book = books + (size_t)seg * kBookStride;
   uint32_t* enc = w.enc + (size_t)seg * kTable;
@@ -588,6 +592,7 @@ __global__ void __launch_bounds__(kBookThreads) huff_dec_book(const uint8_t* __r
     s_bad = 0;
     s_kraft = 0;
     s_m = 0;
+    if (!report && seg == 0) w.status[0] = 0;
   }
   if (t <= kMaxLen) cnt[t] = 0;
   for (int i = t; i < kTable; i += kBookThreads) len[i] = 0;
@@ -640,7 +645,7 @@ __global__ void __launch_bounds__(kBookThreads) huff_dec_book(const uint8_t* __r
   __syncthreads();
   if (s_bad) {
     if (t == 0) {
-      status_or(w.status, kStCorrupt);
+      if (report) status_or(w.status, kStCorrupt);
       w.valid[seg] = 0;
     }
     return;
@@ -877,9 +882,9 @@ ec_status decode_impl(const uint8_t* d_books, uint64_t book_bytes, const uint32_
   if (wbytes < work_bytes(nseg)) return EC_ERR_CAPACITY;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Ws w = ws_of(d_work, nseg);
-  hipLaunchKernelGGL(huff_clear, dim3(1), dim3(kThreads), 0, s, w, 0u);
+  if (n == 0) hipLaunchKernelGGL(huff_clear, dim3(1), dim3(kThreads), 0, s, w, 0u);
   hipLaunchKernelGGL(huff_dec_book, dim3(nseg), dim3(kBookThreads), 0, s, d_books, book_bytes,
-                     d_chunk_off, n, w);
+                     d_chunk_off, n, w, n == 0 ? 1 : 0);
   if (n) {
     const uint32_t nch = num_chunks(n);
     hipLaunchKernelGGL(huff_decode, dim3((nch + kDecChunks - 1) / kDecChunks, nseg),
