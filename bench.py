@@ -64,30 +64,113 @@ def load_traffic(kernel: str, workload: str, coder: str = "bitpack"):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(x_cpu, w, min_seconds: float):
-    """The oracle (single-threaded C) on a bounded sample of the same batch:
-    round trips of table subsets until `min_seconds` of CPU work is done."""
+def _host_cpus():
+    """(usable host CPUs, CPU model string)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return n, model
+
+
+def _oracle_cfg(w, tables):
+    """Oracle configuration for a subset of the workload's tables (one
+    segment each, P = 1: a table's segment depends on that table alone)."""
+    import oracle as O
+    T, B, D = w.shape
+    return O.Config(T=len(tables), B=B, D=D, eb_mode=w.eb_mode,
+                    eb=tuple(w.eb[t] for t in tables), sched_kind=w.sched_kind,
+                    sched_t0=w.sched_t0)
+
+
+def _oracle_segment_compress(job):
+    """Worker of the all-cores leg: compress one table (one segment)."""
+    import oracle as O
+    cfg, it, x = job
+    t0 = time.perf_counter()
+    st = O.compress(cfg, it, x, debug=False).stream
+    return st, time.perf_counter() - t0
+
+
+def _oracle_segment_decompress(job):
+    import oracle as O
+    cfg, st = job
+    t0 = time.perf_counter()
+    O.decompress(cfg, st)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(w, min_seconds: float, workers: int):
+    """The oracle (single-threaded C, as it stands) on bounded samples of one
+    batch of the workload, run before the GPU is touched (the all-cores leg
+    forks worker processes):
+      - one core: round trips of two tables at a time until min_seconds of
+        CPU work, compress and decompress timed separately;
+      - all cores: one oracle per segment (table) in a pool of `workers`
+        processes, the batch's tables repeated until about min_seconds/2 of
+        wall time, compress then decompress."""
+    import multiprocessing as mp
     import numpy as np
     import oracle as O
-    T, B, D = x_cpu.shape
-    done_bytes, spent, tables = 0, 0.0, 0
+    O.build(force=False)
+    x = w.x.numpy()
+    T, B, D = x.shape
+    nbytes_t = 4 * B * D
+    n_cpu, model = _host_cpus()
+    tc = td = 0.0
+    done = tables = 0
     t = 0
-    while spent < min_seconds:
+    while tc + td < min_seconds:
         sel = [t % T, (t + 1) % T]
-        xs = np.ascontiguousarray(x_cpu[sel])
-        cfg = O.Config(T=2, B=B, D=D, eb_mode=w.eb_mode, eb=tuple(w.eb[:2]),
-                       sched_kind=w.sched_kind, sched_t0=w.sched_t0)
+        xs = np.ascontiguousarray(x[sel])
+        cfg = _oracle_cfg(w, sel)
         t0 = time.perf_counter()
         c = O.compress(cfg, w.iteration, xs, debug=False)
+        t1 = time.perf_counter()
         O.decompress(cfg, c.stream)
-        spent += time.perf_counter() - t0
-        done_bytes += xs.nbytes
+        t2 = time.perf_counter()
+        tc += t1 - t0
+        td += t2 - t1
+        done += xs.nbytes
         tables += 2
         t += 2
-    return {"value": round(done_bytes / spent / 1e9, 5), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{tables} table round trips ({tables}x{B}x{D} fp32, "
-                      f"{done_bytes / 2**20:.0f} MiB) of batch t={w.iteration}, {spent:.1f} s"}
+    one = {"value": round(done / (tc + td) / 1e9, 5), "unit": "GB/s", "cores": 1,
+           "kind": "oracle",
+           "sample": f"{tables} table round trips ({tables}x{B}x{D} fp32, "
+                     f"{done / 2**20:.0f} MiB) of batch t={w.iteration}, {tc + td:.1f} s",
+           "compress_GBps": round(done / tc / 1e9, 5),
+           "decompress_GBps": round(done / td / 1e9, 5),
+           "host_cpus": n_cpu, "cpu_model": model}
+    # all cores: enough repetitions of the batch's T segments for the target time
+    per_seg = (tc + td) / tables
+    reps = max(1, int(min_seconds / 2 * workers / (per_seg * T) + 0.5))
+    jobs = [(_oracle_cfg(w, [tt]), w.iteration, np.ascontiguousarray(x[tt:tt + 1]))
+            for _ in range(reps) for tt in range(T)]
+    with mp.get_context("fork").Pool(workers) as pool:
+        t0 = time.perf_counter()
+        res = pool.map(_oracle_segment_compress, jobs, chunksize=1)
+        t1 = time.perf_counter()
+        pool.map(_oracle_segment_decompress, [(j[0], r[0]) for j, r in zip(jobs, res)],
+                 chunksize=1)
+        t2 = time.perf_counter()
+    tot = len(jobs) * nbytes_t
+    one["all_cores"] = {
+        "value": round(tot / (t2 - t0) / 1e9, 5), "unit": "GB/s", "cores": workers,
+        "compress_GBps": round(tot / (t1 - t0) / 1e9, 5),
+        "decompress_GBps": round(tot / (t2 - t1) / 1e9, 5),
+        "sample": f"{len(jobs)} segment round trips ({reps} x the {T} tables of batch "
+                  f"t={w.iteration}, {tot / 2**20:.0f} MiB), one oracle per segment in "
+                  f"{workers} processes, {t2 - t0:.1f} s wall"}
+    return one
 
 
 KERNEL_PREFIX = {"prep": "ec_prep", "encode": ("ec_encode", "ec_quantize"),
@@ -350,6 +433,8 @@ def main():
     ap.add_argument("--batches", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-workers", type=int, default=16,
+                    help="processes of the all-cores oracle leg (at most the usable CPUs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (counter calibration)")
     ap.add_argument("--summarize-counters", metavar="DIR",
@@ -381,6 +466,15 @@ def main():
 
     import torch
     import synth
+
+    # the CPU baseline first: its worker processes fork before the GPU is used
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on a CPU sample", file=sys.stderr, flush=True)
+        n_cpu, _ = _host_cpus()
+        cpu = cpu_baseline(synth.workload(args.workload, iteration=0, device="cpu"),
+                           args.cpu_seconds, min(n_cpu, args.cpu_workers))
+
     import error_bounded_lossy_amd as ec
 
     dev = torch.device("cuda:0")
@@ -395,44 +489,78 @@ def main():
     plan = ec.Plan(T, B, D, 1, w0.eb_mode, w0.eb, schedule=sched, device=dev)
     out = plan.empty_stream()
     y = torch.empty(T, B, D, dtype=torch.float32, device=dev)
+    # read (untimed) before every timed call of the cold protocol: 512 MiB,
+    # twice the Infinity Cache, so the call finds neither its input nor the
+    # stream in any cache.  A read, not a write: a written buffer would leave
+    # dirty lines whose write-back the next call would pay for.
+    scratch = torch.ones(128 << 20, dtype=torch.int32, device=dev)
 
-    # compression ratio of every batch (untimed)
+    def flush(i):
+        torch.amax(scratch)
+
+    # compressed size of every batch (untimed)
     crs, sizes = [], []
     for w in batches:
         plan.compress(w.x, out, w.iteration)
         cr, nb, _ = plan.ratio()
         crs.append(cr)
         sizes.append(nb)
-    mean_bytes = sum(sizes) / len(sizes)
 
-    def step(i):
-        w = batches[i % len(batches)]
-        plan.compress(w.x, out, w.iteration)
-        plan.decompress(out, y)
+    def batch(i):
+        return batches[i % len(batches)]
 
     for i in range(args.warmup):
-        step(i)
+        w = batch(i)
+        plan.compress(w.x, out, w.iteration)
+        plan.decompress(out, y)
     torch.cuda.synchronize()
-    # timed region: K steps, no profiling events between the launches
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+
+    # cold (primary): every call timed alone by events on its stream, after a
+    # scratch write that evicts the caches
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4 * args.steps)]
     wall0 = time.perf_counter()
-    e0.record()
     for i in range(args.steps):
-        step(args.warmup + i)
-    e1.record()
+        w = batch(args.warmup + i)
+        flush(i)
+        ev[4 * i].record()
+        plan.compress(w.x, out, w.iteration)
+        ev[4 * i + 1].record()
+        flush(i + 1)
+        ev[4 * i + 2].record()
+        plan.decompress(out, y)
+        ev[4 * i + 3].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms = e0.elapsed_time(e1)
+    tc_ms = sum(ev[4 * i].elapsed_time(ev[4 * i + 1]) for i in range(args.steps))
+    td_ms = sum(ev[4 * i + 2].elapsed_time(ev[4 * i + 3]) for i in range(args.steps))
     _, _, st = plan.ratio(raise_on_error=False)
     if st != 0:
         print(f"[bench] device status {st}", file=sys.stderr)
         sys.exit(1)
-    # per-kernel durations: the same K steps again, each launch bracketed by
-    # HIP events on the stream it runs on
+
+    # warm: the same steps back to back (the batches cycle through 1 GiB, so
+    # each compression still reads its input from HBM; the stream it writes is
+    # read by the decompression from the caches)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        w = batch(args.warmup + i)
+        plan.compress(w.x, out, w.iteration)
+        plan.decompress(out, y)
+    e1.record()
+    torch.cuda.synchronize()
+    warm_ms = e0.elapsed_time(e1)
+
+    # per-kernel durations, cold protocol: every launch bracketed by HIP events
+    # on the stream it runs on
     plan.profile_enable(True, max_launches=5 * args.steps + 8)
     for i in range(args.steps):
-        step(args.warmup + i)
+        w = batch(args.warmup + i)
+        flush(i)
+        plan.compress(w.x, out, w.iteration)
+        flush(i + 1)
+        plan.decompress(out, y)
     torch.cuda.synchronize()
     t_prep, n_prep = plan.profile_read(ec.KERNEL_PREP)
     t_enc, n_enc = plan.profile_read(ec.KERNEL_ENCODE)
@@ -445,19 +573,21 @@ def main():
         sys.exit(1)
 
     rel = w0.eb_mode == ec.EB_REL_RANGE
-    S = mean_bytes
-    tc = (t_prep + t_enc + t_asm) / args.steps * 1e-3  # kernel time only
-    td = t_dec / args.steps * 1e-3
-    step_s = ms / args.steps * 1e-3
-    # the round trip's minimum HBM traffic: read x, write the stream, read it,
-    # write y (a second read of x for the range is not counted)
-    bytes_c = 4 * N + S
+    K = args.steps
+    # compressed bytes: the batches the timed steps ran on, in total
+    S_tot = sum(sizes[(args.warmup + i) % len(batches)] for i in range(K))
+    S = S_tot / K
+    tc = tc_ms / K * 1e-3
+    td = td_ms / K * 1e-3
+    step_s = tc + td
+    # algorithmic bytes: compression reads x (twice with a range-relative
+    # bound: the range pass, then quantization) and writes the stream;
+    # decompression reads the stream and writes x^
+    bytes_c = 4 * N * (2 if rel else 1) + S
     bytes_d = S + 4 * N
-    # algorithmic bytes per launch: the input read by the range pass (REL, when
-    # it is a kernel of its own) and by the quantize pass (which also computes
-    # the range when there is no range pass: its second read of a tile is not
-    # counted), the stream written by assembly (by the one encode kernel when
-    # there is no assembly pass), and both for decode
+    # per launch: the input read by the range pass (REL) and by the quantize
+    # pass, the stream written by assembly (by the one encode kernel when there
+    # is no assembly pass), and both for decode
     kernels = {
         "encode": (t_enc / max(n_enc, 1), 4 * N + (0 if n_asm else S)),
         "decode": (t_dec / max(n_dec, 1), S + 4 * N),
@@ -470,26 +600,34 @@ def main():
     dom_ms, dom_bytes = kernels[dom]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     traffic = load_traffic(dom, args.workload)
+    warm_step = warm_ms / K * 1e-3
     res = {
         "metric": "compress+decompress GB/s (uncompressed) per MI355X; ratio at eb; % HBM roof",
         "value": round(4 * N / step_s / 1e9, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": round(ms / args.steps, 5),
+        "ms_per_step": round(step_s * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp32",
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {WORKLOADS[args.workload]}", "tables": T,
-                   "batch": B, "dim": D, "chunks": 1, "batches_cycled": len(batches)},
+                   "batch": B, "dim": D, "chunks": 1, "batches_cycled": len(batches),
+                   "protocol": "cold: 512 MiB scratch read before each timed call"},
         "compress_GBps": round(4 * N / tc / 1e9, 2),
         "decompress_GBps": round(4 * N / td / 1e9, 2),
-        "compression_ratio": round(sum(crs) / len(crs), 4),
+        "compression_ratio": round(4 * N * K / S_tot, 4),
         "compression_ratio_per_batch": [round(c, 4) for c in crs],
         "hbm_roof_frac_roundtrip": round((bytes_c + bytes_d) / step_s / 1e9 / HBM_PEAK_GBS, 4),
+        "hbm_roof_frac_compress": round(bytes_c / tc / 1e9 / HBM_PEAK_GBS, 4),
+        "hbm_roof_frac_decompress": round(bytes_d / td / 1e9 / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes": {"compress": int(bytes_c), "decompress": int(bytes_d)},
+        "warm": {"value": round(4 * N / warm_step / 1e9, 2), "ms_per_step": round(warm_ms / K, 5),
+                 "hbm_roof_frac_roundtrip":
+                     round((bytes_c + bytes_d) / warm_step / 1e9 / HBM_PEAK_GBS, 4)},
         "kernel_ms": {k: round(v[0], 5) for k, v in kernels.items()},
         "wall_s": round(wall, 4),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
@@ -497,9 +635,8 @@ def main():
                      "traffic": traffic,
                      "algorithmic_bytes_per_launch": int(dom_bytes)},
     }
-    if not args.no_cpu_baseline:
-        print("[bench] timing the oracle on a CPU sample", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(w0.x.cpu().numpy(), w0, args.cpu_seconds)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
 
 

@@ -1848,7 +1848,7 @@ struct DecTile {
 struct DecShared {
   uint32_t ok, seg, tile, n, rows, ntiles, valid, bad;
   float eb;
-  uint64_t seg_off, seg_bytes;
+  uint64_t seg_off, seg_bytes, total;
   DecTile tl;
   uint32_t part[kThreads / 64];
 };
@@ -1919,6 +1919,37 @@ __device__ DecTile locate_tile(const uint8_t* seg, uint64_t seg_bytes, uint32_t 
   }
   r.ok = 1;
   return r;
+}
+
+// Whole wave, uniform control flow: the segment header's U and n_out (words 4
+// and 5) must equal the sums over the segment's tile records.  Entries that
+// fail their own checks are skipped here (their tiles' workgroups report
+// them); every read stays inside the segment.
+__device__ bool seg_totals_ok(const uint8_t* sg, uint64_t sbytes, uint32_t ntiles) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint64_t prefix = 32 + align_up(4ull * ntiles, 16);
+  uint32_t u = 0, o = 0;
+  for (uint32_t j = lane; j < ntiles; j += 64) {
+    const uint32_t off = reinterpret_cast<const uint32_t*>(sg + 32)[j];
+    if (off >= prefix && !(off & 15u) && (uint64_t)off + 16 <= sbytes) {
+      o += reinterpret_cast<const uint32_t*>(sg + off)[2];
+      u += reinterpret_cast<const uint32_t*>(sg + off)[3] & 0xffffu;
+    }
+  }
+  u = wave_sum_u32(u);
+  o = wave_sum_u32(o);
+  return u == reinterpret_cast<const uint32_t*>(sg)[4] && o == reinterpret_cast<const uint32_t*>(sg)[5];
+}
+
+// Whole wave, uniform control flow: the stream header's total equals the
+// header and chunk table plus the sum of the P chunk byte counts (each
+// already checked to lie inside the stream).
+__device__ bool chunk_totals_ok(const uint8_t* in, uint32_t P, uint64_t total) {
+  const uint32_t lane = threadIdx.x & 63;
+  uint64_t sum = 0;
+  for (uint32_t q = lane; q < P; q += 64) sum += reinterpret_cast<const uint64_t*>(in + 64)[q];
+  sum = wave_sum_u64(sum);
+  return sum + 64 + align_up(8ull * P, 16) == total;
 }
 
 // Decode the D values of E[e0 .. e0 + D) into y (whole wave, lane = element
@@ -2042,6 +2073,7 @@ __global__ void __launch_bounds__(kThreads) ec_decode_kernel(DecArgs a) {
     }
     sh.seg_off = chunk + so;
     sh.seg_bytes = sb;
+    sh.total = total;
     if (ok && nt) {
       DecTile tl = locate_tile(in + chunk + so, sb, nt, rows, k, D, sh.valid != 0);
       ok = tl.ok;
@@ -2050,6 +2082,11 @@ __global__ void __launch_bounds__(kThreads) ec_decode_kernel(DecArgs a) {
     sh.ok = ok;
   }
   __syncthreads();
+  if (wv == 0 && sh.ok) {  // a segment's first tile checks its totals, tile 0 the chunk sizes
+    bool good = sh.tile != 0 || seg_totals_ok(a.in + sh.seg_off, sh.seg_bytes, sh.ntiles);
+    if (ticket == 0) good = good && chunk_totals_ok(a.in, P, sh.total);
+    if (!good && lane == 0) report_error(a.report, kDevErrCorrupt);
+  }
   const uint32_t s = sh.seg, k = sh.tile, n = sh.n, rows = sh.rows;
   const uint32_t pch = s / T, t = s % T;
   float* yseg = a.y + ((uint64_t)t * B + chunk_row0(a.sh, pch)) * D;
@@ -2108,6 +2145,17 @@ __global__ void __launch_bounds__(kThreads) ec_decode_kernel(DecArgs a) {
       s_opos[i] = g_opos[i];
       s_oval[i] = g_oval[i];
     }
+  {
+    // outlier positions index E (U*D values) and strictly increase; the
+    // decoders' searches assume both, so a stream breaking either is corrupt
+    const uint32_t nE = tl.U * D;
+    uint32_t obad = 0;
+    for (uint32_t i = tid; i < tl.nout; i += kThreads) {
+      const uint32_t p = g_opos[i];
+      obad |= p >= nE || (i > 0 && g_opos[i - 1] >= p);
+    }
+    if (obad) sh.bad = 1;
+  }
   // source of every row: a uid of this record, or a reference into an
   // earlier record (resolved lane-parallel so the metadata loads overlap)
   if (tid < n) {
@@ -2275,6 +2323,7 @@ __device__ void dec_locate(const DecArgs& a, const uint8_t* in, uint32_t ticket,
   }
   sh.seg_off = chunk + so;
   sh.seg_bytes = sb;
+  sh.total = total;
   rec_off = 0;
   if (ok && nt) {
     DecTile tl = locate_tile(in + chunk + so, sb, nt, rows, k, D, sh.valid != 0);
@@ -2433,6 +2482,11 @@ __device__ __forceinline__ void index_tile(const uint8_t* __restrict__ in, const
     if (lane == 0) report_error(a.report, kDevErrCorrupt);
     put_tile();
     return;
+  }
+  {  // a segment's first tile checks its totals, tile 0 the chunk sizes
+    bool good = k != 0 || seg_totals_ok(in + seg_off, sbytes, sh.ntiles);
+    if (ticket == 0) good = good && chunk_totals_ok(in, a.sh.P, sh.total);
+    if (!good && lane == 0) report_error(a.report, kDevErrCorrupt);
   }
   if (n == 0) {
     flags = kTileOk;

@@ -126,35 +126,53 @@ typedef struct {
 /* Largest supported D on the current device (limited by LDS per workgroup). */
 uint32_t ec_max_dim(void);
 
-/* Workspace bytes the plan needs (0 if the descriptor is invalid). */
+/* Workspace bytes the plan needs (0 if the descriptor is invalid).  The
+ * workspace holds the per-table error bounds (section III-C), the hash tables
+ * of the repeated-vector detection (section III-D "Vector-based LZ
+ * Encoding") and the staging between the compression passes. */
 size_t ec_workspace_bytes(const ec_plan_desc* desc);
 
-/* Validate the descriptor and build a plan.  Host work plus one blocking copy
- * of the per-table constants into the workspace.  *out is NULL on failure. */
+/* Validate the descriptor and build a plan: the shape, the per-table error
+ * bounds with their class multipliers and the iteration-wise schedule of
+ * section III-C / Algorithm 1 (table-wise and iteration-wise levels).  Host
+ * work plus one blocking copy of the per-table constants into the workspace.
+ * *out is NULL on failure. */
 ec_status ec_plan(const ec_plan_desc* desc, ec_plan_t* out);
 
 /* Release the plan's host resources (the workspace stays the caller's). */
 ec_status ec_plan_destroy(ec_plan_t plan);
 
-/* Upper bound of a compressed stream (every tile stored raw); 0 for NULL. */
+/* Upper bound of a compressed stream (every tile stored raw); 0 for NULL.
+ * Sizes the send buffer that section III-E "Buffer Optimization" writes the
+ * whole multi-table stream into. */
 size_t ec_max_compressed_bytes(ec_plan_t plan);
 
 /* Compress d_in (fp32 [T][B][D]) at iteration `iter` into d_out (capacity
- * out_cap >= ec_max_compressed_bytes).  The stream's size becomes known on the
- * host through ec_ratio; on the device it is the u64 at byte 48 of d_out. */
+ * out_cap >= ec_max_compressed_bytes): the lossy compressor of sections I and
+ * III-D (quantization encoder q = round(x / 2eb) with every reconstructed value
+ * within eb, repeated vectors stored once, the codes bit-plane packed), all
+ * tables of all destination chunks into ONE contiguous stream (section III-E,
+ * Fig. 7).  The stream's size becomes known on the host through ec_ratio; on
+ * the device it is the u64 at byte 48 of d_out, and chunk p's size is the u64
+ * at byte 64 + 8p (the size metadata of section III-A, stage 2).  Errors:
+ * EC_ERR_INVALID (NULL or misaligned pointers),
+ * EC_ERR_CAPACITY (out_cap too small), EC_ERR_DEVICE (a launch failed). */
 ec_status ec_compress(ec_plan_t plan, int64_t iter, const float* d_in, void* d_out,
                       size_t out_cap, void* stream);
 
 /* Decompress a stream of this plan's shape (d_stream holds stream_cap readable
- * bytes) into d_out (fp32 [T][B][D]).  Every field is validated on the device
- * before use; a corrupt stream makes ec_ratio return EC_ERR_CORRUPT and leaves
- * the affected rows zero. */
+ * bytes) into d_out (fp32 [T][B][D]): the inverse path of section III-A stage
+ * 4 (the receiver decodes each source's slice; every row is written once).
+ * Every field is validated on the device before use; a corrupt stream makes
+ * ec_ratio return EC_ERR_CORRUPT and leaves the affected rows zero. */
 ec_status ec_decompress(ec_plan_t plan, const void* d_stream, size_t stream_cap, float* d_out,
                         void* stream);
 
 /* Wait for this plan's last enqueued call, then report the last compression:
  * total_cr = 4*T*B*D / stream bytes (headers included), the stream bytes, and
- * per_segment_cr[p*T + t] = 4*rows(p)*D / segment bytes (may be NULL).  Returns
+ * per_segment_cr[p*T + t] = 4*rows(p)*D / segment bytes (may be NULL).  The
+ * total is a ratio of total bytes, which is what Table V's "avg." row
+ * averages (its values are harmonic means of the per-table ratios).  Returns
  * and clears the sticky device status. */
 ec_status ec_ratio(ec_plan_t plan, double* total_cr, uint64_t* compressed_bytes,
                    double* per_segment_cr);

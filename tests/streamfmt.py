@@ -121,9 +121,16 @@ def parse(buf: np.ndarray) -> Stream:
                           int(buf[ro + 14]), n)
                 mark(ro, 15)
                 assert bin(tl.bitmap).count("1") == tl.U
+                raw_size = 16 + _a(4 * n * D, 16)
                 if tl.mode == 0:
                     mark(ro + 16, 4 * n * D)
-                    tl.size = 16 + _a(4 * n * D, 16)
+                    tl.size = raw_size
+                    if seg.valid:
+                        # the rule: BITPACK only when strictly smaller than RAW
+                        raw = np.frombuffer(bytes(buf[ro + 16:ro + 16 + 4 * n * D]),
+                                            np.float32).reshape(n, D)
+                        assert bitpack_size(raw, tl.bitmap, n, D, seg.eb, rows) >= raw_size, \
+                            "RAW tile whose BITPACK record would be smaller"
                 else:
                     assert tl.mode == 1 and seg.valid
                     nE = tl.U * D
@@ -157,11 +164,32 @@ def parse(buf: np.ndarray) -> Stream:
                     tl.zz = zz[:nE]
                     assert not zz[nE:].any()
                     tl.size = _a(opl + 8 * sw, 16)
+                    assert tl.size < raw_size, "BITPACK tile not smaller than RAW"
                 seg.tiles.append(tl)
             segs.append(seg)
         at += chunk_bytes[p]
     assert at == total
     return Stream(T, B, D, P, eb_mode, it, total, chunk_bytes, segs, cov)
+
+
+def bitpack_size(raw, bitmap, n, D, eb, rows):
+    """Bytes the BITPACK record of a tile would take, rebuilt from its raw rows
+    (n x D), its first-occurrence bitmap and the segment's eb."""
+    us = [i for i in range(n) if (bitmap >> i) & 1]
+    q, o = quantize_np(raw[us].reshape(-1), eb)
+    z = np.where(q >= 0, 2 * q, -2 * q - 1)
+    nE = len(us) * D
+    nblk = (nE + 63) // 64
+    zb = np.zeros(nblk * 64, np.int64)
+    zb[:nE] = z
+    m = zb.reshape(nblk, 64).max(axis=1) if nblk else np.zeros(0, np.int64)
+    sw = int(sum(int(v).bit_length() for v in m))
+    n_out = int(o.sum())
+    rb = 2 if rows <= 65536 else 4
+    orf = _a(16 + nblk, 4)
+    oop = _a(orf + rb * (n - len(us)), 4)
+    opl = _a(oop + 8 * n_out, 8)
+    return _a(opl + 8 * sw, 16)
 
 
 def quantize_np(x, eb):

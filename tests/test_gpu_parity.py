@@ -246,10 +246,12 @@ def describe_segment_diff(g, r, D):
 
 
 @pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
-def test_workloads_full_size_sampled_tables(name):
-    """Full-size batch on the GPU (the launch the benchmark times); the oracle
-    recomputes two sampled tables, whose segment bytes and reconstruction must
-    match the GPU stream exactly."""
+def test_workloads_full_size_whole_stream(name):
+    """Full-size batch on the GPU, in the launch configuration the benchmark
+    times.  The oracle compresses the whole batch: the complete GPU stream
+    (header, chunk table, every segment header, tile directory and record) must
+    equal it byte for byte, and the GPU reconstruction of every table must be
+    bitwise the oracle's (hence within eb of the input)."""
     import synth
     say(f"[workload] {name} full size")
     w = synth.workload(name, iteration=3, device="cuda")
@@ -263,29 +265,35 @@ def test_workloads_full_size_sampled_tables(name):
     plan.decompress(out[:nbytes], y)
     plan.ratio()
     gst = out[:nbytes].cpu().numpy()
-    gsegs = SF.parse_segments(gst)
-    picks = [0, T - 1] if T > 1 else [0]
-    xs = w.x[picks].cpu().numpy()
-    cfg = make_cfg(len(picks), B, D, 1, eb_mode=w.eb_mode, eb=tuple(w.eb[:len(picks)]),
+    del out
+    xs = w.x.cpu().numpy()
+    cfg = make_cfg(T, B, D, 1, eb_mode=w.eb_mode, eb=tuple(w.eb),
                    sched={"kind": w.sched_kind, "t0": w.sched_t0})
-    ref = O.compress(cfg, w.iteration, xs)
-    rsegs = SF.parse_segments(ref.stream)
-    for j, t in enumerate(picks):
-        gs, rs = gsegs[t], rsegs[j]
-        assert gs.nbytes == rs.nbytes, (t, gs.nbytes, rs.nbytes)
-        gb = gst[gs.offset:gs.offset + gs.nbytes]
-        rb = ref.stream[rs.offset:rs.offset + rs.nbytes]
-        assert np.array_equal(gb, rb), f"table {t}: " + describe_segment_diff(gb, rb, D)
+    say(f"[workload] {name} oracle on {xs.nbytes >> 20} MiB")
+    ref = O.compress(cfg, w.iteration, xs, debug=False)
+    assert gst.size == ref.stream.size, (gst.size, ref.stream.size)
+    if not np.array_equal(gst, ref.stream):
+        gsegs, rsegs = SF.parse_segments(gst), SF.parse_segments(ref.stream)
+        for t in range(T):
+            gs, rs = gsegs[t], rsegs[t]
+            gb = gst[gs.offset:gs.offset + gs.nbytes]
+            rb = ref.stream[rs.offset:rs.offset + rs.nbytes]
+            assert gs.offset == rs.offset and np.array_equal(gb, rb), \
+                f"table {t}: " + describe_segment_diff(gb, rb, D)
+        raise AssertionError("stream headers differ")
+    del xs
     yo = O.decompress(cfg, ref.stream)
-    yg = y[picks].cpu().numpy()
-    np.testing.assert_array_equal(yg.view(np.uint32), yo.view(np.uint32))
+    yg = y.cpu().numpy()
+    assert np.array_equal(yg.view(np.uint32), yo.view(np.uint32)), "reconstruction differs"
     # the bound on every element of the whole batch
+    gsegs = SF.parse_segments(gst)
     xg = w.x
     ebs = torch.tensor([s.eb for s in gsegs], device="cuda").view(T, 1, 1)
     fin = torch.isfinite(xg)
     err = (xg.double() - y.double()).abs()
     assert bool((err[fin] <= ebs.expand_as(xg).double()[fin]).all())
-    say(f"[workload] {name} CR={cr:.3f}")
+    assert cr == pytest.approx(4.0 * T * B * D / ref.stream.size, rel=1e-12)
+    say(f"[workload] {name} CR={cr:.3f} ({ref.stream.size} bytes, whole stream equal)")
 
 
 @pytest.mark.parametrize("T,B,D,mode", [(3, 1000, 128, 1), (2, 8192, 64, 1), (5, 4096, 64, 1),
@@ -367,15 +375,19 @@ def test_hot_rows_many_duplicates(D, bits):
     assert_parity(make_cfg(T, B, D, eb_mode=1, eb=(0.02,)), x, hash_bits=bits, label=f"hot-{D}-{bits}")
 
 
-def test_corrupt_streams_are_rejected_or_decoded_like_the_oracle():
-    """The decoder validates every field it uses.  Targeted corruptions (magic,
+@pytest.mark.parametrize("D", [128, 24])
+def test_corrupt_streams_are_rejected_or_decoded_like_the_oracle(D):
+    """The decoders validate every field they use (D = 128 runs the wave64
+    decoder, D = 24 the generic one).  Targeted corruptions (magic,
     truncation, wrong shape, a segment offset, a tile directory entry, a block
     width above 12, a forward reference, an outlier position past its record's
-    rows) must be reported as corrupt, as the oracle's reader reports them;
+    rows, outlier positions out of order, a segment header's U or n_out that
+    disagrees with its records, a stream total that disagrees with the chunk
+    sizes) must be reported as corrupt, as the oracle's reader reports them;
     random bit flips and cuts must end in OK or corrupt, and a stream the
     oracle's reader accepts must decode to the same bits."""
-    rng = np.random.default_rng(23)
-    T, B, D = 2, 300, 128
+    rng = np.random.default_rng(23 + D)
+    T, B = 2, 300
     x = dup_rows(rng, T, B, D, scale=0.05, frac_unique=0.3)
     x[0, 5, 7], x[0, 5, 9], x[1, 200, 3] = 1e6, -1e6, np.nan  # outliers
     x[1, 64:128] = rng.normal(0, 1e4, (64, D)).astype(np.float32)  # a raw tile
@@ -416,6 +428,16 @@ def test_corrupt_streams_are_rejected_or_decoded_like_the_oracle():
     oop = tl.offset + ((16 + nblk + 3) // 4 * 4 + 2 * (tl.n - tl.U) + 3) // 4 * 4
     b = good.copy(); b[oop:oop + 4] = np.frombuffer(np.uint32(tl.U * D + 5).tobytes(), np.uint8)
     cases.append(("outlier position", b))
+    tl = [t for t in with_out if t.n_out >= 2][0]; nblk = (tl.U * D + 63) // 64
+    oop = tl.offset + ((16 + nblk + 3) // 4 * 4 + 2 * (tl.n - tl.U) + 3) // 4 * 4
+    b = good.copy(); b[oop + 4:oop + 8] = b[oop:oop + 4]
+    cases.append(("outlier order", b))
+    sg = [s for s in st.segments if s.n_out > 0][0]
+    b = good.copy(); b[seg0.offset + 16] ^= 1; cases.append(("segment U", b))
+    b = good.copy(); b[sg.offset + 20] ^= 2; cases.append(("segment n_out", b))
+    b = np.concatenate([good, np.zeros(16, np.uint8)])
+    b[48:56] = np.frombuffer(np.uint64(good.size + 16).tobytes(), np.uint8)
+    cases.append(("total vs chunk sizes", b))
     for label, bad in cases:
         say(f"[corrupt] {label}")
         rc_o, _ = O.decompress(cfg, bad, status=True)

@@ -337,6 +337,28 @@ def test_references_into_raw_tiles_decode_by_requantization():
     assert c.first[0, 100] == 3 and c.first[0, 150] == 10
 
 
+def test_raw_record_when_bitpack_is_not_strictly_smaller():
+    """A one-row tile of D = 8 with eb = 1/2 (bin width 1, integer values):
+    the RAW record is 16 + 32 = 48 bytes; the BITPACK record is 24 bytes of
+    header, widths and padding plus 8 bytes per plane, padded to 16.  One plane
+    (32 bytes) is smaller, so the tile is packed; two or three planes make it
+    exactly 48 bytes, not smaller, so the tile stays RAW (the independent
+    reader re-derives the rule for every tile it walks)."""
+    cfg = O.Config(T=1, B=1, D=8, eb_mode=O.EB_ABS, eb=(0.5,))
+    for vals, w, mode in [([-1, 0, 0, 0, 0, 0, 0, 0], 1, 1), ([1, 0, 0, 0, 0, 0, 0, 0], 2, 0),
+                          ([-2, 0, 0, 0, 0, 0, 0, 0], 2, 0), ([2, -2, 0, 0, 0, 0, 0, 0], 3, 0),
+                          ([0] * 8, 0, 1)]:
+        x = np.array(vals, np.float32).reshape(1, 1, 8)
+        ref = O.compress(cfg, 0, x)
+        st = SF.parse(ref.stream)
+        tl = st.segments[0].tiles[0]
+        assert tl.mode == mode, (vals, tl.mode)
+        zz = [2 * v if v >= 0 else -2 * v - 1 for v in vals]
+        assert max(zz).bit_length() == w
+        assert SF.bitpack_size(x[0], 1, 1, 8, 0.5, 1) == (32 if w <= 1 else 48)
+        np.testing.assert_array_equal(O.decompress(cfg, ref.stream), x)
+
+
 def test_compression_ratio_is_total_bytes_based():
     # Table V "avg." is the harmonic mean of per-table ratios, i.e. the ratio
     # of total bytes for equal-sized tables; the stream reports total bytes.
