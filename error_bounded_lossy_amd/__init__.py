@@ -73,6 +73,8 @@ def lib():
     L.ec_max_compressed_bytes.argtypes = [vp]
     L.ec_compress.restype = st
     L.ec_compress.argtypes = [vp, ctypes.c_int64, vp, vp, sz, vp]
+    L.ec_compress_static.restype = st
+    L.ec_compress_static.argtypes = [vp, ctypes.c_int64, vp, vp, sz, vp]
     L.ec_decompress.restype = st
     L.ec_decompress.argtypes = [vp, vp, sz, vp, vp]
     L.ec_ratio.restype = st
@@ -172,7 +174,11 @@ class Plan:
     """
 
     def __init__(self, T: int, B: int, D: int, P: int = 1, eb_mode: int = EB_ABS, eb=1e-4,
-                 table_mult=None, schedule=None, debug_hash_bits: int = 0, device=None):
+                 table_mult=None, schedule=None, debug_hash_bits: int = 0, device=None,
+                 workspace: bool = True):
+        """workspace=False builds a plan without a workspace: compress with
+        compress_static (the library's static device scratch), decompress as
+        usual."""
         import torch
         self.T, self.B, self.D, self.P = T, B, D, P
         self._keep = []
@@ -182,12 +188,15 @@ class Plan:
         nbytes = int(L.ec_workspace_bytes(ctypes.byref(self._desc)))
         if nbytes == 0:
             raise ECError(EC_ERR_INVALID, "ec_workspace_bytes")
+        self.workspace_bytes = nbytes
         self.device = torch.device(device or "cuda")
-        self.workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
-        base = self.workspace.data_ptr()
-        aligned = (base + 255) // 256 * 256
-        self._desc.d_workspace = aligned
-        self._desc.workspace_bytes = nbytes
+        self.workspace = None
+        if workspace:
+            self.workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
+            base = self.workspace.data_ptr()
+            aligned = (base + 255) // 256 * 256
+            self._desc.d_workspace = aligned
+            self._desc.workspace_bytes = nbytes
         h = ctypes.c_void_p()
         _check(L.ec_plan(ctypes.byref(self._desc), ctypes.byref(h)), "ec_plan")
         self._h = h
@@ -215,6 +224,16 @@ class Plan:
         assert out.dtype == torch.uint8 and out.is_contiguous()
         _check(lib().ec_compress(self._h, int(iteration), x.data_ptr(), out.data_ptr(),
                                  out.numel(), _stream_handle(stream)), "ec_compress")
+
+    def compress_static(self, x, out, iteration: int = 0, stream=None):
+        """Enqueue compression like compress(), with the library's static
+        device scratch instead of the plan's workspace (ec_compress_static)."""
+        import torch
+        assert x.dtype == torch.float32 and x.is_contiguous() and x.numel() == self.T * self.B * self.D
+        assert out.dtype == torch.uint8 and out.is_contiguous()
+        _check(lib().ec_compress_static(self._h, int(iteration), x.data_ptr(), out.data_ptr(),
+                                        out.numel(), _stream_handle(stream)),
+               "ec_compress_static")
 
     def decompress(self, stream_bytes, y, stream=None):
         """Enqueue decompression of the uint8 stream into fp32 y [T,B,D]."""

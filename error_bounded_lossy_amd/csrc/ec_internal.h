@@ -133,5 +133,11 @@ bool encode_has_assembly(uint32_t D);
 hipError_t launch_assemble(const EncArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecArgs& a, hipStream_t s);
 hipError_t set_encode_lds_limit(size_t bytes);
+// Address of the current device's copy of the library's static device scratch
+// (EC_STATIC_SCRATCH_BYTES, include/ec.h), looked up once per device.
+hipError_t static_scratch(void** out);
+// Copy `bytes` (a multiple of 16) from src (device memory or device-mapped
+// pinned host memory) to dst on stream s, with a kernel.
+hipError_t launch_copy_words(void* dst, const void* src, uint64_t bytes, hipStream_t s);
 
 }  // namespace ec

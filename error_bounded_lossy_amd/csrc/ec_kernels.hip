@@ -24,7 +24,10 @@
 // sequence div, rint, mul, sub.
 #include "ec_internal.h"
 
+#include <mutex>
 #include <type_traits>
+
+#include "../../include/ec.h"
 
 #ifndef EC_PREP_LOADS
 #define EC_PREP_LOADS 8  // 128-bit loads in flight per thread in the range pass
@@ -2846,7 +2849,51 @@ __global__ void __launch_bounds__(kThreads) ec_decode_fast(const uint8_t* __rest
   }
 }
 
+// ---------------------------------------------------------------------------
+// the library's own scratch for ec_compress_static (callers that cannot
+// allocate): one copy per device, alive until the process ends
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[EC_STATIC_SCRATCH_BYTES];
+
+__global__ void __launch_bounds__(kThreads) ec_copy_kernel(uint4* __restrict__ dst,
+                                                          const uint4* __restrict__ src,
+                                                          uint64_t n16) {
+  for (uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x; i < n16;
+       i += (uint64_t)gridDim.x * kThreads)
+    dst[i] = src[i];
+}
+
 }  // namespace
+
+hipError_t static_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(mu);
+  if (!addr[dev]) {
+    // the array's name in host code is not a device address: every use goes
+    // through the address the runtime reports for this device's copy
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_copy_words(void* dst, const void* src, uint64_t bytes, hipStream_t s) {
+  const uint64_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  uint64_t g = (n16 + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(ec_copy_kernel, dim3((uint32_t)(g > 1024 ? 1024 : g)), dim3(kThreads), 0, s,
+                     static_cast<uint4*>(dst), static_cast<const uint4*>(src), n16);
+  return hipGetLastError();
+}
 
 hipError_t launch_prep(const PrepArgs& a, uint32_t grid, hipStream_t s) {
   hipLaunchKernelGGL(ec_prep_kernel, dim3(grid), dim3(kThreads), 0, s, a);

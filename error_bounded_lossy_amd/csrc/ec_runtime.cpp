@@ -208,6 +208,12 @@ struct ec_plan_s {
   ec::Work work{};
   ec::Report* report_host = nullptr;
   ec::Report* report_dev = nullptr;
+  // the workspace's constant region [0, L.dyn) as written at plan time, in
+  // pinned device-mapped host memory: copied into the static scratch by every
+  // ec_compress_static call, and read by decompression when the plan has no
+  // workspace
+  uint8_t* consts_host = nullptr;
+  uint8_t* consts_dev = nullptr;
   hipEvent_t done = nullptr;
   bool have_done = false;
   int32_t* dbg_codes = nullptr;
@@ -253,6 +259,49 @@ void record_done(ec_plan_s* pl, hipStream_t s) {
   if (hipEventRecord(pl->done, s) == hipSuccess) pl->have_done = true;
 }
 
+// Workspace pointers of layout L inside the buffer at `ws` (a caller's
+// workspace or the library's static scratch).
+ec::Work make_work(const Layout& L, uint8_t* ws) {
+  ec::Work w{};
+  w.eb_base = reinterpret_cast<const float*>(ws + L.eb_base);
+  w.mult = reinterpret_cast<const float*>(ws + L.mult);
+  w.seg_tile_base = reinterpret_cast<const uint32_t*>(ws + L.seg_tile_base);
+  w.hash_off = reinterpret_cast<const uint64_t*>(ws + L.hash_off);
+  w.hash_log2 = reinterpret_cast<const uint32_t*>(ws + L.hash_log2);
+  w.range_part = reinterpret_cast<float*>(ws + L.range_part);
+  w.nbr = L.nbr;
+  w.dyn = reinterpret_cast<uint64_t*>(ws + L.dyn);
+  w.dyn_words = L.dyn_bytes / 8;
+  w.seg_start = reinterpret_cast<uint64_t*>(ws + L.seg_start);
+  w.seg_end = reinterpret_cast<uint64_t*>(ws + L.seg_end);
+  w.chunk_start = reinterpret_cast<uint64_t*>(ws + L.chunk_start);
+  w.seg_fin = reinterpret_cast<uint32_t*>(ws + L.seg_fin);
+  w.tile_status = reinterpret_cast<uint64_t*>(ws + L.tile_status);
+  w.block_status = reinterpret_cast<uint64_t*>(ws + L.block_status);
+  w.tile_inserted = reinterpret_cast<uint32_t*>(ws + L.tile_inserted);
+  w.tile_rec = reinterpret_cast<uint64_t*>(ws + L.tile_rec);
+  w.tile_U = reinterpret_cast<uint32_t*>(ws + L.tile_U);
+  w.tile_nout = reinterpret_cast<uint32_t*>(ws + L.tile_nout);
+  w.hash = reinterpret_cast<uint64_t*>(ws + L.hash);
+  if (ec::encode_has_assembly(L.sh.D)) {
+    w.stage_pl = reinterpret_cast<uint64_t*>(ws + L.stage_pl);
+    w.stage_w = ws + L.stage_w;
+    w.stage_om = reinterpret_cast<uint64_t*>(ws + L.stage_om);
+    w.stage_slot = reinterpret_cast<uint32_t*>(ws + L.stage_slot);
+    w.tile_info = reinterpret_cast<uint32_t*>(ws + L.tile_info);
+    w.tile_bitmap = reinterpret_cast<uint64_t*>(ws + L.tile_bitmap);
+    w.tile_first = reinterpret_cast<uint32_t*>(ws + L.tile_first);
+    w.seg_eb = reinterpret_cast<uint32_t*>(ws + L.seg_eb);
+  }
+  return w;
+}
+
+// Enqueue one compression into the workspace described by `work`: the range
+// pass (and the clearing of the dynamic region when `clear`), quantization,
+// and for D = 64, 128, 256 the assembly passes.
+ec_status enqueue_compress(ec_plan_s* pl, const ec::Work& work, bool clear, int64_t iter,
+                           const float* d_in, void* d_out, size_t out_cap, hipStream_t s);
+
 }  // namespace
 
 extern "C" {
@@ -276,8 +325,10 @@ ec_status ec_plan(const ec_plan_desc* desc, ec_plan_t* out) {
     return st;
   }
   const Layout& L = pl->L;
-  if (!desc->d_workspace || desc->workspace_bytes < L.total ||
-      ((uintptr_t)desc->d_workspace & 255u)) {
+  // no workspace at all: a plan for ec_compress_static (and ec_decompress) only
+  const bool no_ws = !desc->d_workspace && desc->workspace_bytes == 0;
+  if (!no_ws && (!desc->d_workspace || desc->workspace_bytes < L.total ||
+                 ((uintptr_t)desc->d_workspace & 255u))) {
     delete pl;
     return desc->d_workspace && desc->workspace_bytes < L.total ? EC_ERR_CAPACITY
                                                                  : EC_ERR_INVALID;
@@ -313,52 +364,40 @@ ec_status ec_plan(const ec_plan_desc* desc, ec_plan_t* out) {
   }
   pl->report_dev = static_cast<ec::Report*>(dp);
 
-  // constants into the workspace (blocking copies, plan time only)
-  uint8_t* ws = pl->ws;
-  bool ok = hipMemcpy(ws + L.eb_base, pl->eb.data(), 4ull * T, hipMemcpyHostToDevice) == hipSuccess;
-  ok = ok && hipMemcpy(ws + L.mult, pl->mult.data(), 4ull * T, hipMemcpyHostToDevice) == hipSuccess;
-  ok = ok && hipMemcpy(ws + L.seg_tile_base, L.seg_tile_base_v.data(),
-                       4ull * L.seg_tile_base_v.size(), hipMemcpyHostToDevice) == hipSuccess;
-  ok = ok && hipMemcpy(ws + L.hash_off, L.hash_off_v.data(), 8ull * L.hash_off_v.size(),
-                       hipMemcpyHostToDevice) == hipSuccess;
-  ok = ok && hipMemcpy(ws + L.hash_log2, L.hash_log2_v.data(), 4ull * L.hash_log2_v.size(),
-                       hipMemcpyHostToDevice) == hipSuccess;
-  if (!ok) {
+  // the constant region, built on the host in pinned device-mapped memory
+  void* cp = nullptr;
+  void* cdp = nullptr;
+  const uint64_t cbytes = L.dyn;
+  if (hipHostMalloc(&cp, cbytes, hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess ||
+      hipHostGetDevicePointer(&cdp, cp, 0) != hipSuccess) {
+    if (cp) (void)hipHostFree(cp);
     (void)hipEventDestroy(pl->done);
     (void)hipHostFree(hp);
     delete pl;
     return EC_ERR_DEVICE;
   }
-  ec::Work& w = pl->work;
-  w.eb_base = reinterpret_cast<const float*>(ws + L.eb_base);
-  w.mult = reinterpret_cast<const float*>(ws + L.mult);
-  w.seg_tile_base = reinterpret_cast<const uint32_t*>(ws + L.seg_tile_base);
-  w.hash_off = reinterpret_cast<const uint64_t*>(ws + L.hash_off);
-  w.hash_log2 = reinterpret_cast<const uint32_t*>(ws + L.hash_log2);
-  w.range_part = reinterpret_cast<float*>(ws + L.range_part);
-  w.nbr = L.nbr;
-  w.dyn = reinterpret_cast<uint64_t*>(ws + L.dyn);
-  w.dyn_words = L.dyn_bytes / 8;
-  w.seg_start = reinterpret_cast<uint64_t*>(ws + L.seg_start);
-  w.seg_end = reinterpret_cast<uint64_t*>(ws + L.seg_end);
-  w.chunk_start = reinterpret_cast<uint64_t*>(ws + L.chunk_start);
-  w.seg_fin = reinterpret_cast<uint32_t*>(ws + L.seg_fin);
-  w.tile_status = reinterpret_cast<uint64_t*>(ws + L.tile_status);
-  w.block_status = reinterpret_cast<uint64_t*>(ws + L.block_status);
-  w.tile_inserted = reinterpret_cast<uint32_t*>(ws + L.tile_inserted);
-  w.tile_rec = reinterpret_cast<uint64_t*>(ws + L.tile_rec);
-  w.tile_U = reinterpret_cast<uint32_t*>(ws + L.tile_U);
-  w.tile_nout = reinterpret_cast<uint32_t*>(ws + L.tile_nout);
-  w.hash = reinterpret_cast<uint64_t*>(ws + L.hash);
-  if (ec::encode_has_assembly(L.sh.D)) {
-    w.stage_pl = reinterpret_cast<uint64_t*>(ws + L.stage_pl);
-    w.stage_w = ws + L.stage_w;
-    w.stage_om = reinterpret_cast<uint64_t*>(ws + L.stage_om);
-    w.stage_slot = reinterpret_cast<uint32_t*>(ws + L.stage_slot);
-    w.tile_info = reinterpret_cast<uint32_t*>(ws + L.tile_info);
-    w.tile_bitmap = reinterpret_cast<uint64_t*>(ws + L.tile_bitmap);
-    w.tile_first = reinterpret_cast<uint32_t*>(ws + L.tile_first);
-    w.seg_eb = reinterpret_cast<uint32_t*>(ws + L.seg_eb);
+  pl->consts_host = static_cast<uint8_t*>(cp);
+  pl->consts_dev = static_cast<uint8_t*>(cdp);
+  uint8_t* img = pl->consts_host;
+  std::memset(img, 0, cbytes);
+  std::memcpy(img + L.eb_base, pl->eb.data(), 4ull * T);
+  std::memcpy(img + L.mult, pl->mult.data(), 4ull * T);
+  std::memcpy(img + L.seg_tile_base, L.seg_tile_base_v.data(), 4ull * L.seg_tile_base_v.size());
+  std::memcpy(img + L.hash_off, L.hash_off_v.data(), 8ull * L.hash_off_v.size());
+  std::memcpy(img + L.hash_log2, L.hash_log2_v.data(), 4ull * L.hash_log2_v.size());
+  // set-up of the static scratch on this device (its address, once per device)
+  void* scr = nullptr;
+  if (ec::static_scratch(&scr) != hipSuccess) {
+    ec_plan_destroy(pl);
+    return EC_ERR_DEVICE;
+  }
+  if (!no_ws) {
+    // constants into the workspace (a blocking copy, plan time only)
+    if (hipMemcpy(pl->ws, img, cbytes, hipMemcpyHostToDevice) != hipSuccess) {
+      ec_plan_destroy(pl);
+      return EC_ERR_DEVICE;
+    }
+    pl->work = make_work(L, pl->ws);
   }
   *out = pl;
   return EC_OK;
@@ -370,6 +409,7 @@ ec_status ec_plan_destroy(ec_plan_t pl) {
   for (hipEvent_t e : pl->prof_pool) (void)hipEventDestroy(e);
   if (pl->done) (void)hipEventDestroy(pl->done);
   if (pl->report_host) (void)hipHostFree(pl->report_host);
+  if (pl->consts_host) (void)hipHostFree(pl->consts_host);
   delete pl;
   return EC_OK;
 }
@@ -378,55 +418,45 @@ size_t ec_max_compressed_bytes(ec_plan_t pl) { return pl ? (size_t)pl->L.max_byt
 
 ec_status ec_compress(ec_plan_t pl, int64_t iter, const float* d_in, void* d_out, size_t out_cap,
                       void* stream) {
-  if (!pl || !d_out) return EC_ERR_INVALID;
+  if (!pl || !d_out || !pl->ws) return EC_ERR_INVALID;
   const ec::Shape& sh = pl->L.sh;
   if (!d_in && (uint64_t)sh.B * sh.D > 0) return EC_ERR_INVALID;
   if (((uintptr_t)d_in & 15u) || ((uintptr_t)d_out & 15u)) return EC_ERR_INVALID;
   if (out_cap < pl->L.max_bytes) return EC_ERR_CAPACITY;
   hipStream_t s = static_cast<hipStream_t>(stream);
-
   // D = 64, 128, 256: the dynamic region is zeroed on the plan's first call
   // only (the write pass leaves the hash tables clear); a call that fails to
   // launch all its kernels makes the next one clear again
   const bool assembled = ec::encode_has_assembly(sh.D);
   const bool clear = !assembled || !pl->hash_clear;
   pl->hash_clear = false;
-  ec::PrepArgs pa{d_in, sh, pl->work, pl->desc.eb_mode == EC_EB_REL_RANGE ? 1 : 0, clear ? 1 : 0};
-  uint32_t grid;
-  if (pa.rel && sh.B > 0) {
-    grid = sh.T * pl->L.nbr;
-  } else {
-    pa.rel = 0;
-    uint64_t g = (pl->work.dyn_words + 1023) / 1024;
-    grid = (uint32_t)(g < 1 ? 1 : (g > 2048 ? 2048 : g));
-  }
-  ec_status st = EC_OK;
-  if (pa.rel || pa.clear) st = profiled(pl, EC_KERNEL_PREP, s, [&] { return ec::launch_prep(pa, grid, s); });
+  ec_status st = enqueue_compress(pl, pl->work, clear, iter, d_in, d_out, out_cap, s);
   if (st != EC_OK) return st;
+  if (assembled) pl->hash_clear = true;
+  record_done(pl, s);
+  return EC_OK;
+}
 
-  ec::EncArgs ea{};
-  ea.x = d_in;
-  ea.out = static_cast<uint8_t*>(d_out);
-  ea.out_cap = out_cap;
-  ea.sh = sh;
-  ea.w = pl->work;
-  ea.eb_mode = (uint32_t)pl->desc.eb_mode;
-  ea.iter = iter;
-  ea.sched = schedule_factor(pl->desc.sched, iter);
-  uint32_t hb = pl->desc.debug_hash_bits;
-  ea.hash_keep = (hb == 0 || hb >= 64) ? ~0ull : ((1ull << hb) - 1ull);
-  ea.report = pl->report_dev;
-  ea.dbg_codes = pl->dbg_codes;
-  ea.dbg_outlier = pl->dbg_outlier;
-  ea.dbg_first = pl->dbg_first;
-  ea.dbg_eb = pl->dbg_eb;
-  st = profiled(pl, EC_KERNEL_ENCODE, s, [&] { return ec::launch_encode(ea, s); });
+ec_status ec_compress_static(ec_plan_t pl, int64_t iter, const float* d_in, void* d_out,
+                             size_t out_cap, void* stream) {
+  if (!pl || !d_out) return EC_ERR_INVALID;
+  const ec::Shape& sh = pl->L.sh;
+  if (!d_in && (uint64_t)sh.B * sh.D > 0) return EC_ERR_INVALID;
+  if (((uintptr_t)d_in & 15u) || ((uintptr_t)d_out & 15u)) return EC_ERR_INVALID;
+  if (out_cap < pl->L.max_bytes) return EC_ERR_CAPACITY;
+  if (pl->L.total > EC_STATIC_SCRATCH_BYTES) return EC_ERR_CAPACITY;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* scr = nullptr;  // this device's copy of the scratch (looked up once per device)
+  if (ec::static_scratch(&scr) != hipSuccess) return EC_ERR_DEVICE;
+  uint8_t* base = static_cast<uint8_t*>(scr);
+  // the scratch holds whatever the last call on this device left there: the
+  // plan's constants are copied in and the dynamic region is cleared, every call
+  ec_status st = profiled(pl, EC_KERNEL_PREP, s, [&] {
+    return ec::launch_copy_words(base, pl->consts_dev, pl->L.range_part, s);
+  });
   if (st != EC_OK) return st;
-  if (assembled) {
-    st = profiled(pl, EC_KERNEL_ASSEMBLE, s, [&] { return ec::launch_assemble(ea, s); });
-    if (st != EC_OK) return st;
-    pl->hash_clear = true;
-  }
+  st = enqueue_compress(pl, make_work(pl->L, base), true, iter, d_in, d_out, out_cap, s);
+  if (st != EC_OK) return st;
   record_done(pl, s);
   return EC_OK;
 }
@@ -443,7 +473,10 @@ ec_status ec_decompress(ec_plan_t pl, const void* d_stream, size_t stream_cap, f
   da.cap = stream_cap;
   da.y = d_out;
   da.sh = sh;
-  da.seg_tile_base = pl->work.seg_tile_base;
+  // without a workspace the plan's pinned constants serve (read over the bus,
+  // and only when the segments have different tile counts)
+  da.seg_tile_base = pl->ws ? pl->work.seg_tile_base
+                            : reinterpret_cast<const uint32_t*>(pl->consts_dev + pl->L.seg_tile_base);
   da.report = pl->report_dev;
   const ec_status st = profiled(pl, EC_KERNEL_DECODE, s, [&] { return ec::launch_decode(da, s); });
   if (st != EC_OK) return st;
@@ -531,3 +564,48 @@ ec_status ec_profile_read(ec_plan_t pl, int kernel, double* total_ms, uint64_t* 
 }
 
 }  // extern "C"
+
+namespace {
+
+ec_status enqueue_compress(ec_plan_s* pl, const ec::Work& work, bool clear, int64_t iter,
+                           const float* d_in, void* d_out, size_t out_cap, hipStream_t s) {
+  const ec::Shape& sh = pl->L.sh;
+  ec::PrepArgs pa{d_in, sh, work, pl->desc.eb_mode == EC_EB_REL_RANGE ? 1 : 0, clear ? 1 : 0};
+  uint32_t grid;
+  if (pa.rel && sh.B > 0) {
+    grid = sh.T * pl->L.nbr;
+  } else {
+    pa.rel = 0;
+    uint64_t g = (work.dyn_words + 1023) / 1024;
+    grid = (uint32_t)(g < 1 ? 1 : (g > 2048 ? 2048 : g));
+  }
+  ec_status st = EC_OK;
+  if (pa.rel || pa.clear) st = profiled(pl, EC_KERNEL_PREP, s, [&] { return ec::launch_prep(pa, grid, s); });
+  if (st != EC_OK) return st;
+
+  ec::EncArgs ea{};
+  ea.x = d_in;
+  ea.out = static_cast<uint8_t*>(d_out);
+  ea.out_cap = out_cap;
+  ea.sh = sh;
+  ea.w = work;
+  ea.eb_mode = (uint32_t)pl->desc.eb_mode;
+  ea.iter = iter;
+  ea.sched = schedule_factor(pl->desc.sched, iter);
+  uint32_t hb = pl->desc.debug_hash_bits;
+  ea.hash_keep = (hb == 0 || hb >= 64) ? ~0ull : ((1ull << hb) - 1ull);
+  ea.report = pl->report_dev;
+  ea.dbg_codes = pl->dbg_codes;
+  ea.dbg_outlier = pl->dbg_outlier;
+  ea.dbg_first = pl->dbg_first;
+  ea.dbg_eb = pl->dbg_eb;
+  st = profiled(pl, EC_KERNEL_ENCODE, s, [&] { return ec::launch_encode(ea, s); });
+  if (st != EC_OK) return st;
+  if (ec::encode_has_assembly(sh.D)) {
+    st = profiled(pl, EC_KERNEL_ASSEMBLE, s, [&] { return ec::launch_assemble(ea, s); });
+    if (st != EC_OK) return st;
+  }
+  return EC_OK;
+}
+
+}  // namespace

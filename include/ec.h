@@ -136,7 +136,9 @@ size_t ec_workspace_bytes(const ec_plan_desc* desc);
  * bounds with their class multipliers and the iteration-wise schedule of
  * section III-C / Algorithm 1 (table-wise and iteration-wise levels).  Host
  * work plus one blocking copy of the per-table constants into the workspace.
- * *out is NULL on failure. */
+ * d_workspace == NULL together with workspace_bytes == 0 builds a plan without
+ * a workspace, usable with ec_compress_static, ec_decompress and ec_ratio
+ * only (ec_compress then returns EC_ERR_INVALID).  *out is NULL on failure. */
 ec_status ec_plan(const ec_plan_desc* desc, ec_plan_t* out);
 
 /* Release the plan's host resources (the workspace stays the caller's). */
@@ -155,7 +157,7 @@ size_t ec_max_compressed_bytes(ec_plan_t plan);
  * Fig. 7).  The stream's size becomes known on the host through ec_ratio; on
  * the device it is the u64 at byte 48 of d_out, and chunk p's size is the u64
  * at byte 64 + 8p (the size metadata of section III-A, stage 2).  Errors:
- * EC_ERR_INVALID (NULL or misaligned pointers),
+ * EC_ERR_INVALID (NULL or misaligned pointers, a plan without a workspace),
  * EC_ERR_CAPACITY (out_cap too small), EC_ERR_DEVICE (a launch failed). */
 ec_status ec_compress(ec_plan_t plan, int64_t iter, const float* d_in, void* d_out,
                       size_t out_cap, void* stream);
@@ -176,6 +178,24 @@ ec_status ec_decompress(ec_plan_t plan, const void* d_stream, size_t stream_cap,
  * and clears the sticky device status. */
 ec_status ec_ratio(ec_plan_t plan, double* total_cr, uint64_t* compressed_bytes,
                    double* per_segment_cr);
+
+/* Bytes of the library's static device scratch (one copy per device). */
+#define EC_STATIC_SCRATCH_BYTES (64ull << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): compress
+ * exactly as ec_compress does (same stream bytes), but with the library's own
+ * static device scratch of EC_STATIC_SCRATCH_BYTES instead of the plan's
+ * workspace, so the plan may have none.  Allocates nothing and frees nothing.
+ * The scratch is shared by every call on a device and keeps the last call's
+ * contents: each call copies the plan's constants in and clears what must
+ * start at zero, and calls that overlap on one device (any plan, any stream)
+ * race and corrupt each other's streams.  Errors: those of ec_compress, and
+ * EC_ERR_CAPACITY when the plan needs more than EC_STATIC_SCRATCH_BYTES
+ * (ec_workspace_bytes of its descriptor; e.g. 26 x 8192 x 128 fits, 64 x
+ * 16384 x 256 does not). */
+ec_status ec_compress_static(ec_plan_t plan, int64_t iter, const float* d_in, void* d_out,
+                             size_t out_cap, void* stream);
 
 const char* ec_status_string(ec_status s);
 

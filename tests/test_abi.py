@@ -63,9 +63,16 @@ def test_plan_rejects_bad_arguments_before_touching_the_device():
     assert L.ec_decompress(None, None, 0, None, None) == ec.EC_ERR_INVALID
     assert L.ec_ratio(None, None, None, None) == ec.EC_ERR_INVALID
     assert L.ec_max_compressed_bytes(None) == 0
-    # a valid descriptor without a workspace is rejected on the host
+    # a descriptor that gives a workspace size but no workspace, or a
+    # misaligned workspace, is rejected on the host (no workspace at all, size
+    # 0, is a plan for ec_compress_static)
     d = ec._desc(1, 10, 4, 1, ec.EB_ABS, 1e-3, None, None, 0, keep)
+    d.workspace_bytes = 1 << 20
     assert L.ec_plan(ctypes.byref(d), ctypes.byref(h)) == ec.EC_ERR_INVALID
+    d.d_workspace = 0x1010
+    assert L.ec_plan(ctypes.byref(d), ctypes.byref(h)) == ec.EC_ERR_INVALID
+    assert not h.value
+    assert L.ec_compress_static(None, 0, None, None, 0, None) == ec.EC_ERR_INVALID
 
 
 def test_binding_has_no_fallback(monkeypatch, tmp_path):
