@@ -76,6 +76,12 @@ def lib():
         L.ebo_unzigzag.argtypes = [ctypes.c_uint32]
         L.ebo_homo_index.restype = ctypes.c_double
         L.ebo_homo_index.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
+        L.ebo_homo_counts.restype = ctypes.c_int
+        L.ebo_homo_counts.argtypes = [cfgp, ctypes.c_int64, f32p, ctypes.c_void_p, ctypes.c_void_p]
+        L.ebo_classify.restype = ctypes.c_int
+        L.ebo_classify.argtypes = [ctypes.c_uint32, ctypes.c_void_p, ctypes.c_double,
+                                   ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                   ctypes.c_void_p, ctypes.c_void_p]
         L.ebo_table_eb.restype = ctypes.c_float
         L.ebo_table_eb.argtypes = [cfgp, ctypes.c_uint32, ctypes.c_int64, f32p]
         L.ebo_max_compressed_bytes.restype = ctypes.c_size_t
@@ -188,6 +194,31 @@ def unzigzag(z: int) -> int:
 
 def homo_index(n_original: int, n_compressed: int) -> float:
     return lib().ebo_homo_index(n_original, n_compressed)
+
+
+def homo_counts(cfg: Config, it: int, x: np.ndarray):
+    """(n_orig, n_quant) per segment p*T + t: eq. (1)'s distinct original and
+    distinct quantized rows."""
+    c, keep = cfg._c()
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(cfg.T, cfg.B, cfg.D)
+    no = np.zeros(cfg.P * cfg.T, np.uint32)
+    nq = np.zeros(cfg.P * cfg.T, np.uint32)
+    rc = lib().ebo_homo_counts(ctypes.byref(c), it, _f32ptr(x), no.ctypes.data, nq.ctypes.data)
+    if rc != OK:
+        raise RuntimeError(f"oracle homo_counts failed with status {rc}")
+    return no, nq
+
+
+def classify(hindex, l_thresh: float, s_thresh: float, alpha: float, beta: float):
+    """Algorithm 1's table classes (0 large, 1 medium, 2 small) and eb multipliers."""
+    h = np.ascontiguousarray(hindex, dtype=np.float64)
+    cls = np.zeros(h.size, np.int32)
+    mult = np.zeros(h.size, np.float32)
+    rc = lib().ebo_classify(h.size, h.ctypes.data, l_thresh, s_thresh, alpha, beta,
+                            cls.ctypes.data, mult.ctypes.data)
+    if rc != 0:
+        raise ValueError("invalid classification thresholds or multipliers")
+    return cls, mult
 
 
 def max_compressed_bytes(cfg: Config) -> int:

@@ -266,6 +266,72 @@ static int dedup_first(const uint64_t* keys, uint32_t rows, uint32_t D, uint32_t
   return 0;
 }
 
+static uint32_t count_first(const uint32_t* first, uint32_t rows) {
+  uint32_t n = 0;
+  for (uint32_t r = 0; r < rows; r++) n += first[r] == r;
+  return n;
+}
+
+/* eq. (1)'s counts: distinct original rows and distinct quantized rows of
+   every segment, each found as the first occurrences of a sort by key */
+int ebo_homo_counts(const ebo_cfg* c, int64_t iter, const float* x, uint32_t* n_orig,
+                    uint32_t* n_quant) {
+  if (!cfg_ok(c) || !n_orig || !n_quant || (!x && c->B > 0)) return EBO_ERR_INVALID;
+  uint32_t T = c->T, B = c->B, D = c->D, P = c->P;
+  int rc = EBO_OK;
+  for (uint32_t t = 0; t < T && rc == EBO_OK; t++) {
+    float eb = ebo_table_eb(c, t, iter, x);
+    int valid = ebo_eb_valid(eb);
+    for (uint32_t p = 0; p < P && rc == EBO_OK; p++) {
+      uint32_t row0 = chunk_row0(c, p), rows = chunk_rows(c, p);
+      size_t nel = (size_t)rows * D;
+      const float* xs = x ? x + ((size_t)t * B + row0) * D : NULL;
+      uint64_t* keys = (uint64_t*)calloc(nel + 1, sizeof(uint64_t));
+      uint32_t* first = (uint32_t*)malloc(sizeof(uint32_t) * ((size_t)rows + 1));
+      if (!keys || !first) {
+        rc = EBO_ERR_OOM;
+      } else {
+        for (size_t i = 0; i < nel; i++) keys[i] = f32_bits(xs[i]);
+        if (dedup_first(keys, rows, D, first) != 0) rc = EBO_ERR_OOM;
+        uint32_t no = count_first(first, rows), nq = no;
+        if (rc == EBO_OK && valid) {
+          for (size_t i = 0; i < nel; i++) {
+            int32_t q;
+            int o = ebo_quantize(xs[i], eb, &q);
+            keys[i] = elem_key(q, o, xs[i]);
+          }
+          if (dedup_first(keys, rows, D, first) != 0) rc = EBO_ERR_OOM;
+          nq = count_first(first, rows);
+        }
+        n_orig[(size_t)p * T + t] = no;
+        n_quant[(size_t)p * T + t] = nq;
+      }
+      free(keys);
+      free(first);
+    }
+  }
+  return rc;
+}
+
+int ebo_classify(uint32_t T, const double* hindex, double l_thresh, double s_thresh,
+                 double alpha, double beta, int32_t* cls, float* mult) {
+  if (!hindex || !cls || !mult || !(l_thresh <= s_thresh)) return -1;
+  if (!(alpha > 0.0) || !isfinite(alpha) || !(beta > 0.0) || !isfinite(beta)) return -1;
+  for (uint32_t t = 0; t < T; t++) {
+    if (hindex[t] > s_thresh) { /* strongly homogenized: small error bound */
+      cls[t] = 2;
+      mult[t] = (float)(1.0 / beta);
+    } else if (hindex[t] < l_thresh) { /* weakly homogenized: large error bound */
+      cls[t] = 0;
+      mult[t] = (float)alpha;
+    } else {
+      cls[t] = 1;
+      mult[t] = 1.0f;
+    }
+  }
+  return 0;
+}
+
 /* ------------------------------------------------------------------ */
 /* growable byte buffer                                                */
 /* ------------------------------------------------------------------ */

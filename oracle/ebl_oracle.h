@@ -117,6 +117,22 @@ int32_t ebo_unzigzag(uint32_t z);
 /* Eq. (1) Homogenization Index: (N_original - N_compressed) / N_original. */
 double ebo_homo_index(uint64_t n_original, uint64_t n_compressed);
 
+/* The counts eq. (1) takes, per segment s = p*T + t (the "# Ori. Patterns"
+ * and "# Quant. Patterns" columns of Tables III and IV): n_orig[s] = number of
+ * distinct rows of the segment as fp32 bit patterns, n_quant[s] = number of
+ * distinct quantized rows (the repeated-row key of the compressor, i.e. its
+ * U).  A segment whose eb is invalid is not quantized: n_quant = n_orig. */
+int ebo_homo_counts(const ebo_cfg* c, int64_t iter, const float* x, uint32_t* n_orig,
+                    uint32_t* n_quant);
+
+/* Algorithm 1, EMBClassification and OfflineAnalysis: table t is 'small'
+ * (class 2, multiplier 1/beta) when hindex[t] > s_thresh, 'large' (class 0,
+ * multiplier alpha) when hindex[t] < l_thresh, else 'medium' (class 1,
+ * multiplier 1).  Multipliers are rounded once to fp32.  Returns -1 for
+ * l_thresh > s_thresh or alpha, beta not finite and > 0. */
+int ebo_classify(uint32_t T, const double* hindex, double l_thresh, double s_thresh,
+                 double alpha, double beta, int32_t* cls, float* mult);
+
 /* Per-table error bound used for every segment of table t (fp32). */
 float ebo_table_eb(const ebo_cfg* c, uint32_t t, int64_t iter, const float* x);
 

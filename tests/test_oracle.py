@@ -147,6 +147,21 @@ def test_staircase_schedule_closed_forms():
     assert O.schedule(none, 12345) == 1.0
 
 
+def test_drop_schedule_closed_form():
+    # Drop_2x (Fig. 10 caption): twice the base eb for the whole initial phase,
+    # the base eb from the end of that phase on -- the staircase with one stair
+    cfg = O.Config(T=1, B=1, D=1, sched_kind=O.SCHED_STEP, sched_k=2.0, sched_phase=100,
+                   sched_steps=1)
+    for i in (0, 1, 50, 99):
+        assert O.schedule(cfg, i) == 2.0, i
+    for i in (100, 101, 10 ** 7):
+        assert O.schedule(cfg, i) == 1.0, i
+    # three times the base (the section's other comparison), dropped at 10
+    cfg3 = O.Config(T=1, B=1, D=1, sched_kind=O.SCHED_STEP, sched_k=3.0, sched_phase=10,
+                    sched_steps=1)
+    assert [O.schedule(cfg3, i) for i in (9, 10)] == [3.0, 1.0]
+
+
 def test_table_factor_is_one_rounding_of_the_product():
     cfg = O.Config(T=2, B=1, D=1, eb=(0.005, 0.01), table_mult=(1.0, 3.0),
                    sched_kind=O.SCHED_INV_SQRT, sched_t0=1000.0)
@@ -188,6 +203,101 @@ def test_homo_index_against_printed_tables():
         assert 0.0 <= eta <= 1.0
         assert round(1.0 - eta, 6) == pytest.approx(printed, abs=1e-6)
     assert O.homo_index(110, 68) == pytest.approx(42 / 110, abs=1e-15)
+
+
+def _patterns(x, eb):
+    """Distinct raw rows and distinct quantized rows, by Python sets over an
+    independent fp32 quantizer (outliers keyed by their raw bits)."""
+    raw = {x[r].tobytes() for r in range(x.shape[0])}
+    q, o = SF.quantize_np(x.reshape(-1), eb)
+    q, o = q.reshape(x.shape), o.reshape(x.shape)
+    bits = x.view(np.uint32)
+    keys = set()
+    for r in range(x.shape[0]):
+        keys.add(tuple(("o", int(bits[r, d])) if o[r, d] else ("q", int(q[r, d]))
+                       for d in range(x.shape[1])))
+    return len(raw), len(keys)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_homo_counts_match_sets_of_patterns(seed):
+    """Eq. (1)'s N_original and N_quantized per segment against Python sets of
+    rows: repeated rows, rows differing by less than a bin, outliers, NaN."""
+    rng = np.random.default_rng(40 + seed)
+    T, B, D, P = 2, 37 + 11 * seed, 3 + seed, 1 + seed % 3
+    eb = 0.05
+    base = rng.normal(0, 0.3, (T, 9, D)).astype(np.float32)
+    x = np.take_along_axis(base, rng.integers(0, 9, (T, B))[:, :, None], axis=1).copy()
+    x[:, ::4] += rng.uniform(-eb / 8, eb / 8, x[:, ::4].shape).astype(np.float32)
+    x[0, 1, 0] = np.float32(1e6)
+    x[1, 2, -1] = np.nan
+    cfg = O.Config(T=T, B=B, D=D, P=P, eb_mode=O.EB_ABS, eb=(eb,))
+    no, nq = O.homo_counts(cfg, 0, x)
+    for p in range(P):
+        r0, r1 = p * B // P, (p + 1) * B // P
+        for t in range(T):
+            want_o, want_q = _patterns(x[t, r0:r1], eb)
+            assert (no[p * T + t], nq[p * T + t]) == (want_o, want_q), (p, t)
+            assert nq[p * T + t] <= no[p * T + t]
+
+
+def test_homo_counts_closed_form_and_invalid_eb():
+    """k_i raw variants of each of m quantized patterns (perturbations well
+    inside a bin around bin centres): N_original = sum k_i, N_quantized = m, so
+    eta = 1 - m / sum k_i; a constant table under a range-relative bound has no
+    valid eb and is not quantized (N_quantized = N_original)."""
+    eb = np.float32(0.25)  # bin width 0.5: centres are multiples of 0.5
+    m, D = 5, 4
+    ks = [1, 2, 3, 4, 6]
+    rows = []
+    for i in range(m):
+        centre = np.float32(0.5) * np.arange(i, i + D, dtype=np.float32)
+        for j in range(ks[i]):
+            rows.append(centre + np.float32(0.01 * j))
+    x = np.array(rows * 2, np.float32)[None]  # every variant twice
+    cfg = O.Config(T=1, B=x.shape[1], D=D, eb_mode=O.EB_ABS, eb=(float(eb),))
+    no, nq = O.homo_counts(cfg, 0, x)
+    assert (int(no[0]), int(nq[0])) == (sum(ks), m)
+    assert O.homo_index(int(no[0]), int(nq[0])) == pytest.approx(1 - m / sum(ks))
+    const = np.full((1, 10, D), 3.0, np.float32)
+    rel = O.Config(T=1, B=10, D=D, eb_mode=O.EB_REL, eb=(0.01,))
+    no, nq = O.homo_counts(rel, 0, const)
+    assert (int(no[0]), int(nq[0])) == (1, 1)
+    x2 = np.array(rows, np.float32)[None]
+    x2[0, 0, 0] = np.nan  # range ignores NaN: still valid
+    rel2 = O.Config(T=1, B=x2.shape[1], D=D, eb_mode=O.EB_REL, eb=(0.01,))
+    no, nq = O.homo_counts(rel2, 0, x2)
+    assert int(no[0]) == sum(ks) and int(nq[0]) <= int(no[0])
+
+
+def test_classification_of_printed_kaggle_tables():
+    """Algorithm 1's classes for Table III's tables, eta read from eq. (1)
+    (one minus the printed column), with thresholds 0.1 / 0.3 and the
+    multipliers that give the pages' Large / Medium / Small bounds 0.05 / 0.03
+    / 0.01 around a medium bound of 0.03 (alpha = 5/3, beta = 3); equality
+    with a threshold is medium.  Worked by hand."""
+    rows = []
+    with open(os.path.join(HERE, "golden", "homo_index_tables.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            src, tab, eb, n_o, n_q, batch, printed = line.split()
+            if src == "TableIII":
+                rows.append((int(tab), O.homo_index(int(n_o), int(n_q))))
+    eta = [e for _, e in rows]
+    cls, mult = O.classify(eta, 0.1, 0.3, 5.0 / 3.0, 3.0)
+    want = {20: 2, 11: 2, 2: 2, 15: 1, 3: 1, 23: 0, 25: 0, 0: 0, 1: 0}
+    assert {tab: int(c) for (tab, _), c in zip(rows, cls)} == want
+    m = {0: np.float32(5.0 / 3.0), 1: np.float32(1.0), 2: np.float32(1.0 / 3.0)}
+    assert all(mult[i] == m[int(c)] for i, c in enumerate(cls))
+    assert np.float32(0.03) * m[0] == pytest.approx(0.05, rel=1e-6)
+    assert np.float32(0.03) * m[2] == pytest.approx(0.01, rel=1e-6)
+    cls, _ = O.classify([0.1, 0.3, 0.0999, 0.3001], 0.1, 0.3, 2.0, 2.0)
+    assert list(cls) == [1, 1, 0, 2]
+    with pytest.raises(ValueError):
+        O.classify([0.5], 0.4, 0.3, 2.0, 2.0)
+    with pytest.raises(ValueError):
+        O.classify([0.5], 0.1, 0.3, 0.0, 2.0)
 
 
 # --------------------------------------------------------------------------
