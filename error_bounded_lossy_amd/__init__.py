@@ -75,6 +75,14 @@ def lib():
     L.ec_compress.argtypes = [vp, ctypes.c_int64, vp, vp, sz, vp]
     L.ec_compress_static.restype = st
     L.ec_compress_static.argtypes = [vp, ctypes.c_int64, vp, vp, sz, vp]
+    u32p = ctypes.POINTER(ctypes.c_uint32)
+    L.ec_homo_counts.restype = st
+    L.ec_homo_counts.argtypes = [vp, ctypes.c_int64, vp, vp, sz, u32p, u32p, vp]
+    L.ec_classify_tables.restype = st
+    L.ec_classify_tables.argtypes = [ctypes.c_uint32, ctypes.POINTER(ctypes.c_double),
+                                     ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                     ctypes.c_double, ctypes.POINTER(ctypes.c_int32),
+                                     ctypes.POINTER(ctypes.c_float)]
     L.ec_decompress.restype = st
     L.ec_decompress.argtypes = [vp, vp, sz, vp, vp]
     L.ec_ratio.restype = st
@@ -235,6 +243,20 @@ class Plan:
                                         out.numel(), _stream_handle(stream)),
                "ec_compress_static")
 
+    def homo_counts(self, x, out, iteration: int = 0, stream=None):
+        """Compress x into out and return eq. (1)'s counts per segment p*T + t:
+        (distinct raw rows, distinct quantized rows) as two lists (waits)."""
+        import torch
+        assert x.dtype == torch.float32 and x.is_contiguous() and x.numel() == self.T * self.B * self.D
+        assert out.dtype == torch.uint8 and out.is_contiguous()
+        n = self.P * self.T
+        no = (ctypes.c_uint32 * n)()
+        nq = (ctypes.c_uint32 * n)()
+        _check(lib().ec_homo_counts(self._h, int(iteration), x.data_ptr(), out.data_ptr(),
+                                    out.numel(), no, nq, _stream_handle(stream)),
+               "ec_homo_counts")
+        return list(no), list(nq)
+
     def decompress(self, stream_bytes, y, stream=None):
         """Enqueue decompression of the uint8 stream into fp32 y [T,B,D]."""
         import torch
@@ -272,6 +294,28 @@ class Plan:
         _check(lib().ec_profile_read(self._h, int(kernel), ctypes.byref(ms), ctypes.byref(n)),
                "ec_profile_read")
         return ms.value, int(n.value)
+
+
+CLASS_LARGE, CLASS_MEDIUM, CLASS_SMALL = 0, 1, 2
+
+
+def homo_index(n_orig: int, n_quant: int) -> float:
+    """Eq. (1): (N_original - N_compressed) / N_original."""
+    return (n_orig - n_quant) / n_orig if n_orig else 0.0
+
+
+def classify_tables(homo_index_per_table, l_thresh: float, s_thresh: float, alpha: float,
+                    beta: float):
+    """Algorithm 1's table classes and eb multipliers (ec_classify_tables):
+    returns (classes, multipliers) for ec_plan_desc.table_mult."""
+    h = [float(v) for v in homo_index_per_table]
+    T = len(h)
+    hin = (ctypes.c_double * max(T, 1))(*h)
+    cls = (ctypes.c_int32 * max(T, 1))()
+    mult = (ctypes.c_float * max(T, 1))()
+    _check(lib().ec_classify_tables(T, hin, float(l_thresh), float(s_thresh), float(alpha),
+                                    float(beta), cls, mult), "ec_classify_tables")
+    return list(cls)[:T], list(mult)[:T]
 
 
 # --- canonical Huffman coder (include/ec_huffman.h) ------------------------

@@ -95,6 +95,8 @@ struct EncArgs {
   double sched;                  // iteration-wise factor, computed on the host
   uint64_t hash_keep;            // mask applied to row hashes (tests weaken it)
   Report* report;                // device pointer of the pinned report block
+  uint32_t* seg_meta;            // in the report block: [nseg][2] U, eb valid (or NULL)
+  uint32_t* seg_norig;           // in the report block: [nseg] distinct raw rows (or NULL)
   int32_t* dbg_codes;
   uint8_t* dbg_outlier;
   uint32_t* dbg_first;
@@ -132,6 +134,9 @@ hipError_t launch_encode(const EncArgs& a, hipStream_t s);
 bool encode_has_assembly(uint32_t D);
 hipError_t launch_assemble(const EncArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecArgs& a, hipStream_t s);
+// Distinct rows of every segment as raw fp32 bit patterns (into empty hash
+// tables), summed per segment into a.seg_norig: two kernels.
+hipError_t launch_distinct_raw(const EncArgs& a, hipStream_t s);
 hipError_t set_encode_lds_limit(size_t bytes);
 // Address of the current device's copy of the library's static device scratch
 // (EC_STATIC_SCRATCH_BYTES, include/ec.h), looked up once per device.

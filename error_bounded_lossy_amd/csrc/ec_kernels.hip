@@ -556,6 +556,10 @@ __device__ void complete_tile(const EncArgs& a, EncShared& sh, bool valid, float
       reinterpret_cast<uint64_t*>(sg)[3] = bytes;
       reinterpret_cast<uint64_t*>(a.out + chunk_start)[t] = seg_start - chunk_start;
       if (a.report) a.report->seg_bytes[s] = bytes;
+      if (a.seg_meta) {
+        a.seg_meta[2 * s] = U;
+        a.seg_meta[2 * s + 1] = valid ? 1u : 0u;
+      }
     }
   } else if (tid == 0) {
     report_error(a.report, kDevErrTimeout);
@@ -1631,6 +1635,10 @@ __device__ void write_stream_tables(const EncArgs& a, const TileCoord& c, uint32
       reinterpret_cast<uint64_t*>(a.out + cs)[c.t] = ss - cs;
       if (c.t == T - 1 && (T & 1u)) reinterpret_cast<uint64_t*>(a.out + cs)[T] = 0;  // table pad
       if (a.report) a.report->seg_bytes[c.s] = se - ss;
+      if (a.seg_meta) {
+        a.seg_meta[2 * c.s] = un[0];
+        a.seg_meta[2 * c.s + 1] = ebw ? 1u : 0u;
+      }
       if (c.t == T - 1) reinterpret_cast<uint64_t*>(a.out + 64)[c.pch] = se - cs;  // chunk bytes
     }
   }
@@ -1833,6 +1841,94 @@ ec_write_fast(EncArgs a) {
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// offline analysis (section III-C, eq. (1)): the distinct original rows of
+// every segment.  One workgroup per tile, 16 rows per wave: each row's hash of
+// its raw bits goes into the segment's (empty) hash table by compare-and-swap
+// with linear probing; a tag hit is confirmed by comparing the two rows' bits.
+// Equal rows have equal hashes and so meet at the first empty slot of their
+// common probe sequence, where exactly one of them wins: the winners, summed
+// per segment, are the distinct rows.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kThreads) ec_distinct_raw(EncArgs a) {
+  constexpr uint32_t kRowsPerWave = kTileRows / (kThreads / 64);
+  __shared__ uint32_t s_won[kThreads / 64];
+  const uint32_t lane = threadIdx.x & 63, wv = wave_id();
+  const uint32_t ticket = blockIdx.x;
+  const TileCoord c = tile_coord(a, ticket);
+  const uint32_t D = a.sh.D, n = c.n;
+  const float* xs = a.x + ((uint64_t)c.t * a.sh.B + chunk_row0(a.sh, c.pch)) * D;
+  uint64_t* htab = a.w.hash + a.w.hash_off[c.s];
+  const uint32_t cap_mask = (1u << a.w.hash_log2[c.s]) - 1u;
+  const uint32_t rbeg = wv * kRowsPerWave;
+  // lane L < 16 keeps the hash of the wave's row rbeg + L
+  uint32_t H = 0;
+  for (uint32_t rr = 0; rr < kRowsPerWave && rbeg + rr < n; rr++) {
+    const float* xr = xs + (uint64_t)(c.k * kTileRows + rbeg + rr) * D;
+    uint32_t h = 0;
+    for (uint32_t d = lane; d < D; d += 64) h += fmix32(f2u(xr[d]) ^ (d * 0x9e3779b9u + 0x7f4a7c15u));
+    h = fmix32(wave_sum_u32(h) + D) & (uint32_t)a.hash_keep;
+    if (lane == rr) H = h;
+  }
+  const uint32_t row = c.k * kTileRows + rbeg + lane;  // segment row of the lane's row
+  bool active = lane < kRowsPerWave && rbeg + lane < n;
+  const uint64_t mine = ((uint64_t)H << 32) | (uint64_t)(row + 1);
+  uint32_t slot = H & cap_mask, won = 0, cand = 0, guard = 0;
+  while (__ballot(active) != 0) {
+    bool need = false;
+    if (active) {
+      const uint64_t old = atomicCAS((unsigned long long*)&htab[slot], 0ull, (unsigned long long)mine);
+      if (old == 0) {
+        won = 1;
+        active = false;
+      } else if ((uint32_t)(old >> 32) == H && (uint32_t)old - 1u < c.rows) {
+        need = true;
+        cand = (uint32_t)old - 1u;
+      } else {
+        slot = (slot + 1) & cap_mask;
+      }
+    }
+    uint64_t m = __ballot(need);
+    while (m) {  // the whole wave compares one candidate pair at a time
+      const int L = __ffsll((long long)m) - 1;
+      m &= m - 1;
+      const uint32_t ra = __shfl(row, L), rb = __shfl(cand, L);
+      bool eq = true;
+      for (uint32_t d = lane; d < D; d += 64)
+        eq = eq && f2u(xs[(uint64_t)ra * D + d]) == f2u(xs[(uint64_t)rb * D + d]);
+      eq = __all(eq);
+      if ((int)lane == L) {
+        if (eq) active = false;
+        else slot = (slot + 1) & cap_mask;
+      }
+    }
+    if (++guard > cap_mask + 2) {  // cannot happen: the table is at most a quarter full
+      if (active) report_error(a.report, kDevErrTimeout);
+      active = false;
+    }
+  }
+  const uint32_t w = wave_sum_u32(won);
+  if (lane == 0) s_won[wv] = w;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+    for (uint32_t q = 0; q < kThreads / 64; q++) t += s_won[q];
+    a.w.tile_status[ticket] = t;
+  }
+}
+
+// One wave per segment: the segment's distinct rows, summed over its tiles.
+__global__ void __launch_bounds__(kThreads) ec_distinct_sum(EncArgs a) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t s = blockIdx.x * (kThreads / 64) + wave_id();
+  if (s >= a.sh.nseg) return;
+  const uint32_t b = a.w.seg_tile_base[s], e = a.w.seg_tile_base[s + 1];
+  uint64_t v = 0;
+  for (uint32_t j = b + lane; j < e; j += 64) v += a.w.tile_status[j];
+  v = wave_sum_u64(v);
+  if (lane == 0 && a.seg_norig) a.seg_norig[s] = (uint32_t)v;
 }
 
 // ---------------------------------------------------------------------------
@@ -2944,6 +3040,12 @@ hipError_t launch_assemble(const EncArgs& a, hipStream_t s) {
     default:
       return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_distinct_raw(const EncArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(ec_distinct_raw, dim3(a.sh.ntiles), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(ec_distinct_sum, dim3((a.sh.nseg + 3) / 4), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

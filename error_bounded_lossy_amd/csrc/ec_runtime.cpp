@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstddef>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -208,6 +209,7 @@ struct ec_plan_s {
   ec::Work work{};
   ec::Report* report_host = nullptr;
   ec::Report* report_dev = nullptr;
+  size_t meta_off = 0, norig_off = 0;  // byte offsets in the report block
   // the workspace's constant region [0, L.dyn) as written at plan time, in
   // pinned device-mapped host memory: copied into the static scratch by every
   // ec_compress_static call, and read by decompression when the plan has no
@@ -347,7 +349,11 @@ ec_status ec_plan(const ec_plan_desc* desc, ec_plan_t* out) {
     delete pl;
     return EC_ERR_UNSUPPORTED;
   }
-  size_t rep_bytes = sizeof(ec::Report) + 8ull * L.sh.nseg;
+  // report block: the Report header with seg_bytes[nseg], then per segment
+  // (U, eb valid) and the distinct raw rows of the last pattern count
+  const size_t meta_off = aup(offsetof(ec::Report, seg_bytes) + 8ull * L.sh.nseg, 8);
+  const size_t norig_off = meta_off + 8ull * L.sh.nseg;
+  size_t rep_bytes = norig_off + 4ull * L.sh.nseg + 16;
   void* hp = nullptr;
   if (hipHostMalloc(&hp, rep_bytes, hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess) {
     delete pl;
@@ -363,6 +369,8 @@ ec_status ec_plan(const ec_plan_desc* desc, ec_plan_t* out) {
     return EC_ERR_DEVICE;
   }
   pl->report_dev = static_cast<ec::Report*>(dp);
+  pl->meta_off = meta_off;
+  pl->norig_off = norig_off;
 
   // the constant region, built on the host in pinned device-mapped memory
   void* cp = nullptr;
@@ -507,6 +515,66 @@ ec_status ec_ratio(ec_plan_t pl, double* total_cr, uint64_t* compressed_bytes,
   return EC_OK;
 }
 
+ec_status ec_homo_counts(ec_plan_t pl, int64_t iter, const float* d_in, void* d_out,
+                         size_t out_cap, uint32_t* n_orig, uint32_t* n_quant, void* stream) {
+  if (!pl || !n_orig || !n_quant) return EC_ERR_INVALID;
+  ec_status st = ec_compress(pl, iter, d_in, d_out, out_cap, stream);
+  if (st != EC_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const ec::Shape& sh = pl->L.sh;
+  // the hash tables again, empty, for the raw rows (the next compression
+  // clears them: they are left holding raw rows)
+  pl->hash_clear = false;
+  ec::PrepArgs pa{d_in, sh, pl->work, 0, 1};
+  uint64_t g = (pl->work.dyn_words + 1023) / 1024;
+  const uint32_t grid = (uint32_t)(g < 1 ? 1 : (g > 2048 ? 2048 : g));
+  if (ec::launch_prep(pa, grid, s) != hipSuccess) return EC_ERR_DEVICE;
+  ec::EncArgs ea{};
+  ea.x = d_in;
+  ea.sh = sh;
+  ea.w = pl->work;
+  uint32_t hb = pl->desc.debug_hash_bits;
+  ea.hash_keep = (hb == 0 || hb >= 64) ? ~0ull : ((1ull << hb) - 1ull);
+  ea.report = pl->report_dev;
+  uint8_t* rep = reinterpret_cast<uint8_t*>(pl->report_dev);
+  ea.seg_norig = reinterpret_cast<uint32_t*>(rep + pl->norig_off);
+  if (ec::launch_distinct_raw(ea, s) != hipSuccess) return EC_ERR_DEVICE;
+  if (hipEventRecord(pl->done, s) != hipSuccess) return EC_ERR_DEVICE;
+  pl->have_done = true;
+  if (hipEventSynchronize(pl->done) != hipSuccess) return EC_ERR_DEVICE;
+  const uint8_t* host = reinterpret_cast<const uint8_t*>(pl->report_host);
+  const volatile uint32_t* meta = reinterpret_cast<const volatile uint32_t*>(host + pl->meta_off);
+  const volatile uint32_t* norig = reinterpret_cast<const volatile uint32_t*>(host + pl->norig_off);
+  for (uint32_t i = 0; i < sh.nseg; i++) {
+    n_orig[i] = norig[i];
+    n_quant[i] = meta[2 * i + 1] ? meta[2 * i] : norig[i];  // no valid eb: not quantized
+  }
+  if (pl->report_host->status != 0) return EC_ERR_DEVICE;
+  return EC_OK;
+}
+
+ec_status ec_classify_tables(uint32_t num_tables, const double* homo_index, double l_thresh,
+                             double s_thresh, double alpha, double beta, int32_t* table_class,
+                             float* table_mult) {
+  if (!homo_index || !table_class || !table_mult || !(l_thresh <= s_thresh)) return EC_ERR_INVALID;
+  if (!(alpha > 0.0) || !std::isfinite(alpha) || !(beta > 0.0) || !std::isfinite(beta))
+    return EC_ERR_INVALID;
+  for (uint32_t t = 0; t < num_tables; t++) {
+    const double h = homo_index[t];
+    if (h > s_thresh) {
+      table_class[t] = EC_CLASS_SMALL;
+      table_mult[t] = (float)(1.0 / beta);
+    } else if (h < l_thresh) {
+      table_class[t] = EC_CLASS_LARGE;
+      table_mult[t] = (float)alpha;
+    } else {
+      table_class[t] = EC_CLASS_MEDIUM;
+      table_mult[t] = 1.0f;
+    }
+  }
+  return EC_OK;
+}
+
 const char* ec_status_string(ec_status s) {
   switch (s) {
     case EC_OK: return "ok";
@@ -595,6 +663,8 @@ ec_status enqueue_compress(ec_plan_s* pl, const ec::Work& work, bool clear, int6
   uint32_t hb = pl->desc.debug_hash_bits;
   ea.hash_keep = (hb == 0 || hb >= 64) ? ~0ull : ((1ull << hb) - 1ull);
   ea.report = pl->report_dev;
+  ea.seg_meta = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(pl->report_dev) + pl->meta_off);
+  ea.seg_norig = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(pl->report_dev) + pl->norig_off);
   ea.dbg_codes = pl->dbg_codes;
   ea.dbg_outlier = pl->dbg_outlier;
   ea.dbg_first = pl->dbg_first;

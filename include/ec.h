@@ -73,7 +73,9 @@ typedef enum {
   EC_SCHED_INV_SQRT = 1, /* (1 + i/t0)^(-1/2)                                */
   EC_SCHED_STEP = 2      /* k - (k-1) * floor(steps*min(i,phase)/phase)/steps:
                             staircase from k down to 1 (the pages' default
-                            step-wise decay, section III-C)                 */
+                            step-wise decay, section III-C; Fig. 10's
+                            Decay_2x is k = 2, and its Drop_2x, k held for
+                            the whole initial phase then 1, is steps = 1)  */
 } ec_sched_kind;
 
 typedef enum { EC_CODER_BITPACK = 1 } ec_coder;
@@ -178,6 +180,31 @@ ec_status ec_decompress(ec_plan_t plan, const void* d_stream, size_t stream_cap,
  * and clears the sticky device status. */
 ec_status ec_ratio(ec_plan_t plan, double* total_cr, uint64_t* compressed_bytes,
                    double* per_segment_cr);
+
+/* Offline analysis of section III-C (Algorithm 1, "OfflineAnalysis"), run on
+ * a sampled batch: compresses d_in exactly as ec_compress does (the stream
+ * lands in d_out), then counts for every segment s = p*T + t the numbers that
+ * eq. (1) takes: n_orig[s] = distinct rows of the segment as fp32 bit patterns
+ * (Tables III/IV "# Ori. Patterns") and n_quant[s] = distinct quantized rows
+ * (the repeated-row key, "# Quant. Patterns"; n_orig[s] when the segment's eb
+ * is invalid and nothing is quantized).  The Homogenization Index is then
+ * (n_orig - n_quant) / n_orig.  Host arrays of P*T entries; the call waits for
+ * the device.  Errors: those of ec_compress, EC_ERR_INVALID for NULL arrays,
+ * EC_ERR_DEVICE for a device-side failure. */
+ec_status ec_homo_counts(ec_plan_t plan, int64_t iter, const float* d_in, void* d_out,
+                         size_t out_cap, uint32_t* n_orig, uint32_t* n_quant, void* stream);
+
+typedef enum { EC_CLASS_LARGE = 0, EC_CLASS_MEDIUM = 1, EC_CLASS_SMALL = 2 } ec_table_class;
+
+/* Algorithm 1, EMBClassification: table t is small-eb (EC_CLASS_SMALL,
+ * multiplier 1/beta) when homo_index[t] > s_thresh, large-eb (EC_CLASS_LARGE,
+ * multiplier alpha) when homo_index[t] < l_thresh, else medium (multiplier 1);
+ * the multipliers (rounded once to fp32) go into ec_plan_desc.table_mult, so
+ * LargeEB = eb * alpha and SmallEB = eb / beta.  Host only.  EC_ERR_INVALID
+ * for NULL arrays, l_thresh > s_thresh, or alpha, beta not finite and > 0. */
+ec_status ec_classify_tables(uint32_t num_tables, const double* homo_index, double l_thresh,
+                             double s_thresh, double alpha, double beta, int32_t* table_class,
+                             float* table_mult);
 
 /* Bytes of the library's static device scratch (one copy per device). */
 #define EC_STATIC_SCRATCH_BYTES (64ull << 20)

@@ -119,3 +119,26 @@ def test_huffman_entry_points_check_arguments_on_the_host():
     ds = L.ec_huff_decode_segments
     assert ds(fake, fake, fake, 10, 0, 10, fake, fake, w26, None) == ec.EC_ERR_INVALID
     assert ds(fake, fake, fake, 10, 26, 10, fake, fake, wb, None) == ec.EC_ERR_CAPACITY
+
+
+def test_table_classification_matches_the_oracle():
+    """ec_classify_tables (host code in the library) against the oracle's
+    Algorithm 1 on random homogenization indices, thresholds and multipliers,
+    threshold ties included; invalid arguments are rejected."""
+    import numpy as np
+    import oracle as O
+    rng = np.random.default_rng(7)
+    for _ in range(50):
+        T = int(rng.integers(1, 40))
+        lo, hi = sorted(rng.uniform(0, 1, 2))
+        h = rng.uniform(0, 1, T)
+        h[: T // 4] = lo
+        h[T // 4: T // 2] = hi
+        alpha, beta = float(rng.uniform(1, 4)), float(rng.uniform(1, 4))
+        cls, mult = ec.classify_tables(h, lo, hi, alpha, beta)
+        ocls, omult = O.classify(h, lo, hi, alpha, beta)
+        assert cls == [int(c) for c in ocls]
+        assert np.array_equal(np.array(mult, np.float32), omult)
+    for bad in [(0.5, 0.4, 2.0, 2.0), (0.1, 0.3, 0.0, 2.0), (0.1, 0.3, 2.0, float("inf"))]:
+        with pytest.raises(ec.ECError):
+            ec.classify_tables([0.2], *bad)
