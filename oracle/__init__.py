@@ -23,6 +23,7 @@ SOURCES = [os.path.join(HERE, "ebl_oracle.c"), os.path.join(HERE, "ebl_huffman.c
 EB_ABS, EB_REL = 0, 1
 SCHED_NONE, SCHED_INV_SQRT, SCHED_STEP = 0, 1, 2
 OK, ERR_INVALID, ERR_CAPACITY, ERR_CORRUPT, ERR_OOM = 0, 1, 2, 3, 5
+CODER_BITPACK, CODER_HUFFMAN, CODER_AUTO = 1, 2, 3
 
 
 def build(force: bool = True) -> str:
@@ -43,7 +44,7 @@ class _Cfg(ctypes.Structure):
         ("table_mult", ctypes.POINTER(ctypes.c_float)),
         ("sched_kind", ctypes.c_int32), ("sched_steps", ctypes.c_int32),
         ("sched_t0", ctypes.c_double), ("sched_k", ctypes.c_double),
-        ("sched_phase", ctypes.c_int64),
+        ("sched_phase", ctypes.c_int64), ("coder", ctypes.c_uint32),
     ]
 
 
@@ -132,6 +133,7 @@ class Config:
     sched_k: float = 2.0
     sched_phase: int = 1
     sched_steps: int = 1
+    coder: int = CODER_BITPACK
 
     def _c(self):
         eb = np.ascontiguousarray(np.asarray(self.eb, dtype=np.float32).reshape(-1))
@@ -143,7 +145,7 @@ class Config:
         c = _Cfg(self.T, self.B, self.D, self.P, self.eb_mode, _f32ptr(eb),
                  _f32ptr(mult) if mult is not None else ctypes.POINTER(ctypes.c_float)(),
                  self.sched_kind, self.sched_steps, self.sched_t0, self.sched_k,
-                 self.sched_phase)
+                 self.sched_phase, self.coder)
         return c, (eb, mult)  # keep arrays alive with the struct
 
 

@@ -191,6 +191,7 @@ static int cfg_ok(const ebo_cfg* c) {
   if (!c || !c->eb) return 0;
   if (c->T < 1 || c->D < 1 || c->P < 1) return 0;
   if (c->eb_mode != EBO_EB_ABS && c->eb_mode != EBO_EB_REL) return 0;
+  if (c->coder > EBO_CODER_AUTO) return 0;
   if (c->sched_kind == EBO_SCHED_INV_SQRT && !(c->sched_t0 > 0.0)) return 0;
   if (c->sched_kind == EBO_SCHED_STEP && (c->sched_phase < 1 || c->sched_steps < 1))
     return 0;
@@ -198,7 +199,7 @@ static int cfg_ok(const ebo_cfg* c) {
     uint32_t rows = chunk_rows(c, p);
     uint32_t nt = (rows + 63) / 64;
     uint64_t worst = seg_prefix_bytes(nt) + (uint64_t)nt * 16 + (uint64_t)4 * rows * c->D +
-                     (uint64_t)nt * 16;
+                     (uint64_t)nt * 16 + EBO_BOOK_PAD;
     if (worst >= ((uint64_t)1 << 31)) return 0;
   }
   return 1;
@@ -207,10 +208,12 @@ static int cfg_ok(const ebo_cfg* c) {
 size_t ebo_max_compressed_bytes(const ebo_cfg* c) {
   if (!cfg_ok(c)) return 0;
   uint64_t total = 64 + align_up((uint64_t)8 * c->P, 16);
+  int huff = c->coder == EBO_CODER_HUFFMAN || c->coder == EBO_CODER_AUTO;
   for (uint32_t p = 0; p < c->P; p++) {
     uint32_t rows = chunk_rows(c, p);
     uint32_t nt = (rows + 63) / 64;
-    uint64_t seg = seg_prefix_bytes(nt);
+    /* a Huffman segment may carry a codebook on top of all-RAW records */
+    uint64_t seg = seg_prefix_bytes(nt) + (huff ? EBO_BOOK_PAD : 0);
     for (uint32_t k = 0; k < nt; k++) {
       uint32_t n = rows - 64 * k < 64 ? rows - 64 * k : 64;
       seg += raw_record_bytes(n, c->D);
@@ -372,8 +375,76 @@ typedef struct {
   const uint32_t* first;    /* first occurrence per segment row */
 } seg_view;
 
-/* Append tile k's record to b; returns the n_out of the record (0 if RAW). */
-static uint32_t encode_tile(const seg_view* sv, uint32_t k, buf_t* b, uint32_t* u_tile) {
+/* Huffman-coded record of tile k (mode 2), when the segment's coder is the
+   entropy coder of section III-D with code lengths hlen / codes hcode:
+     header 16 | refs | outlier positions and raw bits (as in mode 1) |
+     chunk table (nch + 1) x u32 word offsets | words, u32 | zero pad to 16
+   with E's symbols q + 2047 (outliers as q = 0) in 256-symbol chunks.
+   Returns the record bytes (0 on allocation failure); writes the record at
+   out when out != NULL. */
+static uint64_t huff_record(const seg_view* sv, uint32_t k, uint64_t bitmap, uint32_t U,
+                            const uint8_t* hlen, const uint32_t* hcode, uint8_t* out,
+                            uint32_t* nout_ret) {
+  uint32_t D = sv->D, r0 = 64 * k;
+  uint32_t n = sv->rows - r0 < 64 ? sv->rows - r0 : 64;
+  uint32_t nE = U * D, nch = (nE + EBO_HUFF_CHUNK - 1) / EBO_HUFF_CHUNK;
+  uint16_t* sym = (uint16_t*)malloc(sizeof(uint16_t) * ((size_t)nE + 1));
+  uint32_t* opos = (uint32_t*)malloc(sizeof(uint32_t) * ((size_t)nE + 1));
+  uint32_t* oval = (uint32_t*)malloc(sizeof(uint32_t) * ((size_t)nE + 1));
+  uint32_t* words = (uint32_t*)calloc((size_t)EBO_HUFF_MAXLEN * nE / 32 + nch + 2, 4);
+  uint32_t* coff = (uint32_t*)calloc((size_t)nch + 1, 4);
+  uint64_t size = 0;
+  if (sym && opos && oval && words && coff) {
+    uint32_t nout = 0, e = 0;
+    for (uint32_t i = 0; i < n; i++) {
+      if (!((bitmap >> i) & 1u)) continue;
+      size_t row = (size_t)(r0 + i) * D;
+      for (uint32_t d = 0; d < D; d++, e++) {
+        sym[e] = (uint16_t)(sv->q[row + d] + EBO_QMAX);
+        if (sv->out[row + d]) {
+          opos[nout] = e;
+          oval[nout] = f32_bits(sv->x[row + d]);
+          nout++;
+        }
+      }
+    }
+    size_t nw = ebo_huff_encode(sym, nE, hlen, hcode, words, coff);
+    uint32_t rb = sv->rows <= 65536 ? 2 : 4;
+    uint64_t off_opos = align_up(16 + (uint64_t)rb * (n - U), 4);
+    uint64_t off_oval = off_opos + 4ull * nout;
+    uint64_t off_ct = off_oval + 4ull * nout;
+    uint64_t off_w = off_ct + 4ull * (nch + 1);
+    size = align_up(off_w + 4ull * nw, 16);
+    *nout_ret = nout;
+    if (out) {
+      put_u64(out + 0, bitmap);
+      put_u32(out + 8, nout);
+      put_u16(out + 12, (uint16_t)U);
+      put_u8(out + 14, 2);
+      uint32_t j = 0;
+      for (uint32_t i = 0; i < n; i++) {
+        if ((bitmap >> i) & 1u) continue;
+        uint32_t ref = sv->first[r0 + i];
+        if (rb == 2) put_u16(out + 16 + 2 * j, (uint16_t)ref);
+        else put_u32(out + 16 + 4 * j, ref);
+        j++;
+      }
+      for (uint32_t o = 0; o < nout; o++) {
+        put_u32(out + off_opos + 4 * o, opos[o]);
+        put_u32(out + off_oval + 4 * o, oval[o]);
+      }
+      for (uint32_t c = 0; c <= nch; c++) put_u32(out + off_ct + 4 * c, coff[c]);
+      for (size_t w = 0; w < nw; w++) put_u32(out + off_w + 4 * w, words[w]);
+    }
+  }
+  free(sym); free(opos); free(oval); free(words); free(coff);
+  return size;
+}
+
+/* Append tile k's record to b; returns the n_out of the record (0 if RAW).
+   hlen != NULL: the segment is Huffman-coded (records of mode 2 or 0). */
+static uint32_t encode_tile(const seg_view* sv, uint32_t k, buf_t* b, uint32_t* u_tile,
+                            const uint8_t* hlen, const uint32_t* hcode) {
   uint32_t D = sv->D;
   uint32_t r0 = 64 * k;
   uint32_t n = sv->rows - r0 < 64 ? sv->rows - r0 : 64;
@@ -389,7 +460,20 @@ static uint32_t encode_tile(const seg_view* sv, uint32_t k, buf_t* b, uint32_t* 
   *u_tile = U;
   uint64_t raw_bytes = raw_record_bytes(n, D);
 
-  if (sv->valid) {
+  if (sv->valid && hlen) {
+    /* a Huffman record when it is strictly smaller than the RAW record */
+    uint32_t nout = 0;
+    uint64_t size = huff_record(sv, k, bitmap, U, hlen, hcode, NULL, &nout);
+    if (size == 0) {
+      b->err = 1;
+      return 0;
+    }
+    if (size < raw_bytes) {
+      uint8_t* r = buf_grow(b, (size_t)size);
+      if (r) huff_record(sv, k, bitmap, U, hlen, hcode, r, &nout);
+      return nout;
+    }
+  } else if (sv->valid) {
     /* E: the first-occurrence rows' codes, row order, flattened */
     uint32_t nE = U * D;
     uint32_t nblk = (nE + 63) / 64;
@@ -483,6 +567,52 @@ static uint32_t encode_tile(const seg_view* sv, uint32_t k, buf_t* b, uint32_t* 
   return 0;
 }
 
+/* Code lengths of a segment's Huffman code: the histogram of E, the codes
+   of every first-occurrence row (outliers as q = 0), as symbols q + 2047. */
+static void segment_lengths(const seg_view* sv, uint8_t* hlen) {
+  uint64_t freq[EBO_HUFF_NSYM];
+  memset(freq, 0, sizeof(freq));
+  for (uint32_t r = 0; r < sv->rows; r++) {
+    if (sv->first[r] != r) continue;
+    for (uint32_t d = 0; d < sv->D; d++) freq[sv->q[(size_t)r * sv->D + d] + EBO_QMAX]++;
+  }
+  ebo_huff_lengths(freq, hlen);
+}
+
+/* One whole segment into b (empty on entry): header, tile directory, the
+   codebook when hlen != NULL (flags bit 1), tile records.  0, or -1. */
+static int encode_segment(const seg_view* sv, uint32_t nt, float eb, const uint8_t* hlen,
+                          buf_t* b) {
+  uint32_t hcode[EBO_HUFF_NSYM];
+  buf_grow(b, 32);
+  buf_grow(b, (size_t)align_up(4ull * nt, 16));
+  if (hlen) {
+    ebo_huff_codes(hlen, hcode);
+    uint8_t book[4 + (EBO_HUFF_NSYM + 1) / 2];
+    size_t nb = ebo_huff_book_write(hlen, book);
+    uint8_t* at = buf_grow(b, (size_t)align_up(nb, 16));
+    if (at) memcpy(at, book, nb);
+  }
+  uint32_t Useg = 0, nout_seg = 0;
+  for (uint32_t k = 0; k < nt; k++) {
+    size_t rec = b->n;
+    if (!b->err) put_u32(b->p + 32 + 4 * k, (uint32_t)rec);
+    uint32_t ut = 0;
+    nout_seg += encode_tile(sv, k, b, &ut, hlen, hlen ? hcode : NULL);
+    Useg += ut;
+  }
+  if (b->err) return -1;
+  uint8_t* sh = b->p;
+  put_u32(sh + 0, sv->rows);
+  put_u32(sh + 4, nt);
+  put_f32(sh + 8, sv->valid ? eb : 0.0f);
+  put_u32(sh + 12, (sv->valid ? 1u : 0u) | (hlen ? 2u : 0u));
+  put_u32(sh + 16, Useg);
+  put_u32(sh + 20, nout_seg);
+  put_u64(sh + 24, (uint64_t)b->n);
+  return 0;
+}
+
 /* ------------------------------------------------------------------ */
 /* compressor                                                          */
 /* ------------------------------------------------------------------ */
@@ -500,6 +630,7 @@ int ebo_compress(const ebo_cfg* c, int64_t iter, const float* x, uint8_t* out, s
   }
   size_t need = ebo_max_compressed_bytes(c);
   if (!out || cap < need) return EBO_ERR_CAPACITY;
+  uint32_t coder = c->coder ? c->coder : EBO_CODER_BITPACK;
 
   float* eb_t = (float*)malloc(sizeof(float) * T);
   if (!eb_t) return EBO_ERR_OOM;
@@ -510,7 +641,7 @@ int ebo_compress(const ebo_cfg* c, int64_t iter, const float* x, uint8_t* out, s
   if (h) {
     put_u32(h + 0, EBO_MAGIC);
     put_u16(h + 4, EBO_VERSION);
-    put_u16(h + 6, EBO_CODER_BITPACK);
+    put_u16(h + 6, (uint16_t)coder);
     put_u32(h + 8, T);
     put_u32(h + 12, B);
     put_u32(h + 16, D);
@@ -563,27 +694,25 @@ int ebo_compress(const ebo_cfg* c, int64_t iter, const float* x, uint8_t* out, s
         }
         if (eb_seg) eb_seg[(size_t)p * T + t] = valid ? eb : 0.0f;
 
-        buf_grow(&s, 32);
-        buf_grow(&s, (size_t)align_up(4ull * nt, 16));
         seg_view sv = {D, rows, valid, xs, q, o, first};
-        uint32_t Useg = 0, nout_seg = 0;
-        for (uint32_t k = 0; k < nt; k++) {
-          size_t rec = s.n;
-          if (!s.err) put_u32(s.p + seg0 + 32 + 4 * k, (uint32_t)(rec - seg0));
-          uint32_t ut = 0;
-          nout_seg += encode_tile(&sv, k, &s, &ut);
-          Useg += ut;
+        /* the bit-plane segment, and with the Huffman coder also the Huffman
+           segment; coder 3 keeps the Huffman one when it is strictly smaller */
+        buf_t bp = {0}, hf = {0};
+        if (encode_segment(&sv, nt, eb, NULL, &bp) != 0) rc = EBO_ERR_OOM;
+        int use_huff = 0;
+        if (rc == EBO_OK && valid && coder != EBO_CODER_BITPACK) {
+          uint8_t hlen[EBO_HUFF_NSYM];
+          segment_lengths(&sv, hlen);
+          if (encode_segment(&sv, nt, eb, hlen, &hf) != 0) rc = EBO_ERR_OOM;
+          use_huff = coder == EBO_CODER_HUFFMAN || hf.n < bp.n;
         }
-        if (!s.err) {
-          uint8_t* sh = s.p + seg0;
-          put_u32(sh + 0, rows);
-          put_u32(sh + 4, nt);
-          put_f32(sh + 8, valid ? eb : 0.0f);
-          put_u32(sh + 12, valid ? 1u : 0u);
-          put_u32(sh + 16, Useg);
-          put_u32(sh + 20, nout_seg);
-          put_u64(sh + 24, (uint64_t)(s.n - seg0));
+        if (rc == EBO_OK) {
+          const buf_t* pick = use_huff ? &hf : &bp;
+          uint8_t* at = buf_grow(&s, pick->n);
+          if (at) memcpy(at, pick->p, pick->n);
         }
+        free(bp.p);
+        free(hf.p);
       }
       free(q); free(o); free(keys); free(first);
     }
@@ -612,13 +741,37 @@ typedef struct {
   uint32_t rows, ntiles, D;
   float eb;
   int valid;
+  int huff;                       /* Huffman segment (flags bit 1) */
+  uint8_t hlen[EBO_HUFF_NSYM];    /* its code lengths */
+  uint64_t rec_lo;                /* records start at or after this offset */
+  uint16_t** sym;                 /* [ntiles]: decoded E symbols of mode-2 records */
 } seg_in;
+
+/* byte offsets inside a record of n rows with U first occurrences */
+typedef struct {
+  uint64_t refs, opos, oval, ct, words, pl;
+  uint32_t nblk, nch;
+} rec_lay;
+static rec_lay record_layout(uint32_t mode, uint32_t n, uint32_t U, uint32_t nout, uint32_t D,
+                             uint32_t rows) {
+  rec_lay L;
+  uint64_t nE = (uint64_t)U * D;
+  uint32_t rb = rows <= 65536 ? 2 : 4;
+  L.nblk = (uint32_t)((nE + 63) / 64);
+  L.nch = (uint32_t)((nE + EBO_HUFF_CHUNK - 1) / EBO_HUFF_CHUNK);
+  L.refs = mode == 2 ? 16 : align_up(16 + L.nblk, 4);
+  L.opos = align_up(L.refs + (uint64_t)rb * (n - U), 4);
+  L.oval = L.opos + 4ull * nout;
+  L.ct = L.oval + 4ull * nout;          /* mode 2 */
+  L.words = L.ct + 4ull * (L.nch + 1);  /* mode 2 */
+  L.pl = align_up(L.oval + 4ull * nout, 8);  /* mode 1 */
+  return L;
+}
 
 /* locate tile record k of segment g; 0 on success */
 static int rec_locate(const seg_in* g, uint32_t k, const uint8_t** rec, uint64_t* avail) {
   uint32_t off = get_u32(g->s + 32 + 4 * (uint64_t)k);
-  uint64_t lo = seg_prefix_bytes(g->ntiles);
-  if (off < lo || (off & 15u) || (uint64_t)off + 16 > g->bytes) return -1;
+  if (off < g->rec_lo || (off & 15u) || (uint64_t)off + 16 > g->bytes) return -1;
   *rec = g->s + off;
   *avail = g->bytes - off;
   return 0;
@@ -647,36 +800,60 @@ static int decode_key_row(const seg_in* g, uint32_t r, float* y) {
     }
     return 0;
   }
-  if (mode != 1) return -1;
+  if (mode != 1 && mode != 2) return -1;
   uint32_t u = popcount64(bitmap & (((uint64_t)1 << i) - 1));
-  uint32_t nblk = (U * D + 63) / 64;
-  uint32_t rb = g->rows <= 65536 ? 2 : 4;
-  uint64_t off_refs = align_up(16 + nblk, 4);
-  uint64_t off_opos = align_up(off_refs + (uint64_t)rb * (n - U), 4);
-  uint64_t off_oval = off_opos + 4ull * nout;
-  uint64_t off_pl = align_up(off_oval + 4ull * nout, 8);
-  if (off_pl > avail) return -1;
-  for (uint32_t d = 0; d < D; d++) {
-    uint64_t e = (uint64_t)u * D + d;
-    uint64_t blk = e / 64, bit = e % 64;
-    uint64_t at = off_pl;
-    for (uint64_t j = 0; j < blk; j++) at += 8ull * rec[16 + j];
-    uint32_t w = rec[16 + blk];
-    if (w > 12 || at + 8ull * w > avail) return -1;
-    uint32_t zz = 0;
-    for (uint32_t j = 0; j < w; j++)
-      zz |= (uint32_t)((get_u64(rec + at + 8 * j) >> bit) & 1u) << j;
-    y[d] = ebo_dequantize(ebo_unzigzag(zz), g->eb);
+  rec_lay L = record_layout(mode, n, U, nout, D, g->rows);
+  if (mode == 2) {
+    /* symbols decoded when the record was checked */
+    if (!g->sym[k]) return -1;
+    for (uint32_t d = 0; d < D; d++)
+      y[d] = ebo_dequantize((int32_t)g->sym[k][(uint64_t)u * D + d] - EBO_QMAX, g->eb);
+  } else {
+    if (L.pl > avail) return -1;
+    for (uint32_t d = 0; d < D; d++) {
+      uint64_t e = (uint64_t)u * D + d;
+      uint64_t blk = e / 64, bit = e % 64;
+      uint64_t at = L.pl;
+      for (uint64_t j = 0; j < blk; j++) at += 8ull * rec[16 + j];
+      uint32_t w = rec[16 + blk];
+      if (w > 12 || at + 8ull * w > avail) return -1;
+      uint32_t zz = 0;
+      for (uint32_t j = 0; j < w; j++)
+        zz |= (uint32_t)((get_u64(rec + at + 8 * j) >> bit) & 1u) << j;
+      y[d] = ebo_dequantize(ebo_unzigzag(zz), g->eb);
+    }
   }
   for (uint32_t o = 0; o < nout; o++) {
-    uint32_t pos = get_u32(rec + off_opos + 4 * o);
+    uint32_t pos = get_u32(rec + L.opos + 4 * o);
     if (pos >= (uint64_t)u * D && pos < (uint64_t)u * D + D)
-      y[pos - (uint64_t)u * D] = bits_f32(get_u32(rec + off_oval + 4 * o));
+      y[pos - (uint64_t)u * D] = bits_f32(get_u32(rec + L.oval + 4 * o));
   }
   return 0;
 }
 
-static int check_record(const seg_in* g, uint32_t k) {
+/* decode the chunks of a mode-2 record into g->sym[k]; 0 on success */
+static int huff_record_decode(seg_in* g, uint32_t k, const uint8_t* rec, uint64_t avail,
+                              const rec_lay* L, uint64_t nE) {
+  if (L->words > avail) return -1;
+  uint32_t* ct = (uint32_t*)malloc(4ull * (L->nch + 1));
+  if (!ct) return -1;
+  for (uint32_t c = 0; c <= L->nch; c++) ct[c] = get_u32(rec + L->ct + 4ull * c);
+  uint64_t nw = ct[L->nch];
+  int rc = -1;
+  if (L->words + 4 * nw <= avail) {
+    uint32_t* w = (uint32_t*)malloc(4 * (nw + 1));
+    g->sym[k] = (uint16_t*)malloc(2 * (nE + 1));
+    if (w && g->sym[k]) {
+      for (uint64_t j = 0; j < nw; j++) w[j] = get_u32(rec + L->words + 4 * j);
+      rc = ebo_huff_decode(w, (size_t)nw, ct, (size_t)nE, g->hlen, g->sym[k]) == 0 ? 0 : -1;
+    }
+    free(w);
+  }
+  free(ct);
+  return rc;
+}
+
+static int check_record(seg_in* g, uint32_t k) {
   uint32_t D = g->D;
   const uint8_t* rec;
   uint64_t avail;
@@ -694,38 +871,39 @@ static int check_record(const seg_in* g, uint32_t k) {
     if (nout != 0 || 16 + 4ull * n * D > avail) return -1;
     return 0;
   }
-  if (mode != 1) return -1;
+  /* bit planes in bit-plane segments, Huffman chunks in Huffman segments */
+  if (mode != (g->huff ? 2u : 1u)) return -1;
   uint64_t nE = (uint64_t)U * D;
   if (nout > nE) return -1;
-  uint32_t nblk = (uint32_t)((nE + 63) / 64);
+  rec_lay L = record_layout(mode, n, U, nout, D, g->rows);
   uint32_t rb = g->rows <= 65536 ? 2 : 4;
-  uint64_t off_refs = align_up(16 + nblk, 4);
-  uint64_t off_opos = align_up(off_refs + (uint64_t)rb * (n - U), 4);
-  uint64_t off_oval = off_opos + 4ull * nout;
-  uint64_t off_pl = align_up(off_oval + 4ull * nout, 8);
-  if (off_pl > avail) return -1;
-  uint64_t sumw = 0;
-  for (uint32_t j = 0; j < nblk; j++) {
-    if (rec[16 + j] > 12) return -1;
-    sumw += rec[16 + j];
+  if (mode == 1) {
+    if (L.pl > avail) return -1;
+    uint64_t sumw = 0;
+    for (uint32_t j = 0; j < L.nblk; j++) {
+      if (rec[16 + j] > 12) return -1;
+      sumw += rec[16 + j];
+    }
+    if (L.pl + 8 * sumw > avail) return -1;
+  } else if (huff_record_decode(g, k, rec, avail, &L, nE)) {
+    return -1;
   }
-  if (off_pl + 8 * sumw > avail) return -1;
   uint32_t j = 0;
   for (uint32_t i = 0; i < n; i++) {
     if ((bitmap >> i) & 1u) continue;
-    uint32_t ref = rb == 2 ? get_u16(rec + off_refs + 2 * j) : get_u32(rec + off_refs + 4 * j);
+    uint32_t ref = rb == 2 ? get_u16(rec + L.refs + 2 * j) : get_u32(rec + L.refs + 4 * j);
     if (ref >= 64 * k + i) return -1; /* must point to an earlier row */
     j++;
   }
   for (uint32_t o = 0; o < nout; o++) {
-    uint32_t pos = get_u32(rec + off_opos + 4 * o);
+    uint32_t pos = get_u32(rec + L.opos + 4 * o);
     if (pos >= nE) return -1;
-    if (o > 0 && pos <= get_u32(rec + off_opos + 4 * (o - 1))) return -1;
+    if (o > 0 && pos <= get_u32(rec + L.opos + 4 * (o - 1))) return -1;
   }
   return 0;
 }
 
-static int decode_segment(const seg_in* g, uint32_t U_seg, uint32_t nout_seg, float* y) {
+static int decode_segment(seg_in* g, uint32_t U_seg, uint32_t nout_seg, float* y) {
   uint32_t D = g->D;
   uint64_t u_sum = 0, o_sum = 0;
   for (uint32_t k = 0; k < g->ntiles; k++) {
@@ -734,7 +912,7 @@ static int decode_segment(const seg_in* g, uint32_t U_seg, uint32_t nout_seg, fl
     uint64_t avail;
     rec_locate(g, k, &rec, &avail);
     u_sum += get_u16(rec + 12);
-    if (rec[14] == 1) o_sum += get_u32(rec + 8);
+    if (rec[14] != 0) o_sum += get_u32(rec + 8);
   }
   if (u_sum != U_seg || o_sum != nout_seg) return -1;
   for (uint32_t k = 0; k < g->ntiles; k++) {
@@ -745,9 +923,8 @@ static int decode_segment(const seg_in* g, uint32_t U_seg, uint32_t nout_seg, fl
     uint64_t bitmap = get_u64(rec);
     uint32_t U = get_u16(rec + 12);
     uint32_t mode = rec[14];
-    uint32_t nblk = (U * D + 63) / 64;
+    rec_lay L = record_layout(mode, n, U, get_u32(rec + 8), D, g->rows);
     uint32_t rb = g->rows <= 65536 ? 2 : 4;
-    uint64_t off_refs = align_up(16 + nblk, 4);
     uint32_t j = 0;
     for (uint32_t i = 0; i < n; i++) {
       float* yr = y + (size_t)(64 * k + i) * D;
@@ -756,7 +933,7 @@ static int decode_segment(const seg_in* g, uint32_t U_seg, uint32_t nout_seg, fl
       } else if ((bitmap >> i) & 1u) {
         if (decode_key_row(g, 64 * k + i, yr)) return -1;
       } else {
-        uint32_t ref = rb == 2 ? get_u16(rec + off_refs + 2 * j) : get_u32(rec + off_refs + 4 * j);
+        uint32_t ref = rb == 2 ? get_u16(rec + L.refs + 2 * j) : get_u32(rec + L.refs + 4 * j);
         j++;
         if (decode_key_row(g, ref, yr)) return -1;
       }
@@ -769,8 +946,9 @@ int ebo_decompress(const uint8_t* s, size_t nbytes, uint32_t T, uint32_t B, uint
                    uint32_t P, float* y) {
   if (!s || T < 1 || D < 1 || P < 1) return EBO_ERR_INVALID;
   if (nbytes < 64) return EBO_ERR_CORRUPT;
-  if (get_u32(s) != EBO_MAGIC || get_u16(s + 4) != EBO_VERSION ||
-      get_u16(s + 6) != EBO_CODER_BITPACK)
+  uint32_t coder = get_u16(s + 6);
+  if (get_u32(s) != EBO_MAGIC || get_u16(s + 4) != EBO_VERSION || coder < EBO_CODER_BITPACK ||
+      coder > EBO_CODER_AUTO)
     return EBO_ERR_CORRUPT;
   if (get_u32(s + 8) != T || get_u32(s + 12) != B || get_u32(s + 16) != D ||
       get_u32(s + 20) != P || get_u32(s + 24) != EBO_TILE_ROWS || get_u32(s + 28) > 1)
@@ -783,34 +961,73 @@ int ebo_decompress(const uint8_t* s, size_t nbytes, uint32_t T, uint32_t B, uint
   uint64_t base = 64 + align_up(8ull * P, 16);
   if (base > total) return EBO_ERR_CORRUPT;
   uint64_t at = base;
-  for (uint32_t p = 0; p < P; p++) {
+  int rc = EBO_OK;
+  seg_in* g = (seg_in*)malloc(sizeof(seg_in));
+  if (!g) return EBO_ERR_OOM;
+  for (uint32_t p = 0; p < P && rc == EBO_OK; p++) {
     uint64_t cb = get_u64(s + 64 + 8 * p);
     uint64_t tab = align_up(8ull * T, 16);
-    if (cb < tab || cb > total - at) return EBO_ERR_CORRUPT;
+    if (cb < tab || cb > total - at) {
+      rc = EBO_ERR_CORRUPT;
+      break;
+    }
     const uint8_t* ch = s + at;
     uint32_t row0 = chunk_row0(&shape, p), rows = chunk_rows(&shape, p);
     uint32_t nt = (rows + 63) / 64;
-    for (uint32_t t = 0; t < T; t++) {
+    for (uint32_t t = 0; t < T && rc == EBO_OK; t++) {
       uint64_t so = get_u64(ch + 8 * t);
-      if (so < tab || (so & 15u) || so + 32 > cb) return EBO_ERR_CORRUPT;
-      seg_in g;
-      g.s = ch + so;
-      g.rows = get_u32(g.s + 0);
-      g.ntiles = get_u32(g.s + 4);
-      g.eb = get_f32(g.s + 8);
-      uint32_t flags = get_u32(g.s + 12);
-      g.bytes = get_u64(g.s + 24);
-      g.D = D;
-      if (g.rows != rows || g.ntiles != nt || flags > 1) return EBO_ERR_CORRUPT;
-      if (g.bytes > cb - so || g.bytes < seg_prefix_bytes(nt)) return EBO_ERR_CORRUPT;
-      g.valid = (int)flags;
-      if (g.valid != ebo_eb_valid(g.eb)) return EBO_ERR_CORRUPT;
-      if (decode_segment(&g, get_u32(g.s + 16), get_u32(g.s + 20),
+      if (so < tab || (so & 15u) || so + 32 > cb) {
+        rc = EBO_ERR_CORRUPT;
+        break;
+      }
+      g->s = ch + so;
+      g->rows = get_u32(g->s + 0);
+      g->ntiles = get_u32(g->s + 4);
+      g->eb = get_f32(g->s + 8);
+      uint32_t flags = get_u32(g->s + 12);
+      g->bytes = get_u64(g->s + 24);
+      g->D = D;
+      g->sym = NULL;
+      if (g->rows != rows || g->ntiles != nt || flags > 3 || flags == 2 ||
+          g->bytes > cb - so || g->bytes < seg_prefix_bytes(nt)) {
+        rc = EBO_ERR_CORRUPT;
+        break;
+      }
+      g->valid = (int)(flags & 1u);
+      g->huff = (int)((flags >> 1) & 1u);
+      if (g->valid != ebo_eb_valid(g->eb) || (g->huff && coder == EBO_CODER_BITPACK) ||
+          (g->valid && !g->huff && coder == EBO_CODER_HUFFMAN)) {
+        rc = EBO_ERR_CORRUPT;
+        break;
+      }
+      g->rec_lo = seg_prefix_bytes(nt);
+      if (g->huff) {
+        /* the codebook follows the tile directory */
+        uint64_t room = g->bytes - g->rec_lo;
+        if (ebo_huff_book_read(g->s + g->rec_lo, (size_t)room, g->hlen) != 0) {
+          rc = EBO_ERR_CORRUPT;
+          break;
+        }
+        g->rec_lo += align_up(ebo_huff_book_bytes(g->hlen), 16);
+        if (g->rec_lo > g->bytes) {
+          rc = EBO_ERR_CORRUPT;
+          break;
+        }
+      }
+      g->sym = (uint16_t**)calloc((size_t)nt + 1, sizeof(uint16_t*));
+      if (!g->sym) {
+        rc = EBO_ERR_OOM;
+        break;
+      }
+      if (decode_segment(g, get_u32(g->s + 16), get_u32(g->s + 20),
                          y + ((size_t)t * B + row0) * D))
-        return EBO_ERR_CORRUPT;
+        rc = EBO_ERR_CORRUPT;
+      for (uint32_t k = 0; k < nt; k++) free(g->sym[k]);
+      free(g->sym);
     }
     at += cb;
   }
-  if (at != total) return EBO_ERR_CORRUPT;
-  return EBO_OK;
+  free(g);
+  if (rc == EBO_OK && at != total) rc = EBO_ERR_CORRUPT;
+  return rc;
 }

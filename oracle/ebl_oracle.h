@@ -25,7 +25,9 @@
  * STREAM
  *   header, 64 bytes:
  *     0  u32 magic 0x434C4245 (bytes "EBLC")   4  u16 version = 1
- *     6  u16 coder = 1 (bit-plane packing)      8  u32 T (tables)
+ *     6  u16 coder: 1 bit-plane packing only, 2 Huffman for every segment
+ *        with a valid eb, 3 per segment the smaller of the two
+ *                                               8  u32 T (tables)
  *     12 u32 B (rows per table)                 16 u32 D (dim)
  *     20 u32 P (destination chunks)             24 u32 tile_rows = 64
  *     28 u32 eb_mode (0 absolute, 1 range-relative)
@@ -41,10 +43,16 @@
  * SEGMENT (p,t)  (16-byte aligned; its size is a multiple of 16)
  *   header, 32 bytes:
  *     0 u32 rows   4 u32 ntiles = ceil(rows/64)   8 f32 eb (0 when invalid)
- *     12 u32 flags (bit 0: eb valid)   16 u32 U (first occurrences)
+ *     12 u32 flags (bit 0: eb valid; bit 1: Huffman segment, only with bit 0)
+ *     16 u32 U (first occurrences)
  *     20 u32 n_out (outliers stored in coded tiles)   24 u64 segment bytes
  *   tile directory: ntiles x u32 offset of each tile record from the segment
- *   start, zero-padded to 16; then the tile records in order.
+ *   start, zero-padded to 16; in a Huffman segment then the codebook
+ *   (ebl_huffman.c's layout, built from the histogram of the symbols q + 2047
+ *   of EVERY first-occurrence row of the segment, outliers as q = 0),
+ *   zero-padded to 16; then the tile records in order.
+ *   With coder 3 a segment is Huffman iff its Huffman form is strictly
+ *   smaller than its bit-plane form; with coder 2 every valid segment is.
  *
  * TILE RECORD (tile k = segment rows [64k, min(64k+64, rows)), n rows)
  *   header, 16 bytes:
@@ -65,8 +73,18 @@
  *     at align8:              bit planes: block b contributes w_b u64 words,
  *                             word j bit i = bit j of zigzag(E[64b+i])
  *     zero pad to 16.
- *   A tile is BITPACK iff its segment's eb is valid and the BITPACK record is
- *   strictly smaller than the RAW record; otherwise RAW.
+ *   mode 2 HUFFMAN (Huffman segments only), same E as mode 1:
+ *     at 16:                  refs as in mode 1
+ *     at align4:              outlier positions and values as in mode 1
+ *     right after:            chunk table, (ceil(U_t*D/256) + 1) x u32: word
+ *                             offset of each 256-symbol chunk of E's symbols
+ *                             q + 2047, then the word count
+ *     right after:            the words (u32), each chunk's canonical codes
+ *                             MSB first from a word boundary, unused bits 0
+ *     zero pad to 16.
+ *   A tile is BITPACK (HUFFMAN in a Huffman segment) iff its segment's eb is
+ *   valid and that record is strictly smaller than the RAW record; otherwise
+ *   RAW.
  */
 #ifndef EBL_ORACLE_H
 #define EBL_ORACLE_H
@@ -81,6 +99,9 @@ extern "C" {
 #define EBO_MAGIC 0x434C4245u
 #define EBO_VERSION 1u
 #define EBO_CODER_BITPACK 1u
+#define EBO_CODER_HUFFMAN 2u
+#define EBO_CODER_AUTO 3u
+#define EBO_BOOK_PAD 2064u /* largest codebook (4 + 2048 bytes) padded to 16 */
 #define EBO_TILE_ROWS 64u
 #define EBO_QMAX 2047
 
@@ -99,6 +120,7 @@ typedef struct {
   double sched_t0;           /* INV_SQRT: (1 + i/t0)^-1/2                  */
   double sched_k;            /* STEP: starting multiple of the base eb     */
   int64_t sched_phase;       /* STEP: length of the decay phase            */
+  uint32_t coder;            /* EBO_CODER_*; 0 means EBO_CODER_BITPACK     */
 } ebo_cfg;
 
 /* Iteration-wise factor (Algorithm 1 OnlineDecay, read non-cumulatively). */

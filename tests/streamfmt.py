@@ -51,6 +51,9 @@ class Segment:
     n_out: int
     nbytes: int
     tiles: list = field(default_factory=list)
+    huff: bool = False
+    lengths: np.ndarray | None = None
+    codes: dict | None = None
 
 
 @dataclass
@@ -65,6 +68,7 @@ class Stream:
     chunk_bytes: list
     segments: list
     covered: np.ndarray
+    coder: int = 1
 
 
 def unzigzag(z):
@@ -81,7 +85,9 @@ def parse(buf: np.ndarray) -> Stream:
         assert not cov[off:off + n].any(), "overlapping structures"
         cov[off:off + n] = True
 
-    assert _u(buf, 0, 4) == 0x434C4245 and _u(buf, 4, 2) == 1 and _u(buf, 6, 2) == 1
+    assert _u(buf, 0, 4) == 0x434C4245 and _u(buf, 4, 2) == 1
+    coder = _u(buf, 6, 2)
+    assert coder in (1, 2, 3)
     T, B, D, P = (_u(buf, o, 4) for o in (8, 12, 16, 20))
     assert _u(buf, 24, 4) == 64
     eb_mode = _u(buf, 28, 4)
@@ -108,11 +114,21 @@ def parse(buf: np.ndarray) -> Stream:
                           float(np.frombuffer(bytes(buf[s0 + 8:s0 + 12]), np.float32)[0]),
                           bool(_u(buf, s0 + 12, 4) & 1), _u(buf, s0 + 16, 4),
                           _u(buf, s0 + 20, 4), _u(buf, s0 + 24, 8))
-            assert _u(buf, s0 + 12, 4) in (0, 1)
+            flags = _u(buf, s0 + 12, 4)
+            assert flags in (0, 1, 3)
+            seg.huff = bool(flags & 2)
+            # coder 1: no Huffman segment; coder 2: every valid segment is one
+            assert not (seg.huff and coder == 1)
+            assert not (coder == 2 and seg.valid and not seg.huff)
             assert seg.rows == rows and seg.ntiles == (rows + 63) // 64
             mark(s0, 32)
             mark(s0 + 32, 4 * seg.ntiles)
             rb = 2 if rows <= 65536 else 4
+            if seg.huff:
+                bo = s0 + 32 + _a(4 * seg.ntiles, 16)
+                seg.lengths, nbook = read_book(buf, bo)
+                mark(bo, nbook)
+                seg.codes = canonical_codes(seg.lengths)
             for k in range(seg.ntiles):
                 ro = s0 + _u(buf, s0 + 32 + 4 * k, 4)
                 assert ro % 16 == 0
@@ -126,13 +142,43 @@ def parse(buf: np.ndarray) -> Stream:
                     mark(ro + 16, 4 * n * D)
                     tl.size = raw_size
                     if seg.valid:
-                        # the rule: BITPACK only when strictly smaller than RAW
+                        # the rule: a coded record only when strictly smaller than RAW
                         raw = np.frombuffer(bytes(buf[ro + 16:ro + 16 + 4 * n * D]),
                                             np.float32).reshape(n, D)
-                        assert bitpack_size(raw, tl.bitmap, n, D, seg.eb, rows) >= raw_size, \
-                            "RAW tile whose BITPACK record would be smaller"
+                        us = [i for i in range(n) if (tl.bitmap >> i) & 1]
+                        q, o = quantize_np(raw[us].reshape(-1), seg.eb)
+                        if seg.huff:
+                            coded = huff_size(q, o, n, len(us), D, rows, seg.lengths)
+                        else:
+                            coded = bitpack_size(raw, tl.bitmap, n, D, seg.eb, rows)
+                        assert coded >= raw_size, "RAW tile whose coded record would be smaller"
+                elif tl.mode == 2:
+                    assert seg.huff and seg.valid
+                    nE = tl.U * D
+                    nd = n - tl.U
+                    tl.refs = np.frombuffer(bytes(buf[ro + 16:ro + 16 + rb * nd]),
+                                            np.uint16 if rb == 2 else np.uint32).astype(np.int64)
+                    mark(ro + 16, rb * nd)
+                    oop = _a(16 + rb * nd, 4)
+                    tl.opos = np.frombuffer(bytes(buf[ro + oop:ro + oop + 4 * tl.n_out]),
+                                            np.uint32).astype(np.int64)
+                    tl.oval = np.frombuffer(bytes(buf[ro + oop + 4 * tl.n_out:
+                                                      ro + oop + 8 * tl.n_out]), np.uint32)
+                    mark(ro + oop, 8 * tl.n_out)
+                    oct_ = oop + 8 * tl.n_out
+                    nch = (nE + 255) // 256
+                    ct = [_u(buf, ro + oct_ + 4 * c, 4) for c in range(nch + 1)]
+                    mark(ro + oct_, 4 * (nch + 1))
+                    ow = oct_ + 4 * (nch + 1)
+                    mark(ro + ow, 4 * ct[-1])
+                    words = np.frombuffer(bytes(buf[ro + ow:ro + ow + 4 * ct[-1]]), np.uint32)
+                    sym = decode_chunks(words, ct, nE, seg.lengths, seg.codes)
+                    q = sym.astype(np.int64) - 2047
+                    tl.zz = np.where(q >= 0, 2 * q, -2 * q - 1)
+                    tl.size = _a(ow + 4 * ct[-1], 16)
+                    assert tl.size < raw_size, "Huffman tile not smaller than RAW"
                 else:
-                    assert tl.mode == 1 and seg.valid
+                    assert tl.mode == 1 and seg.valid and not seg.huff
                     nE = tl.U * D
                     nblk = (nE + 63) // 64
                     tl.widths = buf[ro + 16:ro + 16 + nblk].copy()
@@ -169,7 +215,75 @@ def parse(buf: np.ndarray) -> Stream:
             segs.append(seg)
         at += chunk_bytes[p]
     assert at == total
-    return Stream(T, B, D, P, eb_mode, it, total, chunk_bytes, segs, cov)
+    return Stream(T, B, D, P, eb_mode, it, total, chunk_bytes, segs, cov, coder)
+
+
+def read_book(buf, off):
+    """Codebook at off: u16 lowest, u16 highest symbol, 4-bit lengths (low
+    nibble first).  Returns (lengths [4095], bytes); checks it is tight and a
+    complete prefix code (or one symbol of length 1)."""
+    lo, hi = _u(buf, off, 2), _u(buf, off + 2, 2)
+    lengths = np.zeros(4095, np.int64)
+    if hi < lo:
+        assert (lo, hi) == (1, 0)
+        return lengths, 4
+    nb = hi - lo + 1
+    for k in range(nb):
+        lengths[lo + k] = (int(buf[off + 4 + k // 2]) >> (4 * (k & 1))) & 15
+    if nb & 1:
+        assert int(buf[off + 4 + nb // 2]) >> 4 == 0
+    assert lengths[lo] and lengths[hi] and lengths.max() <= 12
+    used = lengths[lengths > 0]
+    if used.size == 1:
+        assert used[0] == 1
+    else:
+        assert sum(2 ** (12 - int(l)) for l in used) == 2 ** 12
+    return lengths, 4 + (nb + 1) // 2
+
+
+def canonical_codes(lengths):
+    """Bit strings of the canonical code (shorter first, then by symbol;
+    consecutive values, shifted left at each longer length)."""
+    syms = sorted((int(l), s) for s, l in enumerate(lengths) if l)
+    out, code, prev = {}, 0, None
+    for l, s in syms:
+        if prev is not None:
+            code = (code + 1) << (l - prev)
+        out[format(code, f"0{l}b")] = s
+        prev = l
+    return out
+
+
+def decode_chunks(words, ct, n, lengths, codes):
+    """Symbols of n Huffman-coded values in 256-symbol chunks (chunk c in
+    words[ct[c]:ct[c+1]], MSB first, the rest of its last word zero)."""
+    assert ct[0] == 0
+    out = []
+    for c in range(len(ct) - 1):
+        assert ct[c] <= ct[c + 1]
+        bits = "".join(format(int(w), "032b") for w in words[ct[c]:ct[c + 1]])
+        k = 0
+        for _ in range(min(256, n - 256 * c)):
+            cur = ""
+            while cur not in codes:
+                cur += bits[k]
+                k += 1
+            out.append(codes[cur])
+        assert set(bits[k:]) <= {"0"} and len(bits) - k < 32
+    assert len(out) == n
+    return np.array(out, np.int64)
+
+
+def huff_size(q, o, n, U, D, rows, lengths):
+    """Bytes of a tile's Huffman record for the codes q (outliers o) of its U
+    first-occurrence rows."""
+    sym = np.asarray(q, np.int64).reshape(-1) + 2047
+    nE = U * D
+    words = sum((int(lengths[sym[c:c + 256]].sum()) + 31) // 32 for c in range(0, nE, 256))
+    n_out = int(np.asarray(o).sum())
+    rb = 2 if rows <= 65536 else 4
+    oop = _a(16 + rb * (n - U), 4)
+    return _a(oop + 8 * n_out + 4 * ((nE + 255) // 256 + 1) + 4 * words, 16)
 
 
 def bitpack_size(raw, bitmap, n, D, eb, rows):
@@ -289,3 +403,71 @@ def parse_segments(buf: np.ndarray):
         at += chunk_bytes[p]
     assert at == _u(buf, 48, 8)
     return segs
+
+
+def _tile_codes(seg, tl, buf, D):
+    """Codes and outlier flags of a tile's first-occurrence rows (U x D)."""
+    if tl.mode == 0:
+        raw = np.frombuffer(bytes(buf[tl.offset + 16:tl.offset + 16 + 4 * tl.n * D]),
+                            np.float32).reshape(tl.n, D)
+        us = [i for i in range(tl.n) if (tl.bitmap >> i) & 1]
+        q, o = quantize_np(raw[us].reshape(-1), seg.eb)
+        return q, o
+    q = unzigzag(tl.zz)
+    o = np.zeros(tl.U * D, bool)
+    o[tl.opos] = True
+    return q, o
+
+
+def _bitpack_tile_size(q, o, n, U, D, rows):
+    z = np.where(q >= 0, 2 * q, -2 * q - 1)
+    nE = U * D
+    nblk = (nE + 63) // 64
+    zb = np.zeros(nblk * 64, np.int64)
+    zb[:nE] = z
+    sw = sum(int(v).bit_length() for v in (zb.reshape(nblk, 64).max(axis=1) if nblk else []))
+    rb = 2 if rows <= 65536 else 4
+    orf = _a(16 + nblk, 4)
+    oop = _a(orf + rb * (n - U), 4)
+    return _a(_a(oop + 8 * int(o.sum()), 8) + 8 * sw, 16)
+
+
+def segment_form_sizes(seg, buf, D, lengths_of_hist):
+    """(bit-plane form bytes, Huffman form bytes, Huffman lengths) of a valid
+    segment, rebuilt from its codes; lengths_of_hist(freq[4095]) is the
+    Huffman construction (pinned on its own)."""
+    tiles = [(tl, *_tile_codes(seg, tl, buf, D)) for tl in seg.tiles]
+    freq = np.zeros(4095, np.uint64)
+    for tl, q, o in tiles:
+        freq += np.bincount(q + 2047, minlength=4095).astype(np.uint64)
+    lengths = np.asarray(lengths_of_hist(freq), np.int64)
+    used = np.nonzero(lengths)[0]
+    book = 4 if used.size == 0 else 4 + (int(used[-1]) - int(used[0]) + 2) // 2
+    pre = 32 + _a(4 * seg.ntiles, 16)
+    bp, hf = pre, pre + _a(book, 16)
+    for tl, q, o in tiles:
+        raw = 16 + _a(4 * tl.n * D, 16)
+        b = _bitpack_tile_size(q, o, tl.n, tl.U, D, seg.rows)
+        h = huff_size(q, o, tl.n, tl.U, D, seg.rows, lengths)
+        bp += b if b < raw else raw
+        hf += h if h < raw else raw
+    return bp, hf, lengths
+
+
+def check_coder_choice(st, buf, lengths_of_hist):
+    """Every segment has the size of the form its coder rules pick: coder 1
+    bit planes, coder 2 Huffman for valid segments, coder 3 Huffman iff
+    strictly smaller; a Huffman segment's codebook is the histogram's."""
+    picked = []
+    for seg in st.segments:
+        if not seg.valid:
+            assert not seg.huff
+            continue
+        bp, hf, lengths = segment_form_sizes(seg, buf, st.D, lengths_of_hist)
+        want_huff = {1: False, 2: True, 3: hf < bp}[st.coder]
+        assert seg.huff == want_huff, (seg.p, seg.t, bp, hf)
+        assert seg.nbytes == (hf if seg.huff else bp), (seg.p, seg.t, seg.nbytes, bp, hf)
+        if seg.huff:
+            assert np.array_equal(seg.lengths, lengths)
+        picked.append((seg.t, seg.huff, bp, hf))
+    return picked

@@ -541,3 +541,144 @@ def test_workload_subsets_meet_the_bound(name):
     c, st = check_stream(cfg, x, it=w.iteration)
     cr = x.nbytes / c.stream.size
     assert cr > 1.5, cr
+
+
+# --------------------------------------------------------------------------
+# the entropy coder inside the stream (section III-D "Huffman Encoding"):
+# Huffman segments, per-segment choice, same reconstruction as bit planes
+# --------------------------------------------------------------------------
+def test_huffman_segment_bytes_by_hand():
+    """One row of D = 8 values 0,0,0,1,0,0,0,0 at eb = 1/2: symbols 2047 (x7)
+    and 2048 (x1) get one-bit codes 0 and 1, so E's chunk is the bits
+    00010000, one word 0x10000000.  Record: 16-byte header, chunk table
+    [0, 1], the word: 28 -> 32 bytes, smaller than RAW (48).  Segment:
+    header 32, directory 16, codebook ff 07 00 08 11 padded to 16, record
+    32 = 96 bytes.  The bit-plane form is also 96 (its record, width 2, is
+    48 = RAW, not smaller), so the per-segment choice keeps bit planes."""
+    x = np.array([0, 0, 0, 1, 0, 0, 0, 0], np.float32).reshape(1, 1, 8)
+    cfg = O.Config(T=1, B=1, D=8, eb_mode=O.EB_ABS, eb=(0.5,), coder=O.CODER_HUFFMAN)
+    st = O.compress(cfg, 0, x).stream
+    assert st.size == 64 + 16 + 16 + 96
+    assert int.from_bytes(st[6:8].tobytes(), "little") == 2
+    sg = 64 + 16 + 16
+    assert int.from_bytes(st[sg + 12:sg + 16].tobytes(), "little") == 3  # valid | Huffman
+    assert int.from_bytes(st[sg + 24:sg + 32].tobytes(), "little") == 96
+    assert st[sg + 48:sg + 64].tolist() == [0xFF, 0x07, 0x00, 0x08, 0x11] + [0] * 11
+    assert int.from_bytes(st[sg + 32:sg + 36].tobytes(), "little") == 64  # the record
+    rec = st[sg + 64:sg + 96]
+    assert rec[:16].tolist() == [1, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 1, 0, 2, 0]
+    assert rec[16:28].tolist() == [0, 0, 0, 0, 1, 0, 0, 0, 0, 0, 0, 0x10]
+    assert rec[28:].tolist() == [0, 0, 0, 0]
+    np.testing.assert_array_equal(O.decompress(cfg, st), x)
+    auto = O.Config(T=1, B=1, D=8, eb_mode=O.EB_ABS, eb=(0.5,), coder=O.CODER_AUTO)
+    sa = O.compress(auto, 0, x).stream
+    assert int.from_bytes(sa[sg + 12:sg + 16].tobytes(), "little") == 1  # tie: bit planes
+    assert sa.size == st.size
+
+
+def _huff_streams(T, B, D, P, mode, eb, seed, coder):
+    rng = np.random.default_rng(seed)
+    base = rng.normal(0, 0.05, (T, max(1, B // 3), D)).astype(np.float32)
+    x = np.take_along_axis(base, rng.integers(0, base.shape[1], (T, B))[:, :, None], axis=1).copy()
+    if B > 2:
+        x[0, 1, 0] = 1e6
+        x[-1, 2, -1] = np.nan
+    return x, O.Config(T=T, B=B, D=D, P=P, eb_mode=mode, eb=(eb,), coder=coder)
+
+
+@pytest.mark.parametrize("T,B,D,P", [(2, 130, 128, 1), (3, 200, 24, 2), (1, 64, 64, 1),
+                                     (2, 1, 8, 1), (2, 0, 16, 1), (4, 300, 5, 3)])
+@pytest.mark.parametrize("coder", [2, 3])
+def test_huffman_streams_rules_and_reconstruction(T, B, D, P, coder):
+    """The independent reader walks every Huffman structure (zero padding,
+    complete tight codebooks, chunk tables, chunk bits), re-derives each
+    record's and each segment's choice, and finds the codebook built from the
+    histogram of E; the reconstruction is bitwise the bit-plane stream's."""
+    x, cfg = _huff_streams(T, B, D, P, O.EB_REL, 0.02, T * 31 + B + D, coder)
+    ref = O.compress(cfg, 3, x)
+    st = SF.parse(ref.stream)
+    assert st.coder == coder
+    assert not np.any(ref.stream[~st.covered])
+    SF.check_coder_choice(st, ref.stream, O.huff_lengths)
+    y = O.decompress(cfg, ref.stream)
+    codes, outl, first, yr = SF.decode(st, ref.stream)
+    np.testing.assert_array_equal(yr.view(np.uint32), y.view(np.uint32))
+    np.testing.assert_array_equal(codes, ref.codes)
+    assert ref.stream.size <= O.max_compressed_bytes(cfg)
+    # the bound on every element; and rows of tiles coded under both coders
+    # (a tile may be RAW under one and coded under the other) reconstruct
+    # bitwise alike
+    bp = O.Config(**{**cfg.__dict__, "coder": O.CODER_BITPACK})
+    sb = SF.parse(O.compress(bp, 3, x).stream)
+    yb = O.decompress(bp, O.compress(bp, 3, x).stream)
+    for sh, sp in zip(st.segments, sb.segments):
+        r0 = sh.p * B // P
+        xs = x[sh.t, r0:r0 + sh.rows].astype(np.float64)
+        fin = np.isfinite(xs)
+        ys = y[sh.t, r0:r0 + sh.rows].astype(np.float64)
+        assert np.all(np.abs(xs - ys)[fin] <= np.float64(np.float32(sh.eb)) if sh.valid else xs[fin] == ys[fin])
+        for k, (th, tp) in enumerate(zip(sh.tiles, sp.tiles)):
+            if th.mode and tp.mode:
+                a = y[sh.t, r0 + 64 * k:r0 + 64 * k + th.n]
+                b = yb[sh.t, r0 + 64 * k:r0 + 64 * k + th.n]
+                np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_per_segment_choice_follows_the_data():
+    """A table whose codes are all 0 costs no bit planes at all but one bit per
+    code under Huffman: bit planes win.  A table of wide Gaussian codes costs
+    about its entropy under Huffman and the width of each block's largest
+    code as bit planes: Huffman wins.  The per-segment choice is never larger
+    than either forced coder."""
+    rng = np.random.default_rng(5)
+    T, B, D = 2, 512, 64
+    x = np.zeros((T, B, D), np.float32)
+    x[1] = rng.normal(0, 40.0, (B, D)).astype(np.float32)
+    mk = lambda c: O.Config(T=T, B=B, D=D, eb_mode=O.EB_ABS, eb=(0.5,), coder=c)
+    sizes = {c: O.compress(mk(c), 0, x).stream for c in (1, 2, 3)}
+    st = SF.parse(sizes[3])
+    assert [s.huff for s in st.segments] == [False, True]
+    assert sizes[3].size <= min(sizes[1].size, sizes[2].size)
+    assert sizes[3].size < sizes[1].size
+    for c in (1, 2, 3):
+        np.testing.assert_array_equal(O.decompress(mk(c), sizes[c]), x.round())
+
+
+def test_all_raw_huffman_segment_stays_within_the_bound():
+    """Values that are all outliers leave every tile RAW; a forced Huffman
+    segment then carries its codebook on top of the RAW records, which the
+    size bound allows for."""
+    rng = np.random.default_rng(9)
+    x = rng.normal(0, 1e6, (2, 100, 32)).astype(np.float32)
+    cfg = O.Config(T=2, B=100, D=32, eb_mode=O.EB_ABS, eb=(1e-3,), coder=O.CODER_HUFFMAN)
+    st = O.compress(cfg, 0, x).stream
+    assert st.size <= O.max_compressed_bytes(cfg)
+    p = SF.parse(st)
+    assert all(s.huff for s in p.segments) and all(t.mode == 0 for s in p.segments for t in s.tiles)
+    np.testing.assert_array_equal(O.decompress(cfg, st), x)
+
+
+def test_corrupt_huffman_streams_are_rejected():
+    x, cfg = _huff_streams(2, 200, 32, 1, O.EB_ABS, 0.01, 3, O.CODER_HUFFMAN)
+    good = O.compress(cfg, 0, x).stream
+    st = SF.parse(good)
+    seg = st.segments[0]
+    cases = []
+    b = good.copy(); b[6] = 1; cases.append(("Huffman segment in a bit-plane stream", b))
+    bo = seg.offset + 32 + (4 * seg.ntiles + 15) // 16 * 16
+    b = good.copy(); b[bo + 4] ^= 0x11; cases.append(("codebook not a complete code", b))
+    tl = [t for t in seg.tiles if t.mode == 2][0]
+    oop = tl.offset + (16 + 2 * (tl.n - tl.U) + 3) // 4 * 4
+    oct_ = oop + 8 * tl.n_out
+    b = good.copy(); b[oct_:oct_ + 4] = 1; cases.append(("chunk table start", b))
+    b = good.copy(); b[oct_ + 4:oct_ + 8] = 0; cases.append(("chunk table order", b))
+    b = good.copy(); b[tl.offset + 14] = 1; cases.append(("bit-plane record in a Huffman segment", b))
+    for label, bad in cases:
+        rc, _ = O.decompress(cfg, bad, status=True)
+        assert rc == O.ERR_CORRUPT, label
+    rng = np.random.default_rng(0)
+    for i in range(200):
+        bad = good.copy()
+        bad[int(rng.integers(0, bad.size))] ^= np.uint8(1 << int(rng.integers(0, 8)))
+        rc, _ = O.decompress(cfg, bad, status=True)
+        assert rc in (O.OK, O.ERR_CORRUPT)
