@@ -21,7 +21,7 @@ EC_OK, EC_ERR_INVALID, EC_ERR_CAPACITY, EC_ERR_CORRUPT = 0, 1, 2, 3
 EC_ERR_DEVICE, EC_ERR_OOM, EC_ERR_UNSUPPORTED = 4, 5, 6
 EB_ABS, EB_REL_RANGE = 0, 1
 SCHED_NONE, SCHED_INV_SQRT, SCHED_STEP = 0, 1, 2
-CODER_BITPACK = 1
+CODER_BITPACK, CODER_HUFFMAN, CODER_AUTO = 1, 2, 3
 KERNEL_PREP, KERNEL_ENCODE, KERNEL_DECODE, KERNEL_ASSEMBLE = 0, 1, 2, 3
 ABI_VERSION = 1
 
@@ -148,7 +148,8 @@ def _stream_handle(stream) -> int:
     return stream.cuda_stream
 
 
-def _desc(T, B, D, P, eb_mode, eb, table_mult, schedule, debug_hash_bits, keep):
+def _desc(T, B, D, P, eb_mode, eb, table_mult, schedule, debug_hash_bits, keep,
+          coder=CODER_BITPACK):
     ebs = [float(v) for v in (eb if hasattr(eb, "__len__") else [eb])]
     if len(ebs) == 1 and T > 1:
         ebs = ebs * T
@@ -164,13 +165,13 @@ def _desc(T, B, D, P, eb_mode, eb, table_mult, schedule, debug_hash_bits, keep):
                   float(sch.get("t0", 1000.0)), float(sch.get("k", 2.0)),
                   int(sch.get("phase", 1)))
     return _Desc(ABI_VERSION, T, B, D, P, int(eb_mode), ctypes.cast(arr, ctypes.POINTER(ctypes.c_float)),
-                 mult, s, CODER_BITPACK, int(debug_hash_bits), None, 0)
+                 mult, s, int(coder), int(debug_hash_bits), None, 0)
 
 
 def workspace_bytes(T, B, D, P=1, eb_mode=EB_ABS, eb=1e-4, table_mult=None, schedule=None,
-                    debug_hash_bits=0) -> int:
+                    debug_hash_bits=0, coder=CODER_BITPACK) -> int:
     keep = []
-    d = _desc(T, B, D, P, eb_mode, eb, table_mult, schedule, debug_hash_bits, keep)
+    d = _desc(T, B, D, P, eb_mode, eb, table_mult, schedule, debug_hash_bits, keep, coder)
     return int(lib().ec_workspace_bytes(ctypes.byref(d)))
 
 
@@ -183,15 +184,16 @@ class Plan:
 
     def __init__(self, T: int, B: int, D: int, P: int = 1, eb_mode: int = EB_ABS, eb=1e-4,
                  table_mult=None, schedule=None, debug_hash_bits: int = 0, device=None,
-                 workspace: bool = True):
+                 workspace: bool = True, coder: int = CODER_BITPACK):
         """workspace=False builds a plan without a workspace: compress with
         compress_static (the library's static device scratch), decompress as
-        usual."""
+        usual.  coder: CODER_BITPACK, CODER_HUFFMAN or CODER_AUTO."""
         import torch
         self.T, self.B, self.D, self.P = T, B, D, P
+        self.coder = coder
         self._keep = []
         self._desc = _desc(T, B, D, P, eb_mode, eb, table_mult, schedule, debug_hash_bits,
-                           self._keep)
+                           self._keep, coder)
         L = lib()
         nbytes = int(L.ec_workspace_bytes(ctypes.byref(self._desc)))
         if nbytes == 0:

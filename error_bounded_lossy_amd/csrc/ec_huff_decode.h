@@ -1,0 +1,107 @@
+// ec_huff_decode.h -- decoding of one 256-symbol chunk of canonical Huffman
+// codes by 12-bit table lookups (gfx950), shared by the standalone coder
+// (ec_huffman.hip) and the Huffman segments of the compressed stream
+// (ec_kernels.hip).  lut maps every 12-bit prefix to (symbol | length << 12),
+// 0 where no code starts.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ec {
+namespace hd {
+
+// Decode one chunk of `rem` symbols from its nwords words at src (LDS or
+// global memory).  The bits are read as if zero words followed the chunk;
+// whether it really ends in its last word is decided from the bits consumed.
+// Returns false if the chunk is malformed.
+__device__ __forceinline__ bool decode_chunk(const uint32_t* src, uint32_t nwords, uint32_t rem,
+                                             const uint16_t* lut, uint16_t* out, bool vec) {
+  // two words are loaded ahead of the bit buffer, so a refill never waits
+  uint32_t q0 = nwords > 0 ? src[0] : 0u, q1 = nwords > 1 ? src[1] : 0u, p = 2;
+  uint64_t bitbuf = 0;
+  uint32_t have = 0, used = 0;
+  bool bad = false;
+  for (uint32_t g = 0; g < rem; g += 8) {
+    uint32_t pk[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      if (have <= 32) {
+        bitbuf |= (uint64_t)q0 << (32 - have);
+        have += 32;
+        q0 = q1;
+        q1 = p < nwords ? src[p] : 0u;
+        p++;
+      }
+      const uint32_t ent = lut[bitbuf >> 52];
+      const bool act = g + k < rem;
+      const uint32_t l = act ? ent >> 12 : 0u;
+      bad |= act && l == 0;
+      bitbuf <<= l;
+      have -= l;
+      used += l;
+      pk[k >> 1] |= (ent & 0xFFFu) << (16 * (k & 1));
+    }
+    if (vec && g + 8 <= rem) {
+      *reinterpret_cast<uint4*>(out + g) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    } else {
+      for (uint32_t k = 0; k < min(rem - g, 8u); k++)
+        out[g + k] = (uint16_t)(pk[k >> 1] >> (16 * (k & 1)));
+    }
+  }
+  // every consumed bit lies in the chunk, the chunk's last word holds some of
+  // them, and the bits after the last code are zero
+  return !(bad || used > 32 * nwords || used + 32 <= 32 * nwords || bitbuf != 0);
+}
+
+// The same for a chunk staged in LDS, without branches in the symbol loop:
+// the word after the bit buffer's next word is loaded together with every
+// table lookup (one LDS wait per symbol), and a refill after the lookup
+// consumes it with selects, so the buffer holds at least 21 bits at every
+// lookup.  Words past the chunk read as zero.  nwords >= 1.
+__device__ __forceinline__ bool decode_chunk_lds(const uint32_t* src, uint32_t nwords,
+                                                 uint32_t rem, const uint16_t* lut,
+                                                 uint16_t* out, bool vec) {
+  const uint32_t last = nwords - 1;
+  uint64_t bitbuf = (uint64_t)src[0] << 32;
+  uint32_t have = 32, used = 0;
+  uint32_t p = 1;  // index of wq, the next word to insert
+  uint32_t wq = nwords > 1 ? src[1] : 0u;
+  bool bad = false;
+  for (uint32_t g = 0; g < rem; g += 32) {
+    uint32_t pk[16];
+#pragma unroll
+    for (int k = 0; k < 16; k++) pk[k] = 0;
+#pragma unroll
+    for (int k = 0; k < 32; k++) {
+      const uint32_t wn_raw = src[min(p + 1, last)];
+      const uint32_t ent = lut[bitbuf >> 52];
+      const bool act = g + k < rem;
+      const uint32_t l = act ? ent >> 12 : 0u;
+      bad |= act && l == 0;
+      bitbuf <<= l;
+      have -= l;
+      used += l;
+      pk[k >> 1] |= (ent & 0xFFFu) << (16 * (k & 1));
+      const bool rf = have <= 32;
+      const uint32_t wn = p + 1 <= last ? wn_raw : 0u;
+      bitbuf |= rf ? (uint64_t)wq << (32 - have) : 0ull;
+      have += rf ? 32u : 0u;
+      wq = rf ? wn : wq;
+      p += rf ? 1u : 0u;
+    }
+    if (vec && g + 32 <= rem) {  // 64 bytes of one chunk at a time
+#pragma unroll
+      for (int q = 0; q < 4; q++)
+        *reinterpret_cast<uint4*>(out + g + 8 * q) =
+            make_uint4(pk[4 * q], pk[4 * q + 1], pk[4 * q + 2], pk[4 * q + 3]);
+    } else {
+      for (uint32_t k = 0; k < min(rem - g, 32u); k++)
+        out[g + k] = (uint16_t)(pk[k >> 1] >> (16 * (k & 1)));
+    }
+  }
+  return !(bad || used > 32 * nwords || used + 32 <= 32 * nwords || bitbuf != 0);
+}
+
+}  // namespace hd
+}  // namespace ec

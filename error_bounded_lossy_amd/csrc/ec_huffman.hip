@@ -27,9 +27,13 @@
 #include <stdint.h>
 
 #include "ec.h"
+#include "ec_huff_decode.h"
 #include "ec_huffman.h"
 
 namespace {
+
+using ec::hd::decode_chunk;
+using ec::hd::decode_chunk_lds;
 
 constexpr int kNsym = (int)EC_HUFF_NSYM;      // 4095
 constexpr int kMaxLen = (int)EC_HUFF_MAXLEN;  // 12
@@ -682,98 +686,6 @@ __global__ void __launch_bounds__(kBookThreads) huff_dec_book(const uint8_t* __r
   }
 }
 
-// Decode one chunk of `rem` symbols from its nwords words at src (LDS or
-// global memory).  The bits are read as if zero words followed the chunk;
-// whether it really ends in its last word is decided from the bits consumed.
-// Returns false if the chunk is malformed.
-__device__ __forceinline__ bool decode_chunk(const uint32_t* src, uint32_t nwords, uint32_t rem,
-                                             const uint16_t* lut, uint16_t* out, bool vec) {
-  // two words are loaded ahead of the bit buffer, so a refill never waits
-  uint32_t q0 = nwords > 0 ? src[0] : 0u, q1 = nwords > 1 ? src[1] : 0u, p = 2;
-  uint64_t bitbuf = 0;
-  uint32_t have = 0, used = 0;
-  bool bad = false;
-  for (uint32_t g = 0; g < rem; g += 8) {
-    uint32_t pk[4] = {0, 0, 0, 0};
-#pragma unroll
-    for (int k = 0; k < 8; k++) {
-      if (have <= 32) {
-        bitbuf |= (uint64_t)q0 << (32 - have);
-        have += 32;
-        q0 = q1;
-        q1 = p < nwords ? src[p] : 0u;
-        p++;
-      }
-      const uint32_t ent = lut[bitbuf >> 52];
-      const bool act = g + k < rem;
-      const uint32_t l = act ? ent >> 12 : 0u;
-      bad |= act && l == 0;
-      bitbuf <<= l;
-      have -= l;
-      used += l;
-      pk[k >> 1] |= (ent & 0xFFFu) << (16 * (k & 1));
-    }
-    if (vec && g + 8 <= rem) {
-      *reinterpret_cast<uint4*>(out + g) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-    } else {
-      for (uint32_t k = 0; k < min(rem - g, 8u); k++)
-        out[g + k] = (uint16_t)(pk[k >> 1] >> (16 * (k & 1)));
-    }
-  }
-  // every consumed bit lies in the chunk, the chunk's last word holds some of
-  // them, and the bits after the last code are zero
-  return !(bad || used > 32 * nwords || used + 32 <= 32 * nwords || bitbuf != 0);
-}
-
-// The same for a chunk staged in LDS, without branches in the symbol loop:
-// the word after the bit buffer's next word is loaded together with every
-// table lookup (one LDS wait per symbol), and a refill after the lookup
-// consumes it with selects, so the buffer holds at least 21 bits at every
-// lookup.  Words past the chunk read as zero.  nwords >= 1.
-__device__ __forceinline__ bool decode_chunk_lds(const uint32_t* src, uint32_t nwords,
-                                                 uint32_t rem, const uint16_t* lut,
-                                                 uint16_t* out, bool vec) {
-  const uint32_t last = nwords - 1;
-  uint64_t bitbuf = (uint64_t)src[0] << 32;
-  uint32_t have = 32, used = 0;
-  uint32_t p = 1;  // index of wq, the next word to insert
-  uint32_t wq = nwords > 1 ? src[1] : 0u;
-  bool bad = false;
-  for (uint32_t g = 0; g < rem; g += 32) {
-    uint32_t pk[16];
-#pragma unroll
-    for (int k = 0; k < 16; k++) pk[k] = 0;
-#pragma unroll
-    for (int k = 0; k < 32; k++) {
-      const uint32_t wn_raw = src[min(p + 1, last)];
-      const uint32_t ent = lut[bitbuf >> 52];
-      const bool act = g + k < rem;
-      const uint32_t l = act ? ent >> 12 : 0u;
-      bad |= act && l == 0;
-      bitbuf <<= l;
-      have -= l;
-      used += l;
-      pk[k >> 1] |= (ent & 0xFFFu) << (16 * (k & 1));
-      const bool rf = have <= 32;
-      const uint32_t wn = p + 1 <= last ? wn_raw : 0u;
-      bitbuf |= rf ? (uint64_t)wq << (32 - have) : 0ull;
-      have += rf ? 32u : 0u;
-      wq = rf ? wn : wq;
-      p += rf ? 1u : 0u;
-    }
-    if (vec && g + 32 <= rem) {  // 64 bytes of one chunk at a time
-#pragma unroll
-      for (int q = 0; q < 4; q++)
-        *reinterpret_cast<uint4*>(out + g + 8 * q) =
-            make_uint4(pk[4 * q], pk[4 * q + 1], pk[4 * q + 2], pk[4 * q + 3]);
-    } else {
-      for (uint32_t k = 0; k < min(rem - g, 32u); k++)
-        out[g + k] = (uint16_t)(pk[k >> 1] >> (16 * (k & 1)));
-    }
-  }
-  return !(bad || used > 32 * nwords || used + 32 <= 32 * nwords || bitbuf != 0);
-}
-
 // Chunks [128 blockIdx.x, 128 blockIdx.x + 128) of segment blockIdx.y.
 __global__ void __launch_bounds__(kDecChunks) huff_decode(const uint32_t* __restrict__ words,
                                                           uint64_t words_cap,
@@ -894,6 +806,42 @@ ec_status decode_impl(const uint8_t* d_books, uint64_t book_bytes, const uint32_
 }
 
 }  // namespace
+
+namespace ec {
+
+// Codebooks of the compressed stream's Huffman segments: huff_book over nseg
+// histograms of 4096 bins (hist), giving len << 16 | code per symbol (enc)
+// and the codebook bytes at books + seg * EC_HUFF_BOOK_MAX.  status gets the
+// builder's error bits (zeroed first by the caller).
+hipError_t launch_seg_books(uint32_t* hist, uint32_t* enc, uint8_t* books, uint32_t* status,
+                            uint32_t nseg, hipStream_t s) {
+  Ws w{};
+  w.status = status;
+  w.hist = hist;
+  w.enc = enc;
+  // n = 1: the chunk table (here the status word) is not written
+  hipLaunchKernelGGL(huff_book, dim3(nseg), dim3(kBookThreads), 0, s, w, books, status, (uint64_t)1);
+  return hipGetLastError();
+}
+
+// Decode tables from nseg codebooks at books + seg * EC_HUFF_BOOK_MAX (each
+// padded with zeros past the bytes the stream held): lut[seg][4096] and
+// valid[seg] (1 for a well-formed book with at least one symbol); enc is
+// scratch, zero_word a device word holding 0, status a scratch word.
+hipError_t launch_seg_luts(const uint8_t* books, const uint32_t* zero_word, uint32_t* enc,
+                           uint16_t* lut, uint32_t* valid, uint32_t* status, uint32_t nseg,
+                           hipStream_t s) {
+  Ws w{};
+  w.status = status;
+  w.valid = valid;
+  w.enc = enc;
+  w.lut = lut;
+  hipLaunchKernelGGL(huff_dec_book, dim3(nseg), dim3(kBookThreads), 0, s, books,
+                     (uint64_t)kBookStride, zero_word, (uint64_t)1, w, 0);
+  return hipGetLastError();
+}
+
+}  // namespace ec
 
 extern "C" {
 

@@ -12,6 +12,11 @@ constexpr uint32_t kThreads = 256;    // threads per workgroup (4 wave64)
 constexpr uint32_t kMagic = 0x434C4245u;
 constexpr uint32_t kVersion = 1;
 constexpr uint32_t kCoderBitpack = 1;
+constexpr uint32_t kCoderHuffman = 2;   // every segment with a valid eb
+constexpr uint32_t kCoderAuto = 3;      // per segment, the smaller form
+constexpr uint32_t kHuffTable = 4096;   // Huffman alphabet (4095) + 1, per segment
+constexpr uint32_t kBookStride = 2052;  // largest codebook (4 + 4095/2 rounded up)
+constexpr uint32_t kBookPad = 2064;     // its size padded to 16
 
 // Error codes the device stores into the host-visible status word.
 constexpr uint32_t kDevErrCorrupt = 3;
@@ -74,6 +79,18 @@ struct Work {
   uint64_t* tile_bitmap;         // [ntiles] first-occurrence rows
   uint32_t* tile_first;          // [ntiles][64] first occurrence of each row
   uint32_t* seg_eb;              // [nseg] stored error bound bits (0: raw segment), from quantize
+  // Huffman segments (D = 64, 128, 256 with the Huffman or automatic coder;
+  // NULL otherwise)
+  uint16_t* stage_sym;           // [ntiles][64][D] symbols q + 2047 of every row (outliers 2047)
+  uint32_t* hhist;               // [nseg][4096] histogram of the segment's first-occurrence rows
+  uint32_t* henc;                // [nseg][4096] len << 16 | code (also decode scratch)
+  uint8_t* hbooks;               // [nseg][kBookStride] codebook bytes (encode: built; decode:
+                                 // copied from the stream)
+  uint32_t* hstat;               // [4] builder status words
+  uint32_t* tile_hsize;          // [ntiles] Huffman record bytes
+  uint32_t* seg_coder;           // [nseg] 1: the segment is Huffman-coded
+  uint16_t* hlut;                // [nseg][4096] decode tables
+  uint32_t* hvalid;              // [nseg] decode table valid; | 2: empty codebook (no symbol)
 };
 
 struct PrepArgs {
@@ -93,6 +110,7 @@ struct EncArgs {
   uint32_t eb_mode;
   int64_t iter;
   double sched;                  // iteration-wise factor, computed on the host
+  uint32_t coder;                // kCoderBitpack, kCoderHuffman or kCoderAuto
   uint64_t hash_keep;            // mask applied to row hashes (tests weaken it)
   Report* report;                // device pointer of the pinned report block
   uint32_t* seg_meta;            // in the report block: [nseg][2] U, eb valid (or NULL)
@@ -110,6 +128,8 @@ struct DecArgs {
   Shape sh;
   const uint32_t* seg_tile_base;
   Report* report;
+  uint32_t huff;  // the plan decodes Huffman segments (its workspace holds the tables)
+  Work w;         // the plan's workspace (Huffman decoding only)
 };
 
 // LDS bytes of the encode kernel for dimension D.
@@ -133,7 +153,26 @@ hipError_t launch_encode(const EncArgs& a, hipStream_t s);
 // size, place and write kernels)
 bool encode_has_assembly(uint32_t D);
 hipError_t launch_assemble(const EncArgs& a, hipStream_t s);
+// its two kernels one at a time (the Huffman coder's passes run between them)
+hipError_t launch_assemble_size(const EncArgs& a, hipStream_t s);
+hipError_t launch_assemble_write(const EncArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecArgs& a, hipStream_t s);
+// Huffman segments of the stream (D = 64, 128, 256): after the size pass,
+// histograms, codebooks, record sizes, the choice per segment and the tile
+// items; after the write pass, the chunk words.
+hipError_t launch_huff_encode(const EncArgs& a, hipStream_t s);
+hipError_t launch_huff_write(const EncArgs& a, hipStream_t s);
+// Decoding: codebooks gathered from the stream and their tables before the
+// decode kernel, Huffman tiles and the references of their rows after it.
+hipError_t launch_huff_tables(const DecArgs& a, hipStream_t s);
+hipError_t launch_huff_decode(const DecArgs& a, hipStream_t s);
+// in ec_huffman.hip: the codebook builder and the decode-table builder of the
+// Huffman coder, over per-segment arrays
+hipError_t launch_seg_books(uint32_t* hist, uint32_t* enc, uint8_t* books, uint32_t* status,
+                            uint32_t nseg, hipStream_t s);
+hipError_t launch_seg_luts(const uint8_t* books, const uint32_t* zero_word, uint32_t* enc,
+                           uint16_t* lut, uint32_t* valid, uint32_t* status, uint32_t nseg,
+                           hipStream_t s);
 // Distinct rows of every segment as raw fp32 bit patterns (into empty hash
 // tables), summed per segment into a.seg_norig: two kernels.
 hipError_t launch_distinct_raw(const EncArgs& a, hipStream_t s);

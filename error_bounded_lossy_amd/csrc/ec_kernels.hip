@@ -28,6 +28,7 @@
 #include <type_traits>
 
 #include "../../include/ec.h"
+#include "ec_huff_decode.h"
 
 #ifndef EC_PREP_LOADS
 #define EC_PREP_LOADS 8  // 128-bit loads in flight per thread in the range pass
@@ -44,6 +45,10 @@ __device__ __forceinline__ uint64_t align_up(uint64_t v, uint64_t a) {
 }
 
 __device__ __forceinline__ uint32_t f2u(float f) { return __float_as_uint(f); }
+
+// Lanes below this one.  (HIP's __lanemask_lt() also masks with the lanes
+// that are active, so in a divergent branch it is not this.)
+__device__ __forceinline__ uint64_t lanes_below() { return (1ull << (threadIdx.x & 63)) - 1ull; }
 
 // Linear quantization of one value (section III-D): q = rint(x / 2eb); values
 // whose code would leave [-2047, 2047] or whose fp32 reconstruction q*2eb
@@ -833,7 +838,7 @@ __global__ void __launch_bounds__(kThreads) ec_encode_kernel(EncArgs a) {
     bool uniq = valid && inrow && first == k * kTileRows + lane;
     uint64_t bm = __ballot(uniq);
     if (inrow) s_first[lane] = first;
-    if (uniq) s_urow[__popcll(bm & __lanemask_lt())] = (uint8_t)lane;
+    if (uniq) s_urow[__popcll(bm & lanes_below())] = (uint8_t)lane;
     if (lane == 0) {
       sh.bitmap = bm;
       sh.U = (uint32_t)__popcll(bm);
@@ -919,7 +924,7 @@ __global__ void __launch_bounds__(kThreads) ec_encode_kernel(EncArgs a) {
         }
         uint64_t om = __ballot(isout);
         if (isout) {
-          uint32_t o = s_obase[b] + (uint32_t)__popcll(om & __lanemask_lt());
+          uint32_t o = s_obase[b] + (uint32_t)__popcll(om & lanes_below());
           opos[o] = e;
           oval[o] = f2u(xt[(uint64_t)s_urow[u] * D + d]);
         }
@@ -1178,6 +1183,8 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
     }
   }
   __syncthreads();
+  if (a.w.hhist && k == 0)  // the segment's Huffman histogram starts at zero
+    for (uint32_t e = tid; e < kHuffTable; e += kThreads) a.w.hhist[(uint64_t)s * kHuffTable + e] = 0;
   const float eb = sh.eb;
   const float s2 = eb + eb;
   const float r2 = 1.0f / s2;
@@ -1286,6 +1293,13 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
     for (uint32_t rr = 0; rr < kRB; rr++)
 #pragma unroll
       for (uint32_t j = 0; j < C; j++) hs[rr] += __umul24((uint32_t)q[rr][j], hk[j]);
+    if (a.w.stage_sym) {  // Huffman segments: every row's symbols q + 2047 (outliers 2047)
+      uint16_t* sy = a.w.stage_sym + (uint64_t)ticket * kTileRows * D;
+#pragma unroll
+      for (uint32_t rr = 0; rr < kRB; rr++)
+#pragma unroll
+        for (uint32_t j = 0; j < C; j++) sy[(ib + rr) * D + 64 * j + lane] = (uint16_t)(q[rr][j] + 2047);
+    }
     if (dbg) {  // tests only
 #pragma unroll
       for (uint32_t rr = 0; rr < kRB; rr++) {
@@ -1575,6 +1589,7 @@ __global__ void __launch_bounds__(kSizeThreads) ec_size_fast(EncArgs a) {
       info.w = L.mode | (valid[q] ? 0x100u : 0u);
       reinterpret_cast<uint4*>(a.w.tile_info)[ticket] = info;
       a.w.tile_bitmap[ticket] = bm;
+      a.w.tile_nout[ticket] = nout;  // the outliers of its first occurrences, however stored
     }
   }
   if (lane == 0) s_sum[wv] = items;
@@ -1613,22 +1628,33 @@ __device__ __forceinline__ uint64_t tiles_before(const EncArgs& a, uint32_t j) {
 // its chunk table; the stream's first tile writes the chunk byte counts and the
 // stream header.  Whole workgroup.  ss: segment start, se: segment end, cs:
 // start of the segment's chunk, un: the segment's U and n_out.
+// Bytes of the codebook at b (u16 lowest, u16 highest symbol, 4-bit lengths).
+__device__ __forceinline__ uint32_t book_bytes(const uint8_t* b) {
+  const uint32_t lo = b[0] | (uint32_t)b[1] << 8, hi = b[2] | (uint32_t)b[3] << 8;
+  return hi < lo ? 4u : 4u + (hi - lo + 2) / 2;
+}
+
 __device__ void write_stream_tables(const EncArgs& a, const TileCoord& c, uint32_t ticket,
                                     uint64_t rec_abs, uint64_t ss, uint64_t se, uint64_t cs,
-                                    const uint32_t* un, uint64_t total) {
+                                    const uint32_t* un, uint64_t total, bool huff) {
   const uint32_t tid = threadIdx.x, T = a.sh.T, P = a.sh.P;
   if (c.ntiles && tid == 0) reinterpret_cast<uint32_t*>(a.out + ss + 32)[c.k] = (uint32_t)(rec_abs - ss);
   if (c.k == 0) {
     uint8_t* sg = a.out + ss;
     const uint32_t dend = 32 + 4 * c.ntiles, dpad = (uint32_t)align_up(dend, 16) - dend;
     if (tid < dpad) sg[dend + tid] = 0;
+    if (huff) {  // the codebook after the tile directory, zero-padded to 16
+      const uint8_t* bk = a.w.hbooks + (uint64_t)c.s * kBookStride;
+      const uint32_t nb = book_bytes(bk), at = dend + dpad, pad = (uint32_t)align_up(nb, 16);
+      for (uint32_t i = tid; i < pad; i += kThreads) sg[at + i] = i < nb ? bk[i] : (uint8_t)0;
+    }
     if (tid == 0) {
       const uint32_t ebw = a.w.seg_eb[c.s];
       uint32_t* h = reinterpret_cast<uint32_t*>(sg);
       h[0] = c.rows;
       h[1] = c.ntiles;
       h[2] = ebw;
-      h[3] = ebw ? 1u : 0u;
+      h[3] = ebw ? (huff ? 3u : 1u) : 0u;
       h[4] = un[0];
       h[5] = un[1];
       reinterpret_cast<uint64_t*>(sg)[3] = se - ss;
@@ -1646,7 +1672,7 @@ __device__ void write_stream_tables(const EncArgs& a, const TileCoord& c, uint32
     if (P & 1u) reinterpret_cast<uint64_t*>(a.out + 64)[P] = 0;
     uint32_t* h = reinterpret_cast<uint32_t*>(a.out);
     h[0] = kMagic;
-    h[1] = kVersion | (kCoderBitpack << 16);
+    h[1] = kVersion | (a.coder << 16);
     h[2] = T;
     h[3] = a.sh.B;
     h[4] = a.sh.D;
@@ -1680,6 +1706,9 @@ ec_write_fast(EncArgs a) {
   const uint32_t ticket = blockIdx.x;
   const TileCoord c = tile_coord(a, ticket);
   const uint32_t n = c.n;
+  // a Huffman segment: its codebook follows the tile directory
+  const bool huff = a.w.seg_coder && a.w.seg_coder[c.s] != 0;
+  const uint32_t bookpad = huff ? (uint32_t)align_up(book_bytes(a.w.hbooks + (uint64_t)c.s * kBookStride), 16) : 0u;
   const float* xt = a.x + ((uint64_t)c.t * a.sh.B + chunk_row0(a.sh, c.pch) + (uint64_t)c.k * kTileRows) * D;
   // every staged plane word of the tile is requested before the metadata
   // (words above a block's width are loaded and then dropped)
@@ -1728,7 +1757,7 @@ ec_write_fast(EncArgs a) {
     }
     s_obase[lane] = io - ro;
     s_first[lane] = first;
-    if (uniq) s_urow[__popcll(bitmap & __lanemask_lt())] = (uint8_t)lane;
+    if (uniq) s_urow[__popcll(bitmap & lanes_below())] = (uint8_t)lane;
     if (lane == 0) {
       s_bitmap = bitmap;
       s_info = info;
@@ -1739,7 +1768,7 @@ ec_write_fast(EncArgs a) {
       const uint64_t chunk_prefix = c.t == 0 ? align_up(8ull * a.sh.T, 16) : 0;
       const uint64_t ss = a.sh.base_bytes + seg_before + chunk_prefix;
       s_seg_start = ss;
-      s_rec_abs = c.k == 0 ? ss + seg_prefix_bytes(c.ntiles) : a.sh.base_bytes + before;
+      s_rec_abs = c.k == 0 ? ss + seg_prefix_bytes(c.ntiles) + bookpad : a.sh.base_bytes + before;
     }
   } else if (wv == 2 && c.k == 0) {  // the segment's end and its chunk's start
     const uint32_t sched = c.ntiles ? c.ntiles : 1u;
@@ -1772,9 +1801,9 @@ ec_write_fast(EncArgs a) {
       if (tid == 0) report_error(a.report, kDevErrTimeout);
       return;
     }
-    write_stream_tables(a, c, ticket, s_rec_abs, s_seg_start, s_seg_end, cs, s_un, s_total);
+    write_stream_tables(a, c, ticket, s_rec_abs, s_seg_start, s_seg_end, cs, s_un, s_total, huff);
   } else {
-    write_stream_tables(a, c, ticket, s_rec_abs, s_seg_start, 0, 0, s_un, 0);
+    write_stream_tables(a, c, ticket, s_rec_abs, s_seg_start, 0, 0, s_un, 0, huff);
   }
   if (n == 0) return;
   const uint4 info = s_info;
@@ -1782,7 +1811,8 @@ ec_write_fast(EncArgs a) {
   const bool valid = (info.w >> 8) & 1u;
   const uint64_t bitmap = s_bitmap;
   const RecLayout L = rec_layout(n, U, U * C, sumw, mode ? nout : 0u, c.rows, D, valid);
-  if (s_rec_abs + L.rec > a.out_cap) {  // cannot happen when out_cap >= the maximum stream size
+  const uint64_t rec_bytes = mode == 2 ? a.w.tile_hsize[ticket] : L.rec;
+  if (s_rec_abs + rec_bytes > a.out_cap) {  // cannot happen when out_cap >= the maximum stream size
     if (tid == 0) report_error(a.report, kDevErrTimeout);
     return;
   }
@@ -1798,32 +1828,44 @@ ec_write_fast(EncArgs a) {
   }
   const uint32_t nblk = U * C;
   const uint32_t rb = c.rows <= 65536 ? 2 : 4;
-  for (uint32_t b = tid; b < nblk; b += kThreads) rec[16 + b] = s_w[s_urow[b / C]][b % C];
-  for (uint32_t b = nblk + tid; b < L.off_refs - 16; b += kThreads) rec[16 + b] = 0;
+  // a Huffman record has no widths: its references start right after the header
+  const uint32_t off_refs = mode == 2 ? 16u : L.off_refs;
+  const uint32_t off_opos = mode == 2 ? (uint32_t)align_up(16 + rb * (n - U), 4) : L.off_opos;
+  const uint32_t off_oval = off_opos + 4 * nout;
+  if (mode == 1) {
+    for (uint32_t b = tid; b < nblk; b += kThreads) rec[16 + b] = s_w[s_urow[b / C]][b % C];
+    for (uint32_t b = nblk + tid; b < L.off_refs - 16; b += kThreads) rec[16 + b] = 0;
+  }
   if (tid < n && !((bitmap >> tid) & 1ull)) {
     const uint32_t j = tid - (uint32_t)__popcll(bitmap & ((1ull << tid) - 1ull));
-    if (rb == 2) reinterpret_cast<uint16_t*>(rec + L.off_refs)[j] = (uint16_t)s_first[tid];
-    else reinterpret_cast<uint32_t*>(rec + L.off_refs)[j] = s_first[tid];
+    if (rb == 2) reinterpret_cast<uint16_t*>(rec + off_refs)[j] = (uint16_t)s_first[tid];
+    else reinterpret_cast<uint32_t*>(rec + off_refs)[j] = s_first[tid];
   }
   {
-    const uint32_t rend = L.off_refs + rb * (n - U);
-    if (tid < L.off_opos - rend) rec[rend + tid] = 0;
+    const uint32_t rend = off_refs + rb * (n - U);
+    if (tid < off_opos - rend) rec[rend + tid] = 0;
+  }
+  if (mode == 1) {
     const uint32_t oend = L.off_oval + 4 * nout;
     if (tid < L.off_pl - oend) rec[oend + tid] = 0;
     const uint64_t pend = L.off_pl + 8ull * sumw;
     if (tid < L.rec - pend) rec[pend + tid] = 0;
   }
-  // staged plane words (loaded above): 16 lanes per block, lane = plane
-  const __amdgpu_buffer_rsrc_t rdst = buf_rsrc(rec + L.off_pl, sumw * 8);
+  if (mode == 1) {
+    // staged plane words (loaded above): 16 lanes per block, lane = plane
+    const __amdgpu_buffer_rsrc_t rdst = buf_rsrc(rec + L.off_pl, sumw * 8);
 #pragma unroll
-  for (uint32_t ps = 0; ps < kPass; ps++) {
-    const uint32_t blk = ps * (kThreads / 16) + (tid >> 4), row = blk / C, j = blk % C;
-    const bool use = blk < n * C && ((bitmap >> row) & 1ull) && b < s_w[row][j];
-    buf_st_u64(rdst, use ? (s_cbase[row][j] + b) * 8 : kOff, wv_[ps]);
+    for (uint32_t ps = 0; ps < kPass; ps++) {
+      const uint32_t blk = ps * (kThreads / 16) + (tid >> 4), row = blk / C, j = blk % C;
+      const bool use = blk < n * C && ((bitmap >> row) & 1ull) && b < s_w[row][j];
+      buf_st_u64(rdst, use ? (s_cbase[row][j] + b) * 8 : kOff, wv_[ps]);
+    }
+  } else if (tid == 0) {
+    a.w.tile_rec[ticket] = s_rec_abs + 1;  // the chunk table and words: ec_write_huff
   }
   if (nout) {
-    uint32_t* opos = reinterpret_cast<uint32_t*>(rec + L.off_opos);
-    uint32_t* oval = reinterpret_cast<uint32_t*>(rec + L.off_oval);
+    uint32_t* opos = reinterpret_cast<uint32_t*>(rec + off_opos);
+    uint32_t* oval = reinterpret_cast<uint32_t*>(rec + off_oval);
     for (uint32_t u = wv; u < U; u += kThreads / 64) {
       const uint32_t i = s_urow[u];
       uint32_t ob = s_obase[i];
@@ -1832,7 +1874,7 @@ ec_write_fast(EncArgs a) {
         const uint64_t om = s_omask[i][j];
         if (om) {
           if ((om >> lane) & 1ull) {
-            const uint32_t o = ob + (uint32_t)__popcll(om & __lanemask_lt());
+            const uint32_t o = ob + (uint32_t)__popcll(om & lanes_below());
             opos[o] = u * D + 64 * j + lane;
             oval[o] = f2u(xt[(uint64_t)i * D + 64 * j + lane]);
           }
@@ -1841,6 +1883,246 @@ ec_write_fast(EncArgs a) {
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Huffman segments: the entropy coder of section III-D ("Huffman Encoding")
+// as a coder of whole segments of the stream, for D = 64*C.  After the size
+// pass (first occurrences known), five launches:
+//   hist    per tile: LDS histogram of the symbols q + 2047 of its
+//           first-occurrence rows, merged into the segment's histogram
+//   books   per segment: the Huffman coder's codebook builder (ec_huffman.hip)
+//   hsize   per tile: the bytes of its Huffman record
+//   choose  per segment: Huffman or bit planes (the plan's coder, sizes)
+//   items   per size block: every tile's stream item and the block's sum again
+// and after the write pass, for every Huffman record, its chunk table and
+// words.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void wave_lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Wave 0 of a workgroup: the tile's first-occurrence rows in order.
+__device__ __forceinline__ void unique_rows(uint64_t bm, uint8_t* urow) {
+  const uint32_t lane = threadIdx.x & 63;
+  if ((bm >> lane) & 1ull) urow[__popcll(bm & lanes_below())] = (uint8_t)lane;
+}
+
+template <int C>
+__global__ void __launch_bounds__(kThreads) ec_hist_tiles(EncArgs a) {
+  constexpr uint32_t D = 64u * C;
+  __shared__ uint32_t h[kHuffTable];
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wv = wave_id();
+  const uint32_t ticket = blockIdx.x;
+  if (ticket == 0 && tid == 0) a.w.hstat[0] = 0;  // the codebook builder's status
+  const TileCoord c = tile_coord(a, ticket);
+  if (c.n == 0 || a.w.seg_eb[c.s] == 0) return;
+  for (uint32_t i = tid; i < kHuffTable; i += kThreads) h[i] = 0;
+  __syncthreads();
+  const uint64_t bm = a.w.tile_bitmap[ticket];
+  const uint16_t* sy = a.w.stage_sym + (uint64_t)ticket * kTileRows * D;
+  for (uint32_t i = wv; i < c.n; i += kThreads / 64) {
+    if (!((bm >> i) & 1ull)) continue;
+#pragma unroll
+    for (uint32_t j = 0; j < C; j++) atomicAdd(&h[sy[i * D + 64 * j + lane]], 1u);
+  }
+  __syncthreads();
+  uint32_t* g = a.w.hhist + (uint64_t)c.s * kHuffTable;
+  for (uint32_t i = tid; i < kHuffTable; i += kThreads)
+    if (h[i]) atomicAdd(&g[i], h[i]);
+}
+
+// Bits of lane L's four symbols E[256 ch + 4L .. + 3] of the tile (0 past nE);
+// with codes (enc: len << 16 | code) also their codes, first code in the high
+// bits of *val.
+template <uint32_t D>
+__device__ __forceinline__ uint32_t lane_codes(const uint16_t* sy, const uint8_t* urow, uint32_t ch,
+                                               uint32_t nE, const uint32_t* enc, uint64_t* val) {
+  const uint32_t e = ch * 256 + 4 * (threadIdx.x & 63);
+  uint32_t bits = 0;
+  uint64_t v = 0;
+  if (e < nE) {  // four symbols of one row: nE and every row start are multiples of 64
+    const uint32_t u = e / D, d = e % D;
+    const uint2 w = *reinterpret_cast<const uint2*>(sy + (uint32_t)urow[u] * D + d);
+    const uint32_t sym[4] = {w.x & 0xFFFFu, w.x >> 16, w.y & 0xFFFFu, w.y >> 16};
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const uint32_t ent = enc[sym[k]], l = ent >> 16;
+      bits += l;
+      v = (v << l) | (ent & 0xFFFFu);
+    }
+  }
+  *val = v;
+  return bits;
+}
+
+template <int C>
+__global__ void __launch_bounds__(kThreads) ec_hsize_tiles(EncArgs a) {
+  constexpr uint32_t D = 64u * C;
+  __shared__ uint32_t s_enc[kHuffTable];
+  __shared__ uint8_t s_urow[kTileRows];
+  __shared__ uint32_t s_words[kThreads / 64];
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wv = wave_id();
+  const uint32_t ticket = blockIdx.x;
+  const TileCoord c = tile_coord(a, ticket);
+  if (ticket == 0 && tid == 0 && a.w.hstat[0] != 0) report_error(a.report, kDevErrTimeout);
+  if (c.n == 0 || a.w.seg_eb[c.s] == 0) {
+    if (tid == 0) a.w.tile_hsize[ticket] = 0;
+    return;
+  }
+  const uint32_t* enc = a.w.henc + (uint64_t)c.s * kHuffTable;
+  for (uint32_t i = tid; i < kHuffTable; i += kThreads) s_enc[i] = enc[i];
+  const uint64_t bm = a.w.tile_bitmap[ticket];
+  if (wv == 0) unique_rows(bm, s_urow);
+  __syncthreads();
+  const uint32_t U = (uint32_t)__popcll(bm), nE = U * D, nch = (nE + 255) / 256;
+  const uint16_t* sy = a.w.stage_sym + (uint64_t)ticket * kTileRows * D;
+  uint32_t words = 0;
+  for (uint32_t ch = wv; ch < nch; ch += kThreads / 64) {
+    uint64_t v;
+    const uint32_t bits = wave_sum_u32(lane_codes<D>(sy, s_urow, ch, nE, s_enc, &v));
+    words += (bits + 31) / 32;
+  }
+  if (lane == 0) s_words[wv] = words;
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t w = 0;
+    for (uint32_t q = 0; q < kThreads / 64; q++) w += s_words[q];
+    const uint32_t rb = c.rows <= 65536 ? 2 : 4, nout = a.w.tile_nout[ticket];
+    const uint32_t off_ct = (uint32_t)align_up(16 + rb * (c.n - U), 4) + 8 * nout;
+    a.w.tile_hsize[ticket] = (uint32_t)align_up(off_ct + 4ull * (nch + 1) + 4ull * w, 16);
+  }
+}
+
+// One wave per segment: Huffman (with coder 2, or with coder 3 when strictly
+// smaller) or bit planes.  Both forms share the header and tile directory;
+// the Huffman form adds the padded codebook.
+__global__ void __launch_bounds__(kThreads) ec_seg_choose(EncArgs a) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t s = blockIdx.x * (kThreads / 64) + wave_id();
+  if (s >= a.sh.nseg) return;
+  if (a.w.seg_eb[s] == 0 || a.coder == kCoderBitpack) {
+    if (lane == 0) a.w.seg_coder[s] = 0;
+    return;
+  }
+  const uint32_t D = a.sh.D, pch = s / a.sh.T;
+  const uint32_t rows = chunk_row0(a.sh, pch + 1) - chunk_row0(a.sh, pch);
+  const uint32_t nt = (rows + kTileRows - 1) / kTileRows, b = a.w.seg_tile_base[s];
+  uint64_t bp = 0, hf = 0;
+  for (uint32_t k = lane; k < nt; k += 64) {
+    const uint32_t ticket = b + k, n = min(kTileRows, rows - k * kTileRows);
+    const uint4 info = reinterpret_cast<const uint4*>(a.w.tile_info)[ticket];
+    const RecLayout L = rec_layout(n, info.x, info.x * (D / 64), info.z, a.w.tile_nout[ticket], rows, D, true);
+    const uint64_t raw = 16 + align_up(4ull * n * D, 16), h = a.w.tile_hsize[ticket];
+    bp += L.rec;
+    hf += h < raw ? h : raw;
+  }
+  bp = wave_sum_u64(bp);
+  hf = wave_sum_u64(hf) + align_up(book_bytes(a.w.hbooks + (uint64_t)s * kBookStride), 16);
+  if (lane == 0) a.w.seg_coder[s] = (a.coder == kCoderHuffman || hf < bp) ? 1u : 0u;
+}
+
+// One wave per size block: the items (record bytes plus the tables a tile
+// writes first) of a Huffman segment's tiles, their record summaries, and
+// the block's sum, again (bit-plane segments keep the size pass's values).
+__global__ void __launch_bounds__(64) ec_items(EncArgs a) {
+  const uint32_t lane = threadIdx.x;
+  const uint32_t ticket = blockIdx.x * kBlockTiles + lane;
+  uint64_t item = 0;
+  if (lane < kBlockTiles && ticket < a.sh.ntiles) {
+    const TileCoord c = tile_coord(a, ticket);
+    item = a.w.tile_status[ticket];
+    if (a.w.seg_coder[c.s]) {
+      const uint64_t raw = c.n ? 16 + align_up(4ull * c.n * a.sh.D, 16) : 0;
+      const uint32_t h = a.w.tile_hsize[ticket];
+      const bool coded = c.n && h < raw;
+      const uint64_t pre = c.k == 0 ? seg_prefix_bytes(c.ntiles) +
+                                           align_up(book_bytes(a.w.hbooks + (uint64_t)c.s * kBookStride), 16) +
+                                           (c.t == 0 ? align_up(8ull * a.sh.T, 16) : 0)
+                                     : 0;
+      item = (coded ? h : raw) + pre;
+      a.w.tile_status[ticket] = item;
+      uint4 info = reinterpret_cast<const uint4*>(a.w.tile_info)[ticket];
+      info.y = coded ? a.w.tile_nout[ticket] : 0u;
+      info.w = (coded ? 2u : 0u) | 0x100u;
+      reinterpret_cast<uint4*>(a.w.tile_info)[ticket] = info;
+    }
+  }
+  item = wave_sum_u64(item);
+  if (lane == 0) a.w.block_status[blockIdx.x] = item;
+}
+
+// Chunk table and words of a Huffman record (the write pass wrote its header,
+// references and outliers): per wave and chunk, the lanes' code bits are
+// placed by a wave prefix sum and ORed into the wave's LDS buffer of 96
+// words, which is then stored whole; the record's padding is zeroed.
+template <int C>
+__global__ void __launch_bounds__(kThreads) ec_write_huff(EncArgs a) {
+  constexpr uint32_t D = 64u * C;
+  constexpr uint32_t kMaxCh = kTileRows * D / 256;
+  __shared__ uint32_t s_enc[kHuffTable];
+  __shared__ uint32_t s_buf[kThreads / 64][96];
+  __shared__ uint32_t s_cw[kMaxCh + 1];
+  __shared__ uint8_t s_urow[kTileRows];
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wv = wave_id();
+  const uint32_t ticket = blockIdx.x;
+  const uint4 info = reinterpret_cast<const uint4*>(a.w.tile_info)[ticket];
+  if ((info.w & 0xFFu) != 2u) return;
+  const TileCoord c = tile_coord(a, ticket);
+  const uint32_t n = c.n, U = info.x, nout = info.y;
+  uint8_t* rec = a.out + (a.w.tile_rec[ticket] - 1);
+  const uint32_t* enc = a.w.henc + (uint64_t)c.s * kHuffTable;
+  for (uint32_t i = tid; i < kHuffTable; i += kThreads) s_enc[i] = enc[i];
+  const uint64_t bm = a.w.tile_bitmap[ticket];
+  if (wv == 0) unique_rows(bm, s_urow);
+  __syncthreads();
+  const uint32_t rb = c.rows <= 65536 ? 2 : 4;
+  const uint32_t off_ct = (uint32_t)align_up(16 + rb * (n - U), 4) + 8 * nout;
+  const uint32_t nE = U * D, nch = (nE + 255) / 256, off_w = off_ct + 4 * (nch + 1);
+  const uint16_t* sy = a.w.stage_sym + (uint64_t)ticket * kTileRows * D;
+  for (uint32_t ch = wv; ch < nch; ch += kThreads / 64) {  // words of every chunk
+    uint64_t v;
+    const uint32_t bits = wave_sum_u32(lane_codes<D>(sy, s_urow, ch, nE, s_enc, &v));
+    if (lane == 0) s_cw[ch] = (bits + 31) / 32;
+  }
+  __syncthreads();
+  if (wv == 0) {  // word offsets of the chunks (at most 64) and the chunk table
+    const uint32_t cw = lane < nch ? s_cw[lane] : 0u;
+    const uint32_t inc = wave_incl_u32(cw);
+    const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+    uint32_t* ct = reinterpret_cast<uint32_t*>(rec + off_ct);
+    if (lane < nch) {
+      ct[lane] = inc - cw;
+      s_cw[lane] = inc - cw;
+    }
+    if (lane == 0) {
+      ct[nch] = total;
+      s_cw[kMaxCh] = total;
+    }
+  }
+  __syncthreads();
+  uint32_t* buf = s_buf[wv];
+  uint32_t* words = reinterpret_cast<uint32_t*>(rec + off_w);
+  for (uint32_t ch = wv; ch < nch; ch += kThreads / 64) {
+    buf[lane] = 0;
+    if (lane < 32) buf[64 + lane] = 0;
+    wave_lds_wait();
+    uint64_t v;
+    const uint32_t L = lane_codes<D>(sy, s_urow, ch, nE, s_enc, &v);
+    const uint32_t inc = wave_incl_u32(L), start = inc - L;
+    if (L) {  // the bits [start, start + L) of the chunk, first bit in bit 31 of its word
+      const uint32_t w0 = start >> 5, S = (start & 31u) + L;
+      for (uint32_t k = 0; 32 * k < S; k++) {
+        const int sh = (int)S - 32 * (int)(k + 1);
+        const uint32_t part = sh >= 0 ? (uint32_t)(v >> sh) : (uint32_t)(v << -sh);
+        atomicOr(&buf[w0 + k], part);
+      }
+    }
+    wave_lds_wait();
+    const uint32_t cw = ((uint32_t)__builtin_amdgcn_readlane((int)inc, 63) + 31) / 32;
+    for (uint32_t i = lane; i < cw; i += 64) words[s_cw[ch] + i] = buf[i];
+  }
+  // zero padding after the words up to the record's 16-byte end
+  const uint32_t end = off_w + 4 * s_cw[kMaxCh], pad = (uint32_t)align_up(end, 16) - end;
+  if (tid < pad) rec[end + tid] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -1942,12 +2224,14 @@ struct DecTile {
   uint64_t bitmap;
   uint32_t n, U, nout, mode, ok;
   uint32_t nblk, off_refs, off_opos, off_oval, off_pl;
+  uint32_t nch, off_ct, off_w;  // Huffman records: chunks, chunk table, words
 };
 
 struct DecShared {
   uint32_t ok, seg, tile, n, rows, ntiles, valid, bad;
+  uint32_t seg_ok, hseg;  // the segment's headers passed; it is a Huffman segment
   float eb;
-  uint64_t seg_off, seg_bytes, total;
+  uint64_t seg_off, seg_bytes, total, rec_lo;
   DecTile tl;
   uint32_t part[kThreads / 64];
 };
@@ -1976,14 +2260,32 @@ __device__ __forceinline__ uint32_t rd32(const uint8_t* p) {
 
 // Locate and check tile record k of a segment; every read is bounds-checked
 // against the segment.
+// The stream header's version and coder: 1 bit planes only, 2 and 3 with
+// Huffman segments (decodable only by a plan with the Huffman tables).
+__device__ __forceinline__ bool header_coder_ok(uint32_t w, uint32_t huff, uint32_t& coder) {
+  coder = w >> 16;
+  return (w & 0xFFFFu) == kVersion && coder >= kCoderBitpack && coder <= kCoderAuto &&
+         (huff || coder == kCoderBitpack);
+}
+// A segment's flags: bit 0 eb valid, bit 1 Huffman segment (only with bit 0,
+// never in a coder-1 stream, always for a valid segment of a coder-2 stream).
+__device__ __forceinline__ bool seg_flags_ok(uint32_t flags, uint32_t coder) {
+  if (flags > 3 || flags == 2) return false;
+  const bool hs = (flags & 2u) != 0;
+  return !(hs && coder == kCoderBitpack) && !(coder == kCoderHuffman && (flags & 1u) && !hs);
+}
+
+// Locate and check tile record k of a segment whose records start at rec_lo
+// or later (after the tile directory, and the codebook of a Huffman segment);
+// every read is bounds-checked against the segment.
 __device__ DecTile locate_tile(const uint8_t* seg, uint64_t seg_bytes, uint32_t ntiles,
-                               uint32_t rows, uint32_t k, uint32_t D, bool valid) {
+                               uint32_t rows, uint32_t k, uint32_t D, bool valid, uint64_t rec_lo,
+                               bool hseg) {
   DecTile r{};
   r.ok = 0;
   if (k >= ntiles) return r;
-  const uint64_t prefix = 32 + align_up(4ull * ntiles, 16);
   uint32_t off = rd32(seg + 32 + 4ull * k);
-  if (off < prefix || (off & 15u) || (uint64_t)off + 16 > seg_bytes) return r;
+  if (off < rec_lo || (off & 15u) || (uint64_t)off + 16 > seg_bytes) return r;
   r.rec = seg + off;
   r.avail = seg_bytes - off;
   r.n = min(kTileRows, rows - k * kTileRows);
@@ -1998,7 +2300,23 @@ __device__ DecTile locate_tile(const uint8_t* seg, uint64_t seg_bytes, uint32_t 
   if (!valid && (r.bitmap != 0 || r.mode != 0)) return r;
   if (r.mode == 0) {
     if (r.nout != 0 || 16 + 4ull * r.n * D > r.avail) return r;
-  } else if (r.mode == 1) {
+  } else if (r.mode == 2) {
+    if (!hseg) return r;
+    uint64_t nE = (uint64_t)r.U * D;
+    if (r.nout > nE) return r;
+    uint32_t rb = rows <= 65536 ? 2 : 4;
+    uint64_t off_opos = align_up(16 + (uint64_t)rb * (r.n - r.U), 4);
+    uint64_t off_ct = off_opos + 8ull * r.nout;
+    uint64_t nch = (nE + 255) / 256;
+    uint64_t off_w = off_ct + 4 * (nch + 1);
+    if (off_w > r.avail) return r;
+    r.off_refs = 16;
+    r.off_opos = (uint32_t)off_opos;
+    r.off_oval = (uint32_t)(off_opos + 4ull * r.nout);
+    r.off_ct = (uint32_t)off_ct;
+    r.nch = (uint32_t)nch;
+    r.off_w = (uint32_t)off_w;
+  } else if (r.mode == 1 && !hseg) {
     uint64_t nE = (uint64_t)r.U * D;
     if (r.nout > nE) return r;
     uint64_t nblk = (nE + 63) / 64;
@@ -2024,9 +2342,8 @@ __device__ DecTile locate_tile(const uint8_t* seg, uint64_t seg_bytes, uint32_t 
 // and 5) must equal the sums over the segment's tile records.  Entries that
 // fail their own checks are skipped here (their tiles' workgroups report
 // them); every read stays inside the segment.
-__device__ bool seg_totals_ok(const uint8_t* sg, uint64_t sbytes, uint32_t ntiles) {
+__device__ bool seg_totals_ok(const uint8_t* sg, uint64_t sbytes, uint32_t ntiles, uint64_t prefix) {
   const uint32_t lane = threadIdx.x & 63;
-  const uint64_t prefix = 32 + align_up(4ull * ntiles, 16);
   uint32_t u = 0, o = 0;
   for (uint32_t j = lane; j < ntiles; j += 64) {
     const uint32_t off = reinterpret_cast<const uint32_t*>(sg + 32)[j];
@@ -2137,11 +2454,12 @@ __global__ void __launch_bounds__(kThreads) ec_decode_kernel(DecArgs a) {
     uint32_t ok = 1;
     const uint8_t* in = a.in;
     uint64_t total = 0;
+    uint32_t coder = 0;
     if (a.cap < 64) ok = 0;
     if (ok) {
       const uint32_t* h = reinterpret_cast<const uint32_t*>(in);
       total = rd64(in + 48);
-      ok = h[0] == kMagic && h[1] == (kVersion | (kCoderBitpack << 16)) && h[2] == T &&
+      ok = h[0] == kMagic && header_coder_ok(h[1], 0u, coder) && h[2] == T &&
            h[3] == B && h[4] == D && h[5] == P && h[6] == kTileRows && h[7] <= 1 &&
            rd64(in + 40) == 4ull * T * B * D && rd64(in + 56) == 0 && total <= a.cap;
     }
@@ -2164,17 +2482,19 @@ __global__ void __launch_bounds__(kThreads) ec_decode_kernel(DecArgs a) {
       float eb = __uint_as_float(rd32(sg + 8));
       sb = rd64(sg + 24);
       int valid = isfinite(eb) && eb > 0.0f && isfinite(eb + eb);
-      if (rd32(sg) != rows || rd32(sg + 4) != nt || flags > 1 || (int)flags != valid ||
-          sb > cb - so || sb < 32 + align_up(4ull * nt, 16))
+      // (a coder-1 stream: no Huffman segment)
+      if (rd32(sg) != rows || rd32(sg + 4) != nt || !seg_flags_ok(flags, coder) ||
+          (int)(flags & 1u) != valid || sb > cb - so || sb < 32 + align_up(4ull * nt, 16))
         ok = 0;
       sh.eb = eb;
-      sh.valid = flags;
+      sh.valid = flags & 1u;
     }
     sh.seg_off = chunk + so;
     sh.seg_bytes = sb;
     sh.total = total;
+    sh.rec_lo = 32 + align_up(4ull * nt, 16);
     if (ok && nt) {
-      DecTile tl = locate_tile(in + chunk + so, sb, nt, rows, k, D, sh.valid != 0);
+      DecTile tl = locate_tile(in + chunk + so, sb, nt, rows, k, D, sh.valid != 0, sh.rec_lo, false);
       ok = tl.ok;
       sh.tl = tl;
     }
@@ -2182,7 +2502,7 @@ __global__ void __launch_bounds__(kThreads) ec_decode_kernel(DecArgs a) {
   }
   __syncthreads();
   if (wv == 0 && sh.ok) {  // a segment's first tile checks its totals, tile 0 the chunk sizes
-    bool good = sh.tile != 0 || seg_totals_ok(a.in + sh.seg_off, sh.seg_bytes, sh.ntiles);
+    bool good = sh.tile != 0 || seg_totals_ok(a.in + sh.seg_off, sh.seg_bytes, sh.ntiles, sh.rec_lo);
     if (ticket == 0) good = good && chunk_totals_ok(a.in, P, sh.total);
     if (!good && lane == 0) report_error(a.report, kDevErrCorrupt);
   }
@@ -2275,7 +2595,7 @@ __global__ void __launch_bounds__(kThreads) ec_decode_kernel(DecArgs a) {
                                           : kBad;
       } else {
         const uint32_t k2 = ref / kTileRows, i2 = ref % kTileRows;
-        DecTile t2 = locate_tile(sg, sbytes, sh.ntiles, rows, k2, D, true);
+        DecTile t2 = locate_tile(sg, sbytes, sh.ntiles, rows, k2, D, true, sh.rec_lo, false);
         src = kExt | i;
         if (!t2.ok || !((t2.bitmap >> i2) & 1ull)) {
           src = kBad;
@@ -2385,13 +2705,13 @@ __device__ void dec_locate(const DecArgs& a, const uint8_t* in, uint32_t ticket,
   sh.ntiles = nt;
   sh.n = nt ? min(kTileRows, rows - k * kTileRows) : 0;
   sh.bad = 0;
-  uint32_t ok = 1;
+  uint32_t ok = 1, coder = 0;
   uint64_t total = 0;
   if (a.cap < 64) ok = 0;
   if (ok) {
     const uint32_t* h = reinterpret_cast<const uint32_t*>(in);
     total = rd64(in + 48);
-    ok = h[0] == kMagic && h[1] == (kVersion | (kCoderBitpack << 16)) && h[2] == T &&
+    ok = h[0] == kMagic && header_coder_ok(h[1], a.huff, coder) && h[2] == T &&
          h[3] == B && h[4] == D && h[5] == P && h[6] == kTileRows && h[7] <= 1 &&
          rd64(in + 40) == 4ull * T * B * D && rd64(in + 56) == 0 && total <= a.cap;
   }
@@ -2408,24 +2728,37 @@ __device__ void dec_locate(const DecArgs& a, const uint8_t* in, uint32_t ticket,
     so = rd64(in + chunk + 8ull * t);
     if (so < align_up(8ull * T, 16) || (so & 15u) || so + 32 > cb) ok = 0;
   }
+  sh.hseg = 0;
+  sh.rec_lo = 32 + align_up(4ull * nt, 16);
   if (ok) {
     const uint8_t* sg = in + chunk + so;
     uint32_t flags = rd32(sg + 12);
     float eb = __uint_as_float(rd32(sg + 8));
     sb = rd64(sg + 24);
     int valid = isfinite(eb) && eb > 0.0f && isfinite(eb + eb);
-    if (rd32(sg) != rows || rd32(sg + 4) != nt || flags > 1 || (int)flags != valid ||
-        sb > cb - so || sb < 32 + align_up(4ull * nt, 16))
+    if (rd32(sg) != rows || rd32(sg + 4) != nt || !seg_flags_ok(flags, coder) ||
+        (int)(flags & 1u) != valid || sb > cb - so || sb < sh.rec_lo)
       ok = 0;
     sh.eb = eb;
-    sh.valid = flags;
+    sh.valid = flags & 1u;
+    sh.hseg = (flags >> 1) & 1u;
+    if (ok && sh.hseg) {  // records start after the codebook
+      if (sh.rec_lo + 4 > sb) {
+        ok = 0;
+      } else {
+        const uint32_t bw = rd32(sg + sh.rec_lo), lo = bw & 0xFFFFu, hi = bw >> 16;
+        sh.rec_lo += align_up(hi < lo ? 4u : 4u + (hi - lo + 2) / 2, 16);
+        if (sh.rec_lo > sb) ok = 0;
+      }
+    }
   }
+  sh.seg_ok = ok;
   sh.seg_off = chunk + so;
   sh.seg_bytes = sb;
   sh.total = total;
   rec_off = 0;
   if (ok && nt) {
-    DecTile tl = locate_tile(in + chunk + so, sb, nt, rows, k, D, sh.valid != 0);
+    DecTile tl = locate_tile(in + chunk + so, sb, nt, rows, k, D, sh.valid != 0, sh.rec_lo, sh.hseg != 0);
     ok = tl.ok;
     sh.tl = tl;
     rec_off = (uint64_t)(tl.rec - in);
@@ -2530,7 +2863,7 @@ __device__ __forceinline__ uint32_t sum_widths(__amdgpu_buffer_rsrc_t rseg, uint
 // ((L >> 4) & 1); the encoder's transpose, its own inverse, leaves both
 // blocks' zigzag codes of element L in lane L.
 constexpr uint32_t kRowPlanes = 0, kRowRawRef = 1, kRowBad = 2, kRowOutliers = 0x100;
-constexpr uint32_t kTileOk = 1, kTileRaw = 2;
+constexpr uint32_t kTileOk = 1, kTileRaw = 2, kTileHuff = 4;
 
 // LDS of the decoder's index step (one tile)
 template <int C>
@@ -2583,7 +2916,7 @@ __device__ __forceinline__ void index_tile(const uint8_t* __restrict__ in, const
     return;
   }
   {  // a segment's first tile checks its totals, tile 0 the chunk sizes
-    bool good = k != 0 || seg_totals_ok(in + seg_off, sbytes, sh.ntiles);
+    bool good = k != 0 || seg_totals_ok(in + seg_off, sbytes, sh.ntiles, sh.rec_lo);
     if (ticket == 0) good = good && chunk_totals_ok(in, a.sh.P, sh.total);
     if (!good && lane == 0) report_error(a.report, kDevErrCorrupt);
   }
@@ -2598,6 +2931,11 @@ __device__ __forceinline__ void index_tile(const uint8_t* __restrict__ in, const
   const uint32_t mode = sh.tl.mode, U = sh.tl.U, nout = sh.tl.nout;
   if (mode == 0) {
     flags = kTileOk | kTileRaw;
+    put_tile();
+    return;
+  }
+  if (mode == 2) {  // a Huffman record: ec_decode_huff and ec_fill_refs
+    flags = kTileOk | kTileHuff;
     put_tile();
     return;
   }
@@ -2695,7 +3033,7 @@ __device__ __forceinline__ void index_tile(const uint8_t* __restrict__ in, const
       } else {
         local = false;
         const uint32_t k2 = ref / kTileRows, i2 = ref % kTileRows;
-        DecTile t2 = locate_tile(sg, sbytes, sh.ntiles, rows, k2, D, true);
+        DecTile t2 = locate_tile(sg, sbytes, sh.ntiles, rows, k2, D, true, sh.rec_lo, false);
         if (!t2.ok || !((t2.bitmap >> i2) & 1ull)) {
           kind = kRowBad;
         } else {
@@ -2862,6 +3200,7 @@ __global__ void __launch_bounds__(kThreads) ec_decode_fast(const uint8_t* __rest
     for (uint32_t i = tid; i < n * D; i += kThreads) yt[i] = 0.0f;
     return;
   }
+  if (flags & kTileHuff) return;  // decoded by ec_decode_huff and ec_fill_refs
   const uint8_t* sg = in + (((uint64_t)d0.w << 32) | d0.z);
   if (flags & kTileRaw) {  // RAW: rows verbatim
     const uint8_t* rec = in + (((uint64_t)d1.y << 32) | d1.x);
@@ -2946,6 +3285,189 @@ __global__ void __launch_bounds__(kThreads) ec_decode_fast(const uint8_t* __rest
 }
 
 // ---------------------------------------------------------------------------
+// decoding Huffman segments
+//   books    per segment (one wave): the codebook of a Huffman segment copied
+//            out of the stream (zero-padded; a placeholder for the others),
+//            then the Huffman coder's table builder (ec_huffman.hip)
+//   (the bit-plane decoder skips Huffman tiles)
+//   decode   per Huffman tile: chunks decoded one per lane by table lookups
+//            into LDS, first-occurrence rows dequantized with their outliers
+//   refs     per Huffman tile: repeated rows copied from their first
+//            occurrences' decoded rows (re-quantized from a RAW record)
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kThreads) ec_hbook_copy(DecArgs a) {
+  __shared__ DecShared shs[kThreads / 64];
+  const uint32_t lane = threadIdx.x & 63, wv = wave_id();
+  const uint32_t s = blockIdx.x * (kThreads / 64) + wv;
+  if (blockIdx.x == 0 && threadIdx.x == 0) a.w.hstat[2] = 0;  // the table builder's zero word
+  if (s >= a.sh.nseg) return;
+  uint64_t ro;
+  dec_locate(a, a.in, a.seg_tile_base[s], shs[wv], ro);
+  wave_lds_wait();
+  const DecShared& sh = shs[wv];
+  uint8_t* bk = a.w.hbooks + (uint64_t)s * kBookStride;
+  uint64_t avail = 0;
+  const uint8_t* src = a.in;
+  if (sh.seg_ok && sh.hseg) {
+    const uint64_t at = 32 + align_up(4ull * sh.ntiles, 16);  // after the tile directory
+    src = a.in + sh.seg_off + at;
+    avail = min(sh.seg_bytes - at, (uint64_t)kBookStride);
+  }
+  for (uint32_t i = lane; i < kBookStride; i += 64)
+    bk[i] = i < avail ? src[i] : (uint8_t)(i == 0 && avail == 0 ? 1 : 0);
+}
+
+template <int C>
+__global__ void __launch_bounds__(kThreads) ec_decode_huff(const uint8_t* __restrict__ in,
+                                                          float* __restrict__ yout, DecArgs a) {
+  constexpr uint32_t D = 64u * C, kMaxCh = kTileRows * D / 256;
+  __shared__ DecShared sh;
+  __shared__ uint16_t s_lut[kHuffTable];
+  __shared__ __align__(16) uint16_t s_sym[kTileRows * D];
+  __shared__ uint32_t s_ct[kMaxCh + 1];
+  __shared__ uint8_t s_urow[kTileRows];
+  __shared__ uint32_t s_bad;
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wv = wave_id();
+  const uint32_t ticket = blockIdx.x;
+  if (wv == 0) {
+    uint64_t ro;
+    dec_locate(a, in, ticket, sh, ro);
+  }
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  // a Huffman segment's codebook is checked by the segment's first tile
+  if (tid == 0 && sh.seg_ok && sh.hseg && sh.tile == 0) {
+    const uint8_t* bk = a.w.hbooks + (uint64_t)sh.seg * kBookStride;
+    const bool empty = bk[0] == 1 && bk[1] == 0 && bk[2] == 0 && bk[3] == 0;
+    if (!a.w.hvalid[sh.seg] && !empty) report_error(a.report, kDevErrCorrupt);
+  }
+  if (!sh.ok || sh.n == 0 || sh.tl.mode != 2) return;  // checked and reported elsewhere
+  const DecTile tl = sh.tl;
+  const uint32_t seg = sh.seg, n = sh.n, U = tl.U, nout = tl.nout, nE = U * D, nch = tl.nch;
+  const bool book_ok = a.w.hvalid[seg] != 0;
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(a.w.hlut + (uint64_t)seg * kHuffTable);
+    for (uint32_t i = tid; i < kHuffTable * 2 / 16; i += kThreads) reinterpret_cast<uint4*>(s_lut)[i] = src[i];
+  }
+  if (wv == 0) unique_rows(tl.bitmap, s_urow);
+  const uint32_t* ct = reinterpret_cast<const uint32_t*>(tl.rec + tl.off_ct);
+  for (uint32_t i = tid; i <= nch; i += kThreads) s_ct[i] = ct[i];
+  __syncthreads();
+  const uint64_t wavail = (tl.avail - tl.off_w) / 4;  // words the segment still holds
+  const uint32_t* words = reinterpret_cast<const uint32_t*>(tl.rec + tl.off_w);
+  bool bad = (nE > 0 && !book_ok) || (tid == 0 && s_ct[0] != 0);
+  if (tid < nch && !bad) {
+    // every chunk ends exactly in its last word (at most 96 words for 256 codes of
+    // at most 12 bits), the next one starts right after it
+    const uint32_t w0 = s_ct[tid], w1 = s_ct[tid + 1];
+    const uint32_t rem = min(256u, nE - 256 * tid);
+    bad = !(w0 < w1 && w1 - w0 <= 96u && (uint64_t)w1 <= wavail) ||
+          !hd::decode_chunk(words + w0, w1 - w0, rem, s_lut, s_sym + 256 * tid, true);
+  }
+  if (wv == 0) {  // outlier positions index E and strictly increase
+    const uint32_t* op = reinterpret_cast<const uint32_t*>(tl.rec + tl.off_opos);
+    bool obad = false;
+    for (uint32_t g = lane; g < nout; g += 64) obad |= op[g] >= nE || (g > 0 && op[g - 1] >= op[g]);
+    bad = bad || obad;
+  }
+  if (bad) s_bad = 1;
+  __syncthreads();
+  float* yt = yout + ((uint64_t)(seg % a.sh.T) * a.sh.B + chunk_row0(a.sh, seg / a.sh.T) +
+                      (uint64_t)sh.tile * kTileRows) * D;
+  if (s_bad) {
+    for (uint32_t i = tid; i < n * D; i += kThreads) yt[i] = 0.0f;
+    if (tid == 0) report_error(a.report, kDevErrCorrupt);
+    return;
+  }
+  const float s2 = sh.eb + sh.eb;
+  const uint32_t* opos = reinterpret_cast<const uint32_t*>(tl.rec + tl.off_opos);
+  const uint32_t* oval = reinterpret_cast<const uint32_t*>(tl.rec + tl.off_oval);
+  for (uint32_t u = wv; u < U; u += kThreads / 64) {
+    float v[C];
+#pragma unroll
+    for (uint32_t j = 0; j < C; j++) v[j] = (float)((int)s_sym[u * D + 64 * j + lane] - 2047) * s2;
+    patch_outliers<C>(v, u * D, opos, oval, nout);
+    float* y = yt + (uint64_t)s_urow[u] * D;
+#pragma unroll
+    for (uint32_t j = 0; j < C; j++) __builtin_nontemporal_store(v[j], &y[64 * j + lane]);
+  }
+}
+
+// Rows of a Huffman tile that repeat an earlier row: their first occurrences
+// are decoded (this or an earlier Huffman tile) or stored RAW (re-quantized).
+constexpr uint32_t kRefNone = 0, kRefCopy = 1, kRefRaw = 2, kRefBad = 3;
+template <int C>
+__global__ void __launch_bounds__(kThreads) ec_fill_refs(const uint8_t* __restrict__ in,
+                                                        float* __restrict__ yout, DecArgs a) {
+  constexpr uint32_t D = 64u * C;
+  __shared__ DecShared sh;
+  __shared__ uint32_t s_kind[kTileRows], s_src[kTileRows], s_roff[kTileRows];
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wv = wave_id();
+  const uint32_t ticket = blockIdx.x;
+  if (wv == 0) {
+    uint64_t ro;
+    dec_locate(a, in, ticket, sh, ro);
+  }
+  __syncthreads();
+  if (!sh.ok || sh.n == 0 || sh.tl.mode != 2) return;
+  const DecTile tl = sh.tl;
+  const uint32_t seg = sh.seg, k = sh.tile, n = sh.n, rows = sh.rows;
+  const uint8_t* sg = in + sh.seg_off;
+  if (wv == 0) {
+    uint32_t kind = kRefNone, src = 0, roff = 0;
+    if (lane < n && !((tl.bitmap >> lane) & 1ull)) {
+      const uint32_t rb = rows <= 65536 ? 2 : 4;
+      const uint32_t j = lane - (uint32_t)__popcll(tl.bitmap & lanes_below());
+      const uint32_t ref = rb == 2 ? reinterpret_cast<const uint16_t*>(tl.rec + 16)[j]
+                                   : reinterpret_cast<const uint32_t*>(tl.rec + 16)[j];
+      const uint32_t k2 = ref / kTileRows, i2 = ref % kTileRows;
+      kind = kRefBad;
+      src = ref;
+      if (ref >= k * kTileRows + lane) {
+        // a reference must name an earlier row
+      } else if (k2 == k) {
+        if ((tl.bitmap >> i2) & 1ull) kind = kRefCopy;
+      } else {
+        const DecTile t2 = locate_tile(sg, sh.seg_bytes, sh.ntiles, rows, k2, D, true, sh.rec_lo, true);
+        if (t2.ok && ((t2.bitmap >> i2) & 1ull)) {
+          kind = t2.mode == 0 ? kRefRaw : kRefCopy;
+          roff = (uint32_t)(t2.rec - sg);
+        }
+      }
+    }
+    s_kind[lane] = kind;
+    s_src[lane] = src;
+    s_roff[lane] = roff;
+  }
+  __syncthreads();
+  float* yseg = yout + ((uint64_t)(seg % a.sh.T) * a.sh.B + chunk_row0(a.sh, seg / a.sh.T)) * D;
+  const float eb = sh.eb, s2 = eb + eb;
+  bool bad = false;
+  for (uint32_t i = wv; i < n; i += kThreads / 64) {
+    const uint32_t kind = s_kind[i], src = s_src[i];
+    if (kind == kRefNone) continue;
+    float v[C];
+#pragma unroll
+    for (uint32_t j = 0; j < C; j++) {
+      if (kind == kRefCopy) {
+        v[j] = yseg[(uint64_t)src * D + 64 * j + lane];
+      } else if (kind == kRefRaw) {
+        const float xv = reinterpret_cast<const float*>(sg + s_roff[i] + 16)[(src % kTileRows) * D + 64 * j + lane];
+        int q;
+        v[j] = quantize(xv, eb, s2, q) ? xv : (float)q * s2;
+      } else {
+        v[j] = 0.0f;
+      }
+    }
+    bad = bad || kind == kRefBad;
+    float* y = yseg + ((uint64_t)k * kTileRows + i) * D;
+#pragma unroll
+    for (uint32_t j = 0; j < C; j++) y[64 * j + lane] = v[j];
+  }
+  if (bad && lane == 0) report_error(a.report, kDevErrCorrupt);
+}
+
+// ---------------------------------------------------------------------------
 // the library's own scratch for ec_compress_static (callers that cannot
 // allocate): one copy per device, alive until the process ends
 // ---------------------------------------------------------------------------
@@ -3021,6 +3543,28 @@ hipError_t launch_encode(const EncArgs& a, hipStream_t s) {
 
 bool encode_has_assembly(uint32_t D) { return D == 64 || D == 128 || D == 256; }
 
+hipError_t launch_assemble_size(const EncArgs& a, hipStream_t s) {
+  const dim3 blocks((a.sh.ntiles + kBlockTiles - 1) / kBlockTiles), sblock(kSizeThreads);
+  switch (a.sh.D) {
+    case 64: hipLaunchKernelGGL(ec_size_fast<1>, blocks, sblock, 0, s, a); break;
+    case 128: hipLaunchKernelGGL(ec_size_fast<2>, blocks, sblock, 0, s, a); break;
+    case 256: hipLaunchKernelGGL(ec_size_fast<4>, blocks, sblock, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_assemble_write(const EncArgs& a, hipStream_t s) {
+  const dim3 tiles(a.sh.ntiles), block(kThreads);
+  switch (a.sh.D) {
+    case 64: hipLaunchKernelGGL(ec_write_fast<1>, tiles, block, 0, s, a); break;
+    case 128: hipLaunchKernelGGL(ec_write_fast<2>, tiles, block, 0, s, a); break;
+    case 256: hipLaunchKernelGGL(ec_write_fast<4>, tiles, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_assemble(const EncArgs& a, hipStream_t s) {
   const dim3 tiles(a.sh.ntiles), blocks((a.sh.ntiles + kBlockTiles - 1) / kBlockTiles);
   const dim3 block(kThreads), sblock(kSizeThreads);
@@ -3046,6 +3590,65 @@ hipError_t launch_assemble(const EncArgs& a, hipStream_t s) {
 hipError_t launch_distinct_raw(const EncArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(ec_distinct_raw, dim3(a.sh.ntiles), dim3(kThreads), 0, s, a);
   hipLaunchKernelGGL(ec_distinct_sum, dim3((a.sh.nseg + 3) / 4), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_huff_encode(const EncArgs& a, hipStream_t s) {
+  const dim3 tiles(a.sh.ntiles), block(kThreads);
+  const uint32_t segw = (a.sh.nseg + 3) / 4, blocks = (a.sh.ntiles + kBlockTiles - 1) / kBlockTiles;
+  switch (a.sh.D) {
+    case 64: hipLaunchKernelGGL(ec_hist_tiles<1>, tiles, block, 0, s, a); break;
+    case 128: hipLaunchKernelGGL(ec_hist_tiles<2>, tiles, block, 0, s, a); break;
+    case 256: hipLaunchKernelGGL(ec_hist_tiles<4>, tiles, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = launch_seg_books(a.w.hhist, a.w.henc, a.w.hbooks, a.w.hstat, a.sh.nseg, s);
+  if (e != hipSuccess) return e;
+  switch (a.sh.D) {
+    case 64: hipLaunchKernelGGL(ec_hsize_tiles<1>, tiles, block, 0, s, a); break;
+    case 128: hipLaunchKernelGGL(ec_hsize_tiles<2>, tiles, block, 0, s, a); break;
+    default: hipLaunchKernelGGL(ec_hsize_tiles<4>, tiles, block, 0, s, a); break;
+  }
+  hipLaunchKernelGGL(ec_seg_choose, dim3(segw), block, 0, s, a);
+  hipLaunchKernelGGL(ec_items, dim3(blocks), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_huff_write(const EncArgs& a, hipStream_t s) {
+  const dim3 tiles(a.sh.ntiles), block(kThreads);
+  switch (a.sh.D) {
+    case 64: hipLaunchKernelGGL(ec_write_huff<1>, tiles, block, 0, s, a); break;
+    case 128: hipLaunchKernelGGL(ec_write_huff<2>, tiles, block, 0, s, a); break;
+    case 256: hipLaunchKernelGGL(ec_write_huff<4>, tiles, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_huff_tables(const DecArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(ec_hbook_copy, dim3((a.sh.nseg + 3) / 4), dim3(kThreads), 0, s, a);
+  return launch_seg_luts(a.w.hbooks, a.w.hstat + 2, a.w.henc, a.w.hlut, a.w.hvalid, a.w.hstat + 1,
+                         a.sh.nseg, s);
+}
+
+hipError_t launch_huff_decode(const DecArgs& a, hipStream_t s) {
+  const dim3 grid(a.sh.ntiles), block(kThreads);
+  switch (a.sh.D) {
+    case 64:
+      hipLaunchKernelGGL(ec_decode_huff<1>, grid, block, 0, s, a.in, a.y, a);
+      hipLaunchKernelGGL(ec_fill_refs<1>, grid, block, 0, s, a.in, a.y, a);
+      break;
+    case 128:
+      hipLaunchKernelGGL(ec_decode_huff<2>, grid, block, 0, s, a.in, a.y, a);
+      hipLaunchKernelGGL(ec_fill_refs<2>, grid, block, 0, s, a.in, a.y, a);
+      break;
+    case 256:
+      hipLaunchKernelGGL(ec_decode_huff<4>, grid, block, 0, s, a.in, a.y, a);
+      hipLaunchKernelGGL(ec_fill_refs<4>, grid, block, 0, s, a.in, a.y, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -24,6 +24,9 @@ struct Layout {
   uint64_t tile_status, block_status, tile_inserted, tile_rec, tile_U, tile_nout, hash;
   uint64_t stage_pl = 0, stage_w = 0, stage_om = 0, stage_slot = 0;
   uint64_t tile_info = 0, tile_bitmap = 0, tile_first = 0, seg_eb = 0;
+  uint64_t stage_sym = 0, hhist = 0, henc = 0, hbooks = 0, hstat = 0, tile_hsize = 0;
+  uint64_t seg_coder = 0, hlut = 0, hvalid = 0;
+  bool huff = false;  // Huffman segments (coder 2 or 3)
   uint64_t dyn_bytes, total;
   uint32_t nbr;
   std::vector<uint32_t> seg_tile_base_v;
@@ -66,7 +69,11 @@ ec_status make_layout(const ec_plan_desc* d, Layout* L) {
   const uint32_t T = d->num_tables, B = d->rows, D = d->dim, P = d->num_chunks;
   if (T < 1 || D < 1 || P < 1 || !d->eb) return EC_ERR_INVALID;
   if (d->eb_mode != EC_EB_ABS && d->eb_mode != EC_EB_REL_RANGE) return EC_ERR_INVALID;
-  if (d->coder != EC_CODER_BITPACK) return EC_ERR_UNSUPPORTED;
+  if (d->coder != EC_CODER_BITPACK && d->coder != EC_CODER_HUFFMAN && d->coder != EC_CODER_AUTO)
+    return EC_ERR_INVALID;
+  // Huffman segments: for the wave64 paths (D = 64, 128, 256) only
+  if (d->coder != EC_CODER_BITPACK && !ec::encode_has_assembly(D)) return EC_ERR_UNSUPPORTED;
+  L->huff = d->coder != EC_CODER_BITPACK;
   if (d->debug_hash_bits > 64) return EC_ERR_INVALID;
   const ec_schedule& s = d->sched;
   if (s.kind == EC_SCHED_INV_SQRT) {
@@ -109,6 +116,9 @@ ec_status make_layout(const ec_plan_desc* d, Layout* L) {
       uint32_t n = rows - 64 * k < 64 ? rows - 64 * k : 64;
       seg_bytes += 16 + aup(4ull * n * D, 16);
     }
+    // a Huffman segment may carry its codebook on top of all-RAW records
+    if (L->huff) seg_bytes += ec::kBookPad;
+    if (seg_bytes >= (1ull << 31)) return EC_ERR_UNSUPPORTED;
     maxb += aup(8ull * T, 16) + (uint64_t)T * seg_bytes;
     for (uint32_t t = 0; t < T; t++) {
       uint64_t sidx = (uint64_t)p * T + t;
@@ -176,6 +186,17 @@ ec_status make_layout(const ec_plan_desc* d, Layout* L) {
     L->tile_bitmap = take(8ull * tiles);
     L->tile_first = take(4ull * 64 * tiles);
     L->seg_eb = take(4ull * nseg);
+    if (L->huff) {
+      L->stage_sym = take(2ull * 64 * D * tiles);
+      L->hhist = take(4ull * ec::kHuffTable * nseg);
+      L->henc = take(4ull * ec::kHuffTable * nseg);
+      L->hbooks = take((uint64_t)ec::kBookStride * nseg);
+      L->hstat = take(16);
+      L->tile_hsize = take(4ull * tiles);
+      L->seg_coder = take(4ull * nseg);
+      L->hlut = take(2ull * ec::kHuffTable * nseg);
+      L->hvalid = take(4ull * nseg);
+    }
     o = aup(o, 256);
   }
   L->total = o;
@@ -295,6 +316,17 @@ ec::Work make_work(const Layout& L, uint8_t* ws) {
     w.tile_first = reinterpret_cast<uint32_t*>(ws + L.tile_first);
     w.seg_eb = reinterpret_cast<uint32_t*>(ws + L.seg_eb);
   }
+  if (L.huff) {
+    w.stage_sym = reinterpret_cast<uint16_t*>(ws + L.stage_sym);
+    w.hhist = reinterpret_cast<uint32_t*>(ws + L.hhist);
+    w.henc = reinterpret_cast<uint32_t*>(ws + L.henc);
+    w.hbooks = ws + L.hbooks;
+    w.hstat = reinterpret_cast<uint32_t*>(ws + L.hstat);
+    w.tile_hsize = reinterpret_cast<uint32_t*>(ws + L.tile_hsize);
+    w.seg_coder = reinterpret_cast<uint32_t*>(ws + L.seg_coder);
+    w.hlut = reinterpret_cast<uint16_t*>(ws + L.hlut);
+    w.hvalid = reinterpret_cast<uint32_t*>(ws + L.hvalid);
+  }
   return w;
 }
 
@@ -329,6 +361,10 @@ ec_status ec_plan(const ec_plan_desc* desc, ec_plan_t* out) {
   const Layout& L = pl->L;
   // no workspace at all: a plan for ec_compress_static (and ec_decompress) only
   const bool no_ws = !desc->d_workspace && desc->workspace_bytes == 0;
+  if (no_ws && L.huff) {  // Huffman segments keep their tables in the workspace
+    delete pl;
+    return EC_ERR_UNSUPPORTED;
+  }
   if (!no_ws && (!desc->d_workspace || desc->workspace_bytes < L.total ||
                  ((uintptr_t)desc->d_workspace & 255u))) {
     delete pl;
@@ -486,7 +522,16 @@ ec_status ec_decompress(ec_plan_t pl, const void* d_stream, size_t stream_cap, f
   da.seg_tile_base = pl->ws ? pl->work.seg_tile_base
                             : reinterpret_cast<const uint32_t*>(pl->consts_dev + pl->L.seg_tile_base);
   da.report = pl->report_dev;
-  const ec_status st = profiled(pl, EC_KERNEL_DECODE, s, [&] { return ec::launch_decode(da, s); });
+  da.huff = pl->L.huff ? 1u : 0u;
+  da.w = pl->work;
+  const ec_status st = profiled(pl, EC_KERNEL_DECODE, s, [&] {
+    if (!pl->L.huff) return ec::launch_decode(da, s);
+    // the codebooks' tables first; Huffman tiles and their repeated rows after
+    hipError_t e = ec::launch_huff_tables(da, s);
+    if (e == hipSuccess) e = ec::launch_decode(da, s);
+    if (e == hipSuccess) e = ec::launch_huff_decode(da, s);
+    return e;
+  });
   if (st != EC_OK) return st;
   record_done(pl, s);
   return EC_OK;
@@ -660,6 +705,7 @@ ec_status enqueue_compress(ec_plan_s* pl, const ec::Work& work, bool clear, int6
   ea.eb_mode = (uint32_t)pl->desc.eb_mode;
   ea.iter = iter;
   ea.sched = schedule_factor(pl->desc.sched, iter);
+  ea.coder = (uint32_t)pl->desc.coder;
   uint32_t hb = pl->desc.debug_hash_bits;
   ea.hash_keep = (hb == 0 || hb >= 64) ? ~0ull : ((1ull << hb) - 1ull);
   ea.report = pl->report_dev;
@@ -672,7 +718,15 @@ ec_status enqueue_compress(ec_plan_s* pl, const ec::Work& work, bool clear, int6
   st = profiled(pl, EC_KERNEL_ENCODE, s, [&] { return ec::launch_encode(ea, s); });
   if (st != EC_OK) return st;
   if (ec::encode_has_assembly(sh.D)) {
-    st = profiled(pl, EC_KERNEL_ASSEMBLE, s, [&] { return ec::launch_assemble(ea, s); });
+    st = profiled(pl, EC_KERNEL_ASSEMBLE, s, [&] {
+      if (!pl->L.huff) return ec::launch_assemble(ea, s);
+      // size pass, then the Huffman coder's passes, write pass, chunk words
+      hipError_t e = ec::launch_assemble_size(ea, s);
+      if (e == hipSuccess) e = ec::launch_huff_encode(ea, s);
+      if (e == hipSuccess) e = ec::launch_assemble_write(ea, s);
+      if (e == hipSuccess) e = ec::launch_huff_write(ea, s);
+      return e;
+    });
     if (st != EC_OK) return st;
   }
   return EC_OK;

@@ -78,7 +78,16 @@ typedef enum {
                             the whole initial phase then 1, is steps = 1)  */
 } ec_sched_kind;
 
-typedef enum { EC_CODER_BITPACK = 1 } ec_coder;
+/* The lossless stage after quantization and repeated-row detection (section
+ * III-D: "a hybrid method" of the vector-based LZ and an entropy encoder such
+ * as Huffman, chosen per table, section III-D "Selection Between Two
+ * Encoders").  BITPACK: every segment's codes as bit planes per 64-element
+ * block.  HUFFMAN: every segment with a valid eb Huffman-coded (a canonical
+ * code per segment, built from the histogram of its first-occurrence rows;
+ * ec_huffman.h states the code's rules).  AUTO: per segment, the Huffman form
+ * when it is strictly smaller.  HUFFMAN and AUTO need D = 64, 128 or 256 and a
+ * plan with a workspace; a BITPACK plan decodes bit-plane streams only. */
+typedef enum { EC_CODER_BITPACK = 1, EC_CODER_HUFFMAN = 2, EC_CODER_AUTO = 3 } ec_coder;
 
 /* Kernel ids for the profiling counters.  PREP is the value-range pass (and
  * the clearing of the per-call workspace).  For D = 64, 128 and 256,
@@ -115,7 +124,7 @@ typedef struct {
                                large/medium/small table classes of Algorithm 1)
                                or NULL for 1.  Copied by ec_plan.             */
   ec_schedule sched;        /* iteration-wise decay                            */
-  int32_t coder;            /* EC_CODER_BITPACK                                */
+  int32_t coder;            /* ec_coder                                        */
   uint32_t debug_hash_bits; /* 0: normal.  1..32: keep only that many bits of
                                the internal row hash (forces hash collisions;
                                output bytes are unchanged).  Tests only.       */
