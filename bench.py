@@ -282,7 +282,7 @@ def summarize_stats(d: str, workload: str, command: str, coder: str = "bitpack")
     other = [0, 0.0, 0.0]
     for r in rows:
         name = _short_kernel(r["Name"])
-        if not name.startswith(("huff_",) if coder == "huffman" else ("ec_",)):
+        if not name.startswith(("huff_",) if coder == "huffman" else ("ec_", "huff_")):
             # synthetic-input generation and the like
             other[0] += int(r["Calls"])
             other[1] += float(r["TotalDurationNs"])
@@ -443,7 +443,11 @@ def main():
                     help="write profiles/*_kernel_stats.txt from a rocprofv3 --stats run under DIR")
     ap.add_argument("--command", default="", help="command line recorded in a summary")
     ap.add_argument("--coder", default="bitpack", choices=["bitpack", "huffman"],
-                    help="huffman: time the canonical Huffman coder on the workload's codes")
+                    help="huffman: time the standalone canonical Huffman coder on the "
+                         "workload's codes")
+    ap.add_argument("--stream-coder", default="bitpack", choices=["bitpack", "huffman", "auto"],
+                    help="the segment coder of the compressed stream: bit planes, Huffman, "
+                         "or per segment the smaller")
     args = ap.parse_args()
     if args.summarize_counters:
         summarize_counters(args.summarize_counters, args.workload,
@@ -486,7 +490,9 @@ def main():
     T, B, D = w0.shape
     N = T * B * D
     sched = {"kind": w0.sched_kind, "t0": w0.sched_t0} if w0.sched_kind else None
-    plan = ec.Plan(T, B, D, 1, w0.eb_mode, w0.eb, schedule=sched, device=dev)
+    coder = {"bitpack": ec.CODER_BITPACK, "huffman": ec.CODER_HUFFMAN,
+             "auto": ec.CODER_AUTO}[args.stream_coder]
+    plan = ec.Plan(T, B, D, 1, w0.eb_mode, w0.eb, schedule=sched, device=dev, coder=coder)
     out = plan.empty_stream()
     y = torch.empty(T, B, D, dtype=torch.float32, device=dev)
     # read (untimed) before every timed call of the cold protocol: 512 MiB,
@@ -616,6 +622,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {WORKLOADS[args.workload]}", "tables": T,
                    "batch": B, "dim": D, "chunks": 1, "batches_cycled": len(batches),
+                   "stream_coder": args.stream_coder,
                    "protocol": "cold: 512 MiB scratch read before each timed call"},
         "compress_GBps": round(4 * N / tc / 1e9, 2),
         "decompress_GBps": round(4 * N / td / 1e9, 2),

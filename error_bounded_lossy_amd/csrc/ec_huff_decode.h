@@ -12,11 +12,14 @@ namespace ec {
 namespace hd {
 
 // Decode one chunk of `rem` symbols from its nwords words at src (LDS or
-// global memory).  The bits are read as if zero words followed the chunk;
+// global memory), handing every group of 8 symbols (packed as 16-bit halves
+// of pk[4]; the group's first symbol index g, n of them valid) to
+// sink(g, pk, n).  The bits are read as if zero words followed the chunk;
 // whether it really ends in its last word is decided from the bits consumed.
 // Returns false if the chunk is malformed.
-__device__ __forceinline__ bool decode_chunk(const uint32_t* src, uint32_t nwords, uint32_t rem,
-                                             const uint16_t* lut, uint16_t* out, bool vec) {
+template <typename Sink>
+__device__ __forceinline__ bool decode_chunk_sink(const uint32_t* src, uint32_t nwords,
+                                                  uint32_t rem, const uint16_t* lut, Sink&& sink) {
   // two words are loaded ahead of the bit buffer, so a refill never waits
   uint32_t q0 = nwords > 0 ? src[0] : 0u, q1 = nwords > 1 ? src[1] : 0u, p = 2;
   uint64_t bitbuf = 0;
@@ -42,16 +45,23 @@ __device__ __forceinline__ bool decode_chunk(const uint32_t* src, uint32_t nword
       used += l;
       pk[k >> 1] |= (ent & 0xFFFu) << (16 * (k & 1));
     }
-    if (vec && g + 8 <= rem) {
-      *reinterpret_cast<uint4*>(out + g) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-    } else {
-      for (uint32_t k = 0; k < min(rem - g, 8u); k++)
-        out[g + k] = (uint16_t)(pk[k >> 1] >> (16 * (k & 1)));
-    }
+    sink(g, pk, min(rem - g, 8u));
   }
   // every consumed bit lies in the chunk, the chunk's last word holds some of
   // them, and the bits after the last code are zero
   return !(bad || used > 32 * nwords || used + 32 <= 32 * nwords || bitbuf != 0);
+}
+
+// The same, writing the symbols to out[0, rem).
+__device__ __forceinline__ bool decode_chunk(const uint32_t* src, uint32_t nwords, uint32_t rem,
+                                             const uint16_t* lut, uint16_t* out, bool vec) {
+  return decode_chunk_sink(src, nwords, rem, lut, [&](uint32_t g, const uint32_t (&pk)[4], uint32_t n) {
+    if (vec && n == 8) {
+      *reinterpret_cast<uint4*>(out + g) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    } else {
+      for (uint32_t k = 0; k < n; k++) out[g + k] = (uint16_t)(pk[k >> 1] >> (16 * (k & 1)));
+    }
+  });
 }
 
 // The same for a chunk staged in LDS, without branches in the symbol loop:
@@ -59,9 +69,11 @@ __device__ __forceinline__ bool decode_chunk(const uint32_t* src, uint32_t nword
 // table lookup (one LDS wait per symbol), and a refill after the lookup
 // consumes it with selects, so the buffer holds at least 21 bits at every
 // lookup.  Words past the chunk read as zero.  nwords >= 1.
-__device__ __forceinline__ bool decode_chunk_lds(const uint32_t* src, uint32_t nwords,
-                                                 uint32_t rem, const uint16_t* lut,
-                                                 uint16_t* out, bool vec) {
+// Groups of 32 symbols go to sink(g, pk, n), packed as 16-bit halves of pk[16].
+template <typename Sink>
+__device__ __forceinline__ bool decode_chunk_lds_sink(const uint32_t* src, uint32_t nwords,
+                                                      uint32_t rem, const uint16_t* lut,
+                                                      Sink&& sink) {
   const uint32_t last = nwords - 1;
   uint64_t bitbuf = (uint64_t)src[0] << 32;
   uint32_t have = 32, used = 0;
@@ -90,17 +102,25 @@ __device__ __forceinline__ bool decode_chunk_lds(const uint32_t* src, uint32_t n
       wq = rf ? wn : wq;
       p += rf ? 1u : 0u;
     }
-    if (vec && g + 32 <= rem) {  // 64 bytes of one chunk at a time
+    sink(g, pk, min(rem - g, 32u));
+  }
+  return !(bad || used > 32 * nwords || used + 32 <= 32 * nwords || bitbuf != 0);
+}
+
+__device__ __forceinline__ bool decode_chunk_lds(const uint32_t* src, uint32_t nwords,
+                                                 uint32_t rem, const uint16_t* lut,
+                                                 uint16_t* out, bool vec) {
+  return decode_chunk_lds_sink(src, nwords, rem, lut,
+                               [&](uint32_t g, const uint32_t (&pk)[16], uint32_t n) {
+    if (vec && n == 32) {  // 64 bytes of one chunk at a time
 #pragma unroll
       for (int q = 0; q < 4; q++)
         *reinterpret_cast<uint4*>(out + g + 8 * q) =
             make_uint4(pk[4 * q], pk[4 * q + 1], pk[4 * q + 2], pk[4 * q + 3]);
     } else {
-      for (uint32_t k = 0; k < min(rem - g, 32u); k++)
-        out[g + k] = (uint16_t)(pk[k >> 1] >> (16 * (k & 1)));
+      for (uint32_t k = 0; k < n; k++) out[g + k] = (uint16_t)(pk[k >> 1] >> (16 * (k & 1)));
     }
-  }
-  return !(bad || used > 32 * nwords || used + 32 <= 32 * nwords || bitbuf != 0);
+  });
 }
 
 }  // namespace hd

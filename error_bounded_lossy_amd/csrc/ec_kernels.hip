@@ -3317,79 +3317,104 @@ __global__ void __launch_bounds__(kThreads) ec_hbook_copy(DecArgs a) {
     bk[i] = i < avail ? src[i] : (uint8_t)(i == 0 && avail == 0 ? 1 : 0);
 }
 
+// One wave per Huffman tile: lane c decodes chunk c of E (at most 64 chunks
+// of 256 codes) by 12-bit table lookups in LDS, and stores every group of 8
+// values straight into its first-occurrence row; the record's outliers are
+// written over them afterwards.
 template <int C>
-__global__ void __launch_bounds__(kThreads) ec_decode_huff(const uint8_t* __restrict__ in,
-                                                          float* __restrict__ yout, DecArgs a) {
+__global__ void __launch_bounds__(64) ec_decode_huff(const uint8_t* __restrict__ in,
+                                                    float* __restrict__ yout, DecArgs a) {
   constexpr uint32_t D = 64u * C, kMaxCh = kTileRows * D / 256;
+  static_assert(kMaxCh <= 64, "one chunk per lane");
+  // a record's words are staged in LDS when they average at most 56 per chunk
+  // (a code of about 7 bits; larger records are read from global memory)
+  constexpr uint32_t kStage = kMaxCh * 56;
   __shared__ DecShared sh;
   __shared__ uint16_t s_lut[kHuffTable];
-  __shared__ __align__(16) uint16_t s_sym[kTileRows * D];
-  __shared__ uint32_t s_ct[kMaxCh + 1];
+  __shared__ uint32_t s_words[kStage];
   __shared__ uint8_t s_urow[kTileRows];
-  __shared__ uint32_t s_bad;
-  const uint32_t tid = threadIdx.x, lane = tid & 63, wv = wave_id();
+  const uint32_t lane = threadIdx.x;
   const uint32_t ticket = blockIdx.x;
-  if (wv == 0) {
+  {
     uint64_t ro;
     dec_locate(a, in, ticket, sh, ro);
   }
-  if (tid == 0) s_bad = 0;
-  __syncthreads();
+  wave_lds_wait();
   // a Huffman segment's codebook is checked by the segment's first tile
-  if (tid == 0 && sh.seg_ok && sh.hseg && sh.tile == 0) {
+  if (lane == 0 && sh.seg_ok && sh.hseg && sh.tile == 0) {
     const uint8_t* bk = a.w.hbooks + (uint64_t)sh.seg * kBookStride;
     const bool empty = bk[0] == 1 && bk[1] == 0 && bk[2] == 0 && bk[3] == 0;
     if (!a.w.hvalid[sh.seg] && !empty) report_error(a.report, kDevErrCorrupt);
   }
   if (!sh.ok || sh.n == 0 || sh.tl.mode != 2) return;  // checked and reported elsewhere
   const DecTile tl = sh.tl;
-  const uint32_t seg = sh.seg, n = sh.n, U = tl.U, nout = tl.nout, nE = U * D, nch = tl.nch;
+  const uint32_t seg = sh.seg, n = sh.n, nout = tl.nout, nE = tl.U * D, nch = tl.nch;
   const bool book_ok = a.w.hvalid[seg] != 0;
   {
     const uint4* src = reinterpret_cast<const uint4*>(a.w.hlut + (uint64_t)seg * kHuffTable);
-    for (uint32_t i = tid; i < kHuffTable * 2 / 16; i += kThreads) reinterpret_cast<uint4*>(s_lut)[i] = src[i];
+#pragma unroll
+    for (uint32_t i = 0; i < kHuffTable * 2 / 16 / 64; i++)
+      reinterpret_cast<uint4*>(s_lut)[64 * i + lane] = src[64 * i + lane];
   }
-  if (wv == 0) unique_rows(tl.bitmap, s_urow);
-  const uint32_t* ct = reinterpret_cast<const uint32_t*>(tl.rec + tl.off_ct);
-  for (uint32_t i = tid; i <= nch; i += kThreads) s_ct[i] = ct[i];
-  __syncthreads();
-  const uint64_t wavail = (tl.avail - tl.off_w) / 4;  // words the segment still holds
-  const uint32_t* words = reinterpret_cast<const uint32_t*>(tl.rec + tl.off_w);
-  bool bad = (nE > 0 && !book_ok) || (tid == 0 && s_ct[0] != 0);
-  if (tid < nch && !bad) {
-    // every chunk ends exactly in its last word (at most 96 words for 256 codes of
-    // at most 12 bits), the next one starts right after it
-    const uint32_t w0 = s_ct[tid], w1 = s_ct[tid + 1];
-    const uint32_t rem = min(256u, nE - 256 * tid);
-    bad = !(w0 < w1 && w1 - w0 <= 96u && (uint64_t)w1 <= wavail) ||
-          !hd::decode_chunk(words + w0, w1 - w0, rem, s_lut, s_sym + 256 * tid, true);
-  }
-  if (wv == 0) {  // outlier positions index E and strictly increase
-    const uint32_t* op = reinterpret_cast<const uint32_t*>(tl.rec + tl.off_opos);
-    bool obad = false;
-    for (uint32_t g = lane; g < nout; g += 64) obad |= op[g] >= nE || (g > 0 && op[g - 1] >= op[g]);
-    bad = bad || obad;
-  }
-  if (bad) s_bad = 1;
-  __syncthreads();
+  unique_rows(tl.bitmap, s_urow);
+  wave_lds_wait();
   float* yt = yout + ((uint64_t)(seg % a.sh.T) * a.sh.B + chunk_row0(a.sh, seg / a.sh.T) +
                       (uint64_t)sh.tile * kTileRows) * D;
-  if (s_bad) {
-    for (uint32_t i = tid; i < n * D; i += kThreads) yt[i] = 0.0f;
-    if (tid == 0) report_error(a.report, kDevErrCorrupt);
-    return;
-  }
+  const uint64_t wavail = (tl.avail - tl.off_w) / 4;  // words the segment still holds
+  const uint32_t* ct = reinterpret_cast<const uint32_t*>(tl.rec + tl.off_ct);
+  const uint32_t* words = reinterpret_cast<const uint32_t*>(tl.rec + tl.off_w);
   const float s2 = sh.eb + sh.eb;
+  bool bad = (nE > 0 && !book_ok) || ct[0] != 0;
+  // the record's words into LDS when they fit and lie inside the segment
+  const uint32_t total = ct[nch];
+  const bool staged = total <= kStage && (uint64_t)total <= wavail;
+  if (staged)
+    for (uint32_t i = lane; i < total; i += 64) s_words[i] = words[i];
+  wave_lds_wait();
+  if (lane < nch && !bad) {
+    // every chunk ends exactly in its last word (at most 96 words for 256 codes
+    // of at most 12 bits), and the next one starts right after it
+    const uint32_t c = lane, w0 = ct[c], w1 = ct[c + 1];
+    const uint32_t rem = min(256u, nE - 256 * c);
+    bad = !(w0 < w1 && w1 - w0 <= 96u && w1 <= total && (uint64_t)total <= wavail);
+    // groups of codes of one row (D is a multiple of 32) into their row
+    auto put = [&](uint32_t g, const uint32_t* pk, uint32_t cnt) {
+      const uint32_t e = 256 * c + g;
+      float* y = yt + (uint64_t)s_urow[e / D] * D + e % D;
+      for (uint32_t k0 = 0; k0 < cnt; k0 += 4) {
+        float v[4];
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+          const uint32_t kk = k0 + k;
+          v[k] = (float)((int)((pk[kk >> 1] >> (16 * (kk & 1))) & 0xFFFFu) - 2047) * s2;
+        }
+        if (k0 + 4 <= cnt) {
+          *reinterpret_cast<float4*>(y + k0) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+          for (uint32_t k = 0; k0 + k < cnt; k++) y[k0 + k] = v[k];
+        }
+      }
+    };
+    if (!bad && staged) {
+      bad = !hd::decode_chunk_lds_sink(s_words + w0, w1 - w0, rem, s_lut,
+                                       [&](uint32_t g, const uint32_t (&pk)[16], uint32_t cnt) { put(g, pk, cnt); });
+    } else if (!bad) {
+      bad = !hd::decode_chunk_sink(words + w0, w1 - w0, rem, s_lut,
+                                   [&](uint32_t g, const uint32_t (&pk)[4], uint32_t cnt) { put(g, pk, cnt); });
+    }
+  }
   const uint32_t* opos = reinterpret_cast<const uint32_t*>(tl.rec + tl.off_opos);
   const uint32_t* oval = reinterpret_cast<const uint32_t*>(tl.rec + tl.off_oval);
-  for (uint32_t u = wv; u < U; u += kThreads / 64) {
-    float v[C];
-#pragma unroll
-    for (uint32_t j = 0; j < C; j++) v[j] = (float)((int)s_sym[u * D + 64 * j + lane] - 2047) * s2;
-    patch_outliers<C>(v, u * D, opos, oval, nout);
-    float* y = yt + (uint64_t)s_urow[u] * D;
-#pragma unroll
-    for (uint32_t j = 0; j < C; j++) __builtin_nontemporal_store(v[j], &y[64 * j + lane]);
+  for (uint32_t g = lane; g < nout; g += 64) bad = bad || opos[g] >= nE || (g > 0 && opos[g - 1] >= opos[g]);
+  wait_vm();  // this wave's stores are performed before any rewrite of the same words
+  if (__ballot(bad) != 0) {
+    for (uint32_t i = lane; i < n * D; i += 64) yt[i] = 0.0f;
+    if (lane == 0) report_error(a.report, kDevErrCorrupt);
+    return;
+  }
+  for (uint32_t g = lane; g < nout; g += 64) {
+    const uint32_t p = opos[g];
+    yt[(uint64_t)s_urow[p / D] * D + p % D] = __uint_as_float(oval[g]);
   }
 }
 
@@ -3635,15 +3660,15 @@ hipError_t launch_huff_decode(const DecArgs& a, hipStream_t s) {
   const dim3 grid(a.sh.ntiles), block(kThreads);
   switch (a.sh.D) {
     case 64:
-      hipLaunchKernelGGL(ec_decode_huff<1>, grid, block, 0, s, a.in, a.y, a);
+      hipLaunchKernelGGL(ec_decode_huff<1>, grid, dim3(64), 0, s, a.in, a.y, a);
       hipLaunchKernelGGL(ec_fill_refs<1>, grid, block, 0, s, a.in, a.y, a);
       break;
     case 128:
-      hipLaunchKernelGGL(ec_decode_huff<2>, grid, block, 0, s, a.in, a.y, a);
+      hipLaunchKernelGGL(ec_decode_huff<2>, grid, dim3(64), 0, s, a.in, a.y, a);
       hipLaunchKernelGGL(ec_fill_refs<2>, grid, block, 0, s, a.in, a.y, a);
       break;
     case 256:
-      hipLaunchKernelGGL(ec_decode_huff<4>, grid, block, 0, s, a.in, a.y, a);
+      hipLaunchKernelGGL(ec_decode_huff<4>, grid, dim3(64), 0, s, a.in, a.y, a);
       hipLaunchKernelGGL(ec_fill_refs<4>, grid, block, 0, s, a.in, a.y, a);
       break;
     default:
