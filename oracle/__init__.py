@@ -45,6 +45,7 @@ class _Cfg(ctypes.Structure):
         ("sched_kind", ctypes.c_int32), ("sched_steps", ctypes.c_int32),
         ("sched_t0", ctypes.c_double), ("sched_k", ctypes.c_double),
         ("sched_phase", ctypes.c_int64), ("coder", ctypes.c_uint32),
+        ("table_coder", ctypes.POINTER(ctypes.c_int32)),
     ]
 
 
@@ -79,6 +80,11 @@ def lib():
         L.ebo_homo_index.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
         L.ebo_homo_counts.restype = ctypes.c_int
         L.ebo_homo_counts.argtypes = [cfgp, ctypes.c_int64, f32p, ctypes.c_void_p, ctypes.c_void_p]
+        L.ebo_speedup.restype = ctypes.c_double
+        L.ebo_speedup.argtypes = [ctypes.c_double] * 4
+        L.ebo_select.restype = ctypes.c_int
+        L.ebo_select.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p]
         L.ebo_classify.restype = ctypes.c_int
         L.ebo_classify.argtypes = [ctypes.c_uint32, ctypes.c_void_p, ctypes.c_double,
                                    ctypes.c_double, ctypes.c_double, ctypes.c_double,
@@ -134,6 +140,7 @@ class Config:
     sched_phase: int = 1
     sched_steps: int = 1
     coder: int = CODER_BITPACK
+    table_coder: tuple | None = None
 
     def _c(self):
         eb = np.ascontiguousarray(np.asarray(self.eb, dtype=np.float32).reshape(-1))
@@ -142,11 +149,16 @@ class Config:
         mult = None
         if self.table_mult is not None:
             mult = np.ascontiguousarray(np.asarray(self.table_mult, dtype=np.float32))
+        tc = None
+        if self.table_coder is not None:
+            tc = np.ascontiguousarray(np.asarray(self.table_coder, dtype=np.int32))
         c = _Cfg(self.T, self.B, self.D, self.P, self.eb_mode, _f32ptr(eb),
                  _f32ptr(mult) if mult is not None else ctypes.POINTER(ctypes.c_float)(),
                  self.sched_kind, self.sched_steps, self.sched_t0, self.sched_k,
-                 self.sched_phase, self.coder)
-        return c, (eb, mult)  # keep arrays alive with the struct
+                 self.sched_phase, self.coder,
+                 tc.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if tc is not None
+                 else ctypes.POINTER(ctypes.c_int32)())
+        return c, (eb, mult, tc)  # keep arrays alive with the struct
 
 
 def schedule(cfg: Config, it: int) -> float:
@@ -209,6 +221,27 @@ def homo_counts(cfg: Config, it: int, x: np.ndarray):
     if rc != OK:
         raise RuntimeError(f"oracle homo_counts failed with status {rc}")
     return no, nq
+
+
+def speedup(cr: float, bw: float, tc: float, td: float) -> float:
+    """Eq. (2)."""
+    return lib().ebo_speedup(cr, bw, tc, td)
+
+
+def select(cr, tc, td, bw: float):
+    """Algorithm 2: per table, the index of the compressor with the largest
+    eq. (2) speed-up.  cr [ncomp][T], tc / td [ncomp].  (best, speed-ups)."""
+    cr = np.ascontiguousarray(cr, dtype=np.float64)
+    ncomp, T = cr.shape
+    tc = np.ascontiguousarray(tc, dtype=np.float64)
+    td = np.ascontiguousarray(td, dtype=np.float64)
+    best = np.zeros(T, np.int32)
+    sp = np.zeros(T, np.float64)
+    rc = lib().ebo_select(T, ncomp, cr.ctypes.data, tc.ctypes.data, td.ctypes.data, bw,
+                          best.ctypes.data, sp.ctypes.data)
+    if rc != 0:
+        raise ValueError("invalid compressor pool")
+    return best, sp
 
 
 def classify(hindex, l_thresh: float, s_thresh: float, alpha: float, beta: float):

@@ -192,6 +192,10 @@ static int cfg_ok(const ebo_cfg* c) {
   if (c->T < 1 || c->D < 1 || c->P < 1) return 0;
   if (c->eb_mode != EBO_EB_ABS && c->eb_mode != EBO_EB_REL) return 0;
   if (c->coder > EBO_CODER_AUTO) return 0;
+  if (c->table_coder)
+    for (uint32_t t = 0; t < c->T; t++)
+      if (c->table_coder[t] < (int32_t)EBO_CODER_BITPACK || c->table_coder[t] > (int32_t)EBO_CODER_AUTO)
+        return 0;
   if (c->sched_kind == EBO_SCHED_INV_SQRT && !(c->sched_t0 > 0.0)) return 0;
   if (c->sched_kind == EBO_SCHED_STEP && (c->sched_phase < 1 || c->sched_steps < 1))
     return 0;
@@ -209,6 +213,10 @@ size_t ebo_max_compressed_bytes(const ebo_cfg* c) {
   if (!cfg_ok(c)) return 0;
   uint64_t total = 64 + align_up((uint64_t)8 * c->P, 16);
   int huff = c->coder == EBO_CODER_HUFFMAN || c->coder == EBO_CODER_AUTO;
+  if (c->table_coder) {
+    huff = 0;
+    for (uint32_t t = 0; t < c->T; t++) huff |= c->table_coder[t] != (int32_t)EBO_CODER_BITPACK;
+  }
   for (uint32_t p = 0; p < c->P; p++) {
     uint32_t rows = chunk_rows(c, p);
     uint32_t nt = (rows + 63) / 64;
@@ -314,6 +322,36 @@ int ebo_homo_counts(const ebo_cfg* c, int64_t iter, const float* x, uint32_t* n_
     }
   }
   return rc;
+}
+
+double ebo_speedup(double cr, double bw, double tc, double td) {
+  /* the time per uncompressed byte with compression (sending cr times fewer
+     bytes, compressing and decompressing every byte) against without */
+  return 1.0 / (1.0 / cr + bw * (1.0 / tc + 1.0 / td));
+}
+
+int ebo_select(uint32_t T, uint32_t ncomp, const double* cr, const double* tc, const double* td,
+               double bw, int32_t* best, double* sp) {
+  if (ncomp == 0 || !cr || !tc || !td || !best || !(bw > 0.0) || !isfinite(bw)) return -1;
+  for (uint32_t c = 0; c < ncomp; c++) {
+    if (!(tc[c] > 0.0) || !(td[c] > 0.0) || !isfinite(tc[c]) || !isfinite(td[c])) return -1;
+    for (uint32_t t = 0; t < T; t++)
+      if (!(cr[(size_t)c * T + t] > 0.0) || !isfinite(cr[(size_t)c * T + t])) return -1;
+  }
+  for (uint32_t t = 0; t < T; t++) {
+    int32_t b = 0;
+    double v = ebo_speedup(cr[t], bw, tc[0], td[0]);
+    for (uint32_t c = 1; c < ncomp; c++) {
+      double w = ebo_speedup(cr[(size_t)c * T + t], bw, tc[c], td[c]);
+      if (w > v) {
+        v = w;
+        b = (int32_t)c;
+      }
+    }
+    best[t] = b;
+    if (sp) sp[t] = v;
+  }
+  return 0;
 }
 
 int ebo_classify(uint32_t T, const double* hindex, double l_thresh, double s_thresh,
@@ -631,6 +669,14 @@ int ebo_compress(const ebo_cfg* c, int64_t iter, const float* x, uint8_t* out, s
   size_t need = ebo_max_compressed_bytes(c);
   if (!out || cap < need) return EBO_ERR_CAPACITY;
   uint32_t coder = c->coder ? c->coder : EBO_CODER_BITPACK;
+  if (c->table_coder) { /* the stream's coder from the tables' coders */
+    int all1 = 1, all2 = 1;
+    for (uint32_t t = 0; t < c->T; t++) {
+      all1 &= c->table_coder[t] == (int32_t)EBO_CODER_BITPACK;
+      all2 &= c->table_coder[t] == (int32_t)EBO_CODER_HUFFMAN;
+    }
+    coder = all1 ? EBO_CODER_BITPACK : (all2 ? EBO_CODER_HUFFMAN : EBO_CODER_AUTO);
+  }
 
   float* eb_t = (float*)malloc(sizeof(float) * T);
   if (!eb_t) return EBO_ERR_OOM;
@@ -700,11 +746,12 @@ int ebo_compress(const ebo_cfg* c, int64_t iter, const float* x, uint8_t* out, s
         buf_t bp = {0}, hf = {0};
         if (encode_segment(&sv, nt, eb, NULL, &bp) != 0) rc = EBO_ERR_OOM;
         int use_huff = 0;
-        if (rc == EBO_OK && valid && coder != EBO_CODER_BITPACK) {
+        uint32_t tcoder = c->table_coder ? (uint32_t)c->table_coder[t] : coder;
+        if (rc == EBO_OK && valid && tcoder != EBO_CODER_BITPACK) {
           uint8_t hlen[EBO_HUFF_NSYM];
           segment_lengths(&sv, hlen);
           if (encode_segment(&sv, nt, eb, hlen, &hf) != 0) rc = EBO_ERR_OOM;
-          use_huff = coder == EBO_CODER_HUFFMAN || hf.n < bp.n;
+          use_huff = tcoder == EBO_CODER_HUFFMAN || hf.n < bp.n;
         }
         if (rc == EBO_OK) {
           const buf_t* pick = use_huff ? &hf : &bp;

@@ -53,6 +53,9 @@
  *   zero-padded to 16; then the tile records in order.
  *   With coder 3 a segment is Huffman iff its Huffman form is strictly
  *   smaller than its bit-plane form; with coder 2 every valid segment is.
+ *   Coders chosen per table (Algorithm 2's table-wise configuration) apply
+ *   these rules table by table; the stream's coder is then 1 when every
+ *   table is 1, 2 when every table is 2, else 3.
  *
  * TILE RECORD (tile k = segment rows [64k, min(64k+64, rows)), n rows)
  *   header, 16 bytes:
@@ -121,6 +124,7 @@ typedef struct {
   double sched_k;            /* STEP: starting multiple of the base eb     */
   int64_t sched_phase;       /* STEP: length of the decay phase            */
   uint32_t coder;            /* EBO_CODER_*; 0 means EBO_CODER_BITPACK     */
+  const int32_t* table_coder; /* [T] coder of each table, NULL: `coder`    */
 } ebo_cfg;
 
 /* Iteration-wise factor (Algorithm 1 OnlineDecay, read non-cumulatively). */
@@ -154,6 +158,20 @@ int ebo_homo_counts(const ebo_cfg* c, int64_t iter, const float* x, uint32_t* n_
  * l_thresh > s_thresh or alpha, beta not finite and > 0. */
 int ebo_classify(uint32_t T, const double* hindex, double l_thresh, double s_thresh,
                  double alpha, double beta, int32_t* cls, float* mult);
+
+/* Eq. (2): the communication speed-up of a compressor with compression
+ * ratio cr and compression / decompression throughputs tc, td over a link of
+ * bandwidth bw (throughputs and bandwidth in the same unit):
+ * 1 / (1/cr + bw * (1/tc + 1/td)). */
+double ebo_speedup(double cr, double bw, double tc, double td);
+
+/* Algorithm 2 (OfflineCompConfig): for each of T tables, the compressor of
+ * the pool (ncomp of them; cr[c*T + t], tc[c], td[c]) with the largest
+ * eq. (2) speed-up; on equal speed-ups the earlier compressor.  best[t] and,
+ * if not NULL, its speed-up sp[t].  -1 for an empty pool or values that are
+ * not finite and > 0. */
+int ebo_select(uint32_t T, uint32_t ncomp, const double* cr, const double* tc, const double* td,
+               double bw, int32_t* best, double* sp);
 
 /* Per-table error bound used for every segment of table t (fp32). */
 float ebo_table_eb(const ebo_cfg* c, uint32_t t, int64_t iter, const float* x);

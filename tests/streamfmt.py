@@ -454,17 +454,22 @@ def segment_form_sizes(seg, buf, D, lengths_of_hist):
     return bp, hf, lengths
 
 
-def check_coder_choice(st, buf, lengths_of_hist):
+def check_coder_choice(st, buf, lengths_of_hist, table_coder=None):
     """Every segment has the size of the form its coder rules pick: coder 1
     bit planes, coder 2 Huffman for valid segments, coder 3 Huffman iff
-    strictly smaller; a Huffman segment's codebook is the histogram's."""
+    strictly smaller (the stream's coder, or table_coder[t] per table); a
+    Huffman segment's codebook is the histogram's."""
     picked = []
+    if table_coder is not None:
+        tc = list(table_coder)
+        assert st.coder == (1 if all(c == 1 for c in tc) else 2 if all(c == 2 for c in tc) else 3)
     for seg in st.segments:
         if not seg.valid:
             assert not seg.huff
             continue
         bp, hf, lengths = segment_form_sizes(seg, buf, st.D, lengths_of_hist)
-        want_huff = {1: False, 2: True, 3: hf < bp}[st.coder]
+        coder = st.coder if table_coder is None else table_coder[seg.t]
+        want_huff = {1: False, 2: True, 3: hf < bp}[coder]
         assert seg.huff == want_huff, (seg.p, seg.t, bp, hf)
         assert seg.nbytes == (hf if seg.huff else bp), (seg.p, seg.t, seg.nbytes, bp, hf)
         if seg.huff:

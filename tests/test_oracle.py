@@ -682,3 +682,61 @@ def test_corrupt_huffman_streams_are_rejected():
         bad[int(rng.integers(0, bad.size))] ^= np.uint8(1 << int(rng.integers(0, 8)))
         rc, _ = O.decompress(cfg, bad, status=True)
         assert rc in (O.OK, O.ERR_CORRUPT)
+
+
+# --------------------------------------------------------------------------
+# compressor selection (section III-D "Selection Between Two Encoders":
+# eq. (2) and Algorithm 2), and coders chosen per table
+# --------------------------------------------------------------------------
+def test_speedup_closed_forms():
+    """eq. (2) at round numbers worked by hand, and its limits: infinitely
+    fast coders (or a free link) give the compression ratio itself, an
+    infinite ratio gives the coders' own bound."""
+    assert O.speedup(4.0, 1.0, 8.0, 8.0) == 2.0          # 1 / (1/4 + 1/8 + 1/8)
+    assert O.speedup(2.0, 2.0, 4.0, 4.0) == pytest.approx(2.0 / 3.0)  # 1 / (1/2 + 1)
+    assert O.speedup(5.0, 4.0, 1e300, 1e300) == pytest.approx(5.0)
+    assert O.speedup(5.0, 1e-300, 40.5, 205.4) == pytest.approx(5.0)
+    assert O.speedup(1e300, 2.0, 10.0, 10.0) == pytest.approx(2.5)    # 1 / (2 * 0.2)
+    # faster coders or a higher ratio never lower the speed-up
+    assert O.speedup(6.0, 4.0, 80.0, 40.0) > O.speedup(6.0, 4.0, 40.0, 40.0)
+    assert O.speedup(7.0, 4.0, 40.0, 40.0) > O.speedup(6.0, 4.0, 40.0, 40.0)
+
+
+def test_selection_takes_the_largest_speedup_per_table():
+    """Three tables, two compressors: A (ratio 4, 8, 10; coders at 8 GB/s),
+    B (ratio 8, 8, 5; coders at 16 GB/s), link 1 GB/s.  Speed-ups by hand:
+    A = 1/(1/r + 1/4), B = 1/(1/r + 1/8): table 0 A 2, B 4 -> B; table 1
+    A 8/3, B 4 -> B; table 2 A 1/(0.1 + 0.25) = 2.857, B 1/(0.2 + 0.125) =
+    3.077 -> B.  With B's coders at 4 GB/s (B = 1/(1/r + 1/2)): table 0 A 2,
+    B 1.6 -> A; table 1 8/3 vs 1.6 -> A; table 2 2.857 vs 1.429 -> A.  Equal
+    speed-ups keep the earlier compressor."""
+    best, sp = O.select([[4, 8, 10], [8, 8, 5]], [8, 16], [8, 16], 1.0)
+    assert best.tolist() == [1, 1, 1]
+    np.testing.assert_allclose(sp, [4.0, 4.0, 1 / 0.325])
+    best, sp = O.select([[4, 8, 10], [8, 8, 5]], [8, 4], [8, 4], 1.0)
+    assert best.tolist() == [0, 0, 0]
+    np.testing.assert_allclose(sp, [2.0, 8 / 3, 1 / 0.35])
+    best, _ = O.select([[4, 4], [4, 4]], [8, 8], [8, 8], 1.0)
+    assert best.tolist() == [0, 0]
+    with pytest.raises(ValueError):
+        O.select([[4, 0]], [8], [8], 1.0)
+
+
+def test_coders_chosen_per_table():
+    """Algorithm 2's per-table configuration in the stream: each table's
+    segments follow its own coder's rule; the stream's coder is 1 when every
+    table is bit planes, 2 when every table is Huffman, else 3."""
+    rng = np.random.default_rng(21)
+    T, B, D = 4, 300, 64
+    x = rng.normal(0, 0.05, (T, B, D)).astype(np.float32)
+    x[2] = 0.0
+    for tc in [(1, 2, 3, 3), (2, 2, 2, 2), (1, 1, 1, 1), (3, 1, 2, 1)]:
+        cfg = O.Config(T=T, B=B, D=D, eb_mode=O.EB_REL, eb=(0.02,), table_coder=tc)
+        st_bytes = O.compress(cfg, 0, x).stream
+        st = SF.parse(st_bytes)
+        SF.check_coder_choice(st, st_bytes, O.huff_lengths, table_coder=tc)
+        y = O.decompress(cfg, st_bytes)
+        assert np.all(np.abs(y.astype(np.float64) - x) <= 0.02 * (x.max(axis=(1, 2)) - x.min(axis=(1, 2)))[:, None, None] + 1e-9)
+    bp = O.Config(T=T, B=B, D=D, eb_mode=O.EB_REL, eb=(0.02,))
+    allbp = O.Config(T=T, B=B, D=D, eb_mode=O.EB_REL, eb=(0.02,), table_coder=(1, 1, 1, 1))
+    assert np.array_equal(O.compress(bp, 0, x).stream, O.compress(allbp, 0, x).stream)
