@@ -23,7 +23,7 @@ EB_ABS, EB_REL_RANGE = 0, 1
 SCHED_NONE, SCHED_INV_SQRT, SCHED_STEP = 0, 1, 2
 CODER_BITPACK, CODER_HUFFMAN, CODER_AUTO = 1, 2, 3
 KERNEL_PREP, KERNEL_ENCODE, KERNEL_DECODE, KERNEL_ASSEMBLE = 0, 1, 2, 3
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 
 class ECError(RuntimeError):
@@ -45,6 +45,7 @@ class _Desc(ctypes.Structure):
         ("table_mult", ctypes.POINTER(ctypes.c_float)), ("sched", _Schedule),
         ("coder", ctypes.c_int32), ("debug_hash_bits", ctypes.c_uint32),
         ("d_workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("table_coder", ctypes.POINTER(ctypes.c_int32)),
     ]
 
 
@@ -83,6 +84,12 @@ def lib():
                                      ctypes.c_double, ctypes.c_double, ctypes.c_double,
                                      ctypes.c_double, ctypes.POINTER(ctypes.c_int32),
                                      ctypes.POINTER(ctypes.c_float)]
+    dblp = ctypes.POINTER(ctypes.c_double)
+    L.ec_speedup.restype = ctypes.c_double
+    L.ec_speedup.argtypes = [ctypes.c_double] * 4
+    L.ec_select_coders.restype = st
+    L.ec_select_coders.argtypes = [ctypes.c_uint32, ctypes.c_uint32, dblp, dblp, dblp,
+                                   ctypes.c_double, ctypes.POINTER(ctypes.c_int32), dblp]
     L.ec_decompress.restype = st
     L.ec_decompress.argtypes = [vp, vp, sz, vp, vp]
     L.ec_ratio.restype = st
@@ -149,7 +156,7 @@ def _stream_handle(stream) -> int:
 
 
 def _desc(T, B, D, P, eb_mode, eb, table_mult, schedule, debug_hash_bits, keep,
-          coder=CODER_BITPACK):
+          coder=CODER_BITPACK, table_coder=None):
     ebs = [float(v) for v in (eb if hasattr(eb, "__len__") else [eb])]
     if len(ebs) == 1 and T > 1:
         ebs = ebs * T
@@ -164,14 +171,20 @@ def _desc(T, B, D, P, eb_mode, eb, table_mult, schedule, debug_hash_bits, keep,
     s = _Schedule(int(sch.get("kind", SCHED_NONE)), int(sch.get("steps", 1)),
                   float(sch.get("t0", 1000.0)), float(sch.get("k", 2.0)),
                   int(sch.get("phase", 1)))
+    tc = ctypes.POINTER(ctypes.c_int32)()
+    if table_coder is not None:
+        c = (ctypes.c_int32 * max(len(table_coder), 1))(*[int(v) for v in table_coder])
+        keep.append(c)
+        tc = ctypes.cast(c, ctypes.POINTER(ctypes.c_int32))
     return _Desc(ABI_VERSION, T, B, D, P, int(eb_mode), ctypes.cast(arr, ctypes.POINTER(ctypes.c_float)),
-                 mult, s, int(coder), int(debug_hash_bits), None, 0)
+                 mult, s, int(coder), int(debug_hash_bits), None, 0, tc)
 
 
 def workspace_bytes(T, B, D, P=1, eb_mode=EB_ABS, eb=1e-4, table_mult=None, schedule=None,
-                    debug_hash_bits=0, coder=CODER_BITPACK) -> int:
+                    debug_hash_bits=0, coder=CODER_BITPACK, table_coder=None) -> int:
     keep = []
-    d = _desc(T, B, D, P, eb_mode, eb, table_mult, schedule, debug_hash_bits, keep, coder)
+    d = _desc(T, B, D, P, eb_mode, eb, table_mult, schedule, debug_hash_bits, keep, coder,
+              table_coder)
     return int(lib().ec_workspace_bytes(ctypes.byref(d)))
 
 
@@ -184,16 +197,17 @@ class Plan:
 
     def __init__(self, T: int, B: int, D: int, P: int = 1, eb_mode: int = EB_ABS, eb=1e-4,
                  table_mult=None, schedule=None, debug_hash_bits: int = 0, device=None,
-                 workspace: bool = True, coder: int = CODER_BITPACK):
+                 workspace: bool = True, coder: int = CODER_BITPACK, table_coder=None):
         """workspace=False builds a plan without a workspace: compress with
         compress_static (the library's static device scratch), decompress as
-        usual.  coder: CODER_BITPACK, CODER_HUFFMAN or CODER_AUTO."""
+        usual.  coder: CODER_BITPACK, CODER_HUFFMAN or CODER_AUTO;
+        table_coder: one of them per table (Algorithm 2), overriding coder."""
         import torch
         self.T, self.B, self.D, self.P = T, B, D, P
         self.coder = coder
         self._keep = []
         self._desc = _desc(T, B, D, P, eb_mode, eb, table_mult, schedule, debug_hash_bits,
-                           self._keep, coder)
+                           self._keep, coder, table_coder)
         L = lib()
         nbytes = int(L.ec_workspace_bytes(ctypes.byref(self._desc)))
         if nbytes == 0:
@@ -318,6 +332,75 @@ def classify_tables(homo_index_per_table, l_thresh: float, s_thresh: float, alph
     _check(lib().ec_classify_tables(T, hin, float(l_thresh), float(s_thresh), float(alpha),
                                     float(beta), cls, mult), "ec_classify_tables")
     return list(cls)[:T], list(mult)[:T]
+
+
+def speedup(cr: float, bw: float, tc: float, td: float) -> float:
+    """Eq. (2): the communication speed-up 1 / (1/CR + B (1/Tc + 1/Td))."""
+    return float(lib().ec_speedup(float(cr), float(bw), float(tc), float(td)))
+
+
+def select_coders(cr, tc, td, bw: float):
+    """Algorithm 2 (ec_select_coders): cr[c][t] the ratio of compressor c on
+    table t, tc[c] / td[c] its throughputs; returns (best compressor per
+    table, its eq. (2) speed-up)."""
+    C = len(tc)
+    T = len(cr[0]) if C else 0
+    flat = [float(cr[c][t]) for c in range(C) for t in range(T)]
+    a = (ctypes.c_double * max(len(flat), 1))(*flat)
+    b = (ctypes.c_double * max(C, 1))(*[float(v) for v in tc])
+    d = (ctypes.c_double * max(C, 1))(*[float(v) for v in td])
+    best = (ctypes.c_int32 * max(T, 1))()
+    sp = (ctypes.c_double * max(T, 1))()
+    _check(lib().ec_select_coders(T, C, a, b, d, float(bw), best, sp), "ec_select_coders")
+    return list(best)[:T], list(sp)[:T]
+
+
+def offline_comp_config(x, bw: float, pool=(CODER_BITPACK, CODER_HUFFMAN), eb_mode: int = EB_ABS,
+                        eb=1e-4, table_mult=None, schedule=None, iteration: int = 0,
+                        reps: int = 5, stream=None):
+    """Algorithm 2 (OfflineCompConfig) on a sample batch x [T,B,D] (fp32, on
+    the GPU): every compressor of the pool compresses the sample; its
+    per-table compression ratios and its compression / decompression
+    throughputs (bytes of fp32 input per second, the mean of `reps` timed
+    calls) enter eq. (2) with the link bandwidth bw (bytes per second), and
+    each table takes the compressor with the largest speed-up.  Returns a
+    dict with table_coder (ready for Plan(table_coder=...)), best (indices
+    into pool), speedup, cr [c][t], tc [c] and td [c]."""
+    import torch
+    T, B, D = (int(v) for v in x.shape)
+    if B < 1 or reps < 1 or not pool:
+        raise ECError(EC_ERR_INVALID, "offline_comp_config")
+    raw = 4.0 * T * B * D
+    strm = stream or torch.cuda.current_stream()
+    crs, tcs, tds = [], [], []
+    for coder in pool:
+        plan = Plan(T, B, D, 1, eb_mode, eb, table_mult=table_mult, schedule=schedule,
+                    device=x.device, coder=coder)
+        out = plan.empty_stream()
+        y = torch.empty_like(x)
+        plan.compress(x, out, iteration, stream=strm)
+        _, nbytes, per, _ = plan.ratio(per_segment=True)
+        plan.decompress(out[:nbytes], y, stream=strm)
+        plan.ratio()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record(strm)
+        for _ in range(reps):
+            plan.compress(x, out, iteration, stream=strm)
+        ev[1].record(strm)
+        for _ in range(reps):
+            plan.decompress(out[:nbytes], y, stream=strm)
+        ev[2].record(strm)
+        plan.ratio()
+        ev[2].synchronize()
+        tc_s = ev[0].elapsed_time(ev[1]) / 1e3 / reps
+        td_s = ev[1].elapsed_time(ev[2]) / 1e3 / reps
+        crs.append(per)
+        tcs.append(raw / tc_s)
+        tds.append(raw / td_s)
+        plan.close()
+    best, sp = select_coders(crs, tcs, tds, bw)
+    return {"table_coder": [int(pool[b]) for b in best], "best": best, "speedup": sp,
+            "cr": crs, "tc": tcs, "td": tds}
 
 
 # --- canonical Huffman coder (include/ec_huffman.h) ------------------------

@@ -90,7 +90,8 @@ struct Work {
   uint32_t* tile_hsize;          // [ntiles] Huffman record bytes
   uint32_t* seg_coder;           // [nseg] 1: the segment is Huffman-coded
   uint16_t* hlut;                // [nseg][4096] decode tables
-  uint32_t* hvalid;              // [nseg] decode table valid; | 2: empty codebook (no symbol)
+  uint32_t* hvalid;              // [nseg] decode table valid
+  const uint32_t* table_coder;   // [T] coder of each table (constant), or NULL: EncArgs::coder
 };
 
 struct PrepArgs {
@@ -110,7 +111,7 @@ struct EncArgs {
   uint32_t eb_mode;
   int64_t iter;
   double sched;                  // iteration-wise factor, computed on the host
-  uint32_t coder;                // kCoderBitpack, kCoderHuffman or kCoderAuto
+  uint32_t coder;                // the stream's coder: kCoderBitpack, kCoderHuffman or kCoderAuto
   uint64_t hash_keep;            // mask applied to row hashes (tests weaken it)
   Report* report;                // device pointer of the pinned report block
   uint32_t* seg_meta;            // in the report block: [nseg][2] U, eb valid (or NULL)

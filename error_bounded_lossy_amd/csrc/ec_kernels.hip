@@ -1999,7 +1999,8 @@ __global__ void __launch_bounds__(kThreads) ec_seg_choose(EncArgs a) {
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t s = blockIdx.x * (kThreads / 64) + wave_id();
   if (s >= a.sh.nseg) return;
-  if (a.w.seg_eb[s] == 0 || a.coder == kCoderBitpack) {
+  const uint32_t coder = a.w.table_coder ? a.w.table_coder[s % a.sh.T] : a.coder;
+  if (a.w.seg_eb[s] == 0 || coder == kCoderBitpack) {
     if (lane == 0) a.w.seg_coder[s] = 0;
     return;
   }
@@ -2017,7 +2018,7 @@ __global__ void __launch_bounds__(kThreads) ec_seg_choose(EncArgs a) {
   }
   bp = wave_sum_u64(bp);
   hf = wave_sum_u64(hf) + align_up(book_bytes(a.w.hbooks + (uint64_t)s * kBookStride), 16);
-  if (lane == 0) a.w.seg_coder[s] = (a.coder == kCoderHuffman || hf < bp) ? 1u : 0u;
+  if (lane == 0) a.w.seg_coder[s] = (coder == kCoderHuffman || hf < bp) ? 1u : 0u;
 }
 
 // One wave per size block: the items (record bytes plus the tables a tile

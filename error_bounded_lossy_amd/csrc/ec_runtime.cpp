@@ -19,7 +19,8 @@ uint64_t aup(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 
 struct Layout {
   // byte offsets inside the workspace
-  uint64_t eb_base, mult, seg_tile_base, hash_off, hash_log2, range_part;
+  uint64_t eb_base, mult, seg_tile_base, hash_off, hash_log2, range_part, table_coder = 0;
+  uint32_t stream_coder = 1;  // the header's coder field
   uint64_t dyn, seg_start, seg_end, chunk_start, seg_fin;
   uint64_t tile_status, block_status, tile_inserted, tile_rec, tile_U, tile_nout, hash;
   uint64_t stage_pl = 0, stage_w = 0, stage_om = 0, stage_slot = 0;
@@ -69,11 +70,23 @@ ec_status make_layout(const ec_plan_desc* d, Layout* L) {
   const uint32_t T = d->num_tables, B = d->rows, D = d->dim, P = d->num_chunks;
   if (T < 1 || D < 1 || P < 1 || !d->eb) return EC_ERR_INVALID;
   if (d->eb_mode != EC_EB_ABS && d->eb_mode != EC_EB_REL_RANGE) return EC_ERR_INVALID;
-  if (d->coder != EC_CODER_BITPACK && d->coder != EC_CODER_HUFFMAN && d->coder != EC_CODER_AUTO)
-    return EC_ERR_INVALID;
+  auto coder_ok = [](int32_t c) {
+    return c == EC_CODER_BITPACK || c == EC_CODER_HUFFMAN || c == EC_CODER_AUTO;
+  };
+  if (!coder_ok(d->coder)) return EC_ERR_INVALID;
+  L->stream_coder = (uint32_t)d->coder;
+  if (d->table_coder) {  // per table: the stream's coder follows from them
+    bool all1 = true, all2 = true;
+    for (uint32_t t = 0; t < T; t++) {
+      if (!coder_ok(d->table_coder[t])) return EC_ERR_INVALID;
+      all1 = all1 && d->table_coder[t] == EC_CODER_BITPACK;
+      all2 = all2 && d->table_coder[t] == EC_CODER_HUFFMAN;
+    }
+    L->stream_coder = all1 ? EC_CODER_BITPACK : (all2 ? EC_CODER_HUFFMAN : EC_CODER_AUTO);
+  }
+  L->huff = L->stream_coder != EC_CODER_BITPACK;
   // Huffman segments: for the wave64 paths (D = 64, 128, 256) only
-  if (d->coder != EC_CODER_BITPACK && !ec::encode_has_assembly(D)) return EC_ERR_UNSUPPORTED;
-  L->huff = d->coder != EC_CODER_BITPACK;
+  if (L->huff && !ec::encode_has_assembly(D)) return EC_ERR_UNSUPPORTED;
   if (d->debug_hash_bits > 64) return EC_ERR_INVALID;
   const ec_schedule& s = d->sched;
   if (s.kind == EC_SCHED_INV_SQRT) {
@@ -160,6 +173,7 @@ ec_status make_layout(const ec_plan_desc* d, Layout* L) {
   L->seg_tile_base = take(4ull * (nseg + 1));
   L->hash_off = take(8ull * nseg);
   L->hash_log2 = take(4ull * nseg);
+  if (d->table_coder) L->table_coder = take(4ull * T);
   L->range_part = take(8ull * T * L->nbr);
   o = aup(o, 256);
   L->dyn = o;
@@ -292,6 +306,7 @@ ec::Work make_work(const Layout& L, uint8_t* ws) {
   w.hash_off = reinterpret_cast<const uint64_t*>(ws + L.hash_off);
   w.hash_log2 = reinterpret_cast<const uint32_t*>(ws + L.hash_log2);
   w.range_part = reinterpret_cast<float*>(ws + L.range_part);
+  w.table_coder = L.table_coder ? reinterpret_cast<const uint32_t*>(ws + L.table_coder) : nullptr;
   w.nbr = L.nbr;
   w.dyn = reinterpret_cast<uint64_t*>(ws + L.dyn);
   w.dyn_words = L.dyn_bytes / 8;
@@ -378,6 +393,7 @@ ec_status ec_plan(const ec_plan_desc* desc, ec_plan_t* out) {
   if (desc->table_mult) pl->mult.assign(desc->table_mult, desc->table_mult + T);
   pl->desc.eb = pl->eb.data();
   pl->desc.table_mult = nullptr;
+  pl->desc.table_coder = nullptr;  // copied into the constants below
   pl->ws = static_cast<uint8_t*>(desc->d_workspace);
 
   size_t lds = ec::encode_lds_bytes(L.sh.D);
@@ -429,6 +445,7 @@ ec_status ec_plan(const ec_plan_desc* desc, ec_plan_t* out) {
   std::memcpy(img + L.seg_tile_base, L.seg_tile_base_v.data(), 4ull * L.seg_tile_base_v.size());
   std::memcpy(img + L.hash_off, L.hash_off_v.data(), 8ull * L.hash_off_v.size());
   std::memcpy(img + L.hash_log2, L.hash_log2_v.data(), 4ull * L.hash_log2_v.size());
+  if (desc->table_coder) std::memcpy(img + L.table_coder, desc->table_coder, 4ull * T);
   // set-up of the static scratch on this device (its address, once per device)
   void* scr = nullptr;
   if (ec::static_scratch(&scr) != hipSuccess) {
@@ -598,6 +615,35 @@ ec_status ec_homo_counts(ec_plan_t pl, int64_t iter, const float* d_in, void* d_
   return EC_OK;
 }
 
+double ec_speedup(double cr, double bw, double tc, double td) {
+  return 1.0 / (1.0 / cr + bw * (1.0 / tc + 1.0 / td));
+}
+
+ec_status ec_select_coders(uint32_t num_tables, uint32_t ncomp, const double* cr, const double* tc,
+                           const double* td, double bw, int32_t* best, double* speedup) {
+  auto pos = [](double v) { return v > 0.0 && std::isfinite(v); };
+  if (ncomp == 0 || !cr || !tc || !td || !best || !pos(bw)) return EC_ERR_INVALID;
+  for (uint32_t c = 0; c < ncomp; c++) {
+    if (!pos(tc[c]) || !pos(td[c])) return EC_ERR_INVALID;
+    for (uint32_t t = 0; t < num_tables; t++)
+      if (!pos(cr[(size_t)c * num_tables + t])) return EC_ERR_INVALID;
+  }
+  for (uint32_t t = 0; t < num_tables; t++) {
+    int32_t b = 0;
+    double v = ec_speedup(cr[t], bw, tc[0], td[0]);
+    for (uint32_t c = 1; c < ncomp; c++) {
+      const double w = ec_speedup(cr[(size_t)c * num_tables + t], bw, tc[c], td[c]);
+      if (w > v) {
+        v = w;
+        b = (int32_t)c;
+      }
+    }
+    best[t] = b;
+    if (speedup) speedup[t] = v;
+  }
+  return EC_OK;
+}
+
 ec_status ec_classify_tables(uint32_t num_tables, const double* homo_index, double l_thresh,
                              double s_thresh, double alpha, double beta, int32_t* table_class,
                              float* table_mult) {
@@ -705,7 +751,7 @@ ec_status enqueue_compress(ec_plan_s* pl, const ec::Work& work, bool clear, int6
   ea.eb_mode = (uint32_t)pl->desc.eb_mode;
   ea.iter = iter;
   ea.sched = schedule_factor(pl->desc.sched, iter);
-  ea.coder = (uint32_t)pl->desc.coder;
+  ea.coder = pl->L.stream_coder;
   uint32_t hb = pl->desc.debug_hash_bits;
   ea.hash_keep = (hb == 0 || hb >= 64) ? ~0ull : ((1ull << hb) - 1ull);
   ea.report = pl->report_dev;

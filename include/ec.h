@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define EC_ABI_VERSION 1u
+#define EC_ABI_VERSION 2u
 
 typedef struct ec_plan_s* ec_plan_t;
 
@@ -132,6 +132,12 @@ typedef struct {
                                aligned; owned by the caller, used by the plan
                                until ec_plan_destroy                           */
   size_t workspace_bytes;
+  const int32_t* table_coder; /* host [T] ec_coder of each table (Algorithm 2's
+                               table-wise configuration, e.g. from
+                               ec_select_coders) or NULL for `coder`; copied
+                               by ec_plan.  The stream's coder field is then
+                               BITPACK, HUFFMAN or AUTO as the tables' coders
+                               are all bit planes, all Huffman, or mixed.     */
 } ec_plan_desc;
 
 /* Largest supported D on the current device (limited by LDS per workgroup). */
@@ -214,6 +220,22 @@ typedef enum { EC_CLASS_LARGE = 0, EC_CLASS_MEDIUM = 1, EC_CLASS_SMALL = 2 } ec_
 ec_status ec_classify_tables(uint32_t num_tables, const double* homo_index, double l_thresh,
                              double s_thresh, double alpha, double beta, int32_t* table_class,
                              float* table_mult);
+
+/* Eq. (2) of section III-D ("Selection Between Two Encoders"): the
+ * communication speed-up of a compressor with compression ratio cr and
+ * compression / decompression throughputs tc, td over a link of bandwidth bw
+ * (all throughputs in one unit): 1 / (1/cr + bw * (1/tc + 1/td)).  Host only. */
+double ec_speedup(double cr, double bw, double tc, double td);
+
+/* Algorithm 2 (OfflineCompConfig): for each of num_tables tables, the
+ * compressor of a pool of ncomp whose eq. (2) speed-up is largest, from the
+ * ratios cr[c * num_tables + t] measured on a sample of the table and the
+ * pool's throughputs tc[c], td[c] over bandwidth bw; on equal speed-ups the
+ * earlier compressor.  best[t] gets the index, speedup[t] (may be NULL) its
+ * speed-up.  Host only.  EC_ERR_INVALID for an empty pool, NULL arrays, or
+ * values that are not finite and > 0. */
+ec_status ec_select_coders(uint32_t num_tables, uint32_t ncomp, const double* cr, const double* tc,
+                           const double* td, double bw, int32_t* best, double* speedup);
 
 /* Bytes of the library's static device scratch (one copy per device). */
 #define EC_STATIC_SCRATCH_BYTES (64ull << 20)

@@ -142,3 +142,43 @@ def test_table_classification_matches_the_oracle():
     for bad in [(0.5, 0.4, 2.0, 2.0), (0.1, 0.3, 0.0, 2.0), (0.1, 0.3, 2.0, float("inf"))]:
         with pytest.raises(ec.ECError):
             ec.classify_tables([0.2], *bad)
+
+
+def test_speedup_and_selection_match_the_oracle():
+    """ec_speedup / ec_select_coders (host code in the library) against the
+    oracle's eq. (2) and Algorithm 2 on random pools, ties included (the
+    earlier compressor wins); invalid pools are rejected."""
+    import numpy as np
+    import oracle as O
+    rng = np.random.default_rng(11)
+    for _ in range(200):
+        cr, bw, tc, td = (float(v) for v in rng.uniform(0.5, 50, 4))
+        assert ec.speedup(cr, bw, tc, td) == O.speedup(cr, bw, tc, td)
+    for _ in range(50):
+        C, T = int(rng.integers(1, 5)), int(rng.integers(1, 30))
+        cr = rng.uniform(1, 20, (C, T))
+        tc, td = rng.uniform(10, 400, C), rng.uniform(10, 400, C)
+        if C > 1:
+            cr[1, : T // 3] = cr[0, : T // 3]  # a tie where the pool's
+            tc[1], td[1] = tc[0], td[0]        # first two are the same
+        bw = float(rng.uniform(0.5, 50))
+        best, sp = ec.select_coders(cr.tolist(), tc.tolist(), td.tolist(), bw)
+        obest, osp = O.select(cr, tc, td, bw)
+        assert best == [int(b) for b in obest]
+        assert np.array_equal(np.array(sp), osp)
+    for bad in [([[2.0]], [0.0], [1.0], 1.0), ([[2.0]], [1.0], [1.0], float("nan")),
+                ([[-1.0]], [1.0], [1.0], 1.0), ([[2.0]], [1.0], [float("inf")], 1.0)]:
+        with pytest.raises(ec.ECError):
+            ec.select_coders(*bad)
+    with pytest.raises(ec.ECError):
+        ec.select_coders([], [], [], 1.0)
+
+
+def test_table_coder_validation():
+    """A per-table coder array is checked like the plan's coder; Huffman
+    tables need the wave64 paths (D = 64, 128, 256)."""
+    assert ec.workspace_bytes(3, 100, 128, table_coder=[1, 2, 3]) > 0
+    assert ec.workspace_bytes(3, 100, 24, table_coder=[1, 1, 1]) > 0
+    assert ec.workspace_bytes(3, 100, 24, table_coder=[1, 2, 1]) == 0
+    assert ec.workspace_bytes(3, 100, 128, table_coder=[1, 4, 1]) == 0
+    assert ec.workspace_bytes(2, 100, 128, table_coder=[0, 1]) == 0

@@ -116,6 +116,53 @@ def test_workloads_full_size(name, coder):
         f"{sum(1 for s in st if s.valid and _flags(got, s) & 2)}/{len(st)}")
 
 
+@pytest.mark.parametrize("tcoder", [(1, 2, 3, 3), (2, 2, 2, 2), (1, 1, 1, 1), (3, 1, 2, 1)])
+def test_per_table_coders(tcoder):
+    """Algorithm 2's table-wise configuration: each table coded by its own
+    coder; the stream's coder field follows from them; byte for byte the
+    oracle with the same per-table coders."""
+    rng = np.random.default_rng(sum(tcoder) * 7 + tcoder[0])
+    T, B, D = 4, 900, 128
+    x = dup_rows(rng, T, B, D, scale=0.05, frac_unique=0.3)
+    x[2] = rng.normal(0, 1, (B, D)).astype(np.float32)   # few repeats, wide codes
+    x[3, :, 1:] = 0.0                                     # nearly all-zero codes
+    cfg = cfg_of(T, B, D, 2, 1, 0.01, 1)
+    cfg.table_coder = tuple(tcoder)
+    say(f"[huffstream] table coders {tcoder}")
+    ref = O.compress(cfg, 1, x, debug=False)
+    plan = ec.Plan(T, B, D, 2, ec.EB_REL_RANGE, 0.01, coder=ec.CODER_BITPACK,
+                   table_coder=tcoder)
+    got, y, cr = gpu_round_trip(plan, torch.from_numpy(x).cuda(), 1)
+    assert np.array_equal(got, ref.stream)
+    np.testing.assert_array_equal(y.view(np.uint32), O.decompress(cfg, ref.stream).view(np.uint32))
+    st = SF.parse(ref.stream)
+    SF.check_coder_choice(st, ref.stream, O.huff_lengths, table_coder=tcoder)
+
+
+def test_offline_comp_config_selects_and_compresses():
+    """Algorithm 2 end to end: the pool's ratios and throughputs measured on
+    a sample, the selection equal to the oracle's on those figures, and a
+    plan with the selected coders byte for byte the oracle's."""
+    rng = np.random.default_rng(5)
+    T, B, D = 6, 4096, 128
+    x = dup_rows(rng, T, B, D, scale=0.05, frac_unique=0.05)
+    x[1] = rng.normal(0, 1, (B, D)).astype(np.float32)
+    x[4] = rng.normal(0, 3, (B, D)).astype(np.float32)
+    xt = torch.from_numpy(x).cuda()
+    for bw in (1e9, 1e12):
+        r = ec.offline_comp_config(xt, bw, eb_mode=ec.EB_REL_RANGE, eb=0.01, reps=3)
+        say(f"[huffstream] offline selection bw={bw:g}: {r['table_coder']} "
+            f"tc={[round(v / 1e9, 1) for v in r['tc']]} GB/s td={[round(v / 1e9, 1) for v in r['td']]} GB/s")
+        obest, osp = O.select(np.array(r["cr"]), r["tc"], r["td"], bw)
+        assert r["best"] == [int(b) for b in obest]
+        assert np.array_equal(np.array(r["speedup"]), osp)
+        cfg = cfg_of(T, B, D, 1, 1, 0.01, 1)
+        cfg.table_coder = tuple(r["table_coder"])
+        plan = ec.Plan(T, B, D, 1, ec.EB_REL_RANGE, 0.01, table_coder=r["table_coder"])
+        got, y, _ = gpu_round_trip(plan, xt, 0)
+        assert np.array_equal(got, O.compress(cfg, 0, x, debug=False).stream)
+
+
 def _flags(buf, seg):
     return int.from_bytes(buf[seg.offset + 12:seg.offset + 16].tobytes(), "little")
 
