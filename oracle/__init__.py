@@ -45,7 +45,7 @@ class _Cfg(ctypes.Structure):
         ("sched_kind", ctypes.c_int32), ("sched_steps", ctypes.c_int32),
         ("sched_t0", ctypes.c_double), ("sched_k", ctypes.c_double),
         ("sched_phase", ctypes.c_int64), ("coder", ctypes.c_uint32),
-        ("table_coder", ctypes.POINTER(ctypes.c_int32)),
+        ("table_coder", ctypes.POINTER(ctypes.c_int32)), ("window", ctypes.c_uint32),
     ]
 
 
@@ -141,6 +141,7 @@ class Config:
     sched_steps: int = 1
     coder: int = CODER_BITPACK
     table_coder: tuple | None = None
+    window: int = 0
 
     def _c(self):
         eb = np.ascontiguousarray(np.asarray(self.eb, dtype=np.float32).reshape(-1))
@@ -157,7 +158,7 @@ class Config:
                  self.sched_kind, self.sched_steps, self.sched_t0, self.sched_k,
                  self.sched_phase, self.coder,
                  tc.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if tc is not None
-                 else ctypes.POINTER(ctypes.c_int32)())
+                 else ctypes.POINTER(ctypes.c_int32)(), self.window)
         return c, (eb, mult, tc)  # keep arrays alive with the struct
 
 

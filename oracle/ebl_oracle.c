@@ -192,6 +192,7 @@ static int cfg_ok(const ebo_cfg* c) {
   if (c->T < 1 || c->D < 1 || c->P < 1) return 0;
   if (c->eb_mode != EBO_EB_ABS && c->eb_mode != EBO_EB_REL) return 0;
   if (c->coder > EBO_CODER_AUTO) return 0;
+  if (c->window > 255) return 0;
   if (c->table_coder)
     for (uint32_t t = 0; t < c->T; t++)
       if (c->table_coder[t] < (int32_t)EBO_CODER_BITPACK || c->table_coder[t] > (int32_t)EBO_CODER_AUTO)
@@ -272,6 +273,31 @@ static int dedup_first(const uint64_t* keys, uint32_t rows, uint32_t D, uint32_t
     if (memcmp(keys + (size_t)r * D, keys + (size_t)head * D, sizeof(uint64_t) * D) != 0)
       head = r;
     first[r] = head;
+  }
+  free(order);
+  return 0;
+}
+
+/* The window of section III-E ("Compressor Fine-tuning"): the vector-based
+   LZ of section III-D looks back at most W rows for a row with the same key
+   (the pattern length is one row, so rows are compared whole).  match[r] =
+   the nearest earlier row within W rows with r's key, or r itself when
+   there is none.  Sorting rows by (key, row) puts each row right after the
+   nearest earlier row with its key. */
+static int window_match(const uint64_t* keys, uint32_t rows, uint32_t D, uint32_t W,
+                        uint32_t* match) {
+  if (rows == 0) return 0;
+  uint32_t* order = (uint32_t*)malloc(sizeof(uint32_t) * rows);
+  if (!order) return -1;
+  for (uint32_t r = 0; r < rows; r++) order[r] = r;
+  g_sort_keys = keys;
+  g_sort_D = D;
+  qsort(order, rows, sizeof(uint32_t), cmp_rows);
+  match[order[0]] = order[0];
+  for (uint32_t i = 1; i < rows; i++) {
+    uint32_t r = order[i], prev = order[i - 1];
+    int same = memcmp(keys + (size_t)r * D, keys + (size_t)prev * D, sizeof(uint64_t) * D) == 0;
+    match[r] = (same && r - prev <= W) ? prev : r;
   }
   free(order);
   return 0;
@@ -410,8 +436,20 @@ typedef struct {
   const float* x;           /* segment rows, row-major */
   const int32_t* q;         /* codes (0 for outliers) */
   const uint8_t* out;       /* outlier flags */
-  const uint32_t* first;    /* first occurrence per segment row */
+  const uint32_t* first;    /* first occurrence (windowed: match) per row */
+  uint32_t window;          /* 0, or W of a windowed segment */
 } seg_view;
+
+/* bytes of one reference: a u8 distance in windowed segments, else the
+   row as u16 or u32 */
+static uint32_t ref_bytes(uint32_t rows, uint32_t window) {
+  return window ? 1u : (rows <= 65536 ? 2u : 4u);
+}
+static void put_ref(uint8_t* at, uint32_t rb, uint32_t row, uint32_t target) {
+  if (rb == 1) put_u8(at, (uint8_t)(row - target));
+  else if (rb == 2) put_u16(at, (uint16_t)target);
+  else put_u32(at, target);
+}
 
 /* Huffman-coded record of tile k (mode 2), when the segment's coder is the
    entropy coder of section III-D with code lengths hlen / codes hcode:
@@ -447,7 +485,7 @@ static uint64_t huff_record(const seg_view* sv, uint32_t k, uint64_t bitmap, uin
       }
     }
     size_t nw = ebo_huff_encode(sym, nE, hlen, hcode, words, coff);
-    uint32_t rb = sv->rows <= 65536 ? 2 : 4;
+    uint32_t rb = ref_bytes(sv->rows, sv->window);
     uint64_t off_opos = align_up(16 + (uint64_t)rb * (n - U), 4);
     uint64_t off_oval = off_opos + 4ull * nout;
     uint64_t off_ct = off_oval + 4ull * nout;
@@ -462,9 +500,7 @@ static uint64_t huff_record(const seg_view* sv, uint32_t k, uint64_t bitmap, uin
       uint32_t j = 0;
       for (uint32_t i = 0; i < n; i++) {
         if ((bitmap >> i) & 1u) continue;
-        uint32_t ref = sv->first[r0 + i];
-        if (rb == 2) put_u16(out + 16 + 2 * j, (uint16_t)ref);
-        else put_u32(out + 16 + 4 * j, ref);
+        put_ref(out + 16 + rb * j, rb, r0 + i, sv->first[r0 + i]);
         j++;
       }
       for (uint32_t o = 0; o < nout; o++) {
@@ -550,7 +586,7 @@ static uint32_t encode_tile(const seg_view* sv, uint32_t k, buf_t* b, uint32_t* 
       w[blk] = (uint8_t)bits;
       sumw += bits;
     }
-    uint32_t rb = sv->rows <= 65536 ? 2 : 4;
+    uint32_t rb = ref_bytes(sv->rows, sv->window);
     uint64_t off_refs = align_up(16 + nblk, 4);
     uint64_t off_opos = align_up(off_refs + (uint64_t)rb * (n - U), 4);
     uint64_t off_oval = off_opos + 4ull * nout;
@@ -567,9 +603,7 @@ static uint32_t encode_tile(const seg_view* sv, uint32_t k, buf_t* b, uint32_t* 
         uint32_t j = 0;
         for (uint32_t i = 0; i < n; i++) {
           if ((bitmap >> i) & 1u) continue;
-          uint32_t ref = sv->first[r0 + i];
-          if (rb == 2) put_u16(r + off_refs + 2 * j, (uint16_t)ref);
-          else put_u32(r + off_refs + 4 * j, ref);
+          put_ref(r + off_refs + rb * j, rb, r0 + i, sv->first[r0 + i]);
           j++;
         }
         for (uint32_t o = 0; o < nout; o++) {
@@ -644,7 +678,9 @@ static int encode_segment(const seg_view* sv, uint32_t nt, float eb, const uint8
   put_u32(sh + 0, sv->rows);
   put_u32(sh + 4, nt);
   put_f32(sh + 8, sv->valid ? eb : 0.0f);
-  put_u32(sh + 12, (sv->valid ? 1u : 0u) | (hlen ? 2u : 0u));
+  uint32_t flags = sv->valid ? 1u | (hlen ? 2u : 0u) : 0u;
+  if (sv->valid && sv->window) flags |= 4u | (sv->window << 8);
+  put_u32(sh + 12, flags);
   put_u32(sh + 16, Useg);
   put_u32(sh + 20, nout_seg);
   put_u64(sh + 24, (uint64_t)b->n);
@@ -725,7 +761,9 @@ int ebo_compress(const ebo_cfg* c, int64_t iter, const float* x, uint8_t* out, s
             o[i] = (uint8_t)ebo_quantize(xs[i], eb, &q[i]);
             keys[i] = elem_key(q[i], o[i], xs[i]);
           }
-          if (dedup_first(keys, rows, D, first) != 0) rc = EBO_ERR_OOM;
+          int e = c->window ? window_match(keys, rows, D, c->window, first)
+                            : dedup_first(keys, rows, D, first);
+          if (e != 0) rc = EBO_ERR_OOM;
         }
       }
       if (rc == EBO_OK) {
@@ -740,7 +778,7 @@ int ebo_compress(const ebo_cfg* c, int64_t iter, const float* x, uint8_t* out, s
         }
         if (eb_seg) eb_seg[(size_t)p * T + t] = valid ? eb : 0.0f;
 
-        seg_view sv = {D, rows, valid, xs, q, o, first};
+        seg_view sv = {D, rows, valid, xs, q, o, first, c->window};
         /* the bit-plane segment, and with the Huffman coder also the Huffman
            segment; coder 3 keeps the Huffman one when it is strictly smaller */
         buf_t bp = {0}, hf = {0};
@@ -789,6 +827,7 @@ typedef struct {
   float eb;
   int valid;
   int huff;                       /* Huffman segment (flags bit 1) */
+  uint32_t window;                /* W of a windowed segment (flags bit 2), else 0 */
   uint8_t hlen[EBO_HUFF_NSYM];    /* its code lengths */
   uint64_t rec_lo;                /* records start at or after this offset */
   uint16_t** sym;                 /* [ntiles]: decoded E symbols of mode-2 records */
@@ -800,10 +839,10 @@ typedef struct {
   uint32_t nblk, nch;
 } rec_lay;
 static rec_lay record_layout(uint32_t mode, uint32_t n, uint32_t U, uint32_t nout, uint32_t D,
-                             uint32_t rows) {
+                             uint32_t rows, uint32_t window) {
   rec_lay L;
   uint64_t nE = (uint64_t)U * D;
-  uint32_t rb = rows <= 65536 ? 2 : 4;
+  uint32_t rb = ref_bytes(rows, window);
   L.nblk = (uint32_t)((nE + 63) / 64);
   L.nch = (uint32_t)((nE + EBO_HUFF_CHUNK - 1) / EBO_HUFF_CHUNK);
   L.refs = mode == 2 ? 16 : align_up(16 + L.nblk, 4);
@@ -824,10 +863,41 @@ static int rec_locate(const seg_in* g, uint32_t k, const uint8_t** rec, uint64_t
   return 0;
 }
 
+/* the reference of row i of a coded tile record (not a bitmap row): the row
+   it names, or in a windowed segment the distance back */
+static uint32_t get_ref(const seg_in* g, const uint8_t* rec, const rec_lay* L, uint64_t bitmap,
+                        uint32_t i) {
+  uint32_t j = i - popcount64(bitmap & (((uint64_t)1 << i) - 1));
+  uint32_t rb = ref_bytes(g->rows, g->window);
+  if (rb == 1) return rec[L->refs + j];
+  return rb == 2 ? get_u16(rec + L->refs + 2 * j) : get_u32(rec + L->refs + 4 * j);
+}
+
+/* In a windowed segment, the row whose key row r has: follow the matches of
+   repeated rows of coded tiles back (distances are at least 1, so the chain
+   ends) to a literal or a row of a RAW tile.  Records are checked first. */
+static uint32_t window_root(const seg_in* g, uint32_t r) {
+  for (;;) {
+    uint32_t k = r / 64, i = r % 64;
+    const uint8_t* rec;
+    uint64_t avail;
+    if (rec_locate(g, k, &rec, &avail)) return r;
+    uint64_t bitmap = get_u64(rec);
+    uint32_t mode = rec[14];
+    if (mode == 0 || ((bitmap >> i) & 1u)) return r;
+    uint32_t n = g->rows - 64 * k < 64 ? g->rows - 64 * k : 64;
+    rec_lay L = record_layout(mode, n, get_u16(rec + 12), get_u32(rec + 8), g->D, g->rows,
+                              g->window);
+    r -= get_ref(g, rec, &L, bitmap, i);
+  }
+}
+
 /* reconstruct segment row r into y (D floats) as its KEY's values: a coded
-   first-occurrence row is decoded, a row of a RAW tile is requantized.  Used
-   for every row that is the target of a reference.  Returns 0 on success. */
+   first-occurrence row is decoded, a row of a RAW tile is requantized, and in
+   a windowed segment a repeated row takes its chain's root's key.  Used for
+   every row that is the target of a reference.  Returns 0 on success. */
 static int decode_key_row(const seg_in* g, uint32_t r, float* y) {
+  if (g->window) r = window_root(g, r);
   uint32_t D = g->D, k = r / 64, i = r % 64;
   const uint8_t* rec;
   uint64_t avail;
@@ -837,7 +907,9 @@ static int decode_key_row(const seg_in* g, uint32_t r, float* y) {
   uint32_t nout = get_u32(rec + 8);
   uint32_t U = get_u16(rec + 12);
   uint32_t mode = rec[14];
-  if (!((bitmap >> i) & 1u)) return -1; /* a reference must name a first occurrence */
+  /* a reference must name a first occurrence (windowed: any row of a RAW
+     tile, whose raw values give its key) */
+  if (!((bitmap >> i) & 1u) && !(g->window && mode == 0)) return -1;
   if (mode == 0) {
     if (16 + 4ull * n * D > avail) return -1;
     for (uint32_t d = 0; d < D; d++) {
@@ -849,7 +921,7 @@ static int decode_key_row(const seg_in* g, uint32_t r, float* y) {
   }
   if (mode != 1 && mode != 2) return -1;
   uint32_t u = popcount64(bitmap & (((uint64_t)1 << i) - 1));
-  rec_lay L = record_layout(mode, n, U, nout, D, g->rows);
+  rec_lay L = record_layout(mode, n, U, nout, D, g->rows, g->window);
   if (mode == 2) {
     /* symbols decoded when the record was checked */
     if (!g->sym[k]) return -1;
@@ -922,8 +994,7 @@ static int check_record(seg_in* g, uint32_t k) {
   if (mode != (g->huff ? 2u : 1u)) return -1;
   uint64_t nE = (uint64_t)U * D;
   if (nout > nE) return -1;
-  rec_lay L = record_layout(mode, n, U, nout, D, g->rows);
-  uint32_t rb = g->rows <= 65536 ? 2 : 4;
+  rec_lay L = record_layout(mode, n, U, nout, D, g->rows, g->window);
   if (mode == 1) {
     if (L.pl > avail) return -1;
     uint64_t sumw = 0;
@@ -935,12 +1006,14 @@ static int check_record(seg_in* g, uint32_t k) {
   } else if (huff_record_decode(g, k, rec, avail, &L, nE)) {
     return -1;
   }
-  uint32_t j = 0;
   for (uint32_t i = 0; i < n; i++) {
     if ((bitmap >> i) & 1u) continue;
-    uint32_t ref = rb == 2 ? get_u16(rec + L.refs + 2 * j) : get_u32(rec + L.refs + 4 * j);
-    if (ref >= 64 * k + i) return -1; /* must point to an earlier row */
-    j++;
+    uint32_t ref = get_ref(g, rec, &L, bitmap, i);
+    if (g->window) { /* a distance 1..W back, inside the segment */
+      if (ref < 1 || ref > g->window || ref > 64 * k + i) return -1;
+    } else if (ref >= 64 * k + i) {
+      return -1; /* must point to an earlier row */
+    }
   }
   for (uint32_t o = 0; o < nout; o++) {
     uint32_t pos = get_u32(rec + L.opos + 4 * o);
@@ -970,9 +1043,7 @@ static int decode_segment(seg_in* g, uint32_t U_seg, uint32_t nout_seg, float* y
     uint64_t bitmap = get_u64(rec);
     uint32_t U = get_u16(rec + 12);
     uint32_t mode = rec[14];
-    rec_lay L = record_layout(mode, n, U, get_u32(rec + 8), D, g->rows);
-    uint32_t rb = g->rows <= 65536 ? 2 : 4;
-    uint32_t j = 0;
+    rec_lay L = record_layout(mode, n, U, get_u32(rec + 8), D, g->rows, g->window);
     for (uint32_t i = 0; i < n; i++) {
       float* yr = y + (size_t)(64 * k + i) * D;
       if (mode == 0) {
@@ -980,8 +1051,8 @@ static int decode_segment(seg_in* g, uint32_t U_seg, uint32_t nout_seg, float* y
       } else if ((bitmap >> i) & 1u) {
         if (decode_key_row(g, 64 * k + i, yr)) return -1;
       } else {
-        uint32_t ref = rb == 2 ? get_u16(rec + L.refs + 2 * j) : get_u32(rec + L.refs + 4 * j);
-        j++;
+        uint32_t ref = get_ref(g, rec, &L, bitmap, i);
+        if (g->window) ref = 64 * k + i - ref;
         if (decode_key_row(g, ref, yr)) return -1;
       }
     }
@@ -1035,13 +1106,19 @@ int ebo_decompress(const uint8_t* s, size_t nbytes, uint32_t T, uint32_t B, uint
       g->bytes = get_u64(g->s + 24);
       g->D = D;
       g->sym = NULL;
-      if (g->rows != rows || g->ntiles != nt || flags > 3 || flags == 2 ||
+      /* flags: 0, 1 or 3, or 5 / 7 with the window W (1..255) in bits 8-15 */
+      uint32_t fl = flags & 0xFFu, win = (flags >> 8) & 0xFFu;
+      int flags_ok = (flags >> 16) == 0 &&
+                     ((win == 0 && (fl == 0 || fl == 1 || fl == 3)) ||
+                      (win != 0 && (fl == 5 || fl == 7)));
+      if (g->rows != rows || g->ntiles != nt || !flags_ok ||
           g->bytes > cb - so || g->bytes < seg_prefix_bytes(nt)) {
         rc = EBO_ERR_CORRUPT;
         break;
       }
       g->valid = (int)(flags & 1u);
       g->huff = (int)((flags >> 1) & 1u);
+      g->window = win;
       if (g->valid != ebo_eb_valid(g->eb) || (g->huff && coder == EBO_CODER_BITPACK) ||
           (g->valid && !g->huff && coder == EBO_CODER_HUFFMAN)) {
         rc = EBO_ERR_CORRUPT;

@@ -43,8 +43,10 @@
  * SEGMENT (p,t)  (16-byte aligned; its size is a multiple of 16)
  *   header, 32 bytes:
  *     0 u32 rows   4 u32 ntiles = ceil(rows/64)   8 f32 eb (0 when invalid)
- *     12 u32 flags (bit 0: eb valid; bit 1: Huffman segment, only with bit 0)
- *     16 u32 U (first occurrences)
+ *     12 u32 flags (bit 0: eb valid; bit 1: Huffman segment, only with bit 0;
+ *        bit 2: windowed references, only with bit 0, and then bits 8-15
+ *        hold the window W in 1..255; every other bit 0)
+ *     16 u32 U (first occurrences; in a windowed segment, literal rows)
  *     20 u32 n_out (outliers stored in coded tiles)   24 u64 segment bytes
  *   tile directory: ntiles x u32 offset of each tile record from the segment
  *   start, zero-padded to 16; in a Huffman segment then the codebook
@@ -69,7 +71,11 @@
  *     at 16:                  widths, nblk x u8
  *     at align4:              refs, (n-U_t) x (u16 if rows <= 65536 else u32),
  *                             the segment row of each repeated row's first
- *                             occurrence, in row order
+ *                             occurrence, in row order; in a windowed
+ *                             segment (n-U_t) x u8, each the distance o in
+ *                             1..W back to the nearest earlier row with the
+ *                             same key (the vector-based LZ of section III-D
+ *                             with the window of section III-E)
  *     at align4:              outlier positions, n_out x u32, ascending index
  *                             into E
  *     right after:            outlier values, n_out x u32 raw fp32 bits
@@ -88,6 +94,14 @@
  *   A tile is BITPACK (HUFFMAN in a Huffman segment) iff its segment's eb is
  *   valid and that record is strictly smaller than the RAW record; otherwise
  *   RAW.
+ *
+ * WINDOWED SEGMENTS (window W >= 1): row r repeats when one of the W rows
+ * before it in the segment has its key; its match is the nearest such row.
+ * Rows without a match are the literals (bitmap bits).  The key of a row is
+ * decoded as: a row of a RAW tile, its raw values re-quantized; a literal of
+ * a coded tile, its codes and outliers; a repeated row of a coded tile, the
+ * key of its match (matches may chain).  Without a window (W = 0) every
+ * repeated row names the segment's first row with its key, a literal.
  */
 #ifndef EBL_ORACLE_H
 #define EBL_ORACLE_H
@@ -125,6 +139,8 @@ typedef struct {
   int64_t sched_phase;       /* STEP: length of the decay phase            */
   uint32_t coder;            /* EBO_CODER_*; 0 means EBO_CODER_BITPACK     */
   const int32_t* table_coder; /* [T] coder of each table, NULL: `coder`    */
+  uint32_t window;           /* 0: references to first occurrences; 1..255:
+                                windowed references (section III-E)        */
 } ebo_cfg;
 
 /* Iteration-wise factor (Algorithm 1 OnlineDecay, read non-cumulatively). */
@@ -182,8 +198,9 @@ size_t ebo_max_compressed_bytes(const ebo_cfg* c);
 /*
  * Compress x[T][B][D] (row-major fp32) into out.  Optional outputs (NULL to
  * skip): codes[T*B*D] (0 for outliers), outlier[T*B*D] (0/1),
- * first[T*B] (segment row of each row's first occurrence; row itself for
- * invalid-eb segments), eb_seg[P*T] (segment eb as stored).
+ * first[T*B] (segment row of each row's first occurrence, with a window its
+ * match; the row itself for literals and invalid-eb segments), eb_seg[P*T]
+ * (segment eb as stored).
  */
 int ebo_compress(const ebo_cfg* c, int64_t iter, const float* x, uint8_t* out, size_t cap,
                  size_t* out_bytes, int32_t* codes, uint8_t* outlier, uint32_t* first,

@@ -52,6 +52,7 @@ class Segment:
     nbytes: int
     tiles: list = field(default_factory=list)
     huff: bool = False
+    window: int = 0
     lengths: np.ndarray | None = None
     codes: dict | None = None
 
@@ -115,7 +116,9 @@ def parse(buf: np.ndarray) -> Stream:
                           bool(_u(buf, s0 + 12, 4) & 1), _u(buf, s0 + 16, 4),
                           _u(buf, s0 + 20, 4), _u(buf, s0 + 24, 8))
             flags = _u(buf, s0 + 12, 4)
-            assert flags in (0, 1, 3)
+            seg.window = (flags >> 8) & 0xFF
+            assert flags >> 16 == 0
+            assert (flags & 0xFF) in ((0, 1, 3) if seg.window == 0 else (5, 7))
             seg.huff = bool(flags & 2)
             # coder 1: no Huffman segment; coder 2: every valid segment is one
             assert not (seg.huff and coder == 1)
@@ -123,7 +126,8 @@ def parse(buf: np.ndarray) -> Stream:
             assert seg.rows == rows and seg.ntiles == (rows + 63) // 64
             mark(s0, 32)
             mark(s0 + 32, 4 * seg.ntiles)
-            rb = 2 if rows <= 65536 else 4
+            rb = ref_bytes(rows, seg.window)
+            rdt = {1: np.uint8, 2: np.uint16, 4: np.uint32}[rb]
             if seg.huff:
                 bo = s0 + 32 + _a(4 * seg.ntiles, 16)
                 seg.lengths, nbook = read_book(buf, bo)
@@ -148,16 +152,16 @@ def parse(buf: np.ndarray) -> Stream:
                         us = [i for i in range(n) if (tl.bitmap >> i) & 1]
                         q, o = quantize_np(raw[us].reshape(-1), seg.eb)
                         if seg.huff:
-                            coded = huff_size(q, o, n, len(us), D, rows, seg.lengths)
+                            coded = huff_size(q, o, n, len(us), D, rows, seg.lengths, seg.window)
                         else:
-                            coded = bitpack_size(raw, tl.bitmap, n, D, seg.eb, rows)
+                            coded = bitpack_size(raw, tl.bitmap, n, D, seg.eb, rows, seg.window)
                         assert coded >= raw_size, "RAW tile whose coded record would be smaller"
                 elif tl.mode == 2:
                     assert seg.huff and seg.valid
                     nE = tl.U * D
                     nd = n - tl.U
                     tl.refs = np.frombuffer(bytes(buf[ro + 16:ro + 16 + rb * nd]),
-                                            np.uint16 if rb == 2 else np.uint32).astype(np.int64)
+                                            rdt).astype(np.int64)
                     mark(ro + 16, rb * nd)
                     oop = _a(16 + rb * nd, 4)
                     tl.opos = np.frombuffer(bytes(buf[ro + oop:ro + oop + 4 * tl.n_out]),
@@ -186,7 +190,7 @@ def parse(buf: np.ndarray) -> Stream:
                     orf = _a(16 + nblk, 4)
                     nd = n - tl.U
                     tl.refs = np.frombuffer(bytes(buf[ro + orf:ro + orf + rb * nd]),
-                                            np.uint16 if rb == 2 else np.uint32).astype(np.int64)
+                                            rdt).astype(np.int64)
                     mark(ro + orf, rb * nd)
                     oop = _a(orf + rb * nd, 4)
                     tl.opos = np.frombuffer(bytes(buf[ro + oop:ro + oop + 4 * tl.n_out]),
@@ -274,19 +278,25 @@ def decode_chunks(words, ct, n, lengths, codes):
     return np.array(out, np.int64)
 
 
-def huff_size(q, o, n, U, D, rows, lengths):
+def ref_bytes(rows, window=0):
+    """Bytes of one reference: a u8 distance in windowed segments, else the
+    referenced row as u16 (segments up to 65536 rows) or u32."""
+    return 1 if window else (2 if rows <= 65536 else 4)
+
+
+def huff_size(q, o, n, U, D, rows, lengths, window=0):
     """Bytes of a tile's Huffman record for the codes q (outliers o) of its U
     first-occurrence rows."""
     sym = np.asarray(q, np.int64).reshape(-1) + 2047
     nE = U * D
     words = sum((int(lengths[sym[c:c + 256]].sum()) + 31) // 32 for c in range(0, nE, 256))
     n_out = int(np.asarray(o).sum())
-    rb = 2 if rows <= 65536 else 4
+    rb = ref_bytes(rows, window)
     oop = _a(16 + rb * (n - U), 4)
     return _a(oop + 8 * n_out + 4 * ((nE + 255) // 256 + 1) + 4 * words, 16)
 
 
-def bitpack_size(raw, bitmap, n, D, eb, rows):
+def bitpack_size(raw, bitmap, n, D, eb, rows, window=0):
     """Bytes the BITPACK record of a tile would take, rebuilt from its raw rows
     (n x D), its first-occurrence bitmap and the segment's eb."""
     us = [i for i in range(n) if (bitmap >> i) & 1]
@@ -299,7 +309,7 @@ def bitpack_size(raw, bitmap, n, D, eb, rows):
     m = zb.reshape(nblk, 64).max(axis=1) if nblk else np.zeros(0, np.int64)
     sw = int(sum(int(v).bit_length() for v in m))
     n_out = int(o.sum())
-    rb = 2 if rows <= 65536 else 4
+    rb = ref_bytes(rows, window)
     orf = _a(16 + nblk, 4)
     oop = _a(orf + rb * (n - len(us)), 4)
     opl = _a(oop + 8 * n_out, 8)
@@ -375,9 +385,15 @@ def decode(st: Stream, buf: np.ndarray):
                 else:
                     ref = int(tl.refs[j])
                     j += 1
-                    assert ref < r, "reference to a later row"
+                    if seg.window:  # a distance back to the nearest row with the key
+                        assert 1 <= ref <= min(seg.window, r), "distance out of the window"
+                        ref = r - ref
+                        qq, oo, vv = keyrow[ref]
+                        keyrow[r] = (qq, oo, vv)
+                    else:
+                        assert ref < r, "reference to a later row"
+                        qq, oo, vv = keyrow[ref]
                     first[seg.t, r0 + r] = ref
-                    qq, oo, vv = keyrow[ref]
                 codes[seg.t, r0 + r] = qq
                 outl[seg.t, r0 + r] = oo
                 y[seg.t, r0 + r] = vv
@@ -419,14 +435,14 @@ def _tile_codes(seg, tl, buf, D):
     return q, o
 
 
-def _bitpack_tile_size(q, o, n, U, D, rows):
+def _bitpack_tile_size(q, o, n, U, D, rows, window=0):
     z = np.where(q >= 0, 2 * q, -2 * q - 1)
     nE = U * D
     nblk = (nE + 63) // 64
     zb = np.zeros(nblk * 64, np.int64)
     zb[:nE] = z
     sw = sum(int(v).bit_length() for v in (zb.reshape(nblk, 64).max(axis=1) if nblk else []))
-    rb = 2 if rows <= 65536 else 4
+    rb = ref_bytes(rows, window)
     orf = _a(16 + nblk, 4)
     oop = _a(orf + rb * (n - U), 4)
     return _a(_a(oop + 8 * int(o.sum()), 8) + 8 * sw, 16)
@@ -447,8 +463,8 @@ def segment_form_sizes(seg, buf, D, lengths_of_hist):
     bp, hf = pre, pre + _a(book, 16)
     for tl, q, o in tiles:
         raw = 16 + _a(4 * tl.n * D, 16)
-        b = _bitpack_tile_size(q, o, tl.n, tl.U, D, seg.rows)
-        h = huff_size(q, o, tl.n, tl.U, D, seg.rows, lengths)
+        b = _bitpack_tile_size(q, o, tl.n, tl.U, D, seg.rows, seg.window)
+        h = huff_size(q, o, tl.n, tl.U, D, seg.rows, lengths, seg.window)
         bp += b if b < raw else raw
         hf += h if h < raw else raw
     return bp, hf, lengths

@@ -740,3 +740,147 @@ def test_coders_chosen_per_table():
     bp = O.Config(T=T, B=B, D=D, eb_mode=O.EB_REL, eb=(0.02,))
     allbp = O.Config(T=T, B=B, D=D, eb_mode=O.EB_REL, eb=(0.02,), table_coder=(1, 1, 1, 1))
     assert np.array_equal(O.compress(bp, 0, x).stream, O.compress(allbp, 0, x).stream)
+
+
+# --------------------------------------------------------------------------
+# windowed vector-LZ (section III-D "Vector-based LZ Encoding" with the
+# extended window of section III-E, Table VI)
+# --------------------------------------------------------------------------
+def row_keys(x, eb):
+    """Each row's key, quantized element by element with the pinned scalar
+    quantizer: ('q', code) or ('o', raw bits) per element."""
+    keys = []
+    for r in range(x.shape[0]):
+        key = []
+        for v in x[r]:
+            q, out = O.quantize(float(v), eb)
+            key.append(("o", np.float32(v).view(np.uint32).item()) if out else ("q", q))
+        keys.append(tuple(key))
+    return keys
+
+
+def brute_window(keys, W):
+    """Nearest earlier row within W rows with the same key, else the row."""
+    out = []
+    for r in range(len(keys)):
+        m = r
+        for r2 in range(r - 1, max(-1, r - W - 1), -1):
+            if keys[r2] == keys[r]:
+                m = r2
+                break
+        out.append(m)
+    return np.array(out)
+
+
+def zipf_rows(rng, B, D, distinct, a=1.1, scale=0.2):
+    """B rows drawn from `distinct` base rows with Zipf-like popularity."""
+    base = rng.normal(0, scale, (distinct, D)).astype(np.float32)
+    p = 1.0 / np.arange(1, distinct + 1) ** a
+    idx = rng.choice(distinct, size=B, p=p / p.sum())
+    return base[idx].astype(np.float32)
+
+
+@pytest.mark.parametrize("W", [1, 2, 7, 64, 255])
+@pytest.mark.parametrize("seed", range(2))
+def test_window_matches_brute_force(W, seed):
+    """The match of every row is the nearest earlier row within W with its
+    key (brute force over the window), the stream stores its distance, and
+    the reader's reconstruction is the oracle's."""
+    rng = np.random.default_rng(100 * W + seed)
+    B, D, P = 300, int(rng.integers(2, 9)), 2
+    eb = 0.05
+    x = np.stack([zipf_rows(rng, B, D, 40) for _ in range(2)])
+    x[0, 5, 0] = np.nan
+    x[0, 9] = x[0, 5]
+    x[1, 7, -1] = 1e9
+    cfg = O.Config(T=2, B=B, D=D, P=P, eb=(eb,), window=W)
+    c, st = check_stream(cfg, x)
+    for seg in st.segments:
+        assert seg.window == W
+        r0, r1 = seg.p * B // P, (seg.p + 1) * B // P
+        want = brute_window(row_keys(x[seg.t, r0:r1], eb), W)
+        np.testing.assert_array_equal(c.first[seg.t, r0:r1], want)
+        assert seg.U == int((want == np.arange(r1 - r0)).sum())
+        for k, tl in enumerate(seg.tiles):
+            if tl.mode == 0:
+                continue
+            rows = [64 * k + i for i in range(tl.n) if not (tl.bitmap >> i) & 1]
+            np.testing.assert_array_equal(tl.refs, [r - want[r] for r in rows])
+
+
+@pytest.mark.parametrize("coder", [1, 2, 3])
+def test_window_reconstruction_is_the_whole_segment_one(coder):
+    """Rows with one key reconstruct identically wherever their reference
+    points, so every window gives the values of the whole-segment
+    references, and a window covering the segment gives its literals."""
+    rng = np.random.default_rng(coder)
+    T, B, D = 3, 250, 16
+    x = np.stack([zipf_rows(rng, B, D, d) for d in (5, 30, 200)])
+    x[1, 64:128] = rng.normal(0, 1e4, (64, D)).astype(np.float32)  # RAW tiles
+    x[1, 200] = x[1, 70]
+    x[2, 130] = x[2, 10]
+    cfg0 = O.Config(T=T, B=B, D=D, eb_mode=O.EB_REL, eb=(0.01,), coder=coder)
+    y0 = O.decompress(cfg0, O.compress(cfg0, 0, x, debug=False).stream)
+    u_prev = None
+    for W in (1, 3, 16, 64, 128, 255):
+        cfg = O.Config(T=T, B=B, D=D, eb_mode=O.EB_REL, eb=(0.01,), coder=coder, window=W)
+        c, st = check_stream(cfg, x)
+        np.testing.assert_array_equal(O.decompress(cfg, c.stream).view(np.uint32),
+                                      y0.view(np.uint32))
+        u = sum(seg.U for seg in st.segments)
+        assert u_prev is None or u <= u_prev  # a wider window never adds literals
+        u_prev = u
+    st0 = SF.parse(O.compress(cfg0, 0, x, debug=False).stream)
+    assert u_prev == sum(seg.U for seg in st0.segments)  # 255 >= rows - 1
+
+
+def test_window_chains_through_raw_tiles():
+    """A match may itself be a repeated row, also one stored in a RAW tile
+    (whose raw values give its key): every row of a hot key chains back."""
+    rng = np.random.default_rng(9)
+    B, D, W = 400, 8, 40
+    x = rng.normal(0, 0.3, (1, B, D)).astype(np.float32)
+    hot = x[0, 3].copy()
+    x[0, 3::30] = hot                                              # a chain, step 30
+    x[0, 128:192] = rng.normal(0, 1e5, (64, D)).astype(np.float32)  # a RAW tile...
+    x[0, 153] = hot                                                # ...on the chain
+    x[0, 128 + 5] = hot
+    cfg = O.Config(T=1, B=B, D=D, eb=(1e-3,), window=W)
+    c, st = check_stream(cfg, x)
+    assert any(tl.mode == 0 for tl in st.segments[0].tiles)
+    want = brute_window(row_keys(x[0], 1e-3), W)
+    np.testing.assert_array_equal(c.first[0], want)
+    y = O.decompress(cfg, c.stream)
+    for r in range(3, B, 30):
+        if not 128 <= r < 192:
+            np.testing.assert_array_equal(y[0, r].view(np.uint32), y[0, 3].view(np.uint32))
+
+
+def test_corrupt_window_distances_are_rejected():
+    rng = np.random.default_rng(4)
+    B, D, W = 200, 8, 10
+    x = np.stack([zipf_rows(rng, B, D, 12)])
+    cfg = O.Config(T=1, B=B, D=D, eb=(0.02,), window=W)
+    good = O.compress(cfg, 0, x, debug=False).stream
+    st = SF.parse(good)
+    seg = st.segments[0]
+    tl = next(t for t in seg.tiles if t.mode == 1 and t.U < t.n)
+    orf = tl.offset + 16 + (len(tl.widths) + 3) // 4 * 4
+    for v in (0, W + 1, 255):
+        bad = good.copy()
+        bad[orf] = v
+        assert O.decompress(cfg, bad, status=True)[0] == O.ERR_CORRUPT
+    # the first tile: a distance reaching before the segment
+    t0 = seg.tiles[0]
+    rows = [i for i in range(t0.n) if not (t0.bitmap >> i) & 1]
+    if t0.mode == 1 and rows and rows[0] < W:
+        bad = good.copy()
+        bad[t0.offset + 16 + (len(t0.widths) + 3) // 4 * 4] = rows[0] + 1
+        assert O.decompress(cfg, bad, status=True)[0] == O.ERR_CORRUPT
+    # window bits without the windowed flag, and the flag without a window
+    for flags in (1 | (W << 8), 5):
+        bad = good.copy()
+        bad[seg.offset + 12:seg.offset + 16] = np.frombuffer(np.uint32(flags).tobytes(), np.uint8)
+        assert O.decompress(cfg, bad, status=True)[0] == O.ERR_CORRUPT
+    with pytest.raises(ValueError):
+        O.compress(O.Config(T=1, B=B, D=D, eb=(0.02,), window=256), 0, x)
