@@ -17,6 +17,7 @@ constexpr uint32_t kCoderAuto = 3;      // per segment, the smaller form
 constexpr uint32_t kHuffTable = 4096;   // Huffman alphabet (4095) + 1, per segment
 constexpr uint32_t kBookStride = 2052;  // largest codebook (4 + 4095/2 rounded up)
 constexpr uint32_t kBookPad = 2064;     // its size padded to 16
+constexpr uint32_t kWinMaxRows = 32768; // rows of a segment with windowed references (decode LDS)
 
 // Error codes the device stores into the host-visible status word.
 constexpr uint32_t kDevErrCorrupt = 3;
@@ -72,12 +73,13 @@ struct Work {
   uint64_t* stage_pl;            // [ntiles][64][D/64][12] bit-plane words
   uint8_t* stage_w;              // [ntiles][64][D/64] width | 0x80 if outliers
   uint64_t* stage_om;            // [ntiles][64][D/64] outlier masks (flagged only)
-  uint32_t* stage_slot;          // [ntiles][64] hash slot of each row
+  uint32_t* stage_slot;          // [ntiles][64] hash slot of each row (windowed: its hash)
   // per-tile results of the size pass (D = 64, 128, 256 only; written before
   // they are read)
   uint32_t* tile_info;           // [ntiles][4] U, n_out, plane words, mode | valid << 8
   uint64_t* tile_bitmap;         // [ntiles] first-occurrence rows
-  uint32_t* tile_first;          // [ntiles][64] first occurrence of each row
+  uint32_t* tile_first;          // [ntiles][64] first occurrence of each row (windowed: its
+                                 // match); decoding windowed segments: the root of each row
   uint32_t* seg_eb;              // [nseg] stored error bound bits (0: raw segment), from quantize
   // Huffman segments (D = 64, 128, 256 with the Huffman or automatic coder;
   // NULL otherwise)
@@ -112,6 +114,7 @@ struct EncArgs {
   int64_t iter;
   double sched;                  // iteration-wise factor, computed on the host
   uint32_t coder;                // the stream's coder: kCoderBitpack, kCoderHuffman or kCoderAuto
+  uint32_t window;               // W of windowed references (1..255), 0: first occurrences
   uint64_t hash_keep;            // mask applied to row hashes (tests weaken it)
   Report* report;                // device pointer of the pinned report block
   uint32_t* seg_meta;            // in the report block: [nseg][2] U, eb valid (or NULL)
@@ -130,7 +133,8 @@ struct DecArgs {
   const uint32_t* seg_tile_base;
   Report* report;
   uint32_t huff;  // the plan decodes Huffman segments (its workspace holds the tables)
-  Work w;         // the plan's workspace (Huffman decoding only)
+  uint32_t window;  // the plan decodes windowed segments (its workspace holds the roots)
+  Work w;         // the plan's workspace (Huffman and windowed segments)
 };
 
 // LDS bytes of the encode kernel for dimension D.
@@ -158,6 +162,11 @@ hipError_t launch_assemble(const EncArgs& a, hipStream_t s);
 hipError_t launch_assemble_size(const EncArgs& a, hipStream_t s);
 hipError_t launch_assemble_write(const EncArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecArgs& a, hipStream_t s);
+// Windowed references (D = 64, 128, 256): the nearest earlier row within the
+// window with the same key, after the quantize pass (encode), and every
+// row's root before the decode kernels (decode).
+hipError_t launch_window(const EncArgs& a, hipStream_t s);
+hipError_t launch_window_roots(const DecArgs& a, hipStream_t s);
 // Huffman segments of the stream (D = 64, 128, 256): after the size pass,
 // histograms, codebooks, record sizes, the choice per segment and the tile
 // items; after the write pass, the chunk words.

@@ -1319,7 +1319,7 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
       if (lane >= nb * kRB && lane < nb * kRB + kRB) {
         H = h & (uint32_t)a.hash_keep;
         const uint32_t i = rbeg + lane;
-        if (i < n)
+        if (i < n && !a.window)
           old0 = atomicCAS((unsigned long long*)&htab[H & cap_mask], 0ull,
                            (unsigned long long)(((uint64_t)H << 32) | (uint64_t)(k * kTileRows + i + 1)));
       }
@@ -1374,8 +1374,9 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
   }
 
   // ---- insert: each wave owns 16 rows (lanes 0..15); compares use the wave ----
+  // (windowed references: no table, the window pass reads the row hashes)
   const uint32_t i = rbeg + lane;
-  bool active = lane < kRowsPerWave && i < n;
+  bool active = lane < kRowsPerWave && i < n && !a.window;
   bool first = true;  // the first attempt's result is old0
   uint32_t slot = H & cap_mask;
   const uint64_t mine = ((uint64_t)H << 32) | (uint64_t)(k * kTileRows + i + 1);
@@ -1456,7 +1457,7 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
       }
     }
   }
-  if (lane < kRowsPerWave && i < n) a.w.stage_slot[(uint64_t)ticket * kTileRows + i] = slot;
+  if (lane < kRowsPerWave && i < n) a.w.stage_slot[(uint64_t)ticket * kTileRows + i] = a.window ? H : slot;
 }
 
 // ---------------------------------------------------------------------------
@@ -1494,10 +1495,17 @@ struct RecLayout {
   uint32_t mode, off_refs, off_opos, off_oval, off_pl;
   uint64_t rec;  // record bytes
 };
+// Bytes of one reference: a u8 distance with windowed references, else the
+// referenced row as u16 (segments up to 65536 rows) or u32.
+__device__ __forceinline__ uint32_t ref_bytes(uint32_t rows, uint32_t window) {
+  return window ? 1u : (rows <= 65536 ? 2u : 4u);
+}
+
 __device__ __forceinline__ RecLayout rec_layout(uint32_t n, uint32_t U, uint32_t nblk, uint32_t sumw,
-                                                uint32_t nout, uint32_t rows, uint32_t D, bool valid) {
+                                                uint32_t nout, uint32_t rows, uint32_t D, bool valid,
+                                                uint32_t window) {
   RecLayout L;
-  const uint32_t rb = rows <= 65536 ? 2 : 4;
+  const uint32_t rb = ref_bytes(rows, window);
   L.off_refs = (uint32_t)align_up(16 + nblk, 4);
   L.off_opos = (uint32_t)align_up(L.off_refs + rb * (n - U), 4);
   L.off_oval = L.off_opos + 4 * nout;
@@ -1548,8 +1556,12 @@ __global__ void __launch_bounds__(kSizeThreads) ec_size_fast(EncArgs a) {
   for (uint32_t q = 0; q < Q; q++) {
     first[q] = c[q].k * kTileRows + lane;
     if (valid[q] && lane < c[q].n) {
-      const uint32_t cap_mask = (1u << a.w.hash_log2[c[q].s]) - 1u;
-      first[q] = (uint32_t)ld64(&a.w.hash[a.w.hash_off[c[q].s] + (slot[q] & cap_mask)]) - 1u;
+      if (a.window) {  // the match found by the window pass
+        first[q] = a.w.tile_first[(uint64_t)min(t0 + q, a.sh.ntiles - 1) * kTileRows + lane];
+      } else {
+        const uint32_t cap_mask = (1u << a.w.hash_log2[c[q].s]) - 1u;
+        first[q] = (uint32_t)ld64(&a.w.hash[a.w.hash_off[c[q].s] + (slot[q] & cap_mask)]) - 1u;
+      }
     }
   }
   uint64_t items = 0;
@@ -1572,7 +1584,7 @@ __global__ void __launch_bounds__(kSizeThreads) ec_size_fast(EncArgs a) {
     }
     const uint32_t sumw = wave_sum_u32(rw), nout = wave_sum_u32(ro);
     const uint32_t U = (uint32_t)__popcll(bm);
-    const RecLayout L = rec_layout(cq.n, U, U * C, sumw, nout, cq.rows, D, valid[q]);
+    const RecLayout L = rec_layout(cq.n, U, U * C, sumw, nout, cq.rows, D, valid[q], a.window);
     if (inrow) a.w.tile_first[rowi] = first[q];
     if (a.dbg_first && inrow)
       a.dbg_first[(uint64_t)cq.t * a.sh.B + chunk_row0(a.sh, cq.pch) + cq.k * kTileRows + lane] = first[q];
@@ -1654,7 +1666,7 @@ __device__ void write_stream_tables(const EncArgs& a, const TileCoord& c, uint32
       h[0] = c.rows;
       h[1] = c.ntiles;
       h[2] = ebw;
-      h[3] = ebw ? (huff ? 3u : 1u) : 0u;
+      h[3] = ebw ? ((huff ? 3u : 1u) | (a.window ? 4u | (a.window << 8) : 0u)) : 0u;
       h[4] = un[0];
       h[5] = un[1];
       reinterpret_cast<uint64_t*>(sg)[3] = se - ss;
@@ -1734,7 +1746,7 @@ ec_write_fast(EncArgs a) {
     // the hash slot of a first occurrence goes back to zero (read by the size
     // pass, which is done): every slot in use belongs to exactly one first
     // occurrence, so the tables are clear for the next call
-    if (uniq) {
+    if (uniq && !a.window) {
       const uint32_t cap_mask = (1u << a.w.hash_log2[c.s]) - 1u;
       a.w.hash[a.w.hash_off[c.s] + (a.w.stage_slot[rowi] & cap_mask)] = 0ull;
     }
@@ -1810,7 +1822,7 @@ ec_write_fast(EncArgs a) {
   const uint32_t U = info.x, nout = info.y, sumw = info.z, mode = info.w & 0xFFu;
   const bool valid = (info.w >> 8) & 1u;
   const uint64_t bitmap = s_bitmap;
-  const RecLayout L = rec_layout(n, U, U * C, sumw, mode ? nout : 0u, c.rows, D, valid);
+  const RecLayout L = rec_layout(n, U, U * C, sumw, mode ? nout : 0u, c.rows, D, valid, a.window);
   const uint64_t rec_bytes = mode == 2 ? a.w.tile_hsize[ticket] : L.rec;
   if (s_rec_abs + rec_bytes > a.out_cap) {  // cannot happen when out_cap >= the maximum stream size
     if (tid == 0) report_error(a.report, kDevErrTimeout);
@@ -1827,7 +1839,7 @@ ec_write_fast(EncArgs a) {
     return;
   }
   const uint32_t nblk = U * C;
-  const uint32_t rb = c.rows <= 65536 ? 2 : 4;
+  const uint32_t rb = ref_bytes(c.rows, a.window);
   // a Huffman record has no widths: its references start right after the header
   const uint32_t off_refs = mode == 2 ? 16u : L.off_refs;
   const uint32_t off_opos = mode == 2 ? (uint32_t)align_up(16 + rb * (n - U), 4) : L.off_opos;
@@ -1838,7 +1850,8 @@ ec_write_fast(EncArgs a) {
   }
   if (tid < n && !((bitmap >> tid) & 1ull)) {
     const uint32_t j = tid - (uint32_t)__popcll(bitmap & ((1ull << tid) - 1ull));
-    if (rb == 2) reinterpret_cast<uint16_t*>(rec + off_refs)[j] = (uint16_t)s_first[tid];
+    if (rb == 1) rec[off_refs + j] = (uint8_t)(c.k * kTileRows + tid - s_first[tid]);  // distance
+    else if (rb == 2) reinterpret_cast<uint16_t*>(rec + off_refs)[j] = (uint16_t)s_first[tid];
     else reinterpret_cast<uint32_t*>(rec + off_refs)[j] = s_first[tid];
   }
   {
@@ -1986,7 +1999,7 @@ __global__ void __launch_bounds__(kThreads) ec_hsize_tiles(EncArgs a) {
   if (tid == 0) {
     uint32_t w = 0;
     for (uint32_t q = 0; q < kThreads / 64; q++) w += s_words[q];
-    const uint32_t rb = c.rows <= 65536 ? 2 : 4, nout = a.w.tile_nout[ticket];
+    const uint32_t rb = ref_bytes(c.rows, a.window), nout = a.w.tile_nout[ticket];
     const uint32_t off_ct = (uint32_t)align_up(16 + rb * (c.n - U), 4) + 8 * nout;
     a.w.tile_hsize[ticket] = (uint32_t)align_up(off_ct + 4ull * (nch + 1) + 4ull * w, 16);
   }
@@ -2011,7 +2024,8 @@ __global__ void __launch_bounds__(kThreads) ec_seg_choose(EncArgs a) {
   for (uint32_t k = lane; k < nt; k += 64) {
     const uint32_t ticket = b + k, n = min(kTileRows, rows - k * kTileRows);
     const uint4 info = reinterpret_cast<const uint4*>(a.w.tile_info)[ticket];
-    const RecLayout L = rec_layout(n, info.x, info.x * (D / 64), info.z, a.w.tile_nout[ticket], rows, D, true);
+    const RecLayout L =
+        rec_layout(n, info.x, info.x * (D / 64), info.z, a.w.tile_nout[ticket], rows, D, true, a.window);
     const uint64_t raw = 16 + align_up(4ull * n * D, 16), h = a.w.tile_hsize[ticket];
     bp += L.rec;
     hf += h < raw ? h : raw;
@@ -2075,7 +2089,7 @@ __global__ void __launch_bounds__(kThreads) ec_write_huff(EncArgs a) {
   const uint64_t bm = a.w.tile_bitmap[ticket];
   if (wv == 0) unique_rows(bm, s_urow);
   __syncthreads();
-  const uint32_t rb = c.rows <= 65536 ? 2 : 4;
+  const uint32_t rb = ref_bytes(c.rows, a.window);
   const uint32_t off_ct = (uint32_t)align_up(16 + rb * (n - U), 4) + 8 * nout;
   const uint32_t nE = U * D, nch = (nE + 255) / 256, off_w = off_ct + 4 * (nch + 1);
   const uint16_t* sy = a.w.stage_sym + (uint64_t)ticket * kTileRows * D;
@@ -2231,6 +2245,7 @@ struct DecTile {
 struct DecShared {
   uint32_t ok, seg, tile, n, rows, ntiles, valid, bad;
   uint32_t seg_ok, hseg;  // the segment's headers passed; it is a Huffman segment
+  uint32_t win;           // W of a windowed segment, else 0
   float eb;
   uint64_t seg_off, seg_bytes, total, rec_lo;
   DecTile tl;
@@ -2269,9 +2284,15 @@ __device__ __forceinline__ bool header_coder_ok(uint32_t w, uint32_t huff, uint3
          (huff || coder == kCoderBitpack);
 }
 // A segment's flags: bit 0 eb valid, bit 1 Huffman segment (only with bit 0,
-// never in a coder-1 stream, always for a valid segment of a coder-2 stream).
-__device__ __forceinline__ bool seg_flags_ok(uint32_t flags, uint32_t coder) {
-  if (flags > 3 || flags == 2) return false;
+// never in a coder-1 stream, always for a valid segment of a coder-2 stream),
+// bit 2 windowed references with the window W in bits 8-15 (only with bit 0,
+// and only for a plan that decodes them); win gets W.
+__device__ __forceinline__ bool seg_flags_ok(uint32_t flags, uint32_t coder, bool allow_win,
+                                             uint32_t& win) {
+  win = (flags >> 8) & 0xFFu;
+  const uint32_t f = flags & 0xFFu;
+  if ((flags >> 16) != 0) return false;
+  if (win == 0 ? (f > 3 || f == 2) : (!allow_win || (f != 5 && f != 7))) return false;
   const bool hs = (flags & 2u) != 0;
   return !(hs && coder == kCoderBitpack) && !(coder == kCoderHuffman && (flags & 1u) && !hs);
 }
@@ -2281,7 +2302,7 @@ __device__ __forceinline__ bool seg_flags_ok(uint32_t flags, uint32_t coder) {
 // every read is bounds-checked against the segment.
 __device__ DecTile locate_tile(const uint8_t* seg, uint64_t seg_bytes, uint32_t ntiles,
                                uint32_t rows, uint32_t k, uint32_t D, bool valid, uint64_t rec_lo,
-                               bool hseg) {
+                               bool hseg, uint32_t win) {
   DecTile r{};
   r.ok = 0;
   if (k >= ntiles) return r;
@@ -2305,7 +2326,7 @@ __device__ DecTile locate_tile(const uint8_t* seg, uint64_t seg_bytes, uint32_t 
     if (!hseg) return r;
     uint64_t nE = (uint64_t)r.U * D;
     if (r.nout > nE) return r;
-    uint32_t rb = rows <= 65536 ? 2 : 4;
+    uint32_t rb = ref_bytes(rows, win);
     uint64_t off_opos = align_up(16 + (uint64_t)rb * (r.n - r.U), 4);
     uint64_t off_ct = off_opos + 8ull * r.nout;
     uint64_t nch = (nE + 255) / 256;
@@ -2321,7 +2342,7 @@ __device__ DecTile locate_tile(const uint8_t* seg, uint64_t seg_bytes, uint32_t 
     uint64_t nE = (uint64_t)r.U * D;
     if (r.nout > nE) return r;
     uint64_t nblk = (nE + 63) / 64;
-    uint32_t rb = rows <= 65536 ? 2 : 4;
+    uint32_t rb = ref_bytes(rows, win);
     uint64_t off_refs = align_up(16 + nblk, 4);
     uint64_t off_opos = align_up(off_refs + (uint64_t)rb * (r.n - r.U), 4);
     uint64_t off_oval = off_opos + 4ull * r.nout;
@@ -2484,7 +2505,8 @@ __global__ void __launch_bounds__(kThreads) ec_decode_kernel(DecArgs a) {
       sb = rd64(sg + 24);
       int valid = isfinite(eb) && eb > 0.0f && isfinite(eb + eb);
       // (a coder-1 stream: no Huffman segment)
-      if (rd32(sg) != rows || rd32(sg + 4) != nt || !seg_flags_ok(flags, coder) ||
+      uint32_t win = 0;
+      if (rd32(sg) != rows || rd32(sg + 4) != nt || !seg_flags_ok(flags, coder, false, win) ||
           (int)(flags & 1u) != valid || sb > cb - so || sb < 32 + align_up(4ull * nt, 16))
         ok = 0;
       sh.eb = eb;
@@ -2495,7 +2517,7 @@ __global__ void __launch_bounds__(kThreads) ec_decode_kernel(DecArgs a) {
     sh.total = total;
     sh.rec_lo = 32 + align_up(4ull * nt, 16);
     if (ok && nt) {
-      DecTile tl = locate_tile(in + chunk + so, sb, nt, rows, k, D, sh.valid != 0, sh.rec_lo, false);
+      DecTile tl = locate_tile(in + chunk + so, sb, nt, rows, k, D, sh.valid != 0, sh.rec_lo, false, 0);
       ok = tl.ok;
       sh.tl = tl;
     }
@@ -2596,7 +2618,7 @@ __global__ void __launch_bounds__(kThreads) ec_decode_kernel(DecArgs a) {
                                           : kBad;
       } else {
         const uint32_t k2 = ref / kTileRows, i2 = ref % kTileRows;
-        DecTile t2 = locate_tile(sg, sbytes, sh.ntiles, rows, k2, D, true, sh.rec_lo, false);
+        DecTile t2 = locate_tile(sg, sbytes, sh.ntiles, rows, k2, D, true, sh.rec_lo, false, 0);
         src = kExt | i;
         if (!t2.ok || !((t2.bitmap >> i2) & 1ull)) {
           src = kBad;
@@ -2730,6 +2752,7 @@ __device__ void dec_locate(const DecArgs& a, const uint8_t* in, uint32_t ticket,
     if (so < align_up(8ull * T, 16) || (so & 15u) || so + 32 > cb) ok = 0;
   }
   sh.hseg = 0;
+  sh.win = 0;
   sh.rec_lo = 32 + align_up(4ull * nt, 16);
   if (ok) {
     const uint8_t* sg = in + chunk + so;
@@ -2737,9 +2760,11 @@ __device__ void dec_locate(const DecArgs& a, const uint8_t* in, uint32_t ticket,
     float eb = __uint_as_float(rd32(sg + 8));
     sb = rd64(sg + 24);
     int valid = isfinite(eb) && eb > 0.0f && isfinite(eb + eb);
-    if (rd32(sg) != rows || rd32(sg + 4) != nt || !seg_flags_ok(flags, coder) ||
+    uint32_t win = 0;
+    if (rd32(sg) != rows || rd32(sg + 4) != nt || !seg_flags_ok(flags, coder, a.window != 0, win) ||
         (int)(flags & 1u) != valid || sb > cb - so || sb < sh.rec_lo)
       ok = 0;
+    sh.win = win;
     sh.eb = eb;
     sh.valid = flags & 1u;
     sh.hseg = (flags >> 1) & 1u;
@@ -2759,7 +2784,8 @@ __device__ void dec_locate(const DecArgs& a, const uint8_t* in, uint32_t ticket,
   sh.total = total;
   rec_off = 0;
   if (ok && nt) {
-    DecTile tl = locate_tile(in + chunk + so, sb, nt, rows, k, D, sh.valid != 0, sh.rec_lo, sh.hseg != 0);
+    DecTile tl =
+        locate_tile(in + chunk + so, sb, nt, rows, k, D, sh.valid != 0, sh.rec_lo, sh.hseg != 0, sh.win);
     ok = tl.ok;
     sh.tl = tl;
     rec_off = (uint64_t)(tl.rec - in);
@@ -3023,8 +3049,11 @@ __device__ __forceinline__ void index_tile(const uint8_t* __restrict__ in, const
       u = (uint32_t)__popcll(below);
     } else {
       const uint32_t jr = i - (uint32_t)__popcll(below);
-      const uint32_t ref = rb == 2 ? reinterpret_cast<const uint16_t*>(rec + off_refs)[jr]
-                                   : reinterpret_cast<const uint32_t*>(rec + off_refs)[jr];
+      // windowed references: the root found by the roots pass (a literal, or
+      // any row of a RAW tile), else the first occurrence the record names
+      const uint32_t ref = sh.win ? a.w.tile_first[(uint64_t)ticket * kTileRows + i]
+                           : rb == 2 ? reinterpret_cast<const uint16_t*>(rec + off_refs)[jr]
+                                     : reinterpret_cast<const uint32_t*>(rec + off_refs)[jr];
       if (ref >= r) {
         kind = kRowBad;
       } else if (ref >= k * kTileRows) {
@@ -3034,8 +3063,8 @@ __device__ __forceinline__ void index_tile(const uint8_t* __restrict__ in, const
       } else {
         local = false;
         const uint32_t k2 = ref / kTileRows, i2 = ref % kTileRows;
-        DecTile t2 = locate_tile(sg, sbytes, sh.ntiles, rows, k2, D, true, sh.rec_lo, false);
-        if (!t2.ok || !((t2.bitmap >> i2) & 1ull)) {
+        DecTile t2 = locate_tile(sg, sbytes, sh.ntiles, rows, k2, D, true, sh.rec_lo, false, sh.win);
+        if (!t2.ok || !(((t2.bitmap >> i2) & 1ull) || (sh.win && t2.mode == 0))) {
           kind = kRowBad;
         } else {
           orec = (uint32_t)(t2.rec - sg);
@@ -3444,8 +3473,10 @@ __global__ void __launch_bounds__(kThreads) ec_fill_refs(const uint8_t* __restri
     if (lane < n && !((tl.bitmap >> lane) & 1ull)) {
       const uint32_t rb = rows <= 65536 ? 2 : 4;
       const uint32_t j = lane - (uint32_t)__popcll(tl.bitmap & lanes_below());
-      const uint32_t ref = rb == 2 ? reinterpret_cast<const uint16_t*>(tl.rec + 16)[j]
-                                   : reinterpret_cast<const uint32_t*>(tl.rec + 16)[j];
+      // windowed references: the root from the roots pass
+      const uint32_t ref = sh.win ? a.w.tile_first[(uint64_t)ticket * kTileRows + lane]
+                           : rb == 2 ? reinterpret_cast<const uint16_t*>(tl.rec + 16)[j]
+                                     : reinterpret_cast<const uint32_t*>(tl.rec + 16)[j];
       const uint32_t k2 = ref / kTileRows, i2 = ref % kTileRows;
       kind = kRefBad;
       src = ref;
@@ -3454,8 +3485,9 @@ __global__ void __launch_bounds__(kThreads) ec_fill_refs(const uint8_t* __restri
       } else if (k2 == k) {
         if ((tl.bitmap >> i2) & 1ull) kind = kRefCopy;
       } else {
-        const DecTile t2 = locate_tile(sg, sh.seg_bytes, sh.ntiles, rows, k2, D, true, sh.rec_lo, true);
-        if (t2.ok && ((t2.bitmap >> i2) & 1ull)) {
+        const DecTile t2 =
+            locate_tile(sg, sh.seg_bytes, sh.ntiles, rows, k2, D, true, sh.rec_lo, true, sh.win);
+        if (t2.ok && (((t2.bitmap >> i2) & 1ull) || (sh.win && t2.mode == 0))) {
           kind = t2.mode == 0 ? kRefRaw : kRefCopy;
           roff = (uint32_t)(t2.rec - sg);
         }
@@ -3491,6 +3523,187 @@ __global__ void __launch_bounds__(kThreads) ec_fill_refs(const uint8_t* __restri
     for (uint32_t j = 0; j < C; j++) y[64 * j + lane] = v[j];
   }
   if (bad && lane == 0) report_error(a.report, kDevErrCorrupt);
+}
+
+// ---------------------------------------------------------------------------
+// windowed references for D = 64*C (the vector-based LZ of section III-D with
+// the extended window of section III-E), after the quantize pass: one wave
+// per tile, lane i for segment row r = 64k + i.  The row hashes of the tile
+// and of the 256 rows before it (as far as a window of at most 255 reaches)
+// go to LDS; each row scans back from distance 1 for an equal hash, and a hash
+// hit is its match when the two rows' keys are equal (compared by the whole
+// wave, as the hash-table insertion compares).  tile_first gets the match,
+// or the row itself when none is within the window.
+// ---------------------------------------------------------------------------
+template <int C>
+__global__ void __launch_bounds__(kThreads) ec_window_fast(EncArgs a) {
+  constexpr uint32_t D = 64u * C;
+  constexpr uint32_t kBack = 256;
+  __shared__ uint32_t s_h[kThreads / 64][kBack + kTileRows];
+  const uint32_t lane = threadIdx.x & 63, wv = wave_id();
+  const uint32_t ticket = blockIdx.x * (kThreads / 64) + wv;
+  if (ticket >= a.sh.ntiles) return;  // whole waves; no workgroup barrier follows
+  const TileCoord c = tile_coord(a, ticket);
+  const uint32_t n = c.n, r = c.k * kTileRows + lane;
+  const uint64_t rowi = (uint64_t)ticket * kTileRows + lane;
+  if (n == 0 || a.w.seg_eb[c.s] == 0u) {
+    if (lane < n) a.w.tile_first[rowi] = r;
+    return;
+  }
+  // hs[j]: hash of segment row 64k - 256 + j (tile k - b has ticket - b);
+  // entries before the segment are never read
+  uint32_t* hs = s_h[wv];
+#pragma unroll
+  for (uint32_t q = 0; q <= kBack / kTileRows; q++) {
+    const uint32_t back = kBack / kTileRows - q;
+    if (c.k >= back) hs[q * kTileRows + lane] = a.w.stage_slot[(uint64_t)(ticket - back) * kTileRows + lane];
+  }
+  wave_lds_wait();
+  const float eb = __uint_as_float(a.w.seg_eb[c.s]), s2 = eb + eb, r2 = 1.0f / s2;
+  const float* xs = a.x + ((uint64_t)c.t * a.sh.B + chunk_row0(a.sh, c.pch)) * D;
+  const uint32_t h = hs[kBack + lane];
+  const uint32_t dmax = lane < n ? min(a.window, r) : 0u;  // distances 1 .. dmax stay in the segment
+  uint32_t d = 0;      // distances up to d are ruled out
+  uint32_t match = r;  // no match: a literal
+  bool active = lane < n;
+  while (__ballot(active) != 0) {
+    bool need = false;
+    uint32_t cand = 0;
+    if (active) {  // the nearest hash hit past d, eight distances at a time
+      uint32_t dd = d + 1;
+      bool hit = false;
+      while (dd <= dmax) {
+        uint32_t bits = 0;
+#pragma unroll
+        for (uint32_t u = 0; u < 8; u++) {
+          const uint32_t e = min(dd + u, dmax);  // in 1 .. dmax
+          bits |= (uint32_t)(hs[kBack + lane - e] == h && dd + u <= dmax) << u;
+        }
+        if (bits) {
+          dd += (uint32_t)__builtin_ctz(bits);
+          hit = true;
+          break;
+        }
+        dd += 8;
+      }
+      if (hit) {
+        need = true;
+        cand = r - dd;
+        d = dd;
+      } else {
+        active = false;
+      }
+    }
+    // the hits, kCmp at a time with all their row loads in flight together
+    constexpr int kCmp = C >= 4 ? 2 : 8 / C;
+    uint64_t m = __ballot(need);
+    while (m) {
+      int Lk[kCmp];
+      float va[kCmp][C], vb[kCmp][C];
+#pragma unroll
+      for (int kk = 0; kk < kCmp; kk++) {
+        Lk[kk] = m ? __ffsll((long long)m) - 1 : -1;
+        m &= m - 1;
+        const int Ls = Lk[kk] < 0 ? Lk[0] : Lk[kk];  // no candidate: a copy of the first
+        const uint32_t iL = __shfl(r, Ls), cL = __shfl(cand, Ls);
+#pragma unroll
+        for (int j = 0; j < C; j++) {
+          va[kk][j] = xs[(uint64_t)cL * D + 64 * j + lane];
+          vb[kk][j] = xs[(uint64_t)iL * D + 64 * j + lane];
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < kCmp; kk++) {
+        if (Lk[kk] < 0) continue;
+        bool raw = true;
+#pragma unroll
+        for (int j = 0; j < C; j++) raw = raw && f2u(va[kk][j]) == f2u(vb[kk][j]);
+        bool eq = __all(raw);
+        if (!eq) {  // different bits: the same codes and outliers make the keys equal
+          bool e = true;
+#pragma unroll
+          for (int j = 0; j < C; j++) {
+            int qa, qb;
+            const bool oa = quantize_fast(va[kk][j], eb, s2, r2, qa);
+            const bool ob = quantize_fast(vb[kk][j], eb, s2, r2, qb);
+            e = e && oa == ob && (oa ? f2u(va[kk][j]) == f2u(vb[kk][j]) : qa == qb);
+          }
+          eq = __all(e);
+        }
+        if ((int)lane == Lk[kk] && eq) {
+          match = cand;
+          active = false;
+        }
+      }
+    }
+  }
+  if (lane < n) a.w.tile_first[rowi] = match;
+}
+
+// ---------------------------------------------------------------------------
+// decoding windowed segments: one workgroup per segment finds every row's
+// root, the row whose key it has that the decoders can read directly (a
+// literal, or any row of a RAW tile): each repeated row of a coded tile links
+// to its match (distance checked: 1 .. W and inside the segment), other rows
+// to themselves; links always point back, so jumping link to link's link
+// converges in log2(rows) rounds.  Roots go to tile_first for the decode
+// kernels; distances out of range are reported corrupt.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kRootThreads = 1024;
+template <int C>
+__global__ void __launch_bounds__(kRootThreads) ec_win_roots(const uint8_t* __restrict__ in, DecArgs a) {
+  constexpr uint32_t D = 64u * C;
+  constexpr uint32_t kPer = kWinMaxRows / kRootThreads;
+  __shared__ uint16_t s_src[kWinMaxRows];
+  __shared__ DecShared sh;
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wv = wave_id();
+  const uint32_t ticket0 = a.seg_tile_base[blockIdx.x];
+  if (wv == 0) {
+    uint64_t ro;
+    dec_locate(a, in, ticket0, sh, ro);
+  }
+  __syncthreads();
+  if (!sh.seg_ok || sh.win == 0 || sh.ntiles == 0 || sh.rows > kWinMaxRows) return;  // whole workgroup
+  const uint32_t rows = sh.rows, nt = sh.ntiles, W = sh.win;
+  const uint8_t* sg = in + sh.seg_off;
+  bool bad = false;
+  for (uint32_t k = wv; k < nt; k += kRootThreads / 64) {
+    const DecTile t = locate_tile(sg, sh.seg_bytes, nt, rows, k, D, sh.valid != 0, sh.rec_lo, sh.hseg != 0, W);
+    const uint32_t n = min(kTileRows, rows - k * kTileRows), r = k * kTileRows + lane;
+    uint32_t link = r;
+    if (t.ok && t.mode != 0 && lane < n && !((t.bitmap >> lane) & 1ull)) {
+      const uint32_t j = lane - (uint32_t)__popcll(t.bitmap & lanes_below());
+      const uint32_t dist = t.rec[t.off_refs + j];
+      if (dist >= 1 && dist <= W && dist <= r) link = r - dist;
+      else bad = true;
+    }
+    if (lane < n) s_src[r] = (uint16_t)link;
+  }
+  __syncthreads();
+  for (;;) {
+    uint16_t nv[kPer];
+    bool changed = false;
+#pragma unroll
+    for (uint32_t q = 0; q < kPer; q++) {
+      const uint32_t r = q * kRootThreads + tid;
+      nv[q] = 0;
+      if (r < rows) {
+        const uint32_t l1 = s_src[r], l2 = s_src[l1];
+        nv[q] = (uint16_t)l2;
+        changed = changed || l2 != l1;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (uint32_t q = 0; q < kPer; q++) {
+      const uint32_t r = q * kRootThreads + tid;
+      if (r < rows) s_src[r] = nv[q];
+    }
+    if (!__syncthreads_or(changed)) break;
+  }
+  for (uint32_t r = tid; r < rows; r += kRootThreads)
+    a.w.tile_first[(uint64_t)(ticket0 + r / kTileRows) * kTileRows + r % kTileRows] = s_src[r];
+  if (bad) report_error(a.report, kDevErrCorrupt);
 }
 
 // ---------------------------------------------------------------------------
@@ -3609,6 +3822,28 @@ hipError_t launch_assemble(const EncArgs& a, hipStream_t s) {
       break;
     default:
       return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_window(const EncArgs& a, hipStream_t s) {
+  const dim3 grid((a.sh.ntiles + kThreads / 64 - 1) / (kThreads / 64)), block(kThreads);
+  switch (a.sh.D) {
+    case 64: hipLaunchKernelGGL(ec_window_fast<1>, grid, block, 0, s, a); break;
+    case 128: hipLaunchKernelGGL(ec_window_fast<2>, grid, block, 0, s, a); break;
+    case 256: hipLaunchKernelGGL(ec_window_fast<4>, grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_window_roots(const DecArgs& a, hipStream_t s) {
+  const dim3 grid(a.sh.nseg), block(kRootThreads);
+  switch (a.sh.D) {
+    case 64: hipLaunchKernelGGL(ec_win_roots<1>, grid, block, 0, s, a.in, a); break;
+    case 128: hipLaunchKernelGGL(ec_win_roots<2>, grid, block, 0, s, a.in, a); break;
+    case 256: hipLaunchKernelGGL(ec_win_roots<4>, grid, block, 0, s, a.in, a); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

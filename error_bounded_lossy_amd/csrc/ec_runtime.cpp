@@ -87,6 +87,11 @@ ec_status make_layout(const ec_plan_desc* d, Layout* L) {
   L->huff = L->stream_coder != EC_CODER_BITPACK;
   // Huffman segments: for the wave64 paths (D = 64, 128, 256) only
   if (L->huff && !ec::encode_has_assembly(D)) return EC_ERR_UNSUPPORTED;
+  // windowed references: W <= 255 (u8 distances), on the wave64 paths, with
+  // at most kWinMaxRows rows per segment (the decoder's roots pass)
+  if (d->window > 255) return EC_ERR_INVALID;
+  if (d->window && (!ec::encode_has_assembly(D) || (B + P - 1) / P > ec::kWinMaxRows))
+    return EC_ERR_UNSUPPORTED;
   if (d->debug_hash_bits > 64) return EC_ERR_INVALID;
   const ec_schedule& s = d->sched;
   if (s.kind == EC_SCHED_INV_SQRT) {
@@ -376,7 +381,7 @@ ec_status ec_plan(const ec_plan_desc* desc, ec_plan_t* out) {
   const Layout& L = pl->L;
   // no workspace at all: a plan for ec_compress_static (and ec_decompress) only
   const bool no_ws = !desc->d_workspace && desc->workspace_bytes == 0;
-  if (no_ws && L.huff) {  // Huffman segments keep their tables in the workspace
+  if (no_ws && (L.huff || desc->window)) {  // their tables and roots live in the workspace
     delete pl;
     return EC_ERR_UNSUPPORTED;
   }
@@ -540,11 +545,14 @@ ec_status ec_decompress(ec_plan_t pl, const void* d_stream, size_t stream_cap, f
                             : reinterpret_cast<const uint32_t*>(pl->consts_dev + pl->L.seg_tile_base);
   da.report = pl->report_dev;
   da.huff = pl->L.huff ? 1u : 0u;
+  da.window = pl->desc.window ? 1u : 0u;
   da.w = pl->work;
   const ec_status st = profiled(pl, EC_KERNEL_DECODE, s, [&] {
-    if (!pl->L.huff) return ec::launch_decode(da, s);
+    // windowed segments: every row's root before the decode kernels
+    hipError_t e = da.window ? ec::launch_window_roots(da, s) : hipSuccess;
+    if (e != hipSuccess || !pl->L.huff) return e == hipSuccess ? ec::launch_decode(da, s) : e;
     // the codebooks' tables first; Huffman tiles and their repeated rows after
-    hipError_t e = ec::launch_huff_tables(da, s);
+    e = ec::launch_huff_tables(da, s);
     if (e == hipSuccess) e = ec::launch_decode(da, s);
     if (e == hipSuccess) e = ec::launch_huff_decode(da, s);
     return e;
@@ -580,6 +588,7 @@ ec_status ec_ratio(ec_plan_t pl, double* total_cr, uint64_t* compressed_bytes,
 ec_status ec_homo_counts(ec_plan_t pl, int64_t iter, const float* d_in, void* d_out,
                          size_t out_cap, uint32_t* n_orig, uint32_t* n_quant, void* stream) {
   if (!pl || !n_orig || !n_quant) return EC_ERR_INVALID;
+  if (pl->desc.window) return EC_ERR_UNSUPPORTED;  // its U counts literals, not distinct rows
   ec_status st = ec_compress(pl, iter, d_in, d_out, out_cap, stream);
   if (st != EC_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -752,6 +761,7 @@ ec_status enqueue_compress(ec_plan_s* pl, const ec::Work& work, bool clear, int6
   ea.iter = iter;
   ea.sched = schedule_factor(pl->desc.sched, iter);
   ea.coder = pl->L.stream_coder;
+  ea.window = pl->desc.window;
   uint32_t hb = pl->desc.debug_hash_bits;
   ea.hash_keep = (hb == 0 || hb >= 64) ? ~0ull : ((1ull << hb) - 1ull);
   ea.report = pl->report_dev;
@@ -761,7 +771,11 @@ ec_status enqueue_compress(ec_plan_s* pl, const ec::Work& work, bool clear, int6
   ea.dbg_outlier = pl->dbg_outlier;
   ea.dbg_first = pl->dbg_first;
   ea.dbg_eb = pl->dbg_eb;
-  st = profiled(pl, EC_KERNEL_ENCODE, s, [&] { return ec::launch_encode(ea, s); });
+  st = profiled(pl, EC_KERNEL_ENCODE, s, [&] {
+    hipError_t e = ec::launch_encode(ea, s);
+    if (e == hipSuccess && ea.window) e = ec::launch_window(ea, s);  // the matches
+    return e;
+  });
   if (st != EC_OK) return st;
   if (ec::encode_has_assembly(sh.D)) {
     st = profiled(pl, EC_KERNEL_ASSEMBLE, s, [&] {

@@ -132,6 +132,15 @@ typedef struct {
                                aligned; owned by the caller, used by the plan
                                until ec_plan_destroy                           */
   size_t workspace_bytes;
+  uint32_t window;          /* 0: a repeated row references the first row of
+                               its segment with its key; 1..255: the nearest
+                               earlier row within `window` rows (the vector-
+                               based LZ of section III-D with the extended
+                               window of section III-E, Table VI), stored as a
+                               u8 distance.  Needs D = 64, 128 or 256, a
+                               workspace and at most 32768 rows per segment
+                               (else EC_ERR_UNSUPPORTED); decoding windowed
+                               segments needs a windowed plan.                */
   const int32_t* table_coder; /* host [T] ec_coder of each table (Algorithm 2's
                                table-wise configuration, e.g. from
                                ec_select_coders) or NULL for `coder`; copied

@@ -182,3 +182,15 @@ def test_table_coder_validation():
     assert ec.workspace_bytes(3, 100, 24, table_coder=[1, 2, 1]) == 0
     assert ec.workspace_bytes(3, 100, 128, table_coder=[1, 4, 1]) == 0
     assert ec.workspace_bytes(2, 100, 128, table_coder=[0, 1]) == 0
+
+
+def test_window_validation():
+    """Windowed references: W <= 255, wave64 dims only, at most 32768 rows per
+    segment."""
+    assert ec.workspace_bytes(2, 100, 128, window=255) > 0
+    assert ec.workspace_bytes(2, 100, 64, window=1, coder=ec.CODER_AUTO) > 0
+    assert ec.workspace_bytes(2, 100, 128, window=256) == 0
+    assert ec.workspace_bytes(2, 100, 24, window=8) == 0
+    assert ec.workspace_bytes(1, 32768, 64, window=8) > 0
+    assert ec.workspace_bytes(1, 32769, 64, window=8) == 0
+    assert ec.workspace_bytes(1, 65536, 64, P=2, window=8) > 0
