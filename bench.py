@@ -424,6 +424,63 @@ def bench_huffman(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_window_sweep(args):
+    """Table VI's experiment on the workload: the compression ratio of the
+    stream with windowed references for W = 32, 64, 128, 255 (and the
+    whole-segment references, W = 0), total bytes over the batches, each
+    also relative to W = 32 as the table prints it; with each the warm
+    compress and decompress rates."""
+    import torch
+    import synth
+    import error_bounded_lossy_amd as ec
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    batches = [synth.workload(args.workload, iteration=i, device=dev) for i in range(args.batches)]
+    w0 = batches[0]
+    T, B, D = w0.shape
+    N = T * B * D
+    sched = {"kind": w0.sched_kind, "t0": w0.sched_t0} if w0.sched_kind else None
+    rows = []
+    for W in (32, 64, 128, 255, 0):
+        print(f"[bench] window {W}", file=sys.stderr, flush=True)
+        plan = ec.Plan(T, B, D, 1, w0.eb_mode, w0.eb, schedule=sched, device=dev, window=W)
+        out = plan.empty_stream()
+        y = torch.empty(T, B, D, dtype=torch.float32, device=dev)
+        total = 0
+        for w in batches:
+            plan.compress(w.x, out, w.iteration)
+            total += plan.ratio()[1]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        for i in range(args.warmup):
+            w = batches[i % len(batches)]
+            plan.compress(w.x, out, w.iteration)
+            plan.decompress(out, y)
+        tc = td = 0.0
+        for i in range(args.steps):
+            w = batches[i % len(batches)]
+            ev[0].record()
+            plan.compress(w.x, out, w.iteration)
+            ev[1].record()
+            plan.decompress(out, y)
+            ev[2].record()
+            ev[2].synchronize()
+            tc += ev[0].elapsed_time(ev[1])
+            td += ev[1].elapsed_time(ev[2])
+        if plan.ratio(raise_on_error=False)[-1] != ec.EC_OK:
+            sys.exit("[bench] device error")
+        rows.append({"window": W, "compression_ratio": round(4 * N * len(batches) / total, 4),
+                     "compress_GBps": round(4 * N * args.steps / tc / 1e6, 1),
+                     "decompress_GBps": round(4 * N * args.steps / td / 1e6, 1)})
+        plan.close()
+    base = rows[0]["compression_ratio"]
+    for r in rows:
+        r["ratio_vs_window_32"] = round(r["compression_ratio"] / base, 4)
+    print(json.dumps({"experiment": "window sweep (Table VI)", "workload": args.workload,
+                      "config": WORKLOADS[args.workload], "batches": len(batches),
+                      "protocol": "warm, events around each call", "rows": rows}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -448,7 +505,12 @@ def main():
     ap.add_argument("--stream-coder", default="bitpack", choices=["bitpack", "huffman", "auto"],
                     help="the segment coder of the compressed stream: bit planes, Huffman, "
                          "or per segment the smaller")
+    ap.add_argument("--window-sweep", action="store_true",
+                    help="Table VI: the ratio of windowed references for W = 32 .. 255")
     args = ap.parse_args()
+    if args.window_sweep:
+        bench_window_sweep(args)
+        return
     if args.summarize_counters:
         summarize_counters(args.summarize_counters, args.workload,
                            args.copy_calibration or (256 << 20), args.command, args.coder)

@@ -3641,22 +3641,50 @@ __global__ void __launch_bounds__(kThreads) ec_window_fast(EncArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// decoding windowed segments: one workgroup per segment finds every row's
-// root, the row whose key it has that the decoders can read directly (a
-// literal, or any row of a RAW tile): each repeated row of a coded tile links
-// to its match (distance checked: 1 .. W and inside the segment), other rows
-// to themselves; links always point back, so jumping link to link's link
-// converges in log2(rows) rounds.  Roots go to tile_first for the decode
-// kernels; distances out of range are reported corrupt.
+// decoding windowed segments: every row's root, the row whose key it has that
+// the decoders can read directly (a literal, or any row of a RAW tile).
+//   links  one wave per tile: each repeated row of a coded tile links to its
+//          match (the distance checked: 1 .. W and inside the segment, else
+//          reported corrupt), every other row to itself
+//   roots  one workgroup per segment: links always point back, so jumping
+//          from link to link's link (in LDS) converges in log2(rows) rounds
+// Links and then roots go to tile_first, where the decode kernels read them.
 // ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(64) ec_win_links(const uint8_t* __restrict__ in, DecArgs a) {
+  __shared__ DecShared sh;
+  const uint32_t lane = threadIdx.x, ticket = blockIdx.x;
+  uint64_t ro;
+  dec_locate(a, in, ticket, sh, ro);
+  lds_sync();
+  if (!sh.ok || sh.win == 0 || sh.n == 0) return;  // not windowed, or reported by the decoders
+  const DecTile& t = sh.tl;
+  const uint32_t r = sh.tile * kTileRows + lane, W = sh.win;
+  uint32_t link = r;
+  bool bad = false;
+  if (t.mode != 0 && lane < sh.n && !((t.bitmap >> lane) & 1ull)) {
+    const uint32_t j = lane - (uint32_t)__popcll(t.bitmap & lanes_below());
+    const uint32_t dist = t.rec[t.off_refs + j];  // inside the record (checked by locate_tile)
+    if (dist >= 1 && dist <= W && dist <= r) link = r - dist;
+    else bad = true;
+  }
+  // links inside the tile jumped here already (six rounds reach across 64
+  // rows): afterwards a row links to a root or to a row of an earlier tile
+  const uint32_t r0 = sh.tile * kTileRows;
+#pragma unroll
+  for (int k = 0; k < 6; k++) {
+    const uint32_t l2 = (uint32_t)__shfl((int)link, (int)(link >= r0 ? link - r0 : lane));
+    if (link >= r0) link = l2;
+  }
+  if (lane < sh.n) a.w.tile_first[(uint64_t)ticket * kTileRows + lane] = link;
+  if (bad) report_error(a.report, kDevErrCorrupt);
+}
+
 constexpr uint32_t kRootThreads = 1024;
-template <int C>
 __global__ void __launch_bounds__(kRootThreads) ec_win_roots(const uint8_t* __restrict__ in, DecArgs a) {
-  constexpr uint32_t D = 64u * C;
   constexpr uint32_t kPer = kWinMaxRows / kRootThreads;
   __shared__ uint16_t s_src[kWinMaxRows];
   __shared__ DecShared sh;
-  const uint32_t tid = threadIdx.x, lane = tid & 63, wv = wave_id();
+  const uint32_t tid = threadIdx.x, wv = wave_id();
   const uint32_t ticket0 = a.seg_tile_base[blockIdx.x];
   if (wv == 0) {
     uint64_t ro;
@@ -3664,20 +3692,13 @@ __global__ void __launch_bounds__(kRootThreads) ec_win_roots(const uint8_t* __re
   }
   __syncthreads();
   if (!sh.seg_ok || sh.win == 0 || sh.ntiles == 0 || sh.rows > kWinMaxRows) return;  // whole workgroup
-  const uint32_t rows = sh.rows, nt = sh.ntiles, W = sh.win;
-  const uint8_t* sg = in + sh.seg_off;
-  bool bad = false;
-  for (uint32_t k = wv; k < nt; k += kRootThreads / 64) {
-    const DecTile t = locate_tile(sg, sh.seg_bytes, nt, rows, k, D, sh.valid != 0, sh.rec_lo, sh.hseg != 0, W);
-    const uint32_t n = min(kTileRows, rows - k * kTileRows), r = k * kTileRows + lane;
-    uint32_t link = r;
-    if (t.ok && t.mode != 0 && lane < n && !((t.bitmap >> lane) & 1ull)) {
-      const uint32_t j = lane - (uint32_t)__popcll(t.bitmap & lanes_below());
-      const uint32_t dist = t.rec[t.off_refs + j];
-      if (dist >= 1 && dist <= W && dist <= r) link = r - dist;
-      else bad = true;
-    }
-    if (lane < n) s_src[r] = (uint16_t)link;
+  const uint32_t rows = sh.rows;
+  uint32_t* lk = a.w.tile_first + (uint64_t)ticket0 * kTileRows;  // the segment's rows, in order
+  // a tile whose record failed its checks wrote no links: its rows are roots
+  // (their decode workgroups report the stream corrupt)
+  for (uint32_t r = tid; r < rows; r += kRootThreads) {
+    const uint32_t l = lk[r];
+    s_src[r] = (uint16_t)(l < r ? l : r);
   }
   __syncthreads();
   for (;;) {
@@ -3701,9 +3722,7 @@ __global__ void __launch_bounds__(kRootThreads) ec_win_roots(const uint8_t* __re
     }
     if (!__syncthreads_or(changed)) break;
   }
-  for (uint32_t r = tid; r < rows; r += kRootThreads)
-    a.w.tile_first[(uint64_t)(ticket0 + r / kTileRows) * kTileRows + r % kTileRows] = s_src[r];
-  if (bad) report_error(a.report, kDevErrCorrupt);
+  for (uint32_t r = tid; r < rows; r += kRootThreads) lk[r] = s_src[r];
 }
 
 // ---------------------------------------------------------------------------
@@ -3838,13 +3857,8 @@ hipError_t launch_window(const EncArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_window_roots(const DecArgs& a, hipStream_t s) {
-  const dim3 grid(a.sh.nseg), block(kRootThreads);
-  switch (a.sh.D) {
-    case 64: hipLaunchKernelGGL(ec_win_roots<1>, grid, block, 0, s, a.in, a); break;
-    case 128: hipLaunchKernelGGL(ec_win_roots<2>, grid, block, 0, s, a.in, a); break;
-    case 256: hipLaunchKernelGGL(ec_win_roots<4>, grid, block, 0, s, a.in, a); break;
-    default: return hipErrorInvalidValue;
-  }
+  hipLaunchKernelGGL(ec_win_links, dim3(a.sh.ntiles), dim3(64), 0, s, a.in, a);
+  hipLaunchKernelGGL(ec_win_roots, dim3(a.sh.nseg), dim3(kRootThreads), 0, s, a.in, a);
   return hipGetLastError();
 }
 
