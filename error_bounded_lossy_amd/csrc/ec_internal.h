@@ -68,6 +68,8 @@ struct Work {
   uint32_t* tile_U;              // [ntiles] first occurrences in the tile
   uint32_t* tile_nout;           // [ntiles] outliers stored by the tile
   uint64_t* hash;                // slots: (hash32 << 32) | (row + 1), 0 = empty
+  uint64_t* range_slot;          // [T][range_items] (min, max) of each range item of the quantize
+                                 // pass (as ordered keys), 0 until written
   // staging between the quantize and assemble passes (D = 64, 128, 256 only;
   // written by the quantize pass before it is read, never cleared)
   uint64_t* stage_pl;            // [ntiles][64][D/64][12] bit-plane words
@@ -115,6 +117,11 @@ struct EncArgs {
   double sched;                  // iteration-wise factor, computed on the host
   uint32_t coder;                // the stream's coder: kCoderBitpack, kCoderHuffman or kCoderAuto
   uint32_t window;               // W of windowed references (1..255), 0: first occurrences
+  uint32_t fuse_range;           // the quantize pass finds the tables' ranges itself: range
+                                 // items one table ahead of the tiles, in table-major order
+  uint32_t tiles_per_table;      // scheduled tiles of each table (all chunks)
+  uint32_t range_items;          // range items per table
+  uint32_t range_ahead;          // tables whose range items go before the first tile
   uint64_t hash_keep;            // mask applied to row hashes (tests weaken it)
   Report* report;                // device pointer of the pinned report block
   uint32_t* seg_meta;            // in the report block: [nseg][2] U, eb valid (or NULL)

@@ -313,8 +313,7 @@ struct EncShared {
 // tile with a smaller number.  Workgroups are dispatched in increasing order
 // (per XCD), so the lowest unfinished tile is always resident and waits on
 // nothing unfinished: the waits cannot deadlock.  They are also bounded.
-__device__ __forceinline__ void take_tile(const EncArgs& a, EncShared& sh) {
-  const uint32_t ticket = blockIdx.x;
+__device__ __forceinline__ void take_tile(const EncArgs& a, EncShared& sh, uint32_t ticket) {
   uint32_t s, k;
   if (a.sh.tiles_per_seg) {  // every segment has the same number of tiles
     s = ticket / a.sh.tiles_per_seg;
@@ -334,6 +333,116 @@ __device__ __forceinline__ void take_tile(const EncArgs& a, EncShared& sh) {
   sh.n = nt ? min(kTileRows, rows - k * kTileRows) : 0;
 }
 
+// Order-preserving u32 key of a (non-NaN) float: keys compare as the values
+// do, -0 below +0; key 0 is no value's.
+__device__ __forceinline__ uint32_t f2key(float f) {
+  const uint32_t i = f2u(f);
+  return (i & 0x80000000u) ? ~i : (i | 0x80000000u);
+}
+__device__ __forceinline__ float key2f(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// With the range folded into the quantize pass, its workgroups take range
+// items and tiles in table-major order, the range items of table t + k
+// (k = range_ahead) just before the tiles of table t:
+//   R(0) .. R(k-1) | R(k) Q(0) | R(k+1) Q(1) | ... | Q(T-1)
+// A tile waits only for range items with smaller numbers, which wait for
+// nothing, so with workgroups dispatched in increasing order the waits always
+// end.  Returns the tile's ticket, or ~0u for range item *ri of table *rt.
+__device__ __forceinline__ uint32_t fused_item(const EncArgs& a, uint32_t i, uint32_t& rt, uint32_t& ri) {
+  const uint32_t T = a.sh.T, nr = a.range_items, tpt = a.tiles_per_table;
+  const uint32_t k = min(a.range_ahead, T), full = T - k;  // blocks with range items
+  uint32_t t, q;
+  if (i < k * nr) {
+    rt = i / nr;
+    ri = i - rt * nr;
+    return ~0u;
+  }
+  const uint32_t j = i - k * nr, blk = nr + tpt;
+  if (j < full * blk) {
+    t = j / blk;
+    q = j - t * blk;
+    if (q < nr) {
+      rt = t + k;
+      ri = q;
+      return ~0u;
+    }
+    q -= nr;
+  } else {
+    const uint32_t j2 = j - full * blk;
+    t = full + j2 / tpt;
+    q = j2 - (t - full) * tpt;
+  }
+  // tile q of table t in table-major order; segments of chunk p all have the
+  // same number of scheduled tiles, seg_tile_base[pT] / T of them in each
+  // table before chunk p
+  uint32_t lo = 0, hi = a.sh.P;
+  while (hi - lo > 1) {
+    const uint32_t mid = (lo + hi) >> 1;
+    if (a.w.seg_tile_base[mid * T] / T <= q) lo = mid;
+    else hi = mid;
+  }
+  return a.w.seg_tile_base[lo * T + t] + (q - a.w.seg_tile_base[lo * T] / T);
+}
+
+// A range item: (min, max) without NaN of its slice of table t, stored as
+// ordered keys (key(max), ~key(min)), or (0, 1) for no value.  Whole workgroup.
+__device__ void range_item(const EncArgs& a, uint32_t t, uint32_t ri) {
+  __shared__ uint32_t s_kh[kThreads / 64], s_kl[kThreads / 64];
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const uint64_t nel = (uint64_t)a.sh.B * a.sh.D;
+  uint64_t per = (nel + a.range_items - 1) / a.range_items;
+  per = (per + 1023) / 1024 * 1024;
+  const uint64_t beg = min((uint64_t)ri * per, nel), end = min(beg + per, nel);
+  const float* xt = a.x + (uint64_t)t * nel;
+  float lo = INFINITY, hi = -INFINITY;
+  if ((nel & 3) == 0) {  // eight 128-bit loads in flight per thread
+    const float4* x4 = reinterpret_cast<const float4*>(xt);
+    for (uint64_t i = beg / 4 + tid; i < end / 4; i += 8 * kThreads) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; u++) {
+        const uint64_t ii = i + (uint64_t)u * kThreads;
+        v[u] = ii < end / 4 ? x4[ii] : make_float4(NAN, NAN, NAN, NAN);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; u++) {
+        const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+          lo = e[c] < lo ? e[c] : lo;  // NaN compares false: skipped
+          hi = e[c] > hi ? e[c] : hi;
+        }
+      }
+    }
+  } else {
+    for (uint64_t i = beg + tid; i < end; i += kThreads) {
+      const float v = xt[i];
+      lo = v < lo ? v : lo;
+      hi = v > hi ? v : hi;
+    }
+  }
+  uint32_t kh = lo <= hi ? f2key(hi) : 0u, kl = lo <= hi ? ~f2key(lo) : 0u;
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t h2 = (uint32_t)__shfl_xor((int)kh, o), l2 = (uint32_t)__shfl_xor((int)kl, o);
+    kh = h2 > kh ? h2 : kh;
+    kl = l2 > kl ? l2 : kl;
+  }
+  if (lane == 0) {
+    s_kh[wv] = kh;
+    s_kl[wv] = kl;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (uint32_t q = 1; q < kThreads / 64; q++) {
+      kh = s_kh[q] > kh ? s_kh[q] : kh;
+      kl = s_kl[q] > kl ? s_kl[q] : kl;
+    }
+    st64(&a.w.range_slot[(uint64_t)t * a.range_items + ri], kh ? ((uint64_t)kh << 32) | kl : 1ull);
+  }
+}
+
 // Error bound of table t (Algorithm 1's factor times the table's value range
 // in range-relative mode).  Called by one whole wave; lanes reduce the range
 // partials in parallel.  Result and validity are returned to every lane.
@@ -344,7 +453,43 @@ __device__ __forceinline__ float table_eb(const EncArgs& a, uint32_t t, bool& va
   float eb = (float)f;
   if (a.eb_mode == 1) {
     float lo = INFINITY, hi = -INFINITY;
-    if (a.sh.B > 0) {
+    if (a.fuse_range) {
+      // every range item of the table has stored its (min, max): they come
+      // before the table's tiles and wait on nothing, so the wait ends
+      // (bounded all the same; a timeout is reported).  Each item has a word
+      // of its own: waiting waves poll plain loads, no contended atomics.
+      const uint64_t* sl = a.w.range_slot + (uint64_t)t * a.range_items;
+      uint32_t kh = 0, kl = 0, spins = 0;
+      for (;;) {
+        bool ready = true;
+        kh = 0;
+        kl = 0;
+        for (uint32_t j = lane; j < a.range_items; j += 64) {
+          const uint64_t w = ld64(&sl[j]);
+          ready = ready && w != 0;
+          const uint32_t h = (uint32_t)(w >> 32), l = (uint32_t)w;
+          if (h != 0) {  // the tile has values: fold the keys (max key, max ~key)
+            kh = h > kh ? h : kh;
+            kl = l > kl ? l : kl;
+          }
+        }
+        if (__all(ready)) break;
+        __builtin_amdgcn_s_sleep(8);
+        if (++spins > kSpinLimit) {
+          if (lane == 0) report_error(a.report, kDevErrTimeout);
+          break;
+        }
+      }
+      for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t h2 = (uint32_t)__shfl_xor((int)kh, o), l2 = (uint32_t)__shfl_xor((int)kl, o);
+        kh = h2 > kh ? h2 : kh;
+        kl = l2 > kl ? l2 : kl;
+      }
+      if (kh != 0) {
+        hi = key2f(kh);
+        lo = key2f(~kl);
+      }
+    } else if (a.sh.B > 0) {
       const float2* rp = reinterpret_cast<const float2*>(a.w.range_part) + (uint64_t)t * a.w.nbr;
       // eight partials per lane loaded together (one round trip up to 512)
       for (uint32_t j0 = 0; j0 < a.w.nbr; j0 += 8 * 64) {
@@ -708,7 +853,7 @@ __global__ void __launch_bounds__(kThreads) ec_encode_kernel(EncArgs a) {
   p += D + 4;
   uint8_t* s_urow = p;                                 // [64] tile row of each uid
 
-  if (tid == 0) take_tile(a, sh);
+  if (tid == 0) take_tile(a, sh, blockIdx.x);
   __syncthreads();
   const uint32_t ticket = sh.ticket, s = sh.seg, k = sh.tile, n = sh.n, rows = sh.rows;
   const uint32_t pch = s / T, t = s % T;
@@ -1149,7 +1294,16 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
   const uint32_t tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const uint32_t T = a.sh.T;
 
-  if (tid == 0) take_tile(a, sh);
+  uint32_t my_ticket = blockIdx.x;
+  if (a.fuse_range) {  // the same arithmetic in every thread: the branch is uniform
+    uint32_t rt = 0, ri = 0;
+    my_ticket = fused_item(a, blockIdx.x, rt, ri);
+    if (my_ticket == ~0u) {
+      range_item(a, rt, ri);
+      return;
+    }
+  }
+  if (tid == 0) take_tile(a, sh, my_ticket);
   for (uint32_t e = tid; e < kTileRows * C; e += kThreads) (&s_oflag[0][0])[e] = 0;
   __syncthreads();
   const uint32_t ticket = sh.ticket, s = sh.seg, k = sh.tile, n = sh.n, rows = sh.rows;
@@ -1716,6 +1870,8 @@ ec_write_fast(EncArgs a) {
   __shared__ uint4 s_info;
   const uint32_t tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const uint32_t ticket = blockIdx.x;
+  if (a.fuse_range && tid == 0)  // the quantize pass is done with the range items' words
+    for (uint32_t j = ticket; j < a.sh.T * a.range_items; j += a.sh.ntiles) a.w.range_slot[j] = 0;
   const TileCoord c = tile_coord(a, ticket);
   const uint32_t n = c.n;
   // a Huffman segment: its codebook follows the tile directory
@@ -3183,13 +3339,15 @@ __device__ __forceinline__ void decode_rows_special(const DecArgs& a, const uint
   if (!__all(ok) && lane == 0) report_error(a.report, kDevErrCorrupt);
 }
 
+// The decode step of one tile, after its index step (whole workgroup, no
+// barrier), from its descriptors.
 template <int C>
-__global__ void __launch_bounds__(kThreads) ec_decode_fast(const uint8_t* __restrict__ in,
-                                                          float* __restrict__ yout, DecArgs a) {
+__device__ __forceinline__ void decode_tile(const uint8_t* __restrict__ in, float* __restrict__ yout,
+                                            const DecArgs& a, uint32_t ticket, const uint4* td,
+                                            const uint4* drow, const uint32_t* dblk) {
   constexpr uint32_t D = 64u * C;
   constexpr uint32_t kRowsPerWave = kTileRows / (kThreads / 64);  // 16
   const uint32_t tid = threadIdx.x, lane = tid & 63, wv = wave_id();
-  const uint32_t ticket = blockIdx.x;
   const uint32_t T = a.sh.T, B = a.sh.B;
   // tile coordinates (from the plan, not the stream)
   uint32_t s, k;
@@ -3197,13 +3355,9 @@ __global__ void __launch_bounds__(kThreads) ec_decode_fast(const uint8_t* __rest
   const uint32_t pch = s / T, t = s % T;
   const uint32_t rows = chunk_row0(a.sh, pch + 1) - chunk_row0(a.sh, pch);
   const uint32_t n = rows ? min(kTileRows, rows - k * kTileRows) : 0u;
-  // the index step: wave 0 checks the tile and describes its rows in LDS
-  __shared__ DecIndexLds<C> xi;
-  if (wv == 0) index_tile<C>(in, a, ticket, xi);
-  __syncthreads();
   if (n == 0) return;
   float* yt = yout + ((uint64_t)t * B + chunk_row0(a.sh, pch) + (uint64_t)k * kTileRows) * D;
-  const uint4* dt = xi.td;
+  const uint4* dt = td;
   const uint32_t rbeg = wv * kRowsPerWave;
   // four blocks per transpose: group g of the wave holds its blocks
   // 4g .. 4g+3 in (row, block) order; lane L loads half L >> 5 of plane L & 7
@@ -3211,8 +3365,6 @@ __global__ void __launch_bounds__(kThreads) ec_decode_fast(const uint8_t* __rest
   constexpr uint32_t kGroupRows = 4 / C;
   constexpr uint32_t kGroups = kRowsPerWave * C / 4;
   const uint32_t gplane = lane & 7u, half = lane >> 5, gblk = (lane >> 3) & 3u;
-  const uint4* drow = xi.drow;
-  const uint32_t* dblk = xi.dblk;
   // the descriptors of the lane's row and block in every group (kind[]: the
   // row kind, with kRowOutliers when there are outliers to patch; garbage
   // for a raw or failed tile, and then unused)
@@ -3312,6 +3464,21 @@ __global__ void __launch_bounds__(kThreads) ec_decode_fast(const uint8_t* __rest
     if (!((special >> g) & 1u)) continue;
     decode_rows_special<C, kGroupRows>(a, sg, yt, rbeg + g * kGroupRows, n, eb, s2, drow, dblk);
   }
+}
+
+// Two tiles per workgroup: waves 0 and 1 index both at once (their chains of
+// dependent stream reads overlap), then the whole workgroup decodes one after
+// the other.
+constexpr uint32_t kDecTiles = 2;
+template <int C>
+__global__ void __launch_bounds__(kThreads) ec_decode_fast(const uint8_t* __restrict__ in,
+                                                          float* __restrict__ yout, DecArgs a) {
+  __shared__ DecIndexLds<C> xi[kDecTiles];
+  const uint32_t wv = wave_id(), t0 = blockIdx.x * kDecTiles;
+  if (wv < kDecTiles && t0 + wv < a.sh.ntiles) index_tile<C>(in, a, t0 + wv, xi[wv]);
+  __syncthreads();
+  for (uint32_t q = 0; q < kDecTiles && t0 + q < a.sh.ntiles; q++)
+    decode_tile<C>(in, yout, a, t0 + q, xi[q].td, xi[q].drow, xi[q].dblk);
 }
 
 // ---------------------------------------------------------------------------
@@ -3782,7 +3949,8 @@ hipError_t set_encode_lds_limit(size_t bytes) {
 }
 
 hipError_t launch_encode(const EncArgs& a, hipStream_t s) {
-  const dim3 grid(a.sh.ntiles), block(kThreads);
+  // with the range folded in, the quantize grid holds the range items too
+  const dim3 grid(a.sh.ntiles + (a.fuse_range ? a.sh.T * a.range_items : 0u)), block(kThreads);
   switch (a.sh.D) {
     case 64:
       hipLaunchKernelGGL(ec_quantize_fast<1>, grid, block, 0, s, a);
@@ -3929,15 +4097,16 @@ hipError_t launch_huff_decode(const DecArgs& a, hipStream_t s) {
 
 hipError_t launch_decode(const DecArgs& a, hipStream_t s) {
   const dim3 grid(a.sh.ntiles), block(kThreads);
+  const dim3 grid2((a.sh.ntiles + kDecTiles - 1) / kDecTiles);
   switch (a.sh.D) {
     case 64:
-      hipLaunchKernelGGL(ec_decode_fast<1>, grid, block, 0, s, a.in, a.y, a);
+      hipLaunchKernelGGL(ec_decode_fast<1>, grid2, block, 0, s, a.in, a.y, a);
       break;
     case 128:
-      hipLaunchKernelGGL(ec_decode_fast<2>, grid, block, 0, s, a.in, a.y, a);
+      hipLaunchKernelGGL(ec_decode_fast<2>, grid2, block, 0, s, a.in, a.y, a);
       break;
     case 256:
-      hipLaunchKernelGGL(ec_decode_fast<4>, grid, block, 0, s, a.in, a.y, a);
+      hipLaunchKernelGGL(ec_decode_fast<4>, grid2, block, 0, s, a.in, a.y, a);
       break;
     default:
       hipLaunchKernelGGL(ec_decode_kernel, grid, block, decode_lds_bytes(a.sh.D), s, a);

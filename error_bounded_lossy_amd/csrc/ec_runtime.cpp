@@ -23,6 +23,8 @@ struct Layout {
   uint32_t stream_coder = 1;  // the header's coder field
   uint64_t dyn, seg_start, seg_end, chunk_start, seg_fin;
   uint64_t tile_status, block_status, tile_inserted, tile_rec, tile_U, tile_nout, hash;
+  uint64_t range_slot = 0;
+  uint32_t range_items = 1;  // range items per table of the quantize pass (64 KiB of input each)
   uint64_t stage_pl = 0, stage_w = 0, stage_om = 0, stage_slot = 0;
   uint64_t tile_info = 0, tile_bitmap = 0, tile_first = 0, seg_eb = 0;
   uint64_t stage_sym = 0, hhist = 0, henc = 0, hbooks = 0, hstat = 0, tile_hsize = 0;
@@ -193,6 +195,11 @@ ec_status make_layout(const ec_plan_desc* d, Layout* L) {
   L->tile_U = take(4ull * tiles);
   L->tile_nout = take(4ull * tiles);
   L->hash = take(8ull * slots);
+  {
+    const uint64_t items = (4ull * nel + 65535) / 65536;
+    L->range_items = (uint32_t)(items < 1 ? 1 : (items > 256 ? 256 : items));
+  }
+  L->range_slot = take(8ull * T * L->range_items);
   o = aup(o, 256);
   L->dyn_bytes = o - L->dyn;
   if (ec::encode_has_assembly(D)) {
@@ -221,6 +228,11 @@ ec_status make_layout(const ec_plan_desc* d, Layout* L) {
   L->total = o;
   return EC_OK;
 }
+
+// Tables whose range items the quantize pass takes before its first tile: far
+// enough ahead that a tile rarely finds its table's range unfinished (on the
+// 26-table dim-128 batch, 16 ahead beat 1, 2, 4, 8 and all).
+constexpr uint32_t kRangeAhead = 16;
 
 double schedule_factor(const ec_schedule& s, int64_t iter) {
   int64_t i = iter < 0 ? 0 : iter;
@@ -326,6 +338,7 @@ ec::Work make_work(const Layout& L, uint8_t* ws) {
   w.tile_U = reinterpret_cast<uint32_t*>(ws + L.tile_U);
   w.tile_nout = reinterpret_cast<uint32_t*>(ws + L.tile_nout);
   w.hash = reinterpret_cast<uint64_t*>(ws + L.hash);
+  w.range_slot = reinterpret_cast<uint64_t*>(ws + L.range_slot);
   if (ec::encode_has_assembly(L.sh.D)) {
     w.stage_pl = reinterpret_cast<uint64_t*>(ws + L.stage_pl);
     w.stage_w = ws + L.stage_w;
@@ -739,6 +752,12 @@ ec_status enqueue_compress(ec_plan_s* pl, const ec::Work& work, bool clear, int6
                            const float* d_in, void* d_out, size_t out_cap, hipStream_t s) {
   const ec::Shape& sh = pl->L.sh;
   ec::PrepArgs pa{d_in, sh, work, pl->desc.eb_mode == EC_EB_REL_RANGE ? 1 : 0, clear ? 1 : 0};
+  // D = 64, 128, 256: the quantize pass finds the tables' ranges itself, its
+  // range items running one table ahead of its tiles (the input's first
+  // read overlaps the quantization instead of preceding it)
+  const uint32_t tpt = sh.ntiles / sh.T;
+  const bool fuse = pa.rel && sh.B > 0 && ec::encode_has_assembly(sh.D);
+  if (fuse) pa.rel = 0;
   uint32_t grid;
   if (pa.rel && sh.B > 0) {
     grid = sh.T * pl->L.nbr;
@@ -762,6 +781,10 @@ ec_status enqueue_compress(ec_plan_s* pl, const ec::Work& work, bool clear, int6
   ea.sched = schedule_factor(pl->desc.sched, iter);
   ea.coder = pl->L.stream_coder;
   ea.window = pl->desc.window;
+  ea.fuse_range = fuse ? 1u : 0u;
+  ea.tiles_per_table = tpt;
+  ea.range_items = pl->L.range_items;
+  ea.range_ahead = kRangeAhead;
   uint32_t hb = pl->desc.debug_hash_bits;
   ea.hash_keep = (hb == 0 || hb >= 64) ? ~0ull : ((1ull << hb) - 1ull);
   ea.report = pl->report_dev;

@@ -589,3 +589,26 @@ def test_special_values_wide_rows():
     x[1] = np.nan
     x[2] = 0.25
     assert_parity(make_cfg(T, B, D, eb_mode=1, eb=(0.01,)), x, label="special D=256")
+
+
+@pytest.mark.parametrize("T,B,D,P", [(3, 129, 64, 2), (5, 300, 128, 7), (4, 3, 64, 5), (2, 1000, 256, 3),
+                                     (40, 200, 128, 1)])
+def test_ranges_found_by_the_quantize_pass(T, B, D, P):
+    """Range-relative eb on D = 64*C: the quantize pass's range items run
+    ahead of its tiles, which take tables in table-major order across
+    chunks of different tile counts (and chunks without rows).  A table whose
+    extremes are one NaN-free row, one all-NaN table, one whose values are
+    zeros of both signs and one with an infinity are among them."""
+    rng = np.random.default_rng(T * 101 + B + D + P)
+    x = dup_rows(rng, T, B, D, scale=0.2)
+    x[0, -1, 0] = 7.5            # the maximum in the last row of the last chunk
+    x[0, 0, 1] = -3.25           # the minimum in the first row
+    if T > 1:
+        x[1] = np.nan
+        x[1, B // 2, 3] = 0.5    # one value: zero range, eb not valid
+    if T > 2:
+        x[2] = 0.0
+        x[2, ::2] = -0.0
+    if T > 3:
+        x[3, 0, 0] = np.inf
+    assert_parity(make_cfg(T, B, D, P, eb_mode=1, eb=(0.02,)), x, label="fused range")
