@@ -250,8 +250,13 @@ __global__ void __launch_bounds__(kBookThreads) huff_book(Ws w, uint8_t* __restr
   // keys: frequency, then the complement of the symbol (so that reading the
   // sorted keys backwards gives decreasing frequency, then increasing symbol)
   int cm = 0, lo = kTable, hi = -1;
-  for (int s = t; s < kTable; s += kBookThreads) {
-    const uint32_t f = hist[s];
+  uint32_t hv[kTable / kBookThreads];  // every load in flight before the first is used
+#pragma unroll
+  for (int q = 0; q < kTable / kBookThreads; q++) hv[q] = hist[t + q * kBookThreads];
+#pragma unroll
+  for (int q = 0; q < kTable / kBookThreads; q++) {
+    const int s = t + q * kBookThreads;
+    const uint32_t f = hv[q];
     uint64_t k = ~0ull;
     if (s < kNsym && f) {
       k = ((uint64_t)f << 12) | (uint64_t)(4095 - s);
@@ -263,7 +268,14 @@ __global__ void __launch_bounds__(kBookThreads) huff_book(Ws w, uint8_t* __restr
     key[s] = k;
     len[s] = 0;
   }
-  if (cm) {
+  // per wave first (the compiler would serialize lane by lane), then one
+  // update per wave
+  for (int o = 32; o > 0; o >>= 1) {
+    cm += __shfl_xor(cm, o, 64);
+    lo = min(lo, __shfl_xor(lo, o, 64));
+    hi = max(hi, __shfl_xor(hi, o, 64));
+  }
+  if ((t & 63) == 0 && cm) {
     atomicAdd(&s_m, cm);
     atomicMin(&s_lo, lo);
     atomicMax(&s_hi, hi);

@@ -46,6 +46,7 @@ class _Cfg(ctypes.Structure):
         ("sched_t0", ctypes.c_double), ("sched_k", ctypes.c_double),
         ("sched_phase", ctypes.c_int64), ("coder", ctypes.c_uint32),
         ("table_coder", ctypes.POINTER(ctypes.c_int32)), ("window", ctypes.c_uint32),
+        ("book_len", ctypes.c_void_p), ("book_have", ctypes.c_void_p),
     ]
 
 
@@ -142,6 +143,7 @@ class Config:
     coder: int = CODER_BITPACK
     table_coder: tuple | None = None
     window: int = 0
+    books: "BookState | None" = None  # codebook reuse across calls (state kept here)
 
     def _c(self):
         eb = np.ascontiguousarray(np.asarray(self.eb, dtype=np.float32).reshape(-1))
@@ -158,7 +160,9 @@ class Config:
                  self.sched_kind, self.sched_steps, self.sched_t0, self.sched_k,
                  self.sched_phase, self.coder,
                  tc.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if tc is not None
-                 else ctypes.POINTER(ctypes.c_int32)(), self.window)
+                 else ctypes.POINTER(ctypes.c_int32)(), self.window,
+                 self.books.lengths.ctypes.data if self.books is not None else None,
+                 self.books.have.ctypes.data if self.books is not None else None)
         return c, (eb, mult, tc)  # keep arrays alive with the struct
 
 
@@ -260,6 +264,20 @@ def classify(hindex, l_thresh: float, s_thresh: float, alpha: float, beta: float
 def max_compressed_bytes(cfg: Config) -> int:
     c, keep = cfg._c()
     return lib().ebo_max_compressed_bytes(ctypes.byref(c))
+
+
+class BookState:
+    """The codes kept between calls for codebook reuse: lengths [P*T][4095]
+    and a have flag per segment, updated by every compress call."""
+
+    def __init__(self, cfg):
+        self.lengths = np.zeros((cfg.P * cfg.T, 4095), np.uint8)
+        self.have = np.zeros(cfg.P * cfg.T, np.uint8)
+
+    def copy(self):
+        c = BookState.__new__(BookState)
+        c.lengths, c.have = self.lengths.copy(), self.have.copy()
+        return c
 
 
 @dataclass

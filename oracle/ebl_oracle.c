@@ -193,6 +193,7 @@ static int cfg_ok(const ebo_cfg* c) {
   if (c->eb_mode != EBO_EB_ABS && c->eb_mode != EBO_EB_REL) return 0;
   if (c->coder > EBO_CODER_AUTO) return 0;
   if (c->window > 255) return 0;
+  if ((c->book_len == NULL) != (c->book_have == NULL)) return 0;
   if (c->table_coder)
     for (uint32_t t = 0; t < c->T; t++)
       if (c->table_coder[t] < (int32_t)EBO_CODER_BITPACK || c->table_coder[t] > (int32_t)EBO_CODER_AUTO)
@@ -641,12 +642,32 @@ static uint32_t encode_tile(const seg_view* sv, uint32_t k, buf_t* b, uint32_t* 
 
 /* Code lengths of a segment's Huffman code: the histogram of E, the codes
    of every first-occurrence row (outliers as q = 0), as symbols q + 2047. */
-static void segment_lengths(const seg_view* sv, uint8_t* hlen) {
-  uint64_t freq[EBO_HUFF_NSYM];
-  memset(freq, 0, sizeof(freq));
+static void segment_hist(const seg_view* sv, uint64_t* freq) {
+  memset(freq, 0, sizeof(uint64_t) * EBO_HUFF_NSYM);
   for (uint32_t r = 0; r < sv->rows; r++) {
     if (sv->first[r] != r) continue;
     for (uint32_t d = 0; d < sv->D; d++) freq[sv->q[(size_t)r * sv->D + d] + EBO_QMAX]++;
+  }
+}
+
+/* The code of a Huffman segment: built from its histogram, or with codebook
+   reuse the kept code of segment s while it has a length for every symbol
+   the segment holds (then kept as it is, else replaced by the new one). */
+static void segment_lengths(const ebo_cfg* c, uint32_t s, const seg_view* sv, uint8_t* hlen) {
+  uint64_t freq[EBO_HUFF_NSYM];
+  segment_hist(sv, freq);
+  if (c->book_len) {
+    uint8_t* kept = c->book_len + (size_t)s * EBO_HUFF_NSYM;
+    int covers = c->book_have[s] != 0;
+    for (uint32_t x = 0; covers && x < EBO_HUFF_NSYM; x++) covers = !freq[x] || kept[x];
+    if (covers) {
+      memcpy(hlen, kept, EBO_HUFF_NSYM);
+      return;
+    }
+    ebo_huff_lengths(freq, hlen);
+    memcpy(kept, hlen, EBO_HUFF_NSYM);
+    c->book_have[s] = 1;
+    return;
   }
   ebo_huff_lengths(freq, hlen);
 }
@@ -785,9 +806,10 @@ int ebo_compress(const ebo_cfg* c, int64_t iter, const float* x, uint8_t* out, s
         if (encode_segment(&sv, nt, eb, NULL, &bp) != 0) rc = EBO_ERR_OOM;
         int use_huff = 0;
         uint32_t tcoder = c->table_coder ? (uint32_t)c->table_coder[t] : coder;
+        if (c->book_len && !(valid && tcoder != EBO_CODER_BITPACK)) c->book_have[p * T + t] = 0;
         if (rc == EBO_OK && valid && tcoder != EBO_CODER_BITPACK) {
           uint8_t hlen[EBO_HUFF_NSYM];
-          segment_lengths(&sv, hlen);
+          segment_lengths(c, p * T + t, &sv, hlen);
           if (encode_segment(&sv, nt, eb, hlen, &hf) != 0) rc = EBO_ERR_OOM;
           use_huff = tcoder == EBO_CODER_HUFFMAN || hf.n < bp.n;
         }

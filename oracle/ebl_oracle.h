@@ -141,7 +141,19 @@ typedef struct {
   const int32_t* table_coder; /* [T] coder of each table, NULL: `coder`    */
   uint32_t window;           /* 0: references to first occurrences; 1..255:
                                 windowed references (section III-E)        */
+  uint8_t* book_len;         /* [P*T][EBO_HUFF_NSYM] code lengths kept from the
+                                last call, or NULL: every Huffman segment
+                                builds its code (see below); in/out        */
+  uint8_t* book_have;        /* [P*T] 1: book_len[s] holds a code; in/out  */
 } ebo_cfg;
+
+/* Codebook reuse across calls (book_len != NULL): the value distribution of a
+ * table changes little from one training iteration to the next (section IV,
+ * Fig. 14), so a segment that may be Huffman-coded (valid eb, coder not bit
+ * planes) keeps the code of its previous call while that code has a length
+ * for every symbol the segment now holds; otherwise it builds a code from
+ * its histogram and keeps that one.  Segments that cannot be Huffman-coded
+ * keep no code.  The code used is the one stored in the segment. */
 
 /* Iteration-wise factor (Algorithm 1 OnlineDecay, read non-cumulatively). */
 double ebo_schedule(const ebo_cfg* c, int64_t iter);

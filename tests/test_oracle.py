@@ -884,3 +884,58 @@ def test_corrupt_window_distances_are_rejected():
         assert O.decompress(cfg, bad, status=True)[0] == O.ERR_CORRUPT
     with pytest.raises(ValueError):
         O.compress(O.Config(T=1, B=B, D=D, eb=(0.02,), window=256), 0, x)
+
+
+# --------------------------------------------------------------------------
+# codebook reuse across calls (stable distributions over training, Fig. 14)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("coder", [2, 3])
+def test_codebook_reuse_rule(coder):
+    """A segment keeps its previous code while that code has a length for
+    every symbol it now holds, else builds and keeps a new one; the stored
+    codebook is the code used; bit-plane tables keep nothing.  Streams stay
+    within the bound and decode like any other."""
+    rng = np.random.default_rng(40 + coder)
+    T, B, D = 3, 400, 32
+    tc = (coder, 1, coder)
+    books = O.BookState(O.Config(T=T, B=B, D=D))
+    for it, scale in enumerate([0.05, 0.04, 0.05, 0.3, 0.05]):
+        x = rng.normal(0, scale, (T, B, D)).astype(np.float32)
+        cfg = O.Config(T=T, B=B, D=D, eb=(0.01,), coder=coder, table_coder=tc, books=books)
+        before = books.copy()
+        c, st = check_stream(cfg, x)
+        cfg0 = O.Config(T=T, B=B, D=D, eb=(0.01,), coder=coder, table_coder=tc)
+        for seg in st.segments:
+            s = seg.p * T + seg.t
+            if tc[seg.t] == 1:
+                assert books.have[s] == 0
+                continue
+            # the symbols the segment holds, by the independent reader
+            freq = np.zeros(4095, np.int64)
+            for tl in seg.tiles:
+                qq, _ = SF._tile_codes(seg, tl, c.stream, D)
+                freq += np.bincount(qq + 2047, minlength=4095)
+            covered = before.have[s] and np.all((freq == 0) | (before.lengths[s] > 0))
+            fresh = O.huff_lengths(freq)
+            want = before.lengths[s] if covered else fresh
+            assert books.have[s] == 1
+            np.testing.assert_array_equal(books.lengths[s], want)
+            if seg.huff:
+                np.testing.assert_array_equal(seg.lengths, want)
+            if not covered:
+                # a fresh code is the one the call without reuse builds
+                st0 = SF.parse(O.compress(cfg0, 0, x, debug=False).stream)
+                s0 = st0.segments[s]
+                if s0.huff and seg.huff:
+                    np.testing.assert_array_equal(s0.lengths, fresh)
+        if it == 1:
+            assert books.have[0] and np.array_equal(books.lengths[0], before.lengths[0])  # reused
+
+
+def test_codebook_reuse_needs_both_arrays():
+    import ctypes
+    books = O.BookState(O.Config(T=1, B=4, D=4))
+    cfg = O.Config(T=1, B=4, D=4, eb=(0.1,), coder=2, books=books)
+    c, keep = cfg._c()
+    c.book_have = None
+    assert O.lib().ebo_max_compressed_bytes(ctypes.byref(c)) == 0
