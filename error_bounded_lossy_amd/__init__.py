@@ -45,7 +45,8 @@ class _Desc(ctypes.Structure):
         ("table_mult", ctypes.POINTER(ctypes.c_float)), ("sched", _Schedule),
         ("coder", ctypes.c_int32), ("debug_hash_bits", ctypes.c_uint32),
         ("d_workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-        ("window", ctypes.c_uint32), ("table_coder", ctypes.POINTER(ctypes.c_int32)),
+        ("window", ctypes.c_uint32), ("reuse_books", ctypes.c_uint32),
+        ("table_coder", ctypes.POINTER(ctypes.c_int32)),
     ]
 
 
@@ -156,7 +157,7 @@ def _stream_handle(stream) -> int:
 
 
 def _desc(T, B, D, P, eb_mode, eb, table_mult, schedule, debug_hash_bits, keep,
-          coder=CODER_BITPACK, table_coder=None, window=0):
+          coder=CODER_BITPACK, table_coder=None, window=0, reuse_books=False):
     ebs = [float(v) for v in (eb if hasattr(eb, "__len__") else [eb])]
     if len(ebs) == 1 and T > 1:
         ebs = ebs * T
@@ -177,7 +178,8 @@ def _desc(T, B, D, P, eb_mode, eb, table_mult, schedule, debug_hash_bits, keep,
         keep.append(c)
         tc = ctypes.cast(c, ctypes.POINTER(ctypes.c_int32))
     return _Desc(ABI_VERSION, T, B, D, P, int(eb_mode), ctypes.cast(arr, ctypes.POINTER(ctypes.c_float)),
-                 mult, s, int(coder), int(debug_hash_bits), None, 0, int(window), tc)
+                 mult, s, int(coder), int(debug_hash_bits), None, 0, int(window),
+                 1 if reuse_books else 0, tc)
 
 
 def workspace_bytes(T, B, D, P=1, eb_mode=EB_ABS, eb=1e-4, table_mult=None, schedule=None,
@@ -198,18 +200,20 @@ class Plan:
     def __init__(self, T: int, B: int, D: int, P: int = 1, eb_mode: int = EB_ABS, eb=1e-4,
                  table_mult=None, schedule=None, debug_hash_bits: int = 0, device=None,
                  workspace: bool = True, coder: int = CODER_BITPACK, table_coder=None,
-                 window: int = 0):
+                 window: int = 0, reuse_books: bool = False):
         """workspace=False builds a plan without a workspace: compress with
         compress_static (the library's static device scratch), decompress as
         usual.  coder: CODER_BITPACK, CODER_HUFFMAN or CODER_AUTO;
         table_coder: one of them per table (Algorithm 2), overriding coder;
-        window: 0, or 1..255 for windowed references (section III-E)."""
+        window: 0, or 1..255 for windowed references (section III-E);
+        reuse_books: Huffman segments keep their code across calls while it
+        covers their symbols."""
         import torch
         self.T, self.B, self.D, self.P = T, B, D, P
         self.coder = coder
         self._keep = []
         self._desc = _desc(T, B, D, P, eb_mode, eb, table_mult, schedule, debug_hash_bits,
-                           self._keep, coder, table_coder, window)
+                           self._keep, coder, table_coder, window, reuse_books)
         L = lib()
         nbytes = int(L.ec_workspace_bytes(ctypes.byref(self._desc)))
         if nbytes == 0:

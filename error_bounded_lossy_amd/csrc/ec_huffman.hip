@@ -224,8 +224,9 @@ __global__ void __launch_bounds__(kThreads) huff_hist(const uint16_t* __restrict
 // Codebook of segment blockIdx.x (n symbols per segment).
 __global__ void __launch_bounds__(kBookThreads) huff_book(Ws w, uint8_t* __restrict__ books,
                                                           uint32_t* __restrict__ chunk_off,
-                                                          uint64_t n) {
+                                                          uint64_t n, const uint32_t* skip) {
   const uint32_t seg = blockIdx.x;
+  if (skip && skip[seg]) return;  // the segment keeps its code (whole workgroup)
   const uint32_t* hist = w.hist + (size_t)seg * kTable;
   uint32_t* enc = w.enc + (size_t)seg * kTable;
   uint8_t* book = books + (size_t)seg * kBookStride;
@@ -782,7 +783,8 @@ ec_status encode_impl(const uint16_t* d_sym, uint32_t nseg, uint64_t n, uint8_t*
     const uint32_t hb = (uint32_t)(want < 1 ? 1 : (want > cap ? cap : want));
     hipLaunchKernelGGL(huff_hist, dim3(hb, nseg), dim3(kThreads), 0, s, d_sym, n, w);
   }
-  hipLaunchKernelGGL(huff_book, dim3(nseg), dim3(kBookThreads), 0, s, w, d_books, d_chunk_off, n);
+  hipLaunchKernelGGL(huff_book, dim3(nseg), dim3(kBookThreads), 0, s, w, d_books, d_chunk_off, n,
+                     (const uint32_t*)nullptr);
   if (n) {
     const uint32_t nch = num_chunks(n);
     uint32_t groups = (nch + 3) / 4;
@@ -826,13 +828,14 @@ namespace ec {
 // and the codebook bytes at books + seg * EC_HUFF_BOOK_MAX.  status gets the
 // builder's error bits (zeroed first by the caller).
 hipError_t launch_seg_books(uint32_t* hist, uint32_t* enc, uint8_t* books, uint32_t* status,
-                            uint32_t nseg, hipStream_t s) {
+                            const uint32_t* skip, uint32_t nseg, hipStream_t s) {
   Ws w{};
   w.status = status;
   w.hist = hist;
   w.enc = enc;
   // n = 1: the chunk table (here the status word) is not written
-  hipLaunchKernelGGL(huff_book, dim3(nseg), dim3(kBookThreads), 0, s, w, books, status, (uint64_t)1);
+  hipLaunchKernelGGL(huff_book, dim3(nseg), dim3(kBookThreads), 0, s, w, books, status, (uint64_t)1,
+                     skip);
   return hipGetLastError();
 }
 

@@ -95,6 +95,11 @@ struct Work {
   uint32_t* seg_coder;           // [nseg] 1: the segment is Huffman-coded
   uint16_t* hlut;                // [nseg][4096] decode tables
   uint32_t* hvalid;              // [nseg] decode table valid
+  uint32_t* hhave;               // [nseg] henc / hbooks hold the segment's code from the last
+                                 // call (constant region: zero at plan time)
+  uint32_t* hskip;               // [nseg] this call keeps that code (no build)
+  uint8_t* hdbooks;              // [nseg][kBookStride] decoding: codebooks copied from the stream
+  uint32_t* hdenc;               // [nseg][4096] decoding: the table builder's scratch
   const uint32_t* table_coder;   // [T] coder of each table (constant), or NULL: EncArgs::coder
 };
 
@@ -122,6 +127,7 @@ struct EncArgs {
   uint32_t tiles_per_table;      // scheduled tiles of each table (all chunks)
   uint32_t range_items;          // range items per table
   uint32_t range_ahead;          // tables whose range items go before the first tile
+  uint32_t reuse_books;          // keep each segment's Huffman code while it covers the symbols
   uint64_t hash_keep;            // mask applied to row hashes (tests weaken it)
   Report* report;                // device pointer of the pinned report block
   uint32_t* seg_meta;            // in the report block: [nseg][2] U, eb valid (or NULL)
@@ -186,7 +192,7 @@ hipError_t launch_huff_decode(const DecArgs& a, hipStream_t s);
 // in ec_huffman.hip: the codebook builder and the decode-table builder of the
 // Huffman coder, over per-segment arrays
 hipError_t launch_seg_books(uint32_t* hist, uint32_t* enc, uint8_t* books, uint32_t* status,
-                            uint32_t nseg, hipStream_t s);
+                            const uint32_t* skip, uint32_t nseg, hipStream_t s);
 hipError_t launch_seg_luts(const uint8_t* books, const uint32_t* zero_word, uint32_t* enc,
                            uint16_t* lut, uint32_t* valid, uint32_t* status, uint32_t nseg,
                            hipStream_t s);

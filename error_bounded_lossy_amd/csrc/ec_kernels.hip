@@ -2161,6 +2161,30 @@ __global__ void __launch_bounds__(kThreads) ec_hsize_tiles(EncArgs a) {
   }
 }
 
+// Codebook reuse, one wave per segment, after the histograms: a segment that
+// may be Huffman-coded keeps the code of the plan's previous call (henc,
+// hbooks) while that code has a length for every symbol the segment holds
+// (the builder then skips it); the segments that may be Huffman-coded hold a
+// code after this call, the others none.
+__global__ void __launch_bounds__(kThreads) ec_book_reuse(EncArgs a) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t s = blockIdx.x * (kThreads / 64) + wave_id();
+  if (s >= a.sh.nseg) return;
+  const uint32_t coder = a.w.table_coder ? a.w.table_coder[s % a.sh.T] : a.coder;
+  const bool want = a.w.seg_eb[s] != 0 && coder != kCoderBitpack;
+  bool covers = want && a.w.hhave[s] != 0;
+  if (covers) {
+    const uint32_t* h = a.w.hhist + (uint64_t)s * kHuffTable;
+    const uint32_t* e = a.w.henc + (uint64_t)s * kHuffTable;
+    for (uint32_t x = lane; x < kHuffTable; x += 64) covers = covers && !(h[x] != 0 && (e[x] >> 16) == 0);
+    covers = __all(covers);
+  }
+  if (lane == 0) {
+    a.w.hskip[s] = covers ? 1u : 0u;
+    a.w.hhave[s] = want ? 1u : 0u;
+  }
+}
+
 // One wave per segment: Huffman (with coder 2, or with coder 3 when strictly
 // smaller) or bit planes.  Both forms share the header and tile directory;
 // the Huffman form adds the padded codebook.
@@ -3502,7 +3526,7 @@ __global__ void __launch_bounds__(kThreads) ec_hbook_copy(DecArgs a) {
   dec_locate(a, a.in, a.seg_tile_base[s], shs[wv], ro);
   wave_lds_wait();
   const DecShared& sh = shs[wv];
-  uint8_t* bk = a.w.hbooks + (uint64_t)s * kBookStride;
+  uint8_t* bk = a.w.hdbooks + (uint64_t)s * kBookStride;
   uint64_t avail = 0;
   const uint8_t* src = a.in;
   if (sh.seg_ok && sh.hseg) {
@@ -3539,7 +3563,7 @@ __global__ void __launch_bounds__(64) ec_decode_huff(const uint8_t* __restrict__
   wave_lds_wait();
   // a Huffman segment's codebook is checked by the segment's first tile
   if (lane == 0 && sh.seg_ok && sh.hseg && sh.tile == 0) {
-    const uint8_t* bk = a.w.hbooks + (uint64_t)sh.seg * kBookStride;
+    const uint8_t* bk = a.w.hdbooks + (uint64_t)sh.seg * kBookStride;
     const bool empty = bk[0] == 1 && bk[1] == 0 && bk[2] == 0 && bk[3] == 0;
     if (!a.w.hvalid[sh.seg] && !empty) report_error(a.report, kDevErrCorrupt);
   }
@@ -4045,7 +4069,9 @@ hipError_t launch_huff_encode(const EncArgs& a, hipStream_t s) {
     case 256: hipLaunchKernelGGL(ec_hist_tiles<4>, tiles, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
-  hipError_t e = launch_seg_books(a.w.hhist, a.w.henc, a.w.hbooks, a.w.hstat, a.sh.nseg, s);
+  if (a.reuse_books) hipLaunchKernelGGL(ec_book_reuse, dim3(segw), block, 0, s, a);
+  hipError_t e = launch_seg_books(a.w.hhist, a.w.henc, a.w.hbooks, a.w.hstat,
+                                  a.reuse_books ? a.w.hskip : nullptr, a.sh.nseg, s);
   if (e != hipSuccess) return e;
   switch (a.sh.D) {
     case 64: hipLaunchKernelGGL(ec_hsize_tiles<1>, tiles, block, 0, s, a); break;
@@ -4070,7 +4096,7 @@ hipError_t launch_huff_write(const EncArgs& a, hipStream_t s) {
 
 hipError_t launch_huff_tables(const DecArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(ec_hbook_copy, dim3((a.sh.nseg + 3) / 4), dim3(kThreads), 0, s, a);
-  return launch_seg_luts(a.w.hbooks, a.w.hstat + 2, a.w.henc, a.w.hlut, a.w.hvalid, a.w.hstat + 1,
+  return launch_seg_luts(a.w.hdbooks, a.w.hstat + 2, a.w.hdenc, a.w.hlut, a.w.hvalid, a.w.hstat + 1,
                          a.sh.nseg, s);
 }
 

@@ -28,7 +28,7 @@ struct Layout {
   uint64_t stage_pl = 0, stage_w = 0, stage_om = 0, stage_slot = 0;
   uint64_t tile_info = 0, tile_bitmap = 0, tile_first = 0, seg_eb = 0;
   uint64_t stage_sym = 0, hhist = 0, henc = 0, hbooks = 0, hstat = 0, tile_hsize = 0;
-  uint64_t seg_coder = 0, hlut = 0, hvalid = 0;
+  uint64_t seg_coder = 0, hlut = 0, hvalid = 0, hhave = 0, hskip = 0, hdbooks = 0, hdenc = 0;
   bool huff = false;  // Huffman segments (coder 2 or 3)
   uint64_t dyn_bytes, total;
   uint32_t nbr;
@@ -181,6 +181,7 @@ ec_status make_layout(const ec_plan_desc* d, Layout* L) {
   L->hash_off = take(8ull * nseg);
   L->hash_log2 = take(4ull * nseg);
   if (d->table_coder) L->table_coder = take(4ull * T);
+  if (L->huff) L->hhave = take(4ull * nseg);  // constant region: zero at plan time
   L->range_part = take(8ull * T * L->nbr);
   o = aup(o, 256);
   L->dyn = o;
@@ -222,6 +223,9 @@ ec_status make_layout(const ec_plan_desc* d, Layout* L) {
       L->seg_coder = take(4ull * nseg);
       L->hlut = take(2ull * ec::kHuffTable * nseg);
       L->hvalid = take(4ull * nseg);
+      L->hskip = take(4ull * nseg);
+      L->hdbooks = take((uint64_t)ec::kBookStride * nseg);
+      L->hdenc = take(4ull * ec::kHuffTable * nseg);
     }
     o = aup(o, 256);
   }
@@ -355,6 +359,10 @@ ec::Work make_work(const Layout& L, uint8_t* ws) {
     w.henc = reinterpret_cast<uint32_t*>(ws + L.henc);
     w.hbooks = ws + L.hbooks;
     w.hstat = reinterpret_cast<uint32_t*>(ws + L.hstat);
+    w.hhave = reinterpret_cast<uint32_t*>(ws + L.hhave);
+    w.hskip = reinterpret_cast<uint32_t*>(ws + L.hskip);
+    w.hdbooks = ws + L.hdbooks;
+    w.hdenc = reinterpret_cast<uint32_t*>(ws + L.hdenc);
     w.tile_hsize = reinterpret_cast<uint32_t*>(ws + L.tile_hsize);
     w.seg_coder = reinterpret_cast<uint32_t*>(ws + L.seg_coder);
     w.hlut = reinterpret_cast<uint16_t*>(ws + L.hlut);
@@ -785,6 +793,7 @@ ec_status enqueue_compress(ec_plan_s* pl, const ec::Work& work, bool clear, int6
   ea.tiles_per_table = tpt;
   ea.range_items = pl->L.range_items;
   ea.range_ahead = kRangeAhead;
+  ea.reuse_books = pl->desc.reuse_books && pl->L.huff ? 1u : 0u;
   uint32_t hb = pl->desc.debug_hash_bits;
   ea.hash_keep = (hb == 0 || hb >= 64) ? ~0ull : ((1ull << hb) - 1ull);
   ea.report = pl->report_dev;

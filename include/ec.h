@@ -141,6 +141,14 @@ typedef struct {
                                workspace and at most 32768 rows per segment
                                (else EC_ERR_UNSUPPORTED); decoding windowed
                                segments needs a windowed plan.                */
+  uint32_t reuse_books;     /* nonzero: a segment that may be Huffman-coded
+                               keeps its code from the plan's previous call
+                               while that code has a length for every symbol
+                               it holds, else builds one and keeps it (value
+                               distributions are stable over training,
+                               section IV, Fig. 14).  Calls of one plan then
+                               depend on its previous compress call; the
+                               static-scratch entry point never reuses.       */
   const int32_t* table_coder; /* host [T] ec_coder of each table (Algorithm 2's
                                table-wise configuration, e.g. from
                                ec_select_coders) or NULL for `coder`; copied

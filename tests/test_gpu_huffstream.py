@@ -272,3 +272,41 @@ def test_corrupt_huffman_streams(D):
         n_ok += rc_g == ec.EC_OK
         n_bad += rc_g != ec.EC_OK
     say(f"[huffstream corrupt] random: {n_ok} decoded, {n_bad} rejected")
+
+
+@pytest.mark.parametrize("D,coder,tcoder", [(128, 2, None), (64, 3, None), (256, 3, (2, 1, 3))])
+def test_codebook_reuse_across_calls(D, coder, tcoder):
+    """Codebook reuse: a plan's calls keep each segment's code while it
+    covers the segment's symbols; every call's stream is byte for byte the
+    oracle's given the oracle's own kept codes, with decompressions (which
+    build their tables elsewhere in the workspace) between the calls."""
+    rng = np.random.default_rng(D + coder)
+    T, B, P = 3, 700, 2
+    cfg0 = cfg_of(T, B, D, P, 0, 0.01, coder)
+    cfg0.table_coder = tcoder
+    books = O.BookState(cfg0)
+    plan = ec.Plan(T, B, D, P, ec.EB_ABS, 0.01, coder=coder, table_coder=tcoder, reuse_books=True)
+    out = plan.empty_stream()
+    y = torch.empty(T, B, D, device="cuda")
+    reused = 0
+    for it, scale in enumerate([0.05, 0.045, 0.05, 0.4, 0.04, 0.05]):
+        x = dup_rows(rng, T, B, D, scale=scale, frac_unique=0.5)
+        if it == 2:
+            x[0, 5, 7] = 1e6  # an outlier (code 0, already in the code)
+        cfg = cfg_of(T, B, D, P, 0, 0.01, coder)
+        cfg.table_coder = tcoder
+        cfg.books = books
+        have_before = books.have.copy()
+        len_before = books.lengths.copy()
+        say(f"[huffstream] reuse D={D} coder={coder} call {it}")
+        ref = O.compress(cfg, it, x, debug=False)
+        plan.compress(torch.from_numpy(x).cuda(), out, it)
+        _, nbytes, _ = plan.ratio()
+        assert np.array_equal(out[:nbytes].cpu().numpy(), ref.stream), it
+        plan.decompress(out[:nbytes], y)
+        plan.ratio()
+        np.testing.assert_array_equal(y.cpu().numpy().view(np.uint32),
+                                      O.decompress(cfg, ref.stream).view(np.uint32))
+        reused += int(np.sum(have_before.astype(bool) & books.have.astype(bool) &
+                             np.all(len_before == books.lengths, axis=1)))
+    assert reused > 0
