@@ -737,8 +737,22 @@ __global__ void __launch_bounds__(kDecChunks) huff_decode(const uint32_t* __rest
   // kDecChunks * 96; they go through LDS when they fit (the usual case)
   const uint32_t glo = s_lo, ghi = s_hi;
   const bool staged = ghi - glo <= (uint32_t)kStageWords;
-  if (staged)
-    for (uint32_t i = t; i < ghi - glo; i += kDecChunks) stage[i] = words[glo + i];
+  if (staged) {  // eight loads per thread in flight before their stores
+    const uint32_t nw = ghi - glo;
+    for (uint32_t i0 = 0; i0 < nw; i0 += 8 * kDecChunks) {
+      uint32_t v[8];
+#pragma unroll
+      for (uint32_t q = 0; q < 8; q++) {
+        const uint32_t i = i0 + q * kDecChunks + t;
+        v[q] = i < nw ? words[glo + i] : 0u;
+      }
+#pragma unroll
+      for (uint32_t q = 0; q < 8; q++) {
+        const uint32_t i = i0 + q * kDecChunks + t;
+        if (i < nw) stage[i] = v[q];
+      }
+    }
+  }
   __syncthreads();
   if (c >= cend) return;
   const uint64_t sbase = (uint64_t)c * kChunk;

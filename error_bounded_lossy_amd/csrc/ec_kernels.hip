@@ -3589,8 +3589,21 @@ __global__ void __launch_bounds__(64) ec_decode_huff(const uint8_t* __restrict__
   // the record's words into LDS when they fit and lie inside the segment
   const uint32_t total = ct[nch];
   const bool staged = total <= kStage && (uint64_t)total <= wavail;
-  if (staged)
-    for (uint32_t i = lane; i < total; i += 64) s_words[i] = words[i];
+  if (staged) {  // eight loads per lane in flight before their stores
+    for (uint32_t i0 = 0; i0 < total; i0 += 8 * 64) {
+      uint32_t v[8];
+#pragma unroll
+      for (uint32_t q = 0; q < 8; q++) {
+        const uint32_t i = i0 + 64 * q + lane;
+        v[q] = i < total ? words[i] : 0u;
+      }
+#pragma unroll
+      for (uint32_t q = 0; q < 8; q++) {
+        const uint32_t i = i0 + 64 * q + lane;
+        if (i < total) s_words[i] = v[q];
+      }
+    }
+  }
   wave_lds_wait();
   if (lane < nch && !bad) {
     // every chunk ends exactly in its last word (at most 96 words for 256 codes
