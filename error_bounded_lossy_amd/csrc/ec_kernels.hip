@@ -1295,12 +1295,16 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
   const uint32_t T = a.sh.T;
 
   uint32_t my_ticket = blockIdx.x;
-  if (a.fuse_range) {  // the same arithmetic in every thread: the branch is uniform
-    uint32_t rt = 0, ri = 0;
-    my_ticket = fused_item(a, blockIdx.x, rt, ri);
-    if (my_ticket == ~0u) {
-      range_item(a, rt, ri);
-      return;
+  // (D = 256 has no range items: with them compiled in, that instance
+  // spilled registers and ran at half speed)
+  if constexpr (C < 4) {
+    if (a.fuse_range) {  // the same arithmetic in every thread: the branch is uniform
+      uint32_t rt = 0, ri = 0;
+      my_ticket = fused_item(a, blockIdx.x, rt, ri);
+      if (my_ticket == ~0u) {
+        range_item(a, rt, ri);
+        return;
+      }
     }
   }
   if (tid == 0) take_tile(a, sh, my_ticket);
