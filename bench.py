@@ -505,6 +505,9 @@ def main():
     ap.add_argument("--stream-coder", default="bitpack", choices=["bitpack", "huffman", "auto"],
                     help="the segment coder of the compressed stream: bit planes, Huffman, "
                          "or per segment the smaller")
+    ap.add_argument("--reuse-books", action="store_true",
+                    help="Huffman segments keep their code across calls while it covers "
+                         "their symbols (the batches cycled are successive iterations)")
     ap.add_argument("--window-sweep", action="store_true",
                     help="Table VI: the ratio of windowed references for W = 32 .. 255")
     args = ap.parse_args()
@@ -554,7 +557,8 @@ def main():
     sched = {"kind": w0.sched_kind, "t0": w0.sched_t0} if w0.sched_kind else None
     coder = {"bitpack": ec.CODER_BITPACK, "huffman": ec.CODER_HUFFMAN,
              "auto": ec.CODER_AUTO}[args.stream_coder]
-    plan = ec.Plan(T, B, D, 1, w0.eb_mode, w0.eb, schedule=sched, device=dev, coder=coder)
+    plan = ec.Plan(T, B, D, 1, w0.eb_mode, w0.eb, schedule=sched, device=dev, coder=coder,
+                   reuse_books=args.reuse_books)
     out = plan.empty_stream()
     y = torch.empty(T, B, D, dtype=torch.float32, device=dev)
     # read (untimed) before every timed call of the cold protocol: 512 MiB,
@@ -685,6 +689,7 @@ def main():
         "config": {"workload": f"{args.workload}: {WORKLOADS[args.workload]}", "tables": T,
                    "batch": B, "dim": D, "chunks": 1, "batches_cycled": len(batches),
                    "stream_coder": args.stream_coder,
+                   "reuse_books": bool(args.reuse_books),
                    "protocol": "cold: 512 MiB scratch read before each timed call"},
         "compress_GBps": round(4 * N / tc / 1e9, 2),
         "decompress_GBps": round(4 * N / td / 1e9, 2),

@@ -2177,11 +2177,22 @@ __global__ void __launch_bounds__(kThreads) ec_book_reuse(EncArgs a) {
   const uint32_t coder = a.w.table_coder ? a.w.table_coder[s % a.sh.T] : a.coder;
   const bool want = a.w.seg_eb[s] != 0 && coder != kCoderBitpack;
   bool covers = want && a.w.hhave[s] != 0;
-  if (covers) {
+  if (covers) {  // (uniform branch) sixteen pairs of loads per lane in flight at once
     const uint32_t* h = a.w.hhist + (uint64_t)s * kHuffTable;
     const uint32_t* e = a.w.henc + (uint64_t)s * kHuffTable;
-    for (uint32_t x = lane; x < kHuffTable; x += 64) covers = covers && !(h[x] != 0 && (e[x] >> 16) == 0);
-    covers = __all(covers);
+    bool miss = false;
+#pragma unroll
+    for (uint32_t q = 0; q < 4; q++) {
+      uint32_t hv[16], ev[16];
+#pragma unroll
+      for (uint32_t j = 0; j < 16; j++) {
+        hv[j] = h[(q * 16 + j) * 64 + lane];
+        ev[j] = e[(q * 16 + j) * 64 + lane];
+      }
+#pragma unroll
+      for (uint32_t j = 0; j < 16; j++) miss = miss || (hv[j] != 0 && (ev[j] >> 16) == 0);
+    }
+    covers = !__any(miss);
   }
   if (lane == 0) {
     a.w.hskip[s] = covers ? 1u : 0u;
