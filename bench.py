@@ -261,10 +261,13 @@ def summarize_counters(d: str, workload: str, copy_bytes: int, command: str,
               f"(fetch {fetch:.0f} KiB x {f_scale:.3f}, write {write:.0f} KiB x {w_scale:.3f})")
 
 
-def summarize_stats(d: str, workload: str, command: str, coder: str = "bitpack"):
+def summarize_stats(d: str, workload: str, command: str, coder: str = "bitpack",
+                    stream_coder: str = "bitpack"):
     """Kernel-trace statistics (rocprofv3 --stats) of a bench run, as text:
     writes profiles/path_kernels_<workload>_kernel_stats.txt for the path
-    kernels, or profiles/huffman_kernels_<workload>_kernel_stats.txt."""
+    kernels (path_kernels_<workload>_<stream coder>_... for a stream of
+    Huffman or automatically chosen segments), or
+    profiles/huffman_kernels_<workload>_kernel_stats.txt."""
     import csv
     import glob
     rows = []
@@ -296,7 +299,8 @@ def summarize_stats(d: str, workload: str, command: str, coder: str = "bitpack")
     text = "\n".join(lines) + "\n"
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     stem = "huffman_kernels" if coder == "huffman" else "path_kernels"
-    path = os.path.join(ROOT, "profiles", f"{stem}_{workload}_kernel_stats.txt")
+    tag = workload if coder == "huffman" or stream_coder == "bitpack" else f"{workload}_{stream_coder}"
+    path = os.path.join(ROOT, "profiles", f"{stem}_{tag}_kernel_stats.txt")
     with open(path, "w") as fh:
         fh.write(text)
     print(text, end="")
@@ -519,7 +523,8 @@ def main():
                            args.copy_calibration or (256 << 20), args.command, args.coder)
         return
     if args.summarize_stats:
-        summarize_stats(args.summarize_stats, args.workload, args.command, args.coder)
+        summarize_stats(args.summarize_stats, args.workload, args.command, args.coder,
+                        args.stream_coder)
         return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, 8)
@@ -657,11 +662,13 @@ def main():
     # decompression reads the stream and writes x^
     bytes_c = 4 * N * (2 if rel else 1) + S
     bytes_d = S + 4 * N
-    # per launch: the input read by the range pass (REL) and by the quantize
-    # pass, the stream written by assembly (by the one encode kernel when there
-    # is no assembly pass), and both for decode
+    # per launch: the input read by the range pass (REL; a range pass of its
+    # own, or the range items inside the quantize launch for D = 64, 128) and
+    # by the quantize pass, the stream written by assembly (by the one encode
+    # kernel when there is no assembly pass), and both for decode
+    enc_reads = 4 * N * (2 if rel and not n_prep else 1)
     kernels = {
-        "encode": (t_enc / max(n_enc, 1), 4 * N + (0 if n_asm else S)),
+        "encode": (t_enc / max(n_enc, 1), enc_reads + (0 if n_asm else S)),
         "decode": (t_dec / max(n_dec, 1), S + 4 * N),
     }
     if n_prep:
