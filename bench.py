@@ -319,25 +319,21 @@ def copy_calibration(nbytes: int, reps: int):
 
 
 def workload_codes(w, torch):
-    """Symbols q + 2047 of a workload batch: q = round(x / 2eb) with the
-    batch's per-table eb (range-relative eb scaled by the schedule, or the
-    absolute eb), codes beyond +-2047 and non-finite values counted as q = 0.
-    Input construction for the coder, outside any timed region."""
-    x = w.x
-    T = x.shape[0]
-    flat = x.view(T, -1)
-    fin = torch.isfinite(flat)
-    base = torch.tensor(w.eb, dtype=torch.float64, device=x.device)
-    if w.eb_mode == 1:
-        lo = torch.where(fin, flat, torch.full_like(flat, float("inf"))).amin(1).double()
-        hi = torch.where(fin, flat, torch.full_like(flat, float("-inf"))).amax(1).double()
-        base = base * (hi - lo)
-    if w.sched_kind == 1:
-        base = base * (1.0 + w.iteration / w.sched_t0) ** -0.5
-    eb = base.float().clamp_min(1e-30).double()
-    q = torch.round(flat.double() / (2.0 * eb[:, None]))
-    q = torch.where(fin & (q.abs() <= 2047), q, torch.zeros_like(q))
-    return (q + 2047).to(torch.int16).reshape(-1)
+    """Symbols q + 2047 of a workload batch: the quantization codes that the
+    compressor itself computes for the batch (its debug hook writes them out
+    while it compresses; an outlier's code is 0).  Input construction for the
+    coder, outside any timed region."""
+    import error_bounded_lossy_amd as ec
+    T, B, D = w.shape
+    sched = {"kind": w.sched_kind, "t0": w.sched_t0} if w.sched_kind else None
+    plan = ec.Plan(T, B, D, 1, w.eb_mode, w.eb, schedule=sched, device=w.x.device)
+    codes = torch.empty(T * B * D, dtype=torch.int32, device=w.x.device)
+    plan.debug_attach(codes=codes)
+    plan.compress(w.x, plan.empty_stream(), w.iteration)
+    st = plan.ratio()[2]
+    if st != ec.EC_OK:
+        sys.exit(f"[bench] compressing the batch for its codes failed: {st}")
+    return (codes + 2047).to(torch.int16)
 
 
 def bench_huffman(args):
