@@ -1379,6 +1379,12 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
   const uint32_t cap_mask = (1u << a.w.hash_log2[s]) - 1u;
   uint32_t H = 0;      // the row's hash (tag and first slot)
   uint64_t old0 = 0;   // what the first compare-and-swap found in that slot
+  // the wave's first row with the same hash (the row itself when it has
+  // none): a later row compares with that row instead of going to the
+  // table, so that a hot row costs one table operation per wave, not one
+  // per occurrence (atomics on one slot serialize)
+  uint32_t lead = lane;
+  uint64_t leads = 0;  // wave-uniform: 4 bits per row of the wave, its first row's lane
 
   static_for<0, (int)kNB>([&](auto nbc) {
     constexpr uint32_t nb = decltype(nbc)::value;
@@ -1474,12 +1480,27 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
     {  // the batch's row hashes to their owner lanes nb kRB .. nb kRB + kRB - 1
       const uint32_t hv = rows_reduce<kRB>(hs, lane);
       const uint32_t h = fmix32(__shfl(hv, (int)(((lane - nb * kRB) % kRB) * (64 / kRB))));
-      if (lane >= nb * kRB && lane < nb * kRB + kRB) {
-        H = h & (uint32_t)a.hash_keep;
-        const uint32_t i = rbeg + lane;
-        if (i < n && !a.window)
-          old0 = atomicCAS((unsigned long long*)&htab[H & cap_mask], 0ull,
-                           (unsigned long long)(((uint64_t)H << 32) | (uint64_t)(k * kTileRows + i + 1)));
+      if (lane >= nb * kRB && lane < nb * kRB + kRB) H = h & (uint32_t)a.hash_keep;
+      if (!a.window) {
+        // first lane (row) of the wave so far with the hash of each row of the
+        // batch, gathered in scalar registers
+#pragma unroll
+        for (uint32_t rr = 0; rr < kRB; rr++) {
+          const uint32_t ol = nb * kRB + rr;
+          const uint32_t hr = __builtin_amdgcn_readlane(H, ol);
+          const uint64_t m = __ballot(H == hr) & ((2ull << ol) - 1ull);
+          leads |= (uint64_t)__builtin_ctzll(m) << (4 * ol);
+        }
+        lead = lane < kRowsPerWave ? (uint32_t)(leads >> (4 * lane)) & 15u : lane;
+        if (lane >= nb * kRB && lane < nb * kRB + kRB) {
+          const uint32_t i = rbeg + lane;
+          if (i < n)
+            old0 = lead != lane
+                       // a hit on the earlier row, taken without a table operation
+                       ? ((uint64_t)H << 32) | (uint64_t)(k * kTileRows + rbeg + lead + 1)
+                       : atomicCAS((unsigned long long*)&htab[H & cap_mask], 0ull,
+                                   (unsigned long long)(((uint64_t)H << 32) | (uint64_t)(k * kTileRows + i + 1)));
+        }
       }
     }
     // bit planes, four blocks at a time (blocks 4g .. 4g+3 of the batch, in
@@ -1536,6 +1557,8 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
   const uint32_t i = rbeg + lane;
   bool active = lane < kRowsPerWave && i < n && !a.window;
   bool first = true;  // the first attempt's result is old0
+  bool at_lead = lead != lane;  // old0 names the wave's earlier row with the hash
+  bool via_lead = false;        // equal to that row: its slot is this row's
   uint32_t slot = H & cap_mask;
   const uint64_t mine = ((uint64_t)H << 32) | (uint64_t)(k * kTileRows + i + 1);
   uint32_t guard = 0;
@@ -1599,23 +1622,31 @@ __global__ void __launch_bounds__(kThreads) ec_quantize_fast(EncArgs a) {
           if (eq) {
             // the smaller row is the first occurrence; the slot only ever
             // decreases from the value seen, so a larger row needs no update
+            // (a row equal to the wave's earlier row is never the smaller)
             if ((uint32_t)mine < seen)
               __hip_atomic_fetch_min(&htab[slot], mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             active = false;
-          } else {
+            via_lead = at_lead;
+          } else if (!at_lead) {
             slot = (slot + 1) & cap_mask;
           }
+          // an earlier row of the wave with the same hash but another key:
+          // the row goes to the table from its first slot
+          at_lead = false;
         }
       }
     }
-    if (++guard > cap_mask + 2) {  // cannot happen: the table is at most a quarter full
+    if (++guard > cap_mask + 3) {  // cannot happen: the table is at most a quarter full
       if (active) {
         report_error(a.report, kDevErrTimeout);
         active = false;
       }
     }
   }
-  if (lane < kRowsPerWave && i < n) a.w.stage_slot[(uint64_t)ticket * kTileRows + i] = a.window ? H : slot;
+  // a row equal to the wave's earlier row lives in that row's slot (which is
+  // final: every lane has left the loop)
+  const uint32_t fslot = (uint32_t)__shfl((int)slot, (int)(via_lead ? lead : lane));
+  if (lane < kRowsPerWave && i < n) a.w.stage_slot[(uint64_t)ticket * kTileRows + i] = a.window ? H : fslot;
 }
 
 // ---------------------------------------------------------------------------
