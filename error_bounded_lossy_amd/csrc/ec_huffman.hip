@@ -136,6 +136,212 @@ __device__ uint32_t block_excl(uint32_t x, uint32_t* part, uint32_t* total) {
   return before + inc - x;
 }
 
+// ---------------------------------------------------------------------------
+// Huffman tree of the sorted leaf weights wt[0, m) by two queues (leaves,
+// then internal nodes in creation order; of two equal weights the leaf
+// first): pr[v] gets the internal node that takes node v (internal node
+// m + j is the j-th created).  Run by one wave, with uniform control flow.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kNoNode = 0xFFFFFFFFu;  // weight of an empty queue (weights stay below 2^31)
+
+// Element k (< 128, uniform) of a wave array held in two registers.
+__device__ __forceinline__ uint32_t wave_at(uint32_t r0, uint32_t r1, uint32_t k) {
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)r0, (int)(k & 63u));
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)r1, (int)(k & 63u));
+  return k < 64u ? a : b;
+}
+
+// m <= 128: the queues' weights live in registers (lane k of two registers),
+// so that every pick is a register read and a scalar compare (a form with
+// selects instead of branches takes twice the instructions and is slower).
+__device__ void tree_small(const uint32_t* wt, uint32_t* pr, uint32_t m) {
+  const uint32_t lane = lane_id();
+  const uint32_t l0 = lane < m ? wt[lane] : 0u, l1 = lane + 64u < m ? wt[lane + 64u] : 0u;
+  uint32_t i0 = 0, i1 = 0;   // internal node m + j at lane j of i0 (j < 64) or j - 64 of i1
+  uint32_t lq = 0, iq = 0;   // fronts: leaf lq, internal node m + iq
+  uint32_t lf = wave_at(l0, l1, 0), inf = kNoNode;
+  for (uint32_t nj = 0; nj + 1 < m; nj++) {
+    uint32_t sum = 0;
+#pragma unroll
+    for (int k = 0; k < 2; k++) {
+      if (lq < m && lf <= inf) {
+        sum += lf;
+        pr[lq] = m + nj;
+        lq++;
+        lf = lq < m ? wave_at(l0, l1, lq) : kNoNode;
+      } else {
+        sum += inf;
+        pr[m + iq] = m + nj;
+        iq++;
+        inf = iq < nj ? wave_at(i0, i1, iq) : kNoNode;
+      }
+    }
+    if (nj < 64u) i0 = lane == nj ? sum : i0;
+    else i1 = lane == nj - 64u ? sum : i1;
+    if (iq == nj) inf = sum;  // the internal queue was empty: the new node is its front
+  }
+}
+
+// First index in [lo, hi) whose weight is >= w (strict: > w).
+template <bool kStrict>
+__device__ __forceinline__ uint32_t wt_bound(const uint32_t* wt, uint32_t lo, uint32_t hi, uint32_t w) {
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi) >> 1;
+    const uint32_t v = wt[mid];
+    if (kStrict ? v <= w : v < w) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// Any m, in rounds.  A round takes the first two picks, whose sum N is the
+// round's first new node; every remaining older internal node (each at most
+// N) and every leaf of weight at most N is picked before that node in the
+// sequential order, so they are merged at once (a leaf before an internal
+// node of equal weight) and paired in merged order; an odd one out waits for
+// the next round, which then starts with it.  mrg holds at least 2m entries.
+__device__ void tree_rounds(uint32_t* wt, uint32_t* pr, uint32_t* mrg, uint32_t m) {
+  const uint32_t lane = lane_id();
+  const uint32_t nn = 2 * m - 1;
+  uint32_t p = 0, q = m, e = m;  // leaf front, internal front, next node
+  while (e < nn) {
+    uint32_t x[2], wx[2];
+#pragma unroll
+    for (int k = 0; k < 2; k++) {
+      const uint32_t wl = p < m ? __builtin_amdgcn_readfirstlane(wt[p]) : kNoNode;
+      const uint32_t wi = q < e ? __builtin_amdgcn_readfirstlane(wt[q]) : kNoNode;
+      if (p < m && wl <= wi) {
+        x[k] = p++;
+        wx[k] = wl;
+      } else {
+        x[k] = q++;
+        wx[k] = wi;
+      }
+    }
+    const uint32_t n0 = wx[0] + wx[1];
+    const uint32_t eo = e;  // the older internal nodes are [q, eo)
+    if (lane == 0) {
+      wt[eo] = n0;
+      pr[x[0]] = eo;
+      pr[x[1]] = eo;
+    }
+    e++;
+    // leaves [p, p + na) weigh at most n0: blocks of s1 leaves, then one block
+    const uint32_t span = m - p;
+    uint32_t na = 0;
+    if (span) {
+      const uint32_t s1 = (span + 63u) >> 6;  // <= 64: m < 4096
+      const uint32_t b0 = lane * s1;
+      const bool full = b0 < span && wt[p + min(span, b0 + s1) - 1u] <= n0;
+      const uint32_t c1 = (uint32_t)__builtin_popcountll(__ballot(full));
+      const uint32_t base = c1 * s1;
+      if (base >= span) {
+        na = span;
+      } else {
+        const bool in = lane < s1 && base + lane < span && wt[p + base + lane] <= n0;
+        na = base + (uint32_t)__builtin_popcountll(__ballot(in));
+      }
+    }
+    const uint32_t nb = eo - q, tot = na + nb;
+    for (uint32_t t = lane; t < tot; t += 64u) {
+      if (t < na) {
+        const uint32_t w = wt[p + t];
+        mrg[t + wt_bound<false>(wt, q, eo, w) - q] = p + t;
+      } else {
+        const uint32_t j = t - na, w = wt[q + j];
+        mrg[j + wt_bound<true>(wt, p, p + na, w) - p] = q + j;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    const uint32_t np = tot >> 1;
+    uint32_t nleaf = 0;
+    for (uint32_t t = lane; t < np; t += 64u) {
+      const uint32_t u = mrg[2 * t], v = mrg[2 * t + 1];
+      wt[e + t] = wt[u] + wt[v];
+      pr[u] = e + t;
+      pr[v] = e + t;
+      nleaf += (u < m) + (v < m);
+    }
+    nleaf = wave_sum(nleaf);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    p += nleaf;
+    q += 2 * np - nleaf;
+    e += np;
+  }
+}
+
+// T.81 Annex K.3 on the counts per length (lane l of cl holds BITS[l], one
+// wave, uniform control flow), a whole level at a time.  The single steps
+// take two codes of the longest length i, one to length i-1 and the other,
+// with a code of the longest length j < i-1 that exists, to j+1.  At level i
+// the P = BITS[i]/2 steps use the codes below i-1 deepest first, and a code
+// of length k < i-1 takes 2^(i-1-k) - 1 steps before its descendants are all
+// at length i-1 (it becomes two codes of length k+1, each of which does the
+// same): full codes are taken in bulk, a code taken in part leaves one or two
+// codes on each level it passed.  Every code of length i-2 so taken adds two
+// codes of length i-1, and every step one more.
+__device__ uint32_t k3_levels(uint32_t cl) {
+  const uint32_t lane = lane_id();
+  auto at = [&](uint32_t l) { return (uint32_t)__builtin_amdgcn_readlane((int)cl, (int)l); };
+  auto add = [&](uint32_t l, uint32_t d) { cl += lane == l ? d : 0u; };
+  // codes of length k < i-1 that R steps use up in full (R < 2^11: P is at
+  // most half the alphabet), and the steps each takes
+  auto full = [&](uint32_t R, uint32_t sh, uint32_t have, uint32_t& f) {
+    f = sh > 11 ? 0xFFFFFFFFu : (1u << sh) - 1u;
+    return sh > 11 ? 0u : min(have, R / f);
+  };
+  for (;;) {
+    const uint64_t nz = __ballot(cl != 0);
+    if (nz == 0) break;
+    const uint32_t i = 63u - (uint32_t)__builtin_clzll(nz);
+    if (i <= (uint32_t)kMaxLen) break;
+    const uint32_t P = at(i) >> 1;
+    if (P == 0) break;  // an odd count at the deepest level: not a complete code
+    uint32_t R = P, E = 0;
+    for (uint32_t k = i - 2; R > 0 && k > 0; k--) {
+      const uint32_t bk = at(k);
+      if (bk == 0) continue;
+      const uint32_t sh = i - 1 - k;  // a code of length k takes 2^sh - 1 steps
+      uint32_t f;
+      const uint32_t u = full(R, sh, bk, f);
+      add(k, 0u - u);
+      R -= u * f;
+      if (u) E += u << (sh - 1);  // u > 0 only when sh <= 11
+      if (R == 0) break;
+      if (bk > u) {  // one more code of length k, taken in part
+        add(k, 0u - 1u);
+        R--;  // it becomes two codes of length k + 1
+        uint32_t l = k + 1, cnt = 2;
+        for (;;) {
+          if (R == 0) {
+            add(l, cnt);
+            break;
+          }
+          const uint32_t shl = i - 1 - l;
+          uint32_t fl;
+          const uint32_t ul = full(R, shl, cnt, fl);
+          R -= ul * fl;
+          if (ul) E += ul << (shl - 1);
+          cnt -= ul;
+          if (R == 0) {
+            add(l, cnt);
+            break;
+          }
+          add(l, cnt - 1);  // the other stays; this one goes on a level
+          R--;
+          l++;
+          cnt = 2;
+          if (l + 1 >= i) break;  // cannot happen for a complete code
+        }
+        break;
+      }
+    }
+    add(i, 0u - 2u * P);
+    add(i - 1, P + 2u * E);
+  }
+  return cl;
+}
+
 // Canonical codes (RFC 1951 section 3.2.2): the code of symbol s with length
 // l is first[l] plus the number of symbols below s that have length l.  Each
 // thread owns kTable / blockDim.x consecutive symbols; the per-length counts
@@ -326,36 +532,12 @@ __global__ void __launch_bounds__(kBookThreads) huff_book(Ws w, uint8_t* __restr
       syms[i] = (uint16_t)(4095 - (uint32_t)(k & 0xFFFu));
     }
     __syncthreads();
-    // two queues: sorted leaves [0, m) and internal nodes [m, nx) in creation
-    // order; of two equal weights the leaf is taken first
-    if (t == 0) {
-      const int nn = 2 * m - 1;
-      int lq = 0, iq = m;
-      // the first two weights of each queue live in registers (all weights
-      // stay below 2^31, so 2^32-1 marks a node not yet created); a queue's
-      // next weight is loaded one pick before it can be needed
-      uint32_t lf = wt[0], lf2 = wt[1], inf = 0xFFFFFFFFu, inf2 = 0xFFFFFFFFu;
-      for (int nx = m; nx < nn; nx++) {
-        uint32_t sum = 0;
-        for (int k = 0; k < 2; k++) {
-          if (lq < m && lf <= inf) {
-            sum += lf;
-            pr[lq] = (uint32_t)nx;
-            lq++;
-            lf = lf2;
-            lf2 = lq + 1 < m ? wt[lq + 1] : 0u;
-          } else {
-            sum += inf;
-            pr[iq] = (uint32_t)nx;
-            iq++;
-            inf = inf2;
-            inf2 = iq + 1 < nx ? wt[iq + 1] : 0xFFFFFFFFu;
-          }
-        }
-        wt[nx] = sum;
-        if (iq == nx) inf = sum;  // the queue was empty: the new node is its front
-        else if (iq + 1 == nx) inf2 = sum;
-      }
+    // two queues: sorted leaves [0, m) and internal nodes [m, 2m-1) in
+    // creation order; of two equal weights the leaf is taken first (one wave;
+    // the merge buffer of the rounds reuses the sort keys' space)
+    if (t < 64) {
+      if (m <= 128) tree_small(wt, pr, (uint32_t)m);
+      else tree_rounds(wt, pr, reinterpret_cast<uint32_t*>(key), (uint32_t)m);
     }
     __syncthreads();
     const int nn = 2 * m - 1, root = nn - 1;
@@ -389,22 +571,14 @@ __global__ void __launch_bounds__(kBookThreads) huff_book(Ws w, uint8_t* __restr
     // codes of the longest length i: one moves to length i-1 (next to its
     // prefix), and the other becomes a sibling of a code of the longest
     // length j < i-1 that exists, which moves to j+1 with it
-    uint32_t cl = bits[t];
-    for (;;) {
-      const uint64_t nz = __ballot(cl != 0);
-      if (nz == 0) break;
-      const int i = 63 - __builtin_clzll(nz);
-      if (i <= kMaxLen) break;
-      const int j = 63 - __builtin_clzll(nz & ((1ull << (i - 1)) - 1));
-      cl += (t == i ? 0u - 2u : 0u) + (t == i - 1 ? 1u : 0u) + (t == j + 1 ? 2u : 0u) +
-            (t == j ? 0u - 1u : 0u);
-    }
+    const uint32_t cl = k3_levels(bits[t]);
     // cum[l]: codes of length <= l; first[l] = 2 (first[l-1] + BITS[l-1]),
     // i.e. the sum over k < l of BITS[k] << (l - k)
     const uint32_t inc = wave_incl(t >= 1 && t <= kMaxLen ? cl : 0u);
     uint32_t f = 0;
+#pragma unroll
     for (int k = 1; k < kMaxLen; k++) {
-      const uint32_t bk = (uint32_t)__shfl((int)cl, k, 64);
+      const uint32_t bk = (uint32_t)__builtin_amdgcn_readlane((int)cl, k);
       if (k < t) f += bk << (t - k);
     }
     if (t <= kMaxLen) {

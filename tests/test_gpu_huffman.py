@@ -117,6 +117,20 @@ def test_length_limit_with_fibonacci_weights(coder, m):
     check_parity(coder, sym, f"fibonacci m={m}")
 
 
+@pytest.mark.parametrize("m,alpha", [(100, 3.0), (128, 3.0), (129, 3.0), (300, 1.6), (900, 2.0),
+                                     (4095, 1.1)])
+def test_heavy_tailed_counts(coder, m, alpha):
+    """Power-law counts (rank r used about 2e5 / r^alpha times, at least
+    once): trees far deeper than 12, so the length limit moves many codes,
+    on both sides of 128 used symbols."""
+    rng = np.random.default_rng(m)
+    used = rng.choice(4095, m, replace=False)
+    counts = np.maximum(1, (2e5 / np.arange(1, m + 1) ** alpha).astype(np.int64))
+    sym = np.repeat(used, counts).astype(np.uint16)
+    rng.shuffle(sym)
+    check_parity(coder, sym, f"power law m={m}")
+
+
 def test_many_ties(coder):
     rng = np.random.default_rng(9)
     used = rng.choice(4095, 600, replace=False)
