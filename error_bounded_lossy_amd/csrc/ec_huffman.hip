@@ -764,113 +764,173 @@ __global__ void __launch_bounds__(kThreads) huff_write(const uint16_t* __restric
 // report: set the status word for a bad codebook (with no chunks to decode);
 // else workgroup 0 zeroes the status word, and the decode kernel, which runs
 // after this one, reports the segments whose codebook is not valid.
-__global__ void __launch_bounds__(kBookThreads) huff_dec_book(const uint8_t* __restrict__ books,
-                                                          uint64_t book_bytes,
-                                                          const uint32_t* __restrict__ chunk_off,
-                                                          uint64_t n, Ws w, int report) {
+// Decode table of segment blockIdx.x, 256 threads: thread t reads the lengths
+// of symbols lo + 16t .. lo + 16t + 15 (eight codebook bytes, all loads
+// issued together), counts them per length in 16-bit fields (two lengths per
+// word), and the workgroup's prefix of those counts gives every symbol its
+// rank among the codes of its length, i.e. its canonical code (RFC 1951
+// section 3.2.2).  Symbols go to LDS in code order; then thread t fills table
+// entries 16t .. 16t + 15, each from the length whose code range covers it.
+// The codebook is validated as before: lengths up to 12, the first and last
+// symbol of its range used, the padding nibble zero, a complete code.
+constexpr int kDecBookThreads = 256;
+__global__ void __launch_bounds__(kDecBookThreads) huff_dec_book(const uint8_t* __restrict__ books,
+                                                              uint64_t book_bytes,
+                                                              const uint32_t* __restrict__ chunk_off,
+                                                              uint64_t n, Ws w, int report) {
+  constexpr int kPer = kTable / kDecBookThreads;  // 16 symbols and 16 table entries per thread
+  constexpr int kWaves = kDecBookThreads / 64;
   const uint32_t seg = blockIdx.x;
   const uint8_t* book = books + (size_t)seg * kBookStride;
-  uint32_t* enc = w.enc + (size_t)seg * kTable;
   uint16_t* lut = w.lut + (size_t)seg * kTable;
-  __shared__ uint8_t len[kTable];
   __shared__ uint16_t order[kTable];
-  __shared__ uint32_t cnt[kMaxLen + 1], first[kMaxLen + 1], base[kMaxLen + 1];
-  __shared__ uint64_t part[16][3];
-  __shared__ uint32_t s_kraft, s_m;
-  __shared__ int s_bad;
-  const int t = threadIdx.x;
-  if (t == 0) {
-    s_bad = 0;
-    s_kraft = 0;
-    s_m = 0;
-    if (!report && seg == 0) w.status[0] = 0;
-  }
-  if (t <= kMaxLen) cnt[t] = 0;
-  for (int i = t; i < kTable; i += kBookThreads) len[i] = 0;
-  __syncthreads();
-  int bad = 0;
+  __shared__ uint32_t part[kWaves][8];  // per wave: six count words, Kraft sum, flags
+  const uint32_t t = threadIdx.x, lane = t & 63u, wv = t >> 6;
+  if (t == 0 && !report && seg == 0) w.status[0] = 0;
+  bool bad = false;
   uint32_t lo = 1, hi = 0;
   if (book_bytes < 4) {
-    bad = 1;
+    bad = true;
   } else {
     lo = book[0] | (uint32_t)book[1] << 8;
     hi = book[2] | (uint32_t)book[3] << 8;
-    if (hi < lo) {
-      bad = !(lo == 1 && hi == 0);
-    } else if (hi >= (uint32_t)kNsym || 4 + (uint64_t)(hi - lo + 2) / 2 > book_bytes) {
-      bad = 1;
-    }
+    if (hi < lo) bad = !(lo == 1 && hi == 0);
+    else bad = hi >= (uint32_t)kNsym || 4 + (uint64_t)(hi - lo + 2) / 2 > book_bytes;
   }
   const bool empty = !bad && hi < lo;
-  if (empty && n > 0) bad = 1;
-  if (seg == 0 && t == 0 && chunk_off[0] != 0) bad = 1;
-  if (!bad && !empty) {
-    const uint32_t nb = hi - lo + 1;
-    uint32_t kr = 0, mm = 0;
-    for (uint32_t k = t; k < nb; k += kBookThreads) {
-      const uint32_t l = (book[4 + k / 2] >> (4 * (k & 1))) & 15u;
-      if (l > (uint32_t)kMaxLen) bad = 1;
-      else if (l) {
-        len[lo + k] = (uint8_t)l;
+  if (empty && n > 0) bad = true;
+  if (seg == 0 && chunk_off[0] != 0) bad = true;
+  const uint32_t nb = bad || empty ? 0u : hi - lo + 1, nbytes = (nb + 1) / 2;
+  // lengths of this thread's symbols, 4 bits each
+  uint8_t by[kPer / 2];
+#pragma unroll
+  for (int j = 0; j < kPer / 2; j++) {
+    const uint32_t b = (uint32_t)kPer / 2 * t + j;
+    by[j] = b < nbytes ? book[4 + b] : (uint8_t)0;
+  }
+  uint32_t cw[6] = {0, 0, 0, 0, 0, 0};  // count of length l in field (l-1) & 1 of word (l-1) >> 1
+  uint32_t kr = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; j++) {
+    const uint32_t k = (uint32_t)kPer * t + j;
+    const uint32_t l = (by[j >> 1] >> (4 * (j & 1))) & 15u;
+    if (k < nb && l) {
+      if (l > (uint32_t)kMaxLen) {
+        bad = true;
+      } else {
+        cw[(l - 1) >> 1] += 1u << (16 * ((l - 1) & 1));
         kr += 1u << (kMaxLen - l);
-        mm++;
-        atomicAdd(&cnt[l], 1u);
       }
     }
-    if (t == 0) {
-      if ((nb & 1) && (book[4 + nb / 2] >> 4)) bad = 1;
-      const uint32_t llo = book[4] & 15u, lhi = (book[4 + (nb - 1) / 2] >> (4 * ((nb - 1) & 1))) & 15u;
-      if (!llo || !lhi) bad = 1;
+    if (k >= nb && l) bad = true;  // the padding nibble
+    if (nb && (k == 0 || k == nb - 1) && !l) bad = true;  // lo and hi are used
+  }
+  // prefix of the counts over the workgroup
+  uint32_t inc[6];
+#pragma unroll
+  for (int q = 0; q < 6; q++) inc[q] = wave_incl(cw[q]);
+  const uint32_t krw = wave_sum(kr);
+  const uint64_t badw = __ballot(bad);
+  if (lane == 63) {
+#pragma unroll
+    for (int q = 0; q < 6; q++) part[wv][q] = inc[q];
+    part[wv][6] = krw;
+    part[wv][7] = badw != 0;
+  }
+  __syncthreads();
+  uint32_t before[6] = {0, 0, 0, 0, 0, 0}, tot[6] = {0, 0, 0, 0, 0, 0}, kraft = 0, anybad = 0;
+#pragma unroll
+  for (int v = 0; v < kWaves; v++) {
+#pragma unroll
+    for (int q = 0; q < 6; q++) {
+      const uint32_t x = part[v][q];
+      before[q] += (uint32_t)v < wv ? x : 0u;
+      tot[q] += x;
     }
-    if (kr) atomicAdd(&s_kraft, kr);
-    if (mm) atomicAdd(&s_m, mm);
+    kraft += part[v][6];
+    anybad |= part[v][7];
   }
-  if (bad) s_bad = 1;
-  __syncthreads();
-  if (!s_bad && !empty) {
-    const bool complete = s_m == 1 ? cnt[1] == 1 : s_kraft == (1u << kMaxLen);
-    if (!complete) bad = 1;
+  auto field = [](const uint32_t (&a)[6], uint32_t l) {  // the count of length l
+    return (a[(l - 1) >> 1] >> (16 * ((l - 1) & 1))) & 0xFFFFu;
+  };
+  uint32_t m = 0;
+  for (uint32_t l = 1; l <= (uint32_t)kMaxLen; l++) m += field(tot, l);
+  if (!anybad && !empty) {
+    const bool complete = m == 1 ? field(tot, 1) == 1 : kraft == (1u << kMaxLen);
+    if (!complete) anybad = 1;
   }
-  __syncthreads();
-  if (bad) s_bad = 1;
-  __syncthreads();
-  if (s_bad) {
+  if (anybad) {
     if (t == 0) {
       if (report) status_or(w.status, kStCorrupt);
       w.valid[seg] = 0;
     }
     return;
   }
-  if (t == 0) {
+  if (t == 0) w.valid[seg] = 1;
+  // per length l (registers: every index below is a constant): the first
+  // code, the table range [lo_l, hi_l) its codes cover, the code-order index
+  // of its first code, and where this thread's first code of length l goes
+  uint32_t tlo[kMaxLen + 1], thi[kMaxLen + 1], tfirst[kMaxLen + 1], tbase[kMaxLen + 1],
+      tpos[kMaxLen + 1];
+  uint32_t ex[6];  // codes of each length before this thread's (earlier waves and lanes)
+#pragma unroll
+  for (int q = 0; q < 6; q++) ex[q] = before[q] + inc[q] - cw[q];
+  {
     uint32_t code = 0, idx = 0;
+#pragma unroll
     for (int l = 1; l <= kMaxLen; l++) {
-      if (l > 1) code = (code + cnt[l - 1]) << 1;
-      first[l] = code;
-      base[l] = idx;
-      idx += cnt[l];
+      const uint32_t c = field(tot, (uint32_t)l);
+      if (l > 1) code = (code + field(tot, (uint32_t)l - 1)) << 1;
+      tfirst[l] = code;
+      tbase[l] = idx;
+      tlo[l] = code << (kMaxLen - l);
+      thi[l] = (code + c) << (kMaxLen - l);
+      tpos[l] = idx + ((ex[(l - 1) >> 1] >> (16 * ((l - 1) & 1))) & 0xFFFFu);
+      idx += c;
     }
-    w.valid[seg] = 1;
+  }
+  // this thread's symbols in code order: a symbol's rank among the codes of
+  // its length is the workgroup's count before this thread plus the
+  // thread's own earlier symbols of that length
+  uint32_t lj[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; j++) {
+    const uint32_t k = (uint32_t)kPer * t + j;
+    const uint32_t l = (by[j >> 1] >> (4 * (j & 1))) & 15u;
+    lj[j] = k < nb ? l : 0u;
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; j++) {
+    const uint32_t l = lj[j];
+    uint32_t pos = 0;
+#pragma unroll
+    for (int q = 1; q <= kMaxLen; q++) pos = l == (uint32_t)q ? tpos[q] : pos;
+#pragma unroll
+    for (int jj = 0; jj < j; jj++) pos += lj[jj] == l ? 1u : 0u;
+    if (l) order[pos] = (uint16_t)(lo + (uint32_t)kPer * t + j);
   }
   __syncthreads();
-  canonical_codes(len, first, enc, part);
-  __syncthreads();
-  for (int s = t; s < kNsym; s += kBookThreads) {
-    const uint32_t e = enc[s], l = e >> 16;
-    if (l) order[base[l] + (e & 0xFFFFu) - first[l]] = (uint16_t)s;
-  }
-  __syncthreads();
-  // every 12-bit prefix -> the one code that starts it (0 when none does)
-  for (int i = t; i < kTable; i += kBookThreads) {
-    uint32_t e = 0;
+  // table entries 16t .. 16t + 15: entry i holds the code whose range of
+  // 12-bit prefixes covers it (ranges of a complete code tile the table)
+  uint32_t ev[kPer / 2];
+#pragma unroll
+  for (int j = 0; j < kPer / 2; j++) ev[j] = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; j++) {
+    const uint32_t i = (uint32_t)kPer * t + j;
+    uint32_t L = 0, at = 0;
+#pragma unroll
     for (int l = 1; l <= kMaxLen; l++) {
-      const uint32_t p = (uint32_t)i >> (kMaxLen - l);
-      if (p - first[l] < cnt[l]) {
-        e = order[base[l] + p - first[l]] | (uint32_t)l << 12;
-        break;
-      }
+      const bool in = i >= tlo[l] && i < thi[l];
+      L = in ? (uint32_t)l : L;
+      at = in ? tbase[l] + (i >> (kMaxLen - l)) - tfirst[l] : at;
     }
-    lut[i] = (uint16_t)e;
+    const uint32_t e = L ? (uint32_t)order[at] | L << 12 : 0u;
+    ev[j >> 1] |= e << (16 * (j & 1));
   }
+  uint4* dst = reinterpret_cast<uint4*>(lut + (size_t)kPer * t);
+  dst[0] = make_uint4(ev[0], ev[1], ev[2], ev[3]);
+  dst[1] = make_uint4(ev[4], ev[5], ev[6], ev[7]);
 }
 
 // Chunks [128 blockIdx.x, 128 blockIdx.x + 128) of segment blockIdx.y.
@@ -997,7 +1057,7 @@ ec_status decode_impl(const uint8_t* d_books, uint64_t book_bytes, const uint32_
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Ws w = ws_of(d_work, nseg);
   if (n == 0) hipLaunchKernelGGL(huff_clear, dim3(1), dim3(kThreads), 0, s, w, 0u);
-  hipLaunchKernelGGL(huff_dec_book, dim3(nseg), dim3(kBookThreads), 0, s, d_books, book_bytes,
+  hipLaunchKernelGGL(huff_dec_book, dim3(nseg), dim3(kDecBookThreads), 0, s, d_books, book_bytes,
                      d_chunk_off, n, w, n == 0 ? 1 : 0);
   if (n) {
     const uint32_t nch = num_chunks(n);
@@ -1039,7 +1099,7 @@ hipError_t launch_seg_luts(const uint8_t* books, const uint32_t* zero_word, uint
   w.valid = valid;
   w.enc = enc;
   w.lut = lut;
-  hipLaunchKernelGGL(huff_dec_book, dim3(nseg), dim3(kBookThreads), 0, s, books,
+  hipLaunchKernelGGL(huff_dec_book, dim3(nseg), dim3(kDecBookThreads), 0, s, books,
                      (uint64_t)kBookStride, zero_word, (uint64_t)1, w, 0);
   return hipGetLastError();
 }
