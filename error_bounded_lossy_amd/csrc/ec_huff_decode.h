@@ -68,19 +68,24 @@ __device__ __forceinline__ bool decode_chunk(const uint32_t* src, uint32_t nword
 // the word after the bit buffer's next word is loaded together with every
 // table lookup (one LDS wait per symbol), and a refill after the lookup
 // consumes it with selects, so the buffer holds at least 21 bits at every
-// lookup.  Words past the chunk read as zero.  nwords >= 1.
+// lookup.  Words past the chunk read as zero.  nwords >= 1.  A full chunk
+// (256 symbols, all but a segment's last) runs without per-symbol bounds;
+// the bits consumed are counted once at the end (32 per word inserted, less
+// what the buffer still holds), and an entry with no code is found as the
+// smallest entry seen (every code's entry is at least 1 << 12).
 // Groups of 32 symbols go to sink(g, pk, n), packed as 16-bit halves of pk[16].
-template <typename Sink>
-__device__ __forceinline__ bool decode_chunk_lds_sink(const uint32_t* src, uint32_t nwords,
+template <bool kFull, typename Sink>
+__device__ __forceinline__ bool decode_chunk_lds_body(const uint32_t* src, uint32_t nwords,
                                                       uint32_t rem, const uint16_t* lut,
                                                       Sink&& sink) {
   const uint32_t last = nwords - 1;
+  const uint32_t cnt = kFull ? 256u : rem;
   uint64_t bitbuf = (uint64_t)src[0] << 32;
-  uint32_t have = 32, used = 0;
-  uint32_t p = 1;  // index of wq, the next word to insert
+  uint32_t have = 32;
+  uint32_t p = 1;  // index of wq, the next word to insert (words inserted so far)
   uint32_t wq = nwords > 1 ? src[1] : 0u;
-  bool bad = false;
-  for (uint32_t g = 0; g < rem; g += 32) {
+  uint32_t mn = 0xFFFFu;
+  for (uint32_t g = 0; g < cnt; g += 32) {
     uint32_t pk[16];
 #pragma unroll
     for (int k = 0; k < 16; k++) pk[k] = 0;
@@ -88,12 +93,11 @@ __device__ __forceinline__ bool decode_chunk_lds_sink(const uint32_t* src, uint3
     for (int k = 0; k < 32; k++) {
       const uint32_t wn_raw = src[min(p + 1, last)];
       const uint32_t ent = lut[bitbuf >> 52];
-      const bool act = g + k < rem;
+      const bool act = kFull || g + k < cnt;
       const uint32_t l = act ? ent >> 12 : 0u;
-      bad |= act && l == 0;
+      mn = act ? min(mn, ent) : mn;
       bitbuf <<= l;
       have -= l;
-      used += l;
       pk[k >> 1] |= (ent & 0xFFFu) << (16 * (k & 1));
       const bool rf = have <= 32;
       const uint32_t wn = p + 1 <= last ? wn_raw : 0u;
@@ -102,9 +106,18 @@ __device__ __forceinline__ bool decode_chunk_lds_sink(const uint32_t* src, uint3
       wq = rf ? wn : wq;
       p += rf ? 1u : 0u;
     }
-    sink(g, pk, min(rem - g, 32u));
+    sink(g, pk, min(cnt - g, 32u));
   }
-  return !(bad || used > 32 * nwords || used + 32 <= 32 * nwords || bitbuf != 0);
+  const uint32_t used = 32 * p - have;
+  return !(mn < (1u << 12) || used > 32 * nwords || used + 32 <= 32 * nwords || bitbuf != 0);
+}
+
+template <typename Sink>
+__device__ __forceinline__ bool decode_chunk_lds_sink(const uint32_t* src, uint32_t nwords,
+                                                      uint32_t rem, const uint16_t* lut,
+                                                      Sink&& sink) {
+  return rem == 256 ? decode_chunk_lds_body<true>(src, nwords, rem, lut, sink)
+                    : decode_chunk_lds_body<false>(src, nwords, rem, lut, sink);
 }
 
 __device__ __forceinline__ bool decode_chunk_lds(const uint32_t* src, uint32_t nwords,
