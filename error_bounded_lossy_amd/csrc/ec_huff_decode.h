@@ -11,21 +11,15 @@
 namespace ec {
 namespace hd {
 
-// Decode one chunk of `rem` symbols from its nwords words at src (LDS or
-// global memory), handing every group of 8 symbols (packed as 16-bit halves
-// of pk[4]; the group's first symbol index g, n of them valid) to
-// sink(g, pk, n).  The bits are read as if zero words followed the chunk;
-// whether it really ends in its last word is decided from the bits consumed.
-// Returns false if the chunk is malformed.
-template <typename Sink>
-__device__ __forceinline__ bool decode_chunk_sink(const uint32_t* src, uint32_t nwords,
+template <bool kFull, typename Sink>
+__device__ __forceinline__ bool decode_chunk_body(const uint32_t* src, uint32_t nwords,
                                                   uint32_t rem, const uint16_t* lut, Sink&& sink) {
   // two words are loaded ahead of the bit buffer, so a refill never waits
+  const uint32_t cnt = kFull ? 256u : rem;
   uint32_t q0 = nwords > 0 ? src[0] : 0u, q1 = nwords > 1 ? src[1] : 0u, p = 2;
   uint64_t bitbuf = 0;
-  uint32_t have = 0, used = 0;
-  bool bad = false;
-  for (uint32_t g = 0; g < rem; g += 8) {
+  uint32_t have = 0, mn = 0xFFFFu;
+  for (uint32_t g = 0; g < cnt; g += 8) {
     uint32_t pk[4] = {0, 0, 0, 0};
 #pragma unroll
     for (int k = 0; k < 8; k++) {
@@ -37,19 +31,34 @@ __device__ __forceinline__ bool decode_chunk_sink(const uint32_t* src, uint32_t 
         p++;
       }
       const uint32_t ent = lut[bitbuf >> 52];
-      const bool act = g + k < rem;
+      const bool act = kFull || g + k < cnt;
       const uint32_t l = act ? ent >> 12 : 0u;
-      bad |= act && l == 0;
+      mn = act ? min(mn, ent) : mn;
       bitbuf <<= l;
       have -= l;
-      used += l;
       pk[k >> 1] |= (ent & 0xFFFu) << (16 * (k & 1));
     }
-    sink(g, pk, min(rem - g, 8u));
+    sink(g, pk, min(cnt - g, 8u));
   }
-  // every consumed bit lies in the chunk, the chunk's last word holds some of
-  // them, and the bits after the last code are zero
-  return !(bad || used > 32 * nwords || used + 32 <= 32 * nwords || bitbuf != 0);
+  // no entry without a code, every consumed bit lies in the chunk (the bits
+  // inserted, 32 per word, less what the buffer holds), the chunk's last word
+  // holds some of them, and the bits after the last code are zero
+  const uint32_t used = 32 * (p - 2) - have;
+  return !(mn < (1u << 12) || used > 32 * nwords || used + 32 <= 32 * nwords || bitbuf != 0);
+}
+
+// Decode one chunk of `rem` symbols from its nwords words at src (LDS or
+// global memory), handing every group of 8 symbols (packed as 16-bit halves
+// of pk[4]; the group's first symbol index g, n of them valid) to
+// sink(g, pk, n).  The bits are read as if zero words followed the chunk;
+// whether it really ends in its last word is decided from the bits consumed.
+// Returns false if the chunk is malformed.  A full chunk (256 symbols) runs
+// without per-symbol bounds.
+template <typename Sink>
+__device__ __forceinline__ bool decode_chunk_sink(const uint32_t* src, uint32_t nwords,
+                                                  uint32_t rem, const uint16_t* lut, Sink&& sink) {
+  return rem == 256 ? decode_chunk_body<true>(src, nwords, rem, lut, sink)
+                    : decode_chunk_body<false>(src, nwords, rem, lut, sink);
 }
 
 // The same, writing the symbols to out[0, rem).
