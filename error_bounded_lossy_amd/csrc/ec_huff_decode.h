@@ -53,12 +53,13 @@ __device__ __forceinline__ bool decode_chunk_body(const uint32_t* src, uint32_t 
 // sink(g, pk, n).  The bits are read as if zero words followed the chunk;
 // whether it really ends in its last word is decided from the bits consumed.
 // Returns false if the chunk is malformed.  A full chunk (256 symbols) runs
-// without per-symbol bounds.
+// without per-symbol bounds when split is set (as for decode_chunk_lds_sink).
 template <typename Sink>
 __device__ __forceinline__ bool decode_chunk_sink(const uint32_t* src, uint32_t nwords,
-                                                  uint32_t rem, const uint16_t* lut, Sink&& sink) {
-  return rem == 256 ? decode_chunk_body<true>(src, nwords, rem, lut, sink)
-                    : decode_chunk_body<false>(src, nwords, rem, lut, sink);
+                                                  uint32_t rem, const uint16_t* lut, Sink&& sink,
+                                                  bool split = true) {
+  return split && rem == 256 ? decode_chunk_body<true>(src, nwords, rem, lut, sink)
+                             : decode_chunk_body<false>(src, nwords, rem, lut, sink);
 }
 
 // The same, writing the symbols to out[0, rem).
@@ -121,12 +122,15 @@ __device__ __forceinline__ bool decode_chunk_lds_body(const uint32_t* src, uint3
   return !(mn < (1u << 12) || used > 32 * nwords || used + 32 <= 32 * nwords || bitbuf != 0);
 }
 
+// split: full chunks take the loop without bounds.  Where the lanes of a wave
+// decode the chunks of one record (the last of which is usually partial),
+// the two loops would run one after the other: there split is false.
 template <typename Sink>
 __device__ __forceinline__ bool decode_chunk_lds_sink(const uint32_t* src, uint32_t nwords,
                                                       uint32_t rem, const uint16_t* lut,
-                                                      Sink&& sink) {
-  return rem == 256 ? decode_chunk_lds_body<true>(src, nwords, rem, lut, sink)
-                    : decode_chunk_lds_body<false>(src, nwords, rem, lut, sink);
+                                                      Sink&& sink, bool split = true) {
+  return split && rem == 256 ? decode_chunk_lds_body<true>(src, nwords, rem, lut, sink)
+                             : decode_chunk_lds_body<false>(src, nwords, rem, lut, sink);
 }
 
 __device__ __forceinline__ bool decode_chunk_lds(const uint32_t* src, uint32_t nwords,

@@ -3677,10 +3677,12 @@ __global__ void __launch_bounds__(64) ec_decode_huff(const uint8_t* __restrict__
     };
     if (!bad && staged) {
       bad = !hd::decode_chunk_lds_sink(s_words + w0, w1 - w0, rem, s_lut,
-                                       [&](uint32_t g, const uint32_t (&pk)[16], uint32_t cnt) { put(g, pk, cnt); });
+                                       [&](uint32_t g, const uint32_t (&pk)[16], uint32_t cnt) { put(g, pk, cnt); },
+                                       false);
     } else if (!bad) {
       bad = !hd::decode_chunk_sink(words + w0, w1 - w0, rem, s_lut,
-                                   [&](uint32_t g, const uint32_t (&pk)[4], uint32_t cnt) { put(g, pk, cnt); });
+                                   [&](uint32_t g, const uint32_t (&pk)[4], uint32_t cnt) { put(g, pk, cnt); },
+                                   false);
     }
   }
   const uint32_t* opos = reinterpret_cast<const uint32_t*>(tl.rec + tl.off_opos);
