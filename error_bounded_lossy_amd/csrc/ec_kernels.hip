@@ -3580,8 +3580,20 @@ __global__ void __launch_bounds__(kThreads) ec_hbook_copy(DecArgs a) {
     src = a.in + sh.seg_off + at;
     avail = min(sh.seg_bytes - at, (uint64_t)kBookStride);
   }
-  for (uint32_t i = lane; i < kBookStride; i += 64)
-    bk[i] = i < avail ? src[i] : (uint8_t)(i == 0 && avail == 0 ? 1 : 0);
+  // every byte load of the lane in flight before the first store (a loop of
+  // load-store pairs waited for each load in turn)
+  constexpr uint32_t kPer = (kBookStride + 63) / 64;
+  uint8_t v[kPer];
+#pragma unroll
+  for (uint32_t q = 0; q < kPer; q++) {
+    const uint32_t i = 64 * q + lane;
+    v[q] = i < avail ? src[i] : (uint8_t)(i == 0 && avail == 0 ? 1 : 0);
+  }
+#pragma unroll
+  for (uint32_t q = 0; q < kPer; q++) {
+    const uint32_t i = 64 * q + lane;
+    if (i < kBookStride) bk[i] = v[q];
+  }
 }
 
 // One wave per Huffman tile: lane c decodes chunk c of E (at most 64 chunks
