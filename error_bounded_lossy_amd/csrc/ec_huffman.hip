@@ -764,29 +764,41 @@ __global__ void __launch_bounds__(kThreads) huff_write(const uint16_t* __restric
 // report: set the status word for a bad codebook (with no chunks to decode);
 // else workgroup 0 zeroes the status word, and the decode kernel, which runs
 // after this one, reports the segments whose codebook is not valid.
-// Decode table of segment blockIdx.x, 256 threads: thread t reads the lengths
-// of symbols lo + 16t .. lo + 16t + 15 (eight codebook bytes, all loads
-// issued together), counts them per length in 16-bit fields (two lengths per
-// word), and the workgroup's prefix of those counts gives every symbol its
-// rank among the codes of its length, i.e. its canonical code (RFC 1951
-// section 3.2.2).  Symbols go to LDS in code order; then thread t fills table
-// entries 16t .. 16t + 15, each from the length whose code range covers it.
-// The codebook is validated as before: lengths up to 12, the first and last
-// symbol of its range used, the padding nibble zero, a complete code.
-constexpr int kDecBookThreads = 256;
+// Decode table of segment blockIdx.x, 1024 threads: thread t reads the
+// lengths of symbols lo + 4t .. lo + 4t + 3 (two codebook bytes, loaded
+// together with the range header), counts them per length in 16-bit fields
+// (two lengths per word), and a prefix of those counts over the workgroup
+// gives every symbol its rank among the codes of its length, i.e. its
+// canonical code (RFC 1951 section 3.2.2).  Each wave forms the prefix over
+// the waves' totals itself, so the totals and the per-length code ranges
+// are wave-uniform.  Symbols go to LDS in code order; then thread t fills
+// table entries 4t .. 4t + 3.  The codebook is validated as before: lengths
+// up to 12, the first and last symbol of its range used, the padding nibble
+// zero, a complete code.
+constexpr int kDecBookThreads = 1024;
 __global__ void __launch_bounds__(kDecBookThreads) huff_dec_book(const uint8_t* __restrict__ books,
                                                               uint64_t book_bytes,
                                                               const uint32_t* __restrict__ chunk_off,
                                                               uint64_t n, Ws w, int report) {
-  constexpr int kPer = kTable / kDecBookThreads;  // 16 symbols and 16 table entries per thread
+  constexpr int kPer = kTable / kDecBookThreads;  // 4 symbols and 4 table entries per thread
   constexpr int kWaves = kDecBookThreads / 64;
+  static_assert(kPer == 4 && kWaves <= 64, "one 8-byte table store per thread");
   const uint32_t seg = blockIdx.x;
   const uint8_t* book = books + (size_t)seg * kBookStride;
   uint16_t* lut = w.lut + (size_t)seg * kTable;
   __shared__ uint16_t order[kTable];
   __shared__ uint32_t part[kWaves][8];  // per wave: six count words, Kraft sum, flags
-  const uint32_t t = threadIdx.x, lane = t & 63u, wv = t >> 6;
+  const uint32_t t = threadIdx.x, lane = t & 63u;
+  const uint32_t wv = (uint32_t)__builtin_amdgcn_readfirstlane((int)(t >> 6));
   if (t == 0 && !report && seg == 0) w.status[0] = 0;
+  // this thread's two length bytes, issued with the header loads; bytes past
+  // the codebook's range are dropped once the header is known
+  uint8_t raw[kPer / 2];
+#pragma unroll
+  for (int j = 0; j < kPer / 2; j++) {
+    const uint64_t b = 4u + (uint64_t)kPer / 2 * t + j;
+    raw[j] = b < book_bytes ? book[b] : (uint8_t)0;
+  }
   bool bad = false;
   uint32_t lo = 1, hi = 0;
   if (book_bytes < 4) {
@@ -801,23 +813,20 @@ __global__ void __launch_bounds__(kDecBookThreads) huff_dec_book(const uint8_t* 
   if (empty && n > 0) bad = true;
   if (seg == 0 && chunk_off[0] != 0) bad = true;
   const uint32_t nb = bad || empty ? 0u : hi - lo + 1, nbytes = (nb + 1) / 2;
-  // lengths of this thread's symbols, 4 bits each
-  uint8_t by[kPer / 2];
-#pragma unroll
-  for (int j = 0; j < kPer / 2; j++) {
-    const uint32_t b = (uint32_t)kPer / 2 * t + j;
-    by[j] = b < nbytes ? book[4 + b] : (uint8_t)0;
-  }
+  uint32_t lj[kPer];  // lengths of this thread's symbols, 0 past the range
   uint32_t cw[6] = {0, 0, 0, 0, 0, 0};  // count of length l in field (l-1) & 1 of word (l-1) >> 1
   uint32_t kr = 0;
 #pragma unroll
   for (int j = 0; j < kPer; j++) {
     const uint32_t k = (uint32_t)kPer * t + j;
-    const uint32_t l = (by[j >> 1] >> (4 * (j & 1))) & 15u;
+    const uint32_t by = (uint32_t)kPer / 2 * t + (j >> 1) < nbytes ? raw[j >> 1] : 0u;
+    const uint32_t l = (by >> (4 * (j & 1))) & 15u;
+    lj[j] = 0;
     if (k < nb && l) {
       if (l > (uint32_t)kMaxLen) {
         bad = true;
       } else {
+        lj[j] = l;
         cw[(l - 1) >> 1] += 1u << (16 * ((l - 1) & 1));
         kr += 1u << (kMaxLen - l);
       }
@@ -825,7 +834,7 @@ __global__ void __launch_bounds__(kDecBookThreads) huff_dec_book(const uint8_t* 
     if (k >= nb && l) bad = true;  // the padding nibble
     if (nb && (k == 0 || k == nb - 1) && !l) bad = true;  // lo and hi are used
   }
-  // prefix of the counts over the workgroup
+  // prefix of the counts within the wave, then over the waves' totals
   uint32_t inc[6];
 #pragma unroll
   for (int q = 0; q < 6; q++) inc[q] = wave_incl(cw[q]);
@@ -838,17 +847,20 @@ __global__ void __launch_bounds__(kDecBookThreads) huff_dec_book(const uint8_t* 
     part[wv][7] = badw != 0;
   }
   __syncthreads();
-  uint32_t before[6] = {0, 0, 0, 0, 0, 0}, tot[6] = {0, 0, 0, 0, 0, 0}, kraft = 0, anybad = 0;
+  uint32_t before[6], tot[6];  // wave-uniform: codes of each length in earlier waves, in all
+  uint32_t kraft, anybad;
+  {
+    uint32_t x[8];
 #pragma unroll
-  for (int v = 0; v < kWaves; v++) {
+    for (int q = 0; q < 8; q++) x[q] = lane < (uint32_t)kWaves ? part[lane][q] : 0u;
 #pragma unroll
     for (int q = 0; q < 6; q++) {
-      const uint32_t x = part[v][q];
-      before[q] += (uint32_t)v < wv ? x : 0u;
-      tot[q] += x;
+      const uint32_t c = wave_incl(x[q]);
+      tot[q] = (uint32_t)__builtin_amdgcn_readlane((int)c, 63);
+      before[q] = wv ? (uint32_t)__builtin_amdgcn_readlane((int)c, (int)wv - 1) : 0u;
     }
-    kraft += part[v][6];
-    anybad |= part[v][7];
+    kraft = wave_sum(x[6]);
+    anybad = __ballot(x[7] != 0) != 0;
   }
   auto field = [](const uint32_t (&a)[6], uint32_t l) {  // the count of length l
     return (a[(l - 1) >> 1] >> (16 * ((l - 1) & 1))) & 0xFFFFu;
@@ -867,38 +879,28 @@ __global__ void __launch_bounds__(kDecBookThreads) huff_dec_book(const uint8_t* 
     return;
   }
   if (t == 0) w.valid[seg] = 1;
-  // per length l (registers: every index below is a constant): the first
-  // code, the table range [lo_l, hi_l) its codes cover, the code-order index
-  // of its first code, and where this thread's first code of length l goes
-  uint32_t tlo[kMaxLen + 1], thi[kMaxLen + 1], tfirst[kMaxLen + 1], tbase[kMaxLen + 1],
-      tpos[kMaxLen + 1];
-  uint32_t ex[6];  // codes of each length before this thread's (earlier waves and lanes)
-#pragma unroll
-  for (int q = 0; q < 6; q++) ex[q] = before[q] + inc[q] - cw[q];
+  // per length l (every index below is a constant): the table range
+  // [lo_l, hi_l) its codes cover, the code-order index of its first code
+  // less the code itself, and where this thread's first code of length l goes
+  uint32_t tlo[kMaxLen + 1], thi[kMaxLen + 1], tadj[kMaxLen + 1], tpos[kMaxLen + 1];
   {
     uint32_t code = 0, idx = 0;
 #pragma unroll
     for (int l = 1; l <= kMaxLen; l++) {
       const uint32_t c = field(tot, (uint32_t)l);
       if (l > 1) code = (code + field(tot, (uint32_t)l - 1)) << 1;
-      tfirst[l] = code;
-      tbase[l] = idx;
+      tadj[l] = idx - code;
       tlo[l] = code << (kMaxLen - l);
       thi[l] = (code + c) << (kMaxLen - l);
-      tpos[l] = idx + ((ex[(l - 1) >> 1] >> (16 * ((l - 1) & 1))) & 0xFFFFu);
+      const uint32_t q = (uint32_t)(l - 1) >> 1, sh = 16 * ((uint32_t)(l - 1) & 1);
+      // codes of length l before this thread's: earlier waves and lanes
+      tpos[l] = idx + ((before[q] >> sh) & 0xFFFFu) + (((inc[q] - cw[q]) >> sh) & 0xFFFFu);
       idx += c;
     }
   }
   // this thread's symbols in code order: a symbol's rank among the codes of
-  // its length is the workgroup's count before this thread plus the
-  // thread's own earlier symbols of that length
-  uint32_t lj[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; j++) {
-    const uint32_t k = (uint32_t)kPer * t + j;
-    const uint32_t l = (by[j >> 1] >> (4 * (j & 1))) & 15u;
-    lj[j] = k < nb ? l : 0u;
-  }
+  // its length is the count before this thread plus the thread's own
+  // earlier symbols of that length
 #pragma unroll
   for (int j = 0; j < kPer; j++) {
     const uint32_t l = lj[j];
@@ -910,27 +912,34 @@ __global__ void __launch_bounds__(kDecBookThreads) huff_dec_book(const uint8_t* 
     if (l) order[pos] = (uint16_t)(lo + (uint32_t)kPer * t + j);
   }
   __syncthreads();
-  // table entries 16t .. 16t + 15: entry i holds the code whose range of
-  // 12-bit prefixes covers it (ranges of a complete code tile the table)
-  uint32_t ev[kPer / 2];
+  // table entries 4t .. 4t + 3: entry i holds the code whose range of 12-bit
+  // prefixes covers it (ranges of a complete code tile the table in order of
+  // length).  A code of length 10 or less covers whole aligned blocks of
+  // four, so the block's first entry fixes the rest unless it lies in the
+  // ranges of lengths 11 and 12, which the other three entries look up.
+  const uint32_t i0 = (uint32_t)kPer * t;
+  uint32_t L0 = 0, at0 = 0;
 #pragma unroll
-  for (int j = 0; j < kPer / 2; j++) ev[j] = 0;
+  for (int l = 1; l <= kMaxLen; l++) {
+    const bool in = i0 >= tlo[l] && i0 < thi[l];
+    L0 = in ? (uint32_t)l : L0;
+    at0 = in ? tadj[l] + (i0 >> (kMaxLen - l)) : at0;
+  }
+  uint32_t ev[kPer];
+  ev[0] = L0 ? (uint32_t)order[at0] | L0 << 12 : 0u;
 #pragma unroll
-  for (int j = 0; j < kPer; j++) {
-    const uint32_t i = (uint32_t)kPer * t + j;
-    uint32_t L = 0, at = 0;
+  for (int j = 1; j < kPer; j++) {
+    const uint32_t i = i0 + j;
+    uint32_t L = L0, at = at0;
 #pragma unroll
-    for (int l = 1; l <= kMaxLen; l++) {
+    for (int l = kMaxLen - 1; l <= kMaxLen; l++) {
       const bool in = i >= tlo[l] && i < thi[l];
       L = in ? (uint32_t)l : L;
-      at = in ? tbase[l] + (i >> (kMaxLen - l)) - tfirst[l] : at;
+      at = in ? tadj[l] + (i >> (kMaxLen - l)) : at;
     }
-    const uint32_t e = L ? (uint32_t)order[at] | L << 12 : 0u;
-    ev[j >> 1] |= e << (16 * (j & 1));
+    ev[j] = L ? (uint32_t)order[at] | L << 12 : 0u;
   }
-  uint4* dst = reinterpret_cast<uint4*>(lut + (size_t)kPer * t);
-  dst[0] = make_uint4(ev[0], ev[1], ev[2], ev[3]);
-  dst[1] = make_uint4(ev[4], ev[5], ev[6], ev[7]);
+  *reinterpret_cast<uint2*>(lut + i0) = make_uint2(ev[0] | ev[1] << 16, ev[2] | ev[3] << 16);
 }
 
 // Chunks [128 blockIdx.x, 128 blockIdx.x + 128) of segment blockIdx.y.
