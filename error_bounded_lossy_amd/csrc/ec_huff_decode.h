@@ -74,51 +74,53 @@ __device__ __forceinline__ bool decode_chunk(const uint32_t* src, uint32_t nword
   });
 }
 
-// The same for a chunk staged in LDS, without branches in the symbol loop:
-// the word after the bit buffer's next word is loaded together with every
-// table lookup (one LDS wait per symbol), and a refill after the lookup
-// consumes it with selects, so the buffer holds at least 21 bits at every
-// lookup.  Words past the chunk read as zero.  nwords >= 1.  A full chunk
-// (256 symbols, all but a segment's last) runs without per-symbol bounds;
-// the bits consumed are counted once at the end (32 per word inserted, less
-// what the buffer still holds), and an entry with no code is found as the
-// smallest entry seen (every code's entry is at least 1 << 12).
-// Groups of 32 symbols go to sink(g, pk, n), packed as 16-bit halves of pk[16].
+// The same for a chunk staged in LDS, without branches in the symbol loop.
+// The 64-bit buffer holds the chunk's bits [used, 32 p) at its top and zeros
+// below; two codes (at most 24 bits) are decoded per refill, which inserts
+// the next word wq when 32 or fewer bits remain, so every lookup sees at
+// least 12 valid bits and a refill leaves at least 33.  The word after wq is
+// loaded at the start of each pair and is needed only at its end.  Words
+// past the chunk read as zero.  nwords >= 1.  A full chunk (256 symbols, all
+// but a segment's last) runs without per-symbol bounds; an entry with no
+// code is found as the smallest entry seen (every code's entry is at least
+// 1 << 12).  Groups of 32 symbols go to sink(g, pk, n), packed as 16-bit
+// halves of pk[16].
 template <bool kFull, typename Sink>
 __device__ __forceinline__ bool decode_chunk_lds_body(const uint32_t* src, uint32_t nwords,
                                                       uint32_t rem, const uint16_t* lut,
                                                       Sink&& sink) {
   const uint32_t last = nwords - 1;
   const uint32_t cnt = kFull ? 256u : rem;
-  uint64_t bitbuf = (uint64_t)src[0] << 32;
-  uint32_t have = 32;
-  uint32_t p = 1;  // index of wq, the next word to insert (words inserted so far)
-  uint32_t wq = nwords > 1 ? src[1] : 0u;
+  uint64_t bitbuf = (uint64_t)src[0] << 32 | (nwords > 1 ? src[1] : 0u);
+  uint32_t used = 0;                         // bits consumed
+  uint32_t p = 2;                            // words inserted
+  uint32_t wq = nwords > 2 ? src[2] : 0u;    // the next word to insert
   uint32_t mn = 0xFFFFu;
   for (uint32_t g = 0; g < cnt; g += 32) {
     uint32_t pk[16];
 #pragma unroll
-    for (int k = 0; k < 16; k++) pk[k] = 0;
-#pragma unroll
-    for (int k = 0; k < 32; k++) {
+    for (int k = 0; k < 32; k += 2) {
       const uint32_t wn_raw = src[min(p + 1, last)];
-      const uint32_t ent = lut[bitbuf >> 52];
-      const bool act = kFull || g + k < cnt;
-      const uint32_t l = act ? ent >> 12 : 0u;
-      mn = act ? min(mn, ent) : mn;
-      bitbuf <<= l;
-      have -= l;
-      pk[k >> 1] |= (ent & 0xFFFu) << (16 * (k & 1));
-      const bool rf = have <= 32;
-      const uint32_t wn = p + 1 <= last ? wn_raw : 0u;
-      bitbuf |= rf ? (uint64_t)wq << (32 - have) : 0ull;
-      have += rf ? 32u : 0u;
-      wq = rf ? wn : wq;
+      const uint32_t e1 = lut[bitbuf >> 52];
+      const bool a1 = kFull || g + k < cnt;
+      const uint32_t l1 = a1 ? e1 >> 12 : 0u;
+      bitbuf <<= l1;
+      const uint32_t e2 = lut[bitbuf >> 52];
+      const bool a2 = kFull || g + k + 1 < cnt;
+      const uint32_t l2 = a2 ? e2 >> 12 : 0u;
+      bitbuf <<= l2;
+      mn = min(mn, min(a1 ? e1 : 0xFFFFu, a2 ? e2 : 0xFFFFu));
+      pk[k >> 1] = (e1 | e2 << 16) & 0x0FFF0FFFu;
+      used += l1 + l2;
+      // 32 p - used bits remain; wq goes right below them
+      const uint32_t base = 32 * p - 32;
+      const bool rf = used >= base;
+      bitbuf |= (uint64_t)(rf ? wq : 0u) << ((used - base) & 63u);
+      wq = rf ? (p + 1 <= last ? wn_raw : 0u) : wq;
       p += rf ? 1u : 0u;
     }
     sink(g, pk, min(cnt - g, 32u));
   }
-  const uint32_t used = 32 * p - have;
   return !(mn < (1u << 12) || used > 32 * nwords || used + 32 <= 32 * nwords || bitbuf != 0);
 }
 
