@@ -949,18 +949,51 @@ __global__ void __launch_bounds__(kDecChunks) huff_decode(const uint32_t* __rest
                                                           uint64_t n, uint32_t nch, Ws w,
                                                           uint16_t* __restrict__ sym0) {
   __shared__ uint16_t lut[kTable];
-  __shared__ uint32_t stage[kStageWords];
-  __shared__ uint32_t s_lo, s_hi;
+  __shared__ __align__(16) uint32_t stage[kStageWords];
   const uint32_t t = threadIdx.x, seg = blockIdx.y;
   const uint32_t c0 = blockIdx.x * kDecChunks, c = c0 + t;
   const uint32_t cend = min(c0 + kDecChunks, nch);
   const uint32_t* chunk_off = chunk_off0 + (size_t)seg * nch;
   uint16_t* sym = sym0 + (uint64_t)seg * n;
   const bool vec = (n & 7) == 0;  // 16-byte stores when segments start 16-byte aligned
+  // the group's words [glo, ghi) from its bounding offsets; they go through
+  // LDS from the 16-byte boundary at or below glo when they fit (the usual
+  // case), loaded together with the table and the chunks' own offsets.  The
+  // range is checked here only to keep the loads inside the buffer; every
+  // chunk is validated below before anything is decoded.
+  const uint32_t glo = chunk_off[c0], ghi = chunk_off[cend];
+  const uint32_t q0 = glo >> 2, q1 = ghi >> 2;  // whole 16-byte quads [q0, q1), then a tail
+  const bool staged = glo <= ghi && (uint64_t)ghi <= words_cap && ghi - 4 * q0 <= (uint32_t)kStageWords;
   {
     const uint4* src = reinterpret_cast<const uint4*>(w.lut + (size_t)seg * kTable);
     uint4* dst = reinterpret_cast<uint4*>(lut);
-    for (int i = t; i < kTable * 2 / 16; i += kDecChunks) dst[i] = src[i];
+    uint4 v[kTable * 2 / 16 / kDecChunks];
+#pragma unroll
+    for (int j = 0; j < kTable * 2 / 16 / kDecChunks; j++) v[j] = src[j * kDecChunks + t];
+#pragma unroll
+    for (int j = 0; j < kTable * 2 / 16 / kDecChunks; j++) dst[j * kDecChunks + t] = v[j];
+  }
+  if (staged) {
+    if (((uintptr_t)words & 15u) == 0) {
+      constexpr int kQ = kStageWords / 4 / kDecChunks;  // quads per thread, all in flight
+      const uint4* wq = reinterpret_cast<const uint4*>(words);
+      uint4* sq = reinterpret_cast<uint4*>(stage);
+      uint4 v[kQ];
+#pragma unroll
+      for (int j = 0; j < kQ; j++) {
+        const uint32_t i = q0 + j * kDecChunks + t;
+        v[j] = i < q1 ? wq[i] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < kQ; j++) {
+        const uint32_t i = q0 + j * kDecChunks + t;
+        if (i < q1) sq[i - q0] = v[j];
+      }
+      const uint32_t i = 4 * q1 + t;
+      if (t < 3 && i < ghi) stage[i - 4 * q0] = words[i];
+    } else {
+      for (uint32_t i = 4 * q0 + t; i < ghi; i += kDecChunks) stage[i - 4 * q0] = words[i];
+    }
   }
   bool ok = w.valid[seg] != 0;
   uint32_t a = 0, b = 0;
@@ -970,38 +1003,15 @@ __global__ void __launch_bounds__(kDecChunks) huff_decode(const uint32_t* __rest
     ok = ok && a <= b && b - a <= (uint32_t)kChunkWords && (uint64_t)b <= words_cap;
     if (seg == 0 && c == 0) ok = ok && a == 0;
   }
-  if (c == c0) s_lo = a;
-  if (c + 1 == cend) s_hi = b;
   if (!__syncthreads_and(ok)) {
     if (t == 0) status_or(w.status, kStCorrupt);
     return;
   }
-  // consecutive valid chunks: the group's words are [glo, ghi), at most
-  // kDecChunks * 96; they go through LDS when they fit (the usual case)
-  const uint32_t glo = s_lo, ghi = s_hi;
-  const bool staged = ghi - glo <= (uint32_t)kStageWords;
-  if (staged) {  // eight loads per thread in flight before their stores
-    const uint32_t nw = ghi - glo;
-    for (uint32_t i0 = 0; i0 < nw; i0 += 8 * kDecChunks) {
-      uint32_t v[8];
-#pragma unroll
-      for (uint32_t q = 0; q < 8; q++) {
-        const uint32_t i = i0 + q * kDecChunks + t;
-        v[q] = i < nw ? words[glo + i] : 0u;
-      }
-#pragma unroll
-      for (uint32_t q = 0; q < 8; q++) {
-        const uint32_t i = i0 + q * kDecChunks + t;
-        if (i < nw) stage[i] = v[q];
-      }
-    }
-  }
-  __syncthreads();
   if (c >= cend) return;
   const uint64_t sbase = (uint64_t)c * kChunk;
   const uint32_t rem = (uint32_t)min((uint64_t)kChunk, n - sbase);
   const bool good = b == a ? false
-                    : staged ? decode_chunk_lds(stage + (a - glo), b - a, rem, lut, sym + sbase, vec)
+                    : staged ? decode_chunk_lds(stage + (a - 4 * q0), b - a, rem, lut, sym + sbase, vec)
                              : decode_chunk(words + a, b - a, rem, lut, sym + sbase, vec);
   if (!good) status_or(w.status, kStCorrupt);
 }
