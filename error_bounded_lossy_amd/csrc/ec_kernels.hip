@@ -3712,6 +3712,174 @@ __global__ void __launch_bounds__(64) ec_decode_huff(const uint8_t* __restrict__
   }
 }
 
+// Huffman tiles of D = 64 and 128 (at most 32 chunks each), two per wave:
+// half h decodes the chunks of tile 2 blockIdx.x + h, one per lane, so that
+// every lane decodes and the workgroups (a table and two tiles' words in
+// LDS, about 22 KB) all fit the chip at once.  Two tiles of one segment
+// share the decode table; tiles of two segments take one pass each.
+// Checks, staging and the outlier pass are those of ec_decode_huff, per tile.
+template <int C>
+__global__ void __launch_bounds__(64) ec_decode_huff_pair(const uint8_t* __restrict__ in,
+                                                         float* __restrict__ yout, DecArgs a) {
+  constexpr uint32_t D = 64u * C, kMaxCh = kTileRows * D / 256;
+  static_assert(kMaxCh <= 32, "one chunk per lane of a half-wave");
+  // a record's words are staged in LDS when they average at most 52 per chunk
+  constexpr uint32_t kStage = kMaxCh * 52;
+  __shared__ DecShared sh[2];
+  __shared__ uint16_t s_lut[kHuffTable];
+  __shared__ uint32_t s_words[2][kStage];
+  __shared__ uint8_t s_urow[2][kTileRows];
+  const uint32_t lane = threadIdx.x, h = lane >> 5, hl = lane & 31;
+  const uint32_t t0 = 2 * blockIdx.x;
+  uint32_t act = 0;  // bit q: tile t0 + q is a Huffman tile, decoded here
+#pragma unroll
+  for (uint32_t q = 0; q < 2; q++) {
+    if (t0 + q >= a.sh.ntiles) continue;
+    uint64_t ro;
+    dec_locate(a, in, t0 + q, sh[q], ro);
+    wave_lds_wait();
+    // a Huffman segment's codebook is checked by the segment's first tile
+    if (lane == 0 && sh[q].seg_ok && sh[q].hseg && sh[q].tile == 0) {
+      const uint8_t* bk = a.w.hdbooks + (uint64_t)sh[q].seg * kBookStride;
+      const bool empty = bk[0] == 1 && bk[1] == 0 && bk[2] == 0 && bk[3] == 0;
+      if (!a.w.hvalid[sh[q].seg] && !empty) report_error(a.report, kDevErrCorrupt);
+    }
+    if (sh[q].ok && sh[q].n != 0 && sh[q].tl.mode == 2) act |= 1u << q;  // others: checked elsewhere
+  }
+  act = uniform32(act);
+  if (act == 0) return;
+  // per tile: its record's chunk table and words, outliers, output rows
+  struct TV {
+    const uint32_t* ct;
+    const uint32_t* words;
+    const uint32_t* opos;
+    const uint32_t* oval;
+    float* yt;
+    uint64_t wavail;
+    uint32_t seg, n, nE, nch, nout, total;
+    float s2;
+    bool staged, tbad;
+  };
+  TV tv[2];
+#pragma unroll
+  for (uint32_t q = 0; q < 2; q++) {
+    TV& v = tv[q];
+    v = TV{nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, 0, 0, 0, 0, 0, 0.0f, false, false};
+    if (!((act >> q) & 1u)) continue;
+    const DecTile tl = sh[q].tl;
+    v.seg = sh[q].seg;
+    v.n = sh[q].n;
+    v.nE = tl.U * D;
+    v.nch = tl.nch;
+    v.nout = tl.nout;
+    v.ct = reinterpret_cast<const uint32_t*>(tl.rec + tl.off_ct);
+    v.words = reinterpret_cast<const uint32_t*>(tl.rec + tl.off_w);
+    v.opos = reinterpret_cast<const uint32_t*>(tl.rec + tl.off_opos);
+    v.oval = reinterpret_cast<const uint32_t*>(tl.rec + tl.off_oval);
+    v.yt = yout + ((uint64_t)(v.seg % a.sh.T) * a.sh.B + chunk_row0(a.sh, v.seg / a.sh.T) +
+                   (uint64_t)sh[q].tile * kTileRows) * D;
+    v.wavail = (tl.avail - tl.off_w) / 4;  // words the segment still holds
+    v.s2 = sh[q].eb + sh[q].eb;
+    v.total = v.ct[v.nch];
+    v.staged = v.total <= kStage && (uint64_t)v.total <= v.wavail;
+    v.tbad = (v.nE > 0 && a.w.hvalid[v.seg] == 0) || v.ct[0] != 0;
+  }
+  const bool split = act == 3u && tv[0].seg != tv[1].seg;
+  for (uint32_t pass = 0; pass < (split ? 2u : 1u); pass++) {
+    const uint32_t pm = split ? (1u << pass) : act;  // the tiles of this pass
+    {
+      const uint32_t lseg = (pm & 1u) ? tv[0].seg : tv[1].seg;
+      const uint4* src = reinterpret_cast<const uint4*>(a.w.hlut + (uint64_t)lseg * kHuffTable);
+#pragma unroll
+      for (uint32_t i = 0; i < kHuffTable * 2 / 16 / 64; i++)
+        reinterpret_cast<uint4*>(s_lut)[64 * i + lane] = src[64 * i + lane];
+    }
+#pragma unroll
+    for (uint32_t q = 0; q < 2; q++)
+      if ((pm >> q) & 1u) unique_rows(sh[q].tl.bitmap, s_urow[q]);
+    // both tiles' words into LDS, eight loads per lane and tile in flight
+    const uint32_t tot0 = ((pm & 1u) && tv[0].staged) ? tv[0].total : 0u;
+    const uint32_t tot1 = ((pm & 2u) && tv[1].staged) ? tv[1].total : 0u;
+    for (uint32_t i0 = 0; i0 < max(tot0, tot1); i0 += 8 * 64) {
+      uint32_t v0[8], v1[8];
+#pragma unroll
+      for (uint32_t k = 0; k < 8; k++) {
+        const uint32_t i = i0 + 64 * k + lane;
+        v0[k] = i < tot0 ? tv[0].words[i] : 0u;
+        v1[k] = i < tot1 ? tv[1].words[i] : 0u;
+      }
+#pragma unroll
+      for (uint32_t k = 0; k < 8; k++) {
+        const uint32_t i = i0 + 64 * k + lane;
+        if (i < tot0) s_words[0][i] = v0[k];
+        if (i < tot1) s_words[1][i] = v1[k];
+      }
+    }
+    wave_lds_wait();
+    bool dbad = false;
+    {
+      const TV& v = h ? tv[1] : tv[0];
+      if (((pm >> h) & 1u) && hl < v.nch && !v.tbad) {
+        // every chunk ends exactly in its last word (at most 96 words for 256
+        // codes of at most 12 bits), and the next one starts right after it
+        const uint32_t c = hl, w0 = v.ct[c], w1 = v.ct[c + 1];
+        const uint32_t rem = min(256u, v.nE - 256 * c);
+        dbad = !(w0 < w1 && w1 - w0 <= 96u && w1 <= v.total && (uint64_t)v.total <= v.wavail);
+        const uint8_t* urow = s_urow[h];
+        float* const yt = v.yt;
+        const float s2 = v.s2;
+        // groups of codes of one row (D is a multiple of 32) into their row
+        auto put = [&](uint32_t g, const uint32_t* pk, uint32_t cnt) {
+          const uint32_t e = 256 * c + g;
+          float* y = yt + (uint64_t)urow[e / D] * D + e % D;
+          for (uint32_t k0 = 0; k0 < cnt; k0 += 4) {
+            float f[4];
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+              const uint32_t kk = k0 + k;
+              f[k] = (float)((int)((pk[kk >> 1] >> (16 * (kk & 1))) & 0xFFFFu) - 2047) * s2;
+            }
+            if (k0 + 4 <= cnt) {
+              *reinterpret_cast<float4*>(y + k0) = make_float4(f[0], f[1], f[2], f[3]);
+            } else {
+              for (uint32_t k = 0; k0 + k < cnt; k++) y[k0 + k] = f[k];
+            }
+          }
+        };
+        if (!dbad && v.staged) {
+          dbad = !hd::decode_chunk_lds_sink(s_words[h] + w0, w1 - w0, rem, s_lut,
+                                            [&](uint32_t g, const uint32_t (&pk)[16], uint32_t cnt) { put(g, pk, cnt); },
+                                            false);
+        } else if (!dbad) {
+          dbad = !hd::decode_chunk_sink(v.words + w0, w1 - w0, rem, s_lut,
+                                        [&](uint32_t g, const uint32_t (&pk)[4], uint32_t cnt) { put(g, pk, cnt); },
+                                        false);
+        }
+      }
+    }
+    wait_vm();  // this wave's stores are performed before any rewrite of the same words
+    const uint64_t dbm = __ballot(dbad);
+#pragma unroll
+    for (uint32_t q = 0; q < 2; q++) {
+      if (!((pm >> q) & 1u)) continue;
+      const TV& v = tv[q];
+      bool bad = v.tbad || (q ? (dbm >> 32) : (dbm & 0xFFFFFFFFull)) != 0;
+      for (uint32_t g = lane; g < v.nout; g += 64)
+        bad = bad || v.opos[g] >= v.nE || (g > 0 && v.opos[g - 1] >= v.opos[g]);
+      if (__ballot(bad) != 0) {
+        for (uint32_t i = lane; i < v.n * D; i += 64) v.yt[i] = 0.0f;
+        if (lane == 0) report_error(a.report, kDevErrCorrupt);
+        continue;
+      }
+      for (uint32_t g = lane; g < v.nout; g += 64) {
+        const uint32_t p = v.opos[g];
+        v.yt[(uint64_t)s_urow[q][p / D] * D + p % D] = __uint_as_float(v.oval[g]);
+      }
+    }
+    wave_lds_wait();  // the next pass rewrites the table
+  }
+}
+
 // Rows of a Huffman tile that repeat an earlier row: their first occurrences
 // are decoded (this or an earlier Huffman tile) or stored RAW (re-quantized).
 constexpr uint32_t kRefNone = 0, kRefCopy = 1, kRefRaw = 2, kRefBad = 3;
@@ -4177,11 +4345,11 @@ hipError_t launch_huff_decode(const DecArgs& a, hipStream_t s) {
   const dim3 grid(a.sh.ntiles), block(kThreads);
   switch (a.sh.D) {
     case 64:
-      hipLaunchKernelGGL(ec_decode_huff<1>, grid, dim3(64), 0, s, a.in, a.y, a);
+      hipLaunchKernelGGL(ec_decode_huff_pair<1>, dim3((a.sh.ntiles + 1) / 2), dim3(64), 0, s, a.in, a.y, a);
       hipLaunchKernelGGL(ec_fill_refs<1>, grid, block, 0, s, a.in, a.y, a);
       break;
     case 128:
-      hipLaunchKernelGGL(ec_decode_huff<2>, grid, dim3(64), 0, s, a.in, a.y, a);
+      hipLaunchKernelGGL(ec_decode_huff_pair<2>, dim3((a.sh.ntiles + 1) / 2), dim3(64), 0, s, a.in, a.y, a);
       hipLaunchKernelGGL(ec_fill_refs<2>, grid, block, 0, s, a.in, a.y, a);
       break;
     case 256:
