@@ -2120,13 +2120,38 @@ __global__ void __launch_bounds__(kThreads) ec_hist_tiles(EncArgs a) {
   const TileCoord c = tile_coord(a, ticket);
   if (c.n == 0 || a.w.seg_eb[c.s] == 0) return;
   for (uint32_t i = tid; i < kHuffTable; i += kThreads) h[i] = 0;
-  __syncthreads();
   const uint64_t bm = a.w.tile_bitmap[ticket];
   const uint16_t* sy = a.w.stage_sym + (uint64_t)ticket * kTileRows * D;
-  for (uint32_t i = wv; i < c.n; i += kThreads / 64) {
-    if (!((bm >> i) & 1ull)) continue;
+  // the symbols of the wave's rows (every staged row has them), loaded
+  // eight rows at a time with all their loads in flight
+  constexpr uint32_t kRowsPerWave = kTileRows / (kThreads / 64), kBatch = 8;
+  uint32_t v[kRowsPerWave][C];
 #pragma unroll
-    for (uint32_t j = 0; j < C; j++) atomicAdd(&h[sy[i * D + 64 * j + lane]], 1u);
+  for (uint32_t r = 0; r < kBatch; r++)
+#pragma unroll
+    for (uint32_t j = 0; j < C; j++) {
+      const uint32_t i = wv + (kThreads / 64) * r;
+      v[r][j] = i < c.n ? sy[i * D + 64 * j + lane] : 0u;
+    }
+  __syncthreads();
+#pragma unroll
+  for (uint32_t r0 = 0; r0 < kRowsPerWave; r0 += kBatch) {
+    if (r0 + kBatch < kRowsPerWave) {
+#pragma unroll
+      for (uint32_t r = r0 + kBatch; r < r0 + 2 * kBatch; r++)
+#pragma unroll
+        for (uint32_t j = 0; j < C; j++) {
+          const uint32_t i = wv + (kThreads / 64) * r;
+          v[r][j] = i < c.n ? sy[i * D + 64 * j + lane] : 0u;
+        }
+    }
+#pragma unroll
+    for (uint32_t r = r0; r < r0 + kBatch; r++) {
+      const uint32_t i = wv + (kThreads / 64) * r;
+      if (i < c.n && ((bm >> i) & 1ull))
+#pragma unroll
+        for (uint32_t j = 0; j < C; j++) atomicAdd(&h[v[r][j]], 1u);
+    }
   }
   __syncthreads();
   uint32_t* g = a.w.hhist + (uint64_t)c.s * kHuffTable;
@@ -2134,18 +2159,32 @@ __global__ void __launch_bounds__(kThreads) ec_hist_tiles(EncArgs a) {
     if (h[i]) atomicAdd(&g[i], h[i]);
 }
 
-// Bits of lane L's four symbols E[256 ch + 4L .. + 3] of the tile (0 past nE);
-// with codes (enc: len << 16 | code) also their codes, first code in the high
-// bits of *val.
+// A segment's code table (kHuffTable words) into LDS, every load of a
+// thread in flight before its stores.
+__device__ __forceinline__ void copy_table(uint32_t* dst, const uint32_t* src, uint32_t tid) {
+  constexpr uint32_t kQ = kHuffTable / 4 / kThreads;
+  uint4 v[kQ];
+#pragma unroll
+  for (uint32_t q = 0; q < kQ; q++) v[q] = reinterpret_cast<const uint4*>(src)[kThreads * q + tid];
+#pragma unroll
+  for (uint32_t q = 0; q < kQ; q++) reinterpret_cast<uint4*>(dst)[kThreads * q + tid] = v[q];
+}
+
+// Lane L's four symbols E[256 ch + 4L .. + 3] of the tile (four symbols of
+// one row: nE and every row start are multiples of 64), zero past nE.
 template <uint32_t D>
-__device__ __forceinline__ uint32_t lane_codes(const uint16_t* sy, const uint8_t* urow, uint32_t ch,
-                                               uint32_t nE, const uint32_t* enc, uint64_t* val) {
+__device__ __forceinline__ uint2 lane_syms(const uint16_t* sy, const uint8_t* urow, uint32_t ch, uint32_t nE) {
   const uint32_t e = ch * 256 + 4 * (threadIdx.x & 63);
+  if (e >= nE) return make_uint2(0, 0);
+  return *reinterpret_cast<const uint2*>(sy + (uint32_t)urow[e / D] * D + e % D);
+}
+
+// Bits of those four symbols (none past nE); with codes (enc: len << 16 |
+// code) also their codes, first code in the high bits of *val.
+__device__ __forceinline__ uint32_t lane_code_bits(uint2 w, bool has, const uint32_t* enc, uint64_t* val) {
   uint32_t bits = 0;
   uint64_t v = 0;
-  if (e < nE) {  // four symbols of one row: nE and every row start are multiples of 64
-    const uint32_t u = e / D, d = e % D;
-    const uint2 w = *reinterpret_cast<const uint2*>(sy + (uint32_t)urow[u] * D + d);
+  if (has) {
     const uint32_t sym[4] = {w.x & 0xFFFFu, w.x >> 16, w.y & 0xFFFFu, w.y >> 16};
 #pragma unroll
     for (int k = 0; k < 4; k++) {
@@ -2162,7 +2201,7 @@ template <int C>
 __global__ void __launch_bounds__(kThreads) ec_hsize_tiles(EncArgs a) {
   constexpr uint32_t D = 64u * C;
   __shared__ uint32_t s_enc[kHuffTable];
-  __shared__ uint8_t s_urow[kTileRows];
+  __shared__ uint8_t s_urow[kThreads / 64][kTileRows];
   __shared__ uint32_t s_words[kThreads / 64];
   const uint32_t tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const uint32_t ticket = blockIdx.x;
@@ -2173,16 +2212,26 @@ __global__ void __launch_bounds__(kThreads) ec_hsize_tiles(EncArgs a) {
     return;
   }
   const uint32_t* enc = a.w.henc + (uint64_t)c.s * kHuffTable;
-  for (uint32_t i = tid; i < kHuffTable; i += kThreads) s_enc[i] = enc[i];
   const uint64_t bm = a.w.tile_bitmap[ticket];
-  if (wv == 0) unique_rows(bm, s_urow);
-  __syncthreads();
+  unique_rows(bm, s_urow[wv]);  // every wave its own copy: no barrier before the loads
+  wave_lds_wait();
   const uint32_t U = (uint32_t)__popcll(bm), nE = U * D, nch = (nE + 255) / 256;
   const uint16_t* sy = a.w.stage_sym + (uint64_t)ticket * kTileRows * D;
+  // the symbols of the wave's chunks, then the code table: all loads in flight
+  constexpr uint32_t kChPerWave = kTileRows * D / 256 / (kThreads / 64);
+  uint2 sw[kChPerWave];
+#pragma unroll
+  for (uint32_t k = 0; k < kChPerWave; k++) sw[k] = lane_syms<D>(sy, s_urow[wv], wv + (kThreads / 64) * k, nE);
+  copy_table(s_enc, enc, tid);
+  __syncthreads();
   uint32_t words = 0;
-  for (uint32_t ch = wv; ch < nch; ch += kThreads / 64) {
+#pragma unroll
+  for (uint32_t k = 0; k < kChPerWave; k++) {
+    const uint32_t ch = wv + (kThreads / 64) * k;
+    if (ch >= nch) break;
     uint64_t v;
-    const uint32_t bits = wave_sum_u32(lane_codes<D>(sy, s_urow, ch, nE, s_enc, &v));
+    const uint32_t bits =
+        wave_sum_u32(lane_code_bits(sw[k], ch * 256 + 4 * lane < nE, s_enc, &v));
     words += (bits + 31) / 32;
   }
   if (lane == 0) s_words[wv] = words;
@@ -2302,7 +2351,7 @@ __global__ void __launch_bounds__(kThreads) ec_write_huff(EncArgs a) {
   __shared__ uint32_t s_enc[kHuffTable];
   __shared__ uint32_t s_buf[kThreads / 64][96];
   __shared__ uint32_t s_cw[kMaxCh + 1];
-  __shared__ uint8_t s_urow[kTileRows];
+  __shared__ uint8_t s_urow[kThreads / 64][kTileRows];
   const uint32_t tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const uint32_t ticket = blockIdx.x;
   const uint4 info = reinterpret_cast<const uint4*>(a.w.tile_info)[ticket];
@@ -2311,17 +2360,27 @@ __global__ void __launch_bounds__(kThreads) ec_write_huff(EncArgs a) {
   const uint32_t n = c.n, U = info.x, nout = info.y;
   uint8_t* rec = a.out + (a.w.tile_rec[ticket] - 1);
   const uint32_t* enc = a.w.henc + (uint64_t)c.s * kHuffTable;
-  for (uint32_t i = tid; i < kHuffTable; i += kThreads) s_enc[i] = enc[i];
   const uint64_t bm = a.w.tile_bitmap[ticket];
-  if (wv == 0) unique_rows(bm, s_urow);
-  __syncthreads();
+  unique_rows(bm, s_urow[wv]);  // every wave its own copy: no barrier before the loads
+  wave_lds_wait();
   const uint32_t rb = ref_bytes(c.rows, a.window);
   const uint32_t off_ct = (uint32_t)align_up(16 + rb * (n - U), 4) + 8 * nout;
   const uint32_t nE = U * D, nch = (nE + 255) / 256, off_w = off_ct + 4 * (nch + 1);
   const uint16_t* sy = a.w.stage_sym + (uint64_t)ticket * kTileRows * D;
-  for (uint32_t ch = wv; ch < nch; ch += kThreads / 64) {  // words of every chunk
+  // the symbols of the wave's chunks (used twice), then the code table: all
+  // loads in flight
+  constexpr uint32_t kChPerWave = kMaxCh / (kThreads / 64);
+  uint2 sw[kChPerWave];
+#pragma unroll
+  for (uint32_t k = 0; k < kChPerWave; k++) sw[k] = lane_syms<D>(sy, s_urow[wv], wv + (kThreads / 64) * k, nE);
+  copy_table(s_enc, enc, tid);
+  __syncthreads();
+#pragma unroll
+  for (uint32_t k = 0; k < kChPerWave; k++) {  // words of every chunk
+    const uint32_t ch = wv + (kThreads / 64) * k;
+    if (ch >= nch) break;
     uint64_t v;
-    const uint32_t bits = wave_sum_u32(lane_codes<D>(sy, s_urow, ch, nE, s_enc, &v));
+    const uint32_t bits = wave_sum_u32(lane_code_bits(sw[k], ch * 256 + 4 * lane < nE, s_enc, &v));
     if (lane == 0) s_cw[ch] = (bits + 31) / 32;
   }
   __syncthreads();
@@ -2342,12 +2401,15 @@ __global__ void __launch_bounds__(kThreads) ec_write_huff(EncArgs a) {
   __syncthreads();
   uint32_t* buf = s_buf[wv];
   uint32_t* words = reinterpret_cast<uint32_t*>(rec + off_w);
-  for (uint32_t ch = wv; ch < nch; ch += kThreads / 64) {
+#pragma unroll
+  for (uint32_t k = 0; k < kChPerWave; k++) {
+    const uint32_t ch = wv + (kThreads / 64) * k;
+    if (ch >= nch) break;
     buf[lane] = 0;
     if (lane < 32) buf[64 + lane] = 0;
     wave_lds_wait();
     uint64_t v;
-    const uint32_t L = lane_codes<D>(sy, s_urow, ch, nE, s_enc, &v);
+    const uint32_t L = lane_code_bits(sw[k], ch * 256 + 4 * lane < nE, s_enc, &v);
     const uint32_t inc = wave_incl_u32(L), start = inc - L;
     if (L) {  // the bits [start, start + L) of the chunk, first bit in bit 31 of its word
       const uint32_t w0 = start >> 5, S = (start & 31u) + L;
