@@ -635,23 +635,36 @@ __global__ void __launch_bounds__(kThreads) huff_size(const uint16_t* __restrict
   const uint32_t wv = threadIdx.x >> 6, ln = lane_id();
   const uint32_t c0 = blockIdx.x * per_group, c1 = min(c0 + per_group, nch);
   uint32_t gsum = 0;
-  for (uint32_t c = c0 + wv; c < c1; c += kThreads / 64) {
-    const uint64_t base = (uint64_t)c * kChunk;
-    const uint64_t cnt = min((uint64_t)kChunk, n - base);
-    uint32_t b = 0;
-    if (vec && cnt == (uint64_t)kChunk) {
-      const uint2 q = reinterpret_cast<const uint2*>(sym + base)[ln];
-      b = lens[min(q.x & 0xFFFFu, 4095u)] + lens[min(q.x >> 16, 4095u)] +
-          lens[min(q.y & 0xFFFFu, 4095u)] + lens[min(q.y >> 16, 4095u)];
-    } else {
-      for (uint32_t k = 0; k < 4; k++) {
-        const uint32_t i = ln * 4 + k;
-        if (i < cnt) b += lens[min((uint32_t)sym[base + i], 4095u)];
-      }
+  // the wave's chunks kBatch at a time, the loads of full chunks all in flight
+  constexpr uint32_t kBatch = 8, kW = kThreads / 64;
+  for (uint32_t cb = c0 + wv; cb < c1; cb += kBatch * kW) {
+    uint2 q[kBatch];
+#pragma unroll
+    for (uint32_t u = 0; u < kBatch; u++) {
+      const uint32_t c = cb + kW * u;
+      const bool full = vec && c < c1 && (uint64_t)(c + 1) * kChunk <= n;
+      q[u] = full ? reinterpret_cast<const uint2*>(sym + (uint64_t)c * kChunk)[ln] : make_uint2(0, 0);
     }
-    const uint32_t words = (wave_sum(b) + 31) >> 5;
-    if (ln == 0) chunk_off[c + 1] = words;
-    gsum += words;
+#pragma unroll
+    for (uint32_t u = 0; u < kBatch; u++) {
+      const uint32_t c = cb + kW * u;
+      if (c >= c1) break;
+      const uint64_t base = (uint64_t)c * kChunk;
+      const uint64_t cnt = min((uint64_t)kChunk, n - base);
+      uint32_t b = 0;
+      if (vec && cnt == (uint64_t)kChunk) {
+        b = lens[min(q[u].x & 0xFFFFu, 4095u)] + lens[min(q[u].x >> 16, 4095u)] +
+            lens[min(q[u].y & 0xFFFFu, 4095u)] + lens[min(q[u].y >> 16, 4095u)];
+      } else {
+        for (uint32_t k = 0; k < 4; k++) {
+          const uint32_t i = ln * 4 + k;
+          if (i < cnt) b += lens[min((uint32_t)sym[base + i], 4095u)];
+        }
+      }
+      const uint32_t words = (wave_sum(b) + 31) >> 5;
+      if (ln == 0) chunk_off[c + 1] = words;
+      gsum += words;
+    }
   }
   if (ln == 0) wsum[wv] = gsum;
   __syncthreads();
@@ -669,7 +682,7 @@ __global__ void __launch_bounds__(kThreads) huff_write(const uint16_t* __restric
                                                        Ws w, uint32_t* __restrict__ chunk_off0,
                                                        uint32_t nch, uint32_t per_group,
                                                        uint32_t* __restrict__ words) {
-  __shared__ uint32_t enc[kTable];
+  __shared__ __align__(16) uint32_t enc[kTable];
   __shared__ uint32_t offs[kThreads], cnts[kThreads];
   __shared__ uint32_t buf[kThreads / 64][kChunkWords];
   __shared__ uint32_t part[16];
@@ -678,7 +691,15 @@ __global__ void __launch_bounds__(kThreads) huff_write(const uint16_t* __restric
   const uint16_t* sym = sym0 + (uint64_t)seg * n;
   uint32_t* chunk_off = chunk_off0 + (size_t)seg * nch;
   const bool vec = (n & 3) == 0;
-  for (int i = t; i < kTable; i += kThreads) enc[i] = w.enc[(size_t)seg * kTable + i];
+  {  // the segment's code table, every load of a thread in flight before its stores
+    constexpr int kQ = kTable / 4 / kThreads;
+    const uint4* src = reinterpret_cast<const uint4*>(w.enc + (size_t)seg * kTable);
+    uint4 v[kQ];
+#pragma unroll
+    for (int q = 0; q < kQ; q++) v[q] = src[kThreads * q + t];
+#pragma unroll
+    for (int q = 0; q < kQ; q++) reinterpret_cast<uint4*>(enc)[kThreads * q + t] = v[q];
+  }
   for (int i = t; i < kChunkWords * (kThreads / 64); i += kThreads) (&buf[0][0])[i] = 0;
   // words of all groups before this one
   uint32_t before = 0;
@@ -697,8 +718,20 @@ __global__ void __launch_bounds__(kThreads) huff_write(const uint16_t* __restric
     cnts[t] = cw;
     base += total;
     __syncthreads();
-    for (uint32_t j0 = 0; j0 < (uint32_t)kThreads; j0 += kThreads / 64) {
-      const uint32_t j = j0 + wv, cc = r0 + j;
+    // the wave's chunks of the round kBatch at a time, the loads of full
+    // chunks all in flight
+    constexpr uint32_t kBatch = 8, kW = kThreads / 64;
+    for (uint32_t jb = 0; jb < (uint32_t)kThreads && r0 + jb < c1; jb += kBatch * kW) {
+    uint2 qb[kBatch];
+#pragma unroll
+    for (uint32_t u = 0; u < kBatch; u++) {
+      const uint32_t cc = r0 + jb + kW * u + wv;
+      const bool full = vec && cc < c1 && (uint64_t)(cc + 1) * kChunk <= n;
+      qb[u] = full ? reinterpret_cast<const uint2*>(sym + (uint64_t)cc * kChunk)[ln] : make_uint2(0, 0);
+    }
+#pragma unroll
+    for (uint32_t u = 0; u < kBatch; u++) {
+      const uint32_t j = jb + kW * u + wv, cc = r0 + j;
       const bool active = cc < c1;
       uint32_t nbits_wave = 0;
       if (active) {
@@ -706,7 +739,7 @@ __global__ void __launch_bounds__(kThreads) huff_write(const uint16_t* __restric
         const uint64_t cnt = min((uint64_t)kChunk, n - sbase);
         uint32_t s[4];
         if (vec && cnt == (uint64_t)kChunk) {
-          const uint2 q = reinterpret_cast<const uint2*>(sym + sbase)[ln];
+          const uint2 q = qb[u];
           s[0] = q.x & 0xFFFFu;
           s[1] = q.x >> 16;
           s[2] = q.y & 0xFFFFu;
@@ -754,6 +787,7 @@ __global__ void __launch_bounds__(kThreads) huff_write(const uint16_t* __restric
       }
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       __builtin_amdgcn_wave_barrier();
+    }
     }
     __syncthreads();  // offs[] is rewritten by the next round
   }
@@ -948,7 +982,7 @@ __global__ void __launch_bounds__(kDecChunks) huff_decode(const uint32_t* __rest
                                                           const uint32_t* __restrict__ chunk_off0,
                                                           uint64_t n, uint32_t nch, Ws w,
                                                           uint16_t* __restrict__ sym0) {
-  __shared__ uint16_t lut[kTable];
+  __shared__ __align__(16) uint16_t lut[kTable];
   __shared__ __align__(16) uint32_t stage[kStageWords];
   const uint32_t t = threadIdx.x, seg = blockIdx.y;
   const uint32_t c0 = blockIdx.x * kDecChunks, c = c0 + t;

@@ -2200,7 +2200,7 @@ __device__ __forceinline__ uint32_t lane_code_bits(uint2 w, bool has, const uint
 template <int C>
 __global__ void __launch_bounds__(kThreads) ec_hsize_tiles(EncArgs a) {
   constexpr uint32_t D = 64u * C;
-  __shared__ uint32_t s_enc[kHuffTable];
+  __shared__ __align__(16) uint32_t s_enc[kHuffTable];
   __shared__ uint8_t s_urow[kThreads / 64][kTileRows];
   __shared__ uint32_t s_words[kThreads / 64];
   const uint32_t tid = threadIdx.x, lane = tid & 63, wv = wave_id();
@@ -2348,7 +2348,7 @@ template <int C>
 __global__ void __launch_bounds__(kThreads) ec_write_huff(EncArgs a) {
   constexpr uint32_t D = 64u * C;
   constexpr uint32_t kMaxCh = kTileRows * D / 256;
-  __shared__ uint32_t s_enc[kHuffTable];
+  __shared__ __align__(16) uint32_t s_enc[kHuffTable];
   __shared__ uint32_t s_buf[kThreads / 64][96];
   __shared__ uint32_t s_cw[kMaxCh + 1];
   __shared__ uint8_t s_urow[kThreads / 64][kTileRows];
@@ -3671,7 +3671,7 @@ __global__ void __launch_bounds__(64) ec_decode_huff(const uint8_t* __restrict__
   // (a code of about 7 bits; larger records are read from global memory)
   constexpr uint32_t kStage = kMaxCh * 56;
   __shared__ DecShared sh;
-  __shared__ uint16_t s_lut[kHuffTable];
+  __shared__ __align__(16) uint16_t s_lut[kHuffTable];
   __shared__ uint32_t s_words[kStage];
   __shared__ uint8_t s_urow[kTileRows];
   const uint32_t lane = threadIdx.x;
@@ -3788,7 +3788,7 @@ __global__ void __launch_bounds__(64) ec_decode_huff_pair(const uint8_t* __restr
   // a record's words are staged in LDS when they average at most 52 per chunk
   constexpr uint32_t kStage = kMaxCh * 52;
   __shared__ DecShared sh[2];
-  __shared__ uint16_t s_lut[kHuffTable];
+  __shared__ __align__(16) uint16_t s_lut[kHuffTable];
   __shared__ uint32_t s_words[2][kStage];
   __shared__ uint8_t s_urow[2][kTileRows];
   const uint32_t lane = threadIdx.x, h = lane >> 5, hl = lane & 31;
