@@ -635,36 +635,23 @@ __global__ void __launch_bounds__(kThreads) huff_size(const uint16_t* __restrict
   const uint32_t wv = threadIdx.x >> 6, ln = lane_id();
   const uint32_t c0 = blockIdx.x * per_group, c1 = min(c0 + per_group, nch);
   uint32_t gsum = 0;
-  // the wave's chunks kBatch at a time, the loads of full chunks all in flight
-  constexpr uint32_t kBatch = 8, kW = kThreads / 64;
-  for (uint32_t cb = c0 + wv; cb < c1; cb += kBatch * kW) {
-    uint2 q[kBatch];
-#pragma unroll
-    for (uint32_t u = 0; u < kBatch; u++) {
-      const uint32_t c = cb + kW * u;
-      const bool full = vec && c < c1 && (uint64_t)(c + 1) * kChunk <= n;
-      q[u] = full ? reinterpret_cast<const uint2*>(sym + (uint64_t)c * kChunk)[ln] : make_uint2(0, 0);
-    }
-#pragma unroll
-    for (uint32_t u = 0; u < kBatch; u++) {
-      const uint32_t c = cb + kW * u;
-      if (c >= c1) break;
-      const uint64_t base = (uint64_t)c * kChunk;
-      const uint64_t cnt = min((uint64_t)kChunk, n - base);
-      uint32_t b = 0;
-      if (vec && cnt == (uint64_t)kChunk) {
-        b = lens[min(q[u].x & 0xFFFFu, 4095u)] + lens[min(q[u].x >> 16, 4095u)] +
-            lens[min(q[u].y & 0xFFFFu, 4095u)] + lens[min(q[u].y >> 16, 4095u)];
-      } else {
-        for (uint32_t k = 0; k < 4; k++) {
-          const uint32_t i = ln * 4 + k;
-          if (i < cnt) b += lens[min((uint32_t)sym[base + i], 4095u)];
-        }
+  for (uint32_t c = c0 + wv; c < c1; c += kThreads / 64) {
+    const uint64_t base = (uint64_t)c * kChunk;
+    const uint64_t cnt = min((uint64_t)kChunk, n - base);
+    uint32_t b = 0;
+    if (vec && cnt == (uint64_t)kChunk) {
+      const uint2 q = reinterpret_cast<const uint2*>(sym + base)[ln];
+      b = lens[min(q.x & 0xFFFFu, 4095u)] + lens[min(q.x >> 16, 4095u)] +
+          lens[min(q.y & 0xFFFFu, 4095u)] + lens[min(q.y >> 16, 4095u)];
+    } else {
+      for (uint32_t k = 0; k < 4; k++) {
+        const uint32_t i = ln * 4 + k;
+        if (i < cnt) b += lens[min((uint32_t)sym[base + i], 4095u)];
       }
-      const uint32_t words = (wave_sum(b) + 31) >> 5;
-      if (ln == 0) chunk_off[c + 1] = words;
-      gsum += words;
     }
+    const uint32_t words = (wave_sum(b) + 31) >> 5;
+    if (ln == 0) chunk_off[c + 1] = words;
+    gsum += words;
   }
   if (ln == 0) wsum[wv] = gsum;
   __syncthreads();
