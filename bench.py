@@ -31,6 +31,8 @@ WORKLOADS = {
     "c3": "26x8192x128 fp32 multi-hot pooled lookups, eb 0.005*range*(1+t/1000)^-1/2",
     "c4": "26x8192x128 fp32 gradients N(0,1e-3)+5% Laplace rows, sum-duplicated, abs eb 1e-5",
     "c5": "64x16384x256 fp32 one-hot Zipf(1.2) lookups, eb 0.01*range",
+    "c5d40": "64x16384x256 fp32 one-hot Zipf-Mandelbrot(1.2, shift solved per table for "
+             "an expected 40% repeated rows) lookups, eb 0.01*range",
 }
 
 
@@ -179,6 +181,13 @@ KERNEL_PREFIX = {"prep": "ec_prep", "encode": ("ec_encode", "ec_quantize"),
 KERNEL_PREFIX_HUFF = {"huffman_encode": ("huff_clear", "huff_hist", "huff_book", "huff_size",
                                          "huff_write"),
                       "huffman_decode": ("huff_dec_book", "huff_decode")}
+
+
+def dup_summary(batches):
+    """Measured fraction of lookups that repeat an earlier row of their table,
+    over the tables of the timed batches (one-hot workloads)."""
+    d = [v for w in batches for v in w.dup]
+    return {"mean": round(sum(d) / len(d), 4), "min": round(min(d), 4), "max": round(max(d), 4)}
 
 
 def _short_kernel(name: str) -> str:
@@ -693,7 +702,8 @@ def main():
                    "batch": B, "dim": D, "chunks": 1, "batches_cycled": len(batches),
                    "stream_coder": args.stream_coder,
                    "reuse_books": bool(args.reuse_books),
-                   "protocol": "cold: 512 MiB scratch read before each timed call"},
+                   "protocol": "cold: 512 MiB scratch read before each timed call",
+                   **({"repeated_rows": dup_summary(batches)} if w0.dup else {})},
         "compress_GBps": round(4 * N / tc / 1e9, 2),
         "decompress_GBps": round(4 * N / td / 1e9, 2),
         "compression_ratio": round(4 * N * K / S_tot, 4),

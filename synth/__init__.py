@@ -23,6 +23,13 @@ Workloads (name -> shape, error bound):
       rows that share an index replaced by their fp32 sum in row order,
       abs eb 1e-5
   c5  64 x 16384 x 256, one-hot Zipf(1.2), eb = 0.01 * range per table
+  c5d40  c5 with Zipf-Mandelbrot draws P(k) ~ (k + q_t)^-1.2, the shift q_t
+      solved per table so that 16384 draws repeat a row with expected
+      fraction 0.40 (tables too small for that are drawn uniformly, the
+      closest their size allows)
+
+One-hot workloads carry the measured fraction of rows that repeat an earlier
+row of their table (`Workload.dup`).
 """
 from __future__ import annotations
 
@@ -97,6 +104,72 @@ def zipf_cdf(n: int, alpha: float, device="cpu") -> torch.Tensor:
     return c / c[-1]
 
 
+def zm_cdf(n: int, alpha: float, q: float, device="cpu") -> torch.Tensor:
+    """Normalized CDF of the Zipf-Mandelbrot law P(k) ~ (k + q)^-alpha, k = 1..n."""
+    k = torch.arange(1, n + 1, dtype=torch.float64, device=device)
+    c = torch.cumsum((k + q).pow(-alpha), 0)
+    return c / c[-1]
+
+
+def expected_dup(n: int, alpha: float, q: float, draws: int) -> float:
+    """Expected fraction of `draws` independent draws of P(k) ~ (k + q)^-alpha
+    on k = 1..n that repeat an earlier draw: 1 - E[distinct] / draws, with
+    E[distinct] = sum_k 1 - (1 - p_k)^draws.  Exact over the first 65536 ranks;
+    beyond, ranks are grouped in geometric bins (ratio about 1.002) that take
+    the weight of their middle rank."""
+    head = min(n, 65536)
+    k = torch.arange(1, head + 1, dtype=torch.float64)
+    w = (k + q).pow(-alpha)
+    cnt = torch.ones_like(w)
+    if n > head:
+        nb = max(1, int(torch.log(torch.tensor(n / head)).item() / 0.002))
+        e = torch.unique(torch.round(torch.logspace(torch.log10(torch.tensor(head + 0.5)).item(),
+                                                    torch.log10(torch.tensor(n + 0.5)).item(),
+                                                    nb + 1, dtype=torch.float64))) + 0.5
+        e = torch.unique(torch.clamp(e, head + 0.5, n + 0.5))  # edges between ranks
+        e[0], e[-1] = head + 0.5, n + 0.5
+        lo, hi = torch.ceil(e[:-1]), torch.floor(e[1:])
+        c = hi - lo + 1
+        keep = c > 0
+        lo, hi, c = lo[keep], hi[keep], c[keep]
+        w = torch.cat([w, ((lo + hi) / 2 + q).pow(-alpha)])
+        cnt = torch.cat([cnt, c])
+    p = w / (w * cnt).sum()
+    distinct = (cnt * -torch.expm1(draws * torch.log1p(-p))).sum().item()
+    return 1.0 - distinct / draws
+
+
+_ZM_SHIFT: dict = {}
+
+
+def zm_shift(n: int, alpha: float, draws: int, target: float) -> float:
+    """Shift q >= 0 with expected_dup(n, alpha, q, draws) = target (bisection on
+    log q; the expected fraction falls as q grows).  A table too small to get
+    down to the target is drawn (nearly) uniformly: q = 1e12."""
+    key = (n, alpha, draws, target)
+    if key not in _ZM_SHIFT:
+        if expected_dup(n, alpha, 1e12, draws) >= target:
+            q = 1e12
+        elif expected_dup(n, alpha, 0.0, draws) <= target:
+            q = 0.0
+        else:
+            lo, hi = -3.0, 12.0
+            for _ in range(48):
+                mid = 0.5 * (lo + hi)
+                if expected_dup(n, alpha, 10.0 ** mid, draws) > target:
+                    lo = mid
+                else:
+                    hi = mid
+            q = 10.0 ** (0.5 * (lo + hi))
+        _ZM_SHIFT[key] = q
+    return _ZM_SHIFT[key]
+
+
+def dup_fraction(idx: torch.Tensor) -> float:
+    """Fraction of the lookups that repeat an earlier row of the table."""
+    return 1.0 - torch.unique(idx).numel() / max(1, idx.numel())
+
+
 def zipf_rows(cdf: torch.Tensor, h: torch.Tensor) -> torch.Tensor:
     """Inverse-CDF Zipf draw: rank k (1-based) -> table row k-1."""
     u = u01_f64(h)
@@ -112,8 +185,8 @@ def table_rows(seed: int, t: int, rows: torch.Tensor, D: int, n_rows: int) -> to
     return sym_f32(h, float(1.0 / (n_rows ** 0.5)))
 
 
-def _lookup_one_hot(seed, it, t, B, D, n_rows, alpha, device):
-    cdf = zipf_cdf(n_rows, alpha, device)
+def _lookup_one_hot(seed, it, t, B, D, n_rows, alpha, device, shift=None):
+    cdf = zipf_cdf(n_rows, alpha, device) if shift is None else zm_cdf(n_rows, alpha, shift, device)
     idx = zipf_rows(cdf, keyed(seed, P_INDEX, it, t, torch.arange(B, device=device),
                                device=device))
     uniq, inv = torch.unique(idx, return_inverse=True)
@@ -181,6 +254,7 @@ class Workload:
     sched_kind: int = 0             # 0 none, 1 (1 + i/t0)^-1/2, 2 staircase
     sched_t0: float = 1000.0
     iteration: int = 0
+    dup: list | None = None         # one-hot workloads: measured repeat fraction per table
 
     @property
     def shape(self):
@@ -193,7 +267,9 @@ SHAPES = {
     "c3": (26, 8192, 128),
     "c4": (26, 8192, 128),
     "c5": (64, 16384, 256),
+    "c5d40": (64, 16384, 256),
 }
+DUP40 = 0.40  # the c5d40 target: expected fraction of repeated rows per table
 
 
 def workload(name: str, iteration: int = 0, device="cpu", seed: int = 0,
@@ -206,19 +282,22 @@ def workload(name: str, iteration: int = 0, device="cpu", seed: int = 0,
     T, B, D = SHAPES[name]
     ts = list(range(T)) if tables is None else list(tables)
     out = []
+    dup = []
     if name == "c1":
         for t in ts:
-            v, _ = _lookup_one_hot(seed, iteration, t, B, D, 100_000, 1.05, device)
+            v, idx = _lookup_one_hot(seed, iteration, t, B, D, 100_000, 1.05, device)
             out.append(v)
+            dup.append(dup_fraction(idx))
         x = torch.stack(out)
-        return Workload(name, x, 0, [1e-4] * len(ts), iteration=iteration)
+        return Workload(name, x, 0, [1e-4] * len(ts), iteration=iteration, dup=dup)
     sizes = table_sizes(seed, T)
     if name == "c2":
         alphas = (0.9 + 0.3 * u01_f64(keyed(seed, P_ALPHA, torch.arange(T)))).tolist()
         for t in ts:
-            v, _ = _lookup_one_hot(seed, iteration, t, B, D, sizes[t], alphas[t], device)
+            v, idx = _lookup_one_hot(seed, iteration, t, B, D, sizes[t], alphas[t], device)
             out.append(v)
-        return Workload(name, torch.stack(out), 1, [0.01] * len(ts), iteration=iteration)
+            dup.append(dup_fraction(idx))
+        return Workload(name, torch.stack(out), 1, [0.01] * len(ts), iteration=iteration, dup=dup)
     if name == "c3":
         for t in ts:
             out.append(_lookup_pooled(seed, iteration, t, B, D, sizes[t], 1.05, 20, device))
@@ -228,9 +307,11 @@ def workload(name: str, iteration: int = 0, device="cpu", seed: int = 0,
         for t in ts:
             out.append(_gradients(seed, iteration, t, B, D, sizes[t], device))
         return Workload(name, torch.stack(out), 0, [1e-5] * len(ts), iteration=iteration)
-    if name == "c5":
+    if name in ("c5", "c5d40"):
         for t in ts:
-            v, _ = _lookup_one_hot(seed, iteration, t, B, D, sizes[t], 1.2, device)
+            shift = zm_shift(sizes[t], 1.2, B, DUP40) if name == "c5d40" else None
+            v, idx = _lookup_one_hot(seed, iteration, t, B, D, sizes[t], 1.2, device, shift)
             out.append(v)
-        return Workload(name, torch.stack(out), 1, [0.01] * len(ts), iteration=iteration)
+            dup.append(dup_fraction(idx))
+        return Workload(name, torch.stack(out), 1, [0.01] * len(ts), iteration=iteration, dup=dup)
     raise KeyError(name)

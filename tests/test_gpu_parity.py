@@ -245,7 +245,7 @@ def describe_segment_diff(g, r, D):
     return f"{head}: tile {j} (U_t={u_t}, n_out={n_out}, mode={mode}) {part} byte {o}"
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5", "c5d40"])
 def test_workloads_full_size_whole_stream(name):
     """Full-size batch on the GPU, in the launch configuration the benchmark
     times.  The oracle compresses the whole batch: the complete GPU stream
