@@ -615,6 +615,10 @@ def main():
     wall = time.perf_counter() - wall0
     tc_ms = sum(ev[4 * i].elapsed_time(ev[4 * i + 1]) for i in range(args.steps))
     td_ms = sum(ev[4 * i + 2].elapsed_time(ev[4 * i + 3]) for i in range(args.steps))
+    # the median step beside the mean (the value): compress + decompress per step
+    step_ms = sorted(ev[4 * i].elapsed_time(ev[4 * i + 1]) + ev[4 * i + 2].elapsed_time(ev[4 * i + 3])
+                     for i in range(args.steps))
+    med_ms = (step_ms[(args.steps - 1) // 2] + step_ms[args.steps // 2]) / 2
     _, _, st = plan.ratio(raise_on_error=False)
     if st != 0:
         print(f"[bench] device status {st}", file=sys.stderr)
@@ -693,6 +697,7 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(step_s * 1e3, 5),
+        "median": {"ms_per_step": round(med_ms, 5), "value": round(4 * N / (med_ms * 1e-3) / 1e9, 2)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
