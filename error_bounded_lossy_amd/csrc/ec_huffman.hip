@@ -971,7 +971,7 @@ __global__ void __launch_bounds__(kDecChunks) huff_decode(const uint32_t* __rest
                                                           uint16_t* __restrict__ sym0) {
   __shared__ __align__(16) uint16_t lut[kTable];
   __shared__ __align__(16) uint32_t stage[kStageWords];
-  const uint32_t t = threadIdx.x, seg = blockIdx.y;
+  const uint32_t t = threadIdx.x, seg = blockIdx.y, wv = t >> 6, ln = t & 63u;
   const uint32_t c0 = blockIdx.x * kDecChunks, c = c0 + t;
   const uint32_t cend = min(c0 + kDecChunks, nch);
   const uint32_t* chunk_off = chunk_off0 + (size_t)seg * nch;
@@ -1028,13 +1028,63 @@ __global__ void __launch_bounds__(kDecChunks) huff_decode(const uint32_t* __rest
     if (t == 0) status_or(w.status, kStCorrupt);
     return;
   }
-  if (c >= cend) return;
   const uint64_t sbase = (uint64_t)c * kChunk;
-  const uint32_t rem = (uint32_t)min((uint64_t)kChunk, n - sbase);
-  const bool good = b == a ? false
-                    : staged ? decode_chunk_lds(stage + (a - 4 * q0), b - a, rem, lut, sym + sbase, vec)
-                             : decode_chunk(words + a, b - a, rem, lut, sym + sbase, vec);
-  if (!good) status_or(w.status, kStCorrupt);
+  const uint32_t rem = c < cend ? (uint32_t)min((uint64_t)kChunk, n - sbase) : 0u;
+  auto decode_from = [&](const uint32_t* src_words) {  // this lane's chunk
+    if (c >= cend) return;
+    const bool good = b != a && decode_chunk_lds(src_words + a, b - a, rem, lut, sym + sbase, vec);
+    if (!good) status_or(w.status, kStCorrupt);
+  };
+  if (staged) {
+    decode_from(stage - 4 * q0);
+    return;
+  }
+  // The group's words do not fit (codes of about 7 bits and more): each
+  // wave's 64 chunks (every chunk now checked, so the offsets increase) take
+  // at most 64 * kChunkWords words, which fit the stage, so the waves take
+  // turns: one stages its words and decodes while the other waits; every
+  // wave passes every barrier.
+  static_assert(64 * kChunkWords + 3 <= kStageWords, "a wave's words fit the stage");
+  const uint32_t mid = chunk_off[min(c0 + 64u, cend)];  // wave 0: [glo, mid), wave 1: [mid, ghi)
+  const uint32_t wlo = wv == 0 ? glo : mid, whi = wv == 0 ? mid : ghi, wq0 = wlo >> 2;
+  auto stage_wave = [&](uint32_t* dst) {  // words [4 wq0, whi) of this wave into dst
+    const uint4* wq = reinterpret_cast<const uint4*>(words);
+    uint4* sq = reinterpret_cast<uint4*>(dst);
+    const uint32_t wq1 = whi >> 2;
+    for (uint32_t i0 = wq0 + ln; i0 < wq1; i0 += 8 * 64) {
+      uint4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const uint32_t i = i0 + 64 * j;
+        v[j] = i < wq1 ? wq[i] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const uint32_t i = i0 + 64 * j;
+        if (i < wq1) sq[i - wq0] = v[j];
+      }
+    }
+    const uint32_t i = 4 * wq1 + ln;
+    if (ln < 3 && i < whi) dst[i - 4 * wq0] = words[i];
+    // a wave's LDS operations complete in order: the fence keeps the
+    // compiler from moving the chunk reads above these stores
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  };
+  if (((uintptr_t)words & 15u) != 0) {  // (aligned by the API's contract)
+    if (c < cend) {
+      const bool good = b != a && decode_chunk(words + a, b - a, rem, lut, sym + sbase, vec);
+      if (!good) status_or(w.status, kStCorrupt);
+    }
+  } else {
+    for (uint32_t pass = 0; pass < kDecChunks / 64; pass++) {
+      if (wv == pass) {
+        stage_wave(stage);
+        decode_from(stage - 4 * wq0);
+      }
+      __syncthreads();  // the next wave rewrites the stage
+    }
+  }
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
