@@ -1030,13 +1030,14 @@ __global__ void __launch_bounds__(kDecChunks) huff_decode(const uint32_t* __rest
   }
   const uint64_t sbase = (uint64_t)c * kChunk;
   const uint32_t rem = c < cend ? (uint32_t)min((uint64_t)kChunk, n - sbase) : 0u;
-  auto decode_from = [&](const uint32_t* src_words) {  // this lane's chunk
+  // this lane's chunk from the staged words that start at word `base`
+  auto decode_from = [&](const uint32_t* staged_words, uint32_t base) {
     if (c >= cend) return;
-    const bool good = b != a && decode_chunk_lds(src_words + a, b - a, rem, lut, sym + sbase, vec);
+    const bool good = b != a && decode_chunk_lds(staged_words + (a - base), b - a, rem, lut, sym + sbase, vec);
     if (!good) status_or(w.status, kStCorrupt);
   };
   if (staged) {
-    decode_from(stage - 4 * q0);
+    decode_from(stage, 4 * q0);
     return;
   }
   // The group's words do not fit (codes of about 7 bits and more): each
@@ -1080,7 +1081,7 @@ __global__ void __launch_bounds__(kDecChunks) huff_decode(const uint32_t* __rest
     for (uint32_t pass = 0; pass < kDecChunks / 64; pass++) {
       if (wv == pass) {
         stage_wave(stage);
-        decode_from(stage - 4 * wq0);
+        decode_from(stage, 4 * wq0);
       }
       __syncthreads();  // the next wave rewrites the stage
     }

@@ -3843,12 +3843,24 @@ __global__ void __launch_bounds__(64) ec_decode_huff_pair(const uint8_t* __restr
     v.wavail = (tl.avail - tl.off_w) / 4;  // words the segment still holds
     v.s2 = sh[q].eb + sh[q].eb;
     v.total = v.ct[v.nch];
-    v.staged = v.total <= kStage && (uint64_t)v.total <= v.wavail;
+    v.staged = v.total <= kStage && (uint64_t)v.total <= v.wavail;  // fits half the stage
     v.tbad = (v.nE > 0 && a.w.hvalid[v.seg] == 0) || v.ct[0] != 0;
   }
-  const bool split = act == 3u && tv[0].seg != tv[1].seg;
+  // one pass for both tiles when they share a table and each fits half the
+  // stage; else one pass per tile, which then has the whole stage (any valid
+  // tile fits it: at most 96 words per chunk)
+  static_assert(kMaxCh * 96 <= 2 * kStage, "a tile's words fit the whole stage");
+  const bool split = act == 3u && (tv[0].seg != tv[1].seg || !tv[0].staged || !tv[1].staged);
   for (uint32_t pass = 0; pass < (split ? 2u : 1u); pass++) {
     const uint32_t pm = split ? (1u << pass) : act;  // the tiles of this pass
+    const bool alone = pm != 3u;                       // one tile: the whole stage
+    const uint32_t cap = alone ? 2 * kStage : kStage;
+    bool st[2];  // the tile's words are staged (at s_words[q], or the whole stage when alone)
+#pragma unroll
+    for (uint32_t q = 0; q < 2; q++)
+      st[q] = ((pm >> q) & 1u) && tv[q].total <= cap && (uint64_t)tv[q].total <= tv[q].wavail;
+    uint32_t* const base0 = &s_words[0][0];
+    uint32_t* const base1 = alone ? base0 : &s_words[1][0];
     {
       const uint32_t lseg = (pm & 1u) ? tv[0].seg : tv[1].seg;
       const uint4* src = reinterpret_cast<const uint4*>(a.w.hlut + (uint64_t)lseg * kHuffTable);
@@ -3860,8 +3872,8 @@ __global__ void __launch_bounds__(64) ec_decode_huff_pair(const uint8_t* __restr
     for (uint32_t q = 0; q < 2; q++)
       if ((pm >> q) & 1u) unique_rows(sh[q].tl.bitmap, s_urow[q]);
     // both tiles' words into LDS, eight loads per lane and tile in flight
-    const uint32_t tot0 = ((pm & 1u) && tv[0].staged) ? tv[0].total : 0u;
-    const uint32_t tot1 = ((pm & 2u) && tv[1].staged) ? tv[1].total : 0u;
+    const uint32_t tot0 = st[0] ? tv[0].total : 0u;
+    const uint32_t tot1 = st[1] ? tv[1].total : 0u;
     for (uint32_t i0 = 0; i0 < max(tot0, tot1); i0 += 8 * 64) {
       uint32_t v0[8], v1[8];
 #pragma unroll
@@ -3873,8 +3885,8 @@ __global__ void __launch_bounds__(64) ec_decode_huff_pair(const uint8_t* __restr
 #pragma unroll
       for (uint32_t k = 0; k < 8; k++) {
         const uint32_t i = i0 + 64 * k + lane;
-        if (i < tot0) s_words[0][i] = v0[k];
-        if (i < tot1) s_words[1][i] = v1[k];
+        if (i < tot0) base0[i] = v0[k];
+        if (i < tot1) base1[i] = v1[k];
       }
     }
     wave_lds_wait();
@@ -3908,8 +3920,8 @@ __global__ void __launch_bounds__(64) ec_decode_huff_pair(const uint8_t* __restr
             }
           }
         };
-        if (!dbad && v.staged) {
-          dbad = !hd::decode_chunk_lds_sink(s_words[h] + w0, w1 - w0, rem, s_lut,
+        if (!dbad && (h ? st[1] : st[0])) {
+          dbad = !hd::decode_chunk_lds_sink((h ? base1 : base0) + w0, w1 - w0, rem, s_lut,
                                             [&](uint32_t g, const uint32_t (&pk)[16], uint32_t cnt) { put(g, pk, cnt); },
                                             false);
         } else if (!dbad) {
