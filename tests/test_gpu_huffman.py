@@ -131,6 +131,20 @@ def test_heavy_tailed_counts(coder, m, alpha):
     check_parity(coder, sym, f"power law m={m}")
 
 
+@pytest.mark.parametrize("n", [3 * 128 * 256, 3 * 128 * 256 + 77])
+def test_wide_codes_overflow_the_stage(coder, n):
+    """Near-uniform codes over the whole alphabet (about 12 bits each, about
+    96 words per chunk): every 128-chunk decode group exceeds the LDS stage
+    and is staged one wave at a time, with a ragged last chunk; then a last
+    group of 100 chunks (about 9600 words, still too many) whose second wave
+    holds 36 chunks, the last one partial."""
+    rng = np.random.default_rng(n)
+    sym = rng.integers(0, 4095, n).astype(np.uint16)
+    check_parity(coder, sym, f"wide codes n={n}")
+    tail = rng.integers(0, 4095, 128 * 256 + 100 * 256 - 100).astype(np.uint16)
+    check_parity(coder, tail, "wide codes, short last group")
+
+
 def test_many_ties(coder):
     rng = np.random.default_rng(9)
     used = rng.choice(4095, 600, replace=False)

@@ -93,7 +93,7 @@ def test_raw_tiles_hot_rows_and_weak_hashes(D, bits):
             assert not st.segments[3].huff
 
 
-@pytest.mark.parametrize("name,coder", [("c2", 3), ("c3", 3), ("c3", 2), ("c4", 3)])
+@pytest.mark.parametrize("name,coder", [("c2", 3), ("c3", 3), ("c3", 2), ("c4", 3), ("c4", 2)])
 def test_workloads_full_size(name, coder):
     """Full-size batches, whole stream byte for byte against the oracle."""
     import synth
