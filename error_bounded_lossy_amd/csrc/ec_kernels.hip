@@ -3201,6 +3201,33 @@ __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)"
 // where every row's values are (the tile descriptor td[2], row descriptors
 // drow[64] and block descriptors dblk[64*C], all in LDS).  LDS written by
 // one lane and read by others of the same wave is ordered by lds_sync.
+// First index in [0, n) whose position is at least v in a sorted list of
+// positions (n if none), eight probes per round trip: the probes split the
+// range into nine parts and the count of probes below v picks the part.
+// On a list that is not sorted (a corrupt stream) the result stays in
+// [0, n] and every read stays in [0, n).
+__device__ __forceinline__ uint32_t lower_bound8(const uint32_t* op, uint32_t n, uint32_t v) {
+  uint32_t lo = 0, hi = n;
+  while (hi - lo > 8) {
+    const uint32_t span = hi - lo;
+    uint32_t pr[8], c = 0;
+#pragma unroll
+    for (uint32_t q = 0; q < 8; q++) pr[q] = op[lo + (uint32_t)(((uint64_t)(q + 1) * span) / 9)];
+#pragma unroll
+    for (uint32_t q = 0; q < 8; q++) c += pr[q] < v ? 1u : 0u;
+    const uint32_t nlo = c ? lo + (uint32_t)(((uint64_t)c * span) / 9) + 1 : lo;
+    const uint32_t nhi = c < 8 ? lo + (uint32_t)(((uint64_t)(c + 1) * span) / 9) : hi;
+    lo = nlo;
+    hi = nhi > nlo ? nhi : nlo;
+  }
+  uint32_t pr[8], c = 0;
+#pragma unroll
+  for (uint32_t q = 0; q < 8; q++) pr[q] = lo + q < hi ? op[lo + q] : v;
+#pragma unroll
+  for (uint32_t q = 0; q < 8; q++) c += pr[q] < v ? 1u : 0u;
+  return lo + c;
+}
+
 template <int C>
 __device__ __forceinline__ void index_tile(const uint8_t* __restrict__ in, const DecArgs& a, uint32_t ticket,
                                            DecIndexLds<C>& x) {
@@ -3391,17 +3418,11 @@ __device__ __forceinline__ void index_tile(const uint8_t* __restrict__ in, const
       const uint32_t f = x.ofirst[u], e = x.oend[u];
       ocnt = e > f ? e - f : 0u;
       ofirst = oofs + 4 * f;
-    } else if (kind == kRowPlanes && onum) {  // an earlier tile's record: binary search
+    } else if (kind == kRowPlanes && onum) {  // an earlier tile's record: 8-way searches
       const uint32_t* op = reinterpret_cast<const uint32_t*>(sg + oofs);
-      uint32_t lo = 0, hi2 = onum;
-      while (lo < hi2) {
-        const uint32_t mid = (lo + hi2) >> 1;
-        if (op[mid] < u * D) lo = mid + 1;
-        else hi2 = mid;
-      }
-      uint32_t e = lo;
-      while (e < onum && op[e] < u * D + D) e++;
-      ocnt = e - lo;
+      const uint32_t lo = lower_bound8(op, onum, u * D);
+      const uint32_t e = lower_bound8(op, onum, u * D + D);
+      ocnt = e > lo ? e - lo : 0u;
       ofirst = oofs + 4 * lo;
     }
     // x: the kind (| kRowOutliers when the row has outliers); y: first-occurrence
