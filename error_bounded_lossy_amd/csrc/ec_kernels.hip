@@ -3276,7 +3276,7 @@ __device__ __forceinline__ void index_tile(const uint8_t* __restrict__ in, const
     put_tile();
     return;
   }
-  if (mode == 2) {  // a Huffman record: ec_decode_huff and ec_fill_refs
+  if (mode == 2) {  // a Huffman record: ec_decode_huff_pair / ec_decode_huff and ec_fill_refs
     flags = kTileOk | kTileHuff;
     put_tile();
     return;
@@ -3535,7 +3535,7 @@ __device__ __forceinline__ void decode_tile(const uint8_t* __restrict__ in, floa
     for (uint32_t i = tid; i < n * D; i += kThreads) yt[i] = 0.0f;
     return;
   }
-  if (flags & kTileHuff) return;  // decoded by ec_decode_huff and ec_fill_refs
+  if (flags & kTileHuff) return;  // decoded by ec_decode_huff_pair / ec_decode_huff and ec_fill_refs
   const uint8_t* sg = in + (((uint64_t)d0.w << 32) | d0.z);
   if (flags & kTileRaw) {  // RAW: rows verbatim
     const uint8_t* rec = in + (((uint64_t)d1.y << 32) | d1.x);
@@ -3640,8 +3640,9 @@ __global__ void __launch_bounds__(kThreads) ec_decode_fast(const uint8_t* __rest
 //            out of the stream (zero-padded; a placeholder for the others),
 //            then the Huffman coder's table builder (ec_huffman.hip)
 //   (the bit-plane decoder skips Huffman tiles)
-//   decode   per Huffman tile: chunks decoded one per lane by table lookups
-//            into LDS, first-occurrence rows dequantized with their outliers
+//   decode   two Huffman tiles per wave (D = 64, 128; one per wave at
+//            D = 256): chunks decoded one per lane by table lookups into
+//            LDS, first-occurrence rows dequantized with their outliers
 //   refs     per Huffman tile: repeated rows copied from their first
 //            occurrences' decoded rows (re-quantized from a RAW record)
 // ---------------------------------------------------------------------------
@@ -3799,14 +3800,15 @@ __global__ void __launch_bounds__(64) ec_decode_huff(const uint8_t* __restrict__
 // half h decodes the chunks of tile 2 blockIdx.x + h, one per lane, so that
 // every lane decodes and the workgroups (a table and two tiles' words in
 // LDS, about 22 KB) all fit the chip at once.  Two tiles of one segment
-// share the decode table; tiles of two segments take one pass each.
+// share the decode table; tiles of two segments, or a tile whose words do
+// not fit half the stage, take one pass each with the whole stage.
 // Checks, staging and the outlier pass are those of ec_decode_huff, per tile.
 template <int C>
 __global__ void __launch_bounds__(64) ec_decode_huff_pair(const uint8_t* __restrict__ in,
                                                          float* __restrict__ yout, DecArgs a) {
   constexpr uint32_t D = 64u * C, kMaxCh = kTileRows * D / 256;
   static_assert(kMaxCh <= 32, "one chunk per lane of a half-wave");
-  // a record's words are staged in LDS when they average at most 52 per chunk
+  // half the stage: a record's words averaging at most 52 per chunk
   constexpr uint32_t kStage = kMaxCh * 52;
   __shared__ DecShared sh[2];
   __shared__ __align__(16) uint16_t s_lut[kHuffTable];
