@@ -963,7 +963,10 @@ __global__ void __launch_bounds__(kDecBookThreads) huff_dec_book(const uint8_t* 
   *reinterpret_cast<uint2*>(lut + i0) = make_uint2(ev[0] | ev[1] << 16, ev[2] | ev[3] << 16);
 }
 
-// Chunks [128 blockIdx.x, 128 blockIdx.x + 128) of segment blockIdx.y.
+// Chunks [128 blockIdx.x, 128 blockIdx.x + 128) of segment blockIdx.y, one
+// lane per chunk: the decode table and the group's words go to LDS (the
+// words one wave at a time when they do not all fit), then every lane
+// decodes its chunk from LDS.
 __global__ void __launch_bounds__(kDecChunks) huff_decode(const uint32_t* __restrict__ words,
                                                           uint64_t words_cap,
                                                           const uint32_t* __restrict__ chunk_off0,
