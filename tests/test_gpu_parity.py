@@ -468,17 +468,19 @@ def test_corrupt_streams_are_rejected_or_decoded_like_the_oracle(D):
     assert n_bad > 0
 
 
-def test_graph_replays_match_eager_calls():
+@pytest.mark.parametrize("coder", [ec.CODER_BITPACK, ec.CODER_HUFFMAN, ec.CODER_AUTO])
+def test_graph_replays_match_eager_calls(coder):
     """Compression and decompression captured in HIP graphs (one per input)
     and replayed several times, with eager calls of the same plan in between:
     every replay's stream and output equal the eager results for its input
-    (nothing in either call allocates, clears with a memset or synchronizes)."""
+    (nothing in either call allocates, clears with a memset or synchronizes),
+    with bit planes, with Huffman segments, and with the automatic choice."""
     T, B, D = 3, 1000, 128
     rng = np.random.default_rng(31)
     xs = [torch.from_numpy(dup_rows(rng, T, B, D, scale=sc, frac_unique=fu)).cuda()
           for sc, fu in ((1.0, 0.4), (0.01, 0.9))]
     xs[1][0, 7, 5] = float("nan")
-    plan = ec.Plan(T, B, D, 1, ec.EB_REL_RANGE, 0.01)
+    plan = ec.Plan(T, B, D, 1, ec.EB_REL_RANGE, 0.01, coder=coder)
     out = plan.empty_stream()
     y = torch.empty(T, B, D, device="cuda")
     refs = []
