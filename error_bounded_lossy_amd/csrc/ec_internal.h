@@ -27,7 +27,7 @@ constexpr uint32_t kDevErrTimeout = 4;
 struct Report {
   uint64_t total_bytes;
   uint32_t status;
-  uint32_t pad;
+  uint32_t seq;  // the number of the last call that has finished (stored by its last launch)
   uint64_t seg_bytes[1];  // [nseg], allocated past the struct
 };
 
@@ -206,5 +206,7 @@ hipError_t static_scratch(void** out);
 // Copy `bytes` (a multiple of 16) from src (device memory or device-mapped
 // pinned host memory) to dst on stream s, with a kernel.
 hipError_t launch_copy_words(void* dst, const void* src, uint64_t bytes, hipStream_t s);
+// one wave that stores `seq` into the report once every earlier launch on s has finished
+hipError_t launch_done(Report* r, uint32_t seq, hipStream_t s);
 
 }  // namespace ec

@@ -4268,7 +4268,19 @@ __global__ void __launch_bounds__(kThreads) ec_copy_kernel(uint4* __restrict__ d
     dst[i] = src[i];
 }
 
+// A call's last launch: its number into the pinned report, where the host
+// waits for it (a release at system scope, so the report's other fields,
+// written by the call's earlier kernels, are visible first)
+__global__ void __launch_bounds__(64) ec_done_kernel(Report* r, uint32_t seq) {
+  if (threadIdx.x == 0) __hip_atomic_store(&r->seq, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 }  // namespace
+
+hipError_t launch_done(Report* r, uint32_t seq, hipStream_t s) {
+  hipLaunchKernelGGL(ec_done_kernel, dim3(1), dim3(64), 0, s, r, seq);
+  return hipGetLastError();
+}
 
 hipError_t static_scratch(void** out) {
   constexpr int kMaxDevices = 64;

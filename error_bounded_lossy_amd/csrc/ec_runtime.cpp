@@ -4,10 +4,13 @@
 // caller's stream, the pinned report block, and opt-in launch profiling.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstddef>
 #include <cstring>
 #include <new>
+#include <thread>
 #include <vector>
 
 #include "../../include/ec.h"
@@ -272,8 +275,8 @@ struct ec_plan_s {
   // workspace
   uint8_t* consts_host = nullptr;
   uint8_t* consts_dev = nullptr;
-  hipEvent_t done = nullptr;
-  bool have_done = false;
+  uint32_t seq = 0;         // the number of the last call enqueued outside a graph capture
+  bool have_done = false;   // such a call exists
   int32_t* dbg_codes = nullptr;
   uint8_t* dbg_outlier = nullptr;
   uint32_t* dbg_first = nullptr;
@@ -312,9 +315,43 @@ ec_status profiled(ec_plan_s* pl, int kernel, hipStream_t s, F&& launch) {
   return EC_OK;
 }
 
-void record_done(ec_plan_s* pl, hipStream_t s) {
-  if (capturing(s)) return;
-  if (hipEventRecord(pl->done, s) == hipSuccess) pl->have_done = true;
+// The call's completion, marked by its last launch: one wave that stores the
+// call's number into the pinned report once the stream reaches it.  (An event
+// recorded after every call holds the stream for several microseconds per
+// call in its marker packet, several times what this wave costs.)  Not while
+// the stream is captured: the number would be fixed in the graph.
+ec_status mark_done(ec_plan_s* pl, hipStream_t s) {
+  if (capturing(s)) return EC_OK;
+  const uint32_t next = pl->seq + 1;
+  if (ec::launch_done(pl->report_dev, next, s) != hipSuccess) return EC_ERR_DEVICE;
+  pl->seq = next;
+  pl->have_done = true;
+  return EC_OK;
+}
+
+// Wait until the report holds the last marked call's number (or a later one,
+// compared modulo 2^32).  Calls of one plan finish in order when they are
+// ordered on the device, as they must be (they share the workspace); if the
+// number has not arrived after 200 ms (a busy stream, or calls left unordered
+// on two streams, whose numbers may arrive out of order), the whole device is
+// waited for instead, after which every call has finished.
+ec_status wait_done(ec_plan_s* pl) {
+  if (!pl->have_done) return EC_OK;
+  const volatile uint32_t* q = &pl->report_host->seq;
+  const auto t0 = std::chrono::steady_clock::now();
+  for (uint32_t k = 0; (int32_t)(*q - pl->seq) < 0; k++) {
+    if (k < 256) {
+      std::this_thread::yield();
+      continue;
+    }
+    if (std::chrono::steady_clock::now() - t0 > std::chrono::milliseconds(200)) {
+      if (hipDeviceSynchronize() != hipSuccess) return EC_ERR_DEVICE;
+      break;
+    }
+    std::this_thread::sleep_for(std::chrono::microseconds(20));
+  }
+  std::atomic_thread_fence(std::memory_order_acquire);
+  return EC_OK;
 }
 
 // Workspace pointers of layout L inside the buffer at `ws` (a caller's
@@ -440,8 +477,7 @@ ec_status ec_plan(const ec_plan_desc* desc, ec_plan_t* out) {
   std::memset(hp, 0, rep_bytes);
   pl->report_host = static_cast<ec::Report*>(hp);
   void* dp = nullptr;
-  if (hipHostGetDevicePointer(&dp, hp, 0) != hipSuccess ||
-      hipEventCreateWithFlags(&pl->done, hipEventDisableTiming) != hipSuccess) {
+  if (hipHostGetDevicePointer(&dp, hp, 0) != hipSuccess) {
     (void)hipHostFree(hp);
     delete pl;
     return EC_ERR_DEVICE;
@@ -457,7 +493,6 @@ ec_status ec_plan(const ec_plan_desc* desc, ec_plan_t* out) {
   if (hipHostMalloc(&cp, cbytes, hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess ||
       hipHostGetDevicePointer(&cdp, cp, 0) != hipSuccess) {
     if (cp) (void)hipHostFree(cp);
-    (void)hipEventDestroy(pl->done);
     (void)hipHostFree(hp);
     delete pl;
     return EC_ERR_DEVICE;
@@ -492,9 +527,8 @@ ec_status ec_plan(const ec_plan_desc* desc, ec_plan_t* out) {
 
 ec_status ec_plan_destroy(ec_plan_t pl) {
   if (!pl) return EC_ERR_INVALID;
-  if (pl->have_done) (void)hipEventSynchronize(pl->done);
+  (void)wait_done(pl);
   for (hipEvent_t e : pl->prof_pool) (void)hipEventDestroy(e);
-  if (pl->done) (void)hipEventDestroy(pl->done);
   if (pl->report_host) (void)hipHostFree(pl->report_host);
   if (pl->consts_host) (void)hipHostFree(pl->consts_host);
   delete pl;
@@ -520,8 +554,7 @@ ec_status ec_compress(ec_plan_t pl, int64_t iter, const float* d_in, void* d_out
   ec_status st = enqueue_compress(pl, pl->work, clear, iter, d_in, d_out, out_cap, s);
   if (st != EC_OK) return st;
   if (assembled) pl->hash_clear = true;
-  record_done(pl, s);
-  return EC_OK;
+  return mark_done(pl, s);
 }
 
 ec_status ec_compress_static(ec_plan_t pl, int64_t iter, const float* d_in, void* d_out,
@@ -544,8 +577,7 @@ ec_status ec_compress_static(ec_plan_t pl, int64_t iter, const float* d_in, void
   if (st != EC_OK) return st;
   st = enqueue_compress(pl, make_work(pl->L, base), true, iter, d_in, d_out, out_cap, s);
   if (st != EC_OK) return st;
-  record_done(pl, s);
-  return EC_OK;
+  return mark_done(pl, s);
 }
 
 ec_status ec_decompress(ec_plan_t pl, const void* d_stream, size_t stream_cap, float* d_out,
@@ -579,14 +611,13 @@ ec_status ec_decompress(ec_plan_t pl, const void* d_stream, size_t stream_cap, f
     return e;
   });
   if (st != EC_OK) return st;
-  record_done(pl, s);
-  return EC_OK;
+  return mark_done(pl, s);
 }
 
 ec_status ec_ratio(ec_plan_t pl, double* total_cr, uint64_t* compressed_bytes,
                    double* per_segment_cr) {
   if (!pl) return EC_ERR_INVALID;
-  if (pl->have_done && hipEventSynchronize(pl->done) != hipSuccess) return EC_ERR_DEVICE;
+  if (wait_done(pl) != EC_OK) return EC_ERR_DEVICE;
   const ec::Shape& sh = pl->L.sh;
   volatile ec::Report* r = pl->report_host;
   uint64_t total = r->total_bytes;
@@ -631,9 +662,7 @@ ec_status ec_homo_counts(ec_plan_t pl, int64_t iter, const float* d_in, void* d_
   uint8_t* rep = reinterpret_cast<uint8_t*>(pl->report_dev);
   ea.seg_norig = reinterpret_cast<uint32_t*>(rep + pl->norig_off);
   if (ec::launch_distinct_raw(ea, s) != hipSuccess) return EC_ERR_DEVICE;
-  if (hipEventRecord(pl->done, s) != hipSuccess) return EC_ERR_DEVICE;
-  pl->have_done = true;
-  if (hipEventSynchronize(pl->done) != hipSuccess) return EC_ERR_DEVICE;
+  if (mark_done(pl, s) != EC_OK || wait_done(pl) != EC_OK) return EC_ERR_DEVICE;
   const uint8_t* host = reinterpret_cast<const uint8_t*>(pl->report_host);
   const volatile uint32_t* meta = reinterpret_cast<const volatile uint32_t*>(host + pl->meta_off);
   const volatile uint32_t* norig = reinterpret_cast<const volatile uint32_t*>(host + pl->norig_off);
@@ -721,7 +750,7 @@ ec_status ec_debug_attach(ec_plan_t pl, int32_t* d_codes, uint8_t* d_outlier, ui
 
 ec_status ec_profile_enable(ec_plan_t pl, int enable, uint32_t max_launches) {
   if (!pl) return EC_ERR_INVALID;
-  if (pl->have_done) (void)hipEventSynchronize(pl->done);
+  (void)wait_done(pl);
   pl->prof_recs.clear();
   pl->prof_next = 0;
   pl->prof_dropped = 0;

@@ -175,7 +175,8 @@ size_t ec_workspace_bytes(const ec_plan_desc* desc);
  * only (ec_compress then returns EC_ERR_INVALID).  *out is NULL on failure. */
 ec_status ec_plan(const ec_plan_desc* desc, ec_plan_t* out);
 
-/* Release the plan's host resources (the workspace stays the caller's). */
+/* Wait for the plan's last enqueued call, then release the plan's host
+ * resources (the workspace stays the caller's). */
 ec_status ec_plan_destroy(ec_plan_t plan);
 
 /* Upper bound of a compressed stream (every tile stored raw); 0 for NULL.
@@ -204,7 +205,9 @@ ec_status ec_compress(ec_plan_t plan, int64_t iter, const float* d_in, void* d_o
 ec_status ec_decompress(ec_plan_t plan, const void* d_stream, size_t stream_cap, float* d_out,
                         void* stream);
 
-/* Wait for this plan's last enqueued call, then report the last compression:
+/* Wait for this plan's last enqueued call (its last launch stores the call's
+ * number into the plan's pinned report; after 200 ms without it the whole
+ * device is waited for), then report the last compression:
  * total_cr = 4*T*B*D / stream bytes (headers included), the stream bytes, and
  * per_segment_cr[p*T + t] = 4*rows(p)*D / segment bytes (may be NULL).  The
  * total is a ratio of total bytes, which is what Table V's "avg." row

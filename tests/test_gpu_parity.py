@@ -195,6 +195,63 @@ def test_determinism_across_runs():
         assert np.array_equal(run_gpu(cfg, x, debug=False)["stream"], first)
 
 
+def test_ratio_waits_for_queued_calls():
+    """ec_ratio waits for the plan's last call however much work is queued
+    before it: on a side stream behind a little work (the call's completion
+    number seen in the pinned report), and on the current stream behind more
+    than 200 ms of work (then the wait falls back to the whole device).  The
+    report it returns (bytes, then a decoder's corrupt status) is the call's."""
+    rng = np.random.default_rng(31)
+    T, B, D = 4, 4096, 128
+    x = torch.from_numpy(dup_rows(rng, T, B, D, frac_unique=0.3)).cuda()
+    plan = ec.Plan(T, B, D, 1, 1, 0.01)
+    out = plan.empty_stream()
+    plan.compress(x, out, 3)
+    torch.cuda.synchronize()
+    _, nb0, _ = plan.ratio()
+    ref = out[:nb0].clone()
+    a = torch.randn(4096, 4096, device="cuda")
+
+    def busy(ms, stream):
+        # matrix products on `stream` until about `ms` of work is queued
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            c = a
+            e0.record()
+            c = a @ c
+            e1.record()
+        e1.synchronize()
+        per = max(e0.elapsed_time(e1), 1e-3)
+        with torch.cuda.stream(stream):
+            e0.record()
+            for _ in range(int(ms / per) + 1):
+                c = (a @ c) * 1e-3
+            e1.record()
+        return e0, e1
+
+    side = torch.cuda.Stream()
+    for ms, stream in ((20.0, side), (400.0, torch.cuda.current_stream())):
+        out.zero_()
+        stream.wait_stream(torch.cuda.current_stream())
+        e0, e1 = busy(ms, stream)
+        plan.compress(x, out, 3, stream=stream)
+        cr, nb, st = plan.ratio()
+        assert st == ec.EC_OK and nb == nb0, (ms, nb, nb0)
+        torch.cuda.synchronize()
+        say(f"[ratio wait] queued {e0.elapsed_time(e1):.1f} ms on "
+            f"{'the side' if stream is side else 'the current'} stream")
+        assert torch.equal(out[:nb], ref)
+    # a corrupt stream's status, reported after a queued decompression
+    bad = ref.clone()
+    bad[0] ^= 1
+    y = torch.empty(T, B, D, device="cuda")
+    busy(250.0, torch.cuda.current_stream())
+    plan.decompress(bad, y)
+    assert plan.ratio(raise_on_error=False)[-1] == ec.EC_ERR_CORRUPT
+    plan.decompress(ref, y)
+    assert plan.ratio(raise_on_error=False)[-1] == ec.EC_OK
+
+
 def test_per_segment_ratio_and_chunk_sizes():
     rng = np.random.default_rng(13)
     x = dup_rows(rng, 3, 500, 32)
