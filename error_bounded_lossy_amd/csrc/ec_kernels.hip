@@ -2585,12 +2585,33 @@ __device__ __forceinline__ bool seg_flags_ok(uint32_t flags, uint32_t coder, boo
   return !(hs && coder == kCoderBitpack) && !(coder == kCoderHuffman && (flags & 1u) && !hs);
 }
 
+// Whole wave, wave-uniform arguments: loads that pull lines of a buffer of
+// `bytes` bytes at p into the caches ahead of the dependent reads that need
+// them, so that those reads wait for the L2 and not for HBM.  touch_lines:
+// one word of each 128-byte line of the first min(bytes, 8 KiB); touch_two:
+// the words at byte offsets o0 and o1.  Nothing past the buffer (or past
+// 2 GiB) is read.  The caller keeps the returned word alive until its
+// dependent reads are done, so the wait for these loads lands there.
+__device__ __forceinline__ uint32_t touch_lines(const uint8_t* p, uint64_t bytes) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t lim = (uint32_t)min(bytes, (uint64_t)8192);
+  return buf_ld_u32(buf_rsrc(p, lim), lane * 128 + 4 <= lim ? lane * 128 : kOff);
+}
+__device__ __forceinline__ uint32_t touch_two(const uint8_t* p, uint64_t bytes, uint64_t o0, uint64_t o1) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t lim = (uint32_t)min(bytes, (uint64_t)kOff);
+  const uint64_t o = (lane == 0 ? o0 : o1) & ~3ull;
+  return buf_ld_u32(buf_rsrc(p, lim), lane < 2 && o + 4 <= lim ? (uint32_t)o : kOff);
+}
+
 // Locate and check tile record k of a segment whose records start at rec_lo
 // or later (after the tile directory, and the codebook of a Huffman segment);
-// every read is bounds-checked against the segment.
+// every read is bounds-checked against the segment.  With `touch` (a whole
+// wave with uniform arguments), the record's first lines are pulled into the
+// caches together with its header (touch_lines).
 __device__ DecTile locate_tile(const uint8_t* seg, uint64_t seg_bytes, uint32_t ntiles,
                                uint32_t rows, uint32_t k, uint32_t D, bool valid, uint64_t rec_lo,
-                               bool hseg, uint32_t win) {
+                               bool hseg, uint32_t win, uint32_t* touch = nullptr) {
   DecTile r{};
   r.ok = 0;
   if (k >= ntiles) return r;
@@ -2598,6 +2619,7 @@ __device__ DecTile locate_tile(const uint8_t* seg, uint64_t seg_bytes, uint32_t 
   if (off < rec_lo || (off & 15u) || (uint64_t)off + 16 > seg_bytes) return r;
   r.rec = seg + off;
   r.avail = seg_bytes - off;
+  if (touch) *touch += touch_lines(r.rec, r.avail);
   r.n = min(kTileRows, rows - k * kTileRows);
   r.bitmap = rd64(r.rec);
   r.nout = rd32(r.rec + 8);
@@ -3000,9 +3022,12 @@ __global__ void __launch_bounds__(kThreads) ec_decode_kernel(DecArgs a) {
 // ---------------------------------------------------------------------------
 // One whole wave (every lane computes the same): check the stream header,
 // chunk table, segment header and tile record of tile `ticket`; lane 0 fills
-// sh_out (offsets relative to `in`).
+// sh_out (offsets relative to `in`).  With `touch`, the lines its later
+// steps read (the segment's chunk-table entry, the tile's directory entry,
+// the record) are pulled into the caches as soon as their addresses are
+// known; the word returned there must be kept alive by the caller.
 __device__ void dec_locate(const DecArgs& a, const uint8_t* in, uint32_t ticket, DecShared& sh_out,
-                           uint64_t& rec_off) {
+                           uint64_t& rec_off, uint32_t* touch = nullptr) {
   DecShared sh;  // computed by the whole wave (uniform), stored by lane 0
   const uint32_t T = a.sh.T, B = a.sh.B, D = a.sh.D, P = a.sh.P;
   uint32_t s, k;
@@ -3027,6 +3052,7 @@ __device__ void dec_locate(const DecArgs& a, const uint8_t* in, uint32_t ticket,
          rd64(in + 40) == 4ull * T * B * D && rd64(in + 56) == 0 && total <= a.cap;
   }
   uint64_t base = 64 + align_up(8ull * P, 16);
+  if (touch && pch == 0) *touch += touch_two(in, a.cap, base + 8ull * t, base + 8ull * t);
   uint64_t chunk = base, cb = 0;
   if (ok && base > total) ok = 0;
   for (uint32_t q = 0; ok && q <= pch; q++) {
@@ -3038,6 +3064,7 @@ __device__ void dec_locate(const DecArgs& a, const uint8_t* in, uint32_t ticket,
   if (ok) {
     so = rd64(in + chunk + 8ull * t);
     if (so < align_up(8ull * T, 16) || (so & 15u) || so + 32 > cb) ok = 0;
+    if (touch && ok) *touch += touch_two(in + chunk + so, cb - so, 32 + 4ull * k, 32 + 4ull * k);
   }
   sh.hseg = 0;
   sh.win = 0;
@@ -3072,8 +3099,8 @@ __device__ void dec_locate(const DecArgs& a, const uint8_t* in, uint32_t ticket,
   sh.total = total;
   rec_off = 0;
   if (ok && nt) {
-    DecTile tl =
-        locate_tile(in + chunk + so, sb, nt, rows, k, D, sh.valid != 0, sh.rec_lo, sh.hseg != 0, sh.win);
+    DecTile tl = locate_tile(in + chunk + so, sb, nt, rows, k, D, sh.valid != 0, sh.rec_lo,
+                             sh.hseg != 0, sh.win, touch);
     ok = tl.ok;
     sh.tl = tl;
     rec_off = (uint64_t)(tl.rec - in);
@@ -3229,16 +3256,17 @@ __device__ __forceinline__ uint32_t lower_bound8(const uint32_t* op, uint32_t n,
 }
 
 template <int C>
-__device__ __forceinline__ void index_tile(const uint8_t* __restrict__ in, const DecArgs& a, uint32_t ticket,
+__device__ __forceinline__ uint32_t index_tile(const uint8_t* __restrict__ in, const DecArgs& a, uint32_t ticket,
                                            DecIndexLds<C>& x) {
   constexpr uint32_t D = 64u * C;
   DecShared& sh = x.sh;
   const uint32_t lane = threadIdx.x & 63;
+  uint32_t tv = 0;  // the lines pulled into the caches ahead (kept alive by the caller)
   {
     // every lane runs the same checks on the same (wave-uniform) words, so
     // the reads and the arithmetic can be scalar; lane 0 stores the result
     uint64_t ro;
-    dec_locate(a, in, ticket, sh, ro);
+    dec_locate(a, in, ticket, sh, ro, &tv);
     if (lane == 0) x.rec = ro;
   }
   lds_sync();
@@ -3255,7 +3283,7 @@ __device__ __forceinline__ void index_tile(const uint8_t* __restrict__ in, const
   if (!sh.ok || sbytes >= (1ull << 31)) {
     if (lane == 0) report_error(a.report, kDevErrCorrupt);
     put_tile();
-    return;
+    return tv;
   }
   {  // a segment's first tile checks its totals, tile 0 the chunk sizes
     bool good = k != 0 || seg_totals_ok(in + seg_off, sbytes, sh.ntiles, sh.rec_lo);
@@ -3265,7 +3293,7 @@ __device__ __forceinline__ void index_tile(const uint8_t* __restrict__ in, const
   if (n == 0) {
     flags = kTileOk;
     put_tile();
-    return;
+    return tv;
   }
   const uint8_t* sg = in + seg_off;
   const uint8_t* rec = in + rec_off;
@@ -3274,12 +3302,12 @@ __device__ __forceinline__ void index_tile(const uint8_t* __restrict__ in, const
   if (mode == 0) {
     flags = kTileOk | kTileRaw;
     put_tile();
-    return;
+    return tv;
   }
   if (mode == 2) {  // a Huffman record: ec_decode_huff_pair / ec_decode_huff and ec_fill_refs
     flags = kTileOk | kTileHuff;
     put_tile();
-    return;
+    return tv;
   }
   const uint32_t rb = rows <= 65536 ? 2 : 4;
   const uint64_t bitmap = sh.tl.bitmap;
@@ -3313,7 +3341,7 @@ __device__ __forceinline__ void index_tile(const uint8_t* __restrict__ in, const
   if (bad) {
     if (lane == 0) report_error(a.report, kDevErrCorrupt);
     put_tile();
-    return;
+    return tv;
   }
   flags = kTileOk;
   put_tile();
@@ -3433,6 +3461,7 @@ __device__ __forceinline__ void index_tile(const uint8_t* __restrict__ in, const
 #pragma unroll
     for (uint32_t j = 0; j < C; j++) x.dblk[i * C + j] = (bo[j] << 4) | bw[j];
   }
+  return tv;
 }
 
 // Rows of one decode step (row i0, and i0 + 1 when C = 1) that need more than
@@ -3628,7 +3657,9 @@ __global__ void __launch_bounds__(kThreads) ec_decode_fast(const uint8_t* __rest
                                                           float* __restrict__ yout, DecArgs a) {
   __shared__ DecIndexLds<C> xi[kDecTiles];
   const uint32_t wv = wave_id(), t0 = blockIdx.x * kDecTiles;
-  if (wv < kDecTiles && t0 + wv < a.sh.ntiles) index_tile<C>(in, a, t0 + wv, xi[wv]);
+  uint32_t tv = 0;
+  if (wv < kDecTiles && t0 + wv < a.sh.ntiles) tv = index_tile<C>(in, a, t0 + wv, xi[wv]);
+  asm volatile("" ::"v"(tv));  // the lines the index step pulled ahead are in (see touch_lines)
   __syncthreads();
   for (uint32_t q = 0; q < kDecTiles && t0 + q < a.sh.ntiles; q++)
     decode_tile<C>(in, yout, a, t0 + q, xi[q].td, xi[q].drow, xi[q].dblk);
