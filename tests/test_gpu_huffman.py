@@ -153,6 +153,23 @@ def test_many_ties(coder):
     check_parity(coder, sym, "ties")
 
 
+@pytest.mark.parametrize("m", [2, 3, 63, 64, 65, 66, 100, 126, 127, 128])
+@pytest.mark.parametrize("pattern", ["small", "equal"])
+def test_ties_in_the_small_tree(coder, m, pattern):
+    """Up to 127 used symbols the tree is built by selects on one wave, from
+    both queues in registers (two registers each, lanes 0-63 and 64-127);
+    128 symbols take the rounds form.  Counts of 1-3 (or all equal) make
+    leaves and internal nodes tie at almost every step, where the leaf must
+    be taken first: the code lengths, hence the codebook bytes, must be the
+    oracle's on both sides of 64 and of 127/128."""
+    rng = np.random.default_rng(1000 + m)
+    used = rng.choice(4095, m, replace=False)
+    counts = rng.integers(1, 4, m) if pattern == "small" else np.full(m, 5)
+    sym = np.repeat(used, counts).astype(np.uint16)
+    rng.shuffle(sym)
+    check_parity(coder, sym, f"small-tree ties m={m} {pattern}")
+
+
 def test_symbol_outside_the_alphabet_is_reported(coder):
     sym = np.full(1000, 2047, np.uint16)
     sym[517] = 4095
