@@ -2588,8 +2588,8 @@ __device__ __forceinline__ bool seg_flags_ok(uint32_t flags, uint32_t coder, boo
 // Whole wave, wave-uniform arguments: loads that pull lines of a buffer of
 // `bytes` bytes at p into the caches ahead of the dependent reads that need
 // them, so that those reads wait for the L2 and not for HBM.  touch_lines:
-// one word of each 128-byte line of the first min(bytes, 8 KiB); touch_two:
-// the words at byte offsets o0 and o1.  Nothing past the buffer (or past
+// one word of each 128-byte line of the first min(bytes, 8 KiB); touch_word:
+// the word at byte offset o (lane 0).  Nothing past the buffer (or past
 // 2 GiB) is read.  The caller keeps the returned word alive until its
 // dependent reads are done, so the wait for these loads lands there.
 __device__ __forceinline__ uint32_t touch_lines(const uint8_t* p, uint64_t bytes) {
@@ -2597,11 +2597,11 @@ __device__ __forceinline__ uint32_t touch_lines(const uint8_t* p, uint64_t bytes
   const uint32_t lim = (uint32_t)min(bytes, (uint64_t)8192);
   return buf_ld_u32(buf_rsrc(p, lim), lane * 128 + 4 <= lim ? lane * 128 : kOff);
 }
-__device__ __forceinline__ uint32_t touch_two(const uint8_t* p, uint64_t bytes, uint64_t o0, uint64_t o1) {
+__device__ __forceinline__ uint32_t touch_word(const uint8_t* p, uint64_t bytes, uint64_t o) {
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t lim = (uint32_t)min(bytes, (uint64_t)kOff);
-  const uint64_t o = (lane == 0 ? o0 : o1) & ~3ull;
-  return buf_ld_u32(buf_rsrc(p, lim), lane < 2 && o + 4 <= lim ? (uint32_t)o : kOff);
+  o &= ~3ull;
+  return buf_ld_u32(buf_rsrc(p, lim), lane == 0 && o + 4 <= lim ? (uint32_t)o : kOff);
 }
 
 // Locate and check tile record k of a segment whose records start at rec_lo
@@ -2619,7 +2619,10 @@ __device__ DecTile locate_tile(const uint8_t* seg, uint64_t seg_bytes, uint32_t 
   if (off < rec_lo || (off & 15u) || (uint64_t)off + 16 > seg_bytes) return r;
   r.rec = seg + off;
   r.avail = seg_bytes - off;
-  if (touch) *touch += touch_lines(r.rec, r.avail);
+  if (touch) {  // up to the next record (its directory entry is read with this one)
+    const uint32_t nxt = k + 1 < ntiles ? rd32(seg + 32 + 4ull * (k + 1)) : 0u;
+    *touch += touch_lines(r.rec, nxt > off ? min((uint64_t)(nxt - off), r.avail) : r.avail);
+  }
   r.n = min(kTileRows, rows - k * kTileRows);
   r.bitmap = rd64(r.rec);
   r.nout = rd32(r.rec + 8);
@@ -3052,7 +3055,7 @@ __device__ void dec_locate(const DecArgs& a, const uint8_t* in, uint32_t ticket,
          rd64(in + 40) == 4ull * T * B * D && rd64(in + 56) == 0 && total <= a.cap;
   }
   uint64_t base = 64 + align_up(8ull * P, 16);
-  if (touch && pch == 0) *touch += touch_two(in, a.cap, base + 8ull * t, base + 8ull * t);
+  if (touch && pch == 0) *touch += touch_word(in, a.cap, base + 8ull * t);
   uint64_t chunk = base, cb = 0;
   if (ok && base > total) ok = 0;
   for (uint32_t q = 0; ok && q <= pch; q++) {
@@ -3064,7 +3067,7 @@ __device__ void dec_locate(const DecArgs& a, const uint8_t* in, uint32_t ticket,
   if (ok) {
     so = rd64(in + chunk + 8ull * t);
     if (so < align_up(8ull * T, 16) || (so & 15u) || so + 32 > cb) ok = 0;
-    if (touch && ok) *touch += touch_two(in + chunk + so, cb - so, 32 + 4ull * k, 32 + 4ull * k);
+    if (touch && ok) *touch += touch_word(in + chunk + so, cb - so, 32 + 4ull * k);
   }
   sh.hseg = 0;
   sh.win = 0;
