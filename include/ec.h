@@ -32,8 +32,10 @@
  *     workspace).  The plan owns only host memory (a copy of the descriptor
  *     and a small pinned host block the device reports sizes into).
  *   - ec_compress / ec_decompress enqueue kernels and return; they never
- *     allocate, free or synchronize.  One plan serves one stream at a time;
- *     separate plans are independent.
+ *     allocate, free or synchronize.  One plan serves one stream and one host
+ *     thread at a time (its calls share the workspace, the report and the
+ *     count of calls that ec_ratio waits for); separate plans are
+ *     independent.
  *   - Every entry point returns ec_status; nothing is printed and no C++
  *     exception crosses the ABI.  Argument errors are detected on the host
  *     before anything is enqueued.  Conditions found on the device (corrupt
