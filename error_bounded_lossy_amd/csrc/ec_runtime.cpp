@@ -238,8 +238,9 @@ ec_status make_layout(const ec_plan_desc* d, Layout* L) {
 
 // Tables whose range items the quantize pass takes before its first tile: far
 // enough ahead that a tile rarely finds its table's range unfinished (on the
-// 26-table dim-128 batch, 16 ahead beat 1, 2, 4, 8 and all).
-constexpr uint32_t kRangeAhead = 16;
+// 26-table dim-128 batch, 12 ahead beat 1, 2, 4, 6, 8, 10, 14, 16 and all by
+// 0.5-2 us of the launch; the dim-64 batch does not tell them apart).
+constexpr uint32_t kRangeAhead = 12;
 
 double schedule_factor(const ec_schedule& s, int64_t iter) {
   int64_t i = iter < 0 ? 0 : iter;
